@@ -1,0 +1,315 @@
+"""Benchmark of the verification step on one MI355X.
+
+One step = one spec_verify (target pass over the draft, greedy choice, accepted-path walk) plus
+one spec_commit_kv (the accepted path's K/V rows compacted, context advanced), on synthetic
+random-init weights of the 27B-class dense shape (64 layers, hidden 5120, 40 q / 8 kv heads of
+128, SwiGLU 17408, vocab 151936), bf16, inputs resident in HBM. Steps are replayed from a HIP
+graph captured once.
+
+Workloads (--config):
+  block   (default) batch 1, linear block of 16 uniform-random draft tokens, context 4096
+  tree    batch 1, 64-node draft tree of depth <= 10, context 8192
+  batched 32 requests x block of 16, contexts uniform in [512, 8192], shuffled 16-token pages
+
+Prints one JSON line: verified draft tokens/s (batch * k / step time), the step's algorithmic
+HBM bytes and GB/s, the roofline of the dominant kernel (the weight-streaming projection GEMM,
+timed per launch with HIP events on the stream it runs on), and the CPU oracle timed on a
+bounded sample of the same workload on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np
+import torch
+
+import synth
+import tree_verification_skinny_amd as tv
+
+METRIC = "verified tokens/sec + verify-step HBM GB/s (% peak), 27B-shape dense, 1 GPU"
+HBM_PEAK_GBPS = 8000.0
+SEED = 20261202
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def workload(name):
+    if name == "block":
+        return dict(batch=1, k=16, ctx=[4096], tree=False)
+    if name == "tree":
+        return dict(batch=1, k=64, ctx=[8192], tree=True)
+    if name == "batched":
+        rng = np.random.default_rng(synth.seed_of(SEED, "ctx"))
+        return dict(batch=32, k=16, ctx=[int(c) for c in rng.integers(512, 8193, 32)], tree=False)
+    raise ValueError(name)
+
+
+def build_model(shape, device):
+    t0 = time.time()
+    layers = [synth.layer_weights(shape, SEED, l, device) for l in range(shape.n_layers)]
+    embed = synth.randn_bf16((shape.vocab, shape.hidden), 0.02, device, SEED, "embed")
+    lm = synth.randn_bf16((shape.vocab, shape.hidden), 0.02, device, SEED, "lm_head")
+    fn = torch.ones(shape.hidden, dtype=torch.bfloat16, device=device)
+    torch.cuda.synchronize()
+    log(f"weights generated on the GPU in {time.time() - t0:.1f}s")
+    return tv.Weights(tv.ModelCfg.of(shape), embed, fn, lm, layers)
+
+
+def step_bytes(shape, batch, k, ctx):
+    """Algorithmic HBM bytes of one verify step: every weight once (embedding rows only for the
+    tokens), every context K/V row once per layer, the draft rows' K/V writes."""
+    H, F, V, L = shape.hidden, shape.ffn, shape.vocab, shape.n_layers
+    d, nq, nkv = shape.head_dim, shape.n_q_heads, shape.n_kv_heads
+    per_layer_w = 2 * (shape.qkv_rows * H + H * nq * d + 2 * F * H + H * F + 2 * H)
+    weights = L * per_layer_w + 2 * (V * H + H) + 2 * batch * k * H
+    kv_read = L * sum(c for c in ctx) * nkv * d * 2 * 2
+    kv_write = L * batch * k * nkv * d * 2 * 2
+    return weights + kv_read + kv_write
+
+
+def step_flops(shape, batch, k, ctx, depth_mean):
+    H, F, V, L = shape.hidden, shape.ffn, shape.vocab, shape.n_layers
+    d, nq = shape.head_dim, shape.n_q_heads
+    M = batch * k
+    gemm = 2 * M * (shape.qkv_rows * H + H * nq * d + 2 * F * H + H * F) * L + 2 * M * V * H
+    keys = sum(ctx) * k + batch * k * (depth_mean + 1)
+    attn = L * 4 * nq * d * keys
+    return gemm + attn
+
+
+def time_dominant_gemm(weights, shape, m, device, reps=8):
+    """Per-launch durations of the projection GEMM (the kernel spec_verify runs for every weight
+    matrix) at this workload's row count, on the model's own weights, rotating through the
+    layers so that no launch finds its weights in cache. HIP events on the launch stream.
+    Returns (bytes per launch, seconds per launch), averaged over the four projections."""
+    H, F = shape.hidden, shape.ffn
+    shapes = [("w_qkv", H), ("w_o", shape.n_q_heads * shape.head_dim), ("w_gate_up", H), ("w_down", F)]
+    stream = torch.cuda.current_stream()
+    tot_bytes, tot_s, n = 0, 0.0, 0
+    xs = {kd: torch.randn((m, kd), device=device).to(torch.bfloat16) for _, kd in shapes}
+    part = torch.empty(max(tv.spec_skinny_gemm_bytes(m, weights.tensors["layers"][0][nm].shape[0], kd) // 4
+                           for nm, kd in shapes), dtype=torch.float32, device=device)
+    evs = []
+    for r in range(reps + 1):
+        for l in range(shape.n_layers):
+            for nm, kd in shapes:
+                w = weights.tensors["layers"][l][nm]
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                tv.spec_skinny_gemm(xs[kd], w, part)
+                e1.record(stream)
+                if r > 0:
+                    evs.append((e0, e1, w.numel() * 2 + m * kd * 2 + m * w.shape[0] * 2))
+    torch.cuda.synchronize()
+    for e0, e1, b in evs:
+        tot_s += e0.elapsed_time(e1) / 1e3
+        tot_bytes += b
+        n += 1
+    return tot_bytes / n, tot_s / n
+
+
+def copy_probe(device, nbytes=4 << 30):
+    a = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=device)
+    b = torch.empty_like(a)
+    a.fill_(1.0)
+    for _ in range(2):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    s = e0.elapsed_time(e1) / 1e3 / 5
+    del a, b
+    return 2 * nbytes / s / 1e9
+
+
+def cpu_baseline(weights, shape, kv, tokens, parent, ctx, budget_s):
+    """The CPU oracle as it stands, on a bounded sample of the same workload: request 0's pass
+    through the first n layers (n grows until the budget is spent) and the output head, scaled
+    to the whole step (per-layer time x 64, plus the head, times the number of requests)."""
+    import oracle
+    from tree_verification_skinny_amd import kvlayout
+
+    def host(t):
+        return t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+
+    cfg = oracle.Cfg(shape.n_layers, shape.hidden, shape.n_q_heads, shape.n_kv_heads,
+                     shape.head_dim, shape.ffn, shape.vocab, shape.rms_eps, shape.rope_theta)
+    W = weights.tensors
+    model = oracle.Model(cfg, host(W["embed"]), host(W["final_norm"]), host(W["lm_head"]),
+                         layer_fn=lambda l: {k: host(v) for k, v in W["layers"][l].items()})
+    tok0 = tokens[0]
+    par0 = oracle.chain(len(tok0)) if parent is None else parent[0]
+    x = oracle.embed(model, tok0)
+    spent, n = 0.0, 0
+    pos = torch.arange(ctx[0])
+    while n < shape.n_layers and spent < budget_s:
+        lw = model.layer(n)
+        kc, vc = kvlayout.read_rows(kv, n, 0, pos)
+        kc, vc = host(kc), host(vc)
+        t0 = time.time()
+        x, _, _ = oracle.layer_forward(cfg, lw, kc, vc, par0, x)
+        spent += time.time() - t0
+        n += 1
+    t0 = time.time()
+    lg = oracle.logits(model, x)
+    oracle.argmax(lg)
+    head = time.time() - t0
+    per_request = spent / n * shape.n_layers + head
+    step = per_request * len(tokens)
+    k = len(tok0)
+    return {"value": len(tokens) * k / step, "unit": "verified tokens/s", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": (f"request 0 of {len(tokens)}, layers 0..{n - 1} of {shape.n_layers} "
+                       f"({spent:.1f}s) + output head ({head:.1f}s), scaled to the full step "
+                       f"({step:.1f}s per step)")}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="block", choices=["block", "tree", "batched"])
+    ap.add_argument("--eager", action="store_true", help="launch every step instead of a HIP graph")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-timing", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the verify step of "
+              "this build runs on a single MI355X).", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs the GPU", file=sys.stderr)
+        sys.exit(2)
+    device = "cuda"
+    shape = synth.DENSE_27B
+    wl = workload(args.config)
+    B, K, ctx = wl["batch"], wl["k"], wl["ctx"]
+    total_steps = args.steps + args.warmup + 3
+    weights = build_model(shape, device)
+
+    # cache: room for the context, the draft, and every step's commit (at most K rows each)
+    pages = [(c + K + K * total_steps + 15) // 16 for c in ctx]
+    table, n_pages = synth.page_table(B, pages, SEED, shuffle=(B > 1))
+    kv = tv.PagedKV.empty(tv.ModelCfg.of(shape), n_pages, torch.from_numpy(table), device)
+    g = torch.Generator(device=device)
+    g.manual_seed(SEED)
+    kv.k_pool.normal_(generator=g)
+    kv.v_pool.normal_(generator=g)
+
+    if wl["tree"]:
+        parent = np.stack([synth.random_tree(K, 10, SEED, b) for b in range(B)]).astype(np.int32)
+        tokens = np.stack([synth.tree_tokens(parent[b], shape.vocab, SEED, b) for b in range(B)])
+        depths = []
+        for b in range(B):
+            dep = [0] * K
+            for i in range(1, K):
+                dep[i] = dep[parent[b][i]] + 1
+            depths.extend(dep)
+        depth_mean = float(np.mean(depths))
+    else:
+        parent = None
+        tokens = np.stack([synth.uniform_tokens(K, shape.vocab, SEED, b) for b in range(B)])
+        depth_mean = (K - 1) / 2
+    tokens = tokens.astype(np.int32)
+    t_tok = torch.from_numpy(tokens).to(device)
+    t_par = None if parent is None else torch.from_numpy(parent).to(device)
+    ctx0 = torch.tensor(ctx, dtype=torch.int32, device=device)
+    t_ctx = ctx0.clone()
+    acc = torch.empty(B, dtype=torch.int32, device=device)
+    bonus = torch.empty(B, dtype=torch.int32, device=device)
+    path = torch.empty((B, K), dtype=torch.int32, device=device)
+    ws = tv.workspace(tv.spec_workspace_bytes(weights.cfg, B, K, kv.max_pages), device)
+    mcfg = weights.cfg
+
+    def step():
+        tv.spec_verify(weights, kv, t_tok, t_par, t_ctx, B, K, acc, bonus, path, ws)
+        tv.spec_commit_kv(mcfg, kv, acc, path, t_ctx, B, K)
+
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        step()                              # first launch: module load, checks
+        stream.synchronize()
+        graph = None
+        if not args.eager:
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=stream):
+                step()
+        run = graph.replay if graph is not None else step
+        for _ in range(args.warmup):
+            run()
+        stream.synchronize()
+        log(f"warmup done; accepted {acc.cpu().tolist()[:4]} ctx {t_ctx.cpu().tolist()[:4]}")
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            run()
+        e1.record(stream)
+        e1.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    ctx_now = t_ctx.cpu().tolist()
+    nbytes = step_bytes(shape, B, K, ctx)
+    flops = step_flops(shape, B, K, ctx, depth_mean)
+    value = B * K / (ms / 1e3)
+    gbps = nbytes / (ms / 1e3) / 1e9
+    log(f"step {ms:.3f} ms  {value:.1f} verified tok/s  {gbps:.0f} GB/s ({gbps / HBM_PEAK_GBPS:.1%} of peak)")
+
+    result = {
+        "metric": METRIC, "value": round(value, 2), "unit": "verified tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded random-init weights N(0,0.02), context K/V N(0,1))",
+        "config": {"workload": {"block": "27B-shape dense, 64 layers + lm_head 151936, batch 1, "
+                                          "linear block of 16, context 4096",
+                                "tree": "27B-shape dense, 64 layers + lm_head, batch 1, 64-node "
+                                        "tree (depth<=10), context 8192",
+                                "batched": "27B-shape dense, 64 layers + lm_head, 32 requests x "
+                                           "block of 16, contexts U[512,8192], paged"}[args.config],
+                   "batch": B, "k": K, "ctx_mean": float(np.mean(ctx)), "layers": shape.n_layers,
+                   "vocab": shape.vocab, "hip_graph": not args.eager, "parallelism": "single GPU"},
+        "hbm": {"bytes_per_step": nbytes, "achieved_gbps": round(gbps, 1),
+                "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4)},
+        "mfma": {"flops_per_step": flops, "tflops": round(flops / (ms / 1e3) / 1e12, 2),
+                 "frac_of_bf16_peak": round(flops / (ms / 1e3) / 2.5e15, 5)},
+        "ctx_after": ctx_now[:4],
+    }
+    if not args.no_kernel_timing:
+        with torch.cuda.stream(stream):
+            b_launch, s_launch = time_dominant_gemm(weights, shape, B * K, device)
+        ach = b_launch / s_launch / 1e9
+        result["roofline"] = {"kernel": "gemm_partials_kernel (weight-streaming projection)",
+                              "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS,
+                              "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
+                              "traffic": None,
+                              "bytes_per_launch": int(b_launch),
+                              "us_per_launch": round(s_launch * 1e6, 2)}
+        result["copy_probe_gbps"] = round(copy_probe(device), 1)
+        log(f"projection GEMM: {ach:.0f} GB/s per launch ({s_launch * 1e6:.1f} us avg); "
+            f"copy probe {result['copy_probe_gbps']} GB/s")
+    if not args.no_cpu_baseline:
+        t_ctx.copy_(ctx0)
+        result["cpu_baseline"] = cpu_baseline(weights, shape, kv, tokens, parent, ctx,
+                                              args.cpu_seconds)
+        log(f"cpu baseline: {result['cpu_baseline']}")
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,170 @@
+/*
+ * specverify.h — C ABI of the MI355X (gfx950) verification step of lossless greedy speculative
+ * decoding.
+ *
+ * The operation. A drafter proposes several tokens per step and the target model checks all of
+ * them in one forward pass [JetSpec article, seventnews.com — opening section]. Parallel
+ * drafters propose a whole block [SpecPilot news piece, wireai.ir — "The main challenge"]; tree
+ * drafters propose a tree in which every token is conditioned on the path leading to it
+ * [JetSpec article — "Technical architecture"]. Verification is lossless in the greedy sense:
+ * every emitted token is the target's greedy choice [SpecPilot digest, airadar.tv — "Risks"].
+ * So one call scores a draft tree of k nodes per request against the request's KV cache and
+ * accepts the deepest root path whose every token equals the target's argmax given that path.
+ * At batch 1 that pass reads all target weights for a few tokens, and per-request overhead is
+ * what erodes batched speedups [SpecPilot digest — summary paragraph]: the library therefore
+ * runs every request of a batch in the same kernels, with no per-request launches and no host
+ * synchronisation.
+ *
+ * Target model (the pages fix none): pre-norm decoder, RMSNorm, rotate-half RoPE, grouped-query
+ * attention, SwiGLU MLP, untied embedding and output head, bf16 weights, fp32 accumulation.
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless marked HOST. Every call only enqueues work on
+ *     `stream` and returns; outputs are valid once the stream work has completed.
+ *   - The library never allocates or frees device memory; the caller owns every buffer and must
+ *     keep it alive until the enqueued work completes. Scratch comes from `workspace`.
+ *   - Problems visible on the host (NULL pointer, unsupported shape, small workspace) return a
+ *     negative SPEC_E* code and enqueue nothing. Problems visible only in device data (a token
+ *     outside the vocabulary, a malformed tree, a context that does not fit the request's
+ *     pages) mark that request alone: its accepted_len and bonus_token become -1, its path all
+ *     -1, its KV cache is not written; other requests in the batch proceed normally.
+ *   - Calls on different streams with disjoint outputs and workspaces may run concurrently; the
+ *     library keeps no global state.
+ *   - bf16 = IEEE binary32 truncated to its upper 16 bits (storage), rounded to nearest even.
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+#define SPEC_OK 0
+#define SPEC_EINVAL (-1)        /* NULL pointer, negative size, malformed argument */
+#define SPEC_EUNSUPPORTED (-2)  /* a shape this build does not implement (see spec_verify) */
+#define SPEC_EWORKSPACE (-3)    /* workspace smaller than the *_workspace_bytes answer */
+#define SPEC_EHIP (-4)          /* a HIP launch or runtime call failed */
+
+#define SPEC_PAGE_SIZE 16       /* tokens per KV page */
+#define SPEC_MAX_K 64           /* draft nodes per request (one 64-bit ancestor mask per node) */
+
+/* Model shape. Supported: head_dim in {64, 128}; n_q_heads a multiple of n_kv_heads;
+ * hidden, n_q_heads*head_dim and ffn multiples of 32; hidden <= 16384; vocab a multiple of 16.
+ * The workspace must be 256-byte aligned. */
+typedef struct {
+    int n_layers, hidden, n_q_heads, n_kv_heads, head_dim, ffn, vocab;
+    float rms_eps;              /* RMSNorm epsilon, added to mean(x^2) */
+    double rope_theta;          /* RoPE base: pair j of a head turns by pos * theta^(-2j/d) */
+} spec_model_cfg;
+
+/* One decoder layer, all bf16, row-major [out][in] (DEVICE pointers):
+ *   attn_norm [H]; w_qkv [(nq + 2 nkv) d][H] rows = q heads, then k heads, then v heads;
+ *   w_o [H][nq d]; mlp_norm [H]; w_gate_up [2F][H] rows = F gate rows, then F up rows;
+ *   w_down [H][F]. */
+typedef struct {
+    const void *attn_norm, *w_qkv, *w_o, *mlp_norm, *w_gate_up, *w_down;
+} spec_layer_weights;
+
+typedef struct {
+    spec_model_cfg cfg;
+    const spec_layer_weights *layers;   /* HOST array of cfg.n_layers entries */
+    const void *embed;                  /* bf16 [V][H] */
+    const void *final_norm;             /* bf16 [H] */
+    const void *lm_head;                /* bf16 [V][H] */
+} spec_weights;
+
+/* Paged KV cache, bf16. A page holds SPEC_PAGE_SIZE consecutive positions of one request.
+ *   k_pool [n_layers][n_pages][n_kv_heads][16][head_dim]   (keys, one row per position)
+ *   v_pool [n_layers][n_pages][n_kv_heads][head_dim][16]   (values, transposed in the page)
+ *   block_table [batch][max_pages_per_req]: page ids; position p of request b lives in page
+ *   block_table[b][p / 16], slot p % 16. Keys are stored after RoPE. */
+typedef struct {
+    void *k_pool;
+    void *v_pool;
+    const int32_t *block_table;
+    int n_pages;
+    int max_pages_per_req;
+} spec_kv_cache;
+
+/* Optional extra outputs of spec_verify (any member may be NULL; the struct pointer too). */
+typedef struct {
+    float *logits;          /* fp32 [batch*k][vocab]: the target's logits for every draft node */
+    int32_t *greedy;        /* int32 [batch*k]: argmax of each node's logits (lowest index) */
+    void *hidden;           /* bf16 [n_layers + 1][batch*k][hidden]: residual stream entering
+                               each layer, then after the last layer (before the final norm) */
+} spec_verify_extras;
+
+/* Workspace bytes spec_verify needs for this shape, batch, k and cache page budget per request
+ * (kv->max_pages_per_req of the calls it will serve). HOST out-pointer. */
+int spec_workspace_bytes(const spec_model_cfg *cfg, int batch, int k, int max_pages_per_req,
+                         size_t *bytes);
+
+/* One verification pass.
+ *   draft_tokens [batch][k]: node 0 of each request is the root, the last committed token
+ *       (its K/V is not yet in the cache); nodes 1..k-1 are draft tokens.
+ *   tree_parent  [batch][k] or NULL: parent[0] = -1 and 0 <= parent[i] < i (nodes in
+ *       topological order, one root). NULL means a linear block (parent[i] = i - 1).
+ *   ctx_len      [batch]: committed positions per request. Node i sits at position
+ *       ctx_len + depth(i). The caller must provide pages for positions [0, ctx_len + k).
+ * Effects: writes every node's rotated key and value into cache slots ctx_len .. ctx_len+k-1
+ *   (node order) of every layer. Outputs per request:
+ *   accepted_len [batch]: accepted draft tokens on the deepest accepted root path, 0..k-1 (the
+ *       root is not counted); bonus_token [batch]: the target's greedy token after that path's
+ *       last node; accepted_path [batch][k]: node ids of that path from the root, then -1.
+ *   Equal-depth accepted nodes (possible only with duplicate sibling tokens) resolve to the
+ *   lowest node id. Arithmetic: bf16 storage between steps, fp32 accumulation and softmax.
+ * Shapes: 1 <= k <= SPEC_MAX_K; batch >= 1. */
+int spec_verify(const spec_weights *weights, const spec_kv_cache *kv,
+                const int32_t *draft_tokens, const int32_t *tree_parent, const int32_t *ctx_len,
+                int batch, int k,
+                int32_t *accepted_len, int32_t *bonus_token, int32_t *accepted_path,
+                const spec_verify_extras *extras /* HOST, may be NULL */,
+                void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Commit the accepted path into the cache: for every layer, K and V, slot ctx_len + t receives
+ * the row of slot ctx_len + accepted_path[t], t = 0..accepted_len (the moves are ordered so
+ * that no source is overwritten before it is read); then ctx_len += accepted_len + 1, on the
+ * device. Requests whose accepted_len is negative are left untouched. Takes the outputs of
+ * spec_verify on the same stream; k and batch as given to it. */
+int spec_commit_kv(const spec_model_cfg *cfg, const spec_kv_cache *kv,
+                   const int32_t *accepted_len, const int32_t *accepted_path, int32_t *ctx_len,
+                   int batch, int k, hipStream_t stream);
+
+/* Workspace bytes spec_accept needs. HOST out-pointer. */
+int spec_accept_workspace_bytes(int batch, int k, int vocab, size_t *bytes);
+
+/* The acceptance half of spec_verify on caller-supplied logits: per node the greedy token
+ * (lowest index of the row maximum), then the accepted-path walk, with the same outputs and
+ * conventions as spec_verify. logits: fp32 [batch*k][vocab]. */
+int spec_accept(const float *logits, const int32_t *draft_tokens, const int32_t *tree_parent,
+                int batch, int k, int vocab,
+                int32_t *accepted_len, int32_t *bonus_token, int32_t *accepted_path,
+                int32_t *greedy /* [batch*k] or NULL */,
+                void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* The weight-streaming projection spec_verify runs for every weight matrix, on its own:
+ * partials[s][m][n] = sum, over split s's share of the reduction dimension, of x[m][j]*w[n][j]
+ * (bf16 operands, fp32 sums), with the split count spec_verify picks for this shape; the
+ * projection is the sum of the splits in index order. A single pass at batch 1 reads every
+ * weight once for a few rows [SpecPilot digest, airadar.tv — summary paragraph], so this is the
+ * kernel whose HBM bandwidth the pass lives on. For kernel-level tests and bandwidth
+ * measurement.
+ *   x: bf16 [m][kd]; w: bf16 [n][kd]; partials: fp32, spec_skinny_gemm_bytes() bytes;
+ *   *splits (HOST) receives the split count. Needs kd % 32 == 0, n % 16 == 0, m >= 1. */
+int spec_skinny_gemm_bytes(int m, int n, int kd, size_t *bytes);
+int spec_skinny_gemm(const void *x, int m, int kd, const void *w, int n, float *partials,
+                     size_t partial_bytes, int *splits, hipStream_t stream);
+
+/* Static text for a return code. */
+const char *spec_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECVERIFY_H */

@@ -68,6 +68,7 @@ def lib():
         if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
             build(force=True)
         L = ctypes.CDLL(_LIB)
+        L.orc_max_threads.restype = ctypes.c_int
         L.orc_f32_to_bf16.argtypes = [_f32p, _u16p, ctypes.c_int64]
         L.orc_bf16_to_f32.argtypes = [_u16p, _f32p, ctypes.c_int64]
         L.orc_tree_depth.argtypes = [_i32p, ctypes.c_int, _i32p]
@@ -100,6 +101,11 @@ def _p(a: Optional[np.ndarray], ptype):
     if a is None:
         return ctypes.cast(None, ptype)
     return a.ctypes.data_as(ptype)
+
+
+def threads() -> int:
+    """OpenMP threads the oracle's loops use on this host."""
+    return int(lib().orc_max_threads())
 
 
 # ---------------------------------------------------------------------------------------------

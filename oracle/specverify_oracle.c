@@ -32,6 +32,7 @@
  * independent output elements; every reduction stays in one thread, in index order.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -57,6 +58,9 @@ static uint16_t f32_to_bf16(float f) {
     u += 0x7fffu + lsb;
     return (uint16_t)(u >> 16);
 }
+
+/* Threads the OpenMP loops below use. */
+int orc_max_threads(void) { return omp_get_max_threads(); }
 
 void orc_f32_to_bf16(const float *in, uint16_t *out, int64_t n) {
     for (int64_t i = 0; i < n; ++i) out[i] = f32_to_bf16(in[i]);

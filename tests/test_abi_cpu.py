@@ -1,0 +1,135 @@
+"""The C ABI without a GPU: the library loads, exports every function include/specverify.h
+declares, sizes workspaces, and rejects bad host-visible arguments before enqueueing anything
+(none of these calls reaches the device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import tree_verification_skinny_amd as tv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADERS = [os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+           if f.endswith(".h")]
+
+TINY = tv.ModelCfg(2, 256, 4, 2, 64, 704, 1024)
+D27 = tv.ModelCfg(64, 5120, 40, 8, 128, 17408, 151936)
+
+
+def declared_functions():
+    names = set()
+    for h in HEADERS:
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\**\s*(spec_[a-z_]+)\s*\(",
+                             text, flags=re.M):
+            names.add(m.group(1))
+    return names
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert {"spec_verify", "spec_commit_kv", "spec_accept", "spec_workspace_bytes",
+            "spec_accept_workspace_bytes", "spec_strerror"} <= names
+    L = ctypes.CDLL(tv.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(tv.EXPORTED) == names
+
+
+def test_strerror_codes():
+    assert tv.spec_strerror(tv.SPEC_OK) == "ok"
+    for c in (tv.SPEC_EINVAL, tv.SPEC_EUNSUPPORTED, tv.SPEC_EWORKSPACE, tv.SPEC_EHIP):
+        assert tv.spec_strerror(c) not in ("ok", "unknown error")
+    assert tv.spec_strerror(12345) == "unknown error"
+
+
+def test_workspace_sizes_grow_with_batch_and_context():
+    a = tv.spec_workspace_bytes(D27, 1, 16, 257)
+    b = tv.spec_workspace_bytes(D27, 32, 16, 514)
+    c = tv.spec_workspace_bytes(D27, 1, 64, 517)
+    assert 0 < a < b and a < c
+    assert a % 256 == 0
+    assert tv.spec_workspace_bytes(TINY, 1, 8, 9) > 0
+
+
+@pytest.mark.parametrize("cfg,code", [
+    (tv.ModelCfg(2, 256, 4, 2, 96, 704, 1024), tv.SPEC_EUNSUPPORTED),     # head_dim 96
+    (tv.ModelCfg(2, 256, 4, 3, 64, 704, 1024), tv.SPEC_EUNSUPPORTED),     # 4 q heads, 3 kv heads
+    (tv.ModelCfg(2, 250, 4, 2, 64, 704, 1024), tv.SPEC_EUNSUPPORTED),     # hidden % 32
+    (tv.ModelCfg(2, 256, 4, 2, 64, 700, 1024), tv.SPEC_EUNSUPPORTED),     # ffn % 32
+    (tv.ModelCfg(2, 256, 4, 2, 64, 704, 1000), tv.SPEC_EUNSUPPORTED),     # vocab % 16
+    (tv.ModelCfg(0, 256, 4, 2, 64, 704, 1024), tv.SPEC_EINVAL),
+    (tv.ModelCfg(2, 256, 4, 2, 64, 704, 1024, rope_theta=-1.0), tv.SPEC_EINVAL),
+])
+def test_workspace_rejects_bad_shapes(cfg, code):
+    with pytest.raises(tv.SpecError) as e:
+        tv.spec_workspace_bytes(cfg, 1, 8, 9)
+    assert e.value.code == code
+
+
+def test_workspace_rejects_bad_sizes():
+    for batch, k, pages, code in [(0, 8, 9, tv.SPEC_EINVAL), (1, 0, 9, tv.SPEC_EINVAL),
+                                  (1, 65, 9, tv.SPEC_EUNSUPPORTED), (1, 8, 0, tv.SPEC_EINVAL)]:
+        with pytest.raises(tv.SpecError) as e:
+            tv.spec_workspace_bytes(TINY, batch, k, pages)
+        assert e.value.code == code
+
+
+def _raw_verify(weights_c, kv_c, ptrs, batch, k, ws_ptr, ws_bytes):
+    L = tv.lib()
+    extras = tv.ExtrasC(None, None, None)
+    return L.spec_verify(ctypes.byref(weights_c) if weights_c is not None else None,
+                         ctypes.byref(kv_c) if kv_c is not None else None,
+                         ptrs["tok"], ptrs["par"], ptrs["ctx"], batch, k, ptrs["a"], ptrs["b"],
+                         ptrs["p"], ctypes.byref(extras), ws_ptr, ws_bytes, None)
+
+
+def _fake_structs(cfg, n_layers_ptrs=True):
+    fake = 0x10000   # never dereferenced on the host; calls below fail validation first
+    layers = (tv.LayerWeightsC * cfg.n_layers)(
+        *[tv.LayerWeightsC(*([fake] * 6 if n_layers_ptrs else [fake] * 5 + [None]))
+          for _ in range(cfg.n_layers)])
+    w = tv.WeightsC(cfg.c(), ctypes.cast(layers, ctypes.POINTER(tv.LayerWeightsC)), fake, fake, fake)
+    kv = tv.KVCacheC(fake, fake, fake, 16, 9)
+    return w, kv, layers
+
+
+def test_verify_rejects_host_visible_errors_without_launching():
+    w, kv, keep = _fake_structs(TINY)
+    fake = 0x10000
+    ptrs = dict(tok=fake, par=None, ctx=fake, a=fake, b=fake, p=fake)
+    need = tv.spec_workspace_bytes(TINY, 1, 8, 9)
+    assert _raw_verify(None, kv, ptrs, 1, 8, 0x100000, need) == tv.SPEC_EINVAL
+    assert _raw_verify(w, None, ptrs, 1, 8, 0x100000, need) == tv.SPEC_EINVAL
+    for key in ("tok", "ctx", "a", "b", "p"):
+        bad = dict(ptrs, **{key: None})
+        assert _raw_verify(w, kv, bad, 1, 8, 0x100000, need) == tv.SPEC_EINVAL
+    assert _raw_verify(w, kv, ptrs, 1, 8, None, need) == tv.SPEC_EINVAL
+    assert _raw_verify(w, kv, ptrs, 1, 8, 0x100000, need - 1) == tv.SPEC_EWORKSPACE
+    assert _raw_verify(w, kv, ptrs, 1, 8, 0x100010, need) == tv.SPEC_EINVAL          # unaligned
+    assert _raw_verify(w, kv, ptrs, 1, 65, 0x100000, 1 << 40) == tv.SPEC_EUNSUPPORTED
+    assert _raw_verify(w, kv, ptrs, 0, 8, 0x100000, need) == tv.SPEC_EINVAL
+    w2, kv2, keep2 = _fake_structs(TINY, n_layers_ptrs=False)
+    assert _raw_verify(w2, kv2, ptrs, 1, 8, 0x100000, need) == tv.SPEC_EINVAL       # NULL weight
+    kv_bad = tv.KVCacheC(fake, fake, fake, 0, 9)
+    assert _raw_verify(w, kv_bad, ptrs, 1, 8, 0x100000, need) == tv.SPEC_EINVAL
+
+
+def test_commit_and_accept_reject_bad_arguments():
+    L = tv.lib()
+    fake = 0x10000
+    cfg = TINY.c()
+    kv = tv.KVCacheC(fake, fake, fake, 16, 9)
+    assert L.spec_commit_kv(ctypes.byref(cfg), ctypes.byref(kv), None, fake, fake, 1, 8, None) == tv.SPEC_EINVAL
+    assert L.spec_commit_kv(ctypes.byref(cfg), ctypes.byref(kv), fake, fake, fake, 1, 65, None) == tv.SPEC_EUNSUPPORTED
+    assert L.spec_commit_kv(None, ctypes.byref(kv), fake, fake, fake, 1, 8, None) == tv.SPEC_EINVAL
+    need = tv.spec_accept_workspace_bytes(2, 16, 151936)
+    assert need > 0
+    args = [fake, fake, None, 2, 16, 151936, fake, fake, fake, None]
+    assert L.spec_accept(*args, 0x100000, need - 1, None) == tv.SPEC_EWORKSPACE
+    assert L.spec_accept(None, *args[1:], 0x100000, need, None) == tv.SPEC_EINVAL
+    args_k = list(args)
+    args_k[4] = 65
+    assert L.spec_accept(*args_k, 0x100000, 1 << 30, None) == tv.SPEC_EUNSUPPORTED

@@ -1,0 +1,88 @@
+"""The full 27B-class stack (64 layers + output head over 151936 tokens, ~45 GB of bf16
+weights drawn on the GPU) at the launch configuration bench.py times, checked layer by layer
+with teacher forcing: the oracle (and an exact float64 evaluation) take the GPU's own residual
+stream entering a sampled layer, and their outputs are compared with the GPU's output of that
+layer; the output head and the greedy walk are checked from the GPU's final residual stream.
+Teacher forcing separates kernel errors from the growth of legitimate rounding differences over
+64 layers of a random-weight model."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import ref64
+import synth
+import tree_verification_skinny_amd as tv
+from tree_verification_skinny_amd import kvlayout
+
+from helpers import bits, check_accept, check_as_exact, check_logits, oracle_cfg, run_verify
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+SEED = 27
+
+
+@pytest.fixture(scope="module")
+def stack():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    shape = synth.DENSE_27B
+    layers = [synth.layer_weights(shape, SEED, l, DEV) for l in range(shape.n_layers)]
+    embed = synth.randn_bf16((shape.vocab, shape.hidden), 0.02, DEV, SEED, "embed")
+    lm = synth.randn_bf16((shape.vocab, shape.hidden), 0.02, DEV, SEED, "lm_head")
+    fn = torch.ones(shape.hidden, dtype=torch.bfloat16, device=DEV)
+    w = tv.Weights(tv.ModelCfg.of(shape), embed, fn, lm, layers)
+    yield shape, w
+    del w, layers, embed, lm
+    torch.cuda.empty_cache()
+
+
+def _case(shape, w, kind):
+    if kind == "block":
+        k, ctx = 16, 4096
+        parent = oracle.chain(k)
+        tokens = synth.uniform_tokens(k, shape.vocab, SEED, "blk")
+    else:
+        k, ctx = 64, 8192
+        parent = synth.random_tree(k, 10, SEED, "tree")
+        tokens = synth.tree_tokens(parent, shape.vocab, SEED, "tree")
+    pages = (ctx + k + 15) // 16
+    table = torch.arange(pages, dtype=torch.int32).view(1, pages)
+    kv = tv.PagedKV.empty(w.cfg, pages, table, DEV)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(SEED)
+    kv.k_pool.normal_(generator=g)
+    kv.v_pool.normal_(generator=g)
+    ctx_rows = [kvlayout.read_rows(kv, l, 0, torch.arange(ctx)) for l in range(shape.n_layers)]
+    out = run_verify(w, kv, tokens[None], None if kind == "block" else parent[None], [ctx],
+                     want_hidden=True)
+    return k, ctx, parent, tokens, kv, ctx_rows, out
+
+
+@pytest.mark.parametrize("kind", ["block", "tree"])
+def test_27b_stack_teacher_forced(stack, kind):
+    shape, w = stack
+    k, ctx, parent, tokens, kv, ctx_rows, out = _case(shape, w, kind)
+    cfg = oracle_cfg(shape)
+    for l in (0, 1, 31, 62, 63):
+        lw = {nm: bits(t) for nm, t in w.tensors["layers"][l].items()}
+        kc, vc = bits(ctx_rows[l][0]), bits(ctx_rows[l][1])
+        x_in = bits(out.hidden[l])
+        x_o, k_o, v_o = oracle.layer_forward(cfg, lw, kc, vc, parent, x_in)
+        x_r, _, _ = ref64.layer(shape, lw, kc, vc, parent, x_in)
+        kg, vg = kvlayout.read_rows(kv, l, 0, torch.arange(ctx, ctx + k))
+        check_logits(kg.float().cpu().numpy(), oracle.from_bf16(k_o), f"layer {l} k_new")
+        check_logits(vg.float().cpu().numpy(), oracle.from_bf16(v_o), f"layer {l} v_new")
+        print(check_as_exact(out.hidden[l + 1].float().cpu().numpy(), oracle.from_bf16(x_o),
+                             x_r.numpy(), f"layer {l} output"))
+    # output head and greedy walk from the GPU's final residual stream: fixed tolerance
+    model = oracle.Model(cfg, bits(w.tensors["embed"][:1]), bits(w.tensors["final_norm"]),
+                         bits(w.tensors["lm_head"]), layers=[])
+    lg = oracle.logits(model, bits(out.hidden[shape.n_layers]))
+    err = check_logits(out.logits[0], lg, "output head")
+    arg, margin = oracle.argmax(lg)
+    a, b, p = oracle.accept(tokens, parent, arg)
+    r = oracle.VerifyResult(lg, arg, margin, a, b, p, [], [], [])
+    near = check_accept(r, tokens, parent, out.greedy[0], int(out.accepted_len[0]),
+                        int(out.bonus[0]), out.path[0])
+    print(f"{kind}: head max err {err:.2e}, accepted {out.accepted_len[0]}, near-tie {near}")

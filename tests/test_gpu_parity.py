@@ -1,0 +1,327 @@
+"""Parity of the HIP verify path (called through the C ABI) with the CPU oracle, on the tiny
+decoder and on one layer of the 27B-class shape; acceptance on planted logits; edge cases;
+commit; determinism."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import tree_verification_skinny_amd as tv
+from tree_verification_skinny_amd import kvlayout
+
+import ref64
+from helpers import (bits, check_accept, check_as_exact, check_logits, device_weights, from_bits,
+                     make_kv, oracle_model_from, run_verify, tiny_case, upload_context)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def setup_module(module):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    tv.lib()
+
+
+# ------------------------------------------------------------------------------------------
+# acceptance on planted logits (spec_accept)
+# ------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("batch,k,kind,vocab", [(1, 16, "chain", 151936), (32, 16, "chain", 151936),
+                                                 (1, 64, "tree", 151936), (4, 1, "chain", 1024),
+                                                 (3, 64, "chain", 2048), (5, 12, "tree", 1000)])
+def test_accept_planted_logits(batch, k, kind, vocab):
+    toks, pars, lgs, gs = [], [], [], []
+    for b in range(batch):
+        seed = (batch, k, kind, b)
+        if kind == "chain":
+            par = oracle.chain(k)
+            tok = synth.uniform_tokens(k, vocab, seed, "acc")
+        else:
+            par = synth.random_tree(k, 10, seed)
+            tok = synth.tree_tokens(par, vocab, seed)
+        g = synth.geometric(0.25, seed)
+        lg, _ = synth.planted_logits(tok, par, vocab, g, seed)
+        if b % 4 == 3 and k > 2:                       # plant exact ties: lowest index must win
+            lg[1, 5] = lg[1, 900 % vocab] = lg[1].max() + 2.0
+        toks.append(tok); pars.append(par); lgs.append(lg); gs.append(g)
+    tokens = np.stack(toks).astype(np.int32)
+    parent = np.stack(pars).astype(np.int32)
+    logits = torch.from_numpy(np.stack(lgs).reshape(batch * k, vocab)).to(DEV)
+    ws = tv.workspace(tv.spec_accept_workspace_bytes(batch, k, vocab), DEV)
+    acc = torch.empty(batch, dtype=torch.int32, device=DEV)
+    bon = torch.empty(batch, dtype=torch.int32, device=DEV)
+    path = torch.empty((batch, k), dtype=torch.int32, device=DEV)
+    greedy = torch.empty(batch * k, dtype=torch.int32, device=DEV)
+    tv.spec_accept(logits, torch.from_numpy(tokens).to(DEV),
+                   None if kind == "chain" else torch.from_numpy(parent).to(DEV), batch, k, vocab,
+                   acc, bon, path, ws, greedy=greedy)
+    torch.cuda.synchronize()
+    acc, bon, path, greedy = (x.cpu().numpy() for x in (acc, bon, path, greedy))
+    for b in range(batch):
+        arg, _ = oracle.argmax(lgs[b])
+        assert np.array_equal(greedy[b * k:(b + 1) * k], arg)
+        a, bo, p = oracle.accept(tokens[b], parent[b], arg)
+        assert (acc[b], bon[b]) == (a, bo) and np.array_equal(path[b], p)
+        if kind == "chain" and not (b % 4 == 3 and k > 2):     # (a planted tie moves row 1)
+            assert a == min(gs[b], k - 1)
+
+
+def test_accept_marks_bad_requests_only():
+    k, vocab = 8, 1024
+    tokens = np.stack([synth.uniform_tokens(k, vocab, i, "bad") for i in range(4)]).astype(np.int32)
+    parent = np.stack([oracle.chain(k)] * 4).astype(np.int32)
+    tokens[1, 3] = vocab            # out of range
+    parent[2, 4] = 4                # not an earlier node
+    parent[3, 0] = 0                # root without -1
+    lg = np.random.default_rng(0).standard_normal((4 * k, vocab)).astype(np.float32)
+    ws = tv.workspace(tv.spec_accept_workspace_bytes(4, k, vocab), DEV)
+    acc = torch.empty(4, dtype=torch.int32, device=DEV)
+    bon = torch.empty(4, dtype=torch.int32, device=DEV)
+    path = torch.empty((4, k), dtype=torch.int32, device=DEV)
+    tv.spec_accept(torch.from_numpy(lg).to(DEV), torch.from_numpy(tokens).to(DEV),
+                   torch.from_numpy(parent).to(DEV), 4, k, vocab, acc, bon, path, ws)
+    torch.cuda.synchronize()
+    acc, bon, path = acc.cpu().numpy(), bon.cpu().numpy(), path.cpu().numpy()
+    arg, _ = oracle.argmax(lg[:k])
+    a, b, p = oracle.accept(tokens[0], parent[0], arg)
+    assert (acc[0], bon[0]) == (a, b) and np.array_equal(path[0], p)
+    for r in (1, 2, 3):
+        assert acc[r] == -1 and bon[r] == -1 and np.all(path[r] == -1)
+
+
+# ------------------------------------------------------------------------------------------
+# tiny decoder: block of 8, oracle-prefilled prompt of 128, one replaced token
+# ------------------------------------------------------------------------------------------
+
+N_TINY_SEEDS = 40
+
+
+def test_tiny_block_parity_many_seeds():
+    near_ties, accepted = 0, []
+    for seed in range(N_TINY_SEEDS):
+        w, m, kc, vc, tokens, G = tiny_case(seed)
+        k = tokens.size
+        r = oracle.verify(m, kc, vc, tokens)
+        weights = device_weights(synth.TINY, w, DEV)
+        kv = make_kv(synth.TINY, [128], k, seed, DEV)
+        upload_context(kv, 0, kc, vc)
+        out = run_verify(weights, kv, tokens[None], None, [128])
+        check_logits(out.logits[0], r.logits, f"seed {seed} logits")
+        near = check_accept(r, tokens, None, out.greedy[0], int(out.accepted_len[0]),
+                            int(out.bonus[0]), out.path[0])
+        near_ties += near
+        if not near:
+            assert out.accepted_len[0] == min(G, k - 1)
+        accepted.append(int(out.accepted_len[0]))
+        # the pass wrote every node's K/V at slots 128..135, as the oracle computed them
+        for l in range(2):
+            kg, vg = kvlayout.read_rows(kv, l, 0, torch.arange(128, 128 + k))
+            check_logits(kg.float().cpu().numpy(), oracle.from_bf16(r.k_new[l]), f"k_new l{l}")
+            check_logits(vg.float().cpu().numpy(), oracle.from_bf16(r.v_new[l]), f"v_new l{l}")
+    print(f"tiny block: {near_ties} near-ties of {N_TINY_SEEDS}; mean accepted {np.mean(accepted):.2f}")
+    assert near_ties <= N_TINY_SEEDS // 4
+
+
+def test_tiny_commit_matches_ar_cache():
+    w, m, kc, vc, tokens, G = tiny_case(1234)
+    k = tokens.size
+    weights = device_weights(synth.TINY, w, DEV)
+    kv = make_kv(synth.TINY, [128], k, 5, DEV)
+    upload_context(kv, 0, kc, vc)
+    out = run_verify(weights, kv, tokens[None], None, [128])
+    r = oracle.verify(m, kc, vc, tokens)
+    a = int(out.accepted_len[0])
+    before = [kvlayout.read_rows(kv, l, 0, torch.arange(128, 128 + k)) for l in range(2)]
+    tv.spec_commit_kv(weights.cfg, kv, out.acc_t, out.path_t, out.ctx, 1, k)
+    torch.cuda.synchronize()
+    assert int(out.ctx.cpu()[0]) == 128 + a + 1
+    for l in range(2):
+        after = kvlayout.read_rows(kv, l, 0, torch.arange(128, 128 + a + 1))
+        sel = torch.from_numpy(out.path[0][: a + 1]).long().to(DEV)
+        assert torch.equal(after[0], before[l][0][sel]) and torch.equal(after[1], before[l][1][sel])
+        # and the committed cache is the one AR decoding builds, within tolerance
+        kc2, vc2 = oracle.commit(kc, vc, r)
+        check_logits(after[0].float().cpu().numpy(), oracle.from_bf16(kc2[l][128:]), "committed k")
+        check_logits(after[1].float().cpu().numpy(), oracle.from_bf16(vc2[l][128:]), "committed v")
+        ctx_rows = kvlayout.read_rows(kv, l, 0, torch.arange(0, 128))
+        assert np.array_equal(bits(ctx_rows[0]), kc[l])          # context untouched
+
+
+# ------------------------------------------------------------------------------------------
+# tiny decoder: trees with greedy-planted paths, and a ragged paged batch
+# ------------------------------------------------------------------------------------------
+
+def planted_tree(m, kc, vc, k, seed, p_follow=0.7):
+    """A k-node tree (depth <= 10) whose tokens follow the oracle's greedy choice with
+    probability p_follow, level by level (BFS ids make every level a prefix)."""
+    parent = synth.random_tree(k, 10, seed, "pt")
+    depth = oracle.tree_depth(parent)
+    rng = np.random.default_rng(synth.seed_of(seed, "pt"))
+    tokens = synth.tree_tokens(parent, m.cfg.vocab, seed, "pt")
+    tokens[0] = int(rng.integers(0, m.cfg.vocab))
+    for d in range(1, depth.max() + 1):
+        n_prev = int(np.sum(depth < d))
+        r = oracle.verify(m, kc, vc, tokens[:n_prev], parent[:n_prev])
+        level = np.nonzero(depth == d)[0]
+        used = {}
+        for i in level:
+            pa = int(parent[i])
+            want = int(r.arg[pa])
+            s = used.setdefault(pa, set())
+            if rng.random() < p_follow and want not in s:
+                tokens[i] = want
+            else:
+                t = int(rng.integers(0, m.cfg.vocab))
+                while t in s or t == want:
+                    t = (t + 1) % m.cfg.vocab
+                tokens[i] = t
+            s.add(int(tokens[i]))
+    return tokens, parent
+
+
+@pytest.mark.parametrize("k", [64, 13, 2])
+def test_tiny_tree_parity(k):
+    near, oracle_accepted = 0, 0
+    for seed in range(6):
+        w = synth.model_weights(synth.TINY, 700 + seed)
+        m = oracle_model_from(synth.TINY, w)
+        ctx = 64 + 37 * seed
+        kc = [np.ascontiguousarray(bits(x)) for x, _ in
+              [synth.kv_context(synth.TINY, ctx, seed, l) for l in range(2)]]
+        vc = [np.ascontiguousarray(bits(y)) for _, y in
+              [synth.kv_context(synth.TINY, ctx, seed, l) for l in range(2)]]
+        tokens, parent = planted_tree(m, kc, vc, k, seed)
+        r = oracle.verify(m, kc, vc, tokens, parent)
+        weights = device_weights(synth.TINY, w, DEV)
+        kv = make_kv(synth.TINY, [ctx], k, seed, DEV)
+        upload_context(kv, 0, kc, vc)
+        out = run_verify(weights, kv, tokens[None], parent[None], [ctx])
+        check_logits(out.logits[0], r.logits)
+        near += check_accept(r, tokens, parent, out.greedy[0], int(out.accepted_len[0]),
+                             int(out.bonus[0]), out.path[0])
+        oracle_accepted += r.accepted_len
+    assert near <= 2
+    if k > 2:
+        assert oracle_accepted > 0        # the planted trees do exercise acceptance
+
+
+def test_tiny_ragged_batch_with_shuffled_pages():
+    B, k = 7, 8
+    w = synth.model_weights(synth.TINY, 99)
+    m = oracle_model_from(synth.TINY, w)
+    ctxs = [0, 1, 15, 16, 17, 130, 301]
+    weights = device_weights(synth.TINY, w, DEV)
+    kv = make_kv(synth.TINY, ctxs, k, 99, DEV, extra_pages=1)
+    toks, cases = [], []
+    for b, ctx in enumerate(ctxs):
+        kvs = [synth.kv_context(synth.TINY, ctx, 99, l, request=b) for l in range(2)]
+        kc = [bits(x) for x, _ in kvs]
+        vc = [bits(y) for _, y in kvs]
+        upload_context(kv, b, kc, vc)
+        tok = synth.uniform_tokens(k, 1024, 99, b)
+        if b % 2 == 0:                       # make some drafts follow the target greedily
+            r0 = oracle.verify(m, kc, vc, tok[:1])
+            cont, _, _, _ = oracle.ar_greedy(m, kc, vc, int(tok[0]), k - 1)
+            tok[1:] = cont
+            tok[1 + b // 2] = (tok[1 + b // 2] + 1) % 1024
+        toks.append(tok)
+        cases.append((kc, vc))
+    tokens = np.stack(toks).astype(np.int32)
+    out = run_verify(weights, kv, tokens, None, ctxs)
+    for b in range(B):
+        kc, vc = cases[b]
+        r = oracle.verify(m, kc, vc, tokens[b])
+        check_logits(out.logits[b], r.logits, f"request {b}")
+        check_accept(r, tokens[b], None, out.greedy[b], int(out.accepted_len[b]),
+                     int(out.bonus[b]), out.path[b])
+
+
+def test_bad_requests_are_isolated():
+    B, k = 4, 8
+    w = synth.model_weights(synth.TINY, 5)
+    m = oracle_model_from(synth.TINY, w)
+    weights = device_weights(synth.TINY, w, DEV)
+    ctxs = [20, 20, 20, 20]
+    kv = make_kv(synth.TINY, ctxs, k, 5, DEV)
+    kvs = [synth.kv_context(synth.TINY, 20, 5, l) for l in range(2)]
+    kc = [bits(x) for x, _ in kvs]
+    vc = [bits(y) for _, y in kvs]
+    for b in range(B):
+        upload_context(kv, b, kc, vc)
+    tokens = np.stack([synth.uniform_tokens(k, 1024, 5, b) for b in range(B)]).astype(np.int32)
+    parent = np.stack([oracle.chain(k)] * B).astype(np.int32)
+    tokens[1, 2] = -3                      # bad token
+    parent[2, 5] = 6                       # bad tree
+    ctx_bad = list(ctxs)
+    ctx_bad[3] = 10_000                    # context beyond the request's pages
+    before = kvlayout.read_rows(kv, 0, 1, torch.arange(20, 28))
+    out = run_verify(weights, kv, tokens, parent, ctx_bad)
+    r = oracle.verify(m, kc, vc, tokens[0], parent[0])
+    check_logits(out.logits[0], r.logits)
+    check_accept(r, tokens[0], parent[0], out.greedy[0], int(out.accepted_len[0]),
+                 int(out.bonus[0]), out.path[0])
+    for b in (1, 2, 3):
+        assert out.accepted_len[b] == -1 and out.bonus[b] == -1 and np.all(out.path[b] == -1)
+    after = kvlayout.read_rows(kv, 0, 1, torch.arange(20, 28))
+    assert torch.equal(before[0], after[0]) and torch.equal(before[1], after[1])
+
+
+def test_root_only_and_empty_context():
+    w = synth.model_weights(synth.TINY, 8)
+    m = oracle_model_from(synth.TINY, w)
+    weights = device_weights(synth.TINY, w, DEV)
+    empty = [np.zeros((0, 2, 64), np.uint16)] * 2
+    for k in (1, 3):
+        tokens = synth.uniform_tokens(k, 1024, 8, k)
+        kv = make_kv(synth.TINY, [0], k, 8, DEV)
+        out = run_verify(weights, kv, tokens[None], None, [0])
+        r = oracle.verify(m, empty, empty, tokens)
+        check_logits(out.logits[0], r.logits)
+        check_accept(r, tokens, None, out.greedy[0], int(out.accepted_len[0]), int(out.bonus[0]),
+                     out.path[0])
+
+
+def test_repeat_runs_are_bit_identical():
+    w, m, kc, vc, tokens, G = tiny_case(77)
+    weights = device_weights(synth.TINY, w, DEV)
+    outs = []
+    for _ in range(2):
+        kv = make_kv(synth.TINY, [128], 8, 77, DEV)
+        upload_context(kv, 0, kc, vc)
+        outs.append(run_verify(weights, kv, tokens[None], None, [128]))
+    assert np.array_equal(outs[0].logits, outs[1].logits)
+    assert np.array_equal(outs[0].path, outs[1].path)
+
+
+# ------------------------------------------------------------------------------------------
+# one decoder layer at the 27B-class shape, context 4096, block of 16
+# ------------------------------------------------------------------------------------------
+
+def test_27b_single_layer_parity():
+    shape = synth.DENSE_27B.with_layers(1).with_vocab(8192)
+    seed, ctx, k = 2024, 4096, 16
+    w = synth.model_weights(shape, seed)
+    m = oracle_model_from(shape, w)
+    kx, vx = synth.kv_context(shape, ctx, seed, 0)
+    kc, vc = [bits(kx)], [bits(vx)]
+    tokens = synth.uniform_tokens(k, shape.vocab, seed, "tok")
+    r = oracle.verify(m, kc, vc, tokens, keep_hidden=True)
+    ref_logits, ref_hidden = ref64.decoder(w, shape, tokens, oracle.chain(k), kc, vc)
+    weights = device_weights(shape, w, DEV)
+    kv = make_kv(shape, [ctx], k, seed, DEV)
+    upload_context(kv, 0, kc, vc)
+    out = run_verify(weights, kv, tokens[None], None, [ctx], want_hidden=True)
+    # the draft rows' keys and values (QKV projection + RoPE) meet the fixed tolerance
+    kg, vg = kvlayout.read_rows(kv, 0, 0, torch.arange(ctx, ctx + k))
+    check_logits(kg.float().cpu().numpy(), oracle.from_bf16(r.k_new[0]), "k_new")
+    check_logits(vg.float().cpu().numpy(), oracle.from_bf16(r.v_new[0]), "v_new")
+    assert np.mean(bits(kg) == r.k_new[0]) > 0.98
+    # layer output and logits: as close to the oracle as an exact evaluation
+    print(check_as_exact(out.hidden[1].float().cpu().numpy(), oracle.from_bf16(r.hidden[1]),
+                         ref_hidden[1].numpy(), "layer output"))
+    print(check_as_exact(out.logits[0], r.logits, ref_logits, "logits"))
+    spread = float(np.abs(ref_logits - r.logits).max())
+    check_accept(r, tokens, None, out.greedy[0], int(out.accepted_len[0]), int(out.bonus[0]),
+                 out.path[0], near_tie=max(1e-2, 2 * spread))

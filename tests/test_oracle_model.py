@@ -12,9 +12,9 @@
 import numpy as np
 import pytest
 import torch
-import torch.nn.functional as F
 
 import oracle
+import ref64
 import synth
 
 
@@ -40,64 +40,11 @@ def tiny():
 
 
 # ------------------------------------------------------------------------------------------
-# independent float64 decoder
+# independent float64 decoder (tests/ref64.py)
 # ------------------------------------------------------------------------------------------
 
-def rb(t):
-    """Round to bf16 (through fp32) and return float64."""
-    return t.float().to(torch.bfloat16).double()
-
-
 def ref_decoder(w, shape, tokens, parent, k_ctx, v_ctx):
-    """Pre-norm decoder in float64 torch ops, rounding to bf16 where tensors are stored."""
-    H, nq, nkv, d, Fd = shape.hidden, shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.ffn
-    eps = shape.rms_eps
-    m = len(tokens)
-    ctx = k_ctx[0].shape[0]
-    depth = [0] * m
-    vis = torch.zeros(m, ctx + m, dtype=torch.bool)
-    vis[:, :ctx] = True
-    for i in range(m):
-        if i:
-            depth[i] = depth[parent[i]] + 1
-        j = i
-        while j >= 0:
-            vis[i, ctx + j] = True
-            j = int(parent[j])
-    pos = torch.tensor([ctx + dd for dd in depth], dtype=torch.float64)
-    inv = shape.rope_theta ** (-torch.arange(0, d, 2, dtype=torch.float64) / d)
-    ang = pos[:, None] * inv[None, :]
-    cos = torch.cat([ang.cos(), ang.cos()], -1)[:, None, :].float().double()
-    sin = torch.cat([ang.sin(), ang.sin()], -1)[:, None, :].float().double()
-
-    def norm(x, g):
-        return rb(x / torch.sqrt((x * x).mean(-1, keepdim=True) + eps) * g)
-
-    def rot(t):
-        t1, t2 = t[..., : d // 2], t[..., d // 2:]
-        return rb(t * cos + torch.cat([-t2, t1], -1) * sin)
-
-    x = w["embed"].double()[torch.tensor(tokens, dtype=torch.long)]
-    for l, lw in enumerate(w["layers"]):
-        lw = {k: v.double() for k, v in lw.items()}
-        u = norm(x, lw["attn_norm"])
-        qkv = u @ lw["w_qkv"].T
-        q = rot(rb(qkv[:, : nq * d]).view(m, nq, d))
-        k = rot(rb(qkv[:, nq * d: (nq + nkv) * d]).view(m, nkv, d))
-        v = rb(qkv[:, (nq + nkv) * d:]).view(m, nkv, d)
-        K = torch.cat([torch.tensor(oracle.from_bf16(k_ctx[l])).double(), k], 0)
-        V = torch.cat([torch.tensor(oracle.from_bf16(v_ctx[l])).double(), v], 0)
-        K = K.permute(1, 0, 2).repeat_interleave(nq // nkv, 0)
-        V = V.permute(1, 0, 2).repeat_interleave(nq // nkv, 0)
-        o = F.scaled_dot_product_attention(q.permute(1, 0, 2), K, V, attn_mask=vis)
-        o = rb(o.permute(1, 0, 2).reshape(m, nq * d))
-        x = rb(x + rb(o @ lw["w_o"].T))
-        u = norm(x, lw["mlp_norm"])
-        gu = u @ lw["w_gate_up"].T
-        h = rb(F.silu(rb(gu[:, :Fd])) * rb(gu[:, Fd:]))
-        x = rb(x + rb(h @ lw["w_down"].T))
-    u = norm(x, w["final_norm"].double())
-    return (u @ w["lm_head"].double().T).numpy()
+    return ref64.decoder(w, shape, tokens, parent, k_ctx, v_ctx)[0]
 
 
 @pytest.mark.parametrize("kind", ["chain", "tree"])

@@ -1,0 +1,254 @@
+"""Python binding of libspecverify, the MI355X (gfx950) verification step of lossless greedy
+speculative decoding.
+
+Argument marshalling only: every step of the pass runs in the library's HIP kernels, called
+through its C ABI (``include/specverify.h``) with ``ctypes``. PyTorch supplies device memory
+and the current HIP stream. There is no fallback: if the built library is missing, importing
+the entry points raises.
+
+Entry points (same names as the C ABI): ``spec_workspace_bytes``, ``spec_verify``,
+``spec_commit_kv``, ``spec_accept_workspace_bytes``, ``spec_accept``,
+``spec_skinny_gemm_bytes``, ``spec_skinny_gemm``, ``spec_strerror``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libspecverify.so")
+
+SPEC_OK = 0
+SPEC_EINVAL = -1
+SPEC_EUNSUPPORTED = -2
+SPEC_EWORKSPACE = -3
+SPEC_EHIP = -4
+PAGE_SIZE = 16
+MAX_K = 64
+LAYER_KEYS = ("attn_norm", "w_qkv", "w_o", "mlp_norm", "w_gate_up", "w_down")
+
+
+class SpecError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        super().__init__(f"{where}: {spec_strerror(code)} ({code})")
+        self.code = code
+
+
+class ModelCfgC(ctypes.Structure):
+    _fields_ = [("n_layers", ctypes.c_int), ("hidden", ctypes.c_int), ("n_q_heads", ctypes.c_int),
+                ("n_kv_heads", ctypes.c_int), ("head_dim", ctypes.c_int), ("ffn", ctypes.c_int),
+                ("vocab", ctypes.c_int), ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_double)]
+
+
+class LayerWeightsC(ctypes.Structure):
+    _fields_ = [(k, ctypes.c_void_p) for k in LAYER_KEYS]
+
+
+class WeightsC(ctypes.Structure):
+    _fields_ = [("cfg", ModelCfgC), ("layers", ctypes.POINTER(LayerWeightsC)),
+                ("embed", ctypes.c_void_p), ("final_norm", ctypes.c_void_p),
+                ("lm_head", ctypes.c_void_p)]
+
+
+class KVCacheC(ctypes.Structure):
+    _fields_ = [("k_pool", ctypes.c_void_p), ("v_pool", ctypes.c_void_p),
+                ("block_table", ctypes.c_void_p), ("n_pages", ctypes.c_int),
+                ("max_pages_per_req", ctypes.c_int)]
+
+
+class ExtrasC(ctypes.Structure):
+    _fields_ = [("logits", ctypes.c_void_p), ("greedy", ctypes.c_void_p), ("hidden", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the built library (fails loudly when it is absent)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() or "
+                              "python tree_verification_skinny_amd/build.py")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        L.spec_strerror.argtypes = [i32]
+        L.spec_strerror.restype = ctypes.c_char_p
+        L.spec_workspace_bytes.argtypes = [ctypes.POINTER(ModelCfgC), i32, i32, i32, ctypes.POINTER(sz)]
+        L.spec_verify.argtypes = [ctypes.POINTER(WeightsC), ctypes.POINTER(KVCacheC), vp, vp, vp, i32, i32,
+                                  vp, vp, vp, ctypes.POINTER(ExtrasC), vp, sz, vp]
+        L.spec_commit_kv.argtypes = [ctypes.POINTER(ModelCfgC), ctypes.POINTER(KVCacheC), vp, vp, vp,
+                                     i32, i32, vp]
+        L.spec_accept_workspace_bytes.argtypes = [i32, i32, i32, ctypes.POINTER(sz)]
+        L.spec_accept.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
+        L.spec_skinny_gemm_bytes.argtypes = [i32, i32, i32, ctypes.POINTER(sz)]
+        L.spec_skinny_gemm.argtypes = [vp, i32, i32, vp, i32, vp, sz, ctypes.POINTER(i32), vp]
+        for f in (L.spec_workspace_bytes, L.spec_verify, L.spec_commit_kv,
+                  L.spec_accept_workspace_bytes, L.spec_accept, L.spec_skinny_gemm_bytes,
+                  L.spec_skinny_gemm):
+            f.restype = i32
+        _lib = L
+    return _lib
+
+
+EXPORTED = ("spec_workspace_bytes", "spec_verify", "spec_commit_kv", "spec_accept_workspace_bytes",
+            "spec_accept", "spec_skinny_gemm_bytes", "spec_skinny_gemm", "spec_strerror")
+
+
+def spec_strerror(code: int) -> str:
+    return lib().spec_strerror(int(code)).decode()
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libspecverify must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(rc: int, where: str):
+    if rc != SPEC_OK:
+        raise SpecError(rc, where)
+
+
+@dataclass(frozen=True)
+class ModelCfg:
+    n_layers: int
+    hidden: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    ffn: int
+    vocab: int
+    rms_eps: float = 1e-6
+    rope_theta: float = 1e4
+
+    def c(self) -> ModelCfgC:
+        return ModelCfgC(self.n_layers, self.hidden, self.n_q_heads, self.n_kv_heads, self.head_dim,
+                         self.ffn, self.vocab, self.rms_eps, self.rope_theta)
+
+    @staticmethod
+    def of(shape) -> "ModelCfg":
+        return ModelCfg(shape.n_layers, shape.hidden, shape.n_q_heads, shape.n_kv_heads,
+                        shape.head_dim, shape.ffn, shape.vocab, shape.rms_eps, shape.rope_theta)
+
+
+class Weights:
+    """Device weights (bf16 tensors the caller owns) and the C struct that points at them."""
+
+    def __init__(self, cfg: ModelCfg, embed: torch.Tensor, final_norm: torch.Tensor,
+                 lm_head: torch.Tensor, layers: Sequence[dict]):
+        if len(layers) != cfg.n_layers:
+            raise ValueError("need one weight dict per layer")
+        self.cfg = cfg
+        self.tensors = dict(embed=embed, final_norm=final_norm, lm_head=lm_head, layers=list(layers))
+        self._layers = (LayerWeightsC * cfg.n_layers)(
+            *[LayerWeightsC(*[_ptr(lw[k]) for k in LAYER_KEYS]) for lw in layers])
+        self.c = WeightsC(cfg.c(), ctypes.cast(self._layers, ctypes.POINTER(LayerWeightsC)),
+                          _ptr(embed), _ptr(final_norm), _ptr(lm_head))
+
+
+class PagedKV:
+    """Paged bf16 KV cache in the library's layout (see include/specverify.h):
+    k_pool [L][pages][n_kv][16][d], v_pool [L][pages][n_kv][d][16], block_table [B][max_pages]."""
+
+    def __init__(self, k_pool: torch.Tensor, v_pool: torch.Tensor, block_table: torch.Tensor):
+        self.k_pool, self.v_pool = k_pool, v_pool
+        self.block_table = block_table.to(torch.int32).contiguous()
+        self.n_pages = k_pool.shape[1]
+        self.max_pages = self.block_table.shape[1]
+        self.c = KVCacheC(_ptr(k_pool), _ptr(v_pool), _ptr(self.block_table), self.n_pages, self.max_pages)
+
+    @staticmethod
+    def empty(cfg: ModelCfg, n_pages: int, block_table: torch.Tensor, device) -> "PagedKV":
+        L, nkv, d = cfg.n_layers, cfg.n_kv_heads, cfg.head_dim
+        k = torch.zeros((L, n_pages, nkv, PAGE_SIZE, d), dtype=torch.bfloat16, device=device)
+        v = torch.zeros((L, n_pages, nkv, d, PAGE_SIZE), dtype=torch.bfloat16, device=device)
+        return PagedKV(k, v, block_table.to(device))
+
+
+def spec_workspace_bytes(cfg: ModelCfg, batch: int, k: int, max_pages_per_req: int) -> int:
+    n = ctypes.c_size_t(0)
+    c = cfg.c()
+    _check(lib().spec_workspace_bytes(ctypes.byref(c), batch, k, max_pages_per_req, ctypes.byref(n)),
+           "spec_workspace_bytes")
+    return n.value
+
+
+def workspace(nbytes: int, device) -> torch.Tensor:
+    """A 256-byte aligned device buffer (torch's caching allocator aligns to 512 bytes)."""
+    t = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+    assert t.data_ptr() % 256 == 0
+    return t
+
+
+def spec_verify(weights: Weights, kv: PagedKV, draft_tokens: torch.Tensor,
+                tree_parent: Optional[torch.Tensor], ctx_len: torch.Tensor, batch: int, k: int,
+                accepted_len: torch.Tensor, bonus_token: torch.Tensor, accepted_path: torch.Tensor,
+                ws: torch.Tensor, logits: Optional[torch.Tensor] = None,
+                greedy: Optional[torch.Tensor] = None, hidden: Optional[torch.Tensor] = None,
+                stream=None) -> None:
+    extras = ExtrasC(_ptr(logits), _ptr(greedy), _ptr(hidden))
+    rc = lib().spec_verify(ctypes.byref(weights.c), ctypes.byref(kv.c), _ptr(draft_tokens),
+                           _ptr(tree_parent), _ptr(ctx_len), batch, k, _ptr(accepted_len),
+                           _ptr(bonus_token), _ptr(accepted_path), ctypes.byref(extras), _ptr(ws),
+                           ws.numel(), _stream(stream))
+    _check(rc, "spec_verify")
+
+
+def spec_commit_kv(cfg: ModelCfg, kv: PagedKV, accepted_len: torch.Tensor,
+                   accepted_path: torch.Tensor, ctx_len: torch.Tensor, batch: int, k: int,
+                   stream=None) -> None:
+    c = cfg.c()
+    rc = lib().spec_commit_kv(ctypes.byref(c), ctypes.byref(kv.c), _ptr(accepted_len),
+                              _ptr(accepted_path), _ptr(ctx_len), batch, k, _stream(stream))
+    _check(rc, "spec_commit_kv")
+
+
+def spec_accept_workspace_bytes(batch: int, k: int, vocab: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().spec_accept_workspace_bytes(batch, k, vocab, ctypes.byref(n)),
+           "spec_accept_workspace_bytes")
+    return n.value
+
+
+def spec_accept(logits: torch.Tensor, draft_tokens: torch.Tensor,
+                tree_parent: Optional[torch.Tensor], batch: int, k: int, vocab: int,
+                accepted_len: torch.Tensor, bonus_token: torch.Tensor,
+                accepted_path: torch.Tensor, ws: torch.Tensor,
+                greedy: Optional[torch.Tensor] = None, stream=None) -> None:
+    rc = lib().spec_accept(_ptr(logits), _ptr(draft_tokens), _ptr(tree_parent), batch, k, vocab,
+                           _ptr(accepted_len), _ptr(bonus_token), _ptr(accepted_path), _ptr(greedy),
+                           _ptr(ws), ws.numel(), _stream(stream))
+    _check(rc, "spec_accept")
+
+
+def spec_skinny_gemm_bytes(m: int, n: int, kd: int) -> int:
+    nb = ctypes.c_size_t(0)
+    _check(lib().spec_skinny_gemm_bytes(m, n, kd, ctypes.byref(nb)), "spec_skinny_gemm_bytes")
+    return nb.value
+
+
+def spec_skinny_gemm(x: torch.Tensor, w: torch.Tensor, partials: torch.Tensor, stream=None) -> int:
+    """partials[s][m][n] for x [m][kd], w [n][kd] (bf16); returns the split count."""
+    m, kd = x.shape
+    n = w.shape[0]
+    splits = ctypes.c_int(0)
+    rc = lib().spec_skinny_gemm(_ptr(x), m, kd, _ptr(w), n, _ptr(partials),
+                                partials.numel() * partials.element_size(), ctypes.byref(splits),
+                                _stream(stream))
+    _check(rc, "spec_skinny_gemm")
+    return splits.value

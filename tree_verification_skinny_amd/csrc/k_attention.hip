@@ -1,0 +1,200 @@
+// k_attention.hip — tree-masked grouped-query attention of the draft nodes over the paged KV
+// cache, on gfx950 MFMA with the KV chunk staged in LDS.
+//
+// Each draft token sees the committed context plus the nodes on its own root path: tree tokens
+// are conditioned on the path that leads to them [JetSpec article, seventnews.com — "Technical
+// architecture"]. The path is a 64-bit ancestor mask per node (bit j set = node j is on the
+// path), so the mask test in the inner loop is one shift and one AND.
+//
+// Work split (split-KV): one workgroup per (request, kv head, chunk of 128 key positions). The
+// 4 waves stage the chunk's keys [128][D] and transposed values [D][128] from the cache pages
+// into LDS with 128-bit loads, then each wave takes 16-column query tiles: the columns are the
+// (q head of this kv group, draft node) pairs, so one K/V tile in LDS serves every q head of the
+// group. Per 32 keys and tile:
+//   S^T = K . Q^T   (A = keys from LDS, B = Q^T held in registers for the whole chunk)
+//   online softmax per query column, in the log2 domain
+//   O^T += V^T . P^T (A = transposed values from LDS, B = the probabilities this lane already
+//                     holds, as a bf16 high part plus a bf16 low part)
+// The S^T tiles take their 16 key rows in the order 8*(r/4) + 4*tile + r%4, which leaves each
+// lane holding 8 consecutive keys: exactly the P^T fragment the V^T MFMA wants, so no lane
+// exchange is needed between the two products. Chunk partials (unnormalised O, running max,
+// running sum) are merged by attn_combine.
+#include "kernels.hpp"
+
+namespace sv {
+
+template <int D>
+__global__ __launch_bounds__(256) void attn_partial_kernel(
+    const bf16 *__restrict__ q, const bf16 *__restrict__ k_pool, const bf16 *__restrict__ v_pool,
+    const int32_t *__restrict__ block_table, int max_pages, const int32_t *__restrict__ ctx_len,
+    const uint64_t *__restrict__ anc, const int32_t *__restrict__ status, int K, int nq, int nkv,
+    int n_chunks, float scale_log2, float *__restrict__ part_o, float2 *__restrict__ part_ml) {
+    constexpr int CH = kAttnChunk;
+    constexpr int KP = D + 8;    // padded LDS row of K (bf16)
+    constexpr int VP = CH + 8;   // padded LDS row of V^T (bf16)
+    __shared__ __attribute__((aligned(16))) bf16 Ks[CH * KP];
+    __shared__ __attribute__((aligned(16))) bf16 Vt[D * VP];
+
+    const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    if (status[b] != 0) return;
+    const int ctx = ctx_len[b];
+    const int T = ctx + K;
+    const int kb = c * CH;
+    if (kb >= T) return;
+    const int nvalid = min(CH, T - kb);
+    const int npages = (nvalid + 15) >> 4;
+    const int group = nq / nkv;
+    const int R = group * K;
+    const int QT = (R + 15) >> 4;
+
+    // ---- stage the chunk: K rows as stored, V already transposed in the page ---------------
+    for (int p = 0; p < CH / 16; ++p) {
+        const bool live = p < npages;
+        const int page = live ? block_table[(int64_t)b * max_pages + (kb >> 4) + p] : 0;
+        const bf16 *kp = k_pool + ((int64_t)page * nkv + g) * 16 * D;
+        const bf16 *vp = v_pool + ((int64_t)page * nkv + g) * D * 16;
+        for (int e = threadIdx.x * 8; e < 16 * D; e += 256 * 8) {
+            const int row = e / D, col = e % D;
+            bf16x8 kv = live ? *(const bf16x8 *)(kp + e) : bf16x8{};
+            *(bf16x8 *)&Ks[(p * 16 + row) * KP + col] = kv;
+            const int d = e >> 4, slot = e & 15;
+            bf16x8 vv = live ? *(const bf16x8 *)(vp + e) : bf16x8{};
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (p * 16 + slot + j >= nvalid) vv[j] = (bf16)0.0f;   // never multiply stale data
+            *(bf16x8 *)&Vt[d * VP + p * 16 + slot] = vv;
+        }
+    }
+    __syncthreads();
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r16 = lane & 15, grp = lane >> 4;
+    const int nsteps = (nvalid + 31) >> 5;
+    const int kr0 = 8 * (r16 >> 2) + (r16 & 3);   // S^T tile 0 key row of this lane (tile 1: +4)
+
+    for (int t = wave; t < QT; t += 4) {
+        const int rho = 16 * t + r16;             // query column of this lane
+        const bool col_ok = rho < R;
+        const int hh = col_ok ? rho / K : 0, tok = col_ok ? rho % K : 0;
+        const int node = b * K + tok;
+        const uint64_t am = anc[node];
+        const bf16 *qrow = q + ((int64_t)node * nq + g * group + hh) * D;
+        bf16x8 qf[D / 32];
+#pragma unroll
+        for (int ds = 0; ds < D / 32; ++ds) qf[ds] = *(const bf16x8 *)(qrow + ds * 32 + grp * 8);
+        floatx4 o[D / 16];
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+        float m_run = -INFINITY, l_run = 0.f;
+
+        for (int st = 0; st < nsteps; ++st) {
+            floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+            const bf16 *k0 = &Ks[(st * 32 + kr0) * KP + grp * 8];
+            const bf16 *k1 = k0 + 4 * KP;
+#pragma unroll
+            for (int ds = 0; ds < D / 32; ++ds) {
+                s0 = mfma16x16x32(*(const bf16x8 *)(k0 + ds * 32), qf[ds], s0);
+                s1 = mfma16x16x32(*(const bf16x8 *)(k1 + ds * 32), qf[ds], s1);
+            }
+            float sv[8];
+            float mloc = -INFINITY;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float raw = e < 4 ? s0[e] : s1[e - 4];
+                const int kl = st * 32 + 8 * grp + e;
+                const int ka = kb + kl;
+                const bool vis = col_ok && kl < nvalid && (ka < ctx || ((am >> (ka - ctx)) & 1ull));
+                sv[e] = vis ? raw * scale_log2 : -INFINITY;
+                mloc = fmaxf(mloc, sv[e]);
+            }
+            mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
+            mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+            const float m_new = fmaxf(m_run, mloc);
+            const bool none = (m_new == -INFINITY);
+            const float alpha = none ? 1.f : exp2f(m_run - m_new);
+            // p = p_hi + p_lo, both bf16: the two products carry ~16 bits of p, so the weighted
+            // sum of values is as precise as the fp32 probabilities it stands for.
+            bf16x8 ph, pl;
+            float psum = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float pv = none ? 0.f : exp2f(sv[e] - m_new);
+                const bf16 hi = to_bf(pv);
+                ph[e] = hi;
+                pl[e] = to_bf(pv - to_f(hi));
+                psum += pv;
+            }
+            l_run = l_run * alpha + psum;
+            m_run = m_new;
+            const bf16 *vrow = &Vt[r16 * VP + st * 32 + grp * 8];
+#pragma unroll
+            for (int dt = 0; dt < D / 16; ++dt) {
+                const bf16x8 vf = *(const bf16x8 *)(vrow + dt * 16 * VP);
+                o[dt] *= alpha;
+                o[dt] = mfma16x16x32(vf, ph, o[dt]);
+                o[dt] = mfma16x16x32(vf, pl, o[dt]);
+            }
+        }
+        l_run += __shfl_xor(l_run, 16, 64);
+        l_run += __shfl_xor(l_run, 32, 64);
+        if (col_ok) {
+            const int64_t base = (((int64_t)b * nkv + g) * n_chunks + c) * R + rho;
+#pragma unroll
+            for (int dt = 0; dt < D / 16; ++dt)
+                *(floatx4 *)(part_o + base * D + dt * 16 + 4 * grp) = o[dt];
+            if (grp == 0) part_ml[base] = make_float2(m_run, l_run);
+        }
+    }
+}
+
+// Merge the chunk partials of one (node, q head): o = sum_c 2^(m_c - m*) O_c / sum_c 2^(m_c - m*) l_c.
+template <int D>
+__global__ __launch_bounds__(D) void attn_combine_kernel(
+    const float *__restrict__ part_o, const float2 *__restrict__ part_ml,
+    const int32_t *__restrict__ ctx_len, const int32_t *__restrict__ status, int K, int nq,
+    int nkv, int n_chunks, bf16 *__restrict__ out) {
+    const int row = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
+    const int b = row / K, tok = row % K;
+    bf16 *dst = out + ((int64_t)row * nq + h) * D + d;
+    if (status[b] != 0) { *dst = (bf16)0.0f; return; }
+    const int group = nq / nkv, g = h / group, hh = h % group;
+    const int R = group * K, rho = hh * K + tok;
+    const int nc = (ctx_len[b] + K + kAttnChunk - 1) / kAttnChunk;
+    const int64_t base = ((int64_t)b * nkv + g) * n_chunks * R + rho;
+    float mstar = -INFINITY;
+    for (int c = 0; c < nc; ++c) mstar = fmaxf(mstar, part_ml[base + (int64_t)c * R].x);
+    float num = 0.f, den = 0.f;
+    for (int c = 0; c < nc; ++c) {
+        const float2 ml = part_ml[base + (int64_t)c * R];
+        if (ml.x == -INFINITY) continue;
+        const float w = exp2f(ml.x - mstar);
+        den += w * ml.y;
+        num += w * part_o[(base + (int64_t)c * R) * D + d];
+    }
+    *dst = to_bf(num / den);
+}
+
+hipError_t attention(const AttnArgs &a, hipStream_t st) {
+    const float scale_log2 = kLog2e / sqrtf((float)a.D);
+    dim3 grid(a.n_chunks, a.nkv, a.B);
+    if (a.D == 128) {
+        hipLaunchKernelGGL(attn_partial_kernel<128>, grid, dim3(256), 0, st, a.q, a.k_pool, a.v_pool,
+                           a.block_table, a.max_pages, a.ctx_len, a.anc, a.status, a.K, a.nq, a.nkv,
+                           a.n_chunks, scale_log2, a.part_o, a.part_ml);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(attn_combine_kernel<128>, dim3(a.B * a.K, a.nq), dim3(128), 0, st, a.part_o,
+                           a.part_ml, a.ctx_len, a.status, a.K, a.nq, a.nkv, a.n_chunks, a.out);
+    } else {
+        hipLaunchKernelGGL(attn_partial_kernel<64>, grid, dim3(256), 0, st, a.q, a.k_pool, a.v_pool,
+                           a.block_table, a.max_pages, a.ctx_len, a.anc, a.status, a.K, a.nq, a.nkv,
+                           a.n_chunks, scale_log2, a.part_o, a.part_ml);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(attn_combine_kernel<64>, dim3(a.B * a.K, a.nq), dim3(64), 0, st, a.part_o,
+                           a.part_ml, a.ctx_len, a.status, a.K, a.nq, a.nkv, a.n_chunks, a.out);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace sv

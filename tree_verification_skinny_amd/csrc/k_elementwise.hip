@@ -1,0 +1,450 @@
+// k_elementwise.hip — the small kernels around the GEMMs and attention of the verify pass:
+// draft-tree bookkeeping, embedding + RMSNorm, split-K reduction fused with RoPE and the KV
+// tail write, residual add + RMSNorm, SwiGLU, the vocab-wide greedy choice with the accepted-path
+// walk, and the commit of the accepted path's KV rows.
+//
+// Lossless greedy verification: a draft token is accepted only if it equals the target's greedy
+// choice after its parent, and only along a path whose every earlier token was accepted
+// [SpecPilot digest, airadar.tv — "Risks"]; tree tokens are conditioned on their own root path
+// [JetSpec article, seventnews.com — "Technical architecture"].
+#include "kernels.hpp"
+
+namespace sv {
+
+// ---- draft tree: validation, depth, ancestor mask, position ---------------------------------
+// One wavefront per request. A request is marked bad (status -1) for a token outside the
+// vocabulary, a malformed parent array (parent[0] != -1, or parent[i] outside [0, i)), a
+// negative context, or pages that do not cover positions [0, ctx + K).
+__global__ __launch_bounds__(64) void tree_prep_kernel(
+    const int32_t *__restrict__ tokens, const int32_t *__restrict__ parent,
+    const int32_t *__restrict__ ctx_len, const int32_t *__restrict__ block_table, int max_pages,
+    int n_pages, int K, int vocab, int32_t *__restrict__ depth, int32_t *__restrict__ pos,
+    uint64_t *__restrict__ anc, int32_t *__restrict__ status) {
+    __shared__ int32_t s_depth[64];
+    __shared__ uint64_t s_anc[64];
+    __shared__ int s_tree_bad;
+    const int b = blockIdx.x, lane = threadIdx.x;
+    int bad = 0;
+    if (lane < K) {
+        const int t = tokens[(int64_t)b * K + lane];
+        bad |= (t < 0 || t >= vocab);
+    }
+    int ctx = 0;
+    if (ctx_len != nullptr) {
+        ctx = ctx_len[b];
+        if (ctx < 0) {
+            bad = 1;
+        } else {
+            const int64_t need = ((int64_t)ctx + K + 15) / 16;
+            if (need > max_pages) {
+                bad = 1;
+            } else {
+                for (int p = lane; p < need; p += 64) {
+                    const int id = block_table[(int64_t)b * max_pages + p];
+                    bad |= (id < 0 || id >= n_pages);
+                }
+            }
+        }
+    }
+    if (lane == 0) {
+        int tb = 0;
+        s_depth[0] = 0;
+        s_anc[0] = 1ull;
+        if (parent != nullptr && parent[(int64_t)b * K] != -1) tb = 1;
+        for (int i = 1; i < K; ++i) {
+            int p = parent != nullptr ? parent[(int64_t)b * K + i] : i - 1;
+            if (p < 0 || p >= i) { tb = 1; p = 0; }
+            s_depth[i] = s_depth[p] + 1;
+            s_anc[i] = s_anc[p] | (1ull << i);
+        }
+        s_tree_bad = tb;
+    }
+    __syncthreads();
+    bad |= s_tree_bad;
+    bad = __any(bad);
+    if (lane < K) {
+        const int64_t n = (int64_t)b * K + lane;
+        const int dd = bad ? 0 : s_depth[lane];
+        depth[n] = dd;
+        pos[n] = ctx + dd;
+        anc[n] = bad ? (1ull << lane) : s_anc[lane];
+    }
+    if (lane == 0) status[b] = bad ? -1 : 0;
+}
+
+hipError_t tree_prep(const int32_t *tokens, const int32_t *parent, const int32_t *ctx_len,
+                     const int32_t *block_table, int max_pages, int n_pages, int B, int K,
+                     int vocab, const NodeInfo &ni, hipStream_t st) {
+    hipLaunchKernelGGL(tree_prep_kernel, dim3(B), dim3(64), 0, st, tokens, parent, ctx_len,
+                       block_table, max_pages, n_pages, K, vocab, ni.depth, ni.pos, ni.anc,
+                       ni.status);
+    return hipGetLastError();
+}
+
+// ---- RoPE angles: (cos, sin) of pos * theta^(-2j/d), evaluated in double --------------------
+__global__ void rope_table_kernel(const int32_t *__restrict__ pos, int D, double theta,
+                                  float2 *__restrict__ cs) {
+    const int row = blockIdx.x, j = threadIdx.x;
+    const double inv_freq = pow(theta, -2.0 * (double)j / (double)D);
+    const double ang = (double)pos[row] * inv_freq;
+    cs[(int64_t)row * (D / 2) + j] = make_float2((float)cos(ang), (float)sin(ang));
+}
+
+hipError_t rope_table(const NodeInfo &ni, int M, int D, double theta, hipStream_t st) {
+    hipLaunchKernelGGL(rope_table_kernel, dim3(M), dim3(D / 2), 0, st, ni.pos, D, theta, ni.rope);
+    return hipGetLastError();
+}
+
+// ---- embedding + first RMSNorm ----------------------------------------------------------------
+// RMSNorm: u = bf16((x / sqrt(mean(x^2) + eps)) * g), sum of squares in fp32. Each thread
+// re-reads its own elements for the second pass (cache resident) instead of holding them.
+__global__ __launch_bounds__(256) void embed_norm_kernel(const int32_t *__restrict__ tokens,
+                                                         const bf16 *__restrict__ embed,
+                                                         const bf16 *__restrict__ gain, int H,
+                                                         int vocab, float eps,
+                                                         bf16 *__restrict__ x, bf16 *__restrict__ u,
+                                                         bf16 *__restrict__ trace) {
+    __shared__ float red[4];
+    const int row = blockIdx.x;
+    int tok = tokens[row];
+    if (tok < 0 || tok >= vocab) tok = 0;   // the request is already marked bad; stay in bounds
+    const bf16 *src = embed + (int64_t)tok * H;
+    float ss = 0.f;
+    for (int e = threadIdx.x * 8; e < H; e += 256 * 8) {
+        bf16x8 xv = *(const bf16x8 *)(src + e);
+        *(bf16x8 *)(x + (int64_t)row * H + e) = xv;
+        if (trace) *(bf16x8 *)(trace + (int64_t)row * H + e) = xv;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ss += to_f(xv[j]) * to_f(xv[j]);
+    }
+    ss = block_sum_256(ss, red);
+    const float inv = 1.0f / sqrtf(ss / (float)H + eps);
+    for (int e = threadIdx.x * 8; e < H; e += 256 * 8) {
+        bf16x8 xv = *(const bf16x8 *)(src + e), gv = *(const bf16x8 *)(gain + e), uv;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) uv[j] = to_bf((to_f(xv[j]) * inv) * to_f(gv[j]));
+        *(bf16x8 *)(u + (int64_t)row * H + e) = uv;
+    }
+}
+
+hipError_t embed_norm(const int32_t *tokens, const bf16 *embed, const bf16 *gain, int M, int H,
+                      int vocab, float eps, bf16 *x, bf16 *u, bf16 *trace, hipStream_t st) {
+    hipLaunchKernelGGL(embed_norm_kernel, dim3(M), dim3(256), 0, st, tokens, embed, gain, H, vocab,
+                       eps, x, u, trace);
+    return hipGetLastError();
+}
+
+// ---- QKV: split-K sum, bf16, RoPE on q and k, k and v into the request's cache pages -------
+// Node i (local index il of request b) goes to cache slot ctx + il; its rotation angle uses
+// its tree position ctx + depth(i).
+__global__ __launch_bounds__(256) void qkv_rope_store_kernel(
+    const float *__restrict__ P, int splits, int M, const float2 *__restrict__ rope,
+    const int32_t *__restrict__ status, const int32_t *__restrict__ ctx_len,
+    const int32_t *__restrict__ block_table, int max_pages, int K, int nq, int nkv, int D,
+    bf16 *__restrict__ q, bf16 *__restrict__ k_pool, bf16 *__restrict__ v_pool) {
+#pragma clang fp contract(off)
+    const int row = blockIdx.x;
+    const int b = row / K, il = row % K;
+    const bool ok = status[b] == 0;
+    const int N = (nq + 2 * nkv) * D;
+    const int half = D / 2;
+    int page = 0, so = 0;
+    if (ok) {
+        const int slot = ctx_len[b] + il;
+        page = page_of(block_table, max_pages, b, slot);
+        so = slot & 15;
+    }
+    const float *Pr = P + (int64_t)row * N;
+    const int64_t pstride = (int64_t)M * N;
+    const int npairs = (nq + nkv) * half;
+    for (int w = threadIdx.x; w < npairs; w += 256) {
+        const int hh = w / half, j = w % half;
+        const int c1 = hh * D + j, c2 = c1 + half;
+        float a = 0.f, bb = 0.f;
+        for (int s = 0; s < splits; ++s) { a += Pr[s * pstride + c1]; bb += Pr[s * pstride + c2]; }
+        a = round_bf(a);
+        bb = round_bf(bb);
+        const float2 cs = rope[(int64_t)row * half + j];
+        const float ra = a * cs.x - bb * cs.y;
+        const float rb = bb * cs.x + a * cs.y;
+        if (hh < nq) {
+            bf16 *qh = q + ((int64_t)row * nq + hh) * D;
+            qh[j] = to_bf(ra);
+            qh[j + half] = to_bf(rb);
+        } else if (ok) {
+            bf16 *kr = k_pool + (((int64_t)page * nkv + (hh - nq)) * 16 + so) * D;
+            kr[j] = to_bf(ra);
+            kr[j + half] = to_bf(rb);
+        }
+    }
+    if (!ok) return;
+    const int vbase = (nq + nkv) * D;
+    for (int w = threadIdx.x; w < nkv * D; w += 256) {
+        float a = 0.f;
+        for (int s = 0; s < splits; ++s) a += Pr[s * pstride + vbase + w];
+        const int g = w / D, dd = w % D;
+        v_pool[(((int64_t)page * nkv + g) * D + dd) * 16 + so] = to_bf(a);
+    }
+}
+
+hipError_t qkv_rope_store(const float *P, int splits, const NodeInfo &ni, const int32_t *ctx_len,
+                          const int32_t *block_table, int max_pages, int B, int K, int nq,
+                          int nkv, int D, bf16 *q, bf16 *k_pool, bf16 *v_pool, hipStream_t st) {
+    hipLaunchKernelGGL(qkv_rope_store_kernel, dim3(B * K), dim3(256), 0, st, P, splits, B * K,
+                       ni.rope, ni.status, ctx_len, block_table, max_pages, K, nq, nkv, D, q,
+                       k_pool, v_pool);
+    return hipGetLastError();
+}
+
+// ---- projection split-K sum, residual add, RMSNorm -------------------------------------------
+// x = bf16(x + bf16(sum_s P[s])), splits added in index order; u = RMSNorm(x) * g.
+__global__ __launch_bounds__(256) void residual_norm_kernel(const float *__restrict__ P, int splits,
+                                                            int M, int H,
+                                                            const bf16 *__restrict__ gain,
+                                                            float eps, bf16 *__restrict__ x,
+                                                            bf16 *__restrict__ u,
+                                                            bf16 *__restrict__ trace) {
+    __shared__ float red[4];
+    const int row = blockIdx.x;
+    const int64_t pstride = (int64_t)M * H;
+    bf16 *xr = x + (int64_t)row * H;
+    float ss = 0.f;
+    for (int e = threadIdx.x * 4; e < H; e += 256 * 4) {
+        floatx4 y = *(const floatx4 *)(P + (int64_t)row * H + e);
+        for (int s = 1; s < splits; ++s) y += *(const floatx4 *)(P + s * pstride + (int64_t)row * H + e);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float xn = round_bf(to_f(xr[e + j]) + round_bf(y[j]));
+            ss += xn * xn;
+            xr[e + j] = to_bf(xn);
+            if (trace) trace[(int64_t)row * H + e + j] = to_bf(xn);
+        }
+    }
+    ss = block_sum_256(ss, red);
+    const float inv = 1.0f / sqrtf(ss / (float)H + eps);
+    for (int e = threadIdx.x * 4; e < H; e += 256 * 4) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) u[(int64_t)row * H + e + j] = to_bf((to_f(xr[e + j]) * inv) * to_f(gain[e + j]));
+    }
+}
+
+hipError_t residual_norm(const float *P, int splits, int M, int H, const bf16 *gain, float eps,
+                         bf16 *x, bf16 *u, bf16 *trace, hipStream_t st) {
+    hipLaunchKernelGGL(residual_norm_kernel, dim3(M), dim3(256), 0, st, P, splits, M, H, gain, eps,
+                       x, u, trace);
+    return hipGetLastError();
+}
+
+// ---- SwiGLU: h = bf16(silu(gate) * up), gate and up rounded to bf16 first -------------------
+__global__ __launch_bounds__(256) void swiglu_kernel(const float *__restrict__ P, int splits, int M,
+                                                     int F, bf16 *__restrict__ h) {
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (int64_t)M * F) return;
+    const int64_t row = idx / F, n = idx % F;
+    const int64_t pstride = (int64_t)M * 2 * F;
+    float ga = 0.f, up = 0.f;
+    for (int s = 0; s < splits; ++s) {
+        ga += P[s * pstride + row * 2 * F + n];
+        up += P[s * pstride + row * 2 * F + F + n];
+    }
+    ga = round_bf(ga);
+    up = round_bf(up);
+    const float silu = ga / (1.0f + expf(-ga));
+    h[idx] = to_bf(silu * up);
+}
+
+hipError_t swiglu(const float *P, int splits, int M, int F, bf16 *h, hipStream_t st) {
+    const int64_t n = (int64_t)M * F;
+    hipLaunchKernelGGL(swiglu_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, P, splits,
+                       M, F, h);
+    return hipGetLastError();
+}
+
+// ---- greedy choice from caller logits: per (row, chunk of 2048 columns) -----------------------
+constexpr int kArgChunk = 2048;
+
+__device__ __forceinline__ void block_best_256(float &bv, int &bi, float *rv, int *ri) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const float ov = __shfl_xor(bv, o, 64);
+        const int oi = __shfl_xor(bi, o, 64);
+        if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+    }
+    const int w = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) { rv[w] = bv; ri[w] = bi; }
+    __syncthreads();
+    bv = rv[0];
+    bi = ri[0];
+    for (int k = 1; k < 4; ++k)
+        if (better(rv[k], ri[k], bv, bi)) { bv = rv[k]; bi = ri[k]; }
+}
+
+__global__ __launch_bounds__(256) void argmax_partials_kernel(const float *__restrict__ logits,
+                                                              int M, int V,
+                                                              float *__restrict__ amax_val,
+                                                              int *__restrict__ amax_idx) {
+    __shared__ float rv[4];
+    __shared__ int ri[4];
+    const int row = blockIdx.x, c = blockIdx.y;
+    const float *r = logits + (int64_t)row * V;
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+    const int end = min(V, (c + 1) * kArgChunk);
+    for (int i = c * kArgChunk + threadIdx.x; i < end; i += 256)
+        if (better(r[i], i, bv, bi)) { bv = r[i]; bi = i; }
+    block_best_256(bv, bi, rv, ri);
+    if (threadIdx.x == 0) {
+        amax_val[(int64_t)c * M + row] = bv;
+        amax_idx[(int64_t)c * M + row] = bi;
+    }
+}
+
+hipError_t argmax_partials(const float *logits, int M, int V, float *amax_val, int *amax_idx,
+                           int n_chunks, hipStream_t st) {
+    hipLaunchKernelGGL(argmax_partials_kernel, dim3(M, n_chunks), dim3(256), 0, st, logits, M, V,
+                       amax_val, amax_idx);
+    return hipGetLastError();
+}
+
+int argmax_chunks(int V) { return (V + kArgChunk - 1) / kArgChunk; }
+
+// ---- greedy choice per node + longest accepted root path, one workgroup per request ----------
+__global__ __launch_bounds__(256) void argmax_accept_kernel(
+    const float *__restrict__ amax_val, const int *__restrict__ amax_idx, int n_groups,
+    const int32_t *__restrict__ tokens, const int32_t *__restrict__ parent,
+    const int32_t *__restrict__ depth, const int32_t *__restrict__ status, int M, int K,
+    int32_t *__restrict__ greedy, int32_t *__restrict__ accepted_len, int32_t *__restrict__ bonus,
+    int32_t *__restrict__ path) {
+    __shared__ float rv[4];
+    __shared__ int ri[4];
+    __shared__ int s_arg[64];
+    const int b = blockIdx.x;
+    for (int i = 0; i < K; ++i) {
+        const int row = b * K + i;
+        float bv = -INFINITY;
+        int bi = 0x7fffffff;
+        for (int g = threadIdx.x; g < n_groups; g += 256) {
+            const float v = amax_val[(int64_t)g * M + row];
+            const int ix = amax_idx[(int64_t)g * M + row];
+            if (better(v, ix, bv, bi)) { bv = v; bi = ix; }
+        }
+        block_best_256(bv, bi, rv, ri);
+        if (threadIdx.x == 0) {
+            s_arg[i] = bi;
+            if (greedy) greedy[row] = bi;
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x != 0) return;
+    int32_t *pr = path + (int64_t)b * K;
+    for (int i = 0; i < K; ++i) pr[i] = -1;
+    if (status[b] != 0) {
+        accepted_len[b] = -1;
+        bonus[b] = -1;
+        return;
+    }
+    uint64_t ok = 1ull;          // bit i: node i accepted
+    int best = 0;
+    const int32_t *tk = tokens + (int64_t)b * K;
+    const int32_t *dp = depth + (int64_t)b * K;
+    for (int i = 1; i < K; ++i) {
+        const int p = parent != nullptr ? parent[(int64_t)b * K + i] : i - 1;
+        if (((ok >> p) & 1ull) && tk[i] == s_arg[p]) {
+            ok |= 1ull << i;
+            if (dp[i] > dp[best]) best = i;
+        }
+    }
+    accepted_len[b] = dp[best];
+    bonus[b] = s_arg[best];
+    for (int node = best; node >= 0; node = (node == 0 ? -1 : (parent != nullptr ? parent[(int64_t)b * K + node] : node - 1)))
+        pr[dp[node]] = node;
+}
+
+hipError_t argmax_accept(const float *amax_val, const int *amax_idx, int n_groups,
+                         const int32_t *tokens, const int32_t *parent, const NodeInfo &ni, int B,
+                         int K, int32_t *greedy, int32_t *accepted_len, int32_t *bonus,
+                         int32_t *path, hipStream_t st) {
+    hipLaunchKernelGGL(argmax_accept_kernel, dim3(B), dim3(256), 0, st, amax_val, amax_idx, n_groups,
+                       tokens, parent, ni.depth, ni.status, B * K, K, greedy, accepted_len, bonus,
+                       path);
+    return hipGetLastError();
+}
+
+// ---- commit: slot ctx + t <- slot ctx + path[t], t = 0..a, every layer, K and V -------------
+// One workgroup per (layer, request, kv head, K-or-V). All source rows are read into registers
+// before any is written, so overlapping moves are safe. path[t] is a node id at depth t, and
+// node ids are topological, so path[t] >= t.
+__global__ __launch_bounds__(256) void commit_kv_kernel(
+    const int32_t *__restrict__ accepted_len, const int32_t *__restrict__ path,
+    const int32_t *__restrict__ ctx_len, const int32_t *__restrict__ block_table, int max_pages,
+    int n_pages, int B, int K, int nkv, int D, int64_t layer_stride, bf16 *__restrict__ k_pool,
+    bf16 *__restrict__ v_pool) {
+    const int id = blockIdx.x;
+    const int kv = id & 1;
+    const int g = (id >> 1) % nkv;
+    const int b = (id >> 1) / nkv % B;
+    const int l = (id >> 1) / nkv / B;
+    const int a = accepted_len[b];
+    if (a < 0 || a >= K) return;
+    const int ctx = ctx_len[b];
+    if (ctx < 0 || (int64_t)ctx + K > (int64_t)max_pages * 16) return;
+    const int32_t *pr = path + (int64_t)b * K;
+    bf16 *pool = (kv == 0 ? k_pool : v_pool) + (int64_t)l * layer_stride;
+    constexpr int kRegs = 64 * 128 / 256;
+    bf16 vals[kRegs];
+    const int n = (a + 1) * D;
+    int r = 0;
+    for (int e = threadIdx.x; e < n; e += 256, ++r) {
+        const int t = e / D, d = e % D;
+        const int src = pr[t];
+        bf16 val = (bf16)0.0f;
+        if (src >= t && src < K) {
+            const int ps = ctx + src;
+            const int page = page_of(block_table, max_pages, b, ps);
+            if (page >= 0 && page < n_pages) {
+                const int64_t off = kv == 0 ? (((int64_t)page * nkv + g) * 16 + (ps & 15)) * D + d
+                                            : (((int64_t)page * nkv + g) * D + d) * 16 + (ps & 15);
+                val = pool[off];
+            }
+        }
+        vals[r] = val;
+    }
+    __syncthreads();
+    r = 0;
+    for (int e = threadIdx.x; e < n; e += 256, ++r) {
+        const int t = e / D, d = e % D;
+        const int src = pr[t];
+        if (!(src >= t && src < K)) continue;
+        const int pd = ctx + t;
+        const int page = page_of(block_table, max_pages, b, pd);
+        if (page < 0 || page >= n_pages) continue;
+        const int64_t off = kv == 0 ? (((int64_t)page * nkv + g) * 16 + (pd & 15)) * D + d
+                                    : (((int64_t)page * nkv + g) * D + d) * 16 + (pd & 15);
+        pool[off] = vals[r];
+    }
+}
+
+hipError_t commit_kv(const int32_t *accepted_len, const int32_t *path, const int32_t *ctx_len,
+                     const int32_t *block_table, int max_pages, int n_pages, int L, int B, int K,
+                     int nkv, int D, bf16 *k_pool, bf16 *v_pool, hipStream_t st) {
+    const int64_t layer_stride = (int64_t)n_pages * nkv * 16 * D;
+    hipLaunchKernelGGL(commit_kv_kernel, dim3(L * B * nkv * 2), dim3(256), 0, st, accepted_len, path,
+                       ctx_len, block_table, max_pages, n_pages, B, K, nkv, D, layer_stride, k_pool,
+                       v_pool);
+    return hipGetLastError();
+}
+
+__global__ void commit_ctx_kernel(const int32_t *__restrict__ accepted_len,
+                                  int32_t *__restrict__ ctx_len, int B) {
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b < B && accepted_len[b] >= 0) ctx_len[b] += accepted_len[b] + 1;
+}
+
+hipError_t commit_ctx(const int32_t *accepted_len, int32_t *ctx_len, int B, hipStream_t st) {
+    hipLaunchKernelGGL(commit_ctx_kernel, dim3((B + 255) / 256), dim3(256), 0, st, accepted_len,
+                       ctx_len, B);
+    return hipGetLastError();
+}
+
+}  // namespace sv

@@ -1,0 +1,372 @@
+// specverify.hip — host side of libspecverify: argument checks, the per-call plan (GEMM tiles
+// and K splits, attention chunks, workspace layout) and the launch sequence of one
+// verification pass. Everything is enqueued on the caller's stream; nothing here waits for
+// the device, allocates, or keeps global state.
+#include <string.h>
+
+#include "specverify.h"
+#include "kernels.hpp"
+
+namespace sv {
+int argmax_chunks(int V);
+}
+
+namespace {
+
+using namespace sv;
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+struct Carver {
+    size_t off = 0;
+    size_t take(size_t bytes) {
+        const size_t o = off;
+        off = align_up(off + bytes);
+        return o;
+    }
+};
+
+// Target: enough workgroups to keep every CU streaming (256 CUs, a few groups each).
+constexpr int kTargetGroups = 1024;
+
+int pick_splits(int N, int Kd, int nt) {
+    const int groups = (N + 16 * nt - 1) / (16 * nt);
+    const int steps = Kd / 32;
+    int s = kTargetGroups / groups;
+    if (s < 1) s = 1;
+    // keep at least 8 K steps (2 per wave) in every split
+    int max_s = steps / 8;
+    if (max_s < 1) max_s = 1;
+    if (s > max_s) s = max_s;
+    return s;
+}
+
+struct Plan {
+    int B, K, M;
+    int L, H, nq, nkv, D, F, V;
+    int qd, nqkv;
+    GemmShape g_qkv, g_o, g_gu, g_down, g_lm;
+    int lm_groups;
+    int attn_chunks;
+    size_t o_depth, o_pos, o_status, o_anc, o_rope, o_x, o_u, o_q, o_attn, o_h, o_part, o_po,
+        o_pml, o_amv, o_ami, total;
+};
+
+int check_cfg(const spec_model_cfg *c) {
+    if (c == nullptr) return SPEC_EINVAL;
+    if (c->n_layers < 1 || c->hidden < 1 || c->n_q_heads < 1 || c->n_kv_heads < 1 ||
+        c->head_dim < 1 || c->ffn < 1 || c->vocab < 1)
+        return SPEC_EINVAL;
+    if (!(c->rms_eps >= 0.0f) || !(c->rope_theta > 0.0)) return SPEC_EINVAL;
+    if (c->head_dim != 64 && c->head_dim != 128) return SPEC_EUNSUPPORTED;
+    if (c->n_q_heads % c->n_kv_heads != 0) return SPEC_EUNSUPPORTED;
+    if (c->hidden % 32 != 0 || (c->n_q_heads * c->head_dim) % 32 != 0 || c->ffn % 32 != 0)
+        return SPEC_EUNSUPPORTED;
+    if (c->hidden > 16384) return SPEC_EUNSUPPORTED;
+    if (c->vocab % 16 != 0) return SPEC_EUNSUPPORTED;
+    return SPEC_OK;
+}
+
+int make_plan(const spec_model_cfg *c, int B, int K, int max_pages, Plan &p) {
+    int rc = check_cfg(c);
+    if (rc != SPEC_OK) return rc;
+    if (B < 1 || K < 1 || max_pages < 1) return SPEC_EINVAL;
+    if (K > SPEC_MAX_K) return SPEC_EUNSUPPORTED;
+    if ((int64_t)B * K > (1 << 20)) return SPEC_EUNSUPPORTED;
+    p.B = B;
+    p.K = K;
+    p.M = B * K;
+    p.L = c->n_layers;
+    p.H = c->hidden;
+    p.nq = c->n_q_heads;
+    p.nkv = c->n_kv_heads;
+    p.D = c->head_dim;
+    p.F = c->ffn;
+    p.V = c->vocab;
+    p.qd = p.nq * p.D;
+    p.nqkv = (p.nq + 2 * p.nkv) * p.D;
+    const int M = p.M;
+    auto mk = [&](int N, int Kd, int ldx) {
+        GemmShape g;
+        g.M = M;
+        g.N = N;
+        g.Kd = Kd;
+        g.ldx = ldx;
+        g.nt = M <= 16 ? 4 : 2;   // keep the M=32/64 tiles at two waves per SIMD
+        g.splits = pick_splits(N, Kd, g.nt);
+        return g;
+    };
+    p.g_qkv = mk(p.nqkv, p.H, p.H);
+    p.g_o = mk(p.H, p.qd, p.qd);
+    p.g_gu = mk(2 * p.F, p.H, p.H);
+    p.g_down = mk(p.H, p.F, p.F);
+    p.g_lm = mk(p.V, p.H, p.H);
+    p.g_lm.splits = 1;
+    p.lm_groups = gemm_groups(p.g_lm);
+    const int64_t max_keys = (int64_t)max_pages * SPEC_PAGE_SIZE;
+    p.attn_chunks = (int)((max_keys + kAttnChunk - 1) / kAttnChunk);
+    const int group = p.nq / p.nkv;
+
+    size_t part = 0;
+    for (const GemmShape *g : {&p.g_qkv, &p.g_o, &p.g_gu, &p.g_down}) {
+        const size_t b = (size_t)g->splits * M * g->N * sizeof(float);
+        if (b > part) part = b;
+    }
+    const int amax_groups = p.lm_groups > argmax_chunks(p.V) ? p.lm_groups : argmax_chunks(p.V);
+    Carver cv;
+    p.o_depth = cv.take(sizeof(int32_t) * M);
+    p.o_pos = cv.take(sizeof(int32_t) * M);
+    p.o_status = cv.take(sizeof(int32_t) * B);
+    p.o_anc = cv.take(sizeof(uint64_t) * M);
+    p.o_rope = cv.take(sizeof(float2) * M * (p.D / 2));
+    p.o_x = cv.take(sizeof(uint16_t) * M * p.H);
+    p.o_u = cv.take(sizeof(uint16_t) * M * p.H);
+    p.o_q = cv.take(sizeof(uint16_t) * M * p.qd);
+    p.o_attn = cv.take(sizeof(uint16_t) * M * p.qd);
+    p.o_h = cv.take(sizeof(uint16_t) * M * p.F);
+    p.o_part = cv.take(part);
+    p.o_po = cv.take(sizeof(float) * (size_t)B * p.nkv * p.attn_chunks * group * K * p.D);
+    p.o_pml = cv.take(sizeof(float2) * (size_t)B * p.nkv * p.attn_chunks * group * K);
+    p.o_amv = cv.take(sizeof(float) * (size_t)amax_groups * M);
+    p.o_ami = cv.take(sizeof(int32_t) * (size_t)amax_groups * M);
+    p.total = cv.off;
+    return SPEC_OK;
+}
+
+template <typename T>
+T *at(void *ws, size_t off) {
+    return reinterpret_cast<T *>(static_cast<char *>(ws) + off);
+}
+
+#define SV_TRY(x)                                  \
+    do {                                           \
+        if ((x) != hipSuccess) return SPEC_EHIP;   \
+    } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char *spec_strerror(int code) {
+    switch (code) {
+        case SPEC_OK: return "ok";
+        case SPEC_EINVAL: return "invalid argument";
+        case SPEC_EUNSUPPORTED: return "unsupported shape";
+        case SPEC_EWORKSPACE: return "workspace too small";
+        case SPEC_EHIP: return "HIP runtime error";
+        default: return "unknown error";
+    }
+}
+
+int spec_workspace_bytes(const spec_model_cfg *cfg, int batch, int k, int max_pages_per_req,
+                         size_t *bytes) {
+    if (bytes == nullptr) return SPEC_EINVAL;
+    Plan p;
+    const int rc = make_plan(cfg, batch, k, max_pages_per_req, p);
+    if (rc != SPEC_OK) return rc;
+    *bytes = p.total;
+    return SPEC_OK;
+}
+
+int spec_verify(const spec_weights *w, const spec_kv_cache *kv, const int32_t *draft_tokens,
+                const int32_t *tree_parent, const int32_t *ctx_len, int batch, int k,
+                int32_t *accepted_len, int32_t *bonus_token, int32_t *accepted_path,
+                const spec_verify_extras *extras, void *workspace, size_t workspace_bytes,
+                hipStream_t stream) {
+    if (w == nullptr || kv == nullptr || draft_tokens == nullptr || ctx_len == nullptr ||
+        accepted_len == nullptr || bonus_token == nullptr || accepted_path == nullptr ||
+        workspace == nullptr)
+        return SPEC_EINVAL;
+    if (w->layers == nullptr || w->embed == nullptr || w->final_norm == nullptr || w->lm_head == nullptr)
+        return SPEC_EINVAL;
+    if (kv->k_pool == nullptr || kv->v_pool == nullptr || kv->block_table == nullptr ||
+        kv->n_pages < 1 || kv->max_pages_per_req < 1)
+        return SPEC_EINVAL;
+    Plan p;
+    int rc = make_plan(&w->cfg, batch, k, kv->max_pages_per_req, p);
+    if (rc != SPEC_OK) return rc;
+    for (int l = 0; l < p.L; ++l) {
+        const spec_layer_weights &lw = w->layers[l];
+        if (!lw.attn_norm || !lw.w_qkv || !lw.w_o || !lw.mlp_norm || !lw.w_gate_up || !lw.w_down)
+            return SPEC_EINVAL;
+    }
+    if (workspace_bytes < p.total) return SPEC_EWORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0) return SPEC_EINVAL;
+
+    float *logits = extras ? extras->logits : nullptr;
+    int32_t *greedy = extras ? extras->greedy : nullptr;
+    bf16 *trace = extras ? static_cast<bf16 *>(extras->hidden) : nullptr;
+    const float eps = w->cfg.rms_eps;
+    const int M = p.M;
+
+    NodeInfo ni;
+    ni.depth = at<int32_t>(workspace, p.o_depth);
+    ni.pos = at<int32_t>(workspace, p.o_pos);
+    ni.status = at<int32_t>(workspace, p.o_status);
+    ni.anc = at<uint64_t>(workspace, p.o_anc);
+    ni.rope = at<float2>(workspace, p.o_rope);
+    bf16 *x = at<bf16>(workspace, p.o_x);
+    bf16 *u = at<bf16>(workspace, p.o_u);
+    bf16 *q = at<bf16>(workspace, p.o_q);
+    bf16 *attn = at<bf16>(workspace, p.o_attn);
+    bf16 *h = at<bf16>(workspace, p.o_h);
+    float *part = at<float>(workspace, p.o_part);
+    float *amv = at<float>(workspace, p.o_amv);
+    int *ami = at<int>(workspace, p.o_ami);
+    bf16 *k_pool = static_cast<bf16 *>(kv->k_pool);
+    bf16 *v_pool = static_cast<bf16 *>(kv->v_pool);
+    const int64_t layer_stride = (int64_t)kv->n_pages * p.nkv * SPEC_PAGE_SIZE * p.D;
+
+    SV_TRY(tree_prep(draft_tokens, tree_parent, ctx_len, kv->block_table, kv->max_pages_per_req,
+                     kv->n_pages, p.B, p.K, p.V, ni, stream));
+    SV_TRY(rope_table(ni, M, p.D, w->cfg.rope_theta, stream));
+    SV_TRY(embed_norm(draft_tokens, static_cast<const bf16 *>(w->embed),
+                      static_cast<const bf16 *>(w->layers[0].attn_norm), M, p.H, p.V, eps, x, u,
+                      trace, stream));
+
+    AttnArgs aa;
+    aa.q = q;
+    aa.block_table = kv->block_table;
+    aa.max_pages = kv->max_pages_per_req;
+    aa.n_pages = kv->n_pages;
+    aa.ctx_len = ctx_len;
+    aa.anc = ni.anc;
+    aa.status = ni.status;
+    aa.B = p.B;
+    aa.K = p.K;
+    aa.nq = p.nq;
+    aa.nkv = p.nkv;
+    aa.D = p.D;
+    aa.n_chunks = p.attn_chunks;
+    aa.part_o = at<float>(workspace, p.o_po);
+    aa.part_ml = at<float2>(workspace, p.o_pml);
+    aa.out = attn;
+
+    for (int l = 0; l < p.L; ++l) {
+        const spec_layer_weights &lw = w->layers[l];
+        bf16 *kl = k_pool + l * layer_stride;
+        bf16 *vl = v_pool + l * layer_stride;
+        SV_TRY(gemm_partials(p.g_qkv, u, static_cast<const bf16 *>(lw.w_qkv), part, stream));
+        SV_TRY(qkv_rope_store(part, p.g_qkv.splits, ni, ctx_len, kv->block_table,
+                              kv->max_pages_per_req, p.B, p.K, p.nq, p.nkv, p.D, q, kl, vl, stream));
+        aa.k_pool = kl;
+        aa.v_pool = vl;
+        SV_TRY(attention(aa, stream));
+        SV_TRY(gemm_partials(p.g_o, attn, static_cast<const bf16 *>(lw.w_o), part, stream));
+        SV_TRY(residual_norm(part, p.g_o.splits, M, p.H, static_cast<const bf16 *>(lw.mlp_norm),
+                             eps, x, u, nullptr, stream));
+        SV_TRY(gemm_partials(p.g_gu, u, static_cast<const bf16 *>(lw.w_gate_up), part, stream));
+        SV_TRY(swiglu(part, p.g_gu.splits, M, p.F, h, stream));
+        SV_TRY(gemm_partials(p.g_down, h, static_cast<const bf16 *>(lw.w_down), part, stream));
+        const bf16 *next_gain = l + 1 < p.L ? static_cast<const bf16 *>(w->layers[l + 1].attn_norm)
+                                            : static_cast<const bf16 *>(w->final_norm);
+        SV_TRY(residual_norm(part, p.g_down.splits, M, p.H, next_gain, eps, x, u,
+                             trace ? trace + (int64_t)(l + 1) * M * p.H : nullptr, stream));
+    }
+    SV_TRY(gemm_argmax(p.g_lm, u, static_cast<const bf16 *>(w->lm_head), logits, amv, ami, stream));
+    SV_TRY(argmax_accept(amv, ami, p.lm_groups, draft_tokens, tree_parent, ni, p.B, p.K, greedy,
+                         accepted_len, bonus_token, accepted_path, stream));
+    return SPEC_OK;
+}
+
+int spec_commit_kv(const spec_model_cfg *cfg, const spec_kv_cache *kv, const int32_t *accepted_len,
+                   const int32_t *accepted_path, int32_t *ctx_len, int batch, int k,
+                   hipStream_t stream) {
+    int rc = check_cfg(cfg);
+    if (rc != SPEC_OK) return rc;
+    if (kv == nullptr || accepted_len == nullptr || accepted_path == nullptr || ctx_len == nullptr)
+        return SPEC_EINVAL;
+    if (kv->k_pool == nullptr || kv->v_pool == nullptr || kv->block_table == nullptr ||
+        kv->n_pages < 1 || kv->max_pages_per_req < 1)
+        return SPEC_EINVAL;
+    if (batch < 1 || k < 1) return SPEC_EINVAL;
+    if (k > SPEC_MAX_K) return SPEC_EUNSUPPORTED;
+    SV_TRY(commit_kv(accepted_len, accepted_path, ctx_len, kv->block_table, kv->max_pages_per_req,
+                     kv->n_pages, cfg->n_layers, batch, k, cfg->n_kv_heads, cfg->head_dim,
+                     static_cast<bf16 *>(kv->k_pool), static_cast<bf16 *>(kv->v_pool), stream));
+    SV_TRY(commit_ctx(accepted_len, ctx_len, batch, stream));
+    return SPEC_OK;
+}
+
+static int skinny_shape(int m, int n, int kd, GemmShape &g) {
+    if (m < 1 || n < 1 || kd < 1) return SPEC_EINVAL;
+    if (kd % 32 != 0 || n % 16 != 0) return SPEC_EUNSUPPORTED;
+    g.M = m;
+    g.N = n;
+    g.Kd = kd;
+    g.ldx = kd;
+    g.nt = m <= 16 ? 4 : 2;
+    g.splits = pick_splits(n, kd, g.nt);
+    return SPEC_OK;
+}
+
+int spec_skinny_gemm_bytes(int m, int n, int kd, size_t *bytes) {
+    if (bytes == nullptr) return SPEC_EINVAL;
+    GemmShape g;
+    const int rc = skinny_shape(m, n, kd, g);
+    if (rc != SPEC_OK) return rc;
+    *bytes = (size_t)g.splits * m * n * sizeof(float);
+    return SPEC_OK;
+}
+
+int spec_skinny_gemm(const void *x, int m, int kd, const void *w, int n, float *partials,
+                     size_t partial_bytes, int *splits, hipStream_t stream) {
+    if (x == nullptr || w == nullptr || partials == nullptr || splits == nullptr) return SPEC_EINVAL;
+    GemmShape g;
+    const int rc = skinny_shape(m, n, kd, g);
+    if (rc != SPEC_OK) return rc;
+    if (partial_bytes < (size_t)g.splits * m * n * sizeof(float)) return SPEC_EWORKSPACE;
+    *splits = g.splits;
+    SV_TRY(gemm_partials(g, static_cast<const bf16 *>(x), static_cast<const bf16 *>(w), partials, stream));
+    return SPEC_OK;
+}
+
+int spec_accept_workspace_bytes(int batch, int k, int vocab, size_t *bytes) {
+    if (bytes == nullptr || batch < 1 || k < 1 || vocab < 1) return SPEC_EINVAL;
+    if (k > SPEC_MAX_K) return SPEC_EUNSUPPORTED;
+    const int M = batch * k;
+    const int nc = argmax_chunks(vocab);
+    Carver cv;
+    cv.take(sizeof(int32_t) * M);        // depth
+    cv.take(sizeof(int32_t) * M);        // pos
+    cv.take(sizeof(int32_t) * batch);    // status
+    cv.take(sizeof(uint64_t) * M);       // anc
+    cv.take(sizeof(float) * (size_t)nc * M);
+    cv.take(sizeof(int32_t) * (size_t)nc * M);
+    *bytes = cv.off;
+    return SPEC_OK;
+}
+
+int spec_accept(const float *logits, const int32_t *draft_tokens, const int32_t *tree_parent,
+                int batch, int k, int vocab, int32_t *accepted_len, int32_t *bonus_token,
+                int32_t *accepted_path, int32_t *greedy, void *workspace, size_t workspace_bytes,
+                hipStream_t stream) {
+    if (logits == nullptr || draft_tokens == nullptr || accepted_len == nullptr ||
+        bonus_token == nullptr || accepted_path == nullptr || workspace == nullptr)
+        return SPEC_EINVAL;
+    size_t need = 0;
+    int rc = spec_accept_workspace_bytes(batch, k, vocab, &need);
+    if (rc != SPEC_OK) return rc;
+    if (workspace_bytes < need) return SPEC_EWORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0) return SPEC_EINVAL;
+    const int M = batch * k;
+    const int nc = argmax_chunks(vocab);
+    Carver cv;
+    NodeInfo ni;
+    ni.depth = at<int32_t>(workspace, cv.take(sizeof(int32_t) * M));
+    ni.pos = at<int32_t>(workspace, cv.take(sizeof(int32_t) * M));
+    ni.status = at<int32_t>(workspace, cv.take(sizeof(int32_t) * batch));
+    ni.anc = at<uint64_t>(workspace, cv.take(sizeof(uint64_t) * M));
+    ni.rope = nullptr;
+    float *amv = at<float>(workspace, cv.take(sizeof(float) * (size_t)nc * M));
+    int *ami = at<int>(workspace, cv.take(sizeof(int32_t) * (size_t)nc * M));
+    SV_TRY(tree_prep(draft_tokens, tree_parent, nullptr, nullptr, 0, 0, batch, k, vocab, ni, stream));
+    SV_TRY(argmax_partials(logits, M, vocab, amv, ami, nc, stream));
+    SV_TRY(argmax_accept(amv, ami, nc, draft_tokens, tree_parent, ni, batch, k, greedy, accepted_len,
+                         bonus_token, accepted_path, stream));
+    return SPEC_OK;
+}
+
+}  // extern "C"
