@@ -61,7 +61,10 @@ def build_model(shape, device):
     fn = torch.ones(shape.hidden, dtype=torch.bfloat16, device=device)
     torch.cuda.synchronize()
     log(f"weights generated on the GPU in {time.time() - t0:.1f}s")
-    return tv.Weights(tv.ModelCfg.of(shape), embed, fn, lm, layers)
+    w = tv.Weights(tv.ModelCfg.of(shape), embed, fn, lm, layers)   # packs the projections once
+    torch.cuda.synchronize()
+    log(f"projection weights packed in {time.time() - t0:.1f}s")
+    return w
 
 
 def step_bytes(shape, batch, k, ctx):
@@ -149,8 +152,9 @@ def cpu_baseline(weights, shape, kv, tokens, parent, ctx, budget_s):
     cfg = oracle.Cfg(shape.n_layers, shape.hidden, shape.n_q_heads, shape.n_kv_heads,
                      shape.head_dim, shape.ffn, shape.vocab, shape.rms_eps, shape.rope_theta)
     W = weights.tensors
-    model = oracle.Model(cfg, host(W["embed"]), host(W["final_norm"]), host(W["lm_head"]),
-                         layer_fn=lambda l: {k: host(v) for k, v in W["layers"][l].items()})
+    R = weights.rowmajor
+    model = oracle.Model(cfg, host(W["embed"]), host(W["final_norm"]), host(R["lm_head"]),
+                         layer_fn=lambda l: {k: host(v) for k, v in R["layers"][l].items()})
     tok0 = tokens[0]
     par0 = oracle.chain(len(tok0)) if parent is None else parent[0]
     x = oracle.embed(model, tok0)

@@ -54,18 +54,21 @@ extern "C" {
 #define SPEC_MAX_K 64           /* draft nodes per request (one 64-bit ancestor mask per node) */
 
 /* Model shape. Supported: head_dim in {64, 128}; n_q_heads a multiple of n_kv_heads;
- * hidden, n_q_heads*head_dim and ffn multiples of 32; hidden <= 16384; vocab a multiple of 16.
- * The workspace must be 256-byte aligned. */
+ * hidden a multiple of 64 and <= 16384; n_q_heads*head_dim and ffn multiples of 32; vocab a
+ * multiple of 64. The workspace must be 256-byte aligned. */
 typedef struct {
     int n_layers, hidden, n_q_heads, n_kv_heads, head_dim, ffn, vocab;
     float rms_eps;              /* RMSNorm epsilon, added to mean(x^2) */
     double rope_theta;          /* RoPE base: pair j of a head turns by pos * theta^(-2j/d) */
 } spec_model_cfg;
 
-/* One decoder layer, all bf16, row-major [out][in] (DEVICE pointers):
+/* One decoder layer, all bf16 (DEVICE pointers). Logical shapes, [out][in]:
  *   attn_norm [H]; w_qkv [(nq + 2 nkv) d][H] rows = q heads, then k heads, then v heads;
  *   w_o [H][nq d]; mlp_norm [H]; w_gate_up [2F][H] rows = F gate rows, then F up rows;
- *   w_down [H][F]. */
+ *   w_down [H][F].
+ * The four projection matrices (and spec_weights.lm_head) are passed PACKED: converted once,
+ * at load time, from row-major [out][in] by spec_pack_weight. The norms and the embedding table
+ * stay row-major. */
 typedef struct {
     const void *attn_norm, *w_qkv, *w_o, *mlp_norm, *w_gate_up, *w_down;
 } spec_layer_weights;
@@ -73,9 +76,9 @@ typedef struct {
 typedef struct {
     spec_model_cfg cfg;
     const spec_layer_weights *layers;   /* HOST array of cfg.n_layers entries */
-    const void *embed;                  /* bf16 [V][H] */
+    const void *embed;                  /* bf16 [V][H], row-major */
     const void *final_norm;             /* bf16 [H] */
-    const void *lm_head;                /* bf16 [V][H] */
+    const void *lm_head;                /* bf16 [V][H], packed (spec_pack_weight) */
 } spec_weights;
 
 /* Paged KV cache, bf16. A page holds SPEC_PAGE_SIZE consecutive positions of one request.
@@ -147,6 +150,15 @@ int spec_accept(const float *logits, const int32_t *draft_tokens, const int32_t 
                 int32_t *greedy /* [batch*k] or NULL */,
                 void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Convert one projection matrix from row-major w [n][kd] bf16 into the packed layout the
+ * verify kernels stream (same size, n*kd*2 bytes, at `packed`, which must not overlap `w`).
+ * Packed order: for every tile of 16 rows (tile t = rows 16t..16t+15) and every step of 32
+ * columns (s = columns 32s..32s+31), in that nesting, 64 slots of 8 consecutive bf16; slot l
+ * holds w[16t + l%16][32s + 8(l/16) .. + 7]. One 128-bit load per lane of a 64-wide wavefront
+ * then fetches one matrix-core operand as 1 KB of contiguous memory. Needs n % 16 == 0 and
+ * kd % 32 == 0. A one-time, load-time transform; enqueued on `stream`. */
+int spec_pack_weight(const void *w, int n, int kd, void *packed, hipStream_t stream);
+
 /* The weight-streaming projection spec_verify runs for every weight matrix, on its own:
  * partials[s][m][n] = sum, over split s's share of the reduction dimension, of x[m][j]*w[n][j]
  * (bf16 operands, fp32 sums), with the split count spec_verify picks for this shape; the
@@ -154,8 +166,9 @@ int spec_accept(const float *logits, const int32_t *draft_tokens, const int32_t 
  * weight once for a few rows [SpecPilot digest, airadar.tv — summary paragraph], so this is the
  * kernel whose HBM bandwidth the pass lives on. For kernel-level tests and bandwidth
  * measurement.
- *   x: bf16 [m][kd]; w: bf16 [n][kd]; partials: fp32, spec_skinny_gemm_bytes() bytes;
- *   *splits (HOST) receives the split count. Needs kd % 32 == 0, n % 16 == 0, m >= 1. */
+ *   x: bf16 [m][kd] row-major; w: bf16 [n][kd] packed (spec_pack_weight); partials: fp32,
+ *   spec_skinny_gemm_bytes() bytes; *splits (HOST) receives the split count. Needs
+ *   kd % 32 == 0, n % 64 == 0 (n % 32 == 0 when m > 16), m >= 1. */
 int spec_skinny_gemm_bytes(int m, int n, int kd, size_t *bytes);
 int spec_skinny_gemm(const void *x, int m, int kd, const void *w, int n, float *partials,
                      size_t partial_bytes, int *splits, hipStream_t stream);

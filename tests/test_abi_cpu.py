@@ -59,7 +59,9 @@ def test_workspace_sizes_grow_with_batch_and_context():
     (tv.ModelCfg(2, 256, 4, 3, 64, 704, 1024), tv.SPEC_EUNSUPPORTED),     # 4 q heads, 3 kv heads
     (tv.ModelCfg(2, 250, 4, 2, 64, 704, 1024), tv.SPEC_EUNSUPPORTED),     # hidden % 32
     (tv.ModelCfg(2, 256, 4, 2, 64, 700, 1024), tv.SPEC_EUNSUPPORTED),     # ffn % 32
-    (tv.ModelCfg(2, 256, 4, 2, 64, 704, 1000), tv.SPEC_EUNSUPPORTED),     # vocab % 16
+    (tv.ModelCfg(2, 256, 4, 2, 64, 704, 1000), tv.SPEC_EUNSUPPORTED),     # vocab % 64
+    (tv.ModelCfg(2, 256, 4, 2, 64, 704, 1040), tv.SPEC_EUNSUPPORTED),     # vocab % 64
+    (tv.ModelCfg(2, 96, 2, 1, 64, 704, 1024), tv.SPEC_EUNSUPPORTED),      # hidden % 64
     (tv.ModelCfg(0, 256, 4, 2, 64, 704, 1024), tv.SPEC_EINVAL),
     (tv.ModelCfg(2, 256, 4, 2, 64, 704, 1024, rope_theta=-1.0), tv.SPEC_EINVAL),
 ])
@@ -115,6 +117,22 @@ def test_verify_rejects_host_visible_errors_without_launching():
     assert _raw_verify(w2, kv2, ptrs, 1, 8, 0x100000, need) == tv.SPEC_EINVAL       # NULL weight
     kv_bad = tv.KVCacheC(fake, fake, fake, 0, 9)
     assert _raw_verify(w, kv_bad, ptrs, 1, 8, 0x100000, need) == tv.SPEC_EINVAL
+
+
+def test_pack_and_skinny_gemm_reject_bad_arguments():
+    L = tv.lib()
+    fake = 0x10000
+    assert L.spec_pack_weight(None, 64, 64, fake, None) == tv.SPEC_EINVAL
+    assert L.spec_pack_weight(fake, 64, 64, fake, None) == tv.SPEC_EINVAL       # in place
+    assert L.spec_pack_weight(fake, 20, 64, fake + 4096, None) == tv.SPEC_EUNSUPPORTED
+    assert L.spec_pack_weight(fake, 64, 40, fake + 4096, None) == tv.SPEC_EUNSUPPORTED
+    n = ctypes.c_size_t(0)
+    assert L.spec_skinny_gemm_bytes(16, 40, 64, ctypes.byref(n)) == tv.SPEC_EUNSUPPORTED
+    assert L.spec_skinny_gemm_bytes(16, 48, 40, ctypes.byref(n)) == tv.SPEC_EUNSUPPORTED
+    assert L.spec_skinny_gemm_bytes(17, 32, 64, ctypes.byref(n)) == tv.SPEC_OK
+    assert L.spec_skinny_gemm_bytes(16, 64, 64, ctypes.byref(n)) == tv.SPEC_OK and n.value > 0
+    sp = ctypes.c_int(0)
+    assert L.spec_skinny_gemm(fake, 16, 64, fake, 64, fake, 4, ctypes.byref(sp), None) == tv.SPEC_EWORKSPACE
 
 
 def test_commit_and_accept_reject_bad_arguments():

@@ -65,7 +65,7 @@ def test_27b_stack_teacher_forced(stack, kind):
     k, ctx, parent, tokens, kv, ctx_rows, out = _case(shape, w, kind)
     cfg = oracle_cfg(shape)
     for l in (0, 1, 31, 62, 63):
-        lw = {nm: bits(t) for nm, t in w.tensors["layers"][l].items()}
+        lw = {nm: bits(t) for nm, t in w.rowmajor["layers"][l].items()}
         kc, vc = bits(ctx_rows[l][0]), bits(ctx_rows[l][1])
         x_in = bits(out.hidden[l])
         x_o, k_o, v_o = oracle.layer_forward(cfg, lw, kc, vc, parent, x_in)
@@ -77,7 +77,7 @@ def test_27b_stack_teacher_forced(stack, kind):
                              x_r.numpy(), f"layer {l} output"))
     # output head and greedy walk from the GPU's final residual stream: fixed tolerance
     model = oracle.Model(cfg, bits(w.tensors["embed"][:1]), bits(w.tensors["final_norm"]),
-                         bits(w.tensors["lm_head"]), layers=[])
+                         bits(w.rowmajor["lm_head"]), layers=[])
     lg = oracle.logits(model, bits(out.hidden[shape.n_layers]))
     err = check_logits(out.logits[0], lg, "output head")
     arg, margin = oracle.argmax(lg)

@@ -25,14 +25,31 @@ def setup_module(module):
         pytest.skip("no GPU")
 
 
+def test_pack_layout_matches_its_definition():
+    """Slot l of (tile t, step s) holds w[16t + l%16][32s + 8(l/16) .. +7], tiles outermost."""
+    n, kd = 48, 96
+    w = synth.randn_bf16((n, kd), 1.0, DEV, "pack")
+    p = tv.spec_pack_weight(w)
+    torch.cuda.synchronize()
+    wb, pb = bits(w), bits(p).reshape(-1)
+    k = 0
+    for t in range(n // 16):
+        for s in range(kd // 32):
+            for l in range(64):
+                r, c = 16 * t + l % 16, 32 * s + 8 * (l // 16)
+                assert np.array_equal(pb[k:k + 8], wb[r, c:c + 8]), (t, s, l)
+                k += 8
+    assert k == n * kd
+
+
 @pytest.mark.parametrize("m,n,kd", [(1, 7168, 5120), (16, 7168, 5120), (16, 5120, 17408),
                                     (16, 34816, 5120), (64, 1024, 5120), (8, 1408, 256),
-                                    (8, 256, 704), (33, 48, 96), (512, 512, 1024), (3, 16, 32)])
+                                    (8, 256, 704), (33, 64, 96), (512, 512, 1024), (3, 64, 32)])
 def test_skinny_gemm_within_summation_bound(m, n, kd):
     x = synth.randn_bf16((m, kd), 1.0, DEV, "gx", m, n, kd)
     w = synth.randn_bf16((n, kd), 0.02, DEV, "gw", m, n, kd)
     part = torch.full((tv.spec_skinny_gemm_bytes(m, n, kd) // 4,), float("nan"), device=DEV)
-    s = tv.spec_skinny_gemm(x, w, part)
+    s = tv.spec_skinny_gemm(x, tv.spec_pack_weight(w), part)
     torch.cuda.synchronize()
     p = part.view(s, m, n).cpu().numpy()
     y = p[0].copy()
@@ -51,6 +68,8 @@ def test_skinny_gemm_within_summation_bound(m, n, kd):
 
 def test_skinny_gemm_rejects_bad_shapes():
     x = torch.zeros((4, 40), dtype=torch.bfloat16, device=DEV)
-    w = torch.zeros((16, 40), dtype=torch.bfloat16, device=DEV)
+    w = torch.zeros((64, 40), dtype=torch.bfloat16, device=DEV)
     with pytest.raises(tv.SpecError):
         tv.spec_skinny_gemm(x, w, torch.zeros(1024, device=DEV))
+    with pytest.raises(tv.SpecError):
+        tv.spec_pack_weight(torch.zeros((20, 64), dtype=torch.bfloat16, device=DEV))

@@ -8,7 +8,11 @@ the entry points raises.
 
 Entry points (same names as the C ABI): ``spec_workspace_bytes``, ``spec_verify``,
 ``spec_commit_kv``, ``spec_accept_workspace_bytes``, ``spec_accept``,
-``spec_skinny_gemm_bytes``, ``spec_skinny_gemm``, ``spec_strerror``.
+``spec_pack_weight``, ``spec_skinny_gemm_bytes``, ``spec_skinny_gemm``, ``spec_strerror``.
+
+``Weights`` takes row-major bf16 tensors and packs the projection matrices once
+(``spec_pack_weight``) into buffers it owns; ``Weights.from_packed`` takes matrices already
+packed.
 """
 from __future__ import annotations
 
@@ -85,18 +89,20 @@ def lib() -> ctypes.CDLL:
                                      i32, i32, vp]
         L.spec_accept_workspace_bytes.argtypes = [i32, i32, i32, ctypes.POINTER(sz)]
         L.spec_accept.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
+        L.spec_pack_weight.argtypes = [vp, i32, i32, vp, vp]
         L.spec_skinny_gemm_bytes.argtypes = [i32, i32, i32, ctypes.POINTER(sz)]
         L.spec_skinny_gemm.argtypes = [vp, i32, i32, vp, i32, vp, sz, ctypes.POINTER(i32), vp]
         for f in (L.spec_workspace_bytes, L.spec_verify, L.spec_commit_kv,
                   L.spec_accept_workspace_bytes, L.spec_accept, L.spec_skinny_gemm_bytes,
-                  L.spec_skinny_gemm):
+                  L.spec_skinny_gemm, L.spec_pack_weight):
             f.restype = i32
         _lib = L
     return _lib
 
 
 EXPORTED = ("spec_workspace_bytes", "spec_verify", "spec_commit_kv", "spec_accept_workspace_bytes",
-            "spec_accept", "spec_skinny_gemm_bytes", "spec_skinny_gemm", "spec_strerror")
+            "spec_accept", "spec_pack_weight", "spec_skinny_gemm_bytes", "spec_skinny_gemm",
+            "spec_strerror")
 
 
 def spec_strerror(code: int) -> str:
@@ -146,19 +152,45 @@ class ModelCfg:
                         shape.head_dim, shape.ffn, shape.vocab, shape.rms_eps, shape.rope_theta)
 
 
+PACKED_KEYS = ("w_qkv", "w_o", "w_gate_up", "w_down")
+
+
+def spec_pack_weight(w: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Packed copy of a row-major bf16 [n][kd] projection matrix (same shape and size)."""
+    if out is None:
+        out = torch.empty_like(w)
+    n, kd = w.shape
+    _check(lib().spec_pack_weight(_ptr(w), n, kd, _ptr(out), _stream(stream)), "spec_pack_weight")
+    return out
+
+
 class Weights:
-    """Device weights (bf16 tensors the caller owns) and the C struct that points at them."""
+    """Device weights and the C struct that points at them. The constructor takes row-major
+    bf16 tensors and packs the projection matrices (and the output head) once; with
+    ``drop_rowmajor`` the row-major projection tensors are released after packing."""
 
     def __init__(self, cfg: ModelCfg, embed: torch.Tensor, final_norm: torch.Tensor,
-                 lm_head: torch.Tensor, layers: Sequence[dict]):
+                 lm_head: torch.Tensor, layers: Sequence[dict], packed: bool = False,
+                 drop_rowmajor: bool = False):
         if len(layers) != cfg.n_layers:
             raise ValueError("need one weight dict per layer")
         self.cfg = cfg
+        self.rowmajor = None
+        if not packed:
+            if not drop_rowmajor:
+                self.rowmajor = dict(lm_head=lm_head, layers=list(layers))
+            lm_head = spec_pack_weight(lm_head)
+            layers = [{k: (spec_pack_weight(v) if k in PACKED_KEYS else v) for k, v in lw.items()}
+                      for lw in layers]
         self.tensors = dict(embed=embed, final_norm=final_norm, lm_head=lm_head, layers=list(layers))
         self._layers = (LayerWeightsC * cfg.n_layers)(
             *[LayerWeightsC(*[_ptr(lw[k]) for k in LAYER_KEYS]) for lw in layers])
         self.c = WeightsC(cfg.c(), ctypes.cast(self._layers, ctypes.POINTER(LayerWeightsC)),
                           _ptr(embed), _ptr(final_norm), _ptr(lm_head))
+
+    @staticmethod
+    def from_packed(cfg: ModelCfg, embed, final_norm, lm_head_packed, layers_packed) -> "Weights":
+        return Weights(cfg, embed, final_norm, lm_head_packed, layers_packed, packed=True)
 
 
 class PagedKV:
@@ -243,7 +275,8 @@ def spec_skinny_gemm_bytes(m: int, n: int, kd: int) -> int:
 
 
 def spec_skinny_gemm(x: torch.Tensor, w: torch.Tensor, partials: torch.Tensor, stream=None) -> int:
-    """partials[s][m][n] for x [m][kd], w [n][kd] (bf16); returns the split count."""
+    """partials[s][m][n] for x [m][kd] (bf16, row-major), w [n][kd] (bf16, packed by
+    spec_pack_weight); returns the split count."""
     m, kd = x.shape
     n = w.shape[0]
     splits = ctypes.c_int(0)

@@ -48,21 +48,39 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
     const int QT = (R + 15) >> 4;
 
     // ---- stage the chunk: K rows as stored, V already transposed in the page ---------------
-    for (int p = 0; p < CH / 16; ++p) {
-        const bool live = p < npages;
-        const int page = live ? block_table[(int64_t)b * max_pages + (kb >> 4) + p] : 0;
-        const bf16 *kp = k_pool + ((int64_t)page * nkv + g) * 16 * D;
-        const bf16 *vp = v_pool + ((int64_t)page * nkv + g) * D * 16;
-        for (int e = threadIdx.x * 8; e < 16 * D; e += 256 * 8) {
-            const int row = e / D, col = e % D;
-            bf16x8 kv = live ? *(const bf16x8 *)(kp + e) : bf16x8{};
-            *(bf16x8 *)&Ks[(p * 16 + row) * KP + col] = kv;
-            const int d = e >> 4, slot = e & 15;
-            bf16x8 vv = live ? *(const bf16x8 *)(vp + e) : bf16x8{};
+    // Every thread issues all of its page loads before the first LDS store, so the chunk's
+    // 2 x 8 x 16 B per thread are in flight together.
+    {
+        constexpr int NP = CH / 16;
+        const int e = threadIdx.x * 8;           // element offset inside a 16 x D page
+        const bool has = e < 16 * D;
+        int pages[NP];
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                if (p * 16 + slot + j >= nvalid) vv[j] = (bf16)0.0f;   // never multiply stale data
-            *(bf16x8 *)&Vt[d * VP + p * 16 + slot] = vv;
+        for (int p = 0; p < NP; ++p)
+            pages[p] = (has && p < npages) ? block_table[(int64_t)b * max_pages + (kb >> 4) + p] : -1;
+        bf16x8 kr[NP], vr[NP];
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            if (pages[p] >= 0) {
+                kr[p] = *(const bf16x8 *)(k_pool + ((int64_t)pages[p] * nkv + g) * 16 * D + e);
+                vr[p] = *(const bf16x8 *)(v_pool + ((int64_t)pages[p] * nkv + g) * D * 16 + e);
+            } else {
+                kr[p] = bf16x8{};
+                vr[p] = bf16x8{};
+            }
+        }
+        if (has) {
+            const int row = e / D, col = e % D;
+            const int d = e >> 4, slot = e & 15;
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+                *(bf16x8 *)&Ks[(p * 16 + row) * KP + col] = kr[p];
+                bf16x8 vv = vr[p];
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    if (p * 16 + slot + j >= nvalid) vv[j] = (bf16)0.0f;   // never multiply stale data
+                *(bf16x8 *)&Vt[d * VP + p * 16 + slot] = vv;
+            }
         }
     }
     __syncthreads();
@@ -147,31 +165,45 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
     }
 }
 
-// Merge the chunk partials of one (node, q head): o = sum_c 2^(m_c - m*) O_c / sum_c 2^(m_c - m*) l_c.
+// Merge the chunk partials of one node: o = sum_c 2^(m_c - m*) O_c / sum_c 2^(m_c - m*) l_c, one
+// pass with a running maximum. A thread owns 4 consecutive elements of one head.
 template <int D>
-__global__ __launch_bounds__(D) void attn_combine_kernel(
+__global__ __launch_bounds__(256) void attn_combine_kernel(
     const float *__restrict__ part_o, const float2 *__restrict__ part_ml,
     const int32_t *__restrict__ ctx_len, const int32_t *__restrict__ status, int K, int nq,
     int nkv, int n_chunks, bf16 *__restrict__ out) {
-    const int row = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
+    constexpr int TPH = D / 4;           // threads per head
+    constexpr int HPB = 256 / TPH;       // heads per block
+    const int row = blockIdx.x;
+    const int h = blockIdx.y * HPB + threadIdx.x / TPH;
+    const int d4 = (threadIdx.x % TPH) * 4;
+    if (h >= nq) return;
     const int b = row / K, tok = row % K;
-    bf16 *dst = out + ((int64_t)row * nq + h) * D + d;
-    if (status[b] != 0) { *dst = (bf16)0.0f; return; }
+    bf16 *dst = out + ((int64_t)row * nq + h) * D + d4;
+    if (status[b] != 0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dst[j] = (bf16)0.0f;
+        return;
+    }
     const int group = nq / nkv, g = h / group, hh = h % group;
     const int R = group * K, rho = hh * K + tok;
     const int nc = (ctx_len[b] + K + kAttnChunk - 1) / kAttnChunk;
     const int64_t base = ((int64_t)b * nkv + g) * n_chunks * R + rho;
-    float mstar = -INFINITY;
-    for (int c = 0; c < nc; ++c) mstar = fmaxf(mstar, part_ml[base + (int64_t)c * R].x);
-    float num = 0.f, den = 0.f;
+    float m = -INFINITY, l = 0.f;
+    floatx4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
     for (int c = 0; c < nc; ++c) {
         const float2 ml = part_ml[base + (int64_t)c * R];
+        const floatx4 oc = *(const floatx4 *)(part_o + (base + (int64_t)c * R) * D + d4);
         if (ml.x == -INFINITY) continue;
-        const float w = exp2f(ml.x - mstar);
-        den += w * ml.y;
-        num += w * part_o[(base + (int64_t)c * R) * D + d];
+        const float mn = fmaxf(m, ml.x);
+        const float a = exp2f(m - mn), w = exp2f(ml.x - mn);
+        l = l * a + ml.y * w;
+        o = o * a + oc * w;
+        m = mn;
     }
-    *dst = to_bf(num / den);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dst[j] = to_bf(o[j] / l);
 }
 
 hipError_t attention(const AttnArgs &a, hipStream_t st) {
@@ -183,16 +215,16 @@ hipError_t attention(const AttnArgs &a, hipStream_t st) {
                            a.n_chunks, scale_log2, a.part_o, a.part_ml);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(attn_combine_kernel<128>, dim3(a.B * a.K, a.nq), dim3(128), 0, st, a.part_o,
-                           a.part_ml, a.ctx_len, a.status, a.K, a.nq, a.nkv, a.n_chunks, a.out);
+        hipLaunchKernelGGL(attn_combine_kernel<128>, dim3(a.B * a.K, (a.nq + 7) / 8), dim3(256), 0, st,
+                           a.part_o, a.part_ml, a.ctx_len, a.status, a.K, a.nq, a.nkv, a.n_chunks, a.out);
     } else {
         hipLaunchKernelGGL(attn_partial_kernel<64>, grid, dim3(256), 0, st, a.q, a.k_pool, a.v_pool,
                            a.block_table, a.max_pages, a.ctx_len, a.anc, a.status, a.K, a.nq, a.nkv,
                            a.n_chunks, scale_log2, a.part_o, a.part_ml);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(attn_combine_kernel<64>, dim3(a.B * a.K, a.nq), dim3(64), 0, st, a.part_o,
-                           a.part_ml, a.ctx_len, a.status, a.K, a.nq, a.nkv, a.n_chunks, a.out);
+        hipLaunchKernelGGL(attn_combine_kernel<64>, dim3(a.B * a.K, (a.nq + 15) / 16), dim3(256), 0, st,
+                           a.part_o, a.part_ml, a.ctx_len, a.status, a.K, a.nq, a.nkv, a.n_chunks, a.out);
     }
     return hipGetLastError();
 }

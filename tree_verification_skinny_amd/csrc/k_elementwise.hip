@@ -1,7 +1,7 @@
 // k_elementwise.hip — the small kernels around the GEMMs and attention of the verify pass:
-// draft-tree bookkeeping, embedding + RMSNorm, split-K reduction fused with RoPE and the KV
-// tail write, residual add + RMSNorm, SwiGLU, the vocab-wide greedy choice with the accepted-path
-// walk, and the commit of the accepted path's KV rows.
+// draft-tree bookkeeping, RoPE angles, the embedding gather (with the per-row sums of squares the
+// first RMSNorm needs), the vocab-wide greedy choice with the accepted-path walk, and the commit
+// of the accepted path's KV rows.
 //
 // Lossless greedy verification: a draft token is accepted only if it equals the target's greedy
 // choice after its parent, and only along a path whose every earlier token was accepted
@@ -95,168 +95,30 @@ hipError_t rope_table(const NodeInfo &ni, int M, int D, double theta, hipStream_
     return hipGetLastError();
 }
 
-// ---- embedding + first RMSNorm ----------------------------------------------------------------
-// RMSNorm: u = bf16((x / sqrt(mean(x^2) + eps)) * g), sum of squares in fp32. Each thread
-// re-reads its own elements for the second pass (cache resident) instead of holding them.
-__global__ __launch_bounds__(256) void embed_norm_kernel(const int32_t *__restrict__ tokens,
-                                                         const bf16 *__restrict__ embed,
-                                                         const bf16 *__restrict__ gain, int H,
-                                                         int vocab, float eps,
-                                                         bf16 *__restrict__ x, bf16 *__restrict__ u,
-                                                         bf16 *__restrict__ trace) {
-    __shared__ float red[4];
-    const int row = blockIdx.x;
+// ---- embedding gather + per-row sums of squares over 64-column groups -------------------------
+// The first projection applies RMSNorm on its operand load from these sums.
+__global__ __launch_bounds__(64) void embed_kernel(const int32_t *__restrict__ tokens,
+                                                   const bf16 *__restrict__ table, int M, int H,
+                                                   int vocab, bf16 *__restrict__ x,
+                                                   float *__restrict__ ss, bf16 *__restrict__ trace) {
+    const int row = blockIdx.x, g = blockIdx.y, lane = threadIdx.x;   // one wave per 64 columns
     int tok = tokens[row];
     if (tok < 0 || tok >= vocab) tok = 0;   // the request is already marked bad; stay in bounds
-    const bf16 *src = embed + (int64_t)tok * H;
-    float ss = 0.f;
-    for (int e = threadIdx.x * 8; e < H; e += 256 * 8) {
-        bf16x8 xv = *(const bf16x8 *)(src + e);
-        *(bf16x8 *)(x + (int64_t)row * H + e) = xv;
-        if (trace) *(bf16x8 *)(trace + (int64_t)row * H + e) = xv;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) ss += to_f(xv[j]) * to_f(xv[j]);
-    }
-    ss = block_sum_256(ss, red);
-    const float inv = 1.0f / sqrtf(ss / (float)H + eps);
-    for (int e = threadIdx.x * 8; e < H; e += 256 * 8) {
-        bf16x8 xv = *(const bf16x8 *)(src + e), gv = *(const bf16x8 *)(gain + e), uv;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) uv[j] = to_bf((to_f(xv[j]) * inv) * to_f(gv[j]));
-        *(bf16x8 *)(u + (int64_t)row * H + e) = uv;
-    }
+    const int col = g * 64 + lane;
+    const bf16 v = table[(int64_t)tok * H + col];
+    x[(int64_t)row * H + col] = v;
+    if (trace) trace[(int64_t)row * H + col] = v;
+    const float f = to_f(v);
+    const float sum = wave_sum(f * f);
+    if (lane == 0) ss[(int64_t)g * M + row] = sum;
 }
 
-hipError_t embed_norm(const int32_t *tokens, const bf16 *embed, const bf16 *gain, int M, int H,
-                      int vocab, float eps, bf16 *x, bf16 *u, bf16 *trace, hipStream_t st) {
-    hipLaunchKernelGGL(embed_norm_kernel, dim3(M), dim3(256), 0, st, tokens, embed, gain, H, vocab,
-                       eps, x, u, trace);
-    return hipGetLastError();
-}
+int embed_ss_groups(int H) { return H / 64; }
 
-// ---- QKV: split-K sum, bf16, RoPE on q and k, k and v into the request's cache pages -------
-// Node i (local index il of request b) goes to cache slot ctx + il; its rotation angle uses
-// its tree position ctx + depth(i).
-__global__ __launch_bounds__(256) void qkv_rope_store_kernel(
-    const float *__restrict__ P, int splits, int M, const float2 *__restrict__ rope,
-    const int32_t *__restrict__ status, const int32_t *__restrict__ ctx_len,
-    const int32_t *__restrict__ block_table, int max_pages, int K, int nq, int nkv, int D,
-    bf16 *__restrict__ q, bf16 *__restrict__ k_pool, bf16 *__restrict__ v_pool) {
-#pragma clang fp contract(off)
-    const int row = blockIdx.x;
-    const int b = row / K, il = row % K;
-    const bool ok = status[b] == 0;
-    const int N = (nq + 2 * nkv) * D;
-    const int half = D / 2;
-    int page = 0, so = 0;
-    if (ok) {
-        const int slot = ctx_len[b] + il;
-        page = page_of(block_table, max_pages, b, slot);
-        so = slot & 15;
-    }
-    const float *Pr = P + (int64_t)row * N;
-    const int64_t pstride = (int64_t)M * N;
-    const int npairs = (nq + nkv) * half;
-    for (int w = threadIdx.x; w < npairs; w += 256) {
-        const int hh = w / half, j = w % half;
-        const int c1 = hh * D + j, c2 = c1 + half;
-        float a = 0.f, bb = 0.f;
-        for (int s = 0; s < splits; ++s) { a += Pr[s * pstride + c1]; bb += Pr[s * pstride + c2]; }
-        a = round_bf(a);
-        bb = round_bf(bb);
-        const float2 cs = rope[(int64_t)row * half + j];
-        const float ra = a * cs.x - bb * cs.y;
-        const float rb = bb * cs.x + a * cs.y;
-        if (hh < nq) {
-            bf16 *qh = q + ((int64_t)row * nq + hh) * D;
-            qh[j] = to_bf(ra);
-            qh[j + half] = to_bf(rb);
-        } else if (ok) {
-            bf16 *kr = k_pool + (((int64_t)page * nkv + (hh - nq)) * 16 + so) * D;
-            kr[j] = to_bf(ra);
-            kr[j + half] = to_bf(rb);
-        }
-    }
-    if (!ok) return;
-    const int vbase = (nq + nkv) * D;
-    for (int w = threadIdx.x; w < nkv * D; w += 256) {
-        float a = 0.f;
-        for (int s = 0; s < splits; ++s) a += Pr[s * pstride + vbase + w];
-        const int g = w / D, dd = w % D;
-        v_pool[(((int64_t)page * nkv + g) * D + dd) * 16 + so] = to_bf(a);
-    }
-}
-
-hipError_t qkv_rope_store(const float *P, int splits, const NodeInfo &ni, const int32_t *ctx_len,
-                          const int32_t *block_table, int max_pages, int B, int K, int nq,
-                          int nkv, int D, bf16 *q, bf16 *k_pool, bf16 *v_pool, hipStream_t st) {
-    hipLaunchKernelGGL(qkv_rope_store_kernel, dim3(B * K), dim3(256), 0, st, P, splits, B * K,
-                       ni.rope, ni.status, ctx_len, block_table, max_pages, K, nq, nkv, D, q,
-                       k_pool, v_pool);
-    return hipGetLastError();
-}
-
-// ---- projection split-K sum, residual add, RMSNorm -------------------------------------------
-// x = bf16(x + bf16(sum_s P[s])), splits added in index order; u = RMSNorm(x) * g.
-__global__ __launch_bounds__(256) void residual_norm_kernel(const float *__restrict__ P, int splits,
-                                                            int M, int H,
-                                                            const bf16 *__restrict__ gain,
-                                                            float eps, bf16 *__restrict__ x,
-                                                            bf16 *__restrict__ u,
-                                                            bf16 *__restrict__ trace) {
-    __shared__ float red[4];
-    const int row = blockIdx.x;
-    const int64_t pstride = (int64_t)M * H;
-    bf16 *xr = x + (int64_t)row * H;
-    float ss = 0.f;
-    for (int e = threadIdx.x * 4; e < H; e += 256 * 4) {
-        floatx4 y = *(const floatx4 *)(P + (int64_t)row * H + e);
-        for (int s = 1; s < splits; ++s) y += *(const floatx4 *)(P + s * pstride + (int64_t)row * H + e);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float xn = round_bf(to_f(xr[e + j]) + round_bf(y[j]));
-            ss += xn * xn;
-            xr[e + j] = to_bf(xn);
-            if (trace) trace[(int64_t)row * H + e + j] = to_bf(xn);
-        }
-    }
-    ss = block_sum_256(ss, red);
-    const float inv = 1.0f / sqrtf(ss / (float)H + eps);
-    for (int e = threadIdx.x * 4; e < H; e += 256 * 4) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) u[(int64_t)row * H + e + j] = to_bf((to_f(xr[e + j]) * inv) * to_f(gain[e + j]));
-    }
-}
-
-hipError_t residual_norm(const float *P, int splits, int M, int H, const bf16 *gain, float eps,
-                         bf16 *x, bf16 *u, bf16 *trace, hipStream_t st) {
-    hipLaunchKernelGGL(residual_norm_kernel, dim3(M), dim3(256), 0, st, P, splits, M, H, gain, eps,
-                       x, u, trace);
-    return hipGetLastError();
-}
-
-// ---- SwiGLU: h = bf16(silu(gate) * up), gate and up rounded to bf16 first -------------------
-__global__ __launch_bounds__(256) void swiglu_kernel(const float *__restrict__ P, int splits, int M,
-                                                     int F, bf16 *__restrict__ h) {
-    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= (int64_t)M * F) return;
-    const int64_t row = idx / F, n = idx % F;
-    const int64_t pstride = (int64_t)M * 2 * F;
-    float ga = 0.f, up = 0.f;
-    for (int s = 0; s < splits; ++s) {
-        ga += P[s * pstride + row * 2 * F + n];
-        up += P[s * pstride + row * 2 * F + F + n];
-    }
-    ga = round_bf(ga);
-    up = round_bf(up);
-    const float silu = ga / (1.0f + expf(-ga));
-    h[idx] = to_bf(silu * up);
-}
-
-hipError_t swiglu(const float *P, int splits, int M, int F, bf16 *h, hipStream_t st) {
-    const int64_t n = (int64_t)M * F;
-    hipLaunchKernelGGL(swiglu_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, P, splits,
-                       M, F, h);
+hipError_t embed(const int32_t *tokens, const bf16 *table, int M, int H, int vocab, bf16 *x,
+                 float *ss, bf16 *trace, hipStream_t st) {
+    hipLaunchKernelGGL(embed_kernel, dim3(M, H / 64), dim3(64), 0, st, tokens, table, M, H, vocab, x,
+                       ss, trace);
     return hipGetLastError();
 }
 

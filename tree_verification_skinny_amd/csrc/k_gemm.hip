@@ -1,65 +1,161 @@
 // k_gemm.hip — weight-streaming skinny GEMM for the verify pass (M = draft nodes, 1..64 rows
-// per launch) on gfx950 MFMA.
+// per launch) on gfx950 MFMA, with the split-K reduction and the consumer's elementwise work
+// fused into its tail.
 //
 // At batch 1 the verify pass reads every target weight for a handful of tokens, so it is bound
 // by HBM, not by arithmetic [SpecPilot digest, airadar.tv — summary paragraph]. The kernel is
 // built around the weight stream:
-//   * Y^T = W . X^T on v_mfma_f32_16x16x32_bf16: the weight W [N][Kd] is the A operand, so each
-//     lane loads its A fragment (8 consecutive bf16 of one weight row = one 128-bit load) straight
-//     from HBM into registers; no LDS round trip for data used exactly once.
-//   * The activations X [M][Kd] (tiny, cache resident) are the B operand, loaded with the same
-//     K-permutation as W, so any K order inside a 32-step is consistent between A and B.
-//   * A workgroup (4 waves) owns 16*NT weight rows and one K range; its waves interleave over
-//     32-wide K steps so that at any moment the 4 waves read 4 adjacent 64-byte pieces of each
-//     row. The 4 waves' sums are added in LDS in a fixed order (w0+w1+w2+w3), and K splits go to
-//     separate partial buffers that the consumer adds in split order: results do not depend on
-//     timing.
+//   * Y^T = W . X^T on v_mfma_f32_16x16x32_bf16. The weight is the A operand, and it is stored
+//     pre-packed in MFMA fragment order (see spec_pack_weight): fragment (tile of 16 rows,
+//     32-wide K step) is 1 KB, lane l's 16 bytes are W[16 tile + l%16][32 step + 8(l/16) .. +7],
+//     and a tile's K steps follow each other. One 128-bit load per lane reads a whole fragment
+//     as 1 KB of contiguous HBM, straight into the registers the MFMA consumes.
+//   * The activations X [M][Kd] (cache resident) are the B operand, loaded with the same K order.
+//     Where the consumer of a projection is an RMSNorm, the norm is applied on this load
+//     (x * rsqrt(mean x^2 + eps) * g, rounded to bf16), from per-row sums of squares the
+//     producer left behind, so no separate norm pass touches the activations.
+//   * A workgroup of W waves (4 or 8) owns NT weight tiles over the whole K range; its waves
+//     interleave over the 32-wide K steps (so together they read each tile front to back) and
+//     add their sums in LDS in wave order. No partial result leaves the workgroup: no split-K
+//     buffers, no cross-workgroup synchronisation, and results do not depend on timing. W is
+//     picked per projection so that a launch keeps roughly 2000 waves streaming.
+//   * Epilogues: RoPE + q/K/V store into the paged cache (QKV), residual add + per-row sum of
+//     squares (O and down projections), SwiGLU (gate/up), and the per-tile greedy maximum of the
+//     output head. Tile groups are laid out so that every pair an epilogue needs (RoPE's j and
+//     j + d/2, SwiGLU's gate n and up n) sits in the same lane.
 // MFMA lane layout (16x16x32): lane l supplies A row l%16, K elements 8*(l/16)..+7, and B
 // column l%16, the same K elements; it receives D rows 4*(l/16)..+3 of column l%16.
 #include "kernels.hpp"
 
 namespace sv {
 
+// ---- packing ------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void pack_kernel(const bf16 *__restrict__ w, int n, int kd,
+                                                   bf16 *__restrict__ out) {
+    // one thread per 16-byte lane slot: (tile, step, lane)
+    const int64_t steps = kd / 32;
+    const int64_t total = (int64_t)(n / 16) * steps * 64;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+        const int lane = (int)(i & 63);
+        const int64_t frag = i >> 6;
+        const int64_t tile = frag / steps, step = frag % steps;
+        const int64_t row = tile * 16 + (lane & 15);
+        const int64_t col = step * 32 + 8 * (lane >> 4);
+        *(bf16x8 *)(out + i * 8) = *(const bf16x8 *)(w + row * kd + col);
+    }
+}
+
+hipError_t pack_weight(const bf16 *w, int n, int kd, bf16 *out, hipStream_t st) {
+    const int64_t total = (int64_t)(n / 16) * (kd / 32) * 64;
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(pack_kernel, dim3((unsigned)blocks), dim3(256), 0, st, w, n, kd, out);
+    return hipGetLastError();
+}
+
+// ---- column layout of a tile group --------------------------------------------------------------
+// Contiguous for plain outputs; paired halves for RoPE (j with j + d/2 inside each head) and for
+// SwiGLU (gate column n with up column F + n).
+template <int NT, int EPI>
+__device__ __forceinline__ int tile_col(int ng, int t, int D, int F) {
+    constexpr int PH = 8 * NT;   // columns in each half of a paired group
+    if constexpr (EPI == EPI_QKV) {
+        const int half = D / 2, per_head = half / PH;
+        const int c0 = (ng / per_head) * D + (ng % per_head) * PH;
+        return t < NT / 2 ? c0 + 16 * t : c0 + half + 16 * (t - NT / 2);
+    } else if constexpr (EPI == EPI_SWIGLU) {
+        return t < NT / 2 ? ng * PH + 16 * t : F + ng * PH + 16 * (t - NT / 2);
+    } else {
+        return ng * 16 * NT + 16 * t;
+    }
+}
+
 template <int NT, int MT>
 struct Acc {
     floatx4 v[NT][MT];
 };
 
-// Main loop shared by both epilogues: accumulates this wave's K steps into acc.
-template <int NT, int MT, int U>
-__device__ __forceinline__ void skinny_mainloop(const bf16 *__restrict__ X, int ldx, int M,
-                                                const bf16 *__restrict__ W, int N, int Kd, int n0,
-                                                int s_begin, int s_end, Acc<NT, MT> &acc) {
+template <int NT, int MT, int W, int EPI, bool NORM>
+__global__ __launch_bounds__(64 * W) void gemm_kernel(GemmIn in, const bf16 *__restrict__ Wp,
+                                                      int N, int Kd, GemmEpi ep) {
+    __shared__ floatx4 red[(W - 1) * NT * MT * 64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r16 = lane & 15, grp = lane >> 4;
+    const int ng = blockIdx.x;
+    const int S = Kd >> 5;
+    const int M = in.M;            // rows in this launch (a chunk of at most 64)
+    const int m0 = in.m0;          // first global row of the chunk
+
     const bf16 *wp[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-        int n = min(n0 + 16 * t + r16, N - 1);
-        wp[t] = W + (int64_t)n * Kd + grp * 8;
+        const int tile = tile_col<NT, EPI>(ng, t, ep.D, ep.F) >> 4;
+        wp[t] = Wp + (((int64_t)tile * S) * 64 + lane) * 8;
     }
     const bf16 *xp[MT];
+    float inv[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-        int m = min(16 * mt + r16, M - 1);
-        xp[mt] = X + (int64_t)m * ldx + grp * 8;
+        const int m = min(16 * mt + r16, M - 1);
+        xp[mt] = in.X + (int64_t)(m0 + m) * in.ldx + grp * 8;
+        inv[mt] = 1.f;
     }
+    if constexpr (NORM) {
+        // RMS of each row from the producer's per-group sums of squares: every wave adds a
+        // strided share of the groups, then the shares are added in wave order.
+        __shared__ float ssr[MT][W][16];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const int m = min(16 * mt + r16, M - 1);
+            float part = 0.f;
+            for (int g = wave * 4 + grp; g < in.ss_groups; g += 4 * W)
+                part += in.ss[(int64_t)g * in.M_total + m0 + m];
+            part += __shfl_xor(part, 16, 64);
+            part += __shfl_xor(part, 32, 64);
+            if (grp == 0) ssr[mt][wave][r16] = part;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            float tot = 0.f;
+            for (int w = 0; w < W; ++w) tot += ssr[mt][w][r16];
+            inv[mt] = 1.0f / sqrtf(tot / (float)in.H + in.eps);
+        }
+    }
+    const bf16 *gp = in.gain + grp * 8;
+
+    auto load_b = [&](int step, int mt) -> bf16x8 {
+        const bf16x8 xv = *(const bf16x8 *)(xp[mt] + step * 32);
+        if constexpr (!NORM) {
+            return xv;
+        } else {
+            const bf16x8 gv = *(const bf16x8 *)(gp + step * 32);
+            bf16x8 u;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) u[j] = to_bf((to_f(xv[j]) * inv[mt]) * to_f(gv[j]));
+            return u;
+        }
+    };
+
+    Acc<NT, MT> acc;
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc.v[t][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    int s = s_begin + wave;
-    for (; s + 4 * (U - 1) < s_end; s += 4 * U) {
+    constexpr int U = (NT * MT >= 8) ? 2 : 4;   // K steps in flight per wave
+    int s = wave;
+    for (; s + W * (U - 1) < S; s += W * U) {
         bf16x8 a[U][NT], b[U][MT];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int k = (s + 4 * u) << 5;
 #pragma unroll
-            for (int t = 0; t < NT; ++t) a[u][t] = *(const bf16x8 *)(wp[t] + k);
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) b[u][mt] = *(const bf16x8 *)(xp[mt] + k);
+            for (int t = 0; t < NT; ++t) a[u][t] = *(const bf16x8 *)(wp[t] + (int64_t)(s + W * u) * 512);
         }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) b[u][mt] = load_b(s + W * u, mt);
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
@@ -67,24 +163,19 @@ __device__ __forceinline__ void skinny_mainloop(const bf16 *__restrict__ X, int 
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) acc.v[t][mt] = mfma16x16x32(a[u][t], b[u][mt], acc.v[t][mt]);
     }
-    for (; s < s_end; s += 4) {
-        const int k = s << 5;
+    for (; s < S; s += W) {
         bf16x8 a[NT], b[MT];
 #pragma unroll
-        for (int t = 0; t < NT; ++t) a[t] = *(const bf16x8 *)(wp[t] + k);
+        for (int t = 0; t < NT; ++t) a[t] = *(const bf16x8 *)(wp[t] + (int64_t)s * 512);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) b[mt] = *(const bf16x8 *)(xp[mt] + k);
+        for (int mt = 0; mt < MT; ++mt) b[mt] = load_b(s, mt);
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) acc.v[t][mt] = mfma16x16x32(a[t], b[mt], acc.v[t][mt]);
     }
-}
 
-// Adds the four waves' accumulators in LDS (w0 + w1 + w2 + w3); the total lands in wave 0.
-template <int NT, int MT>
-__device__ __forceinline__ void reduce_waves(Acc<NT, MT> &acc, floatx4 *red) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // ---- the waves' sums, in wave order ------------------------------------------------------
     if (wave > 0) {
 #pragma unroll
         for (int t = 0; t < NT; ++t)
@@ -92,159 +183,218 @@ __device__ __forceinline__ void reduce_waves(Acc<NT, MT> &acc, floatx4 *red) {
             for (int mt = 0; mt < MT; ++mt) red[((wave - 1) * NT * MT + t * MT + mt) * 64 + lane] = acc.v[t][mt];
     }
     __syncthreads();
-    if (wave == 0) {
+    if (wave != 0) return;
+    for (int w = 0; w < W - 1; ++w)
 #pragma unroll
-        for (int w = 0; w < 3; ++w)
+        for (int t = 0; t < NT; ++t)
 #pragma unroll
-            for (int t = 0; t < NT; ++t)
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
-                    floatx4 o = red[(w * NT * MT + t * MT + mt) * 64 + lane];
-                    acc.v[t][mt] += o;
-                }
-    }
-}
+            for (int mt = 0; mt < MT; ++mt) acc.v[t][mt] += red[(w * NT * MT + t * MT + mt) * 64 + lane];
 
-template <int NT, int MT>
-__global__ __launch_bounds__(256) void gemm_partials_kernel(const bf16 *__restrict__ X, int ldx,
-                                                            int M, int m_total, int m0,
-                                                            const bf16 *__restrict__ W, int N,
-                                                            int Kd, int n_groups, int ksteps,
-                                                            float *__restrict__ P) {
-    extern __shared__ floatx4 red[];
-    const int ng = blockIdx.x % n_groups;
-    const int split = blockIdx.x / n_groups;
-    const int n0 = ng * 16 * NT;
-    const int s_begin = split * ksteps;
-    const int s_end = min(s_begin + ksteps, Kd >> 5);
-    constexpr int U = (NT * MT >= 8) ? 2 : 4;
-    Acc<NT, MT> acc;
-    skinny_mainloop<NT, MT, U>(X, ldx, M, W, N, Kd, n0, s_begin, s_end, acc);
-    reduce_waves<NT, MT>(acc, red);
-    if ((threadIdx.x >> 6) != 0) return;
-    const int lane = threadIdx.x & 63, r16 = lane & 15, grp = lane >> 4;
+    int col[NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-        const int n = n0 + 16 * t + 4 * grp;
-        if (n0 + 16 * t >= N) continue;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const int m = 16 * mt + r16;
-            if (m < M) *(floatx4 *)(P + ((int64_t)split * m_total + m0 + m) * N + n) = acc.v[t][mt];
-        }
-    }
-}
+    for (int t = 0; t < NT; ++t) col[t] = tile_col<NT, EPI>(ng, t, ep.D, ep.F) + 4 * grp;
 
-template <int NT, int MT>
-__global__ __launch_bounds__(256) void gemm_argmax_kernel(const bf16 *__restrict__ X, int ldx,
-                                                          int M, int m_total, int m0,
-                                                          const bf16 *__restrict__ W, int N,
-                                                          int Kd, int n_groups,
-                                                          float *__restrict__ logits,
-                                                          float *__restrict__ amax_val,
-                                                          int *__restrict__ amax_idx) {
-    extern __shared__ floatx4 red[];
-    const int ng = blockIdx.x;
-    const int n0 = ng * 16 * NT;
-    constexpr int U = (NT * MT >= 8) ? 2 : 4;
-    Acc<NT, MT> acc;
-    skinny_mainloop<NT, MT, U>(X, ldx, M, W, N, Kd, n0, 0, Kd >> 5, acc);
-    reduce_waves<NT, MT>(acc, red);
-    if ((threadIdx.x >> 6) != 0) return;
-    const int lane = threadIdx.x & 63, r16 = lane & 15, grp = lane >> 4;
+    // ---- epilogues ------------------------------------------------------------------------------
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
         const int m = 16 * mt + r16;
-        float bv = -INFINITY;
-        int bi = 0x7fffffff;
+        const bool live = m < M;
+        const int row = m0 + m;
+        if constexpr (EPI == EPI_PLAIN) {
+            if (live) {
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            const int n = n0 + 16 * t + 4 * grp;
-            if (n0 + 16 * t >= N) continue;
-            if (logits != nullptr && m < M) *(floatx4 *)(logits + (int64_t)(m0 + m) * N + n) = acc.v[t][mt];
+                for (int t = 0; t < NT; ++t) *(floatx4 *)(ep.y + (int64_t)row * N + col[t]) = acc.v[t][mt];
+            }
+        } else if constexpr (EPI == EPI_QKV) {
+#pragma clang fp contract(off)
+            if (!live) continue;
+            const int b = row / ep.K, il = row % ep.K;
+            const bool ok = ep.status[b] == 0;
+            const int half = ep.D / 2;
+            int page = 0, slot = 0;
+            if (ok) {
+                const int pos = ep.ctx_len[b] + il;
+                page = page_of(ep.block_table, ep.max_pages, b, pos);
+                slot = pos & 15;
+            }
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                if (better(acc.v[t][mt][j], n + j, bv, bi)) { bv = acc.v[t][mt][j]; bi = n + j; }
-        }
-        // the 4 lanes holding column m: lane, lane ^ 16, lane ^ 32, lane ^ 48
+            for (int t = 0; t < NT / 2; ++t) {
+                const int head = col[t] / ep.D, jj = col[t] % ep.D;   // jj < d/2, 4 columns
+                bf16 lo[4], hi[4];
+                if (head < ep.nq + ep.nkv) {
 #pragma unroll
-        for (int o = 16; o < 64; o <<= 1) {
-            float ov = __shfl_xor(bv, o, 64);
-            int oi = __shfl_xor(bi, o, 64);
-            if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-        }
-        if (grp == 0 && m < M) {
-            amax_val[(int64_t)ng * m_total + m0 + m] = bv;
-            amax_idx[(int64_t)ng * m_total + m0 + m] = bi;
+                    for (int j = 0; j < 4; ++j) {
+                        const float a = round_bf(acc.v[t][mt][j]);
+                        const float c = round_bf(acc.v[t + NT / 2][mt][j]);
+                        const float2 cs = ep.rope[(int64_t)row * half + jj + j];
+                        lo[j] = to_bf(a * cs.x - c * cs.y);
+                        hi[j] = to_bf(c * cs.x + a * cs.y);
+                    }
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        lo[j] = to_bf(acc.v[t][mt][j]);
+                        hi[j] = to_bf(acc.v[t + NT / 2][mt][j]);
+                    }
+                }
+                if (head < ep.nq) {
+                    bf16 *qh = ep.q + ((int64_t)row * ep.nq + head) * ep.D + jj;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) { qh[j] = lo[j]; qh[j + half] = hi[j]; }
+                } else if (ok && head < ep.nq + ep.nkv) {
+                    bf16 *kr = ep.k_pool + (((int64_t)page * ep.nkv + (head - ep.nq)) * 16 + slot) * ep.D + jj;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) { kr[j] = lo[j]; kr[j + half] = hi[j]; }
+                } else if (ok) {
+                    bf16 *vr = ep.v_pool + (((int64_t)page * ep.nkv + (head - ep.nq - ep.nkv)) * ep.D + jj) * 16 + slot;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) { vr[j * 16] = lo[j]; vr[(j + half) * 16] = hi[j]; }
+                }
+            }
+        } else if constexpr (EPI == EPI_RESID) {
+            float ss = 0.f;
+            if (live) {
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    bf16 *xr = ep.x + (int64_t)row * N + col[t];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const float xn = round_bf(to_f(xr[j]) + round_bf(acc.v[t][mt][j]));
+                        ss += xn * xn;
+                        xr[j] = to_bf(xn);
+                        if (ep.trace) ep.trace[(int64_t)row * N + col[t] + j] = to_bf(xn);
+                    }
+                }
+            }
+            ss += __shfl_xor(ss, 16, 64);
+            ss += __shfl_xor(ss, 32, 64);
+            if (live && grp == 0) ep.ss_out[(int64_t)ng * in.M_total + row] = ss;
+        } else if constexpr (EPI == EPI_SWIGLU) {
+            if (!live) continue;
+#pragma unroll
+            for (int t = 0; t < NT / 2; ++t) {
+                bf16 *hr = ep.h + (int64_t)row * ep.F + col[t];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float g = round_bf(acc.v[t][mt][j]);
+                    const float u = round_bf(acc.v[t + NT / 2][mt][j]);
+                    hr[j] = to_bf((g / (1.0f + expf(-g))) * u);
+                }
+            }
+        } else if constexpr (EPI == EPI_ARGMAX) {
+            float bv = -INFINITY;
+            int bi = 0x7fffffff;
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                if (ep.logits != nullptr && live) *(floatx4 *)(ep.logits + (int64_t)row * N + col[t]) = acc.v[t][mt];
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (better(acc.v[t][mt][j], col[t] + j, bv, bi)) { bv = acc.v[t][mt][j]; bi = col[t] + j; }
+            }
+#pragma unroll
+            for (int o = 16; o < 64; o <<= 1) {
+                const float ov = __shfl_xor(bv, o, 64);
+                const int oi = __shfl_xor(bi, o, 64);
+                if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+            }
+            if (grp == 0 && live) {
+                ep.amax_val[(int64_t)ng * in.M_total + row] = bv;
+                ep.amax_idx[(int64_t)ng * in.M_total + row] = bi;
+            }
         }
     }
 }
 
 static int mt_for(int m) { return m <= 16 ? 1 : (m <= 32 ? 2 : 4); }
 
-int gemm_groups(const GemmShape &g) {
-    const int rows = 16 * g.nt;
-    return (g.N + rows - 1) / rows;
-}
+int gemm_groups(const GemmShape &g) { return g.N / (16 * g.nt); }
 
-template <int NT, int MT>
-static hipError_t launch_partials(const GemmShape &g, int m0, int mc, const bf16 *X,
-                                  const bf16 *W, float *P, hipStream_t st) {
-    const int ng = gemm_groups(g);
-    const int steps = g.Kd >> 5;
-    const int ks = (steps + g.splits - 1) / g.splits;
-    const size_t lds = sizeof(floatx4) * 3 * NT * MT * 64;
-    hipLaunchKernelGGL((gemm_partials_kernel<NT, MT>), dim3(ng * g.splits), dim3(256), lds, st,
-                       X + (int64_t)m0 * g.ldx, g.ldx, mc, g.M, m0, W, g.N, g.Kd, ng, ks, P);
+template <int NT, int MT, int W, int EPI, bool NORM>
+static hipError_t launch(const GemmShape &g, const GemmIn &in, const bf16 *Wp, const GemmEpi &ep,
+                         hipStream_t st) {
+    hipLaunchKernelGGL((gemm_kernel<NT, MT, W, EPI, NORM>), dim3(gemm_groups(g)), dim3(64 * W), 0, st,
+                       in, Wp, g.N, g.Kd, ep);
     return hipGetLastError();
 }
 
-template <int NT, int MT>
-static hipError_t launch_argmax(const GemmShape &g, int m0, int mc, const bf16 *X, const bf16 *W,
-                                float *logits, float *av, int *ai, hipStream_t st) {
-    const int ng = gemm_groups(g);
-    const size_t lds = sizeof(floatx4) * 3 * NT * MT * 64;
-    hipLaunchKernelGGL((gemm_argmax_kernel<NT, MT>), dim3(ng), dim3(256), lds, st,
-                       X + (int64_t)m0 * g.ldx, g.ldx, mc, g.M, m0, W, g.N, g.Kd, ng, logits, av, ai);
-    return hipGetLastError();
+// Eight waves per workgroup (512 threads) leave each wave 256 registers, enough for up to four
+// 16x16 accumulator tiles without spilling; wider tiles stay at four waves.
+
+template <int NT, int MT, int EPI, bool NORM>
+static hipError_t by_waves(const GemmShape &g, const GemmIn &in, const bf16 *Wp, const GemmEpi &ep,
+                           hipStream_t st) {
+    switch (g.waves) {
+        case 4: return launch<NT, MT, 4, EPI, NORM>(g, in, Wp, ep, st);
+        case 8:
+            if constexpr (NT * MT <= 4) return launch<NT, MT, 8, EPI, NORM>(g, in, Wp, ep, st);
+            return hipErrorInvalidValue;
+        default: return hipErrorInvalidValue;
+    }
 }
 
-#define SV_DISPATCH(NTV, MTV, CALL)                                 \
-    do {                                                            \
-        if ((NTV) == 4) {                                           \
-            if ((MTV) == 1) { CALL(4, 1); }                         \
-            else if ((MTV) == 2) { CALL(4, 2); }                    \
-            else { CALL(4, 4); }                                    \
-        } else {                                                    \
-            if ((MTV) == 1) { CALL(2, 1); }                         \
-            else if ((MTV) == 2) { CALL(2, 2); }                    \
-            else { CALL(2, 4); }                                    \
-        }                                                           \
-    } while (0)
+template <int EPI, bool NORM>
+static hipError_t by_tiles(const GemmShape &g, const GemmIn &in, const bf16 *Wp, const GemmEpi &ep,
+                           hipStream_t st) {
+    const int mt = mt_for(in.M);
+    if (g.nt == 4) {
+        if (mt == 1) return by_waves<4, 1, EPI, NORM>(g, in, Wp, ep, st);
+        if (mt == 2) return by_waves<4, 2, EPI, NORM>(g, in, Wp, ep, st);
+        return by_waves<4, 4, EPI, NORM>(g, in, Wp, ep, st);
+    }
+    if (g.nt == 2) {
+        if (mt == 1) return by_waves<2, 1, EPI, NORM>(g, in, Wp, ep, st);
+        if (mt == 2) return by_waves<2, 2, EPI, NORM>(g, in, Wp, ep, st);
+        return by_waves<2, 4, EPI, NORM>(g, in, Wp, ep, st);
+    }
+    if constexpr (EPI == EPI_QKV || EPI == EPI_SWIGLU) {
+        return hipErrorInvalidValue;   // paired epilogues need two tiles per group
+    } else {
+        if (mt == 1) return by_waves<1, 1, EPI, NORM>(g, in, Wp, ep, st);
+        if (mt == 2) return by_waves<1, 2, EPI, NORM>(g, in, Wp, ep, st);
+        return by_waves<1, 4, EPI, NORM>(g, in, Wp, ep, st);
+    }
+}
 
-hipError_t gemm_partials(const GemmShape &g, const bf16 *X, const bf16 *W, float *P, hipStream_t st) {
+hipError_t gemm(const GemmShape &g, int epi, const GemmIn &in_all, const bf16 *Wp,
+                const GemmEpi &ep, hipStream_t st) {
     for (int m0 = 0; m0 < g.M; m0 += 64) {
-        const int mc = g.M - m0 < 64 ? g.M - m0 : 64;
-        hipError_t e = hipSuccess;
-#define SV_CALL(A, B) e = launch_partials<A, B>(g, m0, mc, X, W, P, st)
-        SV_DISPATCH(g.nt, mt_for(mc), SV_CALL);
-#undef SV_CALL
+        GemmIn in = in_all;
+        in.M_total = g.M;
+        in.m0 = m0;
+        in.M = g.M - m0 < 64 ? g.M - m0 : 64;
+        const bool norm = in.ss != nullptr;
+        hipError_t e;
+        switch (epi) {
+            case EPI_PLAIN: e = by_tiles<EPI_PLAIN, false>(g, in, Wp, ep, st); break;
+            case EPI_QKV: e = norm ? by_tiles<EPI_QKV, true>(g, in, Wp, ep, st)
+                                   : by_tiles<EPI_QKV, false>(g, in, Wp, ep, st); break;
+            case EPI_RESID: e = by_tiles<EPI_RESID, false>(g, in, Wp, ep, st); break;
+            case EPI_SWIGLU: e = by_tiles<EPI_SWIGLU, true>(g, in, Wp, ep, st); break;
+            case EPI_ARGMAX: e = by_tiles<EPI_ARGMAX, true>(g, in, Wp, ep, st); break;
+            default: return hipErrorInvalidValue;
+        }
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
 }
 
-hipError_t gemm_argmax(const GemmShape &g, const bf16 *X, const bf16 *W, float *logits,
-                       float *amax_val, int *amax_idx, hipStream_t st) {
-    for (int m0 = 0; m0 < g.M; m0 += 64) {
-        const int mc = g.M - m0 < 64 ? g.M - m0 : 64;
-        hipError_t e = hipSuccess;
-#define SV_CALL(A, B) e = launch_argmax<A, B>(g, m0, mc, X, W, logits, amax_val, amax_idx, st)
-        SV_DISPATCH(g.nt, mt_for(mc), SV_CALL);
-#undef SV_CALL
-        if (e != hipSuccess) return e;
-    }
-    return hipSuccess;
+// Tiles per group and waves per workgroup for a projection of N outputs over Kd at M rows:
+// paired epilogues need an even tile count; otherwise one tile per group keeps the group count
+// high. Eight waves instead of four split K when the launch would otherwise hold fewer than about
+// 2000 waves, keeping at least 8 K steps per wave.
+GemmShape plan_gemm(int M, int N, int Kd, bool paired) {
+    GemmShape g;
+    g.M = M;
+    g.N = N;
+    g.Kd = Kd;
+    if (paired) g.nt = 2;
+    else g.nt = (N / 16 >= 2048 && M <= 16) ? 4 : 1;
+    const int groups = N / (16 * g.nt);
+    const int steps = Kd / 32;
+    const int mt = mt_for(M < 64 ? M : 64);
+    g.waves = 4;
+    if (groups * 4 < 2048 && steps / 8 >= 8 && g.nt * mt <= 4) g.waves = 8;
+    return g;
 }
 
 }  // namespace sv

@@ -8,22 +8,55 @@
 
 namespace sv {
 
-// ---- skinny GEMM: Y = X . W^T with X [M][Kd] bf16 (row stride ldx), W [N][Kd] bf16 ----------
+// ---- skinny GEMM: Y = X . W^T with X [M][Kd] bf16, W [N][Kd] bf16 packed in fragment order ----
 
 struct GemmShape {
-    int M, N, Kd, ldx;
-    int nt;         // 16-row weight tiles per wave (2 or 4)
-    int splits;     // K splits (partials)
+    int M, N, Kd;
+    int nt;         // 16-row weight tiles per workgroup (1, 2 or 4)
+    int waves;      // waves per workgroup splitting K (4, 8 or 16)
 };
 
-// Number of workgroups (weight tile groups x splits) a partial GEMM launches per 64-row chunk.
+// What a workgroup does with its finished tiles.
+enum { EPI_PLAIN = 0, EPI_QKV = 1, EPI_RESID = 2, EPI_SWIGLU = 3, EPI_ARGMAX = 4 };
+
+// The B operand. When ss != nullptr it is RMSNorm(X) * gain, computed on load from the
+// per-row sums of squares ss[ss_groups][M_total] the producer of X left behind.
+struct GemmIn {
+    const bf16 *X;
+    int ldx;
+    int M, M_total, m0;          // filled per 64-row chunk by gemm()
+    const float *ss;
+    int ss_groups;
+    const bf16 *gain;
+    float eps;
+    int H;
+};
+
+struct GemmEpi {
+    int D, F;                    // head dim; ffn (SwiGLU pairing)
+    // PLAIN: fp32 y [M][N]
+    float *y;
+    // QKV: q [M][nq][D]; K/V into cache slot ctx_len + (row % K) of request row / K
+    bf16 *q, *k_pool, *v_pool;
+    const int32_t *block_table, *ctx_len, *status;
+    const float2 *rope;          // [M][D/2] (cos, sin)
+    int max_pages, K, nq, nkv;
+    // RESID: x [M][N] += y; per-row sum of squares of the new x per tile group
+    bf16 *x;
+    float *ss_out;               // [n_groups][M]
+    bf16 *trace;                 // optional copy of the new x
+    // SWIGLU: h [M][F]
+    bf16 *h;
+    // ARGMAX: per tile group (max, lowest index) [n_groups][M]; optional fp32 logits [M][N]
+    float *logits, *amax_val;
+    int *amax_idx;
+};
+
 int gemm_groups(const GemmShape &g);
-// Partials P[s][m][n] = sum over the split's K range, s = 0..splits-1.
-hipError_t gemm_partials(const GemmShape &g, const bf16 *X, const bf16 *W, float *P, hipStream_t st);
-// Output head: per (group of 16*nt columns, row) the greedy (max, lowest index) into
-// amax_val/amax_idx [n_groups][M]; optionally the fp32 logits [M][N]. splits must be 1.
-hipError_t gemm_argmax(const GemmShape &g, const bf16 *X, const bf16 *W, float *logits,
-                       float *amax_val, int *amax_idx, hipStream_t st);
+GemmShape plan_gemm(int M, int N, int Kd, bool paired);
+hipError_t gemm(const GemmShape &g, int epi, const GemmIn &in, const bf16 *Wp, const GemmEpi &ep,
+                hipStream_t st);
+hipError_t pack_weight(const bf16 *w, int n, int kd, bf16 *out, hipStream_t st);
 
 // ---- attention ------------------------------------------------------------------------------
 
@@ -57,16 +90,13 @@ hipError_t tree_prep(const int32_t *tokens, const int32_t *parent, const int32_t
                      const int32_t *block_table, int max_pages, int n_pages, int B, int K,
                      int vocab, const NodeInfo &ni, hipStream_t st);
 hipError_t rope_table(const NodeInfo &ni, int M, int D, double theta, hipStream_t st);
-hipError_t embed_norm(const int32_t *tokens, const bf16 *embed, const bf16 *gain, int M, int H,
-                      int vocab, float eps, bf16 *x, bf16 *u, bf16 *trace, hipStream_t st);
-hipError_t qkv_rope_store(const float *P, int splits, const NodeInfo &ni, const int32_t *ctx_len,
-                          const int32_t *block_table, int max_pages, int B, int K, int nq,
-                          int nkv, int D, bf16 *q, bf16 *k_pool, bf16 *v_pool, hipStream_t st);
-hipError_t residual_norm(const float *P, int splits, int M, int H, const bf16 *gain, float eps,
-                         bf16 *x, bf16 *u, bf16 *trace, hipStream_t st);
-hipError_t swiglu(const float *P, int splits, int M, int F, bf16 *h, hipStream_t st);
+// x = embedding rows; ss [H/64][M] = per-row sums of squares over 64-column groups.
+hipError_t embed(const int32_t *tokens, const bf16 *table, int M, int H, int vocab, bf16 *x,
+                 float *ss, bf16 *trace, hipStream_t st);
+int embed_ss_groups(int H);
 hipError_t argmax_partials(const float *logits, int M, int V, float *amax_val, int *amax_idx,
                            int n_chunks, hipStream_t st);
+int argmax_chunks(int V);
 hipError_t argmax_accept(const float *amax_val, const int *amax_idx, int n_groups,
                          const int32_t *tokens, const int32_t *parent, const NodeInfo &ni, int B,
                          int K, int32_t *greedy, int32_t *accepted_len, int32_t *bonus,

@@ -1,15 +1,11 @@
 // specverify.hip — host side of libspecverify: argument checks, the per-call plan (GEMM tiles
-// and K splits, attention chunks, workspace layout) and the launch sequence of one
+// and waves, attention chunks, workspace layout) and the launch sequence of one
 // verification pass. Everything is enqueued on the caller's stream; nothing here waits for
 // the device, allocates, or keeps global state.
 #include <string.h>
 
 #include "specverify.h"
 #include "kernels.hpp"
-
-namespace sv {
-int argmax_chunks(int V);
-}
 
 namespace {
 
@@ -28,30 +24,15 @@ struct Carver {
     }
 };
 
-// Target: enough workgroups to keep every CU streaming (256 CUs, a few groups each).
-constexpr int kTargetGroups = 1024;
-
-int pick_splits(int N, int Kd, int nt) {
-    const int groups = (N + 16 * nt - 1) / (16 * nt);
-    const int steps = Kd / 32;
-    int s = kTargetGroups / groups;
-    if (s < 1) s = 1;
-    // keep at least 8 K steps (2 per wave) in every split
-    int max_s = steps / 8;
-    if (max_s < 1) max_s = 1;
-    if (s > max_s) s = max_s;
-    return s;
-}
-
 struct Plan {
     int B, K, M;
     int L, H, nq, nkv, D, F, V;
     int qd, nqkv;
     GemmShape g_qkv, g_o, g_gu, g_down, g_lm;
-    int lm_groups;
+    int lm_groups, ss_groups_resid, ss_groups_embed;
     int attn_chunks;
-    size_t o_depth, o_pos, o_status, o_anc, o_rope, o_x, o_u, o_q, o_attn, o_h, o_part, o_po,
-        o_pml, o_amv, o_ami, total;
+    size_t o_depth, o_pos, o_status, o_anc, o_rope, o_x, o_ss, o_q, o_attn, o_h, o_po, o_pml,
+        o_amv, o_ami, total;
 };
 
 int check_cfg(const spec_model_cfg *c) {
@@ -62,10 +43,10 @@ int check_cfg(const spec_model_cfg *c) {
     if (!(c->rms_eps >= 0.0f) || !(c->rope_theta > 0.0)) return SPEC_EINVAL;
     if (c->head_dim != 64 && c->head_dim != 128) return SPEC_EUNSUPPORTED;
     if (c->n_q_heads % c->n_kv_heads != 0) return SPEC_EUNSUPPORTED;
-    if (c->hidden % 32 != 0 || (c->n_q_heads * c->head_dim) % 32 != 0 || c->ffn % 32 != 0)
+    if (c->hidden % 64 != 0 || (c->n_q_heads * c->head_dim) % 32 != 0 || c->ffn % 32 != 0)
         return SPEC_EUNSUPPORTED;
     if (c->hidden > 16384) return SPEC_EUNSUPPORTED;
-    if (c->vocab % 16 != 0) return SPEC_EUNSUPPORTED;
+    if (c->vocab % 64 != 0) return SPEC_EUNSUPPORTED;
     return SPEC_OK;
 }
 
@@ -88,33 +69,21 @@ int make_plan(const spec_model_cfg *c, int B, int K, int max_pages, Plan &p) {
     p.qd = p.nq * p.D;
     p.nqkv = (p.nq + 2 * p.nkv) * p.D;
     const int M = p.M;
-    auto mk = [&](int N, int Kd, int ldx) {
-        GemmShape g;
-        g.M = M;
-        g.N = N;
-        g.Kd = Kd;
-        g.ldx = ldx;
-        g.nt = M <= 16 ? 4 : 2;   // keep the M=32/64 tiles at two waves per SIMD
-        g.splits = pick_splits(N, Kd, g.nt);
-        return g;
-    };
-    p.g_qkv = mk(p.nqkv, p.H, p.H);
-    p.g_o = mk(p.H, p.qd, p.qd);
-    p.g_gu = mk(2 * p.F, p.H, p.H);
-    p.g_down = mk(p.H, p.F, p.F);
-    p.g_lm = mk(p.V, p.H, p.H);
-    p.g_lm.splits = 1;
+    p.g_qkv = plan_gemm(M, p.nqkv, p.H, true);
+    p.g_o = plan_gemm(M, p.H, p.qd, false);
+    p.g_gu = plan_gemm(M, 2 * p.F, p.H, true);
+    p.g_down = plan_gemm(M, p.H, p.F, false);
+    p.g_lm = plan_gemm(M, p.V, p.H, false);
     p.lm_groups = gemm_groups(p.g_lm);
+    p.ss_groups_resid = gemm_groups(p.g_o);
+    if (gemm_groups(p.g_down) != p.ss_groups_resid) return SPEC_EUNSUPPORTED;
+    p.ss_groups_embed = embed_ss_groups(p.H);
     const int64_t max_keys = (int64_t)max_pages * SPEC_PAGE_SIZE;
     p.attn_chunks = (int)((max_keys + kAttnChunk - 1) / kAttnChunk);
     const int group = p.nq / p.nkv;
 
-    size_t part = 0;
-    for (const GemmShape *g : {&p.g_qkv, &p.g_o, &p.g_gu, &p.g_down}) {
-        const size_t b = (size_t)g->splits * M * g->N * sizeof(float);
-        if (b > part) part = b;
-    }
     const int amax_groups = p.lm_groups > argmax_chunks(p.V) ? p.lm_groups : argmax_chunks(p.V);
+    const int ss_groups = p.ss_groups_resid > p.ss_groups_embed ? p.ss_groups_resid : p.ss_groups_embed;
     Carver cv;
     p.o_depth = cv.take(sizeof(int32_t) * M);
     p.o_pos = cv.take(sizeof(int32_t) * M);
@@ -122,11 +91,10 @@ int make_plan(const spec_model_cfg *c, int B, int K, int max_pages, Plan &p) {
     p.o_anc = cv.take(sizeof(uint64_t) * M);
     p.o_rope = cv.take(sizeof(float2) * M * (p.D / 2));
     p.o_x = cv.take(sizeof(uint16_t) * M * p.H);
-    p.o_u = cv.take(sizeof(uint16_t) * M * p.H);
+    p.o_ss = cv.take(sizeof(float) * (size_t)ss_groups * M);
     p.o_q = cv.take(sizeof(uint16_t) * M * p.qd);
     p.o_attn = cv.take(sizeof(uint16_t) * M * p.qd);
     p.o_h = cv.take(sizeof(uint16_t) * M * p.F);
-    p.o_part = cv.take(part);
     p.o_po = cv.take(sizeof(float) * (size_t)B * p.nkv * p.attn_chunks * group * K * p.D);
     p.o_pml = cv.take(sizeof(float2) * (size_t)B * p.nkv * p.attn_chunks * group * K);
     p.o_amv = cv.take(sizeof(float) * (size_t)amax_groups * M);
@@ -208,11 +176,10 @@ int spec_verify(const spec_weights *w, const spec_kv_cache *kv, const int32_t *d
     ni.anc = at<uint64_t>(workspace, p.o_anc);
     ni.rope = at<float2>(workspace, p.o_rope);
     bf16 *x = at<bf16>(workspace, p.o_x);
-    bf16 *u = at<bf16>(workspace, p.o_u);
+    float *ss = at<float>(workspace, p.o_ss);
     bf16 *q = at<bf16>(workspace, p.o_q);
     bf16 *attn = at<bf16>(workspace, p.o_attn);
     bf16 *h = at<bf16>(workspace, p.o_h);
-    float *part = at<float>(workspace, p.o_part);
     float *amv = at<float>(workspace, p.o_amv);
     int *ami = at<int>(workspace, p.o_ami);
     bf16 *k_pool = static_cast<bf16 *>(kv->k_pool);
@@ -222,9 +189,45 @@ int spec_verify(const spec_weights *w, const spec_kv_cache *kv, const int32_t *d
     SV_TRY(tree_prep(draft_tokens, tree_parent, ctx_len, kv->block_table, kv->max_pages_per_req,
                      kv->n_pages, p.B, p.K, p.V, ni, stream));
     SV_TRY(rope_table(ni, M, p.D, w->cfg.rope_theta, stream));
-    SV_TRY(embed_norm(draft_tokens, static_cast<const bf16 *>(w->embed),
-                      static_cast<const bf16 *>(w->layers[0].attn_norm), M, p.H, p.V, eps, x, u,
-                      trace, stream));
+    SV_TRY(embed(draft_tokens, static_cast<const bf16 *>(w->embed), M, p.H, p.V, x, ss, trace, stream));
+
+    GemmEpi ep = {};
+    ep.D = p.D;
+    ep.F = p.F;
+    ep.q = q;
+    ep.block_table = kv->block_table;
+    ep.ctx_len = ctx_len;
+    ep.status = ni.status;
+    ep.rope = ni.rope;
+    ep.max_pages = kv->max_pages_per_req;
+    ep.K = p.K;
+    ep.nq = p.nq;
+    ep.nkv = p.nkv;
+    ep.x = x;
+    ep.ss_out = ss;
+    ep.h = h;
+    ep.logits = logits;
+    ep.amax_val = amv;
+    ep.amax_idx = ami;
+
+    // operand that is RMSNorm(x) * gain, from the sums of squares in ss
+    auto normed = [&](const void *gain, int ss_groups) {
+        GemmIn in = {};
+        in.X = x;
+        in.ldx = p.H;
+        in.ss = ss;
+        in.ss_groups = ss_groups;
+        in.gain = static_cast<const bf16 *>(gain);
+        in.eps = eps;
+        in.H = p.H;
+        return in;
+    };
+    auto plain = [&](const bf16 *X, int ldx) {
+        GemmIn in = {};
+        in.X = X;
+        in.ldx = ldx;
+        return in;
+    };
 
     AttnArgs aa;
     aa.q = q;
@@ -244,28 +247,28 @@ int spec_verify(const spec_weights *w, const spec_kv_cache *kv, const int32_t *d
     aa.part_ml = at<float2>(workspace, p.o_pml);
     aa.out = attn;
 
+    int ss_groups = p.ss_groups_embed;
     for (int l = 0; l < p.L; ++l) {
         const spec_layer_weights &lw = w->layers[l];
-        bf16 *kl = k_pool + l * layer_stride;
-        bf16 *vl = v_pool + l * layer_stride;
-        SV_TRY(gemm_partials(p.g_qkv, u, static_cast<const bf16 *>(lw.w_qkv), part, stream));
-        SV_TRY(qkv_rope_store(part, p.g_qkv.splits, ni, ctx_len, kv->block_table,
-                              kv->max_pages_per_req, p.B, p.K, p.nq, p.nkv, p.D, q, kl, vl, stream));
-        aa.k_pool = kl;
-        aa.v_pool = vl;
+        ep.k_pool = k_pool + l * layer_stride;
+        ep.v_pool = v_pool + l * layer_stride;
+        SV_TRY(gemm(p.g_qkv, EPI_QKV, normed(lw.attn_norm, ss_groups),
+                    static_cast<const bf16 *>(lw.w_qkv), ep, stream));
+        aa.k_pool = ep.k_pool;
+        aa.v_pool = ep.v_pool;
         SV_TRY(attention(aa, stream));
-        SV_TRY(gemm_partials(p.g_o, attn, static_cast<const bf16 *>(lw.w_o), part, stream));
-        SV_TRY(residual_norm(part, p.g_o.splits, M, p.H, static_cast<const bf16 *>(lw.mlp_norm),
-                             eps, x, u, nullptr, stream));
-        SV_TRY(gemm_partials(p.g_gu, u, static_cast<const bf16 *>(lw.w_gate_up), part, stream));
-        SV_TRY(swiglu(part, p.g_gu.splits, M, p.F, h, stream));
-        SV_TRY(gemm_partials(p.g_down, h, static_cast<const bf16 *>(lw.w_down), part, stream));
-        const bf16 *next_gain = l + 1 < p.L ? static_cast<const bf16 *>(w->layers[l + 1].attn_norm)
-                                            : static_cast<const bf16 *>(w->final_norm);
-        SV_TRY(residual_norm(part, p.g_down.splits, M, p.H, next_gain, eps, x, u,
-                             trace ? trace + (int64_t)(l + 1) * M * p.H : nullptr, stream));
+        ep.trace = nullptr;
+        SV_TRY(gemm(p.g_o, EPI_RESID, plain(attn, p.qd), static_cast<const bf16 *>(lw.w_o), ep,
+                    stream));
+        ss_groups = p.ss_groups_resid;
+        SV_TRY(gemm(p.g_gu, EPI_SWIGLU, normed(lw.mlp_norm, ss_groups),
+                    static_cast<const bf16 *>(lw.w_gate_up), ep, stream));
+        ep.trace = trace ? trace + (int64_t)(l + 1) * M * p.H : nullptr;
+        SV_TRY(gemm(p.g_down, EPI_RESID, plain(h, p.F), static_cast<const bf16 *>(lw.w_down), ep,
+                    stream));
     }
-    SV_TRY(gemm_argmax(p.g_lm, u, static_cast<const bf16 *>(w->lm_head), logits, amv, ami, stream));
+    SV_TRY(gemm(p.g_lm, EPI_ARGMAX, normed(w->final_norm, ss_groups),
+                static_cast<const bf16 *>(w->lm_head), ep, stream));
     SV_TRY(argmax_accept(amv, ami, p.lm_groups, draft_tokens, tree_parent, ni, p.B, p.K, greedy,
                          accepted_len, bonus_token, accepted_path, stream));
     return SPEC_OK;
@@ -293,12 +296,17 @@ int spec_commit_kv(const spec_model_cfg *cfg, const spec_kv_cache *kv, const int
 static int skinny_shape(int m, int n, int kd, GemmShape &g) {
     if (m < 1 || n < 1 || kd < 1) return SPEC_EINVAL;
     if (kd % 32 != 0 || n % 16 != 0) return SPEC_EUNSUPPORTED;
-    g.M = m;
-    g.N = n;
-    g.Kd = kd;
-    g.ldx = kd;
-    g.nt = m <= 16 ? 4 : 2;
-    g.splits = pick_splits(n, kd, g.nt);
+    g = plan_gemm(m, n, kd, false);
+    if (n % (16 * g.nt) != 0) return SPEC_EUNSUPPORTED;
+    return SPEC_OK;
+}
+
+int spec_pack_weight(const void *w, int n, int kd, void *packed, hipStream_t stream) {
+    if (w == nullptr || packed == nullptr) return SPEC_EINVAL;
+    if (n < 1 || kd < 1) return SPEC_EINVAL;
+    if (n % 16 != 0 || kd % 32 != 0) return SPEC_EUNSUPPORTED;
+    if (w == packed) return SPEC_EINVAL;
+    SV_TRY(pack_weight(static_cast<const bf16 *>(w), n, kd, static_cast<bf16 *>(packed), stream));
     return SPEC_OK;
 }
 
@@ -307,7 +315,7 @@ int spec_skinny_gemm_bytes(int m, int n, int kd, size_t *bytes) {
     GemmShape g;
     const int rc = skinny_shape(m, n, kd, g);
     if (rc != SPEC_OK) return rc;
-    *bytes = (size_t)g.splits * m * n * sizeof(float);
+    *bytes = (size_t)m * n * sizeof(float);
     return SPEC_OK;
 }
 
@@ -317,9 +325,14 @@ int spec_skinny_gemm(const void *x, int m, int kd, const void *w, int n, float *
     GemmShape g;
     const int rc = skinny_shape(m, n, kd, g);
     if (rc != SPEC_OK) return rc;
-    if (partial_bytes < (size_t)g.splits * m * n * sizeof(float)) return SPEC_EWORKSPACE;
-    *splits = g.splits;
-    SV_TRY(gemm_partials(g, static_cast<const bf16 *>(x), static_cast<const bf16 *>(w), partials, stream));
+    if (partial_bytes < (size_t)m * n * sizeof(float)) return SPEC_EWORKSPACE;
+    *splits = 1;
+    GemmIn in = {};
+    in.X = static_cast<const bf16 *>(x);
+    in.ldx = kd;
+    GemmEpi ep = {};
+    ep.y = partials;
+    SV_TRY(gemm(g, EPI_PLAIN, in, static_cast<const bf16 *>(w), ep, stream));
     return SPEC_OK;
 }
 
