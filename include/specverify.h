@@ -168,7 +168,7 @@ int spec_pack_weight(const void *w, int n, int kd, void *packed, hipStream_t str
  * measurement.
  *   x: bf16 [m][kd] row-major; w: bf16 [n][kd] packed (spec_pack_weight); partials: fp32,
  *   spec_skinny_gemm_bytes() bytes; *splits (HOST) receives the split count. Needs
- *   kd % 32 == 0, n % 64 == 0 (n % 32 == 0 when m > 16), m >= 1. */
+ *   kd % 32 == 0, n % 16 == 0, m >= 1. */
 int spec_skinny_gemm_bytes(int m, int n, int kd, size_t *bytes);
 int spec_skinny_gemm(const void *x, int m, int kd, const void *w, int n, float *partials,
                      size_t partial_bytes, int *splits, hipStream_t stream);

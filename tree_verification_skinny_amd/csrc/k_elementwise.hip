@@ -1,7 +1,8 @@
 // k_elementwise.hip — the small kernels around the GEMMs and attention of the verify pass:
 // draft-tree bookkeeping, RoPE angles, the embedding gather (with the per-row sums of squares the
-// first RMSNorm needs), the vocab-wide greedy choice with the accepted-path walk, and the commit
-// of the accepted path's KV rows.
+// first RMSNorm needs), the split-K passes of the narrow projections (RoPE + KV store; residual
+// add + sums of squares), the vocab-wide greedy choice with the accepted-path walk, and the
+// commit of the accepted path's KV rows.
 //
 // Lossless greedy verification: a draft token is accepted only if it equals the target's greedy
 // choice after its parent, and only along a path whose every earlier token was accepted
@@ -119,6 +120,96 @@ hipError_t embed(const int32_t *tokens, const bf16 *table, int M, int H, int voc
                  float *ss, bf16 *trace, hipStream_t st) {
     hipLaunchKernelGGL(embed_kernel, dim3(M, H / 64), dim3(64), 0, st, tokens, table, M, H, vocab, x,
                        ss, trace);
+    return hipGetLastError();
+}
+
+// ---- QKV split-K pass: sum, bf16, RoPE, q / K / V stores -----------------------------------------
+// One workgroup per (row, head of q, k or v); thread j handles the rotation pair (j, j + D/2).
+__global__ void reduce_qkv_kernel(const float *__restrict__ P, int splits, int M,
+                                  const float2 *__restrict__ rope, const int32_t *__restrict__ status,
+                                  const int32_t *__restrict__ ctx_len,
+                                  const int32_t *__restrict__ block_table, int max_pages, int K,
+                                  int nq, int nkv, int D, bf16 *__restrict__ q,
+                                  bf16 *__restrict__ k_pool, bf16 *__restrict__ v_pool) {
+#pragma clang fp contract(off)
+    const int row = blockIdx.x, head = blockIdx.y, j = threadIdx.x;
+    const int half = D / 2;
+    const int N = (nq + 2 * nkv) * D;
+    const int64_t pstride = (int64_t)M * N;
+    const float *pr = P + (int64_t)row * N + head * D + j;
+    float a = 0.f, c = 0.f;
+    for (int s = 0; s < splits; ++s) { a += pr[s * pstride]; c += pr[s * pstride + half]; }
+    a = round_bf(a);
+    c = round_bf(c);
+    bf16 lo, hi;
+    if (head < nq + nkv) {
+        const float2 cs = rope[(int64_t)row * half + j];
+        lo = to_bf(a * cs.x - c * cs.y);
+        hi = to_bf(c * cs.x + a * cs.y);
+    } else {
+        lo = to_bf(a);
+        hi = to_bf(c);
+    }
+    if (head < nq) {
+        bf16 *qh = q + ((int64_t)row * nq + head) * D;
+        qh[j] = lo;
+        qh[j + half] = hi;
+        return;
+    }
+    const int b = row / K, il = row % K;
+    if (status[b] != 0) return;
+    const int pos = ctx_len[b] + il;
+    const int page = page_of(block_table, max_pages, b, pos), slot = pos & 15;
+    if (head < nq + nkv) {
+        bf16 *kr = k_pool + (((int64_t)page * nkv + (head - nq)) * 16 + slot) * D;
+        kr[j] = lo;
+        kr[j + half] = hi;
+    } else {
+        bf16 *vr = v_pool + (((int64_t)page * nkv + (head - nq - nkv)) * D) * 16 + slot;
+        vr[j * 16] = lo;
+        vr[(j + half) * 16] = hi;
+    }
+}
+
+hipError_t reduce_qkv(const float *P, int splits, const NodeInfo &ni, const int32_t *ctx_len,
+                      const int32_t *block_table, int max_pages, int B, int K, int nq, int nkv,
+                      int D, bf16 *q, bf16 *k_pool, bf16 *v_pool, hipStream_t st) {
+    hipLaunchKernelGGL(reduce_qkv_kernel, dim3(B * K, nq + 2 * nkv), dim3(D / 2), 0, st, P, splits,
+                       B * K, ni.rope, ni.status, ctx_len, block_table, max_pages, K, nq, nkv, D, q,
+                       k_pool, v_pool);
+    return hipGetLastError();
+}
+
+// ---- residual split-K pass: x = bf16(x + bf16(sum_s P[s])), sums of squares per 256 columns ----
+__global__ __launch_bounds__(64) void reduce_resid_kernel(const float *__restrict__ P, int splits,
+                                                          int M, int H, bf16 *__restrict__ x,
+                                                          float *__restrict__ ss,
+                                                          bf16 *__restrict__ trace) {
+    const int row = blockIdx.x, g = blockIdx.y, lane = threadIdx.x;
+    const int col = g * 256 + lane * 4;
+    const int64_t pstride = (int64_t)M * H;
+    const float *pr = P + (int64_t)row * H + col;
+    floatx4 y = *(const floatx4 *)pr;
+    for (int s = 1; s < splits; ++s) y += *(const floatx4 *)(pr + s * pstride);
+    bf16 *xr = x + (int64_t)row * H + col;
+    float sq = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const float xn = round_bf(to_f(xr[j]) + round_bf(y[j]));
+        sq += xn * xn;
+        xr[j] = to_bf(xn);
+        if (trace) trace[(int64_t)row * H + col + j] = to_bf(xn);
+    }
+    sq = wave_sum(sq);
+    if (lane == 0) ss[(int64_t)g * M + row] = sq;
+}
+
+int resid_ss_groups(int H) { return H / 256; }
+
+hipError_t reduce_resid(const float *P, int splits, int M, int H, bf16 *x, float *ss, bf16 *trace,
+                        hipStream_t st) {
+    hipLaunchKernelGGL(reduce_resid_kernel, dim3(M, H / 256), dim3(64), 0, st, P, splits, M, H, x, ss,
+                       trace);
     return hipGetLastError();
 }
 

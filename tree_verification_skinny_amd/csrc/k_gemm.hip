@@ -14,11 +14,13 @@
 //     Where the consumer of a projection is an RMSNorm, the norm is applied on this load
 //     (x * rsqrt(mean x^2 + eps) * g, rounded to bf16), from per-row sums of squares the
 //     producer left behind, so no separate norm pass touches the activations.
-//   * A workgroup of W waves (4 or 8) owns NT weight tiles over the whole K range; its waves
-//     interleave over the 32-wide K steps (so together they read each tile front to back) and
-//     add their sums in LDS in wave order. No partial result leaves the workgroup: no split-K
-//     buffers, no cross-workgroup synchronisation, and results do not depend on timing. W is
-//     picked per projection so that a launch keeps roughly 2000 waves streaming.
+//   * A workgroup of W waves (4 or 8) owns NT weight tiles over a K range; its waves interleave
+//     over the 32-wide K steps (so together they read each tile front to back) and add their
+//     sums in LDS in wave order. Projections with few output columns split K over workgroups
+//     and leave fp32 partials that a separate pass adds in split order (an in-kernel "last
+//     workgroup adds" fixup needs agent-scope release/acquire fences, which cost more on this
+//     chip than the extra pass); wide projections run whole and finish their epilogue in place.
+//     Either way no workgroup waits for another and results do not depend on timing.
 //   * Epilogues: RoPE + q/K/V store into the paged cache (QKV), residual add + per-row sum of
 //     squares (O and down projections), SwiGLU (gate/up), and the per-tile greedy maximum of the
 //     output head. Tile groups are laid out so that every pair an epilogue needs (RoPE's j and
@@ -77,12 +79,16 @@ struct Acc {
 
 template <int NT, int MT, int W, int EPI, bool NORM>
 __global__ __launch_bounds__(64 * W) void gemm_kernel(GemmIn in, const bf16 *__restrict__ Wp,
-                                                      int N, int Kd, GemmEpi ep) {
+                                                      int N, int Kd, int n_groups, int ksteps,
+                                                      GemmEpi ep) {
     __shared__ floatx4 red[(W - 1) * NT * MT * 64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r16 = lane & 15, grp = lane >> 4;
-    const int ng = blockIdx.x;
+    const int ng = blockIdx.x % n_groups;
+    const int split = blockIdx.x / n_groups;
     const int S = Kd >> 5;
+    const int s_begin = split * ksteps;
+    const int s_end = min(s_begin + ksteps, S);
     const int M = in.M;            // rows in this launch (a chunk of at most 64)
     const int m0 = in.m0;          // first global row of the chunk
 
@@ -143,9 +149,9 @@ __global__ __launch_bounds__(64 * W) void gemm_kernel(GemmIn in, const bf16 *__r
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc.v[t][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    constexpr int U = (NT * MT >= 8) ? 2 : 4;   // K steps in flight per wave
-    int s = wave;
-    for (; s + W * (U - 1) < S; s += W * U) {
+    constexpr int U = (NT * MT >= 8 || (W >= 8 && NT * MT >= 4)) ? 2 : 4;   // K steps in flight per wave
+    int s = s_begin + wave;
+    for (; s + W * (U - 1) < s_end; s += W * U) {
         bf16x8 a[U][NT], b[U][MT];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -163,7 +169,7 @@ __global__ __launch_bounds__(64 * W) void gemm_kernel(GemmIn in, const bf16 *__r
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) acc.v[t][mt] = mfma16x16x32(a[u][t], b[u][mt], acc.v[t][mt]);
     }
-    for (; s < S; s += W) {
+    for (; s < s_end; s += W) {
         bf16x8 a[NT], b[MT];
 #pragma unroll
         for (int t = 0; t < NT; ++t) a[t] = *(const bf16x8 *)(wp[t] + (int64_t)s * 512);
@@ -200,10 +206,11 @@ __global__ __launch_bounds__(64 * W) void gemm_kernel(GemmIn in, const bf16 *__r
         const int m = 16 * mt + r16;
         const bool live = m < M;
         const int row = m0 + m;
-        if constexpr (EPI == EPI_PLAIN) {
+        if constexpr (EPI == EPI_PARTIAL) {
             if (live) {
 #pragma unroll
-                for (int t = 0; t < NT; ++t) *(floatx4 *)(ep.y + (int64_t)row * N + col[t]) = acc.v[t][mt];
+                for (int t = 0; t < NT; ++t)
+                    *(floatx4 *)(ep.y + ((int64_t)split * in.M_total + row) * N + col[t]) = acc.v[t][mt];
             }
         } else if constexpr (EPI == EPI_QKV) {
 #pragma clang fp contract(off)
@@ -312,8 +319,10 @@ int gemm_groups(const GemmShape &g) { return g.N / (16 * g.nt); }
 template <int NT, int MT, int W, int EPI, bool NORM>
 static hipError_t launch(const GemmShape &g, const GemmIn &in, const bf16 *Wp, const GemmEpi &ep,
                          hipStream_t st) {
-    hipLaunchKernelGGL((gemm_kernel<NT, MT, W, EPI, NORM>), dim3(gemm_groups(g)), dim3(64 * W), 0, st,
-                       in, Wp, g.N, g.Kd, ep);
+    const int steps = g.Kd >> 5;
+    const int ks = (steps + g.splits - 1) / g.splits;
+    hipLaunchKernelGGL((gemm_kernel<NT, MT, W, EPI, NORM>), dim3(gemm_groups(g) * g.splits), dim3(64 * W),
+                       0, st, in, Wp, g.N, g.Kd, gemm_groups(g), ks, ep);
     return hipGetLastError();
 }
 
@@ -365,7 +374,8 @@ hipError_t gemm(const GemmShape &g, int epi, const GemmIn &in_all, const bf16 *W
         const bool norm = in.ss != nullptr;
         hipError_t e;
         switch (epi) {
-            case EPI_PLAIN: e = by_tiles<EPI_PLAIN, false>(g, in, Wp, ep, st); break;
+            case EPI_PARTIAL: e = norm ? by_tiles<EPI_PARTIAL, true>(g, in, Wp, ep, st)
+                                       : by_tiles<EPI_PARTIAL, false>(g, in, Wp, ep, st); break;
             case EPI_QKV: e = norm ? by_tiles<EPI_QKV, true>(g, in, Wp, ep, st)
                                    : by_tiles<EPI_QKV, false>(g, in, Wp, ep, st); break;
             case EPI_RESID: e = by_tiles<EPI_RESID, false>(g, in, Wp, ep, st); break;
@@ -378,22 +388,30 @@ hipError_t gemm(const GemmShape &g, int epi, const GemmIn &in_all, const bf16 *W
     return hipSuccess;
 }
 
-// Tiles per group and waves per workgroup for a projection of N outputs over Kd at M rows:
-// paired epilogues need an even tile count; otherwise one tile per group keeps the group count
-// high. Eight waves instead of four split K when the launch would otherwise hold fewer than about
-// 2000 waves, keeping at least 8 K steps per wave.
-GemmShape plan_gemm(int M, int N, int Kd, bool paired) {
+// Tiles per group, waves per workgroup and K splits for a projection of N outputs over Kd at M
+// rows. Every workgroup reads the activation rows of its K range once, so a group of NT tiles
+// costs 1/NT of its weight bytes again in activation reads: groups are four tiles wide where the
+// register budget allows. Projections with few groups are split along K until about 640
+// workgroups stream (partials, added by a separate pass); projections with many groups run whole
+// and finish their epilogue in place. Eight waves when there are few groups or K splits.
+GemmShape plan_gemm(int M, int N, int Kd, bool allow_split) {
     GemmShape g;
     g.M = M;
     g.N = N;
     g.Kd = Kd;
-    if (paired) g.nt = 2;
-    else g.nt = (N / 16 >= 2048 && M <= 16) ? 4 : 1;
+    const int mt = mt_for(M < 64 ? M : 64);
+    g.nt = (N % 64 == 0) ? 4 : (N % 32 == 0 ? 2 : 1);
+    if (mt == 4 && g.nt == 4) g.nt = 2;
     const int groups = N / (16 * g.nt);
     const int steps = Kd / 32;
-    const int mt = mt_for(M < 64 ? M : 64);
+    g.splits = 1;
+    if (allow_split && groups < 400) {
+        g.splits = (640 + groups / 2) / groups;
+        if (g.splits > 16) g.splits = 16;
+        while (g.splits > 1 && steps / g.splits < 16) --g.splits;
+    }
     g.waves = 4;
-    if (groups * 4 < 2048 && steps / 8 >= 8 && g.nt * mt <= 4) g.waves = 8;
+    if (g.nt * mt <= 4 && (groups * g.splits < 1200) && steps / (8 * g.splits) >= 2) g.waves = 8;
     return g;
 }
 

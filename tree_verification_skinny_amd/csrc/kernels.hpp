@@ -13,11 +13,13 @@ namespace sv {
 struct GemmShape {
     int M, N, Kd;
     int nt;         // 16-row weight tiles per workgroup (1, 2 or 4)
-    int waves;      // waves per workgroup splitting K (4, 8 or 16)
+    int waves;      // waves per workgroup splitting K inside it (4 or 8)
+    int splits;     // K splits across workgroups (fp32 partials when > 1)
 };
 
-// What a workgroup does with its finished tiles.
-enum { EPI_PLAIN = 0, EPI_QKV = 1, EPI_RESID = 2, EPI_SWIGLU = 3, EPI_ARGMAX = 4 };
+// What a workgroup does with its finished tiles: partial sums of its K split, or (whole K) one
+// of the fused epilogues.
+enum { EPI_PARTIAL = 0, EPI_QKV = 1, EPI_RESID = 2, EPI_SWIGLU = 3, EPI_ARGMAX = 4 };
 
 // The B operand. When ss != nullptr it is RMSNorm(X) * gain, computed on load from the
 // per-row sums of squares ss[ss_groups][M_total] the producer of X left behind.
@@ -34,7 +36,7 @@ struct GemmIn {
 
 struct GemmEpi {
     int D, F;                    // head dim; ffn (SwiGLU pairing)
-    // PLAIN: fp32 y [M][N]
+    // PARTIAL: fp32 y [splits][M][N]
     float *y;
     // QKV: q [M][nq][D]; K/V into cache slot ctx_len + (row % K) of request row / K
     bf16 *q, *k_pool, *v_pool;
@@ -53,7 +55,7 @@ struct GemmEpi {
 };
 
 int gemm_groups(const GemmShape &g);
-GemmShape plan_gemm(int M, int N, int Kd, bool paired);
+GemmShape plan_gemm(int M, int N, int Kd, bool allow_split);
 hipError_t gemm(const GemmShape &g, int epi, const GemmIn &in, const bf16 *Wp, const GemmEpi &ep,
                 hipStream_t st);
 hipError_t pack_weight(const bf16 *w, int n, int kd, bf16 *out, hipStream_t st);
@@ -94,6 +96,16 @@ hipError_t rope_table(const NodeInfo &ni, int M, int D, double theta, hipStream_
 hipError_t embed(const int32_t *tokens, const bf16 *table, int M, int H, int vocab, bf16 *x,
                  float *ss, bf16 *trace, hipStream_t st);
 int embed_ss_groups(int H);
+// Add the split-K partials of the QKV projection (split order), round to bf16, rotate q and k,
+// store q [M][nq][D] and the keys and values into the cache slots of the draft nodes.
+hipError_t reduce_qkv(const float *P, int splits, const NodeInfo &ni, const int32_t *ctx_len,
+                      const int32_t *block_table, int max_pages, int B, int K, int nq, int nkv,
+                      int D, bf16 *q, bf16 *k_pool, bf16 *v_pool, hipStream_t st);
+// Add the split-K partials of a projection into the residual stream: x = bf16(x + bf16(sum));
+// ss [H/256][M] = per-row sums of squares of the new x over 256-column groups.
+hipError_t reduce_resid(const float *P, int splits, int M, int H, bf16 *x, float *ss, bf16 *trace,
+                        hipStream_t st);
+int resid_ss_groups(int H);
 hipError_t argmax_partials(const float *logits, int M, int V, float *amax_val, int *amax_idx,
                            int n_chunks, hipStream_t st);
 int argmax_chunks(int V);

@@ -29,10 +29,10 @@ struct Plan {
     int L, H, nq, nkv, D, F, V;
     int qd, nqkv;
     GemmShape g_qkv, g_o, g_gu, g_down, g_lm;
-    int lm_groups, ss_groups_resid, ss_groups_embed;
+    int lm_groups, ss_groups_o, ss_groups_down, ss_groups_embed;
     int attn_chunks;
-    size_t o_depth, o_pos, o_status, o_anc, o_rope, o_x, o_ss, o_q, o_attn, o_h, o_po, o_pml,
-        o_amv, o_ami, total;
+    size_t o_depth, o_pos, o_status, o_anc, o_rope, o_x, o_ss, o_q, o_attn, o_h, o_part, o_po,
+        o_pml, o_amv, o_ami, total;
 };
 
 int check_cfg(const spec_model_cfg *c) {
@@ -69,21 +69,30 @@ int make_plan(const spec_model_cfg *c, int B, int K, int max_pages, Plan &p) {
     p.qd = p.nq * p.D;
     p.nqkv = (p.nq + 2 * p.nkv) * p.D;
     const int M = p.M;
+    const bool resid_split = p.H % 256 == 0;   // the residual pass works on 256-column groups
     p.g_qkv = plan_gemm(M, p.nqkv, p.H, true);
-    p.g_o = plan_gemm(M, p.H, p.qd, false);
-    p.g_gu = plan_gemm(M, 2 * p.F, p.H, true);
-    p.g_down = plan_gemm(M, p.H, p.F, false);
+    p.g_o = plan_gemm(M, p.H, p.qd, resid_split);
+    p.g_gu = plan_gemm(M, 2 * p.F, p.H, false);
+    p.g_down = plan_gemm(M, p.H, p.F, resid_split);
     p.g_lm = plan_gemm(M, p.V, p.H, false);
+    if (p.g_qkv.nt < 2 || p.g_gu.nt < 2) return SPEC_EUNSUPPORTED;
     p.lm_groups = gemm_groups(p.g_lm);
-    p.ss_groups_resid = gemm_groups(p.g_o);
-    if (gemm_groups(p.g_down) != p.ss_groups_resid) return SPEC_EUNSUPPORTED;
+    p.ss_groups_o = p.g_o.splits > 1 ? resid_ss_groups(p.H) : gemm_groups(p.g_o);
+    p.ss_groups_down = p.g_down.splits > 1 ? resid_ss_groups(p.H) : gemm_groups(p.g_down);
     p.ss_groups_embed = embed_ss_groups(p.H);
     const int64_t max_keys = (int64_t)max_pages * SPEC_PAGE_SIZE;
     p.attn_chunks = (int)((max_keys + kAttnChunk - 1) / kAttnChunk);
     const int group = p.nq / p.nkv;
+    size_t part = 16;
+    for (const GemmShape *g : {&p.g_qkv, &p.g_o, &p.g_down}) {
+        const size_t b = g->splits > 1 ? (size_t)g->splits * M * g->N * sizeof(float) : 0;
+        if (b > part) part = b;
+    }
+    int ss_groups = p.ss_groups_embed;
+    if (p.ss_groups_o > ss_groups) ss_groups = p.ss_groups_o;
+    if (p.ss_groups_down > ss_groups) ss_groups = p.ss_groups_down;
 
     const int amax_groups = p.lm_groups > argmax_chunks(p.V) ? p.lm_groups : argmax_chunks(p.V);
-    const int ss_groups = p.ss_groups_resid > p.ss_groups_embed ? p.ss_groups_resid : p.ss_groups_embed;
     Carver cv;
     p.o_depth = cv.take(sizeof(int32_t) * M);
     p.o_pos = cv.take(sizeof(int32_t) * M);
@@ -95,6 +104,7 @@ int make_plan(const spec_model_cfg *c, int B, int K, int max_pages, Plan &p) {
     p.o_q = cv.take(sizeof(uint16_t) * M * p.qd);
     p.o_attn = cv.take(sizeof(uint16_t) * M * p.qd);
     p.o_h = cv.take(sizeof(uint16_t) * M * p.F);
+    p.o_part = cv.take(part);
     p.o_po = cv.take(sizeof(float) * (size_t)B * p.nkv * p.attn_chunks * group * K * p.D);
     p.o_pml = cv.take(sizeof(float2) * (size_t)B * p.nkv * p.attn_chunks * group * K);
     p.o_amv = cv.take(sizeof(float) * (size_t)amax_groups * M);
@@ -180,6 +190,7 @@ int spec_verify(const spec_weights *w, const spec_kv_cache *kv, const int32_t *d
     bf16 *q = at<bf16>(workspace, p.o_q);
     bf16 *attn = at<bf16>(workspace, p.o_attn);
     bf16 *h = at<bf16>(workspace, p.o_h);
+    float *part = at<float>(workspace, p.o_part);
     float *amv = at<float>(workspace, p.o_amv);
     int *ami = at<int>(workspace, p.o_ami);
     bf16 *k_pool = static_cast<bf16 *>(kv->k_pool);
@@ -209,6 +220,7 @@ int spec_verify(const spec_weights *w, const spec_kv_cache *kv, const int32_t *d
     ep.logits = logits;
     ep.amax_val = amv;
     ep.amax_idx = ami;
+    ep.y = part;
 
     // operand that is RMSNorm(x) * gain, from the sums of squares in ss
     auto normed = [&](const void *gain, int ss_groups) {
@@ -250,22 +262,49 @@ int spec_verify(const spec_weights *w, const spec_kv_cache *kv, const int32_t *d
     int ss_groups = p.ss_groups_embed;
     for (int l = 0; l < p.L; ++l) {
         const spec_layer_weights &lw = w->layers[l];
-        ep.k_pool = k_pool + l * layer_stride;
-        ep.v_pool = v_pool + l * layer_stride;
-        SV_TRY(gemm(p.g_qkv, EPI_QKV, normed(lw.attn_norm, ss_groups),
-                    static_cast<const bf16 *>(lw.w_qkv), ep, stream));
-        aa.k_pool = ep.k_pool;
-        aa.v_pool = ep.v_pool;
+        bf16 *kl = k_pool + l * layer_stride;
+        bf16 *vl = v_pool + l * layer_stride;
+        ep.k_pool = kl;
+        ep.v_pool = vl;
+        // q, k, v = RMSNorm(x) . Wqkv^T; RoPE; K/V into the cache
+        if (p.g_qkv.splits > 1) {
+            SV_TRY(gemm(p.g_qkv, EPI_PARTIAL, normed(lw.attn_norm, ss_groups),
+                        static_cast<const bf16 *>(lw.w_qkv), ep, stream));
+            SV_TRY(reduce_qkv(part, p.g_qkv.splits, ni, ctx_len, kv->block_table,
+                              kv->max_pages_per_req, p.B, p.K, p.nq, p.nkv, p.D, q, kl, vl, stream));
+        } else {
+            SV_TRY(gemm(p.g_qkv, EPI_QKV, normed(lw.attn_norm, ss_groups),
+                        static_cast<const bf16 *>(lw.w_qkv), ep, stream));
+        }
+        aa.k_pool = kl;
+        aa.v_pool = vl;
         SV_TRY(attention(aa, stream));
+        // x += o . Wo^T
         ep.trace = nullptr;
-        SV_TRY(gemm(p.g_o, EPI_RESID, plain(attn, p.qd), static_cast<const bf16 *>(lw.w_o), ep,
-                    stream));
-        ss_groups = p.ss_groups_resid;
+        if (p.g_o.splits > 1) {
+            SV_TRY(gemm(p.g_o, EPI_PARTIAL, plain(attn, p.qd), static_cast<const bf16 *>(lw.w_o), ep,
+                        stream));
+            SV_TRY(reduce_resid(part, p.g_o.splits, M, p.H, x, ss, nullptr, stream));
+        } else {
+            SV_TRY(gemm(p.g_o, EPI_RESID, plain(attn, p.qd), static_cast<const bf16 *>(lw.w_o), ep,
+                        stream));
+        }
+        ss_groups = p.ss_groups_o;
+        // h = silu(gate) * up from RMSNorm(x)
         SV_TRY(gemm(p.g_gu, EPI_SWIGLU, normed(lw.mlp_norm, ss_groups),
                     static_cast<const bf16 *>(lw.w_gate_up), ep, stream));
-        ep.trace = trace ? trace + (int64_t)(l + 1) * M * p.H : nullptr;
-        SV_TRY(gemm(p.g_down, EPI_RESID, plain(h, p.F), static_cast<const bf16 *>(lw.w_down), ep,
-                    stream));
+        // x += h . Wdown^T
+        bf16 *tr = trace ? trace + (int64_t)(l + 1) * M * p.H : nullptr;
+        if (p.g_down.splits > 1) {
+            SV_TRY(gemm(p.g_down, EPI_PARTIAL, plain(h, p.F), static_cast<const bf16 *>(lw.w_down), ep,
+                        stream));
+            SV_TRY(reduce_resid(part, p.g_down.splits, M, p.H, x, ss, tr, stream));
+        } else {
+            ep.trace = tr;
+            SV_TRY(gemm(p.g_down, EPI_RESID, plain(h, p.F), static_cast<const bf16 *>(lw.w_down), ep,
+                        stream));
+        }
+        ss_groups = p.ss_groups_down;
     }
     SV_TRY(gemm(p.g_lm, EPI_ARGMAX, normed(w->final_norm, ss_groups),
                 static_cast<const bf16 *>(w->lm_head), ep, stream));
@@ -296,8 +335,7 @@ int spec_commit_kv(const spec_model_cfg *cfg, const spec_kv_cache *kv, const int
 static int skinny_shape(int m, int n, int kd, GemmShape &g) {
     if (m < 1 || n < 1 || kd < 1) return SPEC_EINVAL;
     if (kd % 32 != 0 || n % 16 != 0) return SPEC_EUNSUPPORTED;
-    g = plan_gemm(m, n, kd, false);
-    if (n % (16 * g.nt) != 0) return SPEC_EUNSUPPORTED;
+    g = plan_gemm(m, n, kd, true);
     return SPEC_OK;
 }
 
@@ -315,7 +353,7 @@ int spec_skinny_gemm_bytes(int m, int n, int kd, size_t *bytes) {
     GemmShape g;
     const int rc = skinny_shape(m, n, kd, g);
     if (rc != SPEC_OK) return rc;
-    *bytes = (size_t)m * n * sizeof(float);
+    *bytes = (size_t)g.splits * m * n * sizeof(float);
     return SPEC_OK;
 }
 
@@ -325,14 +363,14 @@ int spec_skinny_gemm(const void *x, int m, int kd, const void *w, int n, float *
     GemmShape g;
     const int rc = skinny_shape(m, n, kd, g);
     if (rc != SPEC_OK) return rc;
-    if (partial_bytes < (size_t)m * n * sizeof(float)) return SPEC_EWORKSPACE;
-    *splits = 1;
+    if (partial_bytes < (size_t)g.splits * m * n * sizeof(float)) return SPEC_EWORKSPACE;
+    *splits = g.splits;
     GemmIn in = {};
     in.X = static_cast<const bf16 *>(x);
     in.ldx = kd;
     GemmEpi ep = {};
     ep.y = partials;
-    SV_TRY(gemm(g, EPI_PLAIN, in, static_cast<const bf16 *>(w), ep, stream));
+    SV_TRY(gemm(g, EPI_PARTIAL, in, static_cast<const bf16 *>(w), ep, stream));
     return SPEC_OK;
 }
 
