@@ -47,6 +47,25 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
     const int R = group * K;
     const int QT = (R + 15) >> 4;
 
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r16 = lane & 15, grp = lane >> 4;
+    // the first query tile's fragments are fetched before the chunk, so the two overlap
+    bf16x8 qf_next[D / 32];
+    auto q_ptr = [&](int t, bool &col_ok, int &tok, int &hh) {
+        const int rho = 16 * t + r16;
+        col_ok = rho < R;
+        hh = col_ok ? rho / K : 0;
+        tok = col_ok ? rho % K : 0;
+        return q + ((int64_t)(b * K + tok) * nq + g * group + hh) * D;
+    };
+    if (wave < QT) {
+        bool ok_;
+        int tok_, hh_;
+        const bf16 *qrow = q_ptr(wave, ok_, tok_, hh_);
+#pragma unroll
+        for (int ds = 0; ds < D / 32; ++ds) qf_next[ds] = *(const bf16x8 *)(qrow + ds * 32 + grp * 8);
+    }
+
     // ---- stage the chunk: K rows as stored, V already transposed in the page ---------------
     // Every thread issues all of its page loads before the first LDS store, so the chunk's
     // 2 x 8 x 16 B per thread are in flight together.
@@ -54,10 +73,16 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
         constexpr int NP = CH / 16;
         const int e = threadIdx.x * 8;           // element offset inside a 16 x D page
         const bool has = e < 16 * D;
+        // page ids: read unconditionally (index clamped to the request's last page, always in
+        // bounds) so all reads issue together, then masked
+        const int32_t *bt = block_table + (int64_t)b * max_pages;
+        const int last = (T - 1) >> 4;
         int pages[NP];
 #pragma unroll
+        for (int p = 0; p < NP; ++p) pages[p] = bt[min((kb >> 4) + p, last)];
+#pragma unroll
         for (int p = 0; p < NP; ++p)
-            pages[p] = (has && p < npages) ? block_table[(int64_t)b * max_pages + (kb >> 4) + p] : -1;
+            if (!(has && p < npages)) pages[p] = -1;
         bf16x8 kr[NP], vr[NP];
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
@@ -85,21 +110,25 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
     }
     __syncthreads();
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int r16 = lane & 15, grp = lane >> 4;
     const int nsteps = (nvalid + 31) >> 5;
     const int kr0 = 8 * (r16 >> 2) + (r16 & 3);   // S^T tile 0 key row of this lane (tile 1: +4)
 
     for (int t = wave; t < QT; t += 4) {
         const int rho = 16 * t + r16;             // query column of this lane
-        const bool col_ok = rho < R;
-        const int hh = col_ok ? rho / K : 0, tok = col_ok ? rho % K : 0;
-        const int node = b * K + tok;
-        const uint64_t am = anc[node];
-        const bf16 *qrow = q + ((int64_t)node * nq + g * group + hh) * D;
+        bool col_ok;
+        int tok, hh;
+        q_ptr(t, col_ok, tok, hh);
+        const uint64_t am = anc[b * K + tok];
         bf16x8 qf[D / 32];
 #pragma unroll
-        for (int ds = 0; ds < D / 32; ++ds) qf[ds] = *(const bf16x8 *)(qrow + ds * 32 + grp * 8);
+        for (int ds = 0; ds < D / 32; ++ds) qf[ds] = qf_next[ds];
+        if (t + 4 < QT) {                         // next tile's fragments, one tile ahead
+            bool o2;
+            int t2, h2;
+            const bf16 *qn = q_ptr(t + 4, o2, t2, h2);
+#pragma unroll
+            for (int ds = 0; ds < D / 32; ++ds) qf_next[ds] = *(const bf16x8 *)(qn + ds * 32 + grp * 8);
+        }
         floatx4 o[D / 16];
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt) o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -165,24 +194,29 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
     }
 }
 
-// Merge the chunk partials of one node: o = sum_c 2^(m_c - m*) O_c / sum_c 2^(m_c - m*) l_c, one
-// pass with a running maximum. A thread owns 4 consecutive elements of one head.
+// Merge the chunk partials of one (node, q head): o = sum_c 2^(m_c - m*) O_c / sum_c 2^(m_c - m*) l_c.
+// 256 threads = (D/4) column quads x CG chunk groups; each thread merges its chunks c = cg,
+// cg + CG, ... with every load issued before the arithmetic, then the CG states are merged in
+// LDS in chunk-group order.
 template <int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(
     const float *__restrict__ part_o, const float2 *__restrict__ part_ml,
     const int32_t *__restrict__ ctx_len, const int32_t *__restrict__ status, int K, int nq,
     int nkv, int n_chunks, bf16 *__restrict__ out) {
-    constexpr int TPH = D / 4;           // threads per head
-    constexpr int HPB = 256 / TPH;       // heads per block
-    const int row = blockIdx.x;
-    const int h = blockIdx.y * HPB + threadIdx.x / TPH;
-    const int d4 = (threadIdx.x % TPH) * 4;
-    if (h >= nq) return;
+    constexpr int TQ = D / 4;            // threads per column quad set
+    constexpr int CG = 256 / TQ;         // chunk groups: 8 (D=128) or 16 (D=64)
+    constexpr int PER = 8;               // chunks per thread held in flight
+    __shared__ float s_m[CG][TQ], s_l[CG][TQ];
+    __shared__ floatx4 s_o[CG][TQ];
+    const int row = blockIdx.x, h = blockIdx.y;
+    const int d4 = (threadIdx.x % TQ) * 4, cg = threadIdx.x / TQ;
     const int b = row / K, tok = row % K;
     bf16 *dst = out + ((int64_t)row * nq + h) * D + d4;
     if (status[b] != 0) {
+        if (cg == 0) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) dst[j] = (bf16)0.0f;
+            for (int j = 0; j < 4; ++j) dst[j] = (bf16)0.0f;
+        }
         return;
     }
     const int group = nq / nkv, g = h / group, hh = h % group;
@@ -191,15 +225,43 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(
     const int64_t base = ((int64_t)b * nkv + g) * n_chunks * R + rho;
     float m = -INFINITY, l = 0.f;
     floatx4 o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-    for (int c = 0; c < nc; ++c) {
-        const float2 ml = part_ml[base + (int64_t)c * R];
-        const floatx4 oc = *(const floatx4 *)(part_o + (base + (int64_t)c * R) * D + d4);
-        if (ml.x == -INFINITY) continue;
-        const float mn = fmaxf(m, ml.x);
-        const float a = exp2f(m - mn), w = exp2f(ml.x - mn);
-        l = l * a + ml.y * w;
-        o = o * a + oc * w;
+    for (int c0 = cg; c0 < nc; c0 += CG * PER) {
+        float2 ml[PER];
+        floatx4 oc[PER];
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int c = c0 + i * CG;
+            if (c < nc) {
+                ml[i] = part_ml[base + (int64_t)c * R];
+                oc[i] = *(const floatx4 *)(part_o + (base + (int64_t)c * R) * D + d4);
+            } else {
+                ml[i] = make_float2(-INFINITY, 0.f);
+                oc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            if (ml[i].x == -INFINITY) continue;
+            const float mn = fmaxf(m, ml[i].x);
+            const float a = exp2f(m - mn), w = exp2f(ml[i].x - mn);
+            l = l * a + ml[i].y * w;
+            o = o * a + oc[i] * w;
+            m = mn;
+        }
+    }
+    s_m[cg][threadIdx.x % TQ] = m;
+    s_l[cg][threadIdx.x % TQ] = l;
+    s_o[cg][threadIdx.x % TQ] = o;
+    __syncthreads();
+    if (cg != 0) return;
+    for (int k = 1; k < CG; ++k) {
+        const float mk = s_m[k][threadIdx.x], lk = s_l[k][threadIdx.x];
+        if (mk == -INFINITY) continue;
+        const floatx4 ok = s_o[k][threadIdx.x];
+        const float mn = fmaxf(m, mk);
+        const float a = exp2f(m - mn), w = exp2f(mk - mn);
+        l = l * a + lk * w;
+        o = o * a + ok * w;
         m = mn;
     }
 #pragma unroll
@@ -215,7 +277,7 @@ hipError_t attention(const AttnArgs &a, hipStream_t st) {
                            a.n_chunks, scale_log2, a.part_o, a.part_ml);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(attn_combine_kernel<128>, dim3(a.B * a.K, (a.nq + 7) / 8), dim3(256), 0, st,
+        hipLaunchKernelGGL(attn_combine_kernel<128>, dim3(a.B * a.K, a.nq), dim3(256), 0, st,
                            a.part_o, a.part_ml, a.ctx_len, a.status, a.K, a.nq, a.nkv, a.n_chunks, a.out);
     } else {
         hipLaunchKernelGGL(attn_partial_kernel<64>, grid, dim3(256), 0, st, a.q, a.k_pool, a.v_pool,
@@ -223,7 +285,7 @@ hipError_t attention(const AttnArgs &a, hipStream_t st) {
                            a.n_chunks, scale_log2, a.part_o, a.part_ml);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(attn_combine_kernel<64>, dim3(a.B * a.K, (a.nq + 15) / 16), dim3(256), 0, st,
+        hipLaunchKernelGGL(attn_combine_kernel<64>, dim3(a.B * a.K, a.nq), dim3(256), 0, st,
                            a.part_o, a.part_ml, a.ctx_len, a.status, a.K, a.nq, a.nkv, a.n_chunks, a.out);
     }
     return hipGetLastError();

@@ -1,8 +1,7 @@
 // k_elementwise.hip — the small kernels around the GEMMs and attention of the verify pass:
-// draft-tree bookkeeping, RoPE angles, the embedding gather (with the per-row sums of squares the
-// first RMSNorm needs), the split-K passes of the narrow projections (RoPE + KV store; residual
-// add + sums of squares), the vocab-wide greedy choice with the accepted-path walk, and the
-// commit of the accepted path's KV rows.
+// draft-tree bookkeeping, RoPE angles, the embedding gather with the first RMSNorm, the split-K
+// passes of the narrow projections (RoPE + KV store; residual add + RMSNorm), the vocab-wide
+// greedy choice with the accepted-path walk, and the commit of the accepted path's KV rows.
 //
 // Lossless greedy verification: a draft token is accepted only if it equals the target's greedy
 // choice after its parent, and only along a path whose every earlier token was accepted
@@ -96,30 +95,70 @@ hipError_t rope_table(const NodeInfo &ni, int M, int D, double theta, hipStream_
     return hipGetLastError();
 }
 
-// ---- embedding gather + per-row sums of squares over 64-column groups -------------------------
-// The first projection applies RMSNorm on its operand load from these sums.
-__global__ __launch_bounds__(64) void embed_kernel(const int32_t *__restrict__ tokens,
-                                                   const bf16 *__restrict__ table, int M, int H,
-                                                   int vocab, bf16 *__restrict__ x,
-                                                   float *__restrict__ ss, bf16 *__restrict__ trace) {
-    const int row = blockIdx.x, g = blockIdx.y, lane = threadIdx.x;   // one wave per 64 columns
-    int tok = tokens[row];
-    if (tok < 0 || tok >= vocab) tok = 0;   // the request is already marked bad; stay in bounds
-    const int col = g * 64 + lane;
-    const bf16 v = table[(int64_t)tok * H + col];
-    x[(int64_t)row * H + col] = v;
-    if (trace) trace[(int64_t)row * H + col] = v;
-    const float f = to_f(v);
-    const float sum = wave_sum(f * f);
-    if (lane == 0) ss[(int64_t)g * M + row] = sum;
+// ---- row-wise RMSNorm helpers (one 1024-thread workgroup per row) --------------------------------
+// RMSNorm: u = bf16((x / sqrt(mean(x^2) + eps)) * g), the sum of squares in fp32. A thread owns
+// column quads q = tid, tid + 1024, ...; every load of the row is issued before any is used.
+constexpr int kRowThreads = 1024;
+constexpr int kRowQuads = 4;        // quads per thread: hidden <= 4 * 4 * 1024
+
+__device__ __forceinline__ float block_sum_1024(float v, float *red) {
+    v = wave_sum(v);
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) red[w] = v;
+    __syncthreads();
+    float t = 0.f;
+#pragma unroll
+    for (int i = 0; i < kRowThreads / 64; ++i) t += red[i];
+    return t;
 }
 
-int embed_ss_groups(int H) { return H / 64; }
+__device__ __forceinline__ void norm_store(const float (&xv)[kRowQuads][4], float ss, int H, float eps,
+                                           const bf16 *__restrict__ gain, bf16 *__restrict__ u) {
+    const float inv = 1.0f / sqrtf(ss / (float)H + eps);
+#pragma unroll
+    for (int i = 0; i < kRowQuads; ++i) {
+        const int q = threadIdx.x + i * kRowThreads;
+        if (q * 4 >= H) break;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) u[q * 4 + j] = to_bf((xv[i][j] * inv) * to_f(gain[q * 4 + j]));
+    }
+}
 
-hipError_t embed(const int32_t *tokens, const bf16 *table, int M, int H, int vocab, bf16 *x,
-                 float *ss, bf16 *trace, hipStream_t st) {
-    hipLaunchKernelGGL(embed_kernel, dim3(M, H / 64), dim3(64), 0, st, tokens, table, M, H, vocab, x,
-                       ss, trace);
+// ---- embedding gather + first RMSNorm ------------------------------------------------------------
+__global__ __launch_bounds__(kRowThreads) void embed_norm_kernel(
+    const int32_t *__restrict__ tokens, const bf16 *__restrict__ table, int H, int vocab,
+    const bf16 *__restrict__ gain, float eps, bf16 *__restrict__ x, bf16 *__restrict__ u,
+    bf16 *__restrict__ trace) {
+    __shared__ float red[kRowThreads / 64];
+    const int row = blockIdx.x;
+    int tok = tokens[row];
+    if (tok < 0 || tok >= vocab) tok = 0;   // the request is already marked bad; stay in bounds
+    const bf16 *src = table + (int64_t)tok * H;
+    float xv[kRowQuads][4];
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < kRowQuads; ++i) {
+        const int q = threadIdx.x + i * kRowThreads;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) xv[i][j] = 0.f;
+        if (q * 4 >= H) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const bf16 v = src[q * 4 + j];
+            xv[i][j] = to_f(v);
+            x[(int64_t)row * H + q * 4 + j] = v;
+            if (trace) trace[(int64_t)row * H + q * 4 + j] = v;
+            ss += xv[i][j] * xv[i][j];
+        }
+    }
+    ss = block_sum_1024(ss, red);
+    norm_store(xv, ss, H, eps, gain, u + (int64_t)row * H);
+}
+
+hipError_t embed_norm(const int32_t *tokens, const bf16 *table, const bf16 *gain, int M, int H,
+                      int vocab, float eps, bf16 *x, bf16 *u, bf16 *trace, hipStream_t st) {
+    hipLaunchKernelGGL(embed_norm_kernel, dim3(M), dim3(kRowThreads), 0, st, tokens, table, H, vocab,
+                       gain, eps, x, u, trace);
     return hipGetLastError();
 }
 
@@ -180,36 +219,49 @@ hipError_t reduce_qkv(const float *P, int splits, const NodeInfo &ni, const int3
     return hipGetLastError();
 }
 
-// ---- residual split-K pass: x = bf16(x + bf16(sum_s P[s])), sums of squares per 256 columns ----
-__global__ __launch_bounds__(64) void reduce_resid_kernel(const float *__restrict__ P, int splits,
-                                                          int M, int H, bf16 *__restrict__ x,
-                                                          float *__restrict__ ss,
-                                                          bf16 *__restrict__ trace) {
-    const int row = blockIdx.x, g = blockIdx.y, lane = threadIdx.x;
-    const int col = g * 256 + lane * 4;
+// ---- residual split-K pass + RMSNorm: x = bf16(x + bf16(sum_s P[s])), u = RMSNorm(x) * g --------
+__global__ __launch_bounds__(kRowThreads) void reduce_resid_norm_kernel(
+    const float *__restrict__ P, int splits, int M, int H, const bf16 *__restrict__ gain, float eps,
+    bf16 *__restrict__ x, bf16 *__restrict__ u, bf16 *__restrict__ trace) {
+    __shared__ float red[kRowThreads / 64];
+    const int row = blockIdx.x;
     const int64_t pstride = (int64_t)M * H;
-    const float *pr = P + (int64_t)row * H + col;
-    floatx4 y = *(const floatx4 *)pr;
-    for (int s = 1; s < splits; ++s) y += *(const floatx4 *)(pr + s * pstride);
-    bf16 *xr = x + (int64_t)row * H + col;
-    float sq = 0.f;
+    const float *pr = P + (int64_t)row * H;
+    bf16 *xr = x + (int64_t)row * H;
+    float xv[kRowQuads][4];
+    floatx4 y[kRowQuads];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const float xn = round_bf(to_f(xr[j]) + round_bf(y[j]));
-        sq += xn * xn;
-        xr[j] = to_bf(xn);
-        if (trace) trace[(int64_t)row * H + col + j] = to_bf(xn);
+    for (int i = 0; i < kRowQuads; ++i) {
+        const int q = threadIdx.x + i * kRowThreads;
+        y[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+        if (q * 4 >= H) continue;
+        y[i] = *(const floatx4 *)(pr + q * 4);
+        for (int s = 1; s < splits; ++s) y[i] += *(const floatx4 *)(pr + s * pstride + q * 4);
     }
-    sq = wave_sum(sq);
-    if (lane == 0) ss[(int64_t)g * M + row] = sq;
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < kRowQuads; ++i) {
+        const int q = threadIdx.x + i * kRowThreads;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) xv[i][j] = 0.f;
+        if (q * 4 >= H) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float xn = round_bf(to_f(xr[q * 4 + j]) + round_bf(y[i][j]));
+            xv[i][j] = xn;
+            ss += xn * xn;
+            xr[q * 4 + j] = to_bf(xn);
+            if (trace) trace[(int64_t)row * H + q * 4 + j] = to_bf(xn);
+        }
+    }
+    ss = block_sum_1024(ss, red);
+    norm_store(xv, ss, H, eps, gain, u + (int64_t)row * H);
 }
 
-int resid_ss_groups(int H) { return H / 256; }
-
-hipError_t reduce_resid(const float *P, int splits, int M, int H, bf16 *x, float *ss, bf16 *trace,
-                        hipStream_t st) {
-    hipLaunchKernelGGL(reduce_resid_kernel, dim3(M, H / 256), dim3(64), 0, st, P, splits, M, H, x, ss,
-                       trace);
+hipError_t reduce_resid_norm(const float *P, int splits, int M, int H, const bf16 *gain, float eps,
+                             bf16 *x, bf16 *u, bf16 *trace, hipStream_t st) {
+    hipLaunchKernelGGL(reduce_resid_norm_kernel, dim3(M), dim3(kRowThreads), 0, st, P, splits, M, H,
+                       gain, eps, x, u, trace);
     return hipGetLastError();
 }
 

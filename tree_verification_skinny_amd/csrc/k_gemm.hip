@@ -10,10 +10,8 @@
 //     32-wide K step) is 1 KB, lane l's 16 bytes are W[16 tile + l%16][32 step + 8(l/16) .. +7],
 //     and a tile's K steps follow each other. One 128-bit load per lane reads a whole fragment
 //     as 1 KB of contiguous HBM, straight into the registers the MFMA consumes.
-//   * The activations X [M][Kd] (cache resident) are the B operand, loaded with the same K order.
-//     Where the consumer of a projection is an RMSNorm, the norm is applied on this load
-//     (x * rsqrt(mean x^2 + eps) * g, rounded to bf16), from per-row sums of squares the
-//     producer left behind, so no separate norm pass touches the activations.
+//   * The activations X [M][Kd] (cache resident, already normalised where an RMSNorm precedes
+//     the projection) are the B operand, loaded with the same K order.
 //   * A workgroup of W waves (4 or 8) owns NT weight tiles over a K range; its waves interleave
 //     over the 32-wide K steps (so together they read each tile front to back) and add their
 //     sums in LDS in wave order. Projections with few output columns split K over workgroups
@@ -21,10 +19,9 @@
 //     workgroup adds" fixup needs agent-scope release/acquire fences, which cost more on this
 //     chip than the extra pass); wide projections run whole and finish their epilogue in place.
 //     Either way no workgroup waits for another and results do not depend on timing.
-//   * Epilogues: RoPE + q/K/V store into the paged cache (QKV), residual add + per-row sum of
-//     squares (O and down projections), SwiGLU (gate/up), and the per-tile greedy maximum of the
-//     output head. Tile groups are laid out so that every pair an epilogue needs (RoPE's j and
-//     j + d/2, SwiGLU's gate n and up n) sits in the same lane.
+//   * Epilogues of the whole-K projections: SwiGLU (gate/up; a group holds gate tiles and the
+//     matching up tiles, so gate n and up n sit in the same lane) and the per-group greedy
+//     maximum of the output head.
 // MFMA lane layout (16x16x32): lane l supplies A row l%16, K elements 8*(l/16)..+7, and B
 // column l%16, the same K elements; it receives D rows 4*(l/16)..+3 of column l%16.
 #include "kernels.hpp"
@@ -56,16 +53,12 @@ hipError_t pack_weight(const bf16 *w, int n, int kd, bf16 *out, hipStream_t st) 
 }
 
 // ---- column layout of a tile group --------------------------------------------------------------
-// Contiguous for plain outputs; paired halves for RoPE (j with j + d/2 inside each head) and for
-// SwiGLU (gate column n with up column F + n).
+// Contiguous for plain outputs; paired halves for SwiGLU (gate column n with up column F + n) so
+// that a lane holds both operands of its outputs.
 template <int NT, int EPI>
-__device__ __forceinline__ int tile_col(int ng, int t, int D, int F) {
-    constexpr int PH = 8 * NT;   // columns in each half of a paired group
-    if constexpr (EPI == EPI_QKV) {
-        const int half = D / 2, per_head = half / PH;
-        const int c0 = (ng / per_head) * D + (ng % per_head) * PH;
-        return t < NT / 2 ? c0 + 16 * t : c0 + half + 16 * (t - NT / 2);
-    } else if constexpr (EPI == EPI_SWIGLU) {
+__device__ __forceinline__ int tile_col(int ng, int t, int F) {
+    if constexpr (EPI == EPI_SWIGLU) {
+        constexpr int PH = 8 * NT;   // columns in each half of a paired group
         return t < NT / 2 ? ng * PH + 16 * t : F + ng * PH + 16 * (t - NT / 2);
     } else {
         return ng * 16 * NT + 16 * t;
@@ -77,7 +70,7 @@ struct Acc {
     floatx4 v[NT][MT];
 };
 
-template <int NT, int MT, int W, int EPI, bool NORM>
+template <int NT, int MT, int W, int EPI>
 __global__ __launch_bounds__(64 * W) void gemm_kernel(GemmIn in, const bf16 *__restrict__ Wp,
                                                       int N, int Kd, int n_groups, int ksteps,
                                                       GemmEpi ep) {
@@ -95,53 +88,15 @@ __global__ __launch_bounds__(64 * W) void gemm_kernel(GemmIn in, const bf16 *__r
     const bf16 *wp[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-        const int tile = tile_col<NT, EPI>(ng, t, ep.D, ep.F) >> 4;
+        const int tile = tile_col<NT, EPI>(ng, t, ep.F) >> 4;
         wp[t] = Wp + (((int64_t)tile * S) * 64 + lane) * 8;
     }
     const bf16 *xp[MT];
-    float inv[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
         const int m = min(16 * mt + r16, M - 1);
         xp[mt] = in.X + (int64_t)(m0 + m) * in.ldx + grp * 8;
-        inv[mt] = 1.f;
     }
-    if constexpr (NORM) {
-        // RMS of each row from the producer's per-group sums of squares: every wave adds a
-        // strided share of the groups, then the shares are added in wave order.
-        __shared__ float ssr[MT][W][16];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const int m = min(16 * mt + r16, M - 1);
-            float part = 0.f;
-            for (int g = wave * 4 + grp; g < in.ss_groups; g += 4 * W)
-                part += in.ss[(int64_t)g * in.M_total + m0 + m];
-            part += __shfl_xor(part, 16, 64);
-            part += __shfl_xor(part, 32, 64);
-            if (grp == 0) ssr[mt][wave][r16] = part;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            float tot = 0.f;
-            for (int w = 0; w < W; ++w) tot += ssr[mt][w][r16];
-            inv[mt] = 1.0f / sqrtf(tot / (float)in.H + in.eps);
-        }
-    }
-    const bf16 *gp = in.gain + grp * 8;
-
-    auto load_b = [&](int step, int mt) -> bf16x8 {
-        const bf16x8 xv = *(const bf16x8 *)(xp[mt] + step * 32);
-        if constexpr (!NORM) {
-            return xv;
-        } else {
-            const bf16x8 gv = *(const bf16x8 *)(gp + step * 32);
-            bf16x8 u;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) u[j] = to_bf((to_f(xv[j]) * inv[mt]) * to_f(gv[j]));
-            return u;
-        }
-    };
 
     Acc<NT, MT> acc;
 #pragma unroll
@@ -149,7 +104,7 @@ __global__ __launch_bounds__(64 * W) void gemm_kernel(GemmIn in, const bf16 *__r
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc.v[t][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    constexpr int U = (NT * MT >= 8 || (W >= 8 && NT * MT >= 4)) ? 2 : 4;   // K steps in flight per wave
+    constexpr int U = (NT * MT >= 8 || (W == 8 && NT * MT == 4)) ? 2 : 4;   // K steps per batch
     int s = s_begin + wave;
     for (; s + W * (U - 1) < s_end; s += W * U) {
         bf16x8 a[U][NT], b[U][MT];
@@ -161,7 +116,7 @@ __global__ __launch_bounds__(64 * W) void gemm_kernel(GemmIn in, const bf16 *__r
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) b[u][mt] = load_b(s + W * u, mt);
+            for (int mt = 0; mt < MT; ++mt) b[u][mt] = *(const bf16x8 *)(xp[mt] + (s + W * u) * 32);
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
@@ -174,7 +129,7 @@ __global__ __launch_bounds__(64 * W) void gemm_kernel(GemmIn in, const bf16 *__r
 #pragma unroll
         for (int t = 0; t < NT; ++t) a[t] = *(const bf16x8 *)(wp[t] + (int64_t)s * 512);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) b[mt] = load_b(s, mt);
+        for (int mt = 0; mt < MT; ++mt) b[mt] = *(const bf16x8 *)(xp[mt] + s * 32);
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -198,7 +153,7 @@ __global__ __launch_bounds__(64 * W) void gemm_kernel(GemmIn in, const bf16 *__r
 
     int col[NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) col[t] = tile_col<NT, EPI>(ng, t, ep.D, ep.F) + 4 * grp;
+    for (int t = 0; t < NT; ++t) col[t] = tile_col<NT, EPI>(ng, t, ep.F) + 4 * grp;
 
     // ---- epilogues ------------------------------------------------------------------------------
 #pragma unroll
@@ -212,70 +167,6 @@ __global__ __launch_bounds__(64 * W) void gemm_kernel(GemmIn in, const bf16 *__r
                 for (int t = 0; t < NT; ++t)
                     *(floatx4 *)(ep.y + ((int64_t)split * in.M_total + row) * N + col[t]) = acc.v[t][mt];
             }
-        } else if constexpr (EPI == EPI_QKV) {
-#pragma clang fp contract(off)
-            if (!live) continue;
-            const int b = row / ep.K, il = row % ep.K;
-            const bool ok = ep.status[b] == 0;
-            const int half = ep.D / 2;
-            int page = 0, slot = 0;
-            if (ok) {
-                const int pos = ep.ctx_len[b] + il;
-                page = page_of(ep.block_table, ep.max_pages, b, pos);
-                slot = pos & 15;
-            }
-#pragma unroll
-            for (int t = 0; t < NT / 2; ++t) {
-                const int head = col[t] / ep.D, jj = col[t] % ep.D;   // jj < d/2, 4 columns
-                bf16 lo[4], hi[4];
-                if (head < ep.nq + ep.nkv) {
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const float a = round_bf(acc.v[t][mt][j]);
-                        const float c = round_bf(acc.v[t + NT / 2][mt][j]);
-                        const float2 cs = ep.rope[(int64_t)row * half + jj + j];
-                        lo[j] = to_bf(a * cs.x - c * cs.y);
-                        hi[j] = to_bf(c * cs.x + a * cs.y);
-                    }
-                } else {
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        lo[j] = to_bf(acc.v[t][mt][j]);
-                        hi[j] = to_bf(acc.v[t + NT / 2][mt][j]);
-                    }
-                }
-                if (head < ep.nq) {
-                    bf16 *qh = ep.q + ((int64_t)row * ep.nq + head) * ep.D + jj;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) { qh[j] = lo[j]; qh[j + half] = hi[j]; }
-                } else if (ok && head < ep.nq + ep.nkv) {
-                    bf16 *kr = ep.k_pool + (((int64_t)page * ep.nkv + (head - ep.nq)) * 16 + slot) * ep.D + jj;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) { kr[j] = lo[j]; kr[j + half] = hi[j]; }
-                } else if (ok) {
-                    bf16 *vr = ep.v_pool + (((int64_t)page * ep.nkv + (head - ep.nq - ep.nkv)) * ep.D + jj) * 16 + slot;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) { vr[j * 16] = lo[j]; vr[(j + half) * 16] = hi[j]; }
-                }
-            }
-        } else if constexpr (EPI == EPI_RESID) {
-            float ss = 0.f;
-            if (live) {
-#pragma unroll
-                for (int t = 0; t < NT; ++t) {
-                    bf16 *xr = ep.x + (int64_t)row * N + col[t];
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const float xn = round_bf(to_f(xr[j]) + round_bf(acc.v[t][mt][j]));
-                        ss += xn * xn;
-                        xr[j] = to_bf(xn);
-                        if (ep.trace) ep.trace[(int64_t)row * N + col[t] + j] = to_bf(xn);
-                    }
-                }
-            }
-            ss += __shfl_xor(ss, 16, 64);
-            ss += __shfl_xor(ss, 32, 64);
-            if (live && grp == 0) ep.ss_out[(int64_t)ng * in.M_total + row] = ss;
         } else if constexpr (EPI == EPI_SWIGLU) {
             if (!live) continue;
 #pragma unroll
@@ -316,51 +207,50 @@ static int mt_for(int m) { return m <= 16 ? 1 : (m <= 32 ? 2 : 4); }
 
 int gemm_groups(const GemmShape &g) { return g.N / (16 * g.nt); }
 
-template <int NT, int MT, int W, int EPI, bool NORM>
+template <int NT, int MT, int W, int EPI>
 static hipError_t launch(const GemmShape &g, const GemmIn &in, const bf16 *Wp, const GemmEpi &ep,
                          hipStream_t st) {
     const int steps = g.Kd >> 5;
     const int ks = (steps + g.splits - 1) / g.splits;
-    hipLaunchKernelGGL((gemm_kernel<NT, MT, W, EPI, NORM>), dim3(gemm_groups(g) * g.splits), dim3(64 * W),
-                       0, st, in, Wp, g.N, g.Kd, gemm_groups(g), ks, ep);
+    hipLaunchKernelGGL((gemm_kernel<NT, MT, W, EPI>), dim3(gemm_groups(g) * g.splits), dim3(64 * W), 0,
+                       st, in, Wp, g.N, g.Kd, gemm_groups(g), ks, ep);
     return hipGetLastError();
 }
 
 // Eight waves per workgroup (512 threads) leave each wave 256 registers, enough for up to four
 // 16x16 accumulator tiles without spilling; wider tiles stay at four waves.
-
-template <int NT, int MT, int EPI, bool NORM>
+template <int NT, int MT, int EPI>
 static hipError_t by_waves(const GemmShape &g, const GemmIn &in, const bf16 *Wp, const GemmEpi &ep,
                            hipStream_t st) {
     switch (g.waves) {
-        case 4: return launch<NT, MT, 4, EPI, NORM>(g, in, Wp, ep, st);
+        case 4: return launch<NT, MT, 4, EPI>(g, in, Wp, ep, st);
         case 8:
-            if constexpr (NT * MT <= 4) return launch<NT, MT, 8, EPI, NORM>(g, in, Wp, ep, st);
+            if constexpr (NT * MT <= 4) return launch<NT, MT, 8, EPI>(g, in, Wp, ep, st);
             return hipErrorInvalidValue;
         default: return hipErrorInvalidValue;
     }
 }
 
-template <int EPI, bool NORM>
+template <int EPI>
 static hipError_t by_tiles(const GemmShape &g, const GemmIn &in, const bf16 *Wp, const GemmEpi &ep,
                            hipStream_t st) {
     const int mt = mt_for(in.M);
     if (g.nt == 4) {
-        if (mt == 1) return by_waves<4, 1, EPI, NORM>(g, in, Wp, ep, st);
-        if (mt == 2) return by_waves<4, 2, EPI, NORM>(g, in, Wp, ep, st);
-        return by_waves<4, 4, EPI, NORM>(g, in, Wp, ep, st);
+        if (mt == 1) return by_waves<4, 1, EPI>(g, in, Wp, ep, st);
+        if (mt == 2) return by_waves<4, 2, EPI>(g, in, Wp, ep, st);
+        return by_waves<4, 4, EPI>(g, in, Wp, ep, st);
     }
     if (g.nt == 2) {
-        if (mt == 1) return by_waves<2, 1, EPI, NORM>(g, in, Wp, ep, st);
-        if (mt == 2) return by_waves<2, 2, EPI, NORM>(g, in, Wp, ep, st);
-        return by_waves<2, 4, EPI, NORM>(g, in, Wp, ep, st);
+        if (mt == 1) return by_waves<2, 1, EPI>(g, in, Wp, ep, st);
+        if (mt == 2) return by_waves<2, 2, EPI>(g, in, Wp, ep, st);
+        return by_waves<2, 4, EPI>(g, in, Wp, ep, st);
     }
-    if constexpr (EPI == EPI_QKV || EPI == EPI_SWIGLU) {
-        return hipErrorInvalidValue;   // paired epilogues need two tiles per group
+    if constexpr (EPI == EPI_SWIGLU) {
+        return hipErrorInvalidValue;   // paired epilogue needs two tiles per group
     } else {
-        if (mt == 1) return by_waves<1, 1, EPI, NORM>(g, in, Wp, ep, st);
-        if (mt == 2) return by_waves<1, 2, EPI, NORM>(g, in, Wp, ep, st);
-        return by_waves<1, 4, EPI, NORM>(g, in, Wp, ep, st);
+        if (mt == 1) return by_waves<1, 1, EPI>(g, in, Wp, ep, st);
+        if (mt == 2) return by_waves<1, 2, EPI>(g, in, Wp, ep, st);
+        return by_waves<1, 4, EPI>(g, in, Wp, ep, st);
     }
 }
 
@@ -371,16 +261,11 @@ hipError_t gemm(const GemmShape &g, int epi, const GemmIn &in_all, const bf16 *W
         in.M_total = g.M;
         in.m0 = m0;
         in.M = g.M - m0 < 64 ? g.M - m0 : 64;
-        const bool norm = in.ss != nullptr;
         hipError_t e;
         switch (epi) {
-            case EPI_PARTIAL: e = norm ? by_tiles<EPI_PARTIAL, true>(g, in, Wp, ep, st)
-                                       : by_tiles<EPI_PARTIAL, false>(g, in, Wp, ep, st); break;
-            case EPI_QKV: e = norm ? by_tiles<EPI_QKV, true>(g, in, Wp, ep, st)
-                                   : by_tiles<EPI_QKV, false>(g, in, Wp, ep, st); break;
-            case EPI_RESID: e = by_tiles<EPI_RESID, false>(g, in, Wp, ep, st); break;
-            case EPI_SWIGLU: e = by_tiles<EPI_SWIGLU, true>(g, in, Wp, ep, st); break;
-            case EPI_ARGMAX: e = by_tiles<EPI_ARGMAX, true>(g, in, Wp, ep, st); break;
+            case EPI_PARTIAL: e = by_tiles<EPI_PARTIAL>(g, in, Wp, ep, st); break;
+            case EPI_SWIGLU: e = by_tiles<EPI_SWIGLU>(g, in, Wp, ep, st); break;
+            case EPI_ARGMAX: e = by_tiles<EPI_ARGMAX>(g, in, Wp, ep, st); break;
             default: return hipErrorInvalidValue;
         }
         if (e != hipSuccess) return e;

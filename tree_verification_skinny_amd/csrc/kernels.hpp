@@ -17,36 +17,21 @@ struct GemmShape {
     int splits;     // K splits across workgroups (fp32 partials when > 1)
 };
 
-// What a workgroup does with its finished tiles: partial sums of its K split, or (whole K) one
-// of the fused epilogues.
-enum { EPI_PARTIAL = 0, EPI_QKV = 1, EPI_RESID = 2, EPI_SWIGLU = 3, EPI_ARGMAX = 4 };
+// What a workgroup does with its finished tiles: partial sums of its K split, or (whole K)
+// SwiGLU or the output head's per-group greedy maximum.
+enum { EPI_PARTIAL = 0, EPI_SWIGLU = 1, EPI_ARGMAX = 2 };
 
-// The B operand. When ss != nullptr it is RMSNorm(X) * gain, computed on load from the
-// per-row sums of squares ss[ss_groups][M_total] the producer of X left behind.
+// The B operand X [M][Kd] (row stride ldx).
 struct GemmIn {
     const bf16 *X;
     int ldx;
     int M, M_total, m0;          // filled per 64-row chunk by gemm()
-    const float *ss;
-    int ss_groups;
-    const bf16 *gain;
-    float eps;
-    int H;
 };
 
 struct GemmEpi {
-    int D, F;                    // head dim; ffn (SwiGLU pairing)
+    int F;                       // ffn (SwiGLU pairing)
     // PARTIAL: fp32 y [splits][M][N]
     float *y;
-    // QKV: q [M][nq][D]; K/V into cache slot ctx_len + (row % K) of request row / K
-    bf16 *q, *k_pool, *v_pool;
-    const int32_t *block_table, *ctx_len, *status;
-    const float2 *rope;          // [M][D/2] (cos, sin)
-    int max_pages, K, nq, nkv;
-    // RESID: x [M][N] += y; per-row sum of squares of the new x per tile group
-    bf16 *x;
-    float *ss_out;               // [n_groups][M]
-    bf16 *trace;                 // optional copy of the new x
     // SWIGLU: h [M][F]
     bf16 *h;
     // ARGMAX: per tile group (max, lowest index) [n_groups][M]; optional fp32 logits [M][N]
@@ -92,20 +77,18 @@ hipError_t tree_prep(const int32_t *tokens, const int32_t *parent, const int32_t
                      const int32_t *block_table, int max_pages, int n_pages, int B, int K,
                      int vocab, const NodeInfo &ni, hipStream_t st);
 hipError_t rope_table(const NodeInfo &ni, int M, int D, double theta, hipStream_t st);
-// x = embedding rows; ss [H/64][M] = per-row sums of squares over 64-column groups.
-hipError_t embed(const int32_t *tokens, const bf16 *table, int M, int H, int vocab, bf16 *x,
-                 float *ss, bf16 *trace, hipStream_t st);
-int embed_ss_groups(int H);
+// x = embedding rows, u = RMSNorm(x) * gain.
+hipError_t embed_norm(const int32_t *tokens, const bf16 *table, const bf16 *gain, int M, int H,
+                      int vocab, float eps, bf16 *x, bf16 *u, bf16 *trace, hipStream_t st);
 // Add the split-K partials of the QKV projection (split order), round to bf16, rotate q and k,
 // store q [M][nq][D] and the keys and values into the cache slots of the draft nodes.
 hipError_t reduce_qkv(const float *P, int splits, const NodeInfo &ni, const int32_t *ctx_len,
                       const int32_t *block_table, int max_pages, int B, int K, int nq, int nkv,
                       int D, bf16 *q, bf16 *k_pool, bf16 *v_pool, hipStream_t st);
-// Add the split-K partials of a projection into the residual stream: x = bf16(x + bf16(sum));
-// ss [H/256][M] = per-row sums of squares of the new x over 256-column groups.
-hipError_t reduce_resid(const float *P, int splits, int M, int H, bf16 *x, float *ss, bf16 *trace,
-                        hipStream_t st);
-int resid_ss_groups(int H);
+// Add the split-K partials of a projection into the residual stream, x = bf16(x + bf16(sum)),
+// then u = RMSNorm(x) * gain for the next projection.
+hipError_t reduce_resid_norm(const float *P, int splits, int M, int H, const bf16 *gain, float eps,
+                             bf16 *x, bf16 *u, bf16 *trace, hipStream_t st);
 hipError_t argmax_partials(const float *logits, int M, int V, float *amax_val, int *amax_idx,
                            int n_chunks, hipStream_t st);
 int argmax_chunks(int V);

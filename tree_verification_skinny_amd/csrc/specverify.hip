@@ -29,9 +29,9 @@ struct Plan {
     int L, H, nq, nkv, D, F, V;
     int qd, nqkv;
     GemmShape g_qkv, g_o, g_gu, g_down, g_lm;
-    int lm_groups, ss_groups_o, ss_groups_down, ss_groups_embed;
+    int lm_groups;
     int attn_chunks;
-    size_t o_depth, o_pos, o_status, o_anc, o_rope, o_x, o_ss, o_q, o_attn, o_h, o_part, o_po,
+    size_t o_depth, o_pos, o_status, o_anc, o_rope, o_x, o_u, o_q, o_attn, o_h, o_part, o_po,
         o_pml, o_amv, o_ami, total;
 };
 
@@ -69,28 +69,21 @@ int make_plan(const spec_model_cfg *c, int B, int K, int max_pages, Plan &p) {
     p.qd = p.nq * p.D;
     p.nqkv = (p.nq + 2 * p.nkv) * p.D;
     const int M = p.M;
-    const bool resid_split = p.H % 256 == 0;   // the residual pass works on 256-column groups
     p.g_qkv = plan_gemm(M, p.nqkv, p.H, true);
-    p.g_o = plan_gemm(M, p.H, p.qd, resid_split);
+    p.g_o = plan_gemm(M, p.H, p.qd, true);
     p.g_gu = plan_gemm(M, 2 * p.F, p.H, false);
-    p.g_down = plan_gemm(M, p.H, p.F, resid_split);
+    p.g_down = plan_gemm(M, p.H, p.F, true);
     p.g_lm = plan_gemm(M, p.V, p.H, false);
-    if (p.g_qkv.nt < 2 || p.g_gu.nt < 2) return SPEC_EUNSUPPORTED;
+    if (p.g_gu.nt < 2) return SPEC_EUNSUPPORTED;
     p.lm_groups = gemm_groups(p.g_lm);
-    p.ss_groups_o = p.g_o.splits > 1 ? resid_ss_groups(p.H) : gemm_groups(p.g_o);
-    p.ss_groups_down = p.g_down.splits > 1 ? resid_ss_groups(p.H) : gemm_groups(p.g_down);
-    p.ss_groups_embed = embed_ss_groups(p.H);
     const int64_t max_keys = (int64_t)max_pages * SPEC_PAGE_SIZE;
     p.attn_chunks = (int)((max_keys + kAttnChunk - 1) / kAttnChunk);
     const int group = p.nq / p.nkv;
     size_t part = 16;
     for (const GemmShape *g : {&p.g_qkv, &p.g_o, &p.g_down}) {
-        const size_t b = g->splits > 1 ? (size_t)g->splits * M * g->N * sizeof(float) : 0;
+        const size_t b = (size_t)g->splits * M * g->N * sizeof(float);
         if (b > part) part = b;
     }
-    int ss_groups = p.ss_groups_embed;
-    if (p.ss_groups_o > ss_groups) ss_groups = p.ss_groups_o;
-    if (p.ss_groups_down > ss_groups) ss_groups = p.ss_groups_down;
 
     const int amax_groups = p.lm_groups > argmax_chunks(p.V) ? p.lm_groups : argmax_chunks(p.V);
     Carver cv;
@@ -100,7 +93,7 @@ int make_plan(const spec_model_cfg *c, int B, int K, int max_pages, Plan &p) {
     p.o_anc = cv.take(sizeof(uint64_t) * M);
     p.o_rope = cv.take(sizeof(float2) * M * (p.D / 2));
     p.o_x = cv.take(sizeof(uint16_t) * M * p.H);
-    p.o_ss = cv.take(sizeof(float) * (size_t)ss_groups * M);
+    p.o_u = cv.take(sizeof(uint16_t) * M * p.H);
     p.o_q = cv.take(sizeof(uint16_t) * M * p.qd);
     p.o_attn = cv.take(sizeof(uint16_t) * M * p.qd);
     p.o_h = cv.take(sizeof(uint16_t) * M * p.F);
@@ -186,7 +179,7 @@ int spec_verify(const spec_weights *w, const spec_kv_cache *kv, const int32_t *d
     ni.anc = at<uint64_t>(workspace, p.o_anc);
     ni.rope = at<float2>(workspace, p.o_rope);
     bf16 *x = at<bf16>(workspace, p.o_x);
-    float *ss = at<float>(workspace, p.o_ss);
+    bf16 *u = at<bf16>(workspace, p.o_u);
     bf16 *q = at<bf16>(workspace, p.o_q);
     bf16 *attn = at<bf16>(workspace, p.o_attn);
     bf16 *h = at<bf16>(workspace, p.o_h);
@@ -200,41 +193,18 @@ int spec_verify(const spec_weights *w, const spec_kv_cache *kv, const int32_t *d
     SV_TRY(tree_prep(draft_tokens, tree_parent, ctx_len, kv->block_table, kv->max_pages_per_req,
                      kv->n_pages, p.B, p.K, p.V, ni, stream));
     SV_TRY(rope_table(ni, M, p.D, w->cfg.rope_theta, stream));
-    SV_TRY(embed(draft_tokens, static_cast<const bf16 *>(w->embed), M, p.H, p.V, x, ss, trace, stream));
+    SV_TRY(embed_norm(draft_tokens, static_cast<const bf16 *>(w->embed),
+                      static_cast<const bf16 *>(w->layers[0].attn_norm), M, p.H, p.V, eps, x, u, trace,
+                      stream));
 
     GemmEpi ep = {};
-    ep.D = p.D;
     ep.F = p.F;
-    ep.q = q;
-    ep.block_table = kv->block_table;
-    ep.ctx_len = ctx_len;
-    ep.status = ni.status;
-    ep.rope = ni.rope;
-    ep.max_pages = kv->max_pages_per_req;
-    ep.K = p.K;
-    ep.nq = p.nq;
-    ep.nkv = p.nkv;
-    ep.x = x;
-    ep.ss_out = ss;
+    ep.y = part;
     ep.h = h;
     ep.logits = logits;
     ep.amax_val = amv;
     ep.amax_idx = ami;
-    ep.y = part;
-
-    // operand that is RMSNorm(x) * gain, from the sums of squares in ss
-    auto normed = [&](const void *gain, int ss_groups) {
-        GemmIn in = {};
-        in.X = x;
-        in.ldx = p.H;
-        in.ss = ss;
-        in.ss_groups = ss_groups;
-        in.gain = static_cast<const bf16 *>(gain);
-        in.eps = eps;
-        in.H = p.H;
-        return in;
-    };
-    auto plain = [&](const bf16 *X, int ldx) {
+    auto operand = [](const bf16 *X, int ldx) {
         GemmIn in = {};
         in.X = X;
         in.ldx = ldx;
@@ -259,55 +229,36 @@ int spec_verify(const spec_weights *w, const spec_kv_cache *kv, const int32_t *d
     aa.part_ml = at<float2>(workspace, p.o_pml);
     aa.out = attn;
 
-    int ss_groups = p.ss_groups_embed;
     for (int l = 0; l < p.L; ++l) {
         const spec_layer_weights &lw = w->layers[l];
         bf16 *kl = k_pool + l * layer_stride;
         bf16 *vl = v_pool + l * layer_stride;
-        ep.k_pool = kl;
-        ep.v_pool = vl;
-        // q, k, v = RMSNorm(x) . Wqkv^T; RoPE; K/V into the cache
-        if (p.g_qkv.splits > 1) {
-            SV_TRY(gemm(p.g_qkv, EPI_PARTIAL, normed(lw.attn_norm, ss_groups),
-                        static_cast<const bf16 *>(lw.w_qkv), ep, stream));
-            SV_TRY(reduce_qkv(part, p.g_qkv.splits, ni, ctx_len, kv->block_table,
-                              kv->max_pages_per_req, p.B, p.K, p.nq, p.nkv, p.D, q, kl, vl, stream));
-        } else {
-            SV_TRY(gemm(p.g_qkv, EPI_QKV, normed(lw.attn_norm, ss_groups),
-                        static_cast<const bf16 *>(lw.w_qkv), ep, stream));
-        }
+        // q, k, v = u . Wqkv^T (u = RMSNorm(x) * attn_norm); RoPE; K/V into the cache
+        SV_TRY(gemm(p.g_qkv, EPI_PARTIAL, operand(u, p.H), static_cast<const bf16 *>(lw.w_qkv), ep,
+                    stream));
+        SV_TRY(reduce_qkv(part, p.g_qkv.splits, ni, ctx_len, kv->block_table, kv->max_pages_per_req,
+                          p.B, p.K, p.nq, p.nkv, p.D, q, kl, vl, stream));
         aa.k_pool = kl;
         aa.v_pool = vl;
         SV_TRY(attention(aa, stream));
-        // x += o . Wo^T
-        ep.trace = nullptr;
-        if (p.g_o.splits > 1) {
-            SV_TRY(gemm(p.g_o, EPI_PARTIAL, plain(attn, p.qd), static_cast<const bf16 *>(lw.w_o), ep,
-                        stream));
-            SV_TRY(reduce_resid(part, p.g_o.splits, M, p.H, x, ss, nullptr, stream));
-        } else {
-            SV_TRY(gemm(p.g_o, EPI_RESID, plain(attn, p.qd), static_cast<const bf16 *>(lw.w_o), ep,
-                        stream));
-        }
-        ss_groups = p.ss_groups_o;
-        // h = silu(gate) * up from RMSNorm(x)
-        SV_TRY(gemm(p.g_gu, EPI_SWIGLU, normed(lw.mlp_norm, ss_groups),
-                    static_cast<const bf16 *>(lw.w_gate_up), ep, stream));
-        // x += h . Wdown^T
-        bf16 *tr = trace ? trace + (int64_t)(l + 1) * M * p.H : nullptr;
-        if (p.g_down.splits > 1) {
-            SV_TRY(gemm(p.g_down, EPI_PARTIAL, plain(h, p.F), static_cast<const bf16 *>(lw.w_down), ep,
-                        stream));
-            SV_TRY(reduce_resid(part, p.g_down.splits, M, p.H, x, ss, tr, stream));
-        } else {
-            ep.trace = tr;
-            SV_TRY(gemm(p.g_down, EPI_RESID, plain(h, p.F), static_cast<const bf16 *>(lw.w_down), ep,
-                        stream));
-        }
-        ss_groups = p.ss_groups_down;
+        // x += o . Wo^T; u = RMSNorm(x) * mlp_norm
+        SV_TRY(gemm(p.g_o, EPI_PARTIAL, operand(attn, p.qd), static_cast<const bf16 *>(lw.w_o), ep,
+                    stream));
+        SV_TRY(reduce_resid_norm(part, p.g_o.splits, M, p.H, static_cast<const bf16 *>(lw.mlp_norm),
+                                 eps, x, u, nullptr, stream));
+        // h = silu(u . Wgate^T) * (u . Wup^T)
+        SV_TRY(gemm(p.g_gu, EPI_SWIGLU, operand(u, p.H), static_cast<const bf16 *>(lw.w_gate_up), ep,
+                    stream));
+        // x += h . Wdown^T; u = RMSNorm(x) * (next layer's attn_norm, or the final norm)
+        const bf16 *next_gain = l + 1 < p.L ? static_cast<const bf16 *>(w->layers[l + 1].attn_norm)
+                                            : static_cast<const bf16 *>(w->final_norm);
+        SV_TRY(gemm(p.g_down, EPI_PARTIAL, operand(h, p.F), static_cast<const bf16 *>(lw.w_down), ep,
+                    stream));
+        SV_TRY(reduce_resid_norm(part, p.g_down.splits, M, p.H, next_gain, eps, x, u,
+                                 trace ? trace + (int64_t)(l + 1) * M * p.H : nullptr, stream));
     }
-    SV_TRY(gemm(p.g_lm, EPI_ARGMAX, normed(w->final_norm, ss_groups),
-                static_cast<const bf16 *>(w->lm_head), ep, stream));
+    SV_TRY(gemm(p.g_lm, EPI_ARGMAX, operand(u, p.H), static_cast<const bf16 *>(w->lm_head), ep,
+                stream));
     SV_TRY(argmax_accept(amv, ami, p.lm_groups, draft_tokens, tree_parent, ni, p.B, p.K, greedy,
                          accepted_len, bonus_token, accepted_path, stream));
     return SPEC_OK;
