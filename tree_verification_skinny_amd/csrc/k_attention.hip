@@ -36,8 +36,17 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
     __shared__ __attribute__((aligned(16))) bf16 Vt[D * VP];
 
     const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-    if (status[b] != 0) return;
+    constexpr int NP = CH / 16;
+    // Page ids of this chunk and the request's status and context are read together: the index
+    // is clamped to the request's table row (max_pages entries), so these reads are in bounds
+    // whatever the context turns out to be; entries past the context are masked below.
+    const int32_t *bt = block_table + (int64_t)b * max_pages;
+    int pages[NP];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) pages[p] = bt[min((c * CH >> 4) + p, max_pages - 1)];
+    const int st_b = status[b];
     const int ctx = ctx_len[b];
+    if (st_b != 0) return;
     const int T = ctx + K;
     const int kb = c * CH;
     if (kb >= T) return;
@@ -70,16 +79,8 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
     // Every thread issues all of its page loads before the first LDS store, so the chunk's
     // 2 x 8 x 16 B per thread are in flight together.
     {
-        constexpr int NP = CH / 16;
         const int e = threadIdx.x * 8;           // element offset inside a 16 x D page
         const bool has = e < 16 * D;
-        // page ids: read unconditionally (index clamped to the request's last page, always in
-        // bounds) so all reads issue together, then masked
-        const int32_t *bt = block_table + (int64_t)b * max_pages;
-        const int last = (T - 1) >> 4;
-        int pages[NP];
-#pragma unroll
-        for (int p = 0; p < NP; ++p) pages[p] = bt[min((kb >> 4) + p, last)];
 #pragma unroll
         for (int p = 0; p < NP; ++p)
             if (!(has && p < npages)) pages[p] = -1;
@@ -145,27 +146,37 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
             }
             float sv[8];
             float mloc = -INFINITY;
+            // a 32-key step wholly inside the committed context needs no mask
+            const bool plain = col_ok && st * 32 + 32 <= nvalid && kb + st * 32 + 32 <= ctx;
+            if (plain) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float raw = e < 4 ? s0[e] : s1[e - 4];
-                const int kl = st * 32 + 8 * grp + e;
-                const int ka = kb + kl;
-                const bool vis = col_ok && kl < nvalid && (ka < ctx || ((am >> (ka - ctx)) & 1ull));
-                sv[e] = vis ? raw * scale_log2 : -INFINITY;
-                mloc = fmaxf(mloc, sv[e]);
+                for (int e = 0; e < 8; ++e) {
+                    sv[e] = (e < 4 ? s0[e] : s1[e - 4]) * scale_log2;
+                    mloc = fmaxf(mloc, sv[e]);
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float raw = e < 4 ? s0[e] : s1[e - 4];
+                    const int kl = st * 32 + 8 * grp + e;
+                    const int ka = kb + kl;
+                    const bool vis = col_ok && kl < nvalid && (ka < ctx || ((am >> (ka - ctx)) & 1ull));
+                    sv[e] = vis ? raw * scale_log2 : -INFINITY;
+                    mloc = fmaxf(mloc, sv[e]);
+                }
             }
             mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
             mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
             const float m_new = fmaxf(m_run, mloc);
             const bool none = (m_new == -INFINITY);
-            const float alpha = none ? 1.f : exp2f(m_run - m_new);
+            const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
             // p = p_hi + p_lo, both bf16: the two products carry ~16 bits of p, so the weighted
             // sum of values is as precise as the fp32 probabilities it stands for.
             bf16x8 ph, pl;
             float psum = 0.f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float pv = none ? 0.f : exp2f(sv[e] - m_new);
+                const float pv = none ? 0.f : __builtin_amdgcn_exp2f(sv[e] - m_new);
                 const bf16 hi = to_bf(pv);
                 ph[e] = hi;
                 pl[e] = to_bf(pv - to_f(hi));
@@ -173,11 +184,15 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
             }
             l_run = l_run * alpha + psum;
             m_run = m_new;
+            // the accumulators need rescaling only when some column's running maximum moved
+            if (__any(alpha != 1.f)) {
+#pragma unroll
+                for (int dt = 0; dt < D / 16; ++dt) o[dt] *= alpha;
+            }
             const bf16 *vrow = &Vt[r16 * VP + st * 32 + grp * 8];
 #pragma unroll
             for (int dt = 0; dt < D / 16; ++dt) {
                 const bf16x8 vf = *(const bf16x8 *)(vrow + dt * 16 * VP);
-                o[dt] *= alpha;
                 o[dt] = mfma16x16x32(vf, ph, o[dt]);
                 o[dt] = mfma16x16x32(vf, pl, o[dt]);
             }

@@ -230,13 +230,23 @@ __global__ __launch_bounds__(kRowThreads) void reduce_resid_norm_kernel(
     bf16 *xr = x + (int64_t)row * H;
     float xv[kRowQuads][4];
     floatx4 y[kRowQuads];
+    uint2 xo[kRowQuads];           // the four bf16 residual values of each quad
+    // every load of the row (all splits, the residual) is issued before any is used
 #pragma unroll
     for (int i = 0; i < kRowQuads; ++i) {
         const int q = threadIdx.x + i * kRowThreads;
         y[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+        xo[i] = make_uint2(0u, 0u);
         if (q * 4 >= H) continue;
+        xo[i] = *(const uint2 *)(xr + q * 4);
         y[i] = *(const floatx4 *)(pr + q * 4);
-        for (int s = 1; s < splits; ++s) y[i] += *(const floatx4 *)(pr + s * pstride + q * 4);
+    }
+    for (int s = 1; s < splits; ++s) {
+#pragma unroll
+        for (int i = 0; i < kRowQuads; ++i) {
+            const int q = threadIdx.x + i * kRowThreads;
+            if (q * 4 < H) y[i] += *(const floatx4 *)(pr + s * pstride + q * 4);
+        }
     }
     float ss = 0.f;
 #pragma unroll
@@ -245,14 +255,17 @@ __global__ __launch_bounds__(kRowThreads) void reduce_resid_norm_kernel(
 #pragma unroll
         for (int j = 0; j < 4; ++j) xv[i][j] = 0.f;
         if (q * 4 >= H) continue;
+        const bf16 *xb = reinterpret_cast<const bf16 *>(&xo[i]);
+        bf16 out[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const float xn = round_bf(to_f(xr[q * 4 + j]) + round_bf(y[i][j]));
+            const float xn = round_bf(to_f(xb[j]) + round_bf(y[i][j]));
             xv[i][j] = xn;
             ss += xn * xn;
-            xr[q * 4 + j] = to_bf(xn);
-            if (trace) trace[(int64_t)row * H + q * 4 + j] = to_bf(xn);
+            out[j] = to_bf(xn);
         }
+        *(uint2 *)(xr + q * 4) = *reinterpret_cast<const uint2 *>(out);
+        if (trace) *(uint2 *)(trace + (int64_t)row * H + q * 4) = *reinterpret_cast<const uint2 *>(out);
     }
     ss = block_sum_1024(ss, red);
     norm_store(xv, ss, H, eps, gain, u + (int64_t)row * H);
