@@ -100,6 +100,11 @@ typedef struct {
     int32_t *greedy;        /* int32 [batch*k]: argmax of each node's logits (lowest index) */
     void *hidden;           /* bf16 [n_layers + 1][batch*k][hidden]: residual stream entering
                                each layer, then after the last layer (before the final norm) */
+    hipEvent_t *gate_up_events;  /* HOST array of 2 * n_layers events or NULL: events[2l] is
+                               recorded on `stream` right before layer l's gate/up projection
+                               kernel and events[2l+1] right after it, for per-launch timing
+                               of the pass's largest kernel. Time eager calls: events captured
+                               into a HIP graph are not ordered against its kernels. */
 } spec_verify_extras;
 
 /* Workspace bytes spec_verify needs for this shape, batch, k and cache page budget per request
@@ -166,9 +171,10 @@ int spec_pack_weight(const void *w, int n, int kd, void *packed, hipStream_t str
  * weight once for a few rows [SpecPilot digest, airadar.tv — summary paragraph], so this is the
  * kernel whose HBM bandwidth the pass lives on. For kernel-level tests and bandwidth
  * measurement.
- *   x: bf16 [m][kd] row-major; w: bf16 [n][kd] packed (spec_pack_weight); partials: fp32,
- *   spec_skinny_gemm_bytes() bytes; *splits (HOST) receives the split count. Needs
- *   kd % 32 == 0, n % 16 == 0, m >= 1. */
+ *   x: bf16 [m][kd] row-major; w: bf16 [n][kd] packed (spec_pack_weight); partials: a
+ *   256-byte aligned buffer of spec_skinny_gemm_bytes() bytes, whose first splits*m*n floats
+ *   receive the partial sums (the rest holds a fragment-order copy of x); *splits (HOST)
+ *   receives the split count. Needs kd % 32 == 0, n % 16 == 0, m >= 1. */
 int spec_skinny_gemm_bytes(int m, int n, int kd, size_t *bytes);
 int spec_skinny_gemm(const void *x, int m, int kd, const void *w, int n, float *partials,
                      size_t partial_bytes, int *splits, hipStream_t stream);

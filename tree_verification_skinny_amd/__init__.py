@@ -65,7 +65,8 @@ class KVCacheC(ctypes.Structure):
 
 
 class ExtrasC(ctypes.Structure):
-    _fields_ = [("logits", ctypes.c_void_p), ("greedy", ctypes.c_void_p), ("hidden", ctypes.c_void_p)]
+    _fields_ = [("logits", ctypes.c_void_p), ("greedy", ctypes.c_void_p), ("hidden", ctypes.c_void_p),
+                ("gate_up_events", ctypes.c_void_p)]
 
 
 _lib = None
@@ -232,8 +233,11 @@ def spec_verify(weights: Weights, kv: PagedKV, draft_tokens: torch.Tensor,
                 accepted_len: torch.Tensor, bonus_token: torch.Tensor, accepted_path: torch.Tensor,
                 ws: torch.Tensor, logits: Optional[torch.Tensor] = None,
                 greedy: Optional[torch.Tensor] = None, hidden: Optional[torch.Tensor] = None,
-                stream=None) -> None:
-    extras = ExtrasC(_ptr(logits), _ptr(greedy), _ptr(hidden))
+                gate_up_events=None, stream=None) -> None:
+    """gate_up_events: optional ctypes array of 2 * n_layers hipEvent_t handles (e.g. the
+    cuda_event handles of torch timing events that have been recorded once)."""
+    ev = None if gate_up_events is None else ctypes.cast(gate_up_events, ctypes.c_void_p)
+    extras = ExtrasC(_ptr(logits), _ptr(greedy), _ptr(hidden), ev)
     rc = lib().spec_verify(ctypes.byref(weights.c), ctypes.byref(kv.c), _ptr(draft_tokens),
                            _ptr(tree_parent), _ptr(ctx_len), batch, k, _ptr(accepted_len),
                            _ptr(bonus_token), _ptr(accepted_path), ctypes.byref(extras), _ptr(ws),
@@ -285,3 +289,4 @@ def spec_skinny_gemm(x: torch.Tensor, w: torch.Tensor, partials: torch.Tensor, s
                                 _stream(stream))
     _check(rc, "spec_skinny_gemm")
     return splits.value
+

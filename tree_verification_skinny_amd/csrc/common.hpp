@@ -50,6 +50,20 @@ __device__ __forceinline__ floatx4 mfma16x16x32(bf16x8 a, bf16x8 b, floatx4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// Fragment order of a bf16 matrix A [rows][cols] (cols % 32 == 0), the order the projection
+// kernels stream both operands in: blocks of 16 rows; in each block, steps of 32 columns; in each
+// step, 64 slots of 8 consecutive elements, slot l = A[16 block + l % 16][32 step + 8 (l / 16) ..].
+// Element offset of A[r][c]; the 4-aligned groups c..c+3 stay contiguous.
+__device__ __forceinline__ int64_t frag_off(int64_t r, int c, int cols) {
+    return (((r >> 4) * (cols >> 5) + (c >> 5)) * 64 + (r & 15) + 16 * ((c >> 3) & 3)) * 8 + (c & 7);
+}
+
+// Four bf16 values to one 8-byte store.
+__device__ __forceinline__ void store4(bf16 *dst, float a, float b, float c, float d) {
+    bf16 v[4] = {to_bf(a), to_bf(b), to_bf(c), to_bf(d)};
+    *reinterpret_cast<uint2 *>(dst) = *reinterpret_cast<const uint2 *>(v);
+}
+
 // Position p of request b -> (page id, slot). Caller guarantees p is inside the request's pages.
 __device__ __forceinline__ int page_of(const int32_t *block_table, int max_pages, int b, int p) {
     return block_table[(int64_t)b * max_pages + (p >> 4)];

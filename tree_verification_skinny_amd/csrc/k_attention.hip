@@ -226,7 +226,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(
     const int row = blockIdx.x, h = blockIdx.y;
     const int d4 = (threadIdx.x % TQ) * 4, cg = threadIdx.x / TQ;
     const int b = row / K, tok = row % K;
-    bf16 *dst = out + ((int64_t)row * nq + h) * D + d4;
+    bf16 *dst = out + frag_off(row, h * D + d4, nq * D);   // fragment order: the O operand
     if (status[b] != 0) {
         if (cg == 0) {
 #pragma unroll
@@ -279,8 +279,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(
         o = o * a + ok * w;
         m = mn;
     }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) dst[j] = to_bf(o[j] / l);
+    store4(dst, o[0] / l, o[1] / l, o[2] / l, o[3] / l);
 }
 
 hipError_t attention(const AttnArgs &a, hipStream_t st) {

@@ -112,15 +112,19 @@ __device__ __forceinline__ float block_sum_1024(float v, float *red) {
     return t;
 }
 
-__device__ __forceinline__ void norm_store(const float (&xv)[kRowQuads][4], float ss, int H, float eps,
-                                           const bf16 *__restrict__ gain, bf16 *__restrict__ u) {
+// u is stored in fragment order (frag_off), the operand order of the next projection.
+__device__ __forceinline__ void norm_store(const float (&xv)[kRowQuads][4], float ss, int row, int H,
+                                           float eps, const bf16 *__restrict__ gain,
+                                           bf16 *__restrict__ u) {
     const float inv = 1.0f / sqrtf(ss / (float)H + eps);
 #pragma unroll
     for (int i = 0; i < kRowQuads; ++i) {
         const int q = threadIdx.x + i * kRowThreads;
         if (q * 4 >= H) break;
+        float o[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) u[q * 4 + j] = to_bf((xv[i][j] * inv) * to_f(gain[q * 4 + j]));
+        for (int j = 0; j < 4; ++j) o[j] = (xv[i][j] * inv) * to_f(gain[q * 4 + j]);
+        store4(u + frag_off(row, q * 4, H), o[0], o[1], o[2], o[3]);
     }
 }
 
@@ -152,7 +156,7 @@ __global__ __launch_bounds__(kRowThreads) void embed_norm_kernel(
         }
     }
     ss = block_sum_1024(ss, red);
-    norm_store(xv, ss, H, eps, gain, u + (int64_t)row * H);
+    norm_store(xv, ss, row, H, eps, gain, u);
 }
 
 hipError_t embed_norm(const int32_t *tokens, const bf16 *table, const bf16 *gain, int M, int H,
@@ -268,7 +272,7 @@ __global__ __launch_bounds__(kRowThreads) void reduce_resid_norm_kernel(
         if (trace) *(uint2 *)(trace + (int64_t)row * H + q * 4) = *reinterpret_cast<const uint2 *>(out);
     }
     ss = block_sum_1024(ss, red);
-    norm_store(xv, ss, H, eps, gain, u + (int64_t)row * H);
+    norm_store(xv, ss, row, H, eps, gain, u);
 }
 
 hipError_t reduce_resid_norm(const float *P, int splits, int M, int H, const bf16 *gain, float eps,
@@ -328,49 +332,84 @@ hipError_t argmax_partials(const float *logits, int M, int V, float *amax_val, i
 int argmax_chunks(int V) { return (V + kArgChunk - 1) / kArgChunk; }
 
 // ---- greedy choice per node + longest accepted root path, one workgroup per request ----------
-__global__ __launch_bounds__(256) void argmax_accept_kernel(
+// One workgroup per request. The per-group maxima are laid out [group][row], so thread t reads
+// node i = t % K of groups t / K, t / K + G, ... (G = 1024 / K threads per node): the K rows of a
+// request are adjacent, so each pass reads K contiguous floats per group. The per-thread bests are
+// then merged in LDS over the G threads of each node (the order is total: larger value, then lower
+// index), and thread 0 walks the tree.
+__global__ __launch_bounds__(1024) void argmax_accept_kernel(
     const float *__restrict__ amax_val, const int *__restrict__ amax_idx, int n_groups,
     const int32_t *__restrict__ tokens, const int32_t *__restrict__ parent,
     const int32_t *__restrict__ depth, const int32_t *__restrict__ status, int M, int K,
     int32_t *__restrict__ greedy, int32_t *__restrict__ accepted_len, int32_t *__restrict__ bonus,
     int32_t *__restrict__ path) {
-    __shared__ float rv[4];
-    __shared__ int ri[4];
+    __shared__ float rv[1024];
+    __shared__ int ri[1024];
     __shared__ int s_arg[64];
     const int b = blockIdx.x;
-    for (int i = 0; i < K; ++i) {
-        const int row = b * K + i;
-        float bv = -INFINITY;
-        int bi = 0x7fffffff;
-        for (int g = threadIdx.x; g < n_groups; g += 256) {
+    const int t = threadIdx.x;
+    const int G = 1024 / K;
+    const int i = t % K, sub = t / K;
+    const bool active = sub < G;
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+    if (active) {
+        const int64_t row = (int64_t)b * K + i;
+        constexpr int UN = 8;    // loads in flight per thread
+        int g = sub;
+        for (; g + (UN - 1) * G < n_groups; g += UN * G) {
+            float v[UN];
+            int ix[UN];
+#pragma unroll
+            for (int u = 0; u < UN; ++u) {
+                v[u] = amax_val[(int64_t)(g + u * G) * M + row];
+                ix[u] = amax_idx[(int64_t)(g + u * G) * M + row];
+            }
+#pragma unroll
+            for (int u = 0; u < UN; ++u)
+                if (better(v[u], ix[u], bv, bi)) { bv = v[u]; bi = ix[u]; }
+        }
+        for (; g < n_groups; g += G) {
             const float v = amax_val[(int64_t)g * M + row];
             const int ix = amax_idx[(int64_t)g * M + row];
             if (better(v, ix, bv, bi)) { bv = v; bi = ix; }
         }
-        block_best_256(bv, bi, rv, ri);
-        if (threadIdx.x == 0) {
-            s_arg[i] = bi;
-            if (greedy) greedy[row] = bi;
+    }
+    rv[t] = bv;
+    ri[t] = bi;
+    __syncthreads();
+    for (int s = 1; s < G; s <<= 1) {
+        if (active && (sub & (2 * s - 1)) == 0 && sub + s < G) {
+            const float ov = rv[t + s * K];
+            const int oi = ri[t + s * K];
+            if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+            rv[t] = bv;
+            ri[t] = bi;
         }
+        __syncthreads();
+    }
+    if (t < K) {
+        s_arg[t] = ri[t];
+        if (greedy) greedy[(int64_t)b * K + t] = ri[t];
     }
     __syncthreads();
-    if (threadIdx.x != 0) return;
+    if (t != 0) return;
     int32_t *pr = path + (int64_t)b * K;
-    for (int i = 0; i < K; ++i) pr[i] = -1;
+    for (int j = 0; j < K; ++j) pr[j] = -1;
     if (status[b] != 0) {
         accepted_len[b] = -1;
         bonus[b] = -1;
         return;
     }
-    uint64_t ok = 1ull;          // bit i: node i accepted
+    uint64_t ok = 1ull;          // bit j: node j accepted
     int best = 0;
     const int32_t *tk = tokens + (int64_t)b * K;
     const int32_t *dp = depth + (int64_t)b * K;
-    for (int i = 1; i < K; ++i) {
-        const int p = parent != nullptr ? parent[(int64_t)b * K + i] : i - 1;
-        if (((ok >> p) & 1ull) && tk[i] == s_arg[p]) {
-            ok |= 1ull << i;
-            if (dp[i] > dp[best]) best = i;
+    for (int j = 1; j < K; ++j) {
+        const int p = parent != nullptr ? parent[(int64_t)b * K + j] : j - 1;
+        if (((ok >> p) & 1ull) && tk[j] == s_arg[p]) {
+            ok |= 1ull << j;
+            if (dp[j] > dp[best]) best = j;
         }
     }
     accepted_len[b] = dp[best];
@@ -383,7 +422,7 @@ hipError_t argmax_accept(const float *amax_val, const int *amax_idx, int n_group
                          const int32_t *tokens, const int32_t *parent, const NodeInfo &ni, int B,
                          int K, int32_t *greedy, int32_t *accepted_len, int32_t *bonus,
                          int32_t *path, hipStream_t st) {
-    hipLaunchKernelGGL(argmax_accept_kernel, dim3(B), dim3(256), 0, st, amax_val, amax_idx, n_groups,
+    hipLaunchKernelGGL(argmax_accept_kernel, dim3(B), dim3(1024), 0, st, amax_val, amax_idx, n_groups,
                        tokens, parent, ni.depth, ni.status, B * K, K, greedy, accepted_len, bonus,
                        path);
     return hipGetLastError();

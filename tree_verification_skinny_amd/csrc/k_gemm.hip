@@ -11,7 +11,9 @@
 //     and a tile's K steps follow each other. One 128-bit load per lane reads a whole fragment
 //     as 1 KB of contiguous HBM, straight into the registers the MFMA consumes.
 //   * The activations X [M][Kd] (cache resident, already normalised where an RMSNorm precedes
-//     the projection) are the B operand, loaded with the same K order.
+//     the projection) are the B operand, in the same fragment order (16-row blocks instead of
+//     16-row tiles): the kernels that produce them write them that way, so an activation load
+//     is one contiguous 1 KB read as well.
 //   * A workgroup of W waves (4 or 8) owns NT weight tiles over a K range; its waves interleave
 //     over the 32-wide K steps (so together they read each tile front to back) and add their
 //     sums in LDS in wave order. Projections with few output columns split K over workgroups
@@ -29,23 +31,26 @@
 namespace sv {
 
 // ---- packing ------------------------------------------------------------------------------------
+// Row-major [n][kd] -> fragment order (frag_off), rows past n (up to the next multiple of 16)
+// zero. One thread per 16-byte slot (block, step, lane).
 __global__ __launch_bounds__(256) void pack_kernel(const bf16 *__restrict__ w, int n, int kd,
                                                    bf16 *__restrict__ out) {
-    // one thread per 16-byte lane slot: (tile, step, lane)
     const int64_t steps = kd / 32;
-    const int64_t total = (int64_t)(n / 16) * steps * 64;
+    const int64_t total = (int64_t)((n + 15) / 16) * steps * 64;
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
         const int lane = (int)(i & 63);
         const int64_t frag = i >> 6;
         const int64_t tile = frag / steps, step = frag % steps;
         const int64_t row = tile * 16 + (lane & 15);
         const int64_t col = step * 32 + 8 * (lane >> 4);
-        *(bf16x8 *)(out + i * 8) = *(const bf16x8 *)(w + row * kd + col);
+        bf16x8 v = {};
+        if (row < n) v = *(const bf16x8 *)(w + row * kd + col);
+        *(bf16x8 *)(out + i * 8) = v;
     }
 }
 
 hipError_t pack_weight(const bf16 *w, int n, int kd, bf16 *out, hipStream_t st) {
-    const int64_t total = (int64_t)(n / 16) * (kd / 32) * 64;
+    const int64_t total = (int64_t)((n + 15) / 16) * (kd / 32) * 64;
     int64_t blocks = (total + 255) / 256;
     if (blocks > 65536) blocks = 65536;
     hipLaunchKernelGGL(pack_kernel, dim3((unsigned)blocks), dim3(256), 0, st, w, n, kd, out);
@@ -91,11 +96,14 @@ __global__ __launch_bounds__(64 * W) void gemm_kernel(GemmIn in, const bf16 *__r
         const int tile = tile_col<NT, EPI>(ng, t, ep.F) >> 4;
         wp[t] = Wp + (((int64_t)tile * S) * 64 + lane) * 8;
     }
+    // activation blocks of this chunk; blocks past the last one (MT rounds the chunk up) re-read
+    // it, and their columns are never stored
+    const int nblk = (in.M_total + 15) >> 4;
     const bf16 *xp[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-        const int m = min(16 * mt + r16, M - 1);
-        xp[mt] = in.X + (int64_t)(m0 + m) * in.ldx + grp * 8;
+        const int blk = min((m0 >> 4) + mt, nblk - 1);
+        xp[mt] = in.Xp + (((int64_t)blk * S) * 64 + lane) * 8;
     }
 
     Acc<NT, MT> acc;
@@ -116,7 +124,7 @@ __global__ __launch_bounds__(64 * W) void gemm_kernel(GemmIn in, const bf16 *__r
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) b[u][mt] = *(const bf16x8 *)(xp[mt] + (s + W * u) * 32);
+            for (int mt = 0; mt < MT; ++mt) b[u][mt] = *(const bf16x8 *)(xp[mt] + (int64_t)(s + W * u) * 512);
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
@@ -129,7 +137,7 @@ __global__ __launch_bounds__(64 * W) void gemm_kernel(GemmIn in, const bf16 *__r
 #pragma unroll
         for (int t = 0; t < NT; ++t) a[t] = *(const bf16x8 *)(wp[t] + (int64_t)s * 512);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) b[mt] = *(const bf16x8 *)(xp[mt] + s * 32);
+        for (int mt = 0; mt < MT; ++mt) b[mt] = *(const bf16x8 *)(xp[mt] + (int64_t)s * 512);
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -171,13 +179,15 @@ __global__ __launch_bounds__(64 * W) void gemm_kernel(GemmIn in, const bf16 *__r
             if (!live) continue;
 #pragma unroll
             for (int t = 0; t < NT / 2; ++t) {
-                bf16 *hr = ep.h + (int64_t)row * ep.F + col[t];
+                // h in fragment order: the down projection's activation operand
+                float hv[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const float g = round_bf(acc.v[t][mt][j]);
                     const float u = round_bf(acc.v[t + NT / 2][mt][j]);
-                    hr[j] = to_bf((g / (1.0f + expf(-g))) * u);
+                    hv[j] = (g / (1.0f + expf(-g))) * u;
                 }
+                store4(ep.h + frag_off(row, col[t], ep.F), hv[0], hv[1], hv[2], hv[3]);
             }
         } else if constexpr (EPI == EPI_ARGMAX) {
             float bv = -INFINITY;

@@ -21,10 +21,10 @@ struct GemmShape {
 // SwiGLU or the output head's per-group greedy maximum.
 enum { EPI_PARTIAL = 0, EPI_SWIGLU = 1, EPI_ARGMAX = 2 };
 
-// The B operand X [M][Kd] (row stride ldx).
+// The B operand: activations X [M_total][Kd] in fragment order (frag_off), rows padded to a
+// multiple of 16.
 struct GemmIn {
-    const bf16 *X;
-    int ldx;
+    const bf16 *Xp;
     int M, M_total, m0;          // filled per 64-row chunk by gemm()
 };
 
@@ -32,7 +32,7 @@ struct GemmEpi {
     int F;                       // ffn (SwiGLU pairing)
     // PARTIAL: fp32 y [splits][M][N]
     float *y;
-    // SWIGLU: h [M][F]
+    // SWIGLU: h [M][F] in fragment order
     bf16 *h;
     // ARGMAX: per tile group (max, lowest index) [n_groups][M]; optional fp32 logits [M][N]
     float *logits, *amax_val;
@@ -43,6 +43,7 @@ int gemm_groups(const GemmShape &g);
 GemmShape plan_gemm(int M, int N, int Kd, bool allow_split);
 hipError_t gemm(const GemmShape &g, int epi, const GemmIn &in, const bf16 *Wp, const GemmEpi &ep,
                 hipStream_t st);
+// Row-major [n][kd] -> fragment order; rows up to the next multiple of 16 are zero.
 hipError_t pack_weight(const bf16 *w, int n, int kd, bf16 *out, hipStream_t st);
 
 // ---- attention ------------------------------------------------------------------------------
@@ -61,7 +62,7 @@ struct AttnArgs {
     int n_chunks;                // per request (grid), >= ceil((ctx + K) / kAttnChunk)
     float *part_o;               // [B][nkv][n_chunks][group*K][D]
     float2 *part_ml;             // [B][nkv][n_chunks][group*K]
-    bf16 *out;                   // [B*K][nq*D]
+    bf16 *out;                   // [B*K][nq*D] in fragment order (the O projection's operand)
 };
 hipError_t attention(const AttnArgs &a, hipStream_t st);
 
@@ -77,7 +78,7 @@ hipError_t tree_prep(const int32_t *tokens, const int32_t *parent, const int32_t
                      const int32_t *block_table, int max_pages, int n_pages, int B, int K,
                      int vocab, const NodeInfo &ni, hipStream_t st);
 hipError_t rope_table(const NodeInfo &ni, int M, int D, double theta, hipStream_t st);
-// x = embedding rows, u = RMSNorm(x) * gain.
+// x = embedding rows, u = RMSNorm(x) * gain (u in fragment order).
 hipError_t embed_norm(const int32_t *tokens, const bf16 *table, const bf16 *gain, int M, int H,
                       int vocab, float eps, bf16 *x, bf16 *u, bf16 *trace, hipStream_t st);
 // Add the split-K partials of the QKV projection (split order), round to bf16, rotate q and k,
@@ -86,7 +87,7 @@ hipError_t reduce_qkv(const float *P, int splits, const NodeInfo &ni, const int3
                       const int32_t *block_table, int max_pages, int B, int K, int nq, int nkv,
                       int D, bf16 *q, bf16 *k_pool, bf16 *v_pool, hipStream_t st);
 // Add the split-K partials of a projection into the residual stream, x = bf16(x + bf16(sum)),
-// then u = RMSNorm(x) * gain for the next projection.
+// then u = RMSNorm(x) * gain for the next projection (u in fragment order).
 hipError_t reduce_resid_norm(const float *P, int splits, int M, int H, const bf16 *gain, float eps,
                              bf16 *x, bf16 *u, bf16 *trace, hipStream_t st);
 hipError_t argmax_partials(const float *logits, int M, int V, float *amax_val, int *amax_idx,

@@ -92,11 +92,12 @@ int make_plan(const spec_model_cfg *c, int B, int K, int max_pages, Plan &p) {
     p.o_status = cv.take(sizeof(int32_t) * B);
     p.o_anc = cv.take(sizeof(uint64_t) * M);
     p.o_rope = cv.take(sizeof(float2) * M * (p.D / 2));
+    const size_t Mp = (size_t)(M + 15) / 16 * 16;   // projection operands: whole 16-row blocks
     p.o_x = cv.take(sizeof(uint16_t) * M * p.H);
-    p.o_u = cv.take(sizeof(uint16_t) * M * p.H);
+    p.o_u = cv.take(sizeof(uint16_t) * Mp * p.H);
     p.o_q = cv.take(sizeof(uint16_t) * M * p.qd);
-    p.o_attn = cv.take(sizeof(uint16_t) * M * p.qd);
-    p.o_h = cv.take(sizeof(uint16_t) * M * p.F);
+    p.o_attn = cv.take(sizeof(uint16_t) * Mp * p.qd);
+    p.o_h = cv.take(sizeof(uint16_t) * Mp * p.F);
     p.o_part = cv.take(part);
     p.o_po = cv.take(sizeof(float) * (size_t)B * p.nkv * p.attn_chunks * group * K * p.D);
     p.o_pml = cv.take(sizeof(float2) * (size_t)B * p.nkv * p.attn_chunks * group * K);
@@ -169,6 +170,7 @@ int spec_verify(const spec_weights *w, const spec_kv_cache *kv, const int32_t *d
     float *logits = extras ? extras->logits : nullptr;
     int32_t *greedy = extras ? extras->greedy : nullptr;
     bf16 *trace = extras ? static_cast<bf16 *>(extras->hidden) : nullptr;
+    hipEvent_t *gu_events = extras ? extras->gate_up_events : nullptr;
     const float eps = w->cfg.rms_eps;
     const int M = p.M;
 
@@ -204,10 +206,9 @@ int spec_verify(const spec_weights *w, const spec_kv_cache *kv, const int32_t *d
     ep.logits = logits;
     ep.amax_val = amv;
     ep.amax_idx = ami;
-    auto operand = [](const bf16 *X, int ldx) {
+    auto operand = [](const bf16 *Xp) {
         GemmIn in = {};
-        in.X = X;
-        in.ldx = ldx;
+        in.Xp = Xp;
         return in;
     };
 
@@ -234,7 +235,7 @@ int spec_verify(const spec_weights *w, const spec_kv_cache *kv, const int32_t *d
         bf16 *kl = k_pool + l * layer_stride;
         bf16 *vl = v_pool + l * layer_stride;
         // q, k, v = u . Wqkv^T (u = RMSNorm(x) * attn_norm); RoPE; K/V into the cache
-        SV_TRY(gemm(p.g_qkv, EPI_PARTIAL, operand(u, p.H), static_cast<const bf16 *>(lw.w_qkv), ep,
+        SV_TRY(gemm(p.g_qkv, EPI_PARTIAL, operand(u), static_cast<const bf16 *>(lw.w_qkv), ep,
                     stream));
         SV_TRY(reduce_qkv(part, p.g_qkv.splits, ni, ctx_len, kv->block_table, kv->max_pages_per_req,
                           p.B, p.K, p.nq, p.nkv, p.D, q, kl, vl, stream));
@@ -242,22 +243,24 @@ int spec_verify(const spec_weights *w, const spec_kv_cache *kv, const int32_t *d
         aa.v_pool = vl;
         SV_TRY(attention(aa, stream));
         // x += o . Wo^T; u = RMSNorm(x) * mlp_norm
-        SV_TRY(gemm(p.g_o, EPI_PARTIAL, operand(attn, p.qd), static_cast<const bf16 *>(lw.w_o), ep,
+        SV_TRY(gemm(p.g_o, EPI_PARTIAL, operand(attn), static_cast<const bf16 *>(lw.w_o), ep,
                     stream));
         SV_TRY(reduce_resid_norm(part, p.g_o.splits, M, p.H, static_cast<const bf16 *>(lw.mlp_norm),
                                  eps, x, u, nullptr, stream));
         // h = silu(u . Wgate^T) * (u . Wup^T)
-        SV_TRY(gemm(p.g_gu, EPI_SWIGLU, operand(u, p.H), static_cast<const bf16 *>(lw.w_gate_up), ep,
+        if (gu_events) SV_TRY(hipEventRecord(gu_events[2 * l], stream));
+        SV_TRY(gemm(p.g_gu, EPI_SWIGLU, operand(u), static_cast<const bf16 *>(lw.w_gate_up), ep,
                     stream));
+        if (gu_events) SV_TRY(hipEventRecord(gu_events[2 * l + 1], stream));
         // x += h . Wdown^T; u = RMSNorm(x) * (next layer's attn_norm, or the final norm)
         const bf16 *next_gain = l + 1 < p.L ? static_cast<const bf16 *>(w->layers[l + 1].attn_norm)
                                             : static_cast<const bf16 *>(w->final_norm);
-        SV_TRY(gemm(p.g_down, EPI_PARTIAL, operand(h, p.F), static_cast<const bf16 *>(lw.w_down), ep,
+        SV_TRY(gemm(p.g_down, EPI_PARTIAL, operand(h), static_cast<const bf16 *>(lw.w_down), ep,
                     stream));
         SV_TRY(reduce_resid_norm(part, p.g_down.splits, M, p.H, next_gain, eps, x, u,
                                  trace ? trace + (int64_t)(l + 1) * M * p.H : nullptr, stream));
     }
-    SV_TRY(gemm(p.g_lm, EPI_ARGMAX, operand(u, p.H), static_cast<const bf16 *>(w->lm_head), ep,
+    SV_TRY(gemm(p.g_lm, EPI_ARGMAX, operand(u), static_cast<const bf16 *>(w->lm_head), ep,
                 stream));
     SV_TRY(argmax_accept(amv, ami, p.lm_groups, draft_tokens, tree_parent, ni, p.B, p.K, greedy,
                          accepted_len, bonus_token, accepted_path, stream));
@@ -299,12 +302,20 @@ int spec_pack_weight(const void *w, int n, int kd, void *packed, hipStream_t str
     return SPEC_OK;
 }
 
+// The partials, then (256-byte aligned) x in fragment order.
+static size_t skinny_partial_bytes(const GemmShape &g, int m, int n) {
+    return ((size_t)g.splits * m * n * sizeof(float) + 255) / 256 * 256;
+}
+static size_t skinny_total_bytes(const GemmShape &g, int m, int n, int kd) {
+    return skinny_partial_bytes(g, m, n) + (size_t)(m + 15) / 16 * 16 * kd * sizeof(uint16_t);
+}
+
 int spec_skinny_gemm_bytes(int m, int n, int kd, size_t *bytes) {
     if (bytes == nullptr) return SPEC_EINVAL;
     GemmShape g;
     const int rc = skinny_shape(m, n, kd, g);
     if (rc != SPEC_OK) return rc;
-    *bytes = (size_t)g.splits * m * n * sizeof(float);
+    *bytes = skinny_total_bytes(g, m, n, kd);
     return SPEC_OK;
 }
 
@@ -314,11 +325,14 @@ int spec_skinny_gemm(const void *x, int m, int kd, const void *w, int n, float *
     GemmShape g;
     const int rc = skinny_shape(m, n, kd, g);
     if (rc != SPEC_OK) return rc;
-    if (partial_bytes < (size_t)g.splits * m * n * sizeof(float)) return SPEC_EWORKSPACE;
+    if (partial_bytes < skinny_total_bytes(g, m, n, kd)) return SPEC_EWORKSPACE;
+    if (reinterpret_cast<uintptr_t>(partials) % 256 != 0) return SPEC_EINVAL;
     *splits = g.splits;
+    bf16 *xp = reinterpret_cast<bf16 *>(reinterpret_cast<char *>(partials) +
+                                        skinny_partial_bytes(g, m, n));
+    SV_TRY(pack_weight(static_cast<const bf16 *>(x), m, kd, xp, stream));
     GemmIn in = {};
-    in.X = static_cast<const bf16 *>(x);
-    in.ldx = kd;
+    in.Xp = xp;
     GemmEpi ep = {};
     ep.y = partials;
     SV_TRY(gemm(g, EPI_PARTIAL, in, static_cast<const bf16 *>(w), ep, stream));
