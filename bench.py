@@ -36,6 +36,17 @@ import synth
 import tree_verification_skinny_amd as tv
 
 METRIC = "verified tokens/sec + verify-step HBM GB/s (% peak), 27B-shape dense, 1 GPU"
+
+# HBM traffic of one gate/up projection launch, from two rocprofv3 --pmc passes over this script
+# (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch, averaged over the kernel's dispatches), each
+# scaled by what the same counter reads for a device-to-device copy of 4 GiB (bytes known). The
+# figures hold for the GEMM source they were taken on; any other source reports null.
+PMC_TRAFFIC = {
+    "block": {"source": "tree_verification_skinny_amd/csrc/k_gemm.hip",
+              "sha256": "289718c84cf27539925f9945e93e4d06ee5a465464db232df06aa0874bd328c1",
+              "fetch_kib": 174922.688, "write_kib": 544.0,
+              "fetch_scale": 1.9999857, "write_scale": 1.0},
+}
 HBM_PEAK_GBPS = 8000.0
 SEED = 20261202
 
@@ -119,6 +130,19 @@ def time_gate_up(step_with_events, events, n_layers, stream, reps):
         t_step += s0.elapsed_time(s1)
         durs.extend(events[2 * l].elapsed_time(events[2 * l + 1]) for l in range(n_layers))
     return float(np.mean(durs)) / 1e3, t_step / reps
+
+
+def pmc_traffic(config):
+    """Counter-measured HBM bytes per gate/up launch, or None when there are no counters for this
+    workload or the GEMM source has changed since they were taken."""
+    import hashlib
+    rec = PMC_TRAFFIC.get(config)
+    if rec is None or rec["sha256"] is None:
+        return None
+    with open(os.path.join(ROOT, rec["source"]), "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != rec["sha256"]:
+            return None
+    return int(round((rec["fetch_kib"] * rec["fetch_scale"] + rec["write_kib"] * rec["write_scale"]) * 1024))
 
 
 def copy_probe(device, nbytes=4 << 30):
@@ -261,14 +285,17 @@ def main():
             run()
         stream.synchronize()
         log(f"warmup done; accepted {acc.cpu().tolist()[:4]} ctx {t_ctx.cpu().tolist()[:4]}")
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(args.steps):
+        # one event between consecutive steps: the whole timed region, and each step's duration
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        ctx_before = t_ctx.clone()
+        marks[0].record(stream)
+        for i in range(args.steps):
             run()
-        e1.record(stream)
-        e1.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
+            marks[i + 1].record(stream)
+        marks[-1].synchronize()
+        committed = (t_ctx - ctx_before).sum().item()     # rows committed over the timed steps
+    ms = marks[0].elapsed_time(marks[-1]) / args.steps
+    per_step = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)])
     ctx_now = t_ctx.cpu().tolist()
     nbytes = step_bytes(shape, B, K, ctx)
     flops = step_flops(shape, B, K, ctx, depth_mean)
@@ -293,6 +320,11 @@ def main():
                 "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4)},
         "mfma": {"flops_per_step": flops, "tflops": round(flops / (ms / 1e3) / 1e12, 2),
                  "frac_of_bf16_peak": round(flops / (ms / 1e3) / 2.5e15, 5)},
+        "step_ms": {"mean": round(ms, 4), "median": round(float(np.median(per_step)), 4),
+                    "p5": round(float(np.percentile(per_step, 5)), 4),
+                    "p95": round(float(np.percentile(per_step, 95)), 4)},
+        "draft_tokens_per_s": round(B * (K - 1) / (ms / 1e3), 2),
+        "committed_tokens_per_s": round(committed / args.steps / (ms / 1e3), 2),
         "ctx_after": ctx_now[:4],
     }
     if not args.no_kernel_timing:
@@ -308,10 +340,11 @@ def main():
         t_ctx.copy_(ctx0)
         b_launch = gate_up_bytes(shape, B * K)
         ach = b_launch / s_launch / 1e9
+        traffic = pmc_traffic(args.config)
         result["roofline"] = {"kernel": "gemm_kernel, SwiGLU epilogue (gate/up projection)",
                               "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS,
                               "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
-                              "traffic": None,
+                              "traffic": traffic,
                               "bytes_per_launch": int(b_launch),
                               "us_per_launch": round(s_launch * 1e6, 2),
                               "share_of_step": round(s_launch * L * 1e3 / ms, 4),

@@ -95,7 +95,7 @@ def test_accept_marks_bad_requests_only():
 # tiny decoder: block of 8, oracle-prefilled prompt of 128, one replaced token
 # ------------------------------------------------------------------------------------------
 
-N_TINY_SEEDS = 40
+N_TINY_SEEDS = 200
 
 
 def test_tiny_block_parity_many_seeds():
