@@ -23,19 +23,29 @@
 
 namespace sv {
 
-template <int D>
-__global__ __launch_bounds__(256) void attn_partial_kernel(
+// HPW kv heads per workgroup (NW waves each) share the chunk's page reads and halve the number
+// of workgroups, so that a typical grid is resident at once.
+template <int D, int NW, int HPW>
+__global__ __launch_bounds__(64 * NW * HPW) void attn_partial_kernel(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k_pool, const bf16 *__restrict__ v_pool,
     const int32_t *__restrict__ block_table, int max_pages, const int32_t *__restrict__ ctx_len,
     const uint64_t *__restrict__ anc, const int32_t *__restrict__ status, int K, int nq, int nkv,
     int n_chunks, float scale_log2, float *__restrict__ part_o, float2 *__restrict__ part_ml) {
     constexpr int CH = kAttnChunk;
+    constexpr int NS = CH / 32;  // 32-key steps per chunk
     constexpr int KP = D + 8;    // padded LDS row of K (bf16)
     constexpr int VP = CH + 8;   // padded LDS row of V^T (bf16)
-    __shared__ __attribute__((aligned(16))) bf16 Ks[CH * KP];
-    __shared__ __attribute__((aligned(16))) bf16 Vt[D * VP];
+    constexpr int STAGERS = 16 * D / 8;   // threads that stage one head's 16-position page
+    static_assert(STAGERS <= 64 * NW, "staging needs one thread per 16 bytes of a page");
+    __shared__ __attribute__((aligned(16))) bf16 Ks_all[HPW * CH * KP];
+    __shared__ __attribute__((aligned(16))) bf16 Vt_all[HPW * D * VP];
 
-    const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int c = blockIdx.x, b = blockIdx.z;
+    const int wave_all = threadIdx.x >> 6;
+    const int hl = wave_all / NW;                 // this wave's head within the workgroup
+    const int g = blockIdx.y * HPW + hl;          // its kv head
+    const bf16 *Ks = Ks_all + hl * CH * KP;
+    const bf16 *Vt = Vt_all + hl * D * VP;
     constexpr int NP = CH / 16;
     // Page ids of this chunk and the request's status and context are read together: the index
     // is clamped to the request's table row (max_pages entries), so these reads are in bounds
@@ -56,7 +66,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
     const int R = group * K;
     const int QT = (R + 15) >> 4;
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = wave_all % NW;
     const int r16 = lane & 15, grp = lane >> 4;
     // the first query tile's fragments are fetched before the chunk, so the two overlap
     bf16x8 qf_next[D / 32];
@@ -67,20 +77,24 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
         tok = col_ok ? rho % K : 0;
         return q + ((int64_t)(b * K + tok) * nq + g * group + hh) * D;
     };
+    uint64_t am_next = 0;
     if (wave < QT) {
         bool ok_;
         int tok_, hh_;
         const bf16 *qrow = q_ptr(wave, ok_, tok_, hh_);
 #pragma unroll
         for (int ds = 0; ds < D / 32; ++ds) qf_next[ds] = *(const bf16x8 *)(qrow + ds * 32 + grp * 8);
+        am_next = anc[b * K + tok_];
     }
 
     // ---- stage the chunk: K rows as stored, V already transposed in the page ---------------
-    // Every thread issues all of its page loads before the first LDS store, so the chunk's
-    // 2 x 8 x 16 B per thread are in flight together.
+    // Every staging thread issues all of its page loads before the first LDS store, so the
+    // chunk's 2 x 8 x 16 B per thread are in flight together.
     {
-        const int e = threadIdx.x * 8;           // element offset inside a 16 x D page
-        const bool has = e < 16 * D;
+        const int hs = threadIdx.x / STAGERS;          // head this thread stages
+        const int gs = blockIdx.y * HPW + hs;
+        const int e = (threadIdx.x % STAGERS) * 8;     // element offset inside a 16 x D page
+        const bool has = hs < HPW;
 #pragma unroll
         for (int p = 0; p < NP; ++p)
             if (!(has && p < npages)) pages[p] = -1;
@@ -88,8 +102,8 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
             if (pages[p] >= 0) {
-                kr[p] = *(const bf16x8 *)(k_pool + ((int64_t)pages[p] * nkv + g) * 16 * D + e);
-                vr[p] = *(const bf16x8 *)(v_pool + ((int64_t)pages[p] * nkv + g) * D * 16 + e);
+                kr[p] = *(const bf16x8 *)(k_pool + ((int64_t)pages[p] * nkv + gs) * 16 * D + e);
+                vr[p] = *(const bf16x8 *)(v_pool + ((int64_t)pages[p] * nkv + gs) * D * 16 + e);
             } else {
                 kr[p] = bf16x8{};
                 vr[p] = bf16x8{};
@@ -100,111 +114,160 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
             const int d = e >> 4, slot = e & 15;
 #pragma unroll
             for (int p = 0; p < NP; ++p) {
-                *(bf16x8 *)&Ks[(p * 16 + row) * KP + col] = kr[p];
+                *(bf16x8 *)&Ks_all[hs * CH * KP + (p * 16 + row) * KP + col] = kr[p];
                 bf16x8 vv = vr[p];
 #pragma unroll
                 for (int j = 0; j < 8; ++j)
                     if (p * 16 + slot + j >= nvalid) vv[j] = (bf16)0.0f;   // never multiply stale data
-                *(bf16x8 *)&Vt[d * VP + p * 16 + slot] = vv;
+                *(bf16x8 *)&Vt_all[hs * D * VP + d * VP + p * 16 + slot] = vv;
             }
         }
     }
     __syncthreads();
 
-    const int nsteps = (nvalid + 31) >> 5;
     const int kr0 = 8 * (r16 >> 2) + (r16 & 3);   // S^T tile 0 key row of this lane (tile 1: +4)
+    // the whole chunk lies inside the committed context: no key needs the mask
+    const bool chunk_plain = nvalid == CH && kb + CH <= ctx;
 
-    for (int t = wave; t < QT; t += 4) {
+    for (int t = wave; t < QT; t += NW) {
         const int rho = 16 * t + r16;             // query column of this lane
         bool col_ok;
         int tok, hh;
         q_ptr(t, col_ok, tok, hh);
-        const uint64_t am = anc[b * K + tok];
+        const uint64_t am = am_next;
         bf16x8 qf[D / 32];
 #pragma unroll
         for (int ds = 0; ds < D / 32; ++ds) qf[ds] = qf_next[ds];
-        if (t + 4 < QT) {                         // next tile's fragments, one tile ahead
-            bool o2;
-            int t2, h2;
-            const bf16 *qn = q_ptr(t + 4, o2, t2, h2);
+
+        // S^T for the whole chunk: step st, half h holds key rows st*32 + kr0 + 4h; with the row
+        // order above, this lane ends up with keys st*32 + 8*grp + e, e = 0..7. The staged chunk
+        // is zero past its valid keys, so all NS steps run (masked below). Key fragments are
+        // read from LDS one step ahead of the products that use them.
+        floatx4 s[NS][2];
+        {
+            // stage i = (step i / 2, half i % 2): D/32 key fragments, D/32 products
+            constexpr int NST = 2 * NS, FK = D / 32;
+            bf16x8 kf0[FK], kf1[FK];
+            auto kload = [&](bf16x8 (&kf)[FK], int i) {
 #pragma unroll
-            for (int ds = 0; ds < D / 32; ++ds) qf_next[ds] = *(const bf16x8 *)(qn + ds * 32 + grp * 8);
+                for (int ds = 0; ds < FK; ++ds)
+                    kf[ds] = *(const bf16x8 *)&Ks[((i >> 1) * 32 + kr0 + 4 * (i & 1)) * KP + grp * 8 + ds * 32];
+            };
+            kload(kf0, 0);
+#pragma unroll
+            for (int i = 0; i < NST; ++i) {
+                auto &cur = (i & 1) ? kf1 : kf0;
+                auto &nxt = (i & 1) ? kf0 : kf1;
+                if (i + 1 < NST) {
+                    kload(nxt, i + 1);
+                    __builtin_amdgcn_sched_group_barrier(0x100, FK, 0);   // LDS reads
+                }
+                floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ds = 0; ds < FK; ++ds) acc = mfma16x16x32(cur[ds], qf[ds], acc);
+                s[i >> 1][i & 1] = acc;
+                __builtin_amdgcn_sched_group_barrier(0x008, FK, 0);       // MFMAs
+            }
         }
+        // one softmax over the chunk, in the log2 domain: m = max, p = 2^(s - m), l = sum p
+        float sv[NS][8];
+        float mloc = -INFINITY;
+        if (chunk_plain) {
+            // every key is committed context, visible to every node (columns past R are
+            // computed on a stand-in query and never stored)
+#pragma unroll
+            for (int st = 0; st < NS; ++st)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    sv[st][e] = (e < 4 ? s[st][0][e] : s[st][1][e - 4]) * scale_log2;
+                    mloc = fmaxf(mloc, sv[st][e]);
+                }
+        } else {
+#pragma unroll
+            for (int st = 0; st < NS; ++st) {
+                // visibility of this lane's 8 keys ka = k0 .. k0 + 7 as a bit mask: committed
+                // positions (< ctx) always, draft positions ctx + j when node j is an ancestor
+                const int k0 = kb + st * 32 + 8 * grp;
+                const int n_ctx = min(max(ctx - k0, 0), 8);
+                const int j0 = max(k0 + n_ctx - ctx, 0);     // first draft index among them
+                const unsigned anc8 = j0 < 64 ? (unsigned)(am >> j0) & 0xffu : 0u;
+                const int n_in = min(max(kb + nvalid - k0, 0), 8);   // keys inside the chunk
+                unsigned vis = (((1u << n_ctx) - 1u) | (anc8 << n_ctx)) & ((1u << n_in) - 1u);
+                if (!col_ok) vis = 0u;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float raw = (e < 4 ? s[st][0][e] : s[st][1][e - 4]) * scale_log2;
+                    sv[st][e] = ((vis >> e) & 1u) ? raw : -INFINITY;
+                    mloc = fmaxf(mloc, sv[st][e]);
+                }
+            }
+        }
+        mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
+        mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+        const bool none = (mloc == -INFINITY);
+        // p = p_hi + p_lo, both bf16: the two products carry ~16 bits of p, so the weighted sum
+        // of values is as precise as the fp32 probabilities it stands for.
+        bf16x8 ph[NS], pl[NS];
+        float psum = 0.f;
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float pv = none ? 0.f : __builtin_amdgcn_exp2f(sv[st][e] - mloc);
+                const bf16 hi = to_bf(pv);
+                ph[st][e] = hi;
+                pl[st][e] = to_bf(pv - to_f(hi));
+                psum += pv;
+            }
+        }
+        psum += __shfl_xor(psum, 16, 64);
+        psum += __shfl_xor(psum, 32, 64);
+
+        // O^T = V^T . P^T over the chunk, value fragments read one step ahead
         floatx4 o[D / 16];
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt) o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
-        float m_run = -INFINITY, l_run = 0.f;
-
-        for (int st = 0; st < nsteps; ++st) {
-            floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-            const bf16 *k0 = &Ks[(st * 32 + kr0) * KP + grp * 8];
-            const bf16 *k1 = k0 + 4 * KP;
+        {
+            // stage i = (step i / 2, value rows half i % 2): FV fragments, 2 FV products
+            constexpr int NST = 2 * NS, FV = D / 32;
+            bf16x8 vf0[FV], vf1[FV];
+            auto vload = [&](bf16x8 (&vf)[FV], int i) {
 #pragma unroll
-            for (int ds = 0; ds < D / 32; ++ds) {
-                s0 = mfma16x16x32(*(const bf16x8 *)(k0 + ds * 32), qf[ds], s0);
-                s1 = mfma16x16x32(*(const bf16x8 *)(k1 + ds * 32), qf[ds], s1);
-            }
-            float sv[8];
-            float mloc = -INFINITY;
-            // a 32-key step wholly inside the committed context needs no mask
-            const bool plain = col_ok && st * 32 + 32 <= nvalid && kb + st * 32 + 32 <= ctx;
-            if (plain) {
+                for (int j = 0; j < FV; ++j)
+                    vf[j] = *(const bf16x8 *)&Vt[(r16 + ((i & 1) * FV + j) * 16) * VP + (i >> 1) * 32 + grp * 8];
+            };
+            vload(vf0, 0);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    sv[e] = (e < 4 ? s0[e] : s1[e - 4]) * scale_log2;
-                    mloc = fmaxf(mloc, sv[e]);
+            for (int i = 0; i < NST; ++i) {
+                auto &cur = (i & 1) ? vf1 : vf0;
+                auto &nxt = (i & 1) ? vf0 : vf1;
+                if (i + 1 < NST) {
+                    vload(nxt, i + 1);
+                    __builtin_amdgcn_sched_group_barrier(0x100, FV, 0);        // LDS reads
                 }
-            } else {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float raw = e < 4 ? s0[e] : s1[e - 4];
-                    const int kl = st * 32 + 8 * grp + e;
-                    const int ka = kb + kl;
-                    const bool vis = col_ok && kl < nvalid && (ka < ctx || ((am >> (ka - ctx)) & 1ull));
-                    sv[e] = vis ? raw * scale_log2 : -INFINITY;
-                    mloc = fmaxf(mloc, sv[e]);
+                for (int j = 0; j < FV; ++j) {
+                    const int dt = (i & 1) * FV + j;
+                    o[dt] = mfma16x16x32(cur[j], ph[i >> 1], o[dt]);
+                    o[dt] = mfma16x16x32(cur[j], pl[i >> 1], o[dt]);
                 }
-            }
-            mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
-            mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-            const float m_new = fmaxf(m_run, mloc);
-            const bool none = (m_new == -INFINITY);
-            const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-            // p = p_hi + p_lo, both bf16: the two products carry ~16 bits of p, so the weighted
-            // sum of values is as precise as the fp32 probabilities it stands for.
-            bf16x8 ph, pl;
-            float psum = 0.f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float pv = none ? 0.f : __builtin_amdgcn_exp2f(sv[e] - m_new);
-                const bf16 hi = to_bf(pv);
-                ph[e] = hi;
-                pl[e] = to_bf(pv - to_f(hi));
-                psum += pv;
-            }
-            l_run = l_run * alpha + psum;
-            m_run = m_new;
-            // the accumulators need rescaling only when some column's running maximum moved
-            if (__any(alpha != 1.f)) {
-#pragma unroll
-                for (int dt = 0; dt < D / 16; ++dt) o[dt] *= alpha;
-            }
-            const bf16 *vrow = &Vt[r16 * VP + st * 32 + grp * 8];
-#pragma unroll
-            for (int dt = 0; dt < D / 16; ++dt) {
-                const bf16x8 vf = *(const bf16x8 *)(vrow + dt * 16 * VP);
-                o[dt] = mfma16x16x32(vf, ph, o[dt]);
-                o[dt] = mfma16x16x32(vf, pl, o[dt]);
+                __builtin_amdgcn_sched_group_barrier(0x008, 2 * FV, 0);    // MFMAs
             }
         }
-        l_run += __shfl_xor(l_run, 16, 64);
-        l_run += __shfl_xor(l_run, 32, 64);
+        if (t + NW < QT) {   // the next tile's operands, fetched while this tile's results drain
+            bool o2;
+            int t2, h2;
+            const bf16 *qn = q_ptr(t + NW, o2, t2, h2);
+#pragma unroll
+            for (int ds = 0; ds < D / 32; ++ds) qf_next[ds] = *(const bf16x8 *)(qn + ds * 32 + grp * 8);
+            am_next = anc[b * K + t2];
+        }
         if (col_ok) {
             const int64_t base = (((int64_t)b * nkv + g) * n_chunks + c) * R + rho;
 #pragma unroll
             for (int dt = 0; dt < D / 16; ++dt)
                 *(floatx4 *)(part_o + base * D + dt * 16 + 4 * grp) = o[dt];
-            if (grp == 0) part_ml[base] = make_float2(m_run, l_run);
+            if (grp == 0) part_ml[base] = make_float2(mloc, psum);
         }
     }
 }
@@ -284,24 +347,36 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(
 
 hipError_t attention(const AttnArgs &a, hipStream_t st) {
     const float scale_log2 = kLog2e / sqrtf((float)a.D);
-    dim3 grid(a.n_chunks, a.nkv, a.B);
+    // waves per kv head: 5 when that takes fewer query tiles per wave than 4 (one tile each for
+    // a group of 5 q heads and a block of 16), else 4
+    const int QT = (a.nq / a.nkv * a.K + 15) / 16;
+    const int nw = (QT + 4) / 5 < (QT + 3) / 4 ? 5 : 4;
+    const int hpw = a.nkv % 2 == 0 ? 2 : 1;
+    const dim3 grid_h(a.n_chunks, a.nkv / hpw, a.B);
+#define SV_ATTN(DD, NWV, HP)                                                                      \
+    hipLaunchKernelGGL((attn_partial_kernel<DD, NWV, HP>), grid_h, dim3(64 * NWV * HP), 0, st,    \
+                       a.q, a.k_pool, a.v_pool, a.block_table, a.max_pages, a.ctx_len, a.anc,      \
+                       a.status, a.K, a.nq, a.nkv, a.n_chunks, scale_log2, a.part_o, a.part_ml)
+#define SV_ATTN_H(DD, NWV)          \
+    if (hpw == 2) SV_ATTN(DD, NWV, 2); \
+    else SV_ATTN(DD, NWV, 1)
     if (a.D == 128) {
-        hipLaunchKernelGGL(attn_partial_kernel<128>, grid, dim3(256), 0, st, a.q, a.k_pool, a.v_pool,
-                           a.block_table, a.max_pages, a.ctx_len, a.anc, a.status, a.K, a.nq, a.nkv,
-                           a.n_chunks, scale_log2, a.part_o, a.part_ml);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
+        if (nw == 4) { SV_ATTN_H(128, 4); }
+        else { SV_ATTN_H(128, 5); }
+    } else {
+        if (nw == 4) { SV_ATTN_H(64, 4); }
+        else { SV_ATTN_H(64, 5); }
+    }
+#undef SV_ATTN_H
+#undef SV_ATTN
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (a.D == 128)
         hipLaunchKernelGGL(attn_combine_kernel<128>, dim3(a.B * a.K, a.nq), dim3(256), 0, st,
                            a.part_o, a.part_ml, a.ctx_len, a.status, a.K, a.nq, a.nkv, a.n_chunks, a.out);
-    } else {
-        hipLaunchKernelGGL(attn_partial_kernel<64>, grid, dim3(256), 0, st, a.q, a.k_pool, a.v_pool,
-                           a.block_table, a.max_pages, a.ctx_len, a.anc, a.status, a.K, a.nq, a.nkv,
-                           a.n_chunks, scale_log2, a.part_o, a.part_ml);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
+    else
         hipLaunchKernelGGL(attn_combine_kernel<64>, dim3(a.B * a.K, a.nq), dim3(256), 0, st,
                            a.part_o, a.part_ml, a.ctx_len, a.status, a.K, a.nq, a.nkv, a.n_chunks, a.out);
-    }
     return hipGetLastError();
 }
 
