@@ -213,6 +213,196 @@ __global__ __launch_bounds__(64 * W) void gemm_kernel(GemmIn in, const bf16 *__r
     }
 }
 
+// ---- wide variant (more than 16 rows): waves split the weight tiles, activations via LDS ---------
+// With 32..64 rows each weight fragment meets up to four activation fragments, and reading those
+// from L2 per wave would cost more than the weights themselves. Here the workgroup's 4 waves each
+// own TN = 2 weight tiles over the whole K range of the workgroup, and the activation rows pass
+// through LDS once per workgroup in slabs of KS K-steps (double-buffered: slab j+1 is fetched
+// from L2 while slab j is multiplied). A wave's weight fragments for the next slab are in flight
+// while it multiplies the current one. One barrier per slab.
+constexpr int kWideWaves = 4, kWideTN = 2, kWideKS = 8;
+
+// output column of tile t (0..TN-1) of wave w in group ng: SwiGLU pairs gate and up columns in the
+// same wave and lane
+template <int EPI>
+__device__ __forceinline__ int wide_col(int ng, int w, int t, int F) {
+    if constexpr (EPI == EPI_SWIGLU) {
+        return (t == 0 ? 0 : F) + (ng * kWideWaves + w) * 16;
+    } else {
+        return ((ng * kWideWaves + w) * kWideTN + t) * 16;
+    }
+}
+
+template <int TM, int EPI>
+__global__ __launch_bounds__(64 * kWideWaves) void gemm_wide_kernel(GemmIn in, const bf16 *__restrict__ Wp,
+                                                                     int N, int Kd, int n_groups,
+                                                                     int ksteps, GemmEpi ep) {
+    constexpr int NW = kWideWaves, TN = kWideTN, KS = kWideKS;
+    constexpr int SLOTS = KS * TM * 64;                 // 16-byte slots per slab
+    constexpr int PER = SLOTS / (64 * NW);              // slots staged per thread
+    static_assert(SLOTS % (64 * NW) == 0, "slab must split evenly over the threads");
+    __shared__ bf16x8 xs[2][SLOTS];                     // [buffer][(step * TM + block) * 64 + lane]
+    __shared__ float red_v[NW][64];
+    __shared__ int red_i[NW][64];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r16 = lane & 15, grp = lane >> 4;
+    const int ng = blockIdx.x % n_groups;
+    const int split = blockIdx.x / n_groups;
+    const int S = Kd >> 5;
+    const int s_begin = split * ksteps;
+    const int s_end = min(s_begin + ksteps, S);
+    const int nsteps = s_end > s_begin ? s_end - s_begin : 0;
+    const int nslabs = (nsteps + KS - 1) / KS;
+    const int M = in.M, m0 = in.m0;
+    const int nblk = (in.M_total + 15) >> 4;
+
+    const bf16 *wp[TN];
+#pragma unroll
+    for (int t = 0; t < TN; ++t)
+        wp[t] = Wp + ((((int64_t)(wide_col<EPI>(ng, wave, t, ep.F) >> 4)) * S + s_begin) * 64 + lane) * 8;
+
+    // staging: thread slot i = threadIdx.x + 256 r covers (step, block, lane) of the slab
+    auto stage_load = [&](bf16x8 (&xr)[PER], int slab) {
+#pragma unroll
+        for (int r = 0; r < PER; ++r) {
+            const int i = threadIdx.x + r * 64 * NW;
+            const int l = i & 63, mt = (i >> 6) % TM, k = (i >> 6) / TM;
+            const int s = s_begin + slab * KS + k;
+            const int blk = min((m0 >> 4) + mt, nblk - 1);
+            xr[r] = s < s_end ? *(const bf16x8 *)(in.Xp + (((int64_t)blk * S + s) * 64 + l) * 8) : bf16x8{};
+        }
+    };
+    auto stage_store = [&](const bf16x8 (&xr)[PER], int buf) {
+#pragma unroll
+        for (int r = 0; r < PER; ++r) xs[buf][threadIdx.x + r * 64 * NW] = xr[r];
+    };
+    auto w_load = [&](bf16x8 (&a)[KS][TN], int slab) {
+#pragma unroll
+        for (int k = 0; k < KS; ++k) {
+            const int s = slab * KS + k;                 // relative to s_begin
+#pragma unroll
+            for (int t = 0; t < TN; ++t)
+                a[k][t] = s < nsteps ? *(const bf16x8 *)(wp[t] + (int64_t)s * 512) : bf16x8{};
+        }
+    };
+
+    floatx4 acc[TN][TM];
+#pragma unroll
+    for (int t = 0; t < TN; ++t)
+#pragma unroll
+        for (int mt = 0; mt < TM; ++mt) acc[t][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    auto multiply = [&](const bf16x8 (&a)[KS][TN], int buf, int slab) {
+        const int kmax = min(KS, nsteps - slab * KS);
+#pragma unroll
+        for (int k = 0; k < KS; ++k) {
+            if (k < kmax) {
+                bf16x8 b[TM];
+#pragma unroll
+                for (int mt = 0; mt < TM; ++mt) b[mt] = xs[buf][(k * TM + mt) * 64 + lane];
+#pragma unroll
+                for (int t = 0; t < TN; ++t)
+#pragma unroll
+                    for (int mt = 0; mt < TM; ++mt) acc[t][mt] = mfma16x16x32(a[k][t], b[mt], acc[t][mt]);
+            }
+        }
+    };
+
+    if (nslabs > 0) {
+        bf16x8 wa[KS][TN], wb[KS][TN], xr[PER];
+        stage_load(xr, 0);
+        w_load(wa, 0);
+        stage_store(xr, 0);
+        __syncthreads();
+        // two slabs per iteration so that the register buffers are named statically
+        for (int j = 0; j < nslabs; j += 2) {
+            if (j + 1 < nslabs) { stage_load(xr, j + 1); w_load(wb, j + 1); }
+            multiply(wa, 0, j);
+            if (j + 1 < nslabs) stage_store(xr, 1);
+            __syncthreads();
+            if (j + 1 >= nslabs) break;
+            if (j + 2 < nslabs) { stage_load(xr, j + 2); w_load(wa, j + 2); }
+            multiply(wb, 1, j + 1);
+            if (j + 2 < nslabs) stage_store(xr, 0);
+            __syncthreads();
+        }
+    }
+
+    // ---- epilogues (each wave owns its tiles' whole sums) -------------------------------------
+    int col[TN];
+#pragma unroll
+    for (int t = 0; t < TN; ++t) col[t] = wide_col<EPI>(ng, wave, t, ep.F) + 4 * grp;
+    float bv_all[TM];
+    int bi_all[TM];
+#pragma unroll
+    for (int mt = 0; mt < TM; ++mt) {
+        const int m = 16 * mt + r16;
+        const bool live = m < M;
+        const int row = m0 + m;
+        bv_all[mt] = -INFINITY;
+        bi_all[mt] = 0x7fffffff;
+        if constexpr (EPI == EPI_PARTIAL) {
+            if (live) {
+#pragma unroll
+                for (int t = 0; t < TN; ++t)
+                    *(floatx4 *)(ep.y + ((int64_t)split * in.M_total + row) * N + col[t]) = acc[t][mt];
+            }
+        } else if constexpr (EPI == EPI_SWIGLU) {
+            if (live) {
+                float hv[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float g = round_bf(acc[0][mt][j]);
+                    const float u = round_bf(acc[1][mt][j]);
+                    hv[j] = (g / (1.0f + expf(-g))) * u;
+                }
+                store4(ep.h + frag_off(row, col[0], ep.F), hv[0], hv[1], hv[2], hv[3]);
+            }
+        } else if constexpr (EPI == EPI_ARGMAX) {
+            float bv = -INFINITY;
+            int bi = 0x7fffffff;
+#pragma unroll
+            for (int t = 0; t < TN; ++t) {
+                if (ep.logits != nullptr && live) *(floatx4 *)(ep.logits + (int64_t)row * N + col[t]) = acc[t][mt];
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (better(acc[t][mt][j], col[t] + j, bv, bi)) { bv = acc[t][mt][j]; bi = col[t] + j; }
+            }
+#pragma unroll
+            for (int o = 16; o < 64; o <<= 1) {
+                const float ov = __shfl_xor(bv, o, 64);
+                const int oi = __shfl_xor(bi, o, 64);
+                if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+            }
+            bv_all[mt] = bv;
+            bi_all[mt] = bi;
+        }
+    }
+    if constexpr (EPI == EPI_ARGMAX) {
+        // the group's best per row over its 4 waves, in wave order
+#pragma unroll
+        for (int mt = 0; mt < TM; ++mt) {
+            if (grp == 0) { red_v[wave][r16 + 16 * (mt & 3)] = bv_all[mt]; red_i[wave][r16 + 16 * (mt & 3)] = bi_all[mt]; }
+            if ((mt & 3) == 3 || mt == TM - 1) {
+                __syncthreads();
+                if (wave == 0 && lane < 16 * ((mt & 3) + 1)) {
+                    float bv = red_v[0][lane];
+                    int bi = red_i[0][lane];
+                    for (int w = 1; w < NW; ++w)
+                        if (better(red_v[w][lane], red_i[w][lane], bv, bi)) { bv = red_v[w][lane]; bi = red_i[w][lane]; }
+                    const int m = 16 * (mt & ~3) + lane;
+                    if (m < M) {
+                        ep.amax_val[(int64_t)ng * in.M_total + m0 + m] = bv;
+                        ep.amax_idx[(int64_t)ng * in.M_total + m0 + m] = bi;
+                    }
+                }
+                __syncthreads();
+            }
+        }
+    }
+}
+
 static int mt_for(int m) { return m <= 16 ? 1 : (m <= 32 ? 2 : 4); }
 
 int gemm_groups(const GemmShape &g) { return g.N / (16 * g.nt); }
@@ -264,6 +454,20 @@ static hipError_t by_tiles(const GemmShape &g, const GemmIn &in, const bf16 *Wp,
     }
 }
 
+template <int EPI>
+static hipError_t launch_wide(const GemmShape &g, const GemmIn &in, const bf16 *Wp, const GemmEpi &ep,
+                              hipStream_t st) {
+    const int steps = g.Kd >> 5;
+    const int ks = (steps + g.splits - 1) / g.splits;
+    const dim3 grid(gemm_groups(g) * g.splits), block(64 * kWideWaves);
+    switch (mt_for(in.M)) {
+        case 1: hipLaunchKernelGGL((gemm_wide_kernel<1, EPI>), grid, block, 0, st, in, Wp, g.N, g.Kd, gemm_groups(g), ks, ep); break;
+        case 2: hipLaunchKernelGGL((gemm_wide_kernel<2, EPI>), grid, block, 0, st, in, Wp, g.N, g.Kd, gemm_groups(g), ks, ep); break;
+        default: hipLaunchKernelGGL((gemm_wide_kernel<4, EPI>), grid, block, 0, st, in, Wp, g.N, g.Kd, gemm_groups(g), ks, ep); break;
+    }
+    return hipGetLastError();
+}
+
 hipError_t gemm(const GemmShape &g, int epi, const GemmIn &in_all, const bf16 *Wp,
                 const GemmEpi &ep, hipStream_t st) {
     for (int m0 = 0; m0 < g.M; m0 += 64) {
@@ -272,11 +476,20 @@ hipError_t gemm(const GemmShape &g, int epi, const GemmIn &in_all, const bf16 *W
         in.m0 = m0;
         in.M = g.M - m0 < 64 ? g.M - m0 : 64;
         hipError_t e;
-        switch (epi) {
-            case EPI_PARTIAL: e = by_tiles<EPI_PARTIAL>(g, in, Wp, ep, st); break;
-            case EPI_SWIGLU: e = by_tiles<EPI_SWIGLU>(g, in, Wp, ep, st); break;
-            case EPI_ARGMAX: e = by_tiles<EPI_ARGMAX>(g, in, Wp, ep, st); break;
-            default: return hipErrorInvalidValue;
+        if (g.wide) {
+            switch (epi) {
+                case EPI_PARTIAL: e = launch_wide<EPI_PARTIAL>(g, in, Wp, ep, st); break;
+                case EPI_SWIGLU: e = launch_wide<EPI_SWIGLU>(g, in, Wp, ep, st); break;
+                case EPI_ARGMAX: e = launch_wide<EPI_ARGMAX>(g, in, Wp, ep, st); break;
+                default: return hipErrorInvalidValue;
+            }
+        } else {
+            switch (epi) {
+                case EPI_PARTIAL: e = by_tiles<EPI_PARTIAL>(g, in, Wp, ep, st); break;
+                case EPI_SWIGLU: e = by_tiles<EPI_SWIGLU>(g, in, Wp, ep, st); break;
+                case EPI_ARGMAX: e = by_tiles<EPI_ARGMAX>(g, in, Wp, ep, st); break;
+                default: return hipErrorInvalidValue;
+            }
         }
         if (e != hipSuccess) return e;
     }
@@ -294,11 +507,36 @@ GemmShape plan_gemm(int M, int N, int Kd, bool allow_split) {
     g.M = M;
     g.N = N;
     g.Kd = Kd;
+    g.wide = false;
+    const int steps = Kd / 32;
+    if (M > 16 && N % (16 * kWideWaves * kWideTN) == 0) {
+        // wide variant: 8 tiles per workgroup; split K (multiples of the slab where possible)
+        // until at least 256 workgroups stream
+        g.wide = true;
+        g.nt = kWideWaves * kWideTN;
+        g.waves = kWideWaves;
+        const int groups = N / (16 * g.nt);
+        g.splits = 1;
+        if (allow_split && groups < 256) {
+            int best = 0;
+            for (int sp = 2; sp <= 32 && sp <= steps; ++sp) {
+                if (steps % sp != 0 || (steps / sp) % kWideKS != 0) continue;
+                best = sp;
+                if (groups * sp >= 256) break;
+            }
+            if (best == 0) {
+                best = (256 + groups - 1) / groups;
+                if (best > 32) best = 32;
+                while (best > 1 && steps / best < kWideKS) --best;
+            }
+            g.splits = best;
+        }
+        return g;
+    }
     const int mt = mt_for(M < 64 ? M : 64);
     g.nt = (N % 64 == 0) ? 4 : (N % 32 == 0 ? 2 : 1);
     if (mt == 4 && g.nt == 4) g.nt = 2;
     const int groups = N / (16 * g.nt);
-    const int steps = Kd / 32;
     g.splits = 1;
     if (allow_split && groups < 400) {
         g.splits = (640 + groups / 2) / groups;

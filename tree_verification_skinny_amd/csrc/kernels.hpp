@@ -12,9 +12,10 @@ namespace sv {
 
 struct GemmShape {
     int M, N, Kd;
-    int nt;         // 16-row weight tiles per workgroup (1, 2 or 4)
-    int waves;      // waves per workgroup splitting K inside it (4 or 8)
+    int nt;         // 16-row weight tiles per workgroup (1, 2 or 4; 8 for the wide variant)
+    int waves;      // waves per workgroup (splitting K, or the tiles in the wide variant)
     int splits;     // K splits across workgroups (fp32 partials when > 1)
+    bool wide;      // more than 16 rows: waves split the tiles, activations staged in LDS
 };
 
 // What a workgroup does with its finished tiles: partial sums of its K split, or (whole K)
