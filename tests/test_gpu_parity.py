@@ -238,6 +238,39 @@ def test_tiny_ragged_batch_with_shuffled_pages():
                      int(out.bonus[b]), out.path[b])
 
 
+def test_tiny_large_batch_uses_tile_kernel():
+    """24 requests x 16 nodes = 384 rows: the projections take the matrix-core tile path (one
+    full 256-row launch and a partial one), with ragged contexts and shuffled pages."""
+    B, k = 24, 16
+    w = synth.model_weights(synth.TINY, 123)
+    m = oracle_model_from(synth.TINY, w)
+    ctxs = [int(c) for c in np.random.default_rng(5).integers(0, 300, B)]
+    weights = device_weights(synth.TINY, w, DEV)
+    kv = make_kv(synth.TINY, ctxs, k, 123, DEV)
+    toks, cases = [], []
+    for b, ctx in enumerate(ctxs):
+        kvs = [synth.kv_context(synth.TINY, ctx, 123, l, request=b) for l in range(2)]
+        kc = [bits(x) for x, _ in kvs]
+        vc = [bits(y) for _, y in kvs]
+        upload_context(kv, b, kc, vc)
+        tok = synth.uniform_tokens(k, 1024, 123, b)
+        if b % 3 == 0:                       # some drafts follow the target greedily for a while
+            cont, _, _, _ = oracle.ar_greedy(m, kc, vc, int(tok[0]), k - 1)
+            tok[1:] = cont
+            cut = 1 + (b // 3) % (k - 1)
+            tok[cut] = (tok[cut] + 1) % 1024
+        toks.append(tok)
+        cases.append((kc, vc))
+    tokens = np.stack(toks).astype(np.int32)
+    out = run_verify(weights, kv, tokens, None, ctxs)
+    for b in range(B):
+        kc, vc = cases[b]
+        r = oracle.verify(m, kc, vc, tokens[b])
+        check_logits(out.logits[b], r.logits, f"request {b}")
+        check_accept(r, tokens[b], None, out.greedy[b], int(out.accepted_len[b]),
+                     int(out.bonus[b]), out.path[b])
+
+
 def test_bad_requests_are_isolated():
     B, k = 4, 8
     w = synth.model_weights(synth.TINY, 5)

@@ -470,6 +470,18 @@ static hipError_t launch_wide(const GemmShape &g, const GemmIn &in, const bf16 *
 
 hipError_t gemm(const GemmShape &g, int epi, const GemmIn &in_all, const bf16 *Wp,
                 const GemmEpi &ep, hipStream_t st) {
+    if (g.tc) {
+        const int rows = gemm_tc_rows();
+        for (int m0 = 0; m0 < g.M; m0 += rows) {
+            GemmIn in = in_all;
+            in.M_total = g.M;
+            in.m0 = m0;
+            in.M = g.M - m0 < rows ? g.M - m0 : rows;
+            const hipError_t e = gemm_tc(g, epi, in, Wp, ep, st);
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }
     for (int m0 = 0; m0 < g.M; m0 += 64) {
         GemmIn in = in_all;
         in.M_total = g.M;
@@ -508,7 +520,23 @@ GemmShape plan_gemm(int M, int N, int Kd, bool allow_split) {
     g.N = N;
     g.Kd = Kd;
     g.wide = false;
+    g.tc = false;
     const int steps = Kd / 32;
+    if (M >= 128 && N % gemm_tc_columns() == 0) {
+        // hundreds of rows: the matrix-core tile kernel (two workgroups per compute unit); narrow
+        // projections split K into as many parts as fit one round of 512 workgroups
+        g.tc = true;
+        g.nt = gemm_tc_columns() / 16;
+        g.waves = 4;
+        const int groups = N / gemm_tc_columns();
+        g.splits = 1;
+        if (allow_split && groups < 256) {
+            g.splits = 512 / groups;
+            if (g.splits > 16) g.splits = 16;
+            while (g.splits > 1 && steps / g.splits < 8) --g.splits;
+        }
+        return g;
+    }
     if (M > 16 && N % (16 * kWideWaves * kWideTN) == 0) {
         // wide variant: 8 tiles per workgroup; split K (multiples of the slab where possible)
         // until at least 256 workgroups stream

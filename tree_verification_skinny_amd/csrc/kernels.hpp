@@ -16,6 +16,7 @@ struct GemmShape {
     int waves;      // waves per workgroup (splitting K, or the tiles in the wide variant)
     int splits;     // K splits across workgroups (fp32 partials when > 1)
     bool wide;      // more than 16 rows: waves split the tiles, activations staged in LDS
+    bool tc;        // a batch of hundreds of rows: the matrix-core-bound tile kernel
 };
 
 // What a workgroup does with its finished tiles: partial sums of its K split, or (whole K)
@@ -46,6 +47,12 @@ hipError_t gemm(const GemmShape &g, int epi, const GemmIn &in, const bf16 *Wp, c
                 hipStream_t st);
 // Row-major [n][kd] -> fragment order; rows up to the next multiple of 16 are zero.
 hipError_t pack_weight(const bf16 *w, int n, int kd, bf16 *out, hipStream_t st);
+// The tile kernel for hundreds of rows (k_gemm_tc.hip): one launch covers gemm_tc_rows() rows
+// starting at in.m0 (in.M of them) and gemm_tc_columns() columns per workgroup.
+hipError_t gemm_tc(const GemmShape &g, int epi, const GemmIn &in, const bf16 *Wp, const GemmEpi &ep,
+                   hipStream_t st);
+int gemm_tc_columns();
+int gemm_tc_rows();
 
 // ---- attention ------------------------------------------------------------------------------
 
