@@ -471,16 +471,11 @@ static hipError_t launch_wide(const GemmShape &g, const GemmIn &in, const bf16 *
 hipError_t gemm(const GemmShape &g, int epi, const GemmIn &in_all, const bf16 *Wp,
                 const GemmEpi &ep, hipStream_t st) {
     if (g.tc) {
-        const int rows = gemm_tc_rows();
-        for (int m0 = 0; m0 < g.M; m0 += rows) {
-            GemmIn in = in_all;
-            in.M_total = g.M;
-            in.m0 = m0;
-            in.M = g.M - m0 < rows ? g.M - m0 : rows;
-            const hipError_t e = gemm_tc(g, epi, in, Wp, ep, st);
-            if (e != hipSuccess) return e;
-        }
-        return hipSuccess;
+        GemmIn in = in_all;
+        in.M_total = g.M;
+        in.m0 = 0;
+        in.M = g.M;
+        return gemm_tc(g, epi, in, Wp, ep, st);
     }
     for (int m0 = 0; m0 < g.M; m0 += 64) {
         GemmIn in = in_all;
@@ -523,15 +518,17 @@ GemmShape plan_gemm(int M, int N, int Kd, bool allow_split) {
     g.tc = false;
     const int steps = Kd / 32;
     if (M >= 128 && N % gemm_tc_columns() == 0) {
-        // hundreds of rows: the matrix-core tile kernel (two workgroups per compute unit); narrow
-        // projections split K into as many parts as fit one round of 512 workgroups
+        // hundreds of rows: the matrix-core tile kernel, one launch over all 256-row tiles;
+        // narrow projections split K so that about 768 workgroups (three per compute unit at
+        // most) make one round
         g.tc = true;
         g.nt = gemm_tc_columns() / 16;
         g.waves = 4;
         const int groups = N / gemm_tc_columns();
+        const int mtiles = (M + 255) / 256;
         g.splits = 1;
-        if (allow_split && groups < 256) {
-            g.splits = 512 / groups;
+        if (allow_split && groups * mtiles < 384) {
+            g.splits = 768 / (groups * mtiles);
             if (g.splits > 16) g.splits = 16;
             while (g.splits > 1 && steps / g.splits < 8) --g.splits;
         }

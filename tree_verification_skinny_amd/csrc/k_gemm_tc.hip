@@ -12,9 +12,12 @@
 //     both already in MFMA fragment order, so every load is a contiguous 1 KB wave read) pass
 //     through LDS; a wave reads 12 of them (4 + 8) for its 32 products.
 //   * The fragments go from HBM / L2 straight into LDS (global_load_lds, no register staging),
-//     two K steps ahead of the products, into a ring of three LDS stages (72 KB, so that two
-//     workgroups share a compute unit); one wait and one barrier per step. Without a register
-//     ring the loop body is a single copy and the 128 accumulator registers stay where they are.
+//     one K step ahead of the products, into two LDS stages (48 KB, so that three workgroups
+//     share a compute unit and cover each other's load latency); one wait and one barrier per
+//     step. Without a register ring the loop body is a single copy and the 128 accumulator
+//     registers stay where they are.
+//   * One launch covers every 256-row tile; the tiles of one column group go to workgroups that
+//     run back to back on the same XCD, so the weights come from HBM once and from L2 after.
 //   * Epilogues as in the skinny kernel: fp32 split-K partials, SwiGLU (a wave holds gate tiles
 //     and the matching up tiles), or the per-row greedy maximum of the output head.
 #include "kernels.hpp"
@@ -30,7 +33,10 @@ constexpr int kMB = kWM * kTM;                 // row blocks per workgroup (256 
 constexpr int kThreads = 64 * kWN * kWM;       // 256
 constexpr int kSlots = (kNT + kMB) * 64;       // 16-byte slots per K step: 8 + 16 fragments
 constexpr int kPer = kSlots / kThreads;        // slots staged per thread per step (6)
-constexpr int kStages = 3;                     // LDS stages: K steps in flight + the one in use
+#ifndef SV_TC_STAGES
+#define SV_TC_STAGES 2
+#endif
+constexpr int kStages = SV_TC_STAGES;          // LDS stages: K steps in flight + the one in use
 static_assert(kSlots % kThreads == 0, "a K step must split evenly over the threads");
 
 // s_waitcnt with vmcnt <= n (n < 64) and the other counters unconstrained
@@ -55,7 +61,7 @@ __device__ __forceinline__ int tc_col(int ng, int t, int F) {
 template <int EPI>
 __global__ __launch_bounds__(kThreads, 2) void gemm_tc_kernel(GemmIn in, const bf16 *__restrict__ Wp,
                                                            int N, int Kd, int n_groups, int ksteps,
-                                                           GemmEpi ep) {
+                                                           int n_units, int n_mt, GemmEpi ep) {
     __shared__ bf16x8 lds[kStages][kSlots];
     __shared__ float red_v[kWN][kMB * 16];
     __shared__ int red_i[kWN][kMB * 16];
@@ -64,13 +70,21 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_tc_kernel(GemmIn in, const b
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wn = wave % kWN, wm = wave / kWN;
     const int r16 = lane & 15, grp = lane >> 4;
-    const int ng = blockIdx.x % n_groups;
-    const int split = blockIdx.x / n_groups;
+    // workgroup -> (row tile, column group, split). Consecutive workgroups land on consecutive
+    // XCDs, so the row tiles of one (group, split) are given to workgroups 8 apart: they run back
+    // to back on the same XCD and the second finds the weights in that XCD's L2.
+    const int xcd = blockIdx.x & 7, q = blockIdx.x >> 3;
+    const int mtile = q % n_mt;
+    const int unit = (q / n_mt) * 8 + xcd;
+    if (unit >= n_units) return;                 // grid padding
+    const int ng = unit % n_groups;
+    const int split = unit / n_groups;
     const int S = Kd >> 5;
     const int s_begin = split * ksteps;
     const int s_end = min(s_begin + ksteps, S);
     const int nsteps = s_end > s_begin ? s_end - s_begin : 0;
-    const int M = in.M, m0 = in.m0;
+    const int m0 = mtile * kMB * 16;
+    const int M = min(in.M_total - m0, kMB * 16);
     const int nblk = (in.M_total + 15) >> 4;
 
     // the global source of each of this thread's slots (step 0 of the split): slot
@@ -211,18 +225,19 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_tc_kernel(GemmIn in, const b
 }  // namespace
 
 int gemm_tc_columns() { return kNT * 16; }
-int gemm_tc_rows() { return kMB * 16; }
 
 hipError_t gemm_tc(const GemmShape &g, int epi, const GemmIn &in, const bf16 *Wp, const GemmEpi &ep,
                    hipStream_t st) {
     const int steps = g.Kd >> 5;
     const int ks = (steps + g.splits - 1) / g.splits;
     const int groups = g.N / (kNT * 16);
-    const dim3 grid(groups * g.splits), block(kThreads);
+    const int units = groups * g.splits;
+    const int n_mt = (in.M_total + kMB * 16 - 1) / (kMB * 16);
+    const dim3 grid((unsigned)((units + 7) / 8 * 8 * n_mt)), block(kThreads);
     switch (epi) {
-        case EPI_PARTIAL: hipLaunchKernelGGL(gemm_tc_kernel<EPI_PARTIAL>, grid, block, 0, st, in, Wp, g.N, g.Kd, groups, ks, ep); break;
-        case EPI_SWIGLU: hipLaunchKernelGGL(gemm_tc_kernel<EPI_SWIGLU>, grid, block, 0, st, in, Wp, g.N, g.Kd, groups, ks, ep); break;
-        case EPI_ARGMAX: hipLaunchKernelGGL(gemm_tc_kernel<EPI_ARGMAX>, grid, block, 0, st, in, Wp, g.N, g.Kd, groups, ks, ep); break;
+        case EPI_PARTIAL: hipLaunchKernelGGL(gemm_tc_kernel<EPI_PARTIAL>, grid, block, 0, st, in, Wp, g.N, g.Kd, groups, ks, units, n_mt, ep); break;
+        case EPI_SWIGLU: hipLaunchKernelGGL(gemm_tc_kernel<EPI_SWIGLU>, grid, block, 0, st, in, Wp, g.N, g.Kd, groups, ks, units, n_mt, ep); break;
+        case EPI_ARGMAX: hipLaunchKernelGGL(gemm_tc_kernel<EPI_ARGMAX>, grid, block, 0, st, in, Wp, g.N, g.Kd, groups, ks, units, n_mt, ep); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -47,12 +47,11 @@ hipError_t gemm(const GemmShape &g, int epi, const GemmIn &in, const bf16 *Wp, c
                 hipStream_t st);
 // Row-major [n][kd] -> fragment order; rows up to the next multiple of 16 are zero.
 hipError_t pack_weight(const bf16 *w, int n, int kd, bf16 *out, hipStream_t st);
-// The tile kernel for hundreds of rows (k_gemm_tc.hip): one launch covers gemm_tc_rows() rows
-// starting at in.m0 (in.M of them) and gemm_tc_columns() columns per workgroup.
+// The tile kernel for hundreds of rows (k_gemm_tc.hip): one launch covers all in.M_total rows,
+// gemm_tc_columns() columns per workgroup.
 hipError_t gemm_tc(const GemmShape &g, int epi, const GemmIn &in, const bf16 *Wp, const GemmEpi &ep,
                    hipStream_t st);
 int gemm_tc_columns();
-int gemm_tc_rows();
 
 // ---- attention ------------------------------------------------------------------------------
 
