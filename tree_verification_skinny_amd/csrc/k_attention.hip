@@ -272,15 +272,233 @@ __global__ __launch_bounds__(64 * NW * HPW) void attn_partial_kernel(
     }
 }
 
-// Merge the chunk partials of one (node, q head): o = sum_c 2^(m_c - m*) O_c / sum_c 2^(m_c - m*) l_c.
-// 256 threads = (D/4) column quads x CG chunk groups; each thread merges its chunks c = cg,
-// cg + CG, ... with every load issued before the arithmetic, then the CG states are merged in
-// LDS in chunk-group order.
+// Large grids (a batch, or a draft tree with hundreds of query rows): one kv head per workgroup
+// (two workgroups share a compute unit, so one stages while the other multiplies), a range of CPR
+// chunks walked in order with the online-softmax rescale so that a range leaves one partial
+// instead of CPR of them, and tile groups (grid z = request x tile group) so that no wave holds
+// more than one 16-column query tile. The page ids of the next chunk are fetched while the
+// current chunk is multiplied.
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) void attn_range_kernel(
+    const bf16 *__restrict__ q, const bf16 *__restrict__ k_pool, const bf16 *__restrict__ v_pool,
+    const int32_t *__restrict__ block_table, int max_pages, const int32_t *__restrict__ ctx_len,
+    const uint64_t *__restrict__ anc, const int32_t *__restrict__ status, int K, int nq, int nkv,
+    int n_ranges, int cpr, int n_tg, float scale_log2, float *__restrict__ part_o,
+    float2 *__restrict__ part_ml) {
+    constexpr int CH = kAttnChunk;
+    constexpr int NS = CH / 32;
+    constexpr int KP = D + 8;
+    constexpr int VP = CH + 8;
+    constexpr int STAGERS = 16 * D / 8;
+    constexpr int NP = CH / 16;
+    static_assert(STAGERS <= 64 * NW, "staging needs one thread per 16 bytes of a page");
+    __shared__ __attribute__((aligned(16))) bf16 Ks[CH * KP];
+    __shared__ __attribute__((aligned(16))) bf16 Vt[D * VP];
+
+    const int rg = blockIdx.x, g = blockIdx.y;
+    const int b = blockIdx.z / n_tg, tg = blockIdx.z % n_tg;
+    const int st_b = status[b];
+    const int ctx = ctx_len[b];
+    if (st_b != 0) return;
+    const int T = ctx + K;
+    const int nc = (T + CH - 1) / CH;
+    const int c_begin = rg * cpr;
+    if (c_begin >= nc) return;
+    const int c_end = min(c_begin + cpr, nc);
+    const int group = nq / nkv;
+    const int R = group * K;
+    const int QT = (R + 15) >> 4;
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r16 = lane & 15, grp = lane >> 4;
+    const int t = tg * NW + wave;
+    const bool has_tile = t < QT;
+    const int rho = 16 * t + r16;
+    const bool col_ok = has_tile && rho < R;
+    const int hh = col_ok ? rho / K : 0;
+    const int tok = col_ok ? rho % K : 0;
+    bf16x8 qf[D / 32];
+    uint64_t am = 0;
+    if (has_tile) {
+        const bf16 *qrow = q + ((int64_t)(b * K + tok) * nq + g * group + hh) * D;
+#pragma unroll
+        for (int ds = 0; ds < D / 32; ++ds) qf[ds] = *(const bf16x8 *)(qrow + ds * 32 + grp * 8);
+        am = anc[b * K + tok];
+    }
+    const int kr0 = 8 * (r16 >> 2) + (r16 & 3);
+    const int32_t *bt = block_table + (int64_t)b * max_pages;
+    const bool stager = threadIdx.x < STAGERS;
+    const int e = (threadIdx.x % STAGERS) * 8;
+    const int srow = e / D, scol = e % D, sd = e >> 4, sslot = e & 15;
+    auto page_ids = [&](int c, int (&pg)[NP]) {
+        const int np = (min(CH, T - c * CH) + 15) >> 4;
+#pragma unroll
+        for (int p = 0; p < NP; ++p) pg[p] = (stager && p < np) ? bt[(c * CH >> 4) + p] : -1;
+    };
+    int pg[NP];
+    page_ids(c_begin, pg);
+
+    float m_run = -INFINITY, l_run = 0.f;
+    floatx4 o[D / 16];
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    for (int c = c_begin; c < c_end; ++c) {
+        const int kb = c * CH;
+        const int nvalid = min(CH, T - kb);
+        {
+            bf16x8 kr[NP], vr[NP];
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+                if (pg[p] >= 0) {
+                    kr[p] = *(const bf16x8 *)(k_pool + ((int64_t)pg[p] * nkv + g) * 16 * D + e);
+                    vr[p] = *(const bf16x8 *)(v_pool + ((int64_t)pg[p] * nkv + g) * D * 16 + e);
+                } else {
+                    kr[p] = bf16x8{};
+                    vr[p] = bf16x8{};
+                }
+            }
+            if (c + 1 < c_end) page_ids(c + 1, pg);   // next chunk's pages, in flight meanwhile
+            if (c > c_begin) __syncthreads();          // the previous chunk is consumed
+            if (stager) {
+#pragma unroll
+                for (int p = 0; p < NP; ++p) {
+                    *(bf16x8 *)&Ks[(p * 16 + srow) * KP + scol] = kr[p];
+                    bf16x8 vv = vr[p];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        if (p * 16 + sslot + j >= nvalid) vv[j] = (bf16)0.0f;   // never multiply stale data
+                    *(bf16x8 *)&Vt[sd * VP + p * 16 + sslot] = vv;
+                }
+            }
+        }
+        __syncthreads();
+        if (!has_tile) continue;
+        const bool chunk_plain = nvalid == CH && kb + CH <= ctx;
+
+        floatx4 s[NS][2];
+        {
+            constexpr int NST = 2 * NS, FK = D / 32;
+            bf16x8 kf0[FK], kf1[FK];
+            auto kload = [&](bf16x8 (&kf)[FK], int i) {
+#pragma unroll
+                for (int ds = 0; ds < FK; ++ds)
+                    kf[ds] = *(const bf16x8 *)&Ks[((i >> 1) * 32 + kr0 + 4 * (i & 1)) * KP + grp * 8 + ds * 32];
+            };
+            kload(kf0, 0);
+#pragma unroll
+            for (int i = 0; i < NST; ++i) {
+                auto &cur = (i & 1) ? kf1 : kf0;
+                auto &nxt = (i & 1) ? kf0 : kf1;
+                if (i + 1 < NST) {
+                    kload(nxt, i + 1);
+                    __builtin_amdgcn_sched_group_barrier(0x100, FK, 0);
+                }
+                floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ds = 0; ds < FK; ++ds) acc = mfma16x16x32(cur[ds], qf[ds], acc);
+                s[i >> 1][i & 1] = acc;
+                __builtin_amdgcn_sched_group_barrier(0x008, FK, 0);
+            }
+        }
+        float mloc = -INFINITY;
+        if (chunk_plain) {
+#pragma unroll
+            for (int st = 0; st < NS; ++st)
+#pragma unroll
+                for (int e2 = 0; e2 < 8; ++e2) {
+                    s[st][e2 >> 2][e2 & 3] *= scale_log2;
+                    mloc = fmaxf(mloc, s[st][e2 >> 2][e2 & 3]);
+                }
+        } else {
+#pragma unroll
+            for (int st = 0; st < NS; ++st) {
+                const int k0 = kb + st * 32 + 8 * grp;
+                const int n_ctx = min(max(ctx - k0, 0), 8);
+                const int j0 = max(k0 + n_ctx - ctx, 0);
+                const unsigned anc8 = j0 < 64 ? (unsigned)(am >> j0) & 0xffu : 0u;
+                const int n_in = min(max(kb + nvalid - k0, 0), 8);
+                unsigned vis = (((1u << n_ctx) - 1u) | (anc8 << n_ctx)) & ((1u << n_in) - 1u);
+                if (!col_ok) vis = 0u;
+#pragma unroll
+                for (int e2 = 0; e2 < 8; ++e2) {
+                    const float raw = s[st][e2 >> 2][e2 & 3] * scale_log2;
+                    s[st][e2 >> 2][e2 & 3] = ((vis >> e2) & 1u) ? raw : -INFINITY;
+                    mloc = fmaxf(mloc, s[st][e2 >> 2][e2 & 3]);
+                }
+            }
+        }
+        mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
+        mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+        const float m_new = fmaxf(m_run, mloc);
+        const bool none = (m_new == -INFINITY);
+        const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        if (__any(alpha != 1.f)) {
+#pragma unroll
+            for (int dt = 0; dt < D / 16; ++dt) o[dt] *= alpha;
+        }
+        float psum = 0.f;
+        {
+            constexpr int NST = 2 * NS, FV = D / 32;
+            bf16x8 vf0[FV], vf1[FV];
+            auto vload = [&](bf16x8 (&vf)[FV], int i) {
+#pragma unroll
+                for (int j = 0; j < FV; ++j)
+                    vf[j] = *(const bf16x8 *)&Vt[(r16 + ((i & 1) * FV + j) * 16) * VP + (i >> 1) * 32 + grp * 8];
+            };
+            vload(vf0, 0);
+            bf16x8 ph, pl;
+#pragma unroll
+            for (int i = 0; i < NST; ++i) {
+                auto &cur = (i & 1) ? vf1 : vf0;
+                auto &nxt = (i & 1) ? vf0 : vf1;
+                if (i + 1 < NST) {
+                    vload(nxt, i + 1);
+                    __builtin_amdgcn_sched_group_barrier(0x100, FV, 0);
+                }
+                if ((i & 1) == 0) {
+                    const int st = i >> 1;
+#pragma unroll
+                    for (int e2 = 0; e2 < 8; ++e2) {
+                        const float pv = none ? 0.f : __builtin_amdgcn_exp2f(s[st][e2 >> 2][e2 & 3] - m_new);
+                        const bf16 hi = to_bf(pv);
+                        ph[e2] = hi;
+                        pl[e2] = to_bf(pv - to_f(hi));
+                        psum += pv;
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < FV; ++j) {
+                    const int dt = (i & 1) * FV + j;
+                    o[dt] = mfma16x16x32(cur[j], ph, o[dt]);
+                    o[dt] = mfma16x16x32(cur[j], pl, o[dt]);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, 2 * FV, 0);
+            }
+        }
+        psum += __shfl_xor(psum, 16, 64);
+        psum += __shfl_xor(psum, 32, 64);
+        l_run = l_run * alpha + psum;
+        m_run = m_new;
+    }
+    if (col_ok) {
+        const int64_t base = (((int64_t)b * nkv + g) * n_ranges + rg) * R + rho;
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt)
+            *(floatx4 *)(part_o + base * D + dt * 16 + 4 * grp) = o[dt];
+        if (grp == 0) part_ml[base] = make_float2(m_run, l_run);
+    }
+}
+
+// Merge the partials of one (node, q head): o = sum_c 2^(m_c - m*) O_c / sum_c 2^(m_c - m*) l_c
+// over the partials c (one per chunk, or per range of cpr chunks). 256 threads = (D/4) column
+// quads x CG groups; each thread merges partials c = cg, cg + CG, ... with every load issued
+// before the arithmetic, then the CG states are merged in LDS in group order.
 template <int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(
     const float *__restrict__ part_o, const float2 *__restrict__ part_ml,
     const int32_t *__restrict__ ctx_len, const int32_t *__restrict__ status, int K, int nq,
-    int nkv, int n_chunks, bf16 *__restrict__ out) {
+    int nkv, int n_chunks, int cpr, bf16 *__restrict__ out) {
     constexpr int TQ = D / 4;            // threads per column quad set
     constexpr int CG = 256 / TQ;         // chunk groups: 8 (D=128) or 16 (D=64)
     constexpr int PER = 8;               // chunks per thread held in flight
@@ -299,7 +517,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(
     }
     const int group = nq / nkv, g = h / group, hh = h % group;
     const int R = group * K, rho = hh * K + tok;
-    const int nc = (ctx_len[b] + K + kAttnChunk - 1) / kAttnChunk;
+    const int nc = ((ctx_len[b] + K + kAttnChunk - 1) / kAttnChunk + cpr - 1) / cpr;   // partials
     const int64_t base = ((int64_t)b * nkv + g) * n_chunks * R + rho;
     float m = -INFINITY, l = 0.f;
     floatx4 o = {0.f, 0.f, 0.f, 0.f};
@@ -349,10 +567,21 @@ hipError_t attention(const AttnArgs &a, hipStream_t st) {
     const float scale_log2 = kLog2e / sqrtf((float)a.D);
     // waves per kv head: 5 when that takes fewer query tiles per wave than 4 (one tile each for
     // a group of 5 q heads and a block of 16), else 4
-    const int QT = (a.nq / a.nkv * a.K + 15) / 16;
+    const int R = a.nq / a.nkv * a.K;
+    const int QT = (R + 15) / 16;
     const int nw = (QT + 4) / 5 < (QT + 3) / 4 ? 5 : 4;
-    const int hpw = a.nkv % 2 == 0 ? 2 : 1;
-    const dim3 grid_h(a.n_chunks, a.nkv / hpw, a.B);
+    const int n_tg = (QT + nw - 1) / nw;
+    // A small grid (one request, a short draft) runs one chunk per workgroup, two kv heads each,
+    // so that it is resident at once. A large one (a batch, or hundreds of query rows) runs
+    // ranges of chunks, one kv head per workgroup: chunks per range are chosen so that a
+    // range's partial stays below about a quarter of the keys and values it covers, while at
+    // least ~512 workgroups remain.
+    const int64_t wgs1 = (int64_t)a.n_chunks * a.nkv * a.B * n_tg;
+    int cpr = 1, stride = a.n_chunks;
+    hipError_t e;
+    if (wgs1 <= 512) {
+        const int hpw = a.nkv % 2 == 0 ? 2 : 1;
+        const dim3 grid_h(a.n_chunks, a.nkv / hpw, a.B);
 #define SV_ATTN(DD, NWV, HP)                                                                      \
     hipLaunchKernelGGL((attn_partial_kernel<DD, NWV, HP>), grid_h, dim3(64 * NWV * HP), 0, st,    \
                        a.q, a.k_pool, a.v_pool, a.block_table, a.max_pages, a.ctx_len, a.anc,      \
@@ -360,23 +589,43 @@ hipError_t attention(const AttnArgs &a, hipStream_t st) {
 #define SV_ATTN_H(DD, NWV)          \
     if (hpw == 2) SV_ATTN(DD, NWV, 2); \
     else SV_ATTN(DD, NWV, 1)
-    if (a.D == 128) {
-        if (nw == 4) { SV_ATTN_H(128, 4); }
-        else { SV_ATTN_H(128, 5); }
-    } else {
-        if (nw == 4) { SV_ATTN_H(64, 4); }
-        else { SV_ATTN_H(64, 5); }
-    }
+        if (a.D == 128) {
+            if (nw == 4) { SV_ATTN_H(128, 4); }
+            else { SV_ATTN_H(128, 5); }
+        } else {
+            if (nw == 4) { SV_ATTN_H(64, 4); }
+            else { SV_ATTN_H(64, 5); }
+        }
 #undef SV_ATTN_H
 #undef SV_ATTN
-    hipError_t e = hipGetLastError();
+    } else {
+        cpr = (R + 31) / 32;
+        if (cpr > 8) cpr = 8;
+        while (cpr > 1 && (int64_t)((a.n_chunks + cpr - 1) / cpr) * a.nkv * a.B * n_tg < 512) --cpr;
+        const int n_ranges = (a.n_chunks + cpr - 1) / cpr;
+        stride = n_ranges;
+        const dim3 grid_r(n_ranges, a.nkv, a.B * n_tg);
+#define SV_RANGE(DD, NWV)                                                                         \
+    hipLaunchKernelGGL((attn_range_kernel<DD, NWV>), grid_r, dim3(64 * NWV), 0, st, a.q, a.k_pool, \
+                       a.v_pool, a.block_table, a.max_pages, a.ctx_len, a.anc, a.status, a.K,     \
+                       a.nq, a.nkv, n_ranges, cpr, n_tg, scale_log2, a.part_o, a.part_ml)
+        if (a.D == 128) {
+            if (nw == 4) SV_RANGE(128, 4);
+            else SV_RANGE(128, 5);
+        } else {
+            if (nw == 4) SV_RANGE(64, 4);
+            else SV_RANGE(64, 5);
+        }
+#undef SV_RANGE
+    }
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.D == 128)
         hipLaunchKernelGGL(attn_combine_kernel<128>, dim3(a.B * a.K, a.nq), dim3(256), 0, st,
-                           a.part_o, a.part_ml, a.ctx_len, a.status, a.K, a.nq, a.nkv, a.n_chunks, a.out);
+                           a.part_o, a.part_ml, a.ctx_len, a.status, a.K, a.nq, a.nkv, stride, cpr, a.out);
     else
         hipLaunchKernelGGL(attn_combine_kernel<64>, dim3(a.B * a.K, a.nq), dim3(256), 0, st,
-                           a.part_o, a.part_ml, a.ctx_len, a.status, a.K, a.nq, a.nkv, a.n_chunks, a.out);
+                           a.part_o, a.part_ml, a.ctx_len, a.status, a.K, a.nq, a.nkv, stride, cpr, a.out);
     return hipGetLastError();
 }
 
