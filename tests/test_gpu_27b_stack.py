@@ -86,3 +86,49 @@ def test_27b_stack_teacher_forced(stack, kind):
     near = check_accept(r, tokens, parent, out.greedy[0], int(out.accepted_len[0]),
                         int(out.bonus[0]), out.path[0])
     print(f"{kind}: head max err {err:.2e}, accepted {out.accepted_len[0]}, near-tie {near}")
+
+
+def test_27b_batched_teacher_forced(stack):
+    """The batched launch configuration: 32 requests x block of 16 (512 rows, the matrix-core
+    tile projections and the range attention), contexts uniform in [512, 8192], shuffled pages.
+    Sampled requests are checked layer by layer with teacher forcing, then through the output
+    head and the greedy walk from the GPU's final residual stream."""
+    shape, w = stack
+    B, k = 32, 16
+    rng = np.random.default_rng(synth.seed_of(SEED, "batched ctx"))
+    ctxs = [int(c) for c in rng.integers(512, 8193, B)]
+    table, n_pages = synth.page_table(B, [(c + k + 15) // 16 for c in ctxs], SEED, shuffle=True)
+    kv = tv.PagedKV.empty(w.cfg, n_pages, torch.from_numpy(table), DEV)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(SEED + 1)
+    kv.k_pool.normal_(generator=g)
+    kv.v_pool.normal_(generator=g)
+    tokens = np.stack([synth.uniform_tokens(k, shape.vocab, SEED, "batched", b) for b in range(B)])
+    tokens = tokens.astype(np.int32)
+    out = run_verify(w, kv, tokens, None, ctxs, want_hidden=True)
+    cfg = oracle_cfg(shape)
+    parent = oracle.chain(k)
+    for b in (0, 13, 31):
+        rows = slice(b * k, (b + 1) * k)
+        for l in (0, 37, 63):
+            lw = {nm: bits(t) for nm, t in w.rowmajor["layers"][l].items()}
+            kc, vc = kvlayout.read_rows(kv, l, b, torch.arange(ctxs[b]))
+            kc, vc = bits(kc), bits(vc)
+            x_in = bits(out.hidden[l][rows])
+            x_o, k_o, v_o = oracle.layer_forward(cfg, lw, kc, vc, parent, x_in)
+            x_r, _, _ = ref64.layer(shape, lw, kc, vc, parent, x_in)
+            kg, vg = kvlayout.read_rows(kv, l, b, torch.arange(ctxs[b], ctxs[b] + k))
+            check_logits(kg.float().cpu().numpy(), oracle.from_bf16(k_o), f"request {b} layer {l} k_new")
+            check_logits(vg.float().cpu().numpy(), oracle.from_bf16(v_o), f"request {b} layer {l} v_new")
+            print(check_as_exact(out.hidden[l + 1][rows].float().cpu().numpy(), oracle.from_bf16(x_o),
+                                 x_r.numpy(), f"request {b} layer {l} output"))
+        model = oracle.Model(cfg, bits(w.tensors["embed"][:1]), bits(w.tensors["final_norm"]),
+                             bits(w.rowmajor["lm_head"]), layers=[])
+        lg = oracle.logits(model, bits(out.hidden[shape.n_layers][rows]))
+        err = check_logits(out.logits[b], lg, f"request {b} output head")
+        arg, margin = oracle.argmax(lg)
+        a, bo, p = oracle.accept(tokens[b], parent, arg)
+        r = oracle.VerifyResult(lg, arg, margin, a, bo, p, [], [], [])
+        near = check_accept(r, tokens[b], parent, out.greedy[b], int(out.accepted_len[b]),
+                            int(out.bonus[b]), out.path[b])
+        print(f"batched request {b} (ctx {ctxs[b]}): head max err {err:.2e}, near-tie {near}")
