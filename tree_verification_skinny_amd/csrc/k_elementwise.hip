@@ -96,10 +96,11 @@ hipError_t rope_table(const NodeInfo &ni, int M, int D, double theta, hipStream_
 }
 
 // ---- row-wise RMSNorm helpers (one 1024-thread workgroup per row) --------------------------------
-// RMSNorm: u = bf16((x / sqrt(mean(x^2) + eps)) * g), the sum of squares in fp32. A thread owns
-// column quads q = tid, tid + 1024, ...; every load of the row is issued before any is used.
+// RMSNorm: u = bf16((x / sqrt(mean(x^2) + eps)) * g), the sum of squares in fp32. Thread t owns
+// the column quads t, t + 1024, ... (NQ of them, H <= 4 * 1024 * NQ); quads past the row re-read
+// the last one and take no part in sums or stores, so every load is unconditional and all of a
+// row's loads are in flight together.
 constexpr int kRowThreads = 1024;
-constexpr int kRowQuads = 4;        // quads per thread: hidden <= 4 * 4 * 1024
 
 __device__ __forceinline__ float block_sum_1024(float v, float *red) {
     v = wave_sum(v);
@@ -112,62 +113,129 @@ __device__ __forceinline__ float block_sum_1024(float v, float *red) {
     return t;
 }
 
+template <int NQ>
+struct RowQuads {
+    int off[NQ];                 // column of each quad (clamped into the row)
+    bool live[NQ];
+    __device__ __forceinline__ explicit RowQuads(int H) {
+        const int nquad = H / 4;
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) {
+            const int q = threadIdx.x + i * kRowThreads;
+            live[i] = q < nquad;
+            off[i] = (live[i] ? q : nquad - 1) * 4;
+        }
+    }
+};
+
+__device__ __forceinline__ void unpack4(uint2 v, float (&o)[4]) {
+    const bf16 *b = reinterpret_cast<const bf16 *>(&v);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[j] = to_f(b[j]);
+}
+
 // u is stored in fragment order (frag_off), the operand order of the next projection.
-__device__ __forceinline__ void norm_store(const float (&xv)[kRowQuads][4], float ss, int row, int H,
-                                           float eps, const bf16 *__restrict__ gain,
-                                           bf16 *__restrict__ u) {
+template <int NQ>
+__device__ __forceinline__ void norm_store(const RowQuads<NQ> &rq, const float (&xv)[NQ][4],
+                                           const uint2 (&g)[NQ], float ss, int row, int H,
+                                           float eps, bf16 *__restrict__ u) {
     const float inv = 1.0f / sqrtf(ss / (float)H + eps);
 #pragma unroll
-    for (int i = 0; i < kRowQuads; ++i) {
-        const int q = threadIdx.x + i * kRowThreads;
-        if (q * 4 >= H) break;
+    for (int i = 0; i < NQ; ++i) {
+        if (!rq.live[i]) continue;
+        float gf[4];
+        unpack4(g[i], gf);
         float o[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) o[j] = (xv[i][j] * inv) * to_f(gain[q * 4 + j]);
-        store4(u + frag_off(row, q * 4, H), o[0], o[1], o[2], o[3]);
+        for (int j = 0; j < 4; ++j) o[j] = (xv[i][j] * inv) * gf[j];
+        store4(u + frag_off(row, rq.off[i], H), o[0], o[1], o[2], o[3]);
     }
 }
 
+// y[i] = sum over s of p[s * stride + off[i]], in split order. Loads go out SP splits at a time
+// (slots past the last split re-read it and are not added).
+template <int SP, int NQ>
+__device__ __forceinline__ void split_sum(const float *__restrict__ p, const int (&off)[NQ],
+                                          int64_t stride, int splits, floatx4 (&y)[NQ]) {
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) y[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < splits; s0 += SP) {
+        floatx4 v[SP][NQ];
+#pragma unroll
+        for (int t = 0; t < SP; ++t) {
+            const int s = s0 + t < splits ? s0 + t : splits - 1;
+#pragma unroll
+            for (int i = 0; i < NQ; ++i) v[t][i] = *(const floatx4 *)(p + s * stride + off[i]);
+        }
+#pragma unroll
+        for (int t = 0; t < SP; ++t) {
+            // a select, not a branch: a branch lets the compiler sink the load behind it
+            const bool use = s0 + t < splits;
+#pragma unroll
+            for (int i = 0; i < NQ; ++i) y[i] = use ? y[i] + v[t][i] : y[i];
+        }
+    }
+}
+
+// Split-load group for a split count: the next power of two, at most 8.
+inline int split_group(int splits) { return splits <= 1 ? 1 : splits <= 2 ? 2 : splits <= 4 ? 4 : 8; }
+// Quads per thread for a hidden size: 1, 2 or 4.
+inline int row_quads(int H) {
+    const int n = (H / 4 + kRowThreads - 1) / kRowThreads;
+    return n <= 1 ? 1 : n <= 2 ? 2 : 4;
+}
+
 // ---- embedding gather + first RMSNorm ------------------------------------------------------------
+template <int NQ>
 __global__ __launch_bounds__(kRowThreads) void embed_norm_kernel(
     const int32_t *__restrict__ tokens, const bf16 *__restrict__ table, int H, int vocab,
     const bf16 *__restrict__ gain, float eps, bf16 *__restrict__ x, bf16 *__restrict__ u,
     bf16 *__restrict__ trace) {
     __shared__ float red[kRowThreads / 64];
     const int row = blockIdx.x;
+    const RowQuads<NQ> rq(H);
+    uint2 g[NQ];
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) g[i] = *(const uint2 *)(gain + rq.off[i]);
     int tok = tokens[row];
     if (tok < 0 || tok >= vocab) tok = 0;   // the request is already marked bad; stay in bounds
     const bf16 *src = table + (int64_t)tok * H;
-    float xv[kRowQuads][4];
+    uint2 e[NQ];
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) e[i] = *(const uint2 *)(src + rq.off[i]);
+    float xv[NQ][4];
     float ss = 0.f;
 #pragma unroll
-    for (int i = 0; i < kRowQuads; ++i) {
-        const int q = threadIdx.x + i * kRowThreads;
+    for (int i = 0; i < NQ; ++i) {
+        unpack4(e[i], xv[i]);
+        if (!rq.live[i]) continue;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) xv[i][j] = 0.f;
-        if (q * 4 >= H) continue;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const bf16 v = src[q * 4 + j];
-            xv[i][j] = to_f(v);
-            x[(int64_t)row * H + q * 4 + j] = v;
-            if (trace) trace[(int64_t)row * H + q * 4 + j] = v;
-            ss += xv[i][j] * xv[i][j];
-        }
+        for (int j = 0; j < 4; ++j) ss += xv[i][j] * xv[i][j];
+        *(uint2 *)(x + (int64_t)row * H + rq.off[i]) = e[i];
+        if (trace) *(uint2 *)(trace + (int64_t)row * H + rq.off[i]) = e[i];
     }
     ss = block_sum_1024(ss, red);
-    norm_store(xv, ss, row, H, eps, gain, u);
+    norm_store(rq, xv, g, ss, row, H, eps, u);
 }
 
 hipError_t embed_norm(const int32_t *tokens, const bf16 *table, const bf16 *gain, int M, int H,
                       int vocab, float eps, bf16 *x, bf16 *u, bf16 *trace, hipStream_t st) {
-    hipLaunchKernelGGL(embed_norm_kernel, dim3(M), dim3(kRowThreads), 0, st, tokens, table, H, vocab,
-                       gain, eps, x, u, trace);
+#define SV_EMBED(NQ)                                                                              \
+    hipLaunchKernelGGL(embed_norm_kernel<NQ>, dim3(M), dim3(kRowThreads), 0, st, tokens, table, H, \
+                       vocab, gain, eps, x, u, trace)
+    switch (row_quads(H)) {
+        case 1: SV_EMBED(1); break;
+        case 2: SV_EMBED(2); break;
+        default: SV_EMBED(4); break;
+    }
+#undef SV_EMBED
     return hipGetLastError();
 }
 
 // ---- QKV split-K pass: sum, bf16, RoPE, q / K / V stores -----------------------------------------
 // One workgroup per (row, head of q, k or v); thread j handles the rotation pair (j, j + D/2).
+// The cache slot, the angles and every split's partials are requested before any is used.
+template <int SP>
 __global__ void reduce_qkv_kernel(const float *__restrict__ P, int splits, int M,
                                   const float2 *__restrict__ rope, const int32_t *__restrict__ status,
                                   const int32_t *__restrict__ ctx_len,
@@ -180,30 +248,52 @@ __global__ void reduce_qkv_kernel(const float *__restrict__ P, int splits, int M
     const int N = (nq + 2 * nkv) * D;
     const int64_t pstride = (int64_t)M * N;
     const float *pr = P + (int64_t)row * N + head * D + j;
+    const bool is_q = head < nq, is_k = !is_q && head < nq + nkv;
+    const int b = row / K, il = row % K;
+    int page = 0, slot = 0;
+    bool store_kv = false;
+    if (!is_q) {
+        store_kv = status[b] == 0;
+        const int pos = ctx_len[b] + il;
+        if (store_kv) page = page_of(block_table, max_pages, b, pos);
+        slot = pos & 15;
+    }
+    float2 cs = make_float2(1.f, 0.f);
+    if (head < nq + nkv) cs = rope[(int64_t)row * half + j];
     float a = 0.f, c = 0.f;
-    for (int s = 0; s < splits; ++s) { a += pr[s * pstride]; c += pr[s * pstride + half]; }
+    for (int s0 = 0; s0 < splits; s0 += SP) {
+        float va[SP], vc[SP];
+#pragma unroll
+        for (int t = 0; t < SP; ++t) {
+            const int s = s0 + t < splits ? s0 + t : splits - 1;
+            va[t] = pr[s * pstride];
+            vc[t] = pr[s * pstride + half];
+        }
+#pragma unroll
+        for (int t = 0; t < SP; ++t) {
+            const bool use = s0 + t < splits;   // a select, so the loads stay ahead of the sums
+            a = use ? a + va[t] : a;
+            c = use ? c + vc[t] : c;
+        }
+    }
     a = round_bf(a);
     c = round_bf(c);
     bf16 lo, hi;
     if (head < nq + nkv) {
-        const float2 cs = rope[(int64_t)row * half + j];
         lo = to_bf(a * cs.x - c * cs.y);
         hi = to_bf(c * cs.x + a * cs.y);
     } else {
         lo = to_bf(a);
         hi = to_bf(c);
     }
-    if (head < nq) {
+    if (is_q) {
         bf16 *qh = q + ((int64_t)row * nq + head) * D;
         qh[j] = lo;
         qh[j + half] = hi;
         return;
     }
-    const int b = row / K, il = row % K;
-    if (status[b] != 0) return;
-    const int pos = ctx_len[b] + il;
-    const int page = page_of(block_table, max_pages, b, pos), slot = pos & 15;
-    if (head < nq + nkv) {
+    if (!store_kv) return;
+    if (is_k) {
         bf16 *kr = k_pool + (((int64_t)page * nkv + (head - nq)) * 16 + slot) * D;
         kr[j] = lo;
         kr[j + half] = hi;
@@ -217,68 +307,79 @@ __global__ void reduce_qkv_kernel(const float *__restrict__ P, int splits, int M
 hipError_t reduce_qkv(const float *P, int splits, const NodeInfo &ni, const int32_t *ctx_len,
                       const int32_t *block_table, int max_pages, int B, int K, int nq, int nkv,
                       int D, bf16 *q, bf16 *k_pool, bf16 *v_pool, hipStream_t st) {
-    hipLaunchKernelGGL(reduce_qkv_kernel, dim3(B * K, nq + 2 * nkv), dim3(D / 2), 0, st, P, splits,
-                       B * K, ni.rope, ni.status, ctx_len, block_table, max_pages, K, nq, nkv, D, q,
-                       k_pool, v_pool);
+#define SV_QKV(SP)                                                                                \
+    hipLaunchKernelGGL(reduce_qkv_kernel<SP>, dim3(B * K, nq + 2 * nkv), dim3(D / 2), 0, st, P,    \
+                       splits, B * K, ni.rope, ni.status, ctx_len, block_table, max_pages, K, nq, \
+                       nkv, D, q, k_pool, v_pool)
+    switch (split_group(splits)) {
+        case 1: SV_QKV(1); break;
+        case 2: SV_QKV(2); break;
+        case 4: SV_QKV(4); break;
+        default: SV_QKV(8); break;
+    }
+#undef SV_QKV
     return hipGetLastError();
 }
 
 // ---- residual split-K pass + RMSNorm: x = bf16(x + bf16(sum_s P[s])), u = RMSNorm(x) * g --------
+template <int NQ, int SP>
 __global__ __launch_bounds__(kRowThreads) void reduce_resid_norm_kernel(
     const float *__restrict__ P, int splits, int M, int H, const bf16 *__restrict__ gain, float eps,
     bf16 *__restrict__ x, bf16 *__restrict__ u, bf16 *__restrict__ trace) {
     __shared__ float red[kRowThreads / 64];
     const int row = blockIdx.x;
-    const int64_t pstride = (int64_t)M * H;
-    const float *pr = P + (int64_t)row * H;
+    const RowQuads<NQ> rq(H);
     bf16 *xr = x + (int64_t)row * H;
-    float xv[kRowQuads][4];
-    floatx4 y[kRowQuads];
-    uint2 xo[kRowQuads];           // the four bf16 residual values of each quad
-    // every load of the row (all splits, the residual) is issued before any is used
+    uint2 xo[NQ], g[NQ];
 #pragma unroll
-    for (int i = 0; i < kRowQuads; ++i) {
-        const int q = threadIdx.x + i * kRowThreads;
-        y[i] = floatx4{0.f, 0.f, 0.f, 0.f};
-        xo[i] = make_uint2(0u, 0u);
-        if (q * 4 >= H) continue;
-        xo[i] = *(const uint2 *)(xr + q * 4);
-        y[i] = *(const floatx4 *)(pr + q * 4);
+    for (int i = 0; i < NQ; ++i) {
+        xo[i] = *(const uint2 *)(xr + rq.off[i]);
+        g[i] = *(const uint2 *)(gain + rq.off[i]);
     }
-    for (int s = 1; s < splits; ++s) {
-#pragma unroll
-        for (int i = 0; i < kRowQuads; ++i) {
-            const int q = threadIdx.x + i * kRowThreads;
-            if (q * 4 < H) y[i] += *(const floatx4 *)(pr + s * pstride + q * 4);
-        }
-    }
+    floatx4 y[NQ];
+    split_sum<SP>(P + (int64_t)row * H, rq.off, (int64_t)M * H, splits, y);
+    float xv[NQ][4];
     float ss = 0.f;
 #pragma unroll
-    for (int i = 0; i < kRowQuads; ++i) {
-        const int q = threadIdx.x + i * kRowThreads;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) xv[i][j] = 0.f;
-        if (q * 4 >= H) continue;
-        const bf16 *xb = reinterpret_cast<const bf16 *>(&xo[i]);
+    for (int i = 0; i < NQ; ++i) {
+        float xf[4];
+        unpack4(xo[i], xf);
         bf16 out[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const float xn = round_bf(to_f(xb[j]) + round_bf(y[i][j]));
-            xv[i][j] = xn;
-            ss += xn * xn;
-            out[j] = to_bf(xn);
+            xv[i][j] = round_bf(xf[j] + round_bf(y[i][j]));
+            out[j] = to_bf(xv[i][j]);
         }
-        *(uint2 *)(xr + q * 4) = *reinterpret_cast<const uint2 *>(out);
-        if (trace) *(uint2 *)(trace + (int64_t)row * H + q * 4) = *reinterpret_cast<const uint2 *>(out);
+        if (!rq.live[i]) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ss += xv[i][j] * xv[i][j];
+        *(uint2 *)(xr + rq.off[i]) = *reinterpret_cast<const uint2 *>(out);
+        if (trace)
+            *(uint2 *)(trace + (int64_t)row * H + rq.off[i]) = *reinterpret_cast<const uint2 *>(out);
     }
     ss = block_sum_1024(ss, red);
-    norm_store(xv, ss, row, H, eps, gain, u);
+    norm_store(rq, xv, g, ss, row, H, eps, u);
 }
 
 hipError_t reduce_resid_norm(const float *P, int splits, int M, int H, const bf16 *gain, float eps,
                              bf16 *x, bf16 *u, bf16 *trace, hipStream_t st) {
-    hipLaunchKernelGGL(reduce_resid_norm_kernel, dim3(M), dim3(kRowThreads), 0, st, P, splits, M, H,
-                       gain, eps, x, u, trace);
+#define SV_RRN(NQ, SP)                                                                            \
+    hipLaunchKernelGGL((reduce_resid_norm_kernel<NQ, SP>), dim3(M), dim3(kRowThreads), 0, st, P,   \
+                       splits, M, H, gain, eps, x, u, trace)
+#define SV_RRN_SP(NQ)                        \
+    switch (split_group(splits)) {           \
+        case 1: SV_RRN(NQ, 1); break;        \
+        case 2: SV_RRN(NQ, 2); break;        \
+        case 4: SV_RRN(NQ, 4); break;        \
+        default: SV_RRN(NQ, 8); break;       \
+    }
+    switch (row_quads(H)) {
+        case 1: SV_RRN_SP(1); break;
+        case 2: SV_RRN_SP(2); break;
+        default: SV_RRN_SP(4); break;
+    }
+#undef SV_RRN_SP
+#undef SV_RRN
     return hipGetLastError();
 }
 
