@@ -271,6 +271,82 @@ def test_tiny_large_batch_uses_tile_kernel():
                      int(out.bonus[b]), out.path[b])
 
 
+def test_tiny_batch_long_contexts_stream_attention():
+    """24 requests x 16 nodes over contexts up to ~2100 keys: enough (request, kv head, chunk)
+    units that attention streams ranges of chunks through LDS. Every cache slot that holds no
+    committed or drafted row is NaN, which must never reach an output."""
+    B, k = 24, 16
+    w = synth.model_weights(synth.TINY, 321)
+    m = oracle_model_from(synth.TINY, w)
+    rng = np.random.default_rng(11)
+    ctxs = [0, 1, 127, 128, 129, 2047, 2048] + [int(c) for c in rng.integers(0, 2100, B - 7)]
+    weights = device_weights(synth.TINY, w, DEV)
+    kv = make_kv(synth.TINY, ctxs, k, 321, DEV, extra_pages=1)
+    kv.k_pool.fill_(float("nan"))
+    kv.v_pool.fill_(float("nan"))
+    toks, cases = [], []
+    for b, ctx in enumerate(ctxs):
+        kvs = [synth.kv_context(synth.TINY, ctx, 321, l, request=b) for l in range(2)]
+        kc = [bits(x) for x, _ in kvs]
+        vc = [bits(y) for _, y in kvs]
+        upload_context(kv, b, kc, vc)
+        tok = synth.uniform_tokens(k, 1024, 321, b)
+        if b % 3 == 0:
+            cont, _, _, _ = oracle.ar_greedy(m, kc, vc, int(tok[0]), k - 1)
+            tok[1:] = cont
+            cut = 1 + (b // 3) % (k - 1)
+            tok[cut] = (tok[cut] + 1) % 1024
+        toks.append(tok)
+        cases.append((kc, vc))
+    tokens = np.stack(toks).astype(np.int32)
+    out = run_verify(weights, kv, tokens, None, ctxs)
+    for b in range(B):
+        kc, vc = cases[b]
+        r = oracle.verify(m, kc, vc, tokens[b])
+        assert np.isfinite(out.logits[b]).all(), f"request {b}"
+        check_logits(out.logits[b], r.logits, f"request {b}")
+        check_accept(r, tokens[b], None, out.greedy[b], int(out.accepted_len[b]),
+                     int(out.bonus[b]), out.path[b])
+
+
+def test_tiny_batched_trees_stream_attention():
+    """8 requests, each a 64-node tree with greedy-planted paths, over contexts of 300..2000
+    keys: the streamed-range attention with several chunks per range and two query tile groups
+    per kv head; unused cache slots are NaN."""
+    B, k = 8, 64
+    ctxs = [300, 2000, 1023, 1024, 1025, 640, 1500, 1999]
+    weights_np = synth.model_weights(synth.TINY, 808)
+    m = oracle_model_from(synth.TINY, weights_np)
+    weights = device_weights(synth.TINY, weights_np, DEV)
+    kv = make_kv(synth.TINY, ctxs, k, 808, DEV)
+    kv.k_pool.fill_(float("nan"))
+    kv.v_pool.fill_(float("nan"))
+    toks, pars, cases = [], [], []
+    for b, ctx in enumerate(ctxs):
+        kvs = [synth.kv_context(synth.TINY, ctx, 808, l, request=b) for l in range(2)]
+        kc = [np.ascontiguousarray(bits(x)) for x, _ in kvs]
+        vc = [np.ascontiguousarray(bits(y)) for _, y in kvs]
+        upload_context(kv, b, kc, vc)
+        tokens, parent = planted_tree(m, kc, vc, k, 900 + b)
+        toks.append(tokens)
+        pars.append(parent)
+        cases.append((kc, vc))
+    tokens = np.stack(toks).astype(np.int32)
+    parents = np.stack(pars).astype(np.int32)
+    out = run_verify(weights, kv, tokens, parents, ctxs)
+    near, accepted = 0, 0
+    for b in range(B):
+        kc, vc = cases[b]
+        r = oracle.verify(m, kc, vc, tokens[b], parents[b])
+        assert np.isfinite(out.logits[b]).all(), f"request {b}"
+        check_logits(out.logits[b], r.logits, f"request {b}")
+        near += check_accept(r, tokens[b], parents[b], out.greedy[b], int(out.accepted_len[b]),
+                             int(out.bonus[b]), out.path[b])
+        accepted += r.accepted_len
+    assert near <= 2
+    assert accepted > 0
+
+
 def test_bad_requests_are_isolated():
     B, k = 4, 8
     w = synth.model_weights(synth.TINY, 5)

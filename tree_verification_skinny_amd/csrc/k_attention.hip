@@ -6,11 +6,13 @@
 // architecture"]. The path is a 64-bit ancestor mask per node (bit j set = node j is on the
 // path), so the mask test in the inner loop is one shift and one AND.
 //
-// Work split (split-KV): one workgroup per (request, kv head, chunk of 128 key positions). The
-// 4 waves stage the chunk's keys [128][D] and transposed values [D][128] from the cache pages
-// into LDS with 128-bit loads, then each wave takes 16-column query tiles: the columns are the
-// (q head of this kv group, draft node) pairs, so one K/V tile in LDS serves every q head of the
-// group. Per 32 keys and tile:
+// Two work splits (split-KV), both over chunks of 128 key positions: for a small grid (one
+// request, a block of 16) one workgroup per (request, pair of kv heads, chunk), whose waves
+// stage the chunk's keys [128][D] and values [D][128] from the cache pages into LDS and take
+// 16-column query tiles each; for a large grid (a batch, a 64-node tree) one wave per (request,
+// kv head, tile group, range of chunks), which streams its keys and values through LDS 32 at a
+// time (attn_wave_kernel). The query columns are (q head of this kv group, draft node) pairs, so
+// one K/V tile in LDS serves every q head of the group. Per 32 keys and tile:
 //   S^T = K . Q^T   (A = keys from LDS, B = Q^T held in registers for the whole chunk)
 //   online softmax per query column, in the log2 domain
 //   O^T += V^T . P^T (A = transposed values from LDS, B = the probabilities this lane already
@@ -272,221 +274,355 @@ __global__ __launch_bounds__(64 * NW * HPW) void attn_partial_kernel(
     }
 }
 
-// Large grids (a batch, or a draft tree with hundreds of query rows): one kv head per workgroup
-// (two workgroups share a compute unit, so one stages while the other multiplies), a range of CPR
-// chunks walked in order with the online-softmax rescale so that a range leaves one partial
-// instead of CPR of them, and tile groups (grid z = request x tile group) so that no wave holds
-// more than one 16-column query tile. The page ids of the next chunk are fetched while the
-// current chunk is multiplied.
-template <int D, int NW>
-__global__ __launch_bounds__(64 * NW) void attn_range_kernel(
+// Large grids (a batch, or a draft tree with hundreds of query rows), wave per key range: a
+// workgroup takes one (request, kv head, tile group) and 4 cpr consecutive chunks, dealt to its
+// waves in turn (wave w: chunks w, w + 4, ...). The tile group's TPW query tiles (all five of a
+// block of 16 with 5 q heads per kv head) sit in LDS once for the four waves. Each wave streams
+// its own keys and values through its own two LDS stages of 32 keys, straight from HBM
+// (global_load_lds, the next stage's loads out before the current one is awaited), and reads
+// only what it loaded itself, so the key loop has no workgroup barrier: after s_waitcnt the
+// stage is in LDS. Every key and value fragment read from LDS feeds TPW tiles. At the end the
+// four waves' states are merged in LDS, in wave order, into one partial per workgroup.
+// A stage is written into LDS 1 KB per wave instruction (lane l fills bytes 16 l .. 16 l + 15):
+//   keys   [32][D]; 16-byte column c of key k is stored at column c ^ key_swz(k), so the 16 key
+//          rows an S^T fragment read touches fall in 16 different bank groups;
+//   values page by page as the cache holds them, [page][D][16 slots]; the two 8-slot halves of
+//          row d trade places when bit 3 of d is set, which does the same for V^T reads.
+template <int D>
+__device__ __forceinline__ int key_swz(int k) {
+    if constexpr (D == 128) return (k & 3) | (((k >> 3) & 3) << 2);
+    else return (k & 3) | (((k >> 3) & 1) << 2);
+}
+
+// s_waitcnt with vmcnt <= n (n < 64) and the other counters unconstrained
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(n >= 0 && n < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | 0x70 | 0xF00);
+}
+
+template <int D, int TPW>
+__global__ __launch_bounds__(256) void attn_wave_kernel(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k_pool, const bf16 *__restrict__ v_pool,
     const int32_t *__restrict__ block_table, int max_pages, const int32_t *__restrict__ ctx_len,
     const uint64_t *__restrict__ anc, const int32_t *__restrict__ status, int K, int nq, int nkv,
-    int n_ranges, int cpr, int n_tg, float scale_log2, float *__restrict__ part_o,
+    int n_wr, int cpr, int n_tg, float scale_log2, float *__restrict__ part_o,
     float2 *__restrict__ part_ml) {
-    constexpr int CH = kAttnChunk;
-    constexpr int NS = CH / 32;
-    constexpr int KP = D + 8;
-    constexpr int VP = CH + 8;
-    constexpr int STAGERS = 16 * D / 8;
-    constexpr int NP = CH / 16;
-    static_assert(STAGERS <= 64 * NW, "staging needs one thread per 16 bytes of a page");
-    __shared__ __attribute__((aligned(16))) bf16 Ks[CH * KP];
-    __shared__ __attribute__((aligned(16))) bf16 Vt[D * VP];
+    constexpr int SK = 32;                 // keys per stage
+    constexpr int CD = D / 8;              // 16-byte columns of a key row
+    constexpr int KB = D / 16;             // 1 KB blocks per stage, keys (values alike)
+    constexpr int SLOTS = 2 * KB * 64;     // 16-byte slots per stage
+    constexpr int FK = D / 32;
+    constexpr int DT = D / 16;
+    constexpr int PPC = kAttnChunk / 16;   // pages per chunk
+    constexpr int QOFF = 4 * 2 * SLOTS;    // query fragments after the stages
+    constexpr int MSTRIDE = TPW * DT * 64 + TPW * 16 / 2;   // merge area of one wave (slots)
+    static_assert(3 * MSTRIDE <= QOFF, "the merge reuses the stage area");
+    __shared__ bf16x8 lds[QOFF + TPW * FK * 64];
 
-    const int rg = blockIdx.x, g = blockIdx.y;
-    const int b = blockIdx.z / n_tg, tg = blockIdx.z % n_tg;
-    const int st_b = status[b];
+    const int wr = blockIdx.x;
+    const int g = blockIdx.y / n_tg, tg = blockIdx.y % n_tg;
+    const int b = blockIdx.z;
+    if (status[b] != 0) return;            // uniform over the workgroup
     const int ctx = ctx_len[b];
-    if (st_b != 0) return;
     const int T = ctx + K;
-    const int nc = (T + CH - 1) / CH;
-    const int c_begin = rg * cpr;
-    if (c_begin >= nc) return;
-    const int c_end = min(c_begin + cpr, nc);
+    const int nc = (T + kAttnChunk - 1) / kAttnChunk;
+    const int c0 = wr * 4 * cpr;
+    if (c0 >= nc) return;                  // uniform over the workgroup
     const int group = nq / nkv;
     const int R = group * K;
     const int QT = (R + 15) >> 4;
-
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r16 = lane & 15, grp = lane >> 4;
-    const int t = tg * NW + wave;
-    const bool has_tile = t < QT;
-    const int rho = 16 * t + r16;
-    const bool col_ok = has_tile && rho < R;
-    const int hh = col_ok ? rho / K : 0;
-    const int tok = col_ok ? rho % K : 0;
-    bf16x8 qf[D / 32];
-    uint64_t am = 0;
-    if (has_tile) {
-        const bf16 *qrow = q + ((int64_t)(b * K + tok) * nq + g * group + hh) * D;
+
+    // the tile group's query fragments into LDS, fragment (t, ds) as 64 lanes x 16 bytes; tiles
+    // past the group reuse row 0's query and are never stored
+    for (int i = threadIdx.x; i < TPW * FK * 64; i += 256) {
+        const int t = i / (FK * 64), ds = (i / 64) % FK, l = i % 64;
+        const int tile = tg * TPW + t;
+        const int rho = 16 * tile + (l & 15);
+        const bool ok = tile < QT && rho < R;
+        const int hh = ok ? rho / K : 0, tok = ok ? rho % K : 0;
+        lds[QOFF + i] = *(const bf16x8 *)(q + ((int64_t)(b * K + tok) * nq + g * group + hh) * D +
+                                          ds * 32 + (l >> 4) * 8);
+    }
+    uint64_t am[TPW];
+    bool col_ok[TPW];
 #pragma unroll
-        for (int ds = 0; ds < D / 32; ++ds) qf[ds] = *(const bf16x8 *)(qrow + ds * 32 + grp * 8);
-        am = anc[b * K + tok];
+    for (int t = 0; t < TPW; ++t) {
+        const int tile = tg * TPW + t;
+        const int rho = 16 * tile + r16;
+        col_ok[t] = tile < QT && rho < R;
+        am[t] = anc[b * K + (col_ok[t] ? rho % K : 0)];
+    }
+
+    // this wave's chunks c0 + wave + 4 j (j < n_ch), in stages of 32 keys: stage sl is keys
+    // 32 (sl % 4) .. of chunk j = sl / 4; only the request's last chunk is short, and it is the
+    // last chunk of the wave that holds it
+    const int c_lim = min(c0 + 4 * cpr, nc);
+    const int n_ch = c0 + wave < c_lim ? (c_lim - c0 - wave + 3) / 4 : 0;
+    const int c_last = c0 + wave + 4 * (n_ch - 1);
+    const int n_st = n_ch > 0 ? 4 * (n_ch - 1) + (min(T - c_last * kAttnChunk, kAttnChunk) + SK - 1) / SK : 0;
+    auto stage_key = [&](int sl) __attribute__((always_inline)) { return (c0 + wave + 4 * (sl >> 2)) * kAttnChunk + (sl & 3) * SK; };
+    bf16x8 *ldw = &lds[wave * 2 * SLOTS];
+    // page ids: lane 8 j + p -> page p of chunk j (cpr <= 8 chunks, so at most 64); pages past
+    // the request's last one stand in for the chunk's first (in bounds; values zeroed before use)
+    const int np_req = (T + 15) >> 4;
+    int pg = 0;
+    if ((lane >> 3) < n_ch) {
+        const int c = c0 + wave + 4 * (lane >> 3);
+        const int pidx = c * PPC + (lane & 7);
+        pg = block_table[(int64_t)b * max_pages + (pidx < np_req ? pidx : c * PPC)];
+    }
+    auto issue = [&](int sl, int buf) __attribute__((always_inline)) {
+        const int li = 8 * (sl >> 2) + 2 * (sl & 3);
+        const int64_t p0 = __builtin_amdgcn_readlane(pg, li);
+        const int64_t p1 = __builtin_amdgcn_readlane(pg, li + 1);
+        bf16x8 *dst = ldw + buf * SLOTS;
+#pragma unroll
+        for (int j = 0; j < KB; ++j) {
+            const int key = j * (512 / D) + lane / CD;     // stage key (the block's page is uniform)
+            const int64_t page = (j * (512 / D)) < 16 ? p0 : p1;
+            const int col = (lane % CD) ^ key_swz<D>(key);
+            const bf16 *src = k_pool + ((page * nkv + g) * 16 + (key & 15)) * D + col * 8;
+            __builtin_amdgcn_global_load_lds((const void *)src,
+                                             (__attribute__((address_space(3))) void *)(dst + j * 64),
+                                             16, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < KB; ++j) {
+            const int64_t page = j < D / 32 ? p0 : p1;
+            const int d = (j % (D / 32)) * 32 + (lane >> 1);
+            const int half = (lane & 1) ^ ((d >> 3) & 1);
+            const bf16 *src = v_pool + ((page * nkv + g) * D + d) * 16 + half * 8;
+            __builtin_amdgcn_global_load_lds((const void *)src,
+                                             (__attribute__((address_space(3))) void *)(dst + (KB + j) * 64),
+                                             16, 0, 0);
+        }
+    };
+
+    float m_run[TPW], l_run[TPW];
+    floatx4 o[TPW][DT];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+        m_run[t] = -INFINITY;
+        l_run[t] = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[t][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
     const int kr0 = 8 * (r16 >> 2) + (r16 & 3);
-    const int32_t *bt = block_table + (int64_t)b * max_pages;
-    const bool stager = threadIdx.x < STAGERS;
-    const int e = (threadIdx.x % STAGERS) * 8;
-    const int srow = e / D, scol = e % D, sd = e >> 4, sslot = e & 15;
-    auto page_ids = [&](int c, int (&pg)[NP]) {
-        const int np = (min(CH, T - c * CH) + 15) >> 4;
-#pragma unroll
-        for (int p = 0; p < NP; ++p) pg[p] = (stager && p < np) ? bt[(c * CH >> 4) + p] : -1;
-    };
-    int pg[NP];
-    page_ids(c_begin, pg);
+    const bf16x8 *qs = lds + QOFF;
+    __syncthreads();                       // query fragments in place
 
-    float m_run = -INFINITY, l_run = 0.f;
-    floatx4 o[D / 16];
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-    for (int c = c_begin; c < c_end; ++c) {
-        const int kb = c * CH;
-        const int nvalid = min(CH, T - kb);
-        {
-            bf16x8 kr[NP], vr[NP];
-#pragma unroll
-            for (int p = 0; p < NP; ++p) {
-                if (pg[p] >= 0) {
-                    kr[p] = *(const bf16x8 *)(k_pool + ((int64_t)pg[p] * nkv + g) * 16 * D + e);
-                    vr[p] = *(const bf16x8 *)(v_pool + ((int64_t)pg[p] * nkv + g) * D * 16 + e);
-                } else {
-                    kr[p] = bf16x8{};
-                    vr[p] = bf16x8{};
-                }
-            }
-            if (c + 1 < c_end) page_ids(c + 1, pg);   // next chunk's pages, in flight meanwhile
-            if (c > c_begin) __syncthreads();          // the previous chunk is consumed
-            if (stager) {
-#pragma unroll
-                for (int p = 0; p < NP; ++p) {
-                    *(bf16x8 *)&Ks[(p * 16 + srow) * KP + scol] = kr[p];
-                    bf16x8 vv = vr[p];
-#pragma unroll
-                    for (int j = 0; j < 8; ++j)
-                        if (p * 16 + sslot + j >= nvalid) vv[j] = (bf16)0.0f;   // never multiply stale data
-                    *(bf16x8 *)&Vt[sd * VP + p * 16 + sslot] = vv;
-                }
-            }
-        }
-        __syncthreads();
-        if (!has_tile) continue;
-        const bool chunk_plain = nvalid == CH && kb + CH <= ctx;
-
-        floatx4 s[NS][2];
-        {
-            constexpr int NST = 2 * NS, FK = D / 32;
-            bf16x8 kf0[FK], kf1[FK];
-            auto kload = [&](bf16x8 (&kf)[FK], int i) {
-#pragma unroll
-                for (int ds = 0; ds < FK; ++ds)
-                    kf[ds] = *(const bf16x8 *)&Ks[((i >> 1) * 32 + kr0 + 4 * (i & 1)) * KP + grp * 8 + ds * 32];
-            };
-            kload(kf0, 0);
-#pragma unroll
-            for (int i = 0; i < NST; ++i) {
-                auto &cur = (i & 1) ? kf1 : kf0;
-                auto &nxt = (i & 1) ? kf0 : kf1;
-                if (i + 1 < NST) {
-                    kload(nxt, i + 1);
-                    __builtin_amdgcn_sched_group_barrier(0x100, FK, 0);
-                }
-                floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ds = 0; ds < FK; ++ds) acc = mfma16x16x32(cur[ds], qf[ds], acc);
-                s[i >> 1][i & 1] = acc;
-                __builtin_amdgcn_sched_group_barrier(0x008, FK, 0);
-            }
-        }
-        float mloc = -INFINITY;
-        if (chunk_plain) {
-#pragma unroll
-            for (int st = 0; st < NS; ++st)
-#pragma unroll
-                for (int e2 = 0; e2 < 8; ++e2) {
-                    s[st][e2 >> 2][e2 & 3] *= scale_log2;
-                    mloc = fmaxf(mloc, s[st][e2 >> 2][e2 & 3]);
-                }
+    // Stage sl in two halves. front: wait for the stage, start the next one's loads, S^T for
+    // every tile (masked, unscaled), and where asked each lane's maximum; back: p = 2^(s - m)
+    // against a fixed reference m per column, O^T += V^T . P^T and the column sums l += 1 . P^T
+    // on the matrix core. A column's reference is the maximum of the first stage in which it
+    // sees a key (a wave-wide exchange; o and l are still zero then): a wave's first stage, or
+    // a stage on the draft nodes. It never moves after that, so the hot loop never rescales o.
+    // o / l does not depend on the reference; p may exceed 1, and while no score passes its
+    // reference by more than 64 (log2 units) the fp32 sums and bf16 hi + lo carry it as well as
+    // p <= 1. If one does (l > 2^64 shows it), the wave finds the columns' true maxima in a
+    // max-only pass and streams its chunks again against them.
+    float s[TPW][8];
+    float mloc[TPW];
+    auto front = [&](int sl, bool want_max) __attribute__((always_inline)) {
+        const int buf = sl & 1;
+        const bf16x8 *ks = ldw + buf * SLOTS;
+        const int kb = stage_key(sl);
+        const int nvalid = min(SK, T - kb);
+        // the next stage's loads go out before this one is awaited (its buffer held stage
+        // sl - 1, consumed in the previous iteration), so two stages are in flight meanwhile
+        if (sl + 1 < n_st) {
+            issue(sl + 1, buf ^ 1);
+            wait_vm<2 * KB>();             // all but the next stage's 2 KB loads: this stage landed
         } else {
+            wait_vm<0>();
+        }
+        if (nvalid < SK) {
+            // the request's last keys: values past them (stale slots, stand-in pages) are zeroed,
+            // since a zero probability times a non-finite value is not zero
+            bf16x8 *vz = ldw + buf * SLOTS + KB * 64;
+            for (int idx = lane; idx < 2 * D * 2; idx += 64) {
+                const int pi = idx / (2 * D), d = (idx >> 1) % D, h = idx & 1;
+                const int k0 = pi * 16 + h * 8;
+                if (k0 + 8 <= nvalid) continue;
+                bf16x8 *slot = vz + pi * 2 * D + d * 2 + (h ^ ((d >> 3) & 1));
+                bf16x8 v = *slot;
 #pragma unroll
-            for (int st = 0; st < NS; ++st) {
-                const int k0 = kb + st * 32 + 8 * grp;
-                const int n_ctx = min(max(ctx - k0, 0), 8);
-                const int j0 = max(k0 + n_ctx - ctx, 0);
-                const unsigned anc8 = j0 < 64 ? (unsigned)(am >> j0) & 0xffu : 0u;
-                const int n_in = min(max(kb + nvalid - k0, 0), 8);
-                unsigned vis = (((1u << n_ctx) - 1u) | (anc8 << n_ctx)) & ((1u << n_in) - 1u);
-                if (!col_ok) vis = 0u;
-#pragma unroll
-                for (int e2 = 0; e2 < 8; ++e2) {
-                    const float raw = s[st][e2 >> 2][e2 & 3] * scale_log2;
-                    s[st][e2 >> 2][e2 & 3] = ((vis >> e2) & 1u) ? raw : -INFINITY;
-                    mloc = fmaxf(mloc, s[st][e2 >> 2][e2 & 3]);
-                }
+                for (int j = 0; j < 8; ++j)
+                    if (k0 + j >= nvalid) v[j] = (bf16)0.0f;
+                *slot = v;
             }
         }
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-        const float m_new = fmaxf(m_run, mloc);
-        const bool none = (m_new == -INFINITY);
-        const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-        if (__any(alpha != 1.f)) {
+        // key fragments of the stage: half h covers key rows kr0 + 4h, so that each lane ends
+        // with keys 8 grp .. 8 grp + 7 of every tile's S^T
+        bf16x8 kf[2][FK];
 #pragma unroll
-            for (int dt = 0; dt < D / 16; ++dt) o[dt] *= alpha;
+        for (int h = 0; h < 2; ++h) {
+            const int key = kr0 + 4 * h;
+            const int sw = key_swz<D>(key);
+#pragma unroll
+            for (int ds = 0; ds < FK; ++ds) kf[h][ds] = ks[key * CD + ((grp + 4 * ds) ^ sw)];
         }
-        float psum = 0.f;
-        {
-            constexpr int NST = 2 * NS, FV = D / 32;
-            bf16x8 vf0[FV], vf1[FV];
-            auto vload = [&](bf16x8 (&vf)[FV], int i) {
+        const bool plain = nvalid == SK && kb + SK <= ctx;
+        const int k0 = kb + 8 * grp;
+        const int n_ctx = min(max(ctx - k0, 0), 8);
+        const int j0 = max(k0 + n_ctx - ctx, 0);
+        const int n_in = min(max(kb + nvalid - k0, 0), 8);
 #pragma unroll
-                for (int j = 0; j < FV; ++j)
-                    vf[j] = *(const bf16x8 *)&Vt[(r16 + ((i & 1) * FV + j) * 16) * VP + (i >> 1) * 32 + grp * 8];
-            };
-            vload(vf0, 0);
-            bf16x8 ph, pl;
+        for (int t = 0; t < TPW; ++t) {
+            floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int i = 0; i < NST; ++i) {
-                auto &cur = (i & 1) ? vf1 : vf0;
-                auto &nxt = (i & 1) ? vf0 : vf1;
-                if (i + 1 < NST) {
-                    vload(nxt, i + 1);
-                    __builtin_amdgcn_sched_group_barrier(0x100, FV, 0);
-                }
-                if ((i & 1) == 0) {
-                    const int st = i >> 1;
+            for (int ds = 0; ds < FK; ++ds) {
+                const bf16x8 qv = qs[(t * FK + ds) * 64 + lane];
+                s0 = mfma16x16x32(kf[0][ds], qv, s0);
+                s1 = mfma16x16x32(kf[1][ds], qv, s1);
+            }
 #pragma unroll
-                    for (int e2 = 0; e2 < 8; ++e2) {
-                        const float pv = none ? 0.f : __builtin_amdgcn_exp2f(s[st][e2 >> 2][e2 & 3] - m_new);
-                        const bf16 hi = to_bf(pv);
-                        ph[e2] = hi;
-                        pl[e2] = to_bf(pv - to_f(hi));
-                        psum += pv;
+            for (int e2 = 0; e2 < 4; ++e2) {
+                s[t][e2] = s0[e2];
+                s[t][e2 + 4] = s1[e2];
+            }
+            if (!plain) {
+                // committed positions always, draft positions on the column's root path
+                const unsigned anc8 = j0 < 64 ? (unsigned)(am[t] >> j0) & 0xffu : 0u;
+                unsigned vis = (((1u << n_ctx) - 1u) | (anc8 << n_ctx)) & ((1u << n_in) - 1u);
+                if (!col_ok[t]) vis = 0u;
+#pragma unroll
+                for (int e2 = 0; e2 < 8; ++e2) s[t][e2] = ((vis >> e2) & 1u) ? s[t][e2] : -INFINITY;
+            }
+            if (want_max || !plain)
+                mloc[t] = fmaxf(fmaxf(fmaxf(s[t][0], s[t][1]), fmaxf(s[t][2], s[t][3])),
+                                fmaxf(fmaxf(s[t][4], s[t][5]), fmaxf(s[t][6], s[t][7]))) * scale_log2;
+        }
+        return plain;
+    };
+    bf16x8 ones;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ones[j] = (bf16)1.0f;
+    floatx4 lacc[TPW];
+    auto back = [&](int sl) __attribute__((always_inline)) {
+        const bf16x8 *vs = ldw + (sl & 1) * SLOTS + KB * 64;
+        bf16x8 ph[TPW], pl[TPW];
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            // a column with no visible key yet has only -inf scores, so any finite reference
+            // gives p = 0 there
+            const float m_use = m_run[t] == -INFINITY ? 0.f : m_run[t];
+#pragma unroll
+            for (int e2 = 0; e2 < 8; ++e2) {
+                const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][e2], scale_log2, -m_use));
+                const bf16 hi = to_bf(pv);
+                ph[t][e2] = hi;
+                pl[t][e2] = to_bf(pv - to_f(hi));
+            }
+            lacc[t] = mfma16x16x32(ones, ph[t], lacc[t]);
+            lacc[t] = mfma16x16x32(ones, pl[t], lacc[t]);
+        }
+        // one value fragment per 16 rows of d serves every tile
+        const int vp = grp >> 1, vh = grp & 1;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            const int d = r16 + 16 * dt;
+            const bf16x8 vf = vs[vp * 2 * D + d * 2 + (vh ^ ((d >> 3) & 1))];
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) {
+                o[t][dt] = mfma16x16x32(vf, ph[t], o[t][dt]);
+                o[t][dt] = mfma16x16x32(vf, pl[t], o[t][dt]);
+            }
+        }
+    };
+    auto col_max = [&](float v) __attribute__((always_inline)) {
+        v = fmaxf(v, __shfl_xor(v, 16, 64));
+        return fmaxf(v, __shfl_xor(v, 32, 64));
+    };
+    auto pass = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) lacc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+        if (n_st > 0) issue(0, 0);
+        for (int sl = 0; sl < n_st; ++sl) {
+            const bool plain = front(sl, sl == 0);
+            if (sl == 0 || !plain) {
+                bool fresh = false;
+#pragma unroll
+                for (int t = 0; t < TPW; ++t) fresh |= m_run[t] == -INFINITY && mloc[t] > -INFINITY;
+                if (__any(fresh)) {
+#pragma unroll
+                    for (int t = 0; t < TPW; ++t) {
+                        const float mc = col_max(mloc[t]);
+                        if (m_run[t] == -INFINITY) m_run[t] = mc;
                     }
                 }
-#pragma unroll
-                for (int j = 0; j < FV; ++j) {
-                    const int dt = (i & 1) * FV + j;
-                    o[dt] = mfma16x16x32(cur[j], ph, o[dt]);
-                    o[dt] = mfma16x16x32(cur[j], pl, o[dt]);
-                }
-                __builtin_amdgcn_sched_group_barrier(0x008, 2 * FV, 0);
             }
+            back(sl);
         }
-        psum += __shfl_xor(psum, 16, 64);
-        psum += __shfl_xor(psum, 32, 64);
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-    }
-    if (col_ok) {
-        const int64_t base = (((int64_t)b * nkv + g) * n_ranges + rg) * R + rho;
 #pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt)
-            *(floatx4 *)(part_o + base * D + dt * 16 + 4 * grp) = o[dt];
-        if (grp == 0) part_ml[base] = make_float2(m_run, l_run);
+        for (int t = 0; t < TPW; ++t) l_run[t] = lacc[t][0];
+    };
+    pass();
+    bool ovf = false;
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) ovf |= !(l_run[t] <= 0x1p64f);   // NaN from an inf too
+    if (__any(ovf)) {
+        // some score passed its column's reference by more than 64: the true maxima first
+        float tmax[TPW];
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) tmax[t] = -INFINITY;
+        if (n_st > 0) issue(0, 0);
+        for (int sl = 0; sl < n_st; ++sl) {
+            front(sl, true);
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) tmax[t] = fmaxf(tmax[t], mloc[t]);
+        }
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            m_run[t] = col_max(tmax[t]);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) o[t][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+        }
+        pass();
+    }
+
+    // merge the four waves' states in wave order: waves 1..3 leave theirs in the stage area
+    __syncthreads();                       // every wave is done with its stages
+    if (wave > 0) {
+        floatx4 *mo = reinterpret_cast<floatx4 *>(lds + (wave - 1) * MSTRIDE);
+        float2 *mml = reinterpret_cast<float2 *>(lds + (wave - 1) * MSTRIDE + TPW * DT * 64);
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) mo[(t * DT + dt) * 64 + lane] = o[t][dt];
+            if (grp == 0) mml[t * 16 + r16] = make_float2(m_run[t], l_run[t]);
+        }
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    for (int w = 1; w < 4; ++w) {
+        const floatx4 *mo = reinterpret_cast<const floatx4 *>(lds + (w - 1) * MSTRIDE);
+        const float2 *mml = reinterpret_cast<const float2 *>(lds + (w - 1) * MSTRIDE + TPW * DT * 64);
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            const float2 ml = mml[t * 16 + r16];
+            if (ml.x == -INFINITY) continue;
+            const float mn = fmaxf(m_run[t], ml.x);
+            const float a = __builtin_amdgcn_exp2f(m_run[t] - mn), aw = __builtin_amdgcn_exp2f(ml.x - mn);
+            l_run[t] = l_run[t] * a + ml.y * aw;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) o[t][dt] = o[t][dt] * a + mo[(t * DT + dt) * 64 + lane] * aw;
+            m_run[t] = mn;
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+        if (!col_ok[t]) continue;
+        const int rho = 16 * (tg * TPW + t) + r16;
+        const int64_t base = (((int64_t)b * nkv + g) * n_wr + wr) * R + rho;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+            *(floatx4 *)(part_o + base * D + dt * 16 + 4 * grp) = o[t][dt];
+        if (grp == 0) part_ml[base] = make_float2(m_run[t], l_run[t]);
     }
 }
 
@@ -572,10 +708,8 @@ hipError_t attention(const AttnArgs &a, hipStream_t st) {
     const int nw = (QT + 4) / 5 < (QT + 3) / 4 ? 5 : 4;
     const int n_tg = (QT + nw - 1) / nw;
     // A small grid (one request, a short draft) runs one chunk per workgroup, two kv heads each,
-    // so that it is resident at once. A large one (a batch, or hundreds of query rows) runs
-    // ranges of chunks, one kv head per workgroup: chunks per range are chosen so that a
-    // range's partial stays below about a quarter of the keys and values it covers, while at
-    // least ~512 workgroups remain.
+    // so that it is resident at once. A large one (a batch, or hundreds of query rows) streams
+    // ranges of chunks through LDS, one kv head per workgroup.
     const int64_t wgs1 = (int64_t)a.n_chunks * a.nkv * a.B * n_tg;
     int cpr = 1, stride = a.n_chunks;
     hipError_t e;
@@ -599,24 +733,45 @@ hipError_t attention(const AttnArgs &a, hipStream_t st) {
 #undef SV_ATTN_H
 #undef SV_ATTN
     } else {
-        cpr = (R + 31) / 32;
-        if (cpr > 8) cpr = 8;
-        while (cpr > 1 && (int64_t)((a.n_chunks + cpr - 1) / cpr) * a.nkv * a.B * n_tg < 512) --cpr;
-        const int n_ranges = (a.n_chunks + cpr - 1) / cpr;
-        stride = n_ranges;
-        const dim3 grid_r(n_ranges, a.nkv, a.B * n_tg);
-#define SV_RANGE(DD, NWV)                                                                         \
-    hipLaunchKernelGGL((attn_range_kernel<DD, NWV>), grid_r, dim3(64 * NWV), 0, st, a.q, a.k_pool, \
-                       a.v_pool, a.block_table, a.max_pages, a.ctx_len, a.anc, a.status, a.K,     \
-                       a.nq, a.nkv, n_ranges, cpr, n_tg, scale_log2, a.part_o, a.part_ml)
-        if (a.D == 128) {
-            if (nw == 4) SV_RANGE(128, 4);
-            else SV_RANGE(128, 5);
-        } else {
-            if (nw == 4) SV_RANGE(64, 4);
-            else SV_RANGE(64, 5);
+        // workgroups of four waves, 4 cpr chunks per workgroup (cpr per wave), one partial per
+        // workgroup; one workgroup per compute unit (two at D = 64). At least 2 and
+        // ceil(R / 128) chunks per wave (a partial, R x D fp32, then stays below about a quarter
+        // of the keys and values the workgroup covers), at most 8 (a wave's page ids fit one
+        // wave), and the
+        // count that makes the fewest rounds of workgroups times chunks per wave (rounds counted
+        // over the longest request)
+        const int tpw = QT <= 2 ? 2 : 5;
+        const int tgs = (QT + tpw - 1) / tpw;
+        const int per_round = a.D == 128 ? 256 : 512;
+        int cpr_min = (R + 127) / 128;
+        if (cpr_min < 2) cpr_min = 2;      // eight stages per wave at least
+        if (cpr_min > 8) cpr_min = 8;
+        int64_t best = -1;
+        int cpw = 1;
+        for (int cp = cpr_min; cp <= 8; ++cp) {
+            const int64_t wgs = (int64_t)((a.n_chunks + 4 * cp - 1) / (4 * cp)) * a.nkv * a.B * tgs;
+            const int64_t cost = (wgs + per_round - 1) / per_round * cp;
+            if (best < 0 || cost < best) {
+                best = cost;
+                cpw = cp;
+            }
         }
-#undef SV_RANGE
+        const int n_wr = (a.n_chunks + 4 * cpw - 1) / (4 * cpw);
+        stride = n_wr;
+        cpr = 4 * cpw;                     // chunks per partial, for the combine
+        const dim3 grid_w(n_wr, a.nkv * tgs, a.B);
+#define SV_WAVE(DD, TP)                                                                           \
+    hipLaunchKernelGGL((attn_wave_kernel<DD, TP>), grid_w, dim3(256), 0, st, a.q, a.k_pool,        \
+                       a.v_pool, a.block_table, a.max_pages, a.ctx_len, a.anc, a.status, a.K,     \
+                       a.nq, a.nkv, n_wr, cpw, tgs, scale_log2, a.part_o, a.part_ml)
+        if (a.D == 128) {
+            if (tpw == 2) SV_WAVE(128, 2);
+            else SV_WAVE(128, 5);
+        } else {
+            if (tpw == 2) SV_WAVE(64, 2);
+            else SV_WAVE(64, 5);
+        }
+#undef SV_WAVE
     }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
