@@ -43,9 +43,9 @@ METRIC = "verified tokens/sec + verify-step HBM GB/s (% peak), 27B-shape dense, 
 # figures hold for the GEMM source they were taken on; any other source reports null.
 PMC_TRAFFIC = {
     "block": {"source": "tree_verification_skinny_amd/csrc/k_gemm.hip",
-              "sha256": "307beeab274b9121e8b1ec74f1df91323105bdafd2300ff0dd7d5cd4ede84404",
-              "fetch_kib": 174929.666, "write_kib": 544.0,
-              "fetch_scale": 1.9999860, "write_scale": 1.0},
+              "sha256": "22b5029a2ab5f715ba99b295417fd151b3882e42867b79518167bd009d71eea3",
+              "fetch_kib": 174927.570, "write_kib": 544.0,
+              "fetch_scale": 1.9999858, "write_scale": 1.0},
 }
 HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0     # dense bf16 matrix-core peak of MI355X
