@@ -146,6 +146,26 @@ def pmc_traffic(config):
     return int(round((rec["fetch_kib"] * rec["fetch_scale"] + rec["write_kib"] * rec["write_scale"]) * 1024))
 
 
+def read_probe(device, nbytes=4 << 30):
+    """Streaming-read rate: the library's plain grid-stride read of a 4 GiB buffer (HIP events
+    on the current stream around 5 launches)."""
+    a = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=device)
+    a.fill_(1.0)
+    out = torch.zeros(1, dtype=torch.int32, device=device)
+    for _ in range(2):
+        tv.spec_read_probe(a, out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        tv.spec_read_probe(a, out)
+    e1.record()
+    torch.cuda.synchronize()
+    s = e0.elapsed_time(e1) / 1e3 / 5
+    del a
+    return nbytes / s / 1e9
+
+
 def copy_probe(device, nbytes=4 << 30):
     a = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=device)
     b = torch.empty_like(a)
@@ -210,7 +230,7 @@ def cpu_baseline(weights, shape, kv, tokens, parent, ctx, budget_s):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="block", choices=["block", "tree", "batched"])
     ap.add_argument("--eager", action="store_true", help="launch every step instead of a HIP graph")
@@ -323,7 +343,9 @@ def main():
                  "frac_of_bf16_peak": round(flops / (ms / 1e3) / 2.5e15, 5)},
         "step_ms": {"mean": round(ms, 4), "median": round(float(np.median(per_step)), 4),
                     "p5": round(float(np.percentile(per_step, 5)), 4),
-                    "p95": round(float(np.percentile(per_step, 95)), 4)},
+                    "p95": round(float(np.percentile(per_step, 95)), 4),
+                    "ci95": round(1.96 * float(np.std(per_step, ddof=1)) / len(per_step) ** 0.5, 4)
+                    if len(per_step) > 1 else None},
         "draft_tokens_per_s": round(B * (K - 1) / (ms / 1e3), 2),
         "committed_tokens_per_s": round(committed / args.steps / (ms / 1e3), 2),
         "ctx_after": ctx_now[:4],
@@ -361,9 +383,12 @@ def main():
                                    "share_of_step": round(s_launch * L * 1e3 / ms, 4),
                                    "ms_per_eager_step_with_events": round(ms_ev, 4)})
         result["copy_probe_gbps"] = round(copy_probe(device), 1)
+        rp = read_probe(device)
+        result["read_probe_gbps"] = round(rp, 1)
+        result["hbm"]["frac_of_read_probe"] = round(result["hbm"]["achieved_gbps"] / rp, 4)
         log(f"gate/up projection: {ach:.0f} {result['roofline']['unit']} per launch "
             f"({s_launch * 1e6:.1f} us avg, {s_launch * L * 1e3 / ms:.1%} of the step); "
-            f"copy probe {result['copy_probe_gbps']} GB/s")
+            f"copy probe {result['copy_probe_gbps']} GB/s, read probe {rp:.1f} GB/s")
     if not args.no_cpu_baseline:
         t_ctx.copy_(ctx0)
         result["cpu_baseline"] = cpu_baseline(weights, shape, kv, tokens, parent, ctx,

@@ -179,6 +179,14 @@ int spec_skinny_gemm_bytes(int m, int n, int kd, size_t *bytes);
 int spec_skinny_gemm(const void *x, int m, int kd, const void *w, int n, float *partials,
                      size_t partial_bytes, int *splits, hipStream_t stream);
 
+/* Measurement aid: reads `bytes` of device memory once as a plain grid-stride stream of 16-byte
+ * loads (the access pattern DRAM serves best) and folds them into a word that is written to
+ * *out (a DEVICE uint32) only in the unlikely case that it equals a fixed constant, so the loads
+ * cannot be dropped. Its rate is the streaming-read ceiling the projection kernels are compared
+ * against. buf must be 16-byte aligned and bytes a multiple of 16; returns SPEC_EINVAL
+ * otherwise. Enqueued on `stream`. */
+int spec_read_probe(const void *buf, size_t bytes, uint32_t *out, hipStream_t stream);
+
 /* Static text for a return code. */
 const char *spec_strerror(int code);
 

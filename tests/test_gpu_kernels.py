@@ -73,3 +73,15 @@ def test_skinny_gemm_rejects_bad_shapes():
         tv.spec_skinny_gemm(x, w, torch.zeros(1024, device=DEV))
     with pytest.raises(tv.SpecError):
         tv.spec_pack_weight(torch.zeros((20, 64), dtype=torch.bfloat16, device=DEV))
+
+
+def test_read_probe_runs_and_checks_its_arguments():
+    """The streaming-read probe reads its buffer and leaves the output word alone (the fold of
+    all-zero data is zero, not the trigger constant); misaligned sizes are rejected."""
+    buf = torch.zeros(1 << 20, dtype=torch.int32, device=DEV)
+    out = torch.full((1,), 7, dtype=torch.int32, device=DEV)
+    tv.spec_read_probe(buf, out)
+    torch.cuda.synchronize()
+    assert int(out.item()) == 7
+    with pytest.raises(RuntimeError):
+        tv.spec_read_probe(buf[:3], out)

@@ -93,9 +93,10 @@ def lib() -> ctypes.CDLL:
         L.spec_pack_weight.argtypes = [vp, i32, i32, vp, vp]
         L.spec_skinny_gemm_bytes.argtypes = [i32, i32, i32, ctypes.POINTER(sz)]
         L.spec_skinny_gemm.argtypes = [vp, i32, i32, vp, i32, vp, sz, ctypes.POINTER(i32), vp]
+        L.spec_read_probe.argtypes = [vp, sz, vp, vp]
         for f in (L.spec_workspace_bytes, L.spec_verify, L.spec_commit_kv,
                   L.spec_accept_workspace_bytes, L.spec_accept, L.spec_skinny_gemm_bytes,
-                  L.spec_skinny_gemm, L.spec_pack_weight):
+                  L.spec_skinny_gemm, L.spec_pack_weight, L.spec_read_probe):
             f.restype = i32
         _lib = L
     return _lib
@@ -103,7 +104,7 @@ def lib() -> ctypes.CDLL:
 
 EXPORTED = ("spec_workspace_bytes", "spec_verify", "spec_commit_kv", "spec_accept_workspace_bytes",
             "spec_accept", "spec_pack_weight", "spec_skinny_gemm_bytes", "spec_skinny_gemm",
-            "spec_strerror")
+            "spec_read_probe", "spec_strerror")
 
 
 def spec_strerror(code: int) -> str:
@@ -270,6 +271,13 @@ def spec_accept(logits: torch.Tensor, draft_tokens: torch.Tensor,
                            _ptr(accepted_len), _ptr(bonus_token), _ptr(accepted_path), _ptr(greedy),
                            _ptr(ws), ws.numel(), _stream(stream))
     _check(rc, "spec_accept")
+
+
+def spec_read_probe(buf: torch.Tensor, out: torch.Tensor, stream=None) -> None:
+    """Reads all of buf (a contiguous device tensor, size a multiple of 16 bytes) once as a
+    plain stream; out: a device int32/uint32 tensor of at least one element."""
+    _check(lib().spec_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(out),
+                                 _stream(stream)), "spec_read_probe")
 
 
 def spec_skinny_gemm_bytes(m: int, n: int, kd: int) -> int:

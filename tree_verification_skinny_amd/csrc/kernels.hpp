@@ -108,5 +108,7 @@ hipError_t commit_kv(const int32_t *accepted_len, const int32_t *path, const int
                      const int32_t *block_table, int max_pages, int n_pages, int L, int B, int K,
                      int nkv, int D, bf16 *k_pool, bf16 *v_pool, hipStream_t st);
 hipError_t commit_ctx(const int32_t *accepted_len, int32_t *ctx_len, int B, hipStream_t st);
+// Reads bytes (a multiple of 16, 16-byte aligned) once as a grid-stride stream.
+hipError_t read_probe(const void *buf, int64_t bytes, uint32_t *out, hipStream_t st);
 
 }  // namespace sv

@@ -339,6 +339,13 @@ int spec_skinny_gemm(const void *x, int m, int kd, const void *w, int n, float *
     return SPEC_OK;
 }
 
+int spec_read_probe(const void *buf, size_t bytes, uint32_t *out, hipStream_t stream) {
+    if (buf == nullptr || out == nullptr || bytes == 0 || bytes % 16 != 0) return SPEC_EINVAL;
+    if (reinterpret_cast<uintptr_t>(buf) % 16 != 0) return SPEC_EINVAL;
+    SV_TRY(read_probe(buf, (int64_t)bytes, out, stream));
+    return SPEC_OK;
+}
+
 int spec_accept_workspace_bytes(int batch, int k, int vocab, size_t *bytes) {
     if (bytes == nullptr || batch < 1 || k < 1 || vocab < 1) return SPEC_EINVAL;
     if (k > SPEC_MAX_K) return SPEC_EUNSUPPORTED;
