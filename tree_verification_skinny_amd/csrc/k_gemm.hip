@@ -220,7 +220,13 @@ __global__ __launch_bounds__(64 * W) void gemm_kernel(GemmIn in, const bf16 *__r
 // through LDS once per workgroup in slabs of KS K-steps (double-buffered: slab j+1 is fetched
 // from L2 while slab j is multiplied). A wave's weight fragments for the next slab are in flight
 // while it multiplies the current one. One barrier per slab.
-constexpr int kWideWaves = 4, kWideTN = 2, kWideKS = 8;
+#ifndef SV_WIDE_KS
+#define SV_WIDE_KS 4
+#endif
+#ifndef SV_WIDE_TARGET
+#define SV_WIDE_TARGET 320
+#endif
+constexpr int kWideWaves = 4, kWideTN = 2, kWideKS = SV_WIDE_KS;
 
 // output column of tile t (0..TN-1) of wave w in group ng: SwiGLU pairs gate and up columns in the
 // same wave and lane
@@ -536,7 +542,8 @@ GemmShape plan_gemm(int M, int N, int Kd, bool allow_split) {
     }
     if (M > 16 && N % (16 * kWideWaves * kWideTN) == 0) {
         // wide variant: 8 tiles per workgroup; split K (multiples of the slab where possible)
-        // until at least 256 workgroups stream
+        // until at least SV_WIDE_TARGET workgroups stream (320 and 4-step slabs measured best
+        // on the 64-node tree: 15.7 ms per step against 16.6 with 256 and 8-step slabs)
         g.wide = true;
         g.nt = kWideWaves * kWideTN;
         g.waves = kWideWaves;
@@ -547,10 +554,10 @@ GemmShape plan_gemm(int M, int N, int Kd, bool allow_split) {
             for (int sp = 2; sp <= 32 && sp <= steps; ++sp) {
                 if (steps % sp != 0 || (steps / sp) % kWideKS != 0) continue;
                 best = sp;
-                if (groups * sp >= 256) break;
+                if (groups * sp >= SV_WIDE_TARGET) break;
             }
             if (best == 0) {
-                best = (256 + groups - 1) / groups;
+                best = (SV_WIDE_TARGET + groups - 1) / groups;
                 if (best > 32) best = 32;
                 while (best > 1 && steps / best < kWideKS) --best;
             }
