@@ -699,6 +699,15 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(
     store4(dst, o[0] / l, o[1] / l, o[2] / l, o[3] / l);
 }
 
+// Tunables: the largest chunk-kernel grid (workgroups) before the wave kernel takes over, and
+// a fixed chunk count per wave for the wave kernel (0: chosen per launch, below).
+#ifndef SV_ATTN_SMALL_GRID
+#define SV_ATTN_SMALL_GRID 512
+#endif
+#ifndef SV_ATTN_CPW
+#define SV_ATTN_CPW 0
+#endif
+
 hipError_t attention(const AttnArgs &a, hipStream_t st) {
     const float scale_log2 = kLog2e / sqrtf((float)a.D);
     // waves per kv head: 5 when that takes fewer query tiles per wave than 4 (one tile each for
@@ -713,7 +722,7 @@ hipError_t attention(const AttnArgs &a, hipStream_t st) {
     const int64_t wgs1 = (int64_t)a.n_chunks * a.nkv * a.B * n_tg;
     int cpr = 1, stride = a.n_chunks;
     hipError_t e;
-    if (wgs1 <= 512) {
+    if (wgs1 <= SV_ATTN_SMALL_GRID) {
         const int hpw = a.nkv % 2 == 0 ? 2 : 1;
         const dim3 grid_h(a.n_chunks, a.nkv / hpw, a.B);
 #define SV_ATTN(DD, NWV, HP)                                                                      \
@@ -733,13 +742,12 @@ hipError_t attention(const AttnArgs &a, hipStream_t st) {
 #undef SV_ATTN_H
 #undef SV_ATTN
     } else {
-        // workgroups of four waves, 4 cpr chunks per workgroup (cpr per wave), one partial per
+        // workgroups of four waves, 4 cpw chunks per workgroup (cpw per wave), one partial per
         // workgroup; one workgroup per compute unit (two at D = 64). At least 2 and
         // ceil(R / 128) chunks per wave (a partial, R x D fp32, then stays below about a quarter
         // of the keys and values the workgroup covers), at most 8 (a wave's page ids fit one
-        // wave), and the
-        // count that makes the fewest rounds of workgroups times chunks per wave (rounds counted
-        // over the longest request)
+        // wave), and the count that makes the fewest rounds of workgroups (counted over the
+        // longest request) times the time of one (cpw chunks plus a fixed share)
         const int tpw = QT <= 2 ? 2 : 5;
         const int tgs = (QT + tpw - 1) / tpw;
         const int per_round = a.D == 128 ? 256 : 512;
@@ -748,9 +756,13 @@ hipError_t attention(const AttnArgs &a, hipStream_t st) {
         if (cpr_min > 8) cpr_min = 8;
         int64_t best = -1;
         int cpw = 1;
-        for (int cp = cpr_min; cp <= 8; ++cp) {
+        const int cp_lo = SV_ATTN_CPW > 0 ? SV_ATTN_CPW : cpr_min;
+        const int cp_hi = SV_ATTN_CPW > 0 ? SV_ATTN_CPW : 8;
+        for (int cp = cp_lo; cp <= cp_hi; ++cp) {
             const int64_t wgs = (int64_t)((a.n_chunks + 4 * cp - 1) / (4 * cp)) * a.nkv * a.B * tgs;
-            const int64_t cost = (wgs + per_round - 1) / per_round * cp;
+            // a workgroup's fixed work (query tiles, page ids, the first stage's latency, the
+            // merge, its partial and the combine's read of it) counts as about 3 chunks
+            const int64_t cost = (wgs + per_round - 1) / per_round * (cp + 3);
             if (best < 0 || cost < best) {
                 best = cost;
                 cpw = cp;

@@ -220,6 +220,9 @@ __global__ __launch_bounds__(64 * W) void gemm_kernel(GemmIn in, const bf16 *__r
 // through LDS once per workgroup in slabs of KS K-steps (double-buffered: slab j+1 is fetched
 // from L2 while slab j is multiplied). A wave's weight fragments for the next slab are in flight
 // while it multiplies the current one. One barrier per slab.
+#ifndef SV_TC_TARGET
+#define SV_TC_TARGET 512                                // workgroups a split tile launch aims at
+#endif
 #ifndef SV_WIDE_KS
 #define SV_WIDE_KS 4
 #endif
@@ -525,16 +528,17 @@ GemmShape plan_gemm(int M, int N, int Kd, bool allow_split) {
     const int steps = Kd / 32;
     if (M >= 128 && N % gemm_tc_columns() == 0) {
         // hundreds of rows: the matrix-core tile kernel, one launch over all 256-row tiles;
-        // narrow projections split K so that about 768 workgroups (three per compute unit at
-        // most) make one round
+        // narrow projections split K so that about SV_TC_TARGET workgroups stream (512, two per
+        // compute unit, measured best at 512 rows: fewer splits leave fewer fp32 partials to
+        // write and add; 768, 384 and 256 were 8, 5 and 10 % slower on the batched step)
         g.tc = true;
         g.nt = gemm_tc_columns() / 16;
         g.waves = 4;
         const int groups = N / gemm_tc_columns();
         const int mtiles = (M + 255) / 256;
         g.splits = 1;
-        if (allow_split && groups * mtiles < 384) {
-            g.splits = 768 / (groups * mtiles);
+        if (allow_split && groups * mtiles < SV_TC_TARGET / 2) {
+            g.splits = SV_TC_TARGET / (groups * mtiles);
             if (g.splits > 16) g.splits = 16;
             while (g.splits > 1 && steps / g.splits < 8) --g.splits;
         }
