@@ -220,6 +220,9 @@ __global__ __launch_bounds__(64 * W) void gemm_kernel(GemmIn in, const bf16 *__r
 // through LDS once per workgroup in slabs of KS K-steps (double-buffered: slab j+1 is fetched
 // from L2 while slab j is multiplied). A wave's weight fragments for the next slab are in flight
 // while it multiplies the current one. One barrier per slab.
+#ifndef SV_SKINNY_TARGET
+#define SV_SKINNY_TARGET 640                            // workgroups a split skinny launch aims at
+#endif
 #ifndef SV_TC_TARGET
 #define SV_TC_TARGET 512                                // workgroups a split tile launch aims at
 #endif
@@ -575,7 +578,7 @@ GemmShape plan_gemm(int M, int N, int Kd, bool allow_split) {
     const int groups = N / (16 * g.nt);
     g.splits = 1;
     if (allow_split && groups < 400) {
-        g.splits = (640 + groups / 2) / groups;
+        g.splits = (SV_SKINNY_TARGET + groups / 2) / groups;
         if (g.splits > 16) g.splits = 16;
         while (g.splits > 1 && steps / g.splits < 16) --g.splits;
     }
