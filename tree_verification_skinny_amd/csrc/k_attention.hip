@@ -699,6 +699,54 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(
     store4(dst, o[0] / l, o[1] / l, o[2] / l, o[3] / l);
 }
 
+// Merge for few partials per (node, q head), as the wave kernel leaves them: one thread per
+// (node, q head, column quad), the partials merged in order with every load of a batch of 4 in
+// flight before the arithmetic.
+template <int D>
+__global__ __launch_bounds__(256) void attn_combine_few_kernel(
+    const float *__restrict__ part_o, const float2 *__restrict__ part_ml,
+    const int32_t *__restrict__ ctx_len, const int32_t *__restrict__ status, int K, int nq,
+    int nkv, int stride, int cpr, int64_t total, bf16 *__restrict__ out) {
+    constexpr int NQD = D / 4;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= total) return;
+    const int quad = (int)(i % NQD);
+    const int64_t rh = i / NQD;
+    const int h = (int)(rh % nq), row = (int)(rh / nq);
+    const int b = row / K, tok = row % K;
+    bf16 *dst = out + frag_off(row, h * D + quad * 4, nq * D);   // fragment order: the O operand
+    if (status[b] != 0) {
+        store4(dst, 0.f, 0.f, 0.f, 0.f);
+        return;
+    }
+    const int group = nq / nkv, g = h / group, hh = h % group;
+    const int R = group * K, rho = hh * K + tok;
+    const int nc = ((ctx_len[b] + K + kAttnChunk - 1) / kAttnChunk + cpr - 1) / cpr;
+    const int64_t base = ((int64_t)b * nkv + g) * stride * R + rho;
+    float m = -INFINITY, l = 0.f;
+    floatx4 o = {0.f, 0.f, 0.f, 0.f};
+    for (int c0 = 0; c0 < nc; c0 += 4) {
+        float2 ml[4];
+        floatx4 oc[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int c = min(c0 + t, nc - 1);
+            ml[t] = part_ml[base + (int64_t)c * R];
+            oc[t] = *(const floatx4 *)(part_o + (base + (int64_t)c * R) * D + quad * 4);
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            if (c0 + t >= nc || ml[t].x == -INFINITY) continue;
+            const float mn = fmaxf(m, ml[t].x);
+            const float a = exp2f(m - mn), w = exp2f(ml[t].x - mn);
+            l = l * a + ml[t].y * w;
+            o = o * a + oc[t] * w;
+            m = mn;
+        }
+    }
+    store4(dst, o[0] / l, o[1] / l, o[2] / l, o[3] / l);
+}
+
 // Tunables: the largest chunk-kernel grid (workgroups) before the wave kernel takes over, and
 // a fixed chunk count per wave for the wave kernel (0: chosen per launch, below).
 #ifndef SV_ATTN_SMALL_GRID
@@ -787,12 +835,23 @@ hipError_t attention(const AttnArgs &a, hipStream_t st) {
     }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (a.D == 128)
+    if (cpr > 1) {
+        // the wave kernel's few partials per (node, q head)
+        const int64_t total = (int64_t)a.B * a.K * a.nq * (a.D / 4);
+        const dim3 grid_c((unsigned)((total + 255) / 256));
+        if (a.D == 128)
+            hipLaunchKernelGGL(attn_combine_few_kernel<128>, grid_c, dim3(256), 0, st, a.part_o,
+                               a.part_ml, a.ctx_len, a.status, a.K, a.nq, a.nkv, stride, cpr, total, a.out);
+        else
+            hipLaunchKernelGGL(attn_combine_few_kernel<64>, grid_c, dim3(256), 0, st, a.part_o,
+                               a.part_ml, a.ctx_len, a.status, a.K, a.nq, a.nkv, stride, cpr, total, a.out);
+    } else if (a.D == 128) {
         hipLaunchKernelGGL(attn_combine_kernel<128>, dim3(a.B * a.K, a.nq), dim3(256), 0, st,
                            a.part_o, a.part_ml, a.ctx_len, a.status, a.K, a.nq, a.nkv, stride, cpr, a.out);
-    else
+    } else {
         hipLaunchKernelGGL(attn_combine_kernel<64>, dim3(a.B * a.K, a.nq), dim3(256), 0, st,
                            a.part_o, a.part_ml, a.ctx_len, a.status, a.K, a.nq, a.nkv, stride, cpr, a.out);
+    }
     return hipGetLastError();
 }
 
