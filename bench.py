@@ -43,9 +43,9 @@ METRIC = "verified tokens/sec + verify-step HBM GB/s (% peak), 27B-shape dense, 
 # figures hold for the GEMM source they were taken on; any other source reports null.
 PMC_TRAFFIC = {
     "block": {"source": "tree_verification_skinny_amd/csrc/k_gemm.hip",
-              "sha256": "22b5029a2ab5f715ba99b295417fd151b3882e42867b79518167bd009d71eea3",
-              "fetch_kib": 174927.570, "write_kib": 544.0,
-              "fetch_scale": 1.9999858, "write_scale": 1.0},
+              "sha256": "762a813240ecff179ec1d7b1bf5d0cbfd68c0dc7c3e98efcd3828a9d3220b313",
+              "fetch_kib": 174932.523, "write_kib": 544.0,
+              "fetch_scale": 1.9999851, "write_scale": 1.0},
 }
 HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0     # dense bf16 matrix-core peak of MI355X
