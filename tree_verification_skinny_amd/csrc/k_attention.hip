@@ -752,6 +752,9 @@ __global__ __launch_bounds__(256) void attn_combine_few_kernel(
 #ifndef SV_ATTN_SMALL_GRID
 #define SV_ATTN_SMALL_GRID 512
 #endif
+#ifndef SV_ATTN_HPW
+#define SV_ATTN_HPW 2                                   // kv heads per chunk-kernel workgroup
+#endif
 #ifndef SV_ATTN_CPW
 #define SV_ATTN_CPW 0
 #endif
@@ -771,7 +774,7 @@ hipError_t attention(const AttnArgs &a, hipStream_t st) {
     int cpr = 1, stride = a.n_chunks;
     hipError_t e;
     if (wgs1 <= SV_ATTN_SMALL_GRID) {
-        const int hpw = a.nkv % 2 == 0 ? 2 : 1;
+        const int hpw = a.nkv % SV_ATTN_HPW == 0 ? SV_ATTN_HPW : 1;
         const dim3 grid_h(a.n_chunks, a.nkv / hpw, a.B);
 #define SV_ATTN(DD, NWV, HP)                                                                      \
     hipLaunchKernelGGL((attn_partial_kernel<DD, NWV, HP>), grid_h, dim3(64 * NWV * HP), 0, st,    \
