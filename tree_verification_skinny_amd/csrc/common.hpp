@@ -46,6 +46,10 @@ __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
     return v > bv || (v == bv && i < bi);
 }
 
+// A 16-byte load marked non-temporal: data read once per pass (weights, the KV cache), which
+// should not displace what is reused.
+__device__ __forceinline__ bf16x8 stream_load(const bf16x8 *p) { return __builtin_nontemporal_load(p); }
+
 __device__ __forceinline__ floatx4 mfma16x16x32(bf16x8 a, bf16x8 b, floatx4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }

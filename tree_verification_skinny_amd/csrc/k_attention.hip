@@ -104,8 +104,8 @@ __global__ __launch_bounds__(64 * NW * HPW) void attn_partial_kernel(
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
             if (pages[p] >= 0) {
-                kr[p] = *(const bf16x8 *)(k_pool + ((int64_t)pages[p] * nkv + gs) * 16 * D + e);
-                vr[p] = *(const bf16x8 *)(v_pool + ((int64_t)pages[p] * nkv + gs) * D * 16 + e);
+                kr[p] = stream_load((const bf16x8 *)(k_pool + ((int64_t)pages[p] * nkv + gs) * 16 * D + e));
+                vr[p] = stream_load((const bf16x8 *)(v_pool + ((int64_t)pages[p] * nkv + gs) * D * 16 + e));
             } else {
                 kr[p] = bf16x8{};
                 vr[p] = bf16x8{};

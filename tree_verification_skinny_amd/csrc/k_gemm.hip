@@ -9,7 +9,9 @@
 //     pre-packed in MFMA fragment order (see spec_pack_weight): fragment (tile of 16 rows,
 //     32-wide K step) is 1 KB, lane l's 16 bytes are W[16 tile + l%16][32 step + 8(l/16) .. +7],
 //     and a tile's K steps follow each other. One 128-bit load per lane reads a whole fragment
-//     as 1 KB of contiguous HBM, straight into the registers the MFMA consumes.
+//     as 1 KB of contiguous HBM, straight into the registers the MFMA consumes. The loads are
+//     non-temporal (each weight byte is used once per pass), which measured 6 % faster over the
+//     whole block-of-16 step than plain loads.
 //   * The activations X [M][Kd] (cache resident, already normalised where an RMSNorm precedes
 //     the projection) are the B operand, in the same fragment order (16-row blocks instead of
 //     16-row tiles): the kernels that produce them write them that way, so an activation load
@@ -119,7 +121,7 @@ __global__ __launch_bounds__(64 * W) void gemm_kernel(GemmIn in, const bf16 *__r
 #pragma unroll
         for (int u = 0; u < U; ++u) {
 #pragma unroll
-            for (int t = 0; t < NT; ++t) a[u][t] = *(const bf16x8 *)(wp[t] + (int64_t)(s + W * u) * 512);
+            for (int t = 0; t < NT; ++t) a[u][t] = stream_load((const bf16x8 *)(wp[t] + (int64_t)(s + W * u) * 512));
         }
 #pragma unroll
         for (int u = 0; u < U; ++u)
@@ -135,7 +137,7 @@ __global__ __launch_bounds__(64 * W) void gemm_kernel(GemmIn in, const bf16 *__r
     for (; s < s_end; s += W) {
         bf16x8 a[NT], b[MT];
 #pragma unroll
-        for (int t = 0; t < NT; ++t) a[t] = *(const bf16x8 *)(wp[t] + (int64_t)s * 512);
+        for (int t = 0; t < NT; ++t) a[t] = stream_load((const bf16x8 *)(wp[t] + (int64_t)s * 512));
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) b[mt] = *(const bf16x8 *)(xp[mt] + (int64_t)s * 512);
 #pragma unroll
@@ -295,7 +297,7 @@ __global__ __launch_bounds__(64 * kWideWaves) void gemm_wide_kernel(GemmIn in, c
             const int s = slab * KS + k;                 // relative to s_begin
 #pragma unroll
             for (int t = 0; t < TN; ++t)
-                a[k][t] = s < nsteps ? *(const bf16x8 *)(wp[t] + (int64_t)s * 512) : bf16x8{};
+                a[k][t] = s < nsteps ? stream_load((const bf16x8 *)(wp[t] + (int64_t)s * 512)) : bf16x8{};
         }
     };
 
