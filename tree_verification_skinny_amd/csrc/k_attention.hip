@@ -279,9 +279,9 @@ __global__ __launch_bounds__(64 * NW * HPW) void attn_partial_kernel(
 // waves in turn (wave w: chunks w, w + 4, ...). The tile group's TPW query tiles (all five of a
 // block of 16 with 5 q heads per kv head) sit in LDS once for the four waves. Each wave streams
 // its own keys and values through its own two LDS stages of 32 keys, straight from HBM
-// (global_load_lds, the next stage's loads out before the current one is awaited), and reads
-// only what it loaded itself, so the key loop has no workgroup barrier: after s_waitcnt the
-// stage is in LDS. Every key and value fragment read from LDS feeds TPW tiles. At the end the
+// (global_load_lds, non-temporal, the next stage's loads out before the current one is
+// awaited), and reads only what it loaded itself, so the key loop has no workgroup barrier:
+// after s_waitcnt the stage is in LDS. Every key and value fragment read from LDS feeds TPW tiles. At the end the
 // four waves' states are merged in LDS, in wave order, into one partial per workgroup.
 // A stage is written into LDS 1 KB per wave instruction (lane l fills bytes 16 l .. 16 l + 15):
 //   keys   [32][D]; 16-byte column c of key k is stored at column c ^ key_swz(k), so the 16 key
@@ -388,7 +388,7 @@ __global__ __launch_bounds__(256) void attn_wave_kernel(
             const bf16 *src = k_pool + ((page * nkv + g) * 16 + (key & 15)) * D + col * 8;
             __builtin_amdgcn_global_load_lds((const void *)src,
                                              (__attribute__((address_space(3))) void *)(dst + j * 64),
-                                             16, 0, 0);
+                                             16, 0, 2);   // 2: non-temporal
         }
 #pragma unroll
         for (int j = 0; j < KB; ++j) {
@@ -398,7 +398,7 @@ __global__ __launch_bounds__(256) void attn_wave_kernel(
             const bf16 *src = v_pool + ((page * nkv + g) * D + d) * 16 + half * 8;
             __builtin_amdgcn_global_load_lds((const void *)src,
                                              (__attribute__((address_space(3))) void *)(dst + (KB + j) * 64),
-                                             16, 0, 0);
+                                             16, 0, 2);   // 2: non-temporal
         }
     };
 
