@@ -43,9 +43,9 @@ METRIC = "verified tokens/sec + verify-step HBM GB/s (% peak), 27B-shape dense, 
 # figures hold for the GEMM source they were taken on; any other source reports null.
 PMC_TRAFFIC = {
     "block": {"source": "tree_verification_skinny_amd/csrc/k_gemm.hip",
-              "sha256": "762a813240ecff179ec1d7b1bf5d0cbfd68c0dc7c3e98efcd3828a9d3220b313",
-              "fetch_kib": 174932.523, "write_kib": 544.0,
-              "fetch_scale": 1.9999851, "write_scale": 1.0},
+              "sha256": "5dd564c0f7d3bc3c02f248c9b8d10cef9516f5022e86fe14df34c5ed46cfb7a7",
+              "fetch_kib": 174756.305, "write_kib": 544.0,
+              "fetch_scale": 1.9999858, "write_scale": 1.0},
 }
 HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0     # dense bf16 matrix-core peak of MI355X
