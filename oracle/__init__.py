@@ -69,6 +69,14 @@ def lib():
             build(force=True)
         L = ctypes.CDLL(_LIB)
         L.orc_max_threads.restype = ctypes.c_int
+        _u8p = ctypes.POINTER(ctypes.c_uint8)
+        _i64p = ctypes.POINTER(ctypes.c_int64)
+        L.orc_w12_base.argtypes = [_u16p, ctypes.c_int64]
+        L.orc_w12_base.restype = ctypes.c_int
+        L.orc_w12_encode.argtypes = [_u16p, ctypes.c_int64, ctypes.c_int, _u8p, _u8p, _u8p]
+        L.orc_w12_encode.restype = ctypes.c_int64
+        L.orc_w12_decode.argtypes = [_u8p, _u8p, ctypes.c_int64, ctypes.c_int, _i64p, _u16p,
+                                     ctypes.c_int64, _u16p]
         L.orc_f32_to_bf16.argtypes = [_f32p, _u16p, ctypes.c_int64]
         L.orc_bf16_to_f32.argtypes = [_u16p, _f32p, ctypes.c_int64]
         L.orc_tree_depth.argtypes = [_i32p, ctypes.c_int, _i32p]
@@ -389,3 +397,51 @@ def ar_greedy(model: Model, k_ctx, v_ctx, first_token: int, n: int):
         tok = int(r.arg[0])
         toks.append(tok)
     return np.array(toks, np.int32), np.stack(lgs), k_ctx, v_ctx
+
+
+# ---- W12: lossless 12-bit weight storage ---------------------------------------------------------
+# The SpecPilot digest (airadar.tv — "Reasons") names a lossless 12-bit format that splits each
+# bf16 weight into three 4-bit planes reassembled in the GEMM's registers. The reading (the planes'
+# contents, the per-matrix exponent window, the exception list) is written out in
+# specverify_oracle.c.
+
+@dataclass
+class W12:
+    base: int                 # even exponent-window base b: fields b..b+15 fit
+    lo: np.ndarray            # uint8 [n]: planes 1 and 0 (the value's low byte)
+    nib: np.ndarray           # uint8 [n]: plane 2, (sign, (e - b) >> 1); 0 for an exception
+    esc_idx: np.ndarray       # int64 [n_esc]: flat indices of the exceptions, ascending
+    esc_val: np.ndarray       # uint16 [n_esc]: their bf16 bit patterns
+
+
+def w12_base(w: np.ndarray) -> int:
+    w = _c(w.reshape(-1), np.uint16)
+    return int(lib().orc_w12_base(_p(w, _u16p), w.size))
+
+
+def w12_encode(w: np.ndarray, base: Optional[int] = None) -> W12:
+    """Planes and exception list of a bf16 array (uint16 bit patterns), flattened in C order."""
+    w = _c(w.reshape(-1), np.uint16)
+    b = w12_base(w) if base is None else int(base)
+    u8 = ctypes.POINTER(ctypes.c_uint8)
+    lo = np.empty(w.size, np.uint8)
+    nib = np.empty(w.size, np.uint8)
+    esc = np.empty(w.size, np.uint8)
+    lib().orc_w12_encode(_p(w, _u16p), w.size, b, lo.ctypes.data_as(u8), nib.ctypes.data_as(u8),
+                         esc.ctypes.data_as(u8))
+    idx = np.flatnonzero(esc).astype(np.int64)
+    return W12(b, lo, nib, idx, w[idx].copy())
+
+
+def w12_decode(c: W12) -> np.ndarray:
+    """The bf16 bit patterns (flat, uint16) the planes and exceptions stand for."""
+    u8 = ctypes.POINTER(ctypes.c_uint8)
+    lo = _c(c.lo, np.uint8)
+    nib = _c(c.nib, np.uint8)
+    idx = _c(c.esc_idx, np.int64)
+    val = _c(c.esc_val, np.uint16)
+    out = np.empty(lo.size, np.uint16)
+    lib().orc_w12_decode(lo.ctypes.data_as(u8), nib.ctypes.data_as(u8), lo.size, c.base,
+                         idx.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), _p(val, _u16p), idx.size,
+                         _p(out, _u16p))
+    return out

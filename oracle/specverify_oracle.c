@@ -376,3 +376,76 @@ int orc_accept(const int32_t *tok, const int32_t *parent, const int32_t *arg, in
     free(ok);
     return 0;
 }
+
+/* ------------------------------------------------------------------------------------------ */
+/* W12: lossless 12-bit storage of bf16 weights                                               */
+/* ------------------------------------------------------------------------------------------ */
+/*
+ * The SpecPilot digest (airadar.tv — "Reasons") names a lossless 12-bit weight format, W12:
+ * each bf16 weight is split into three 4-bit planes that the GEMM reassembles bit for bit in
+ * registers. The pages give neither the planes' contents nor how values that do not fit are
+ * kept. The reading implemented here:
+ *   - a bf16 value is (sign s, exponent field e of 8 bits, mantissa m of 7 bits);
+ *   - a matrix has one window of 16 consecutive exponent fields [b, b + 15], b even, b <= 240;
+ *   - plane 0 holds bits 3..0 (mantissa low bits), plane 1 bits 7..4 (e's lowest bit and the
+ *     mantissa's top three), plane 2 holds (s, (e - b) >> 1): since b is even, e >> 1 equals
+ *     b / 2 + ((e - b) >> 1), so the upper byte of the value comes back with one add;
+ *   - a value whose exponent field lies outside the window is an exception: its planes carry
+ *     the low byte and a zero nibble, and its full 16 bits are kept in a separate list.
+ * The window is the one that leaves the fewest exceptions (lowest b on ties).
+ */
+
+static int w12_in_window(uint16_t v, int b) {
+    const int e = (v >> 7) & 0xff;
+    return e >= b && e <= b + 15;
+}
+
+/* The even window base b in [0, 240] with the most values inside [b, b + 15]. */
+int orc_w12_base(const uint16_t *w, int64_t n) {
+    int64_t hist[256];
+    memset(hist, 0, sizeof(hist));
+    for (int64_t i = 0; i < n; ++i) hist[(w[i] >> 7) & 0xff] += 1;
+    int best_b = 0;
+    int64_t best = -1;
+    for (int b = 0; b <= 240; b += 2) {
+        int64_t c = 0;
+        for (int e = b; e <= b + 15; ++e) c += hist[e];
+        if (c > best) {
+            best = c;
+            best_b = b;
+        }
+    }
+    return best_b;
+}
+
+/* Planes of n values for window base b: lo[i] = planes 1 and 0 (the low byte), nib[i] = plane
+ * 2; esc[i] = 1 for an exception (then nib[i] = 0). Returns the number of exceptions. */
+int64_t orc_w12_encode(const uint16_t *w, int64_t n, int b, uint8_t *lo, uint8_t *nib, uint8_t *esc) {
+    int64_t ne = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        const uint16_t v = w[i];
+        lo[i] = (uint8_t)(v & 0xff);
+        if (w12_in_window(v, b)) {
+            const int e = (v >> 7) & 0xff;
+            nib[i] = (uint8_t)(((v >> 15) << 3) | ((e - b) >> 1));
+            esc[i] = 0;
+        } else {
+            nib[i] = 0;
+            esc[i] = 1;
+            ne += 1;
+        }
+    }
+    return ne;
+}
+
+/* bf16 values back from the planes; then the exceptions (element index, 16-bit value) are put
+ * in place. */
+void orc_w12_decode(const uint8_t *lo, const uint8_t *nib, int64_t n, int b,
+                    const int64_t *esc_idx, const uint16_t *esc_val, int64_t n_esc, uint16_t *out) {
+    for (int64_t i = 0; i < n; ++i) {
+        const int s = nib[i] >> 3;
+        const int hi = (b >> 1) + (nib[i] & 7);     /* e >> 1 */
+        out[i] = (uint16_t)((s << 15) | (hi << 8) | lo[i]);
+    }
+    for (int64_t j = 0; j < n_esc; ++j) out[esc_idx[j]] = esc_val[j];
+}
