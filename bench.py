@@ -10,6 +10,9 @@ Workloads (--config):
   block   (default) batch 1, linear block of 16 uniform-random draft tokens, context 4096
   tree    batch 1, 64-node draft tree of depth <= 10, context 8192
   batched 32 requests x block of 16, contexts uniform in [512, 8192], shuffled 16-token pages
+--weights w12 stores the projections and the output head in the lossless 12-bit layout (batch-1
+workloads only); the results are bit-identical to bf16 and the step streams a quarter fewer
+weight bytes.
 
 Prints one JSON line: verified draft tokens/s (batch * k / step time), the step's algorithmic
 HBM bytes and GB/s, the roofline of the dominant kernel (the gate/up projection GEMM with its
@@ -67,7 +70,7 @@ def workload(name):
     raise ValueError(name)
 
 
-def build_model(shape, device):
+def build_model(shape, device, w12=False):
     t0 = time.time()
     layers = [synth.layer_weights(shape, SEED, l, device) for l in range(shape.n_layers)]
     embed = synth.randn_bf16((shape.vocab, shape.hidden), 0.02, device, SEED, "embed")
@@ -75,19 +78,26 @@ def build_model(shape, device):
     fn = torch.ones(shape.hidden, dtype=torch.bfloat16, device=device)
     torch.cuda.synchronize()
     log(f"weights generated on the GPU in {time.time() - t0:.1f}s")
-    w = tv.Weights(tv.ModelCfg.of(shape), embed, fn, lm, layers)   # packs the projections once
+    # packs the projections once (bf16 fragment order, or the lossless 12-bit layout)
+    w = tv.Weights(tv.ModelCfg.of(shape), embed, fn, lm, layers, w12=w12)
     torch.cuda.synchronize()
-    log(f"projection weights packed in {time.time() - t0:.1f}s")
+    log(f"projection weights packed ({'W12' if w12 else 'bf16'}) in {time.time() - t0:.1f}s")
     return w
 
 
-def step_bytes(shape, batch, k, ctx):
+def step_bytes(shape, batch, k, ctx, w12=None):
     """Algorithmic HBM bytes of one verify step: every weight once (embedding rows only for the
-    tokens), every context K/V row once per layer, the draft rows' K/V writes."""
+    tokens), every context K/V row once per layer, the draft rows' K/V writes. With W12 weights
+    (w12: the Weights.w12 dict) the projections and the output head count their W12 bytes:
+    12 bits per value, the per-tile exception offsets and the exceptions."""
     H, F, V, L = shape.hidden, shape.ffn, shape.vocab, shape.n_layers
     d, nq, nkv = shape.head_dim, shape.n_q_heads, shape.n_kv_heads
-    per_layer_w = 2 * (shape.qkv_rows * H + H * nq * d + 2 * F * H + H * F + 2 * H)
-    weights = L * per_layer_w + 2 * (V * H + H) + 2 * batch * k * H
+    if w12 is None:
+        per_layer_w = 2 * (shape.qkv_rows * H + H * nq * d + 2 * F * H + H * F + 2 * H)
+        weights = L * per_layer_w + 2 * (V * H + H) + 2 * batch * k * H
+    else:
+        proj = sum(m.nbytes() for lw in w12["layers"] for m in lw.values()) + w12["lm_head"].nbytes()
+        weights = proj + L * 2 * 2 * H + 2 * H + 2 * batch * k * H
     kv_read = L * sum(c for c in ctx) * nkv * d * 2 * 2
     kv_write = L * batch * k * nkv * d * 2 * 2
     return weights + kv_read + kv_write
@@ -103,11 +113,14 @@ def step_flops(shape, batch, k, ctx, depth_mean):
     return gemm + attn
 
 
-def gate_up_bytes(shape, m):
-    """Algorithmic HBM bytes of one gate/up projection launch: the packed [2F][H] weight once, the
-    normalised activations [m][H] in, the SwiGLU output [m][F] out (bf16)."""
+def gate_up_bytes(shape, m, w12=None):
+    """Algorithmic HBM bytes of one gate/up projection launch: the packed [2F][H] weight once (its
+    W12 bytes, averaged over the layers, with W12 weights), the normalised activations [m][H] in,
+    the SwiGLU output [m][F] out (bf16)."""
     H, F = shape.hidden, shape.ffn
-    return 2 * (2 * F * H) + 2 * m * H + 2 * m * F
+    wb = 2 * (2 * F * H) if w12 is None else \
+        sum(lw["w_gate_up"].nbytes() for lw in w12["layers"]) / len(w12["layers"])
+    return wb + 2 * m * H + 2 * m * F
 
 
 def time_gate_up(step_with_events, events, n_layers, stream, reps):
@@ -237,6 +250,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
+    ap.add_argument("--weights", default="bf16", choices=["bf16", "w12"],
+                    help="projection weight storage: bf16, or the lossless 12-bit layout (W12)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the verify step of "
@@ -250,7 +265,12 @@ def main():
     wl = workload(args.config)
     B, K, ctx = wl["batch"], wl["k"], wl["ctx"]
     total_steps = args.steps + args.warmup + 3 + 12     # + the kernel-timing replays
-    weights = build_model(shape, device)
+    w12 = args.weights == "w12"
+    if w12 and B * K > 64:
+        print("W12 weights serve passes of at most 64 rows (batch 1); use --weights bf16 for the "
+              "batched workload", file=sys.stderr)
+        sys.exit(2)
+    weights = build_model(shape, device, w12)
 
     # cache: room for the context, the draft, and every step's commit (at most K rows each)
     pages = [(c + K + K * total_steps + 15) // 16 for c in ctx]
@@ -318,7 +338,7 @@ def main():
     ms = marks[0].elapsed_time(marks[-1]) / args.steps
     per_step = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)])
     ctx_now = t_ctx.cpu().tolist()
-    nbytes = step_bytes(shape, B, K, ctx)
+    nbytes = step_bytes(shape, B, K, ctx, weights.w12)
     flops = step_flops(shape, B, K, ctx, depth_mean)
     value = B * K / (ms / 1e3)
     gbps = nbytes / (ms / 1e3) / 1e9
@@ -336,7 +356,8 @@ def main():
                                 "batched": "27B-shape dense, 64 layers + lm_head, 32 requests x "
                                            "block of 16, contexts U[512,8192], paged"}[args.config],
                    "batch": B, "k": K, "ctx_mean": float(np.mean(ctx)), "layers": shape.n_layers,
-                   "vocab": shape.vocab, "hip_graph": not args.eager, "parallelism": "single GPU"},
+                   "vocab": shape.vocab, "hip_graph": not args.eager, "parallelism": "single GPU",
+                   "weights": "W12 (lossless 12-bit)" if w12 else "bf16"},
         "hbm": {"bytes_per_step": nbytes, "achieved_gbps": round(gbps, 1),
                 "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4)},
         "mfma": {"flops_per_step": flops, "tflops": round(flops / (ms / 1e3) / 1e12, 2),
@@ -361,8 +382,8 @@ def main():
             s_launch, ms_ev = time_gate_up(lambda: step(handles), events, L, stream,
                                            max(3, min(args.steps, 10)))
         t_ctx.copy_(ctx0)
-        b_launch = gate_up_bytes(shape, B * K)
-        traffic = pmc_traffic(args.config)
+        b_launch = gate_up_bytes(shape, B * K, weights.w12)
+        traffic = None if w12 else pmc_traffic(args.config)
         if args.config == "batched":
             # hundreds of rows: the tile kernel is bound by the matrix cores, not by HBM
             flops = 2 * B * K * (2 * shape.ffn) * shape.hidden
@@ -374,7 +395,9 @@ def main():
                                   "flops_per_launch": int(flops), "bytes_per_launch": int(b_launch)}
         else:
             ach = b_launch / s_launch / 1e9
-            kname = "gemm_kernel" if B * K <= 16 else "gemm_wide_kernel"
+            kname = "gemm_kernel" if B * K <= 16 or w12 else "gemm_wide_kernel"
+            if w12:
+                kname += " over W12 weights"
             result["roofline"] = {"kernel": f"{kname}, SwiGLU epilogue (gate/up projection)",
                                   "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS,
                                   "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),

@@ -73,12 +73,33 @@ typedef struct {
     const void *attn_norm, *w_qkv, *w_o, *mlp_norm, *w_gate_up, *w_down;
 } spec_layer_weights;
 
+/* One projection matrix [n][kd] in W12, the lossless 12-bit layout built by spec_w12_plan and
+ * spec_w12_pack (DEVICE pointers): planes (n*kd*3/2 bytes), plan (spec_w12_plan_ints ints),
+ * exc (2 ints per exception). */
+typedef struct {
+    const void *planes;
+    const int32_t *plan;
+    const int32_t *exc;
+} spec_w12_matrix;
+
+typedef struct {
+    spec_w12_matrix w_qkv, w_o, w_gate_up, w_down;
+} spec_w12_layer;
+
 typedef struct {
     spec_model_cfg cfg;
     const spec_layer_weights *layers;   /* HOST array of cfg.n_layers entries */
     const void *embed;                  /* bf16 [V][H], row-major */
     const void *final_norm;             /* bf16 [H] */
-    const void *lm_head;                /* bf16 [V][H], packed (spec_pack_weight) */
+    const void *lm_head;                /* bf16 [V][H], packed (spec_pack_weight); may be NULL
+                                           when w12_lm_head.planes is set */
+    /* Optional W12 projections. w12_layers: HOST array of cfg.n_layers entries or NULL; when
+     * set, the four projections of every layer are streamed from it and the w_qkv, w_o,
+     * w_gate_up and w_down members of `layers` are ignored (they may be NULL). w12_lm_head:
+     * used when its planes member is set. W12 needs batch * k <= 64 (SPEC_EUNSUPPORTED
+     * otherwise). The results are bit-identical to the bf16 pass over the same weights. */
+    const spec_w12_layer *w12_layers;
+    spec_w12_matrix w12_lm_head;
 } spec_weights;
 
 /* Paged KV cache, bf16. A page holds SPEC_PAGE_SIZE consecutive positions of one request.
@@ -186,6 +207,42 @@ int spec_skinny_gemm(const void *x, int m, int kd, const void *w, int n, float *
  * against. buf must be 16-byte aligned and bytes a multiple of 16; returns SPEC_EINVAL
  * otherwise. Enqueued on `stream`. */
 int spec_read_probe(const void *buf, size_t bytes, uint32_t *out, hipStream_t stream);
+
+/* ---- W12: lossless 12-bit weights -------------------------------------------------------------
+ * The SpecPilot digest (airadar.tv — "Reasons") names a lossless 12-bit weight format: every
+ * bf16 weight split into three 4-bit planes that the GEMM rebuilds bit for bit in registers, so
+ * that a weight-bound batch-1 pass streams a quarter fewer bytes. The pages fix neither the
+ * planes' contents nor what happens to values that do not fit; this library's layout:
+ *   - one window of 16 exponent fields [b, b+15] per matrix, b even (0..240), the one that
+ *     leaves the fewest values outside (lowest b on ties);
+ *   - planes 0 and 1: the value's low byte (mantissa, lowest exponent bit), as is; plane 2: the
+ *     nibble (sign, (e - b) >> 1);
+ *   - a value outside the window is an exception: its planes hold its low byte and a zero
+ *     nibble, and exc holds (position, bf16 bits) pairs sorted by tile, then position, where
+ *     position = s * 512 + l * 8 + j for value j of slot l of step s (the slots of
+ *     spec_pack_weight's order);
+ *   - planes: fragment (tile t, step s) of spec_pack_weight's order is 768 bytes at
+ *     (t * (kd/32) + s) * 768: 64 dwords of the slots' low bytes of values 0..3 (byte j =
+ *     value j), 64 dwords of values 4..7, 64 dwords of nibbles (value 2i at bits 4i..4i+3,
+ *     value 2i+1 at bits 16+4i..16+4i+3);
+ *   - plan (int32): [0] b, [1] exception count E, [2 .. 2 + n/16] per-tile exception offsets
+ *     (exclusive prefix, n/16 + 1 entries), then 256 ints of scratch.
+ * The format pays where the window holds nearly every weight (about 1e-4 of N(0, 0.02) weights
+ * are exceptions); read plan[1] after spec_w12_plan to decide, and to size exc (2*E ints).
+ * Needs n % 16 == 0 and kd % 32 == 0. One-time, load-time transforms, enqueued on `stream`. */
+int spec_w12_plan_ints(int n, int kd, size_t *ints /* HOST */);
+int spec_w12_plan(const void *w /* bf16 [n][kd] row-major */, int n, int kd, int32_t *plan,
+                  hipStream_t stream);
+int spec_w12_pack(const void *w /* bf16 [n][kd] row-major */, int n, int kd, const int32_t *plan,
+                  void *planes, int32_t *exc, hipStream_t stream);
+
+/* spec_skinny_gemm over a W12 matrix: the same partials, bit for bit, as spec_skinny_gemm over
+ * the bf16 matrix it encodes whenever both use the same split (always for m <= 16; above 16
+ * rows spec_skinny_gemm switches to its wide variant while W12 keeps the skinny one). The split
+ * count may differ from spec_skinny_gemm's above 16 rows; partial_bytes as spec_skinny_gemm_bytes
+ * gives covers both. */
+int spec_skinny_gemm_w12(const void *x, int m, int kd, const spec_w12_matrix *w, int n,
+                         float *partials, size_t partial_bytes, int *splits, hipStream_t stream);
 
 /* Static text for a return code. */
 const char *spec_strerror(int code);

@@ -22,7 +22,7 @@ def declared_functions():
     for h in HEADERS:
         text = open(h).read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-        for m in re.finditer(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\**\s*(spec_[a-z_]+)\s*\(",
+        for m in re.finditer(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\**\s*(spec_[a-z0-9_]+)\s*\(",
                              text, flags=re.M):
             names.add(m.group(1))
     return names
@@ -151,3 +151,45 @@ def test_commit_and_accept_reject_bad_arguments():
     args_k = list(args)
     args_k[4] = 65
     assert L.spec_accept(*args_k, 0x100000, 1 << 30, None) == tv.SPEC_EUNSUPPORTED
+
+
+def test_w12_entry_points_reject_bad_arguments():
+    L = tv.lib()
+    fake = 0x10000
+    n = ctypes.c_size_t(0)
+    assert L.spec_w12_plan_ints(64, 64, ctypes.byref(n)) == tv.SPEC_OK
+    assert n.value == 2 + 64 // 16 + 1 + 256
+    assert L.spec_w12_plan_ints(20, 64, ctypes.byref(n)) == tv.SPEC_EUNSUPPORTED
+    assert L.spec_w12_plan_ints(64, 40, ctypes.byref(n)) == tv.SPEC_EUNSUPPORTED
+    assert L.spec_w12_plan_ints(0, 64, ctypes.byref(n)) == tv.SPEC_EINVAL
+    assert L.spec_w12_plan(None, 64, 64, fake, None) == tv.SPEC_EINVAL
+    assert L.spec_w12_plan(fake, 64, 64, None, None) == tv.SPEC_EINVAL
+    assert L.spec_w12_pack(fake, 64, 64, fake, None, fake, None) == tv.SPEC_EINVAL
+    assert L.spec_w12_pack(fake, 64, 64, fake, fake, None, None) == tv.SPEC_EINVAL
+    assert L.spec_w12_pack(fake, 64, 64, fake, fake + 4, fake, None) == tv.SPEC_EINVAL   # unaligned planes
+    sp = ctypes.c_int(0)
+    m = tv.W12MatrixC(fake, fake, None)
+    assert L.spec_skinny_gemm_w12(fake, 16, 64, ctypes.byref(m), 64, fake, 1 << 20, ctypes.byref(sp),
+                                  None) == tv.SPEC_EINVAL
+    m = tv.W12MatrixC(fake, fake, fake)
+    assert L.spec_skinny_gemm_w12(fake, 16, 64, ctypes.byref(m), 64, fake, 4, ctypes.byref(sp),
+                                  None) == tv.SPEC_EWORKSPACE
+
+
+def test_verify_w12_rejects_large_batches_and_missing_parts():
+    w, kv, keep = _fake_structs(TINY)
+    fake = 0x10000
+    ptrs = dict(tok=fake, par=None, ctx=fake, a=fake, b=fake, p=fake)
+    full = tv.W12MatrixC(fake, fake, fake)
+    lay = (tv.W12LayerC * TINY.n_layers)(*[tv.W12LayerC(full, full, full, full)
+                                           for _ in range(TINY.n_layers)])
+    w.w12_layers = ctypes.cast(lay, ctypes.POINTER(tv.W12LayerC))
+    need = tv.spec_workspace_bytes(TINY, 5, 16, 9)
+    assert _raw_verify(w, kv, ptrs, 5, 16, 0x100000, need) == tv.SPEC_EUNSUPPORTED   # 80 rows
+    lay[1].w_down = tv.W12MatrixC(fake, fake, None)
+    need = tv.spec_workspace_bytes(TINY, 1, 8, 9)
+    assert _raw_verify(w, kv, ptrs, 1, 8, 0x100000, need) == tv.SPEC_EINVAL
+    w.w12_layers = None
+    w.w12_lm_head = tv.W12MatrixC(None, fake, fake)   # planes unset: the bf16 head is used
+    w.lm_head = None
+    assert _raw_verify(w, kv, ptrs, 1, 8, 0x100000, need) == tv.SPEC_EINVAL

@@ -52,10 +52,19 @@ class LayerWeightsC(ctypes.Structure):
     _fields_ = [(k, ctypes.c_void_p) for k in LAYER_KEYS]
 
 
+class W12MatrixC(ctypes.Structure):
+    _fields_ = [("planes", ctypes.c_void_p), ("plan", ctypes.c_void_p), ("exc", ctypes.c_void_p)]
+
+
+class W12LayerC(ctypes.Structure):
+    _fields_ = [(k, W12MatrixC) for k in ("w_qkv", "w_o", "w_gate_up", "w_down")]
+
+
 class WeightsC(ctypes.Structure):
     _fields_ = [("cfg", ModelCfgC), ("layers", ctypes.POINTER(LayerWeightsC)),
                 ("embed", ctypes.c_void_p), ("final_norm", ctypes.c_void_p),
-                ("lm_head", ctypes.c_void_p)]
+                ("lm_head", ctypes.c_void_p), ("w12_layers", ctypes.POINTER(W12LayerC)),
+                ("w12_lm_head", W12MatrixC)]
 
 
 class KVCacheC(ctypes.Structure):
@@ -94,9 +103,15 @@ def lib() -> ctypes.CDLL:
         L.spec_skinny_gemm_bytes.argtypes = [i32, i32, i32, ctypes.POINTER(sz)]
         L.spec_skinny_gemm.argtypes = [vp, i32, i32, vp, i32, vp, sz, ctypes.POINTER(i32), vp]
         L.spec_read_probe.argtypes = [vp, sz, vp, vp]
+        L.spec_w12_plan_ints.argtypes = [i32, i32, ctypes.POINTER(sz)]
+        L.spec_w12_plan.argtypes = [vp, i32, i32, vp, vp]
+        L.spec_w12_pack.argtypes = [vp, i32, i32, vp, vp, vp, vp]
+        L.spec_skinny_gemm_w12.argtypes = [vp, i32, i32, ctypes.POINTER(W12MatrixC), i32, vp, sz,
+                                           ctypes.POINTER(i32), vp]
         for f in (L.spec_workspace_bytes, L.spec_verify, L.spec_commit_kv,
                   L.spec_accept_workspace_bytes, L.spec_accept, L.spec_skinny_gemm_bytes,
-                  L.spec_skinny_gemm, L.spec_pack_weight, L.spec_read_probe):
+                  L.spec_skinny_gemm, L.spec_pack_weight, L.spec_read_probe, L.spec_w12_plan_ints,
+                  L.spec_w12_plan, L.spec_w12_pack, L.spec_skinny_gemm_w12):
             f.restype = i32
         _lib = L
     return _lib
@@ -104,7 +119,8 @@ def lib() -> ctypes.CDLL:
 
 EXPORTED = ("spec_workspace_bytes", "spec_verify", "spec_commit_kv", "spec_accept_workspace_bytes",
             "spec_accept", "spec_pack_weight", "spec_skinny_gemm_bytes", "spec_skinny_gemm",
-            "spec_read_probe", "spec_strerror")
+            "spec_read_probe", "spec_w12_plan_ints", "spec_w12_plan", "spec_w12_pack",
+            "spec_skinny_gemm_w12", "spec_strerror")
 
 
 def spec_strerror(code: int) -> str:
@@ -166,19 +182,70 @@ def spec_pack_weight(w: torch.Tensor, out: Optional[torch.Tensor] = None, stream
     return out
 
 
+class W12Matrix:
+    """One projection matrix in the library's lossless 12-bit layout (spec_w12_plan, then
+    spec_w12_pack): planes (uint8, n*kd*3/2), plan (int32) and exceptions (int32 pairs)."""
+
+    def __init__(self, w: torch.Tensor, stream=None):
+        n, kd = w.shape
+        ints = ctypes.c_size_t(0)
+        _check(lib().spec_w12_plan_ints(n, kd, ctypes.byref(ints)), "spec_w12_plan_ints")
+        self.n, self.kd = n, kd
+        self.plan = torch.empty(ints.value, dtype=torch.int32, device=w.device)
+        _check(lib().spec_w12_plan(_ptr(w), n, kd, _ptr(self.plan), _stream(stream)), "spec_w12_plan")
+        self.n_exc = int(self.plan[1].item())          # waits for the plan
+        self.exc = torch.empty(max(2 * self.n_exc, 2), dtype=torch.int32, device=w.device)
+        self.planes = torch.empty(n * kd * 3 // 2, dtype=torch.uint8, device=w.device)
+        _check(lib().spec_w12_pack(_ptr(w), n, kd, _ptr(self.plan), _ptr(self.planes), _ptr(self.exc),
+                                   _stream(stream)), "spec_w12_pack")
+        self.c = W12MatrixC(_ptr(self.planes), _ptr(self.plan), _ptr(self.exc))
+
+    def nbytes(self) -> int:
+        """Bytes a pass streams: the planes, the per-tile offsets and the exceptions."""
+        return self.planes.numel() + 4 * (self.n // 16 + 1) + 8 * self.n_exc
+
+
+def spec_skinny_gemm_w12(x: torch.Tensor, w: W12Matrix, partials: torch.Tensor, stream=None) -> int:
+    """spec_skinny_gemm over a W12 matrix; returns the split count."""
+    m, kd = x.shape
+    splits = ctypes.c_int(0)
+    rc = lib().spec_skinny_gemm_w12(_ptr(x), m, kd, ctypes.byref(w.c), w.n, _ptr(partials),
+                                    partials.numel() * partials.element_size(), ctypes.byref(splits),
+                                    _stream(stream))
+    _check(rc, "spec_skinny_gemm_w12")
+    return splits.value
+
+
 class Weights:
     """Device weights and the C struct that points at them. The constructor takes row-major
     bf16 tensors and packs the projection matrices (and the output head) once; with
-    ``drop_rowmajor`` the row-major projection tensors are released after packing."""
+    ``drop_rowmajor`` the row-major projection tensors are released after packing. With
+    ``w12`` the projections and the output head are stored in the lossless 12-bit layout
+    instead (W12Matrix) and no bf16 copy of them is kept."""
 
     def __init__(self, cfg: ModelCfg, embed: torch.Tensor, final_norm: torch.Tensor,
                  lm_head: torch.Tensor, layers: Sequence[dict], packed: bool = False,
-                 drop_rowmajor: bool = False):
+                 drop_rowmajor: bool = False, w12: bool = False):
         if len(layers) != cfg.n_layers:
             raise ValueError("need one weight dict per layer")
         self.cfg = cfg
         self.rowmajor = None
-        if not packed:
+        self.w12 = None
+        self._w12_layers = None
+        w12_head = W12MatrixC(None, None, None)
+        if w12:
+            if packed:
+                raise ValueError("W12 weights are built from row-major tensors")
+            if not drop_rowmajor:
+                self.rowmajor = dict(lm_head=lm_head, layers=list(layers))
+            self.w12 = dict(lm_head=W12Matrix(lm_head),
+                            layers=[{k: W12Matrix(lw[k]) for k in PACKED_KEYS} for lw in layers])
+            self._w12_layers = (W12LayerC * cfg.n_layers)(
+                *[W12LayerC(*[m[k].c for k in PACKED_KEYS]) for m in self.w12["layers"]])
+            w12_head = self.w12["lm_head"].c
+            lm_head = None
+            layers = [{k: v for k, v in lw.items() if k not in PACKED_KEYS} for lw in layers]
+        elif not packed:
             if not drop_rowmajor:
                 self.rowmajor = dict(lm_head=lm_head, layers=list(layers))
             lm_head = spec_pack_weight(lm_head)
@@ -186,9 +253,11 @@ class Weights:
                       for lw in layers]
         self.tensors = dict(embed=embed, final_norm=final_norm, lm_head=lm_head, layers=list(layers))
         self._layers = (LayerWeightsC * cfg.n_layers)(
-            *[LayerWeightsC(*[_ptr(lw[k]) for k in LAYER_KEYS]) for lw in layers])
+            *[LayerWeightsC(*[_ptr(lw.get(k)) for k in LAYER_KEYS]) for lw in layers])
+        w12p = (ctypes.cast(self._w12_layers, ctypes.POINTER(W12LayerC)) if self._w12_layers is not None
+                else None)
         self.c = WeightsC(cfg.c(), ctypes.cast(self._layers, ctypes.POINTER(LayerWeightsC)),
-                          _ptr(embed), _ptr(final_norm), _ptr(lm_head))
+                          _ptr(embed), _ptr(final_norm), _ptr(lm_head), w12p, w12_head)
 
     @staticmethod
     def from_packed(cfg: ModelCfg, embed, final_norm, lm_head_packed, layers_packed) -> "Weights":

@@ -72,15 +72,78 @@ __device__ __forceinline__ int tile_col(int ng, int t, int F) {
     }
 }
 
+// ---- W12 weights (k_w12.hip) ----------------------------------------------------------------------
+// Lane l's three plane dwords of a fragment (low bytes of v0..v3, of v4..v7, and the nibbles) back
+// to its 8 bf16 values: a pair's low bytes by one byte permute, its high bytes as
+// (sign << 7) | (b/2 + nibble bits 0..2) from the pair's two nibbles shifted under them. cb holds
+// b/2 in both high bytes; b/2 + 7 <= 127, so the add never reaches the sign bit.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t w12_hi(uint32_t x, uint32_t cb) {
+    return ((x & 0x07000700u) + cb) | ((x & 0x08000800u) << 4);
+}
+
+__device__ __forceinline__ bf16x8 w12_decode(uint32_t l0, uint32_t l1, uint32_t h, uint32_t cb) {
+    u32x4 d;
+    d.x = __builtin_amdgcn_perm(0u, l0, 0x0c010c00u) | w12_hi((h << 8) & 0x0f000f00u, cb);
+    d.y = __builtin_amdgcn_perm(0u, l0, 0x0c030c02u) | w12_hi((h << 4) & 0x0f000f00u, cb);
+    d.z = __builtin_amdgcn_perm(0u, l1, 0x0c010c00u) | w12_hi(h & 0x0f000f00u, cb);
+    d.w = __builtin_amdgcn_perm(0u, l1, 0x0c030c02u) | w12_hi((h >> 4) & 0x0f000f00u, cb);
+    return __builtin_bit_cast(bf16x8, d);
+}
+
+// An exception (pos = step * 512 + lane * 8 + j, bf16 bits) written over value j of its lane.
+__device__ __forceinline__ bf16x8 w12_patch(bf16x8 a, int lane, int pos, int val) {
+    u32x4 d = __builtin_bit_cast(u32x4, a);
+    const int j = pos & 7;
+    const bool me = lane == ((pos >> 3) & 63);
+    const uint32_t sh = (uint32_t)(j & 1) * 16u;
+    const uint32_t m = 0xffffu << sh, nv = ((uint32_t)val & 0xffffu) << sh;
+    switch (j >> 1) {
+        case 0: d.x = me ? ((d.x & ~m) | nv) : d.x; break;
+        case 1: d.y = me ? ((d.y & ~m) | nv) : d.y; break;
+        case 2: d.z = me ? ((d.z & ~m) | nv) : d.z; break;
+        default: d.w = me ? ((d.w & ~m) | nv) : d.w; break;
+    }
+    return __builtin_bit_cast(bf16x8, d);
+}
+
+__device__ __forceinline__ uint32_t stream_load32(const uint32_t *p) { return __builtin_nontemporal_load(p); }
+
+// A wave's cursor into one tile's exception list: the next entry at or after the wave's step.
+struct W12Cursor {
+    int i, end, step;   // entry index, end of the tile's entries, step of entry i (INT_MAX: none)
+};
+
+__device__ __forceinline__ int w12_step_of(const int2 *exc, int i, int end) {
+    return i < end ? (exc[i].x >> 9) : 0x7fffffff;
+}
+
+// Apply the tile's exceptions that fall on step su (wave-uniform) to fragment a; entries of
+// earlier steps belong to the other waves of the workgroup and are skipped.
+__device__ __forceinline__ bf16x8 w12_fixup(bf16x8 a, W12Cursor &c, const int2 *exc, int su, int lane) {
+    while (c.step < su) {
+        ++c.i;
+        c.step = w12_step_of(exc, c.i, c.end);
+    }
+    while (c.step == su) {
+        const int2 e = exc[c.i];
+        a = w12_patch(a, lane, e.x, e.y);
+        ++c.i;
+        c.step = w12_step_of(exc, c.i, c.end);
+    }
+    return a;
+}
+
 template <int NT, int MT>
 struct Acc {
     floatx4 v[NT][MT];
 };
 
-template <int NT, int MT, int W, int EPI>
+template <int NT, int MT, int W, int EPI, bool W12>
 __global__ __launch_bounds__(64 * W) void gemm_kernel(GemmIn in, const bf16 *__restrict__ Wp,
-                                                      int N, int Kd, int n_groups, int ksteps,
-                                                      GemmEpi ep) {
+                                                      W12Ref w12, int N, int Kd, int n_groups,
+                                                      int ksteps, GemmEpi ep) {
     __shared__ floatx4 red[(W - 1) * NT * MT * 64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r16 = lane & 15, grp = lane >> 4;
@@ -93,10 +156,26 @@ __global__ __launch_bounds__(64 * W) void gemm_kernel(GemmIn in, const bf16 *__r
     const int m0 = in.m0;          // first global row of the chunk
 
     const bf16 *wp[NT];
+    const uint32_t *qp[NT];          // W12: lane's dword in the tile's first fragment
+    W12Cursor cur[NT];
+    uint32_t cb = 0;
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    if constexpr (W12) cb = (uint32_t)(w12.plan[0] >> 1) * 0x01000100u;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
         const int tile = tile_col<NT, EPI>(ng, t, ep.F) >> 4;
-        wp[t] = Wp + (((int64_t)tile * S) * 64 + lane) * 8;
+        if constexpr (W12) {
+            qp[t] = w12.planes + ((int64_t)tile * S) * 192 + lane;
+            cur[t].i = w12.plan[2 + tile];
+            cur[t].end = w12.plan[3 + tile];
+            cur[t].step = w12_step_of(w12.exc, cur[t].i, cur[t].end);
+            while (cur[t].step < s_begin + wv) {
+                ++cur[t].i;
+                cur[t].step = w12_step_of(w12.exc, cur[t].i, cur[t].end);
+            }
+        } else {
+            wp[t] = Wp + (((int64_t)tile * S) * 64 + lane) * 8;
+        }
     }
     // activation blocks of this chunk; blocks past the last one (MT rounds the chunk up) re-read
     // it, and their columns are never stored
@@ -115,13 +194,23 @@ __global__ __launch_bounds__(64 * W) void gemm_kernel(GemmIn in, const bf16 *__r
         for (int mt = 0; mt < MT; ++mt) acc.v[t][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
     constexpr int U = (NT * MT >= 8 || (W == 8 && NT * MT == 4)) ? 2 : 4;   // K steps per batch
-    int s = s_begin + wave;
+    int s = s_begin + wv;
     for (; s + W * (U - 1) < s_end; s += W * U) {
         bf16x8 a[U][NT], b[U][MT];
+        uint32_t r0[U][NT], r1[U][NT], rh[U][NT];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
 #pragma unroll
-            for (int t = 0; t < NT; ++t) a[u][t] = stream_load((const bf16x8 *)(wp[t] + (int64_t)(s + W * u) * 512));
+            for (int t = 0; t < NT; ++t) {
+                if constexpr (W12) {
+                    const uint32_t *f = qp[t] + (int64_t)(s + W * u) * 192;
+                    r0[u][t] = stream_load32(f);
+                    r1[u][t] = stream_load32(f + 64);
+                    rh[u][t] = stream_load32(f + 128);
+                } else {
+                    a[u][t] = stream_load((const bf16x8 *)(wp[t] + (int64_t)(s + W * u) * 512));
+                }
+            }
         }
 #pragma unroll
         for (int u = 0; u < U; ++u)
@@ -130,14 +219,27 @@ __global__ __launch_bounds__(64 * W) void gemm_kernel(GemmIn in, const bf16 *__r
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
-            for (int t = 0; t < NT; ++t)
+            for (int t = 0; t < NT; ++t) {
+                if constexpr (W12) {
+                    a[u][t] = w12_decode(r0[u][t], r1[u][t], rh[u][t], cb);
+                    if (s + W * u >= cur[t].step) a[u][t] = w12_fixup(a[u][t], cur[t], w12.exc, s + W * u, lane);
+                }
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) acc.v[t][mt] = mfma16x16x32(a[u][t], b[u][mt], acc.v[t][mt]);
+            }
     }
     for (; s < s_end; s += W) {
         bf16x8 a[NT], b[MT];
 #pragma unroll
-        for (int t = 0; t < NT; ++t) a[t] = stream_load((const bf16x8 *)(wp[t] + (int64_t)s * 512));
+        for (int t = 0; t < NT; ++t) {
+            if constexpr (W12) {
+                const uint32_t *f = qp[t] + (int64_t)s * 192;
+                a[t] = w12_decode(stream_load32(f), stream_load32(f + 64), stream_load32(f + 128), cb);
+                if (s >= cur[t].step) a[t] = w12_fixup(a[t], cur[t], w12.exc, s, lane);
+            } else {
+                a[t] = stream_load((const bf16x8 *)(wp[t] + (int64_t)s * 512));
+            }
+        }
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) b[mt] = *(const bf16x8 *)(xp[mt] + (int64_t)s * 512);
 #pragma unroll
@@ -421,50 +523,55 @@ static int mt_for(int m) { return m <= 16 ? 1 : (m <= 32 ? 2 : 4); }
 
 int gemm_groups(const GemmShape &g) { return g.N / (16 * g.nt); }
 
+// The weights: bf16 fragments (Wp) or, when w12.planes is set, a W12 matrix.
 template <int NT, int MT, int W, int EPI>
-static hipError_t launch(const GemmShape &g, const GemmIn &in, const bf16 *Wp, const GemmEpi &ep,
-                         hipStream_t st) {
+static hipError_t launch(const GemmShape &g, const GemmIn &in, const bf16 *Wp, const W12Ref &w12,
+                         const GemmEpi &ep, hipStream_t st) {
     const int steps = g.Kd >> 5;
     const int ks = (steps + g.splits - 1) / g.splits;
-    hipLaunchKernelGGL((gemm_kernel<NT, MT, W, EPI>), dim3(gemm_groups(g) * g.splits), dim3(64 * W), 0,
-                       st, in, Wp, g.N, g.Kd, gemm_groups(g), ks, ep);
+    if (w12.planes != nullptr)
+        hipLaunchKernelGGL((gemm_kernel<NT, MT, W, EPI, true>), dim3(gemm_groups(g) * g.splits), dim3(64 * W),
+                           0, st, in, Wp, w12, g.N, g.Kd, gemm_groups(g), ks, ep);
+    else
+        hipLaunchKernelGGL((gemm_kernel<NT, MT, W, EPI, false>), dim3(gemm_groups(g) * g.splits), dim3(64 * W),
+                           0, st, in, Wp, w12, g.N, g.Kd, gemm_groups(g), ks, ep);
     return hipGetLastError();
 }
 
 // Eight waves per workgroup (512 threads) leave each wave 256 registers, enough for up to four
 // 16x16 accumulator tiles without spilling; wider tiles stay at four waves.
 template <int NT, int MT, int EPI>
-static hipError_t by_waves(const GemmShape &g, const GemmIn &in, const bf16 *Wp, const GemmEpi &ep,
-                           hipStream_t st) {
+static hipError_t by_waves(const GemmShape &g, const GemmIn &in, const bf16 *Wp, const W12Ref &w12,
+                           const GemmEpi &ep, hipStream_t st) {
     switch (g.waves) {
-        case 4: return launch<NT, MT, 4, EPI>(g, in, Wp, ep, st);
+        case 4: return launch<NT, MT, 4, EPI>(g, in, Wp, w12, ep, st);
         case 8:
-            if constexpr (NT * MT <= 4) return launch<NT, MT, 8, EPI>(g, in, Wp, ep, st);
+            if constexpr (NT * MT <= 4) return launch<NT, MT, 8, EPI>(g, in, Wp, w12, ep, st);
             return hipErrorInvalidValue;
         default: return hipErrorInvalidValue;
     }
 }
 
 template <int EPI>
-static hipError_t by_tiles(const GemmShape &g, const GemmIn &in, const bf16 *Wp, const GemmEpi &ep,
-                           hipStream_t st) {
+static hipError_t by_tiles(const GemmShape &g, const GemmIn &in, const bf16 *Wp, const W12Ref &w12,
+                           const GemmEpi &ep, hipStream_t st) {
     const int mt = mt_for(in.M);
     if (g.nt == 4) {
-        if (mt == 1) return by_waves<4, 1, EPI>(g, in, Wp, ep, st);
-        if (mt == 2) return by_waves<4, 2, EPI>(g, in, Wp, ep, st);
-        return by_waves<4, 4, EPI>(g, in, Wp, ep, st);
+        if (mt == 1) return by_waves<4, 1, EPI>(g, in, Wp, w12, ep, st);
+        if (mt == 2) return by_waves<4, 2, EPI>(g, in, Wp, w12, ep, st);
+        return by_waves<4, 4, EPI>(g, in, Wp, w12, ep, st);
     }
     if (g.nt == 2) {
-        if (mt == 1) return by_waves<2, 1, EPI>(g, in, Wp, ep, st);
-        if (mt == 2) return by_waves<2, 2, EPI>(g, in, Wp, ep, st);
-        return by_waves<2, 4, EPI>(g, in, Wp, ep, st);
+        if (mt == 1) return by_waves<2, 1, EPI>(g, in, Wp, w12, ep, st);
+        if (mt == 2) return by_waves<2, 2, EPI>(g, in, Wp, w12, ep, st);
+        return by_waves<2, 4, EPI>(g, in, Wp, w12, ep, st);
     }
     if constexpr (EPI == EPI_SWIGLU) {
         return hipErrorInvalidValue;   // paired epilogue needs two tiles per group
     } else {
-        if (mt == 1) return by_waves<1, 1, EPI>(g, in, Wp, ep, st);
-        if (mt == 2) return by_waves<1, 2, EPI>(g, in, Wp, ep, st);
-        return by_waves<1, 4, EPI>(g, in, Wp, ep, st);
+        if (mt == 1) return by_waves<1, 1, EPI>(g, in, Wp, w12, ep, st);
+        if (mt == 2) return by_waves<1, 2, EPI>(g, in, Wp, w12, ep, st);
+        return by_waves<1, 4, EPI>(g, in, Wp, w12, ep, st);
     }
 }
 
@@ -480,6 +587,16 @@ static hipError_t launch_wide(const GemmShape &g, const GemmIn &in, const bf16 *
         default: hipLaunchKernelGGL((gemm_wide_kernel<4, EPI>), grid, block, 0, st, in, Wp, g.N, g.Kd, gemm_groups(g), ks, ep); break;
     }
     return hipGetLastError();
+}
+
+static hipError_t skinny(const GemmShape &g, int epi, const GemmIn &in, const bf16 *Wp, const W12Ref &w12,
+                         const GemmEpi &ep, hipStream_t st) {
+    switch (epi) {
+        case EPI_PARTIAL: return by_tiles<EPI_PARTIAL>(g, in, Wp, w12, ep, st);
+        case EPI_SWIGLU: return by_tiles<EPI_SWIGLU>(g, in, Wp, w12, ep, st);
+        case EPI_ARGMAX: return by_tiles<EPI_ARGMAX>(g, in, Wp, w12, ep, st);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t gemm(const GemmShape &g, int epi, const GemmIn &in_all, const bf16 *Wp,
@@ -505,13 +622,22 @@ hipError_t gemm(const GemmShape &g, int epi, const GemmIn &in_all, const bf16 *W
                 default: return hipErrorInvalidValue;
             }
         } else {
-            switch (epi) {
-                case EPI_PARTIAL: e = by_tiles<EPI_PARTIAL>(g, in, Wp, ep, st); break;
-                case EPI_SWIGLU: e = by_tiles<EPI_SWIGLU>(g, in, Wp, ep, st); break;
-                case EPI_ARGMAX: e = by_tiles<EPI_ARGMAX>(g, in, Wp, ep, st); break;
-                default: return hipErrorInvalidValue;
-            }
+            e = skinny(g, epi, in, Wp, W12Ref{}, ep, st);
         }
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+hipError_t gemm_w12(const GemmShape &g, int epi, const GemmIn &in_all, const W12Ref &w,
+                    const GemmEpi &ep, hipStream_t st) {
+    if (g.tc || g.wide || w.planes == nullptr) return hipErrorInvalidValue;
+    for (int m0 = 0; m0 < g.M; m0 += 64) {
+        GemmIn in = in_all;
+        in.M_total = g.M;
+        in.m0 = m0;
+        in.M = g.M - m0 < 64 ? g.M - m0 : 64;
+        const hipError_t e = skinny(g, epi, in, nullptr, w, ep, st);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
@@ -523,6 +649,8 @@ hipError_t gemm(const GemmShape &g, int epi, const GemmIn &in_all, const bf16 *W
 // register budget allows. Projections with few groups are split along K until about 640
 // workgroups stream (partials, added by a separate pass); projections with many groups run whole
 // and finish their epilogue in place. Eight waves when there are few groups or K splits.
+static GemmShape plan_skinny(int M, int N, int Kd, bool allow_split);
+
 GemmShape plan_gemm(int M, int N, int Kd, bool allow_split) {
     GemmShape g;
     g.M = M;
@@ -574,6 +702,19 @@ GemmShape plan_gemm(int M, int N, int Kd, bool allow_split) {
         }
         return g;
     }
+    return plan_skinny(M, N, Kd, allow_split);
+}
+
+GemmShape plan_gemm_w12(int M, int N, int Kd, bool allow_split) { return plan_skinny(M, N, Kd, allow_split); }
+
+static GemmShape plan_skinny(int M, int N, int Kd, bool allow_split) {
+    GemmShape g;
+    g.M = M;
+    g.N = N;
+    g.Kd = Kd;
+    g.wide = false;
+    g.tc = false;
+    const int steps = Kd / 32;
     const int mt = mt_for(M < 64 ? M : 64);
     g.nt = (N % 64 == 0) ? 4 : (N % 32 == 0 ? 2 : 1);
     if (mt == 4 && g.nt == 4) g.nt = 2;

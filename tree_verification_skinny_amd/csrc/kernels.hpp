@@ -41,10 +41,27 @@ struct GemmEpi {
     int *amax_idx;
 };
 
+// A projection matrix in W12 form (k_w12.hip): three 4-bit planes per value in fragment order,
+// the plan (window base, per-tile exception offsets) and the exception list.
+struct W12Ref {
+    const uint32_t *planes;
+    const int32_t *plan;
+    const int2 *exc;
+};
+int w12_plan_ints(int n);
+hipError_t w12_plan(const bf16 *w, int n, int kd, int32_t *plan, hipStream_t st);
+hipError_t w12_pack(const bf16 *w, int n, int kd, const int32_t *plan, uint32_t *planes, int2 *exc,
+                    hipStream_t st);
+
 int gemm_groups(const GemmShape &g);
 GemmShape plan_gemm(int M, int N, int Kd, bool allow_split);
 hipError_t gemm(const GemmShape &g, int epi, const GemmIn &in, const bf16 *Wp, const GemmEpi &ep,
                 hipStream_t st);
+// The skinny projection over a W12 matrix: the plan of plan_gemm_w12 (never the wide or tile
+// variants), bit-identical to gemm() over the same matrix in bf16 whenever the plans agree.
+GemmShape plan_gemm_w12(int M, int N, int Kd, bool allow_split);
+hipError_t gemm_w12(const GemmShape &g, int epi, const GemmIn &in, const W12Ref &w, const GemmEpi &ep,
+                    hipStream_t st);
 // Row-major [n][kd] -> fragment order; rows up to the next multiple of 16 are zero.
 hipError_t pack_weight(const bf16 *w, int n, int kd, bf16 *out, hipStream_t st);
 // The tile kernel for hundreds of rows (k_gemm_tc.hip): one launch covers all in.M_total rows,

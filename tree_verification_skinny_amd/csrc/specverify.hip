@@ -29,7 +29,8 @@ struct Plan {
     int L, H, nq, nkv, D, F, V;
     int qd, nqkv;
     GemmShape g_qkv, g_o, g_gu, g_down, g_lm;
-    int lm_groups;
+    GemmShape w_qkv, w_o, w_gu, w_down, w_lm;   // the same projections over W12 weights (M <= 64)
+    int lm_groups, lm_groups_w12;
     int attn_chunks;
     size_t o_depth, o_pos, o_status, o_anc, o_rope, o_x, o_u, o_q, o_attn, o_h, o_part, o_po,
         o_pml, o_amv, o_ami, total;
@@ -76,16 +77,23 @@ int make_plan(const spec_model_cfg *c, int B, int K, int max_pages, Plan &p) {
     p.g_lm = plan_gemm(M, p.V, p.H, false);
     if (p.g_gu.nt < 2) return SPEC_EUNSUPPORTED;
     p.lm_groups = gemm_groups(p.g_lm);
+    p.w_qkv = plan_gemm_w12(M, p.nqkv, p.H, true);
+    p.w_o = plan_gemm_w12(M, p.H, p.qd, true);
+    p.w_gu = plan_gemm_w12(M, 2 * p.F, p.H, false);
+    p.w_down = plan_gemm_w12(M, p.H, p.F, true);
+    p.w_lm = plan_gemm_w12(M, p.V, p.H, false);
+    p.lm_groups_w12 = gemm_groups(p.w_lm);
     const int64_t max_keys = (int64_t)max_pages * SPEC_PAGE_SIZE;
     p.attn_chunks = (int)((max_keys + kAttnChunk - 1) / kAttnChunk);
     const int group = p.nq / p.nkv;
     size_t part = 16;
-    for (const GemmShape *g : {&p.g_qkv, &p.g_o, &p.g_down}) {
+    for (const GemmShape *g : {&p.g_qkv, &p.g_o, &p.g_down, &p.w_qkv, &p.w_o, &p.w_down}) {
         const size_t b = (size_t)g->splits * M * g->N * sizeof(float);
         if (b > part) part = b;
     }
 
-    const int amax_groups = p.lm_groups > argmax_chunks(p.V) ? p.lm_groups : argmax_chunks(p.V);
+    int amax_groups = p.lm_groups > argmax_chunks(p.V) ? p.lm_groups : argmax_chunks(p.V);
+    if (p.lm_groups_w12 > amax_groups) amax_groups = p.lm_groups_w12;
     Carver cv;
     p.o_depth = cv.take(sizeof(int32_t) * M);
     p.o_pos = cv.take(sizeof(int32_t) * M);
@@ -110,6 +118,16 @@ int make_plan(const spec_model_cfg *c, int B, int K, int max_pages, Plan &p) {
 template <typename T>
 T *at(void *ws, size_t off) {
     return reinterpret_cast<T *>(static_cast<char *>(ws) + off);
+}
+
+bool w12_ok(const spec_w12_matrix &m) { return m.planes && m.plan && m.exc; }
+
+W12Ref w12_ref(const spec_w12_matrix &m) {
+    W12Ref r;
+    r.planes = static_cast<const uint32_t *>(m.planes);
+    r.plan = m.plan;
+    r.exc = reinterpret_cast<const int2 *>(m.exc);
+    return r;
 }
 
 #define SV_TRY(x)                                  \
@@ -151,18 +169,28 @@ int spec_verify(const spec_weights *w, const spec_kv_cache *kv, const int32_t *d
         accepted_len == nullptr || bonus_token == nullptr || accepted_path == nullptr ||
         workspace == nullptr)
         return SPEC_EINVAL;
-    if (w->layers == nullptr || w->embed == nullptr || w->final_norm == nullptr || w->lm_head == nullptr)
-        return SPEC_EINVAL;
+    if (w->layers == nullptr || w->embed == nullptr || w->final_norm == nullptr) return SPEC_EINVAL;
     if (kv->k_pool == nullptr || kv->v_pool == nullptr || kv->block_table == nullptr ||
         kv->n_pages < 1 || kv->max_pages_per_req < 1)
         return SPEC_EINVAL;
     Plan p;
     int rc = make_plan(&w->cfg, batch, k, kv->max_pages_per_req, p);
     if (rc != SPEC_OK) return rc;
+    const bool w12 = w->w12_layers != nullptr;
+    const bool w12_lm = w->w12_lm_head.planes != nullptr;
+    if ((w12 || w12_lm) && p.M > 64) return SPEC_EUNSUPPORTED;
+    if (!w12_lm && w->lm_head == nullptr) return SPEC_EINVAL;
+    if (w12_lm && !w12_ok(w->w12_lm_head)) return SPEC_EINVAL;
     for (int l = 0; l < p.L; ++l) {
         const spec_layer_weights &lw = w->layers[l];
-        if (!lw.attn_norm || !lw.w_qkv || !lw.w_o || !lw.mlp_norm || !lw.w_gate_up || !lw.w_down)
+        if (!lw.attn_norm || !lw.mlp_norm) return SPEC_EINVAL;
+        if (w12) {
+            const spec_w12_layer &q = w->w12_layers[l];
+            if (!w12_ok(q.w_qkv) || !w12_ok(q.w_o) || !w12_ok(q.w_gate_up) || !w12_ok(q.w_down))
+                return SPEC_EINVAL;
+        } else if (!lw.w_qkv || !lw.w_o || !lw.w_gate_up || !lw.w_down) {
             return SPEC_EINVAL;
+        }
     }
     if (workspace_bytes < p.total) return SPEC_EWORKSPACE;
     if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0) return SPEC_EINVAL;
@@ -230,39 +258,42 @@ int spec_verify(const spec_weights *w, const spec_kv_cache *kv, const int32_t *d
     aa.part_ml = at<float2>(workspace, p.o_pml);
     aa.out = attn;
 
+    // one projection: bf16 fragments, or the same matrix in W12
+    auto proj = [&](const GemmShape &gb, const GemmShape &gw, int epi, const GemmIn &in, const void *wb,
+                    const spec_w12_matrix *wq) -> hipError_t {
+        if (wq != nullptr) return gemm_w12(gw, epi, in, w12_ref(*wq), ep, stream);
+        return gemm(gb, epi, in, static_cast<const bf16 *>(wb), ep, stream);
+    };
+
     for (int l = 0; l < p.L; ++l) {
         const spec_layer_weights &lw = w->layers[l];
+        const spec_w12_layer *lq = w12 ? &w->w12_layers[l] : nullptr;
         bf16 *kl = k_pool + l * layer_stride;
         bf16 *vl = v_pool + l * layer_stride;
         // q, k, v = u . Wqkv^T (u = RMSNorm(x) * attn_norm); RoPE; K/V into the cache
-        SV_TRY(gemm(p.g_qkv, EPI_PARTIAL, operand(u), static_cast<const bf16 *>(lw.w_qkv), ep,
-                    stream));
-        SV_TRY(reduce_qkv(part, p.g_qkv.splits, ni, ctx_len, kv->block_table, kv->max_pages_per_req,
+        SV_TRY(proj(p.g_qkv, p.w_qkv, EPI_PARTIAL, operand(u), lw.w_qkv, lq ? &lq->w_qkv : nullptr));
+        SV_TRY(reduce_qkv(part, lq ? p.w_qkv.splits : p.g_qkv.splits, ni, ctx_len, kv->block_table, kv->max_pages_per_req,
                           p.B, p.K, p.nq, p.nkv, p.D, q, kl, vl, stream));
         aa.k_pool = kl;
         aa.v_pool = vl;
         SV_TRY(attention(aa, stream));
         // x += o . Wo^T; u = RMSNorm(x) * mlp_norm
-        SV_TRY(gemm(p.g_o, EPI_PARTIAL, operand(attn), static_cast<const bf16 *>(lw.w_o), ep,
-                    stream));
-        SV_TRY(reduce_resid_norm(part, p.g_o.splits, M, p.H, static_cast<const bf16 *>(lw.mlp_norm),
+        SV_TRY(proj(p.g_o, p.w_o, EPI_PARTIAL, operand(attn), lw.w_o, lq ? &lq->w_o : nullptr));
+        SV_TRY(reduce_resid_norm(part, lq ? p.w_o.splits : p.g_o.splits, M, p.H, static_cast<const bf16 *>(lw.mlp_norm),
                                  eps, x, u, nullptr, stream));
         // h = silu(u . Wgate^T) * (u . Wup^T)
         if (gu_events) SV_TRY(hipEventRecord(gu_events[2 * l], stream));
-        SV_TRY(gemm(p.g_gu, EPI_SWIGLU, operand(u), static_cast<const bf16 *>(lw.w_gate_up), ep,
-                    stream));
+        SV_TRY(proj(p.g_gu, p.w_gu, EPI_SWIGLU, operand(u), lw.w_gate_up, lq ? &lq->w_gate_up : nullptr));
         if (gu_events) SV_TRY(hipEventRecord(gu_events[2 * l + 1], stream));
         // x += h . Wdown^T; u = RMSNorm(x) * (next layer's attn_norm, or the final norm)
         const bf16 *next_gain = l + 1 < p.L ? static_cast<const bf16 *>(w->layers[l + 1].attn_norm)
                                             : static_cast<const bf16 *>(w->final_norm);
-        SV_TRY(gemm(p.g_down, EPI_PARTIAL, operand(h), static_cast<const bf16 *>(lw.w_down), ep,
-                    stream));
-        SV_TRY(reduce_resid_norm(part, p.g_down.splits, M, p.H, next_gain, eps, x, u,
+        SV_TRY(proj(p.g_down, p.w_down, EPI_PARTIAL, operand(h), lw.w_down, lq ? &lq->w_down : nullptr));
+        SV_TRY(reduce_resid_norm(part, lq ? p.w_down.splits : p.g_down.splits, M, p.H, next_gain, eps, x, u,
                                  trace ? trace + (int64_t)(l + 1) * M * p.H : nullptr, stream));
     }
-    SV_TRY(gemm(p.g_lm, EPI_ARGMAX, operand(u), static_cast<const bf16 *>(w->lm_head), ep,
-                stream));
-    SV_TRY(argmax_accept(amv, ami, p.lm_groups, draft_tokens, tree_parent, ni, p.B, p.K, greedy,
+    SV_TRY(proj(p.g_lm, p.w_lm, EPI_ARGMAX, operand(u), w->lm_head, w12_lm ? &w->w12_lm_head : nullptr));
+    SV_TRY(argmax_accept(amv, ami, w12_lm ? p.lm_groups_w12 : p.lm_groups, draft_tokens, tree_parent, ni, p.B, p.K, greedy,
                          accepted_len, bonus_token, accepted_path, stream));
     return SPEC_OK;
 }
@@ -286,10 +317,10 @@ int spec_commit_kv(const spec_model_cfg *cfg, const spec_kv_cache *kv, const int
     return SPEC_OK;
 }
 
-static int skinny_shape(int m, int n, int kd, GemmShape &g) {
+static int skinny_shape(int m, int n, int kd, GemmShape &g, bool w12 = false) {
     if (m < 1 || n < 1 || kd < 1) return SPEC_EINVAL;
     if (kd % 32 != 0 || n % 16 != 0) return SPEC_EUNSUPPORTED;
-    g = plan_gemm(m, n, kd, true);
+    g = w12 ? plan_gemm_w12(m, n, kd, true) : plan_gemm(m, n, kd, true);
     return SPEC_OK;
 }
 
@@ -312,10 +343,13 @@ static size_t skinny_total_bytes(const GemmShape &g, int m, int n, int kd) {
 
 int spec_skinny_gemm_bytes(int m, int n, int kd, size_t *bytes) {
     if (bytes == nullptr) return SPEC_EINVAL;
-    GemmShape g;
-    const int rc = skinny_shape(m, n, kd, g);
+    GemmShape g, gq;
+    int rc = skinny_shape(m, n, kd, g);
     if (rc != SPEC_OK) return rc;
-    *bytes = skinny_total_bytes(g, m, n, kd);
+    rc = skinny_shape(m, n, kd, gq, true);
+    if (rc != SPEC_OK) return rc;
+    const size_t a = skinny_total_bytes(g, m, n, kd), b = skinny_total_bytes(gq, m, n, kd);
+    *bytes = a > b ? a : b;
     return SPEC_OK;
 }
 
@@ -336,6 +370,63 @@ int spec_skinny_gemm(const void *x, int m, int kd, const void *w, int n, float *
     GemmEpi ep = {};
     ep.y = partials;
     SV_TRY(gemm(g, EPI_PARTIAL, in, static_cast<const bf16 *>(w), ep, stream));
+    return SPEC_OK;
+}
+
+int spec_skinny_gemm_w12(const void *x, int m, int kd, const spec_w12_matrix *w, int n,
+                         float *partials, size_t partial_bytes, int *splits, hipStream_t stream) {
+    if (x == nullptr || w == nullptr || partials == nullptr || splits == nullptr) return SPEC_EINVAL;
+    if (!w12_ok(*w)) return SPEC_EINVAL;
+    GemmShape g;
+    const int rc = skinny_shape(m, n, kd, g, true);
+    if (rc != SPEC_OK) return rc;
+    if (partial_bytes < skinny_total_bytes(g, m, n, kd)) return SPEC_EWORKSPACE;
+    if (reinterpret_cast<uintptr_t>(partials) % 256 != 0) return SPEC_EINVAL;
+    *splits = g.splits;
+    bf16 *xp = reinterpret_cast<bf16 *>(reinterpret_cast<char *>(partials) +
+                                        skinny_partial_bytes(g, m, n));
+    SV_TRY(pack_weight(static_cast<const bf16 *>(x), m, kd, xp, stream));
+    GemmIn in = {};
+    in.Xp = xp;
+    GemmEpi ep = {};
+    ep.y = partials;
+    SV_TRY(gemm_w12(g, EPI_PARTIAL, in, w12_ref(*w), ep, stream));
+    return SPEC_OK;
+}
+
+static int w12_shape(const void *w, int n, int kd) {
+    if (w == nullptr) return SPEC_EINVAL;
+    if (n < 1 || kd < 1) return SPEC_EINVAL;
+    if (n % 16 != 0 || kd % 32 != 0) return SPEC_EUNSUPPORTED;
+    if ((int64_t)kd * 16 > (1 << 30)) return SPEC_EUNSUPPORTED;   // positions fit an int32
+    return SPEC_OK;
+}
+
+int spec_w12_plan_ints(int n, int kd, size_t *ints) {
+    if (ints == nullptr) return SPEC_EINVAL;
+    int rc = w12_shape(ints, n, kd);
+    if (rc != SPEC_OK) return rc;
+    *ints = (size_t)w12_plan_ints(n);
+    return SPEC_OK;
+}
+
+int spec_w12_plan(const void *w, int n, int kd, int32_t *plan, hipStream_t stream) {
+    int rc = w12_shape(w, n, kd);
+    if (rc != SPEC_OK) return rc;
+    if (plan == nullptr) return SPEC_EINVAL;
+    SV_TRY(w12_plan(static_cast<const bf16 *>(w), n, kd, plan, stream));
+    return SPEC_OK;
+}
+
+int spec_w12_pack(const void *w, int n, int kd, const int32_t *plan, void *planes, int32_t *exc,
+                  hipStream_t stream) {
+    int rc = w12_shape(w, n, kd);
+    if (rc != SPEC_OK) return rc;
+    if (plan == nullptr || planes == nullptr || exc == nullptr) return SPEC_EINVAL;
+    if (reinterpret_cast<uintptr_t>(planes) % 16 != 0 || reinterpret_cast<uintptr_t>(exc) % 8 != 0)
+        return SPEC_EINVAL;
+    SV_TRY(w12_pack(static_cast<const bf16 *>(w), n, kd, plan, static_cast<uint32_t *>(planes),
+                    reinterpret_cast<int2 *>(exc), stream));
     return SPEC_OK;
 }
 
