@@ -222,9 +222,9 @@ int spec_read_probe(const void *buf, size_t bytes, uint32_t *out, hipStream_t st
  *     position = s * 512 + l * 8 + j for value j of slot l of step s (the slots of
  *     spec_pack_weight's order);
  *   - planes: fragment (tile t, step s) of spec_pack_weight's order is 768 bytes at
- *     (t * (kd/32) + s) * 768: 64 dwords of the slots' low bytes of values 0..3 (byte j =
- *     value j), 64 dwords of values 4..7, 64 dwords of nibbles (value 2i at bits 4i..4i+3,
- *     value 2i+1 at bits 16+4i..16+4i+3);
+ *     (t * (kd/32) + s) * 768, 12 bytes per slot l at 12 l: a dword of the low bytes of values
+ *     0..3 (byte j = value j), a dword of values 4..7, a dword of nibbles (value 2i at bits
+ *     4i..4i+3, value 2i+1 at bits 16+4i..16+4i+3);
  *   - plan (int32): [0] b, [1] exception count E, [2 .. 2 + n/16] per-tile exception offsets
  *     (exclusive prefix, n/16 + 1 entries), then 256 ints of scratch.
  * The format pays where the window holds nearly every weight (about 1e-4 of N(0, 0.02) weights

@@ -45,11 +45,12 @@ def with_exceptions(w: torch.Tensor, seed, frac=0.01, big=9.5) -> torch.Tensor:
 
 def unpack_w12(m: tv.W12Matrix) -> oracle.W12:
     """The logical planes and exception list of a W12 matrix, read back from the layout the
-    header documents (fragment order, three 256-byte planes per fragment)."""
+    header documents (fragment order, 12 bytes per slot: two dwords of low bytes, one of
+    nibbles)."""
     n, kd = m.n, m.kd
     S, T = kd // 32, n // 16
     plan = m.plan.cpu().numpy()
-    words = m.planes.cpu().numpy().view(np.uint32).reshape(T, S, 3, 64)
+    words = m.planes.cpu().numpy().view(np.uint32).reshape(T, S, 64, 3).transpose(0, 1, 3, 2)
     lo = np.empty((n, kd), np.uint8)
     nib = np.empty((n, kd), np.uint8)
     lane = np.arange(64)

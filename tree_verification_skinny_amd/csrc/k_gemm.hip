@@ -30,6 +30,13 @@
 // column l%16, the same K elements; it receives D rows 4*(l/16)..+3 of column l%16.
 #include "kernels.hpp"
 
+#ifndef SV_W12_U
+#define SV_W12_U 2                // K steps per batch over W12 weights, split-K projections
+#endif
+#ifndef SV_W12_U_WHOLE
+#define SV_W12_U_WHOLE 2          // the same for whole-K projections (SwiGLU, output head)
+#endif
+
 namespace sv {
 
 // ---- packing ------------------------------------------------------------------------------------
@@ -73,7 +80,7 @@ __device__ __forceinline__ int tile_col(int ng, int t, int F) {
 }
 
 // ---- W12 weights (k_w12.hip) ----------------------------------------------------------------------
-// Lane l's three plane dwords of a fragment (low bytes of v0..v3, of v4..v7, and the nibbles) back
+// Lane l's three dwords of a fragment (low bytes of v0..v3, of v4..v7, and the nibbles) back
 // to its 8 bf16 values: a pair's low bytes by one byte permute, its high bytes as
 // (sign << 7) | (b/2 + nibble bits 0..2) from the pair's two nibbles shifted under them. cb holds
 // b/2 in both high bytes; b/2 + 7 <= 127, so the add never reaches the sign bit.
@@ -156,7 +163,7 @@ __global__ __launch_bounds__(64 * W) void gemm_kernel(GemmIn in, const bf16 *__r
     const int m0 = in.m0;          // first global row of the chunk
 
     const bf16 *wp[NT];
-    const uint32_t *qp[NT];          // W12: lane's dword in the tile's first fragment
+    const uint32_t *qp[NT];          // W12: lane's 12 bytes in the tile's first fragment
     W12Cursor cur[NT];
     uint32_t cb = 0;
     const int wv = __builtin_amdgcn_readfirstlane(wave);
@@ -165,7 +172,7 @@ __global__ __launch_bounds__(64 * W) void gemm_kernel(GemmIn in, const bf16 *__r
     for (int t = 0; t < NT; ++t) {
         const int tile = tile_col<NT, EPI>(ng, t, ep.F) >> 4;
         if constexpr (W12) {
-            qp[t] = w12.planes + ((int64_t)tile * S) * 192 + lane;
+            qp[t] = w12.planes + ((int64_t)tile * S) * 192 + 3 * lane;
             cur[t].i = w12.plan[2 + tile];
             cur[t].end = w12.plan[3 + tile];
             cur[t].step = w12_step_of(w12.exc, cur[t].i, cur[t].end);
@@ -193,7 +200,10 @@ __global__ __launch_bounds__(64 * W) void gemm_kernel(GemmIn in, const bf16 *__r
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc.v[t][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    constexpr int U = (NT * MT >= 8 || (W == 8 && NT * MT == 4)) ? 2 : 4;   // K steps per batch
+    // K steps per batch; W12 fragments are 3/4 the bytes and need a deeper batch for the same
+    // bytes in flight per wave
+    constexpr int U16 = (NT * MT >= 8 || (W == 8 && NT * MT == 4)) ? 2 : 4;
+    constexpr int U = W12 ? (NT * MT >= 8 ? 2 : (EPI == EPI_PARTIAL ? SV_W12_U : SV_W12_U_WHOLE)) : U16;
     int s = s_begin + wv;
     for (; s + W * (U - 1) < s_end; s += W * U) {
         bf16x8 a[U][NT], b[U][MT];
@@ -205,8 +215,8 @@ __global__ __launch_bounds__(64 * W) void gemm_kernel(GemmIn in, const bf16 *__r
                 if constexpr (W12) {
                     const uint32_t *f = qp[t] + (int64_t)(s + W * u) * 192;
                     r0[u][t] = stream_load32(f);
-                    r1[u][t] = stream_load32(f + 64);
-                    rh[u][t] = stream_load32(f + 128);
+                    r1[u][t] = stream_load32(f + 1);
+                    rh[u][t] = stream_load32(f + 2);
                 } else {
                     a[u][t] = stream_load((const bf16x8 *)(wp[t] + (int64_t)(s + W * u) * 512));
                 }
@@ -234,7 +244,7 @@ __global__ __launch_bounds__(64 * W) void gemm_kernel(GemmIn in, const bf16 *__r
         for (int t = 0; t < NT; ++t) {
             if constexpr (W12) {
                 const uint32_t *f = qp[t] + (int64_t)s * 192;
-                a[t] = w12_decode(stream_load32(f), stream_load32(f + 64), stream_load32(f + 128), cb);
+                a[t] = w12_decode(stream_load32(f), stream_load32(f + 1), stream_load32(f + 2), cb);
                 if (s >= cur[t].step) a[t] = w12_fixup(a[t], cur[t], w12.exc, s, lane);
             } else {
                 a[t] = stream_load((const bf16x8 *)(wp[t] + (int64_t)s * 512));

@@ -14,11 +14,12 @@
 //     nibble, and (position, 16-bit value) goes into a per-matrix list sorted by tile, then
 //     position, which the GEMM applies in registers after decoding.
 // Physical order follows the bf16 fragment order (16-row tiles, 32-column steps): fragment
-// (tile t, step s) is 768 bytes at (t * S + s) * 768, three 256-byte planes of one dword per
-// lane. For lane l (row 16t + l%16, columns 32s + 8(l/16) .. +7, values v0..v7):
-//   dword l       = low bytes of v0..v3 (byte j = v_j),
-//   dword 64 + l  = low bytes of v4..v7,
-//   dword 128 + l = nibbles: v_{2i} at bits 4i..4i+3, v_{2i+1} at bits 16+4i..16+4i+3,
+// (tile t, step s) is 768 bytes at (t * S + s) * 768, 12 bytes per lane, so that one 12-byte
+// load per lane reads a whole fragment. For lane l (row 16t + l%16, columns 32s + 8(l/16) .. +7,
+// values v0..v7), at dword 3l of the fragment:
+//   dword 3l     = low bytes of v0..v3 (byte j = v_j),
+//   dword 3l + 1 = low bytes of v4..v7,
+//   dword 3l + 2 = nibbles: v_{2i} at bits 4i..4i+3, v_{2i+1} at bits 16+4i..16+4i+3,
 // so that one shift and mask put a pair's two nibbles under the high bytes of a bf16 pair.
 // An exception entry is (s * 512 + l * 8 + j, bf16 bits).
 //
@@ -138,10 +139,10 @@ __global__ __launch_bounds__(64) void w12_pack_kernel(const uint16_t *__restrict
             nib |= n4 << ((j & 1) ? 16 + 4 * (j >> 1) : 4 * (j >> 1));
             if (!fits) esc_mask |= 1 << j;
         }
-        uint32_t *f = planes + ((int64_t)tile * S + s) * 192;
-        f[lane] = lo0;
-        f[64 + lane] = lo1;
-        f[128 + lane] = nib;
+        uint32_t *f = planes + ((int64_t)tile * S + s) * 192 + 3 * lane;
+        f[0] = lo0;
+        f[1] = lo1;
+        f[2] = nib;
         const int cnt = __popc(esc_mask);
         // in-wave exclusive prefix of the counts
         int incl = cnt;
