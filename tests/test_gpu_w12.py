@@ -101,8 +101,10 @@ def test_w12_layout_matches_oracle_definition(n, kd, frac):
 
 @pytest.mark.parametrize("m,n,kd,frac", [(16, 7168, 5120, 0.0), (16, 5120, 17408, 1e-4),
                                          (16, 5120, 5120, 0.01), (1, 34816, 5120, 0.0),
-                                         (8, 1408, 256, 0.02), (7, 512, 256, 0.3), (3, 64, 32, 0.5)])
+                                         (8, 1408, 256, 0.02), (7, 512, 256, 0.3), (3, 64, 32, 0.5),
+                                         (16, 1024, 8192, 0.05), (5, 2048, 4096, 0.2)])
 def test_w12_gemm_bit_identical_to_bf16(m, n, kd, frac):
+    """Includes K splits that start thousands of exceptions into a tile (the cursor search)."""
     x = synth.randn_bf16((m, kd), 1.0, DEV, "w12x", m, n, kd)
     w = synth.randn_bf16((n, kd), 0.02, DEV, "w12w", m, n, kd)
     if frac:

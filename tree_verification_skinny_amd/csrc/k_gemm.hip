@@ -36,6 +36,9 @@
 #ifndef SV_W12_U_WHOLE
 #define SV_W12_U_WHOLE 2          // the same for whole-K projections (SwiGLU, output head)
 #endif
+#ifndef SV_W12_WHOLE_WAVES
+#define SV_W12_WHOLE_WAVES 8      // waves per workgroup of the whole-K projections over W12
+#endif
 
 namespace sv {
 
@@ -126,6 +129,19 @@ __device__ __forceinline__ int w12_step_of(const int2 *exc, int i, int end) {
     return i < end ? (exc[i].x >> 9) : 0x7fffffff;
 }
 
+// Place a cursor on the first of the tile's entries [i, end) at or after step s0. The wave's
+// 64 lanes test 64 entries per round (one round unless the split starts more than 64 entries
+// into the tile), instead of walking the list one dependent load at a time.
+__device__ __forceinline__ int w12_first_at(const int2 *exc, int i, int end, int s0, int lane, int st) {
+    while (true) {
+        const unsigned long long m = __ballot(st >= s0);
+        if (m != 0ull) return min(i + __ffsll((long long)m) - 1, end);
+        i += 64;
+        const int k = i + lane;
+        st = k < end ? (exc[k].x >> 9) : 0x7fffffff;
+    }
+}
+
 // Apply the tile's exceptions that fall on step su (wave-uniform) to fragment a; entries of
 // earlier steps belong to the other waves of the workgroup and are skipped.
 __device__ __forceinline__ bf16x8 w12_fixup(bf16x8 a, W12Cursor &c, const int2 *exc, int su, int lane) {
@@ -175,13 +191,22 @@ __global__ __launch_bounds__(64 * W) void gemm_kernel(GemmIn in, const bf16 *__r
             qp[t] = w12.planes + ((int64_t)tile * S) * 192 + 3 * lane;
             cur[t].i = w12.plan[2 + tile];
             cur[t].end = w12.plan[3 + tile];
-            cur[t].step = w12_step_of(w12.exc, cur[t].i, cur[t].end);
-            while (cur[t].step < s_begin + wv) {
-                ++cur[t].i;
-                cur[t].step = w12_step_of(w12.exc, cur[t].i, cur[t].end);
-            }
         } else {
             wp[t] = Wp + (((int64_t)tile * S) * 64 + lane) * 8;
+        }
+    }
+    if constexpr (W12) {
+        // cursors at the wave's first step: every tile's first 64 entries are tested at once
+        int st[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const int k = cur[t].i + lane;
+            st[t] = k < cur[t].end ? (w12.exc[k].x >> 9) : 0x7fffffff;
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            cur[t].i = w12_first_at(w12.exc, cur[t].i, cur[t].end, s_begin + wv, lane, st[t]);
+            cur[t].step = w12_step_of(w12.exc, cur[t].i, cur[t].end);
         }
     }
     // activation blocks of this chunk; blocks past the last one (MT rounds the chunk up) re-read
@@ -715,7 +740,13 @@ GemmShape plan_gemm(int M, int N, int Kd, bool allow_split) {
     return plan_skinny(M, N, Kd, allow_split);
 }
 
-GemmShape plan_gemm_w12(int M, int N, int Kd, bool allow_split) { return plan_skinny(M, N, Kd, allow_split); }
+// Over W12 weights the whole-K projections (gate/up, output head) may run a different wave count:
+// their workgroups all fit at once, so the bytes in flight are set by waves x batch depth.
+GemmShape plan_gemm_w12(int M, int N, int Kd, bool allow_split) {
+    GemmShape g = plan_skinny(M, N, Kd, allow_split);
+    if (!allow_split && g.waves == 8) g.waves = SV_W12_WHOLE_WAVES;
+    return g;
+}
 
 static GemmShape plan_skinny(int M, int N, int Kd, bool allow_split) {
     GemmShape g;
