@@ -244,6 +244,26 @@ int spec_w12_pack(const void *w /* bf16 [n][kd] row-major */, int n, int kd, con
 int spec_skinny_gemm_w12(const void *x, int m, int kd, const spec_w12_matrix *w, int n,
                          float *partials, size_t partial_bytes, int *splits, hipStream_t stream);
 
+/* ---- Prefill: a prompt's K/V ahead of the first verify step ----------------------------------
+ * Appends p prompt tokens per request to its committed context: writes their rotated keys and
+ * values into cache slots ctx_len .. ctx_len + p - 1 of every layer, returns the target's greedy
+ * token after the last prompt token (the root of the first verify step) and sets
+ * ctx_len += p on the device. A verify pass over a linear block computes exactly this for its
+ * nodes (each node attends to the committed context and the nodes before it), so the prompt
+ * runs through the verify kernels in chunks of up to SPEC_MAX_K positions, each chunk's K/V
+ * committed before the next chunk's pass; the drafted-block view of the pages
+ * [SpecPilot news piece, wireai.ir — "The main challenge"] with every block fully accepted.
+ *   prompt [batch][p] int32; ctx_len [batch] in/out; next_token [batch] out (-1 for a request
+ *   whose prompt holds a token outside the vocabulary or whose pages do not cover
+ *   ctx_len + p: its ctx_len is left where its last good chunk ended and its cache rows past it
+ *   are unspecified); last_logits [batch][vocab] fp32 or NULL: the last prompt position's
+ *   logits. Weights as for spec_verify (bf16 or W12). Errors as for spec_verify. */
+int spec_prefill_workspace_bytes(const spec_model_cfg *cfg, int batch, int max_pages_per_req,
+                                 int want_logits, size_t *bytes /* HOST */);
+int spec_prefill(const spec_weights *weights, const spec_kv_cache *kv, const int32_t *prompt,
+                 int32_t *ctx_len, int batch, int p, int32_t *next_token, float *last_logits,
+                 void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Static text for a return code. */
 const char *spec_strerror(int code);
 

@@ -193,3 +193,26 @@ def test_verify_w12_rejects_large_batches_and_missing_parts():
     w.w12_lm_head = tv.W12MatrixC(None, fake, fake)   # planes unset: the bf16 head is used
     w.lm_head = None
     assert _raw_verify(w, kv, ptrs, 1, 8, 0x100000, need) == tv.SPEC_EINVAL
+
+
+def test_prefill_rejects_bad_arguments():
+    L = tv.lib()
+    w, kv, keep = _fake_structs(TINY)
+    fake = 0x10000
+    n = ctypes.c_size_t(0)
+    c = TINY.c()
+    assert L.spec_prefill_workspace_bytes(ctypes.byref(c), 2, 9, 0, ctypes.byref(n)) == tv.SPEC_OK
+    need = n.value
+    assert need >= tv.spec_workspace_bytes(TINY, 2, 64, 9)
+    assert L.spec_prefill_workspace_bytes(ctypes.byref(c), 2, 9, 1, ctypes.byref(n)) == tv.SPEC_OK
+    assert n.value >= need + 2 * 64 * TINY.vocab * 4
+    args = lambda **k: [k.get("w", ctypes.byref(w)), k.get("kv", ctypes.byref(kv)), k.get("prompt", fake),
+                        k.get("ctx", fake), k.get("b", 2), k.get("p", 100), k.get("nt", fake), None,
+                        k.get("ws", 0x100000), k.get("wsb", need), None]
+    assert L.spec_prefill(*args(prompt=None)) == tv.SPEC_EINVAL
+    assert L.spec_prefill(*args(ctx=None)) == tv.SPEC_EINVAL
+    assert L.spec_prefill(*args(nt=None)) == tv.SPEC_EINVAL
+    assert L.spec_prefill(*args(p=0)) == tv.SPEC_EINVAL
+    assert L.spec_prefill(*args(b=0)) == tv.SPEC_EINVAL
+    assert L.spec_prefill(*args(wsb=need - 1)) == tv.SPEC_EWORKSPACE
+    assert L.spec_prefill(*args(ws=0x100010)) == tv.SPEC_EINVAL

@@ -108,6 +108,12 @@ def lib() -> ctypes.CDLL:
         L.spec_w12_pack.argtypes = [vp, i32, i32, vp, vp, vp, vp]
         L.spec_skinny_gemm_w12.argtypes = [vp, i32, i32, ctypes.POINTER(W12MatrixC), i32, vp, sz,
                                            ctypes.POINTER(i32), vp]
+        L.spec_prefill_workspace_bytes.argtypes = [ctypes.POINTER(ModelCfgC), i32, i32, i32,
+                                                   ctypes.POINTER(sz)]
+        L.spec_prefill.argtypes = [ctypes.POINTER(WeightsC), ctypes.POINTER(KVCacheC), vp, vp, i32, i32,
+                                   vp, vp, vp, sz, vp]
+        for f in (L.spec_prefill_workspace_bytes, L.spec_prefill):
+            f.restype = i32
         for f in (L.spec_workspace_bytes, L.spec_verify, L.spec_commit_kv,
                   L.spec_accept_workspace_bytes, L.spec_accept, L.spec_skinny_gemm_bytes,
                   L.spec_skinny_gemm, L.spec_pack_weight, L.spec_read_probe, L.spec_w12_plan_ints,
@@ -120,7 +126,7 @@ def lib() -> ctypes.CDLL:
 EXPORTED = ("spec_workspace_bytes", "spec_verify", "spec_commit_kv", "spec_accept_workspace_bytes",
             "spec_accept", "spec_pack_weight", "spec_skinny_gemm_bytes", "spec_skinny_gemm",
             "spec_read_probe", "spec_w12_plan_ints", "spec_w12_plan", "spec_w12_pack",
-            "spec_skinny_gemm_w12", "spec_strerror")
+            "spec_skinny_gemm_w12", "spec_prefill_workspace_bytes", "spec_prefill", "spec_strerror")
 
 
 def spec_strerror(code: int) -> str:
@@ -313,6 +319,28 @@ def spec_verify(weights: Weights, kv: PagedKV, draft_tokens: torch.Tensor,
                            _ptr(bonus_token), _ptr(accepted_path), ctypes.byref(extras), _ptr(ws),
                            ws.numel(), _stream(stream))
     _check(rc, "spec_verify")
+
+
+def spec_prefill_workspace_bytes(cfg: ModelCfg, batch: int, max_pages_per_req: int,
+                                 want_logits: bool = False) -> int:
+    n = ctypes.c_size_t(0)
+    c = cfg.c()
+    _check(lib().spec_prefill_workspace_bytes(ctypes.byref(c), batch, max_pages_per_req,
+                                              1 if want_logits else 0, ctypes.byref(n)),
+           "spec_prefill_workspace_bytes")
+    return n.value
+
+
+def spec_prefill(weights: Weights, kv: PagedKV, prompt: torch.Tensor, ctx_len: torch.Tensor,
+                 next_token: torch.Tensor, ws: torch.Tensor, last_logits: Optional[torch.Tensor] = None,
+                 stream=None) -> None:
+    """Appends prompt [batch][p] (int32, device) to every request's committed context; writes
+    next_token [batch] and, if given, last_logits [batch][vocab]."""
+    batch, p = prompt.shape
+    rc = lib().spec_prefill(ctypes.byref(weights.c), ctypes.byref(kv.c), _ptr(prompt), _ptr(ctx_len),
+                            batch, p, _ptr(next_token), _ptr(last_logits), _ptr(ws), ws.numel(),
+                            _stream(stream))
+    _check(rc, "spec_prefill")
 
 
 def spec_commit_kv(cfg: ModelCfg, kv: PagedKV, accepted_len: torch.Tensor,

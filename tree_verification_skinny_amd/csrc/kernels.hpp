@@ -125,6 +125,12 @@ hipError_t commit_kv(const int32_t *accepted_len, const int32_t *path, const int
                      const int32_t *block_table, int max_pages, int n_pages, int L, int B, int K,
                      int nkv, int D, bf16 *k_pool, bf16 *v_pool, hipStream_t st);
 hipError_t commit_ctx(const int32_t *accepted_len, int32_t *ctx_len, int B, hipStream_t st);
+// Prompt prefill bookkeeping (k_prefill.hip).
+hipError_t prefill_init(int32_t *failed, int B, hipStream_t st);
+hipError_t prefill_gather(const int32_t *prompt, int p, int c0, int n, int B, int32_t *out, hipStream_t st);
+hipError_t prefill_advance(const int32_t *acc, const int32_t *greedy, int n, int B, bool last,
+                           int32_t *failed, int32_t *ctx_len, int32_t *next_token, hipStream_t st);
+hipError_t prefill_last_logits(const float *logits, int n, int B, int V, float *out, hipStream_t st);
 // Reads bytes (a multiple of 16, 16-byte aligned) once as a grid-stride stream.
 hipError_t read_probe(const void *buf, int64_t bytes, uint32_t *out, hipStream_t st);
 

@@ -430,6 +430,81 @@ int spec_w12_pack(const void *w, int n, int kd, const int32_t *plan, void *plane
     return SPEC_OK;
 }
 
+// Prefill workspace: the verify pass's workspace for chunks of SPEC_MAX_K rows, then its outputs
+// (accepted_len, bonus, path, greedy), the chunk's tokens, the failure flags and, when asked for,
+// the last chunk's fp32 logits.
+struct PrefillLayout {
+    size_t verify, acc, bonus, path, greedy, tokens, failed, logits, total;
+};
+
+static int prefill_layout(const spec_model_cfg *cfg, int batch, int max_pages, bool want_logits,
+                          PrefillLayout &o) {
+    size_t vb = 0;
+    const int rc = spec_workspace_bytes(cfg, batch, SPEC_MAX_K, max_pages, &vb);
+    if (rc != SPEC_OK) return rc;
+    const size_t rows = (size_t)batch * SPEC_MAX_K;
+    Carver cv;
+    o.verify = cv.take(vb);
+    o.acc = cv.take(sizeof(int32_t) * batch);
+    o.bonus = cv.take(sizeof(int32_t) * batch);
+    o.path = cv.take(sizeof(int32_t) * rows);
+    o.greedy = cv.take(sizeof(int32_t) * rows);
+    o.tokens = cv.take(sizeof(int32_t) * rows);
+    o.failed = cv.take(sizeof(int32_t) * batch);
+    o.logits = want_logits ? cv.take(sizeof(float) * rows * cfg->vocab) : 0;
+    o.total = cv.off;
+    return SPEC_OK;
+}
+
+int spec_prefill_workspace_bytes(const spec_model_cfg *cfg, int batch, int max_pages_per_req,
+                                 int want_logits, size_t *bytes) {
+    if (bytes == nullptr) return SPEC_EINVAL;
+    PrefillLayout o;
+    const int rc = prefill_layout(cfg, batch, max_pages_per_req, want_logits != 0, o);
+    if (rc != SPEC_OK) return rc;
+    *bytes = o.total;
+    return SPEC_OK;
+}
+
+int spec_prefill(const spec_weights *weights, const spec_kv_cache *kv, const int32_t *prompt,
+                 int32_t *ctx_len, int batch, int p, int32_t *next_token, float *last_logits,
+                 void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (weights == nullptr || kv == nullptr || prompt == nullptr || ctx_len == nullptr ||
+        next_token == nullptr || workspace == nullptr)
+        return SPEC_EINVAL;
+    if (batch < 1 || p < 1) return SPEC_EINVAL;
+    if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0) return SPEC_EINVAL;
+    PrefillLayout o;
+    int rc = prefill_layout(&weights->cfg, batch, kv->max_pages_per_req, last_logits != nullptr, o);
+    if (rc != SPEC_OK) return rc;
+    if (workspace_bytes < o.total) return SPEC_EWORKSPACE;
+    int32_t *acc = at<int32_t>(workspace, o.acc);
+    int32_t *bonus = at<int32_t>(workspace, o.bonus);
+    int32_t *path = at<int32_t>(workspace, o.path);
+    int32_t *greedy = at<int32_t>(workspace, o.greedy);
+    int32_t *tokens = at<int32_t>(workspace, o.tokens);
+    int32_t *failed = at<int32_t>(workspace, o.failed);
+    float *logits = last_logits ? at<float>(workspace, o.logits) : nullptr;
+    SV_TRY(prefill_init(failed, batch, stream));
+    for (int c0 = 0; c0 < p; c0 += SPEC_MAX_K) {
+        const int n = p - c0 < SPEC_MAX_K ? p - c0 : SPEC_MAX_K;
+        const bool last = c0 + n == p;
+        SV_TRY(prefill_gather(prompt, p, c0, n, batch, tokens, stream));
+        spec_verify_extras ex = {};
+        ex.greedy = greedy;
+        ex.logits = last ? logits : nullptr;
+        rc = spec_verify(weights, kv, tokens, nullptr, ctx_len, batch, n, acc, bonus, path, &ex,
+                         at<void>(workspace, o.verify), o.acc - o.verify, stream);
+        if (rc != SPEC_OK) return rc;
+        SV_TRY(prefill_advance(acc, greedy, n, batch, last, failed, ctx_len, next_token, stream));
+    }
+    if (last_logits) {
+        const int n = p - (p - 1) / SPEC_MAX_K * SPEC_MAX_K;   // rows of the last chunk
+        SV_TRY(prefill_last_logits(logits, n, batch, weights->cfg.vocab, last_logits, stream));
+    }
+    return SPEC_OK;
+}
+
 int spec_read_probe(const void *buf, size_t bytes, uint32_t *out, hipStream_t stream) {
     if (buf == nullptr || out == nullptr || bytes == 0 || bytes % 16 != 0) return SPEC_EINVAL;
     if (reinterpret_cast<uintptr_t>(buf) % 16 != 0) return SPEC_EINVAL;
