@@ -237,10 +237,9 @@ int spec_w12_pack(const void *w /* bf16 [n][kd] row-major */, int n, int kd, con
                   void *planes, int32_t *exc, hipStream_t stream);
 
 /* spec_skinny_gemm over a W12 matrix: the same partials, bit for bit, as spec_skinny_gemm over
- * the bf16 matrix it encodes whenever both use the same split (always for m <= 16; above 16
- * rows spec_skinny_gemm switches to its wide variant while W12 keeps the skinny one). The split
- * count may differ from spec_skinny_gemm's above 16 rows; partial_bytes as spec_skinny_gemm_bytes
- * gives covers both. */
+ * the bf16 matrix it encodes for m < 128 (same kernels, tiles and splits). From 128 rows
+ * spec_skinny_gemm switches to its matrix-core tile kernel while W12 keeps 64-row chunks; the
+ * split count may then differ, and partial_bytes as spec_skinny_gemm_bytes gives covers both. */
 int spec_skinny_gemm_w12(const void *x, int m, int kd, const spec_w12_matrix *w, int n,
                          float *partials, size_t partial_bytes, int *splits, hipStream_t stream);
 

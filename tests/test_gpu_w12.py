@@ -122,15 +122,22 @@ def test_w12_gemm_bit_identical_to_bf16(m, n, kd, frac):
         (q.n_exc, (a - b).abs().max().item())
 
 
-@pytest.mark.parametrize("m", [17, 40, 64])
-def test_w12_gemm_many_rows_within_summation_bound(m):
-    n, kd = 1024, 2048
-    x = synth.randn_bf16((m, kd), 1.0, DEV, "w12xm", m)
-    w = with_exceptions(synth.randn_bf16((n, kd), 0.02, DEV, "w12wm", m), m, 0.001)
+@pytest.mark.parametrize("m,n,kd", [(17, 1024, 2048), (40, 7168, 5120), (64, 5120, 17408), (33, 64, 96)])
+def test_w12_gemm_many_rows_bit_identical_to_bf16(m, n, kd):
+    """17..64 rows: both formats run the wide kernel (or the skinny one where N does not split
+    into its 128-column groups) with the same plan, so the partials agree bit for bit; they also
+    meet the classical fp32 summation bound against float64."""
+    x = synth.randn_bf16((m, kd), 1.0, DEV, "w12xm", m, n)
+    w = with_exceptions(synth.randn_bf16((n, kd), 0.02, DEV, "w12wm", m, n), (m, n), 0.001)
     q = tv.W12Matrix(w)
-    part = torch.full((tv.spec_skinny_gemm_bytes(m, n, kd) // 4,), float("nan"), device=DEV)
+    nb = tv.spec_skinny_gemm_bytes(m, n, kd)
+    p16 = torch.full((nb // 4,), float("nan"), device=DEV)
+    part = torch.full((nb // 4,), float("nan"), device=DEV)
+    s16 = tv.spec_skinny_gemm(x, tv.spec_pack_weight(w), p16)
     s = tv.spec_skinny_gemm_w12(x, q, part)
     torch.cuda.synchronize()
+    assert s == s16
+    assert torch.equal(p16[:s * m * n].view(torch.int32), part[:s * m * n].view(torch.int32))
     p = part[:s * m * n].view(s, m, n).cpu().numpy()
     y = p[0].copy()
     for i in range(1, s):
@@ -178,11 +185,10 @@ def test_w12_tiny_block_equals_bf16_and_oracle():
     assert near <= 3
 
 
-@pytest.mark.parametrize("k", [12, 40])
-def test_w12_tiny_tree_matches_oracle(k):
-    """Trees of up to 64 rows: bf16 switches to its wide projection kernel above 16 rows while
-    W12 keeps the skinny one, so the two GPU passes may differ by summation order; both must meet
-    the oracle."""
+@pytest.mark.parametrize("k", [12, 40, 64])
+def test_w12_tiny_tree_equals_bf16_and_oracle(k):
+    """Trees of 12 (skinny kernel) and 40 or 64 nodes (wide kernel): the W12 pass is
+    bit-identical to the bf16 pass and meets the oracle."""
     near = 0
     for seed in range(3):
         w = synth.model_weights(synth.TINY, 900 + seed)
@@ -193,9 +199,14 @@ def test_w12_tiny_tree_matches_oracle(k):
         vc = [np.ascontiguousarray(bits(y)) for _, y in ctxs]
         tokens, parent = planted_tree(m, kc, vc, k, seed)
         r = oracle.verify(m, kc, vc, tokens, parent)
-        kv = make_kv(synth.TINY, [ctx], k, seed, DEV)
-        upload_context(kv, 0, kc, vc)
-        out = run_verify(tiny_weights(w, True), kv, tokens[None], parent[None], [ctx])
+        outs = []
+        for fmt in (False, True):
+            kv = make_kv(synth.TINY, [ctx], k, seed, DEV)
+            upload_context(kv, 0, kc, vc)
+            outs.append(run_verify(tiny_weights(w, fmt), kv, tokens[None], parent[None], [ctx]))
+        b16, out = outs
+        assert np.array_equal(b16.logits.view(np.int32), out.logits.view(np.int32)), seed
+        assert np.array_equal(b16.path, out.path) and np.array_equal(b16.greedy, out.greedy)
         check_logits(out.logits[0], r.logits)
         near += check_accept(r, tokens, parent, out.greedy[0], int(out.accepted_len[0]),
                              int(out.bonus[0]), out.path[0])

@@ -28,6 +28,8 @@
 //     maximum of the output head.
 // MFMA lane layout (16x16x32): lane l supplies A row l%16, K elements 8*(l/16)..+7, and B
 // column l%16, the same K elements; it receives D rows 4*(l/16)..+3 of column l%16.
+#include <type_traits>
+
 #include "kernels.hpp"
 
 #ifndef SV_W12_U
@@ -384,10 +386,16 @@ __device__ __forceinline__ int wide_col(int ng, int w, int t, int F) {
     }
 }
 
-template <int TM, int EPI>
+// A weight fragment as loaded: bf16 operand, or a lane's 12 W12 bytes (decoded at use).
+struct W12Raw {
+    uint32_t a, b, c;
+};
+
+template <int TM, int EPI, bool W12>
 __global__ __launch_bounds__(64 * kWideWaves) void gemm_wide_kernel(GemmIn in, const bf16 *__restrict__ Wp,
-                                                                     int N, int Kd, int n_groups,
+                                                                     W12Ref w12, int N, int Kd, int n_groups,
                                                                      int ksteps, GemmEpi ep) {
+    using Frag = typename std::conditional<W12, W12Raw, bf16x8>::type;
     constexpr int NW = kWideWaves, TN = kWideTN, KS = kWideKS;
     constexpr int SLOTS = KS * TM * 64;                 // 16-byte slots per slab
     constexpr int PER = SLOTS / (64 * NW);              // slots staged per thread
@@ -409,9 +417,34 @@ __global__ __launch_bounds__(64 * kWideWaves) void gemm_wide_kernel(GemmIn in, c
     const int nblk = (in.M_total + 15) >> 4;
 
     const bf16 *wp[TN];
+    const uint32_t *qp[TN];          // W12: lane's 12 bytes in the tile's fragment at s_begin
+    W12Cursor cur[TN];
+    uint32_t cb = 0;
+    if constexpr (W12) cb = (uint32_t)(w12.plan[0] >> 1) * 0x01000100u;
 #pragma unroll
-    for (int t = 0; t < TN; ++t)
-        wp[t] = Wp + ((((int64_t)(wide_col<EPI>(ng, wave, t, ep.F) >> 4)) * S + s_begin) * 64 + lane) * 8;
+    for (int t = 0; t < TN; ++t) {
+        const int tile = wide_col<EPI>(ng, wave, t, ep.F) >> 4;
+        if constexpr (W12) {
+            qp[t] = w12.planes + ((int64_t)tile * S + s_begin) * 192 + 3 * lane;
+            cur[t].i = w12.plan[2 + tile];
+            cur[t].end = w12.plan[3 + tile];
+        } else {
+            wp[t] = Wp + ((((int64_t)tile) * S + s_begin) * 64 + lane) * 8;
+        }
+    }
+    if constexpr (W12) {
+        int st[TN];
+#pragma unroll
+        for (int t = 0; t < TN; ++t) {
+            const int k = cur[t].i + lane;
+            st[t] = k < cur[t].end ? (w12.exc[k].x >> 9) : 0x7fffffff;
+        }
+#pragma unroll
+        for (int t = 0; t < TN; ++t) {
+            cur[t].i = w12_first_at(w12.exc, cur[t].i, cur[t].end, s_begin, lane, st[t]);
+            cur[t].step = w12_step_of(w12.exc, cur[t].i, cur[t].end);
+        }
+    }
 
     // staging: thread slot i = threadIdx.x + 256 r covers (step, block, lane) of the slab
     auto stage_load = [&](bf16x8 (&xr)[PER], int slab) {
@@ -428,13 +461,20 @@ __global__ __launch_bounds__(64 * kWideWaves) void gemm_wide_kernel(GemmIn in, c
 #pragma unroll
         for (int r = 0; r < PER; ++r) xs[buf][threadIdx.x + r * 64 * NW] = xr[r];
     };
-    auto w_load = [&](bf16x8 (&a)[KS][TN], int slab) {
+    auto w_load = [&](Frag (&a)[KS][TN], int slab) {
 #pragma unroll
         for (int k = 0; k < KS; ++k) {
             const int s = slab * KS + k;                 // relative to s_begin
 #pragma unroll
-            for (int t = 0; t < TN; ++t)
-                a[k][t] = s < nsteps ? stream_load((const bf16x8 *)(wp[t] + (int64_t)s * 512)) : bf16x8{};
+            for (int t = 0; t < TN; ++t) {
+                if constexpr (W12) {
+                    const uint32_t *f = qp[t] + (int64_t)s * 192;
+                    a[k][t] = s < nsteps ? W12Raw{stream_load32(f), stream_load32(f + 1), stream_load32(f + 2)}
+                                         : W12Raw{0u, 0u, 0u};
+                } else {
+                    a[k][t] = s < nsteps ? stream_load((const bf16x8 *)(wp[t] + (int64_t)s * 512)) : bf16x8{};
+                }
+            }
         }
     };
 
@@ -444,7 +484,7 @@ __global__ __launch_bounds__(64 * kWideWaves) void gemm_wide_kernel(GemmIn in, c
 #pragma unroll
         for (int mt = 0; mt < TM; ++mt) acc[t][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    auto multiply = [&](const bf16x8 (&a)[KS][TN], int buf, int slab) {
+    auto multiply = [&](const Frag (&a)[KS][TN], int buf, int slab) {
         const int kmax = min(KS, nsteps - slab * KS);
 #pragma unroll
         for (int k = 0; k < KS; ++k) {
@@ -453,15 +493,25 @@ __global__ __launch_bounds__(64 * kWideWaves) void gemm_wide_kernel(GemmIn in, c
 #pragma unroll
                 for (int mt = 0; mt < TM; ++mt) b[mt] = xs[buf][(k * TM + mt) * 64 + lane];
 #pragma unroll
-                for (int t = 0; t < TN; ++t)
+                for (int t = 0; t < TN; ++t) {
+                    bf16x8 w;
+                    if constexpr (W12) {
+                        const int su = s_begin + slab * KS + k;
+                        w = w12_decode(a[k][t].a, a[k][t].b, a[k][t].c, cb);
+                        if (su >= cur[t].step) w = w12_fixup(w, cur[t], w12.exc, su, lane);
+                    } else {
+                        w = a[k][t];
+                    }
 #pragma unroll
-                    for (int mt = 0; mt < TM; ++mt) acc[t][mt] = mfma16x16x32(a[k][t], b[mt], acc[t][mt]);
+                    for (int mt = 0; mt < TM; ++mt) acc[t][mt] = mfma16x16x32(w, b[mt], acc[t][mt]);
+                }
             }
         }
     };
 
     if (nslabs > 0) {
-        bf16x8 wa[KS][TN], wb[KS][TN], xr[PER];
+        Frag wa[KS][TN], wb[KS][TN];
+        bf16x8 xr[PER];
         stage_load(xr, 0);
         w_load(wa, 0);
         stage_store(xr, 0);
@@ -610,22 +660,38 @@ static hipError_t by_tiles(const GemmShape &g, const GemmIn &in, const bf16 *Wp,
     }
 }
 
-template <int EPI>
-static hipError_t launch_wide(const GemmShape &g, const GemmIn &in, const bf16 *Wp, const GemmEpi &ep,
-                              hipStream_t st) {
+template <int EPI, bool W12>
+static void launch_wide_as(const GemmShape &g, const GemmIn &in, const bf16 *Wp, const W12Ref &w12,
+                           const GemmEpi &ep, hipStream_t st) {
     const int steps = g.Kd >> 5;
     const int ks = (steps + g.splits - 1) / g.splits;
     const dim3 grid(gemm_groups(g) * g.splits), block(64 * kWideWaves);
     switch (mt_for(in.M)) {
-        case 1: hipLaunchKernelGGL((gemm_wide_kernel<1, EPI>), grid, block, 0, st, in, Wp, g.N, g.Kd, gemm_groups(g), ks, ep); break;
-        case 2: hipLaunchKernelGGL((gemm_wide_kernel<2, EPI>), grid, block, 0, st, in, Wp, g.N, g.Kd, gemm_groups(g), ks, ep); break;
-        default: hipLaunchKernelGGL((gemm_wide_kernel<4, EPI>), grid, block, 0, st, in, Wp, g.N, g.Kd, gemm_groups(g), ks, ep); break;
+        case 1: hipLaunchKernelGGL((gemm_wide_kernel<1, EPI, W12>), grid, block, 0, st, in, Wp, w12, g.N, g.Kd, gemm_groups(g), ks, ep); break;
+        case 2: hipLaunchKernelGGL((gemm_wide_kernel<2, EPI, W12>), grid, block, 0, st, in, Wp, w12, g.N, g.Kd, gemm_groups(g), ks, ep); break;
+        default: hipLaunchKernelGGL((gemm_wide_kernel<4, EPI, W12>), grid, block, 0, st, in, Wp, w12, g.N, g.Kd, gemm_groups(g), ks, ep); break;
     }
+}
+
+template <int EPI>
+static hipError_t launch_wide(const GemmShape &g, const GemmIn &in, const bf16 *Wp, const W12Ref &w12,
+                              const GemmEpi &ep, hipStream_t st) {
+    if (w12.planes != nullptr) launch_wide_as<EPI, true>(g, in, Wp, w12, ep, st);
+    else launch_wide_as<EPI, false>(g, in, Wp, w12, ep, st);
     return hipGetLastError();
 }
 
-static hipError_t skinny(const GemmShape &g, int epi, const GemmIn &in, const bf16 *Wp, const W12Ref &w12,
-                         const GemmEpi &ep, hipStream_t st) {
+// One 64-row chunk of a skinny or wide launch.
+static hipError_t chunk(const GemmShape &g, int epi, const GemmIn &in, const bf16 *Wp, const W12Ref &w12,
+                        const GemmEpi &ep, hipStream_t st) {
+    if (g.wide) {
+        switch (epi) {
+            case EPI_PARTIAL: return launch_wide<EPI_PARTIAL>(g, in, Wp, w12, ep, st);
+            case EPI_SWIGLU: return launch_wide<EPI_SWIGLU>(g, in, Wp, w12, ep, st);
+            case EPI_ARGMAX: return launch_wide<EPI_ARGMAX>(g, in, Wp, w12, ep, st);
+            default: return hipErrorInvalidValue;
+        }
+    }
     switch (epi) {
         case EPI_PARTIAL: return by_tiles<EPI_PARTIAL>(g, in, Wp, w12, ep, st);
         case EPI_SWIGLU: return by_tiles<EPI_SWIGLU>(g, in, Wp, w12, ep, st);
@@ -648,17 +714,7 @@ hipError_t gemm(const GemmShape &g, int epi, const GemmIn &in_all, const bf16 *W
         in.M_total = g.M;
         in.m0 = m0;
         in.M = g.M - m0 < 64 ? g.M - m0 : 64;
-        hipError_t e;
-        if (g.wide) {
-            switch (epi) {
-                case EPI_PARTIAL: e = launch_wide<EPI_PARTIAL>(g, in, Wp, ep, st); break;
-                case EPI_SWIGLU: e = launch_wide<EPI_SWIGLU>(g, in, Wp, ep, st); break;
-                case EPI_ARGMAX: e = launch_wide<EPI_ARGMAX>(g, in, Wp, ep, st); break;
-                default: return hipErrorInvalidValue;
-            }
-        } else {
-            e = skinny(g, epi, in, Wp, W12Ref{}, ep, st);
-        }
+        const hipError_t e = chunk(g, epi, in, Wp, W12Ref{}, ep, st);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
@@ -666,13 +722,13 @@ hipError_t gemm(const GemmShape &g, int epi, const GemmIn &in_all, const bf16 *W
 
 hipError_t gemm_w12(const GemmShape &g, int epi, const GemmIn &in_all, const W12Ref &w,
                     const GemmEpi &ep, hipStream_t st) {
-    if (g.tc || g.wide || w.planes == nullptr) return hipErrorInvalidValue;
+    if (g.tc || w.planes == nullptr) return hipErrorInvalidValue;
     for (int m0 = 0; m0 < g.M; m0 += 64) {
         GemmIn in = in_all;
         in.M_total = g.M;
         in.m0 = m0;
         in.M = g.M - m0 < 64 ? g.M - m0 : 64;
-        const hipError_t e = skinny(g, epi, in, nullptr, w, ep, st);
+        const hipError_t e = chunk(g, epi, in, nullptr, w, ep, st);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
@@ -686,7 +742,7 @@ hipError_t gemm_w12(const GemmShape &g, int epi, const GemmIn &in_all, const W12
 // and finish their epilogue in place. Eight waves when there are few groups or K splits.
 static GemmShape plan_skinny(int M, int N, int Kd, bool allow_split);
 
-GemmShape plan_gemm(int M, int N, int Kd, bool allow_split) {
+GemmShape plan_gemm(int M, int N, int Kd, bool allow_split, bool allow_tc) {
     GemmShape g;
     g.M = M;
     g.N = N;
@@ -694,7 +750,7 @@ GemmShape plan_gemm(int M, int N, int Kd, bool allow_split) {
     g.wide = false;
     g.tc = false;
     const int steps = Kd / 32;
-    if (M >= 128 && N % gemm_tc_columns() == 0) {
+    if (allow_tc && M >= 128 && N % gemm_tc_columns() == 0) {
         // hundreds of rows: the matrix-core tile kernel, one launch over all 256-row tiles;
         // narrow projections split K so that about SV_TC_TARGET workgroups stream (512, two per
         // compute unit, measured best at 512 rows: fewer splits leave fewer fp32 partials to
@@ -743,8 +799,8 @@ GemmShape plan_gemm(int M, int N, int Kd, bool allow_split) {
 // Over W12 weights the whole-K projections (gate/up, output head) may run a different wave count:
 // their workgroups all fit at once, so the bytes in flight are set by waves x batch depth.
 GemmShape plan_gemm_w12(int M, int N, int Kd, bool allow_split) {
-    GemmShape g = plan_skinny(M, N, Kd, allow_split);
-    if (!allow_split && g.waves == 8) g.waves = SV_W12_WHOLE_WAVES;
+    GemmShape g = plan_gemm(M, N, Kd, allow_split, false);
+    if (!g.wide && !allow_split && g.waves == 8) g.waves = SV_W12_WHOLE_WAVES;
     return g;
 }
 

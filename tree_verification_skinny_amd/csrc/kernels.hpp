@@ -54,11 +54,12 @@ hipError_t w12_pack(const bf16 *w, int n, int kd, const int32_t *plan, uint32_t 
                     hipStream_t st);
 
 int gemm_groups(const GemmShape &g);
-GemmShape plan_gemm(int M, int N, int Kd, bool allow_split);
+GemmShape plan_gemm(int M, int N, int Kd, bool allow_split, bool allow_tc = true);
 hipError_t gemm(const GemmShape &g, int epi, const GemmIn &in, const bf16 *Wp, const GemmEpi &ep,
                 hipStream_t st);
-// The skinny projection over a W12 matrix: the plan of plan_gemm_w12 (never the wide or tile
-// variants), bit-identical to gemm() over the same matrix in bf16 whenever the plans agree.
+// The projection over a W12 matrix: the skinny or wide variant (never the tile kernel) as
+// plan_gemm_w12 picks, bit-identical to gemm() over the same matrix in bf16 whenever the plans
+// agree (every shape below 128 rows).
 GemmShape plan_gemm_w12(int M, int N, int Kd, bool allow_split);
 hipError_t gemm_w12(const GemmShape &g, int epi, const GemmIn &in, const W12Ref &w, const GemmEpi &ep,
                     hipStream_t st);
