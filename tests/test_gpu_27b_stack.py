@@ -132,3 +132,29 @@ def test_27b_batched_teacher_forced(stack):
         near = check_accept(r, tokens[b], parent, out.greedy[b], int(out.accepted_len[b]),
                             int(out.bonus[b]), out.path[b])
         print(f"batched request {b} (ctx {ctxs[b]}): head max err {err:.2e}, near-tie {near}")
+
+
+def test_27b_stack_w12_bit_identical(stack):
+    """The same stack with its projections and output head in the lossless 12-bit layout: the
+    block and the tree pass give bit-identical logits, residual streams, cache rows and accepted
+    paths to the bf16 passes, so the teacher-forced oracle checks above carry over unchanged."""
+    shape, w = stack
+    w12 = tv.Weights(w.cfg, w.tensors["embed"], w.tensors["final_norm"], w.rowmajor["lm_head"],
+                     w.rowmajor["layers"], w12=True)
+    n_exc = sum(m.n_exc for lw in w12.w12["layers"] for m in lw.values()) + w12.w12["lm_head"].n_exc
+    for kind in ("block", "tree"):
+        k, ctx, parent, tokens, kv, _, out = _case(shape, w, kind)
+        k2, _, _, _, kv2, _, out2 = _case(shape, w12, kind)
+        assert np.array_equal(out.logits.view(np.int32), out2.logits.view(np.int32)), kind
+        assert torch.equal(out.hidden.view(torch.int16), out2.hidden.view(torch.int16)), kind
+        assert np.array_equal(out.greedy, out2.greedy) and np.array_equal(out.path, out2.path)
+        assert (out.accepted_len[0], out.bonus[0]) == (out2.accepted_len[0], out2.bonus[0])
+        for l in (0, 63):
+            a = kvlayout.read_rows(kv, l, 0, torch.arange(ctx, ctx + k))
+            b = kvlayout.read_rows(kv2, l, 0, torch.arange(ctx, ctx + k))
+            assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16))
+            assert torch.equal(a[1].view(torch.int16), b[1].view(torch.int16))
+        del kv, kv2, out, out2
+    print(f"W12 stack: {n_exc} exceptions over {len(w12.w12['layers']) * 4 + 1} matrices")
+    del w12
+    torch.cuda.empty_cache()
