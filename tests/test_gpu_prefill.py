@@ -146,3 +146,26 @@ def test_prefill_over_w12_weights_equals_bf16():
     assert np.array_equal(l1.view(np.int32), l2.view(np.int32))
     assert torch.equal(k1.view(torch.int16), k2.view(torch.int16))
     assert torch.equal(v1.view(torch.int16), v2.view(torch.int16))
+
+
+@pytest.mark.parametrize("p,ctx0", [(1, 0), (1, 20), (64, 0), (65, 3), (129, 0)])
+def test_prefill_chunk_boundaries(p, ctx0):
+    """Prompt lengths at and around the 64-position chunk: a single token (also with an empty
+    context), exactly one chunk, one chunk plus one token, two chunks plus one."""
+    shape = synth.TINY
+    seed = 40 + p
+    w = synth.model_weights(shape, seed)
+    m = oracle_model_from(shape, w)
+    weights = device_weights(shape, w, DEV)
+    kv = make_kv(shape, [ctx0 + p], 0, seed, DEV)
+    ctxs = [synth.kv_context(shape, ctx0, seed, l) for l in range(shape.n_layers)]
+    kc0 = [np.ascontiguousarray(bits(x)) for x, _ in ctxs]
+    vc0 = [np.ascontiguousarray(bits(y)) for _, y in ctxs]
+    upload_context(kv, 0, kc0, vc0)
+    prompt = synth.uniform_tokens(p, shape.vocab, seed, "edge")
+    kc, vc, last = oracle.prefill(m, prompt, kc0, vc0)
+    ctx, nt, lg = gpu_prefill(weights, kv, prompt[None], [ctx0])
+    assert ctx[0] == ctx0 + p
+    check_logits(lg[0], last, "last logits")
+    assert greedy_ok(nt[0], last)
+    check_rows(kv, 0, kc, vc, 0, ctx0 + p, "rows")

@@ -211,3 +211,16 @@ def test_w12_tiny_tree_equals_bf16_and_oracle(k):
         near += check_accept(r, tokens, parent, out.greedy[0], int(out.accepted_len[0]),
                              int(out.bonus[0]), out.path[0])
     assert near <= 1
+
+
+def test_w12_root_only_pass_equals_bf16():
+    """A one-node pass (k = 1: the root alone, M = 1 row) over W12 and over bf16."""
+    w, m, kc, vc, tokens, G = tiny_case(5)
+    outs = []
+    for fmt in (False, True):
+        kv = make_kv(synth.TINY, [128], 1, 5, DEV)
+        upload_context(kv, 0, kc, vc)
+        outs.append(run_verify(tiny_weights(w, fmt), kv, tokens[None, :1], None, [128]))
+    assert np.array_equal(outs[0].logits.view(np.int32), outs[1].logits.view(np.int32))
+    assert outs[0].accepted_len[0] == outs[1].accepted_len[0] == 0
+    assert outs[0].bonus[0] == outs[1].bonus[0]
