@@ -45,10 +45,14 @@ METRIC = "verified tokens/sec + verify-step HBM GB/s (% peak), 27B-shape dense, 
 # scaled by what the same counter reads for a device-to-device copy of 4 GiB (bytes known). The
 # figures hold for the GEMM source they were taken on; any other source reports null.
 PMC_TRAFFIC = {
-    "block": {"source": "tree_verification_skinny_amd/csrc/k_gemm.hip",
-              "sha256": "5dd564c0f7d3bc3c02f248c9b8d10cef9516f5022e86fe14df34c5ed46cfb7a7",
-              "fetch_kib": 174756.305, "write_kib": 544.0,
-              "fetch_scale": 1.9999858, "write_scale": 1.0},
+    ("block", "bf16"): {"source": "tree_verification_skinny_amd/csrc/k_gemm.hip",
+                        "sha256": "ae48a2829b0ddd3ce8120a587278326ee4ef58d90e7b925d64aee1aeed6b46b2",
+                        "fetch_kib": 174761.283, "write_kib": 544.0,
+                        "fetch_scale": 1.9999858, "write_scale": 1.0},
+    ("block", "w12"): {"source": "tree_verification_skinny_amd/csrc/k_gemm.hip",
+                       "sha256": "ae48a2829b0ddd3ce8120a587278326ee4ef58d90e7b925d64aee1aeed6b46b2",
+                       "fetch_kib": 131470.243, "write_kib": 544.0,
+                       "fetch_scale": 1.9999851, "write_scale": 1.0},
 }
 HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0     # dense bf16 matrix-core peak of MI355X
@@ -146,11 +150,11 @@ def time_gate_up(step_with_events, events, n_layers, stream, reps):
     return float(np.mean(durs)) / 1e3, t_step / reps
 
 
-def pmc_traffic(config):
+def pmc_traffic(config, weights="bf16"):
     """Counter-measured HBM bytes per gate/up launch, or None when there are no counters for this
-    workload or the GEMM source has changed since they were taken."""
+    workload and weight layout or the GEMM source has changed since they were taken."""
     import hashlib
-    rec = PMC_TRAFFIC.get(config)
+    rec = PMC_TRAFFIC.get((config, weights))
     if rec is None or rec["sha256"] is None:
         return None
     with open(os.path.join(ROOT, rec["source"]), "rb") as f:
@@ -383,7 +387,7 @@ def main():
                                            max(3, min(args.steps, 10)))
         t_ctx.copy_(ctx0)
         b_launch = gate_up_bytes(shape, B * K, weights.w12)
-        traffic = None if w12 else pmc_traffic(args.config)
+        traffic = pmc_traffic(args.config, args.weights)
         if args.config == "batched":
             # hundreds of rows: the tile kernel is bound by the matrix cores, not by HBM
             flops = 2 * B * K * (2 * shape.ffn) * shape.hidden
