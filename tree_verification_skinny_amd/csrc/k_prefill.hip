@@ -1,5 +1,7 @@
-// k_prefill.hip — bookkeeping kernels of the prompt prefill: the pass itself is the verify pass
-// run over consecutive chunks of the prompt as linear blocks (see spec_prefill).
+// k_prefill.hip — bookkeeping kernels of the prompt prefill. The pass itself is the verify pass
+// run over consecutive chunks of the prompt as linear blocks: a drafted block is scored in one
+// target pass [SpecPilot news piece, wireai.ir — "The main challenge"], and a prompt chunk is a
+// block that is accepted whole, its K/V committed before the next chunk (see spec_prefill).
 #include "kernels.hpp"
 
 namespace sv {
