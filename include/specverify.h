@@ -182,7 +182,8 @@ int spec_accept(const float *logits, const int32_t *draft_tokens, const int32_t 
  * columns (s = columns 32s..32s+31), in that nesting, 64 slots of 8 consecutive bf16; slot l
  * holds w[16t + l%16][32s + 8(l/16) .. + 7]. One 128-bit load per lane of a 64-wide wavefront
  * then fetches one matrix-core operand as 1 KB of contiguous memory. Needs n % 16 == 0 and
- * kd % 32 == 0. A one-time, load-time transform; enqueued on `stream`. */
+ * kd % 32 == 0 (SPEC_EUNSUPPORTED otherwise) and 16-byte aligned w and packed (SPEC_EINVAL).
+ * A one-time, load-time transform; enqueued on `stream`. */
 int spec_pack_weight(const void *w, int n, int kd, void *packed, hipStream_t stream);
 
 /* The weight-streaming projection spec_verify runs for every weight matrix, on its own:
@@ -229,7 +230,9 @@ int spec_read_probe(const void *buf, size_t bytes, uint32_t *out, hipStream_t st
  *     (exclusive prefix, n/16 + 1 entries), then 256 ints of scratch.
  * The format pays where the window holds nearly every weight (about 1e-4 of N(0, 0.02) weights
  * are exceptions); read plan[1] after spec_w12_plan to decide, and to size exc (2*E ints).
- * Needs n % 16 == 0 and kd % 32 == 0. One-time, load-time transforms, enqueued on `stream`. */
+ * Needs n % 16 == 0 and kd % 32 == 0 (SPEC_EUNSUPPORTED), a 16-byte aligned w, 16-byte aligned
+ * planes and 8-byte aligned exc (SPEC_EINVAL). One-time, load-time transforms, enqueued on
+ * `stream`. */
 int spec_w12_plan_ints(int n, int kd, size_t *ints /* HOST */);
 int spec_w12_plan(const void *w /* bf16 [n][kd] row-major */, int n, int kd, int32_t *plan,
                   hipStream_t stream);

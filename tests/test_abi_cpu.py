@@ -126,6 +126,8 @@ def test_pack_and_skinny_gemm_reject_bad_arguments():
     assert L.spec_pack_weight(fake, 64, 64, fake, None) == tv.SPEC_EINVAL       # in place
     assert L.spec_pack_weight(fake, 20, 64, fake + 4096, None) == tv.SPEC_EUNSUPPORTED
     assert L.spec_pack_weight(fake, 64, 40, fake + 4096, None) == tv.SPEC_EUNSUPPORTED
+    assert L.spec_pack_weight(fake + 2, 64, 64, fake + 4096, None) == tv.SPEC_EINVAL    # unaligned
+    assert L.spec_pack_weight(fake, 64, 64, fake + 4098, None) == tv.SPEC_EINVAL
     n = ctypes.c_size_t(0)
     assert L.spec_skinny_gemm_bytes(16, 40, 64, ctypes.byref(n)) == tv.SPEC_EUNSUPPORTED
     assert L.spec_skinny_gemm_bytes(16, 48, 40, ctypes.byref(n)) == tv.SPEC_EUNSUPPORTED
@@ -164,6 +166,8 @@ def test_w12_entry_points_reject_bad_arguments():
     assert L.spec_w12_plan_ints(0, 64, ctypes.byref(n)) == tv.SPEC_EINVAL
     assert L.spec_w12_plan(None, 64, 64, fake, None) == tv.SPEC_EINVAL
     assert L.spec_w12_plan(fake, 64, 64, None, None) == tv.SPEC_EINVAL
+    assert L.spec_w12_plan(fake + 2, 64, 64, fake, None) == tv.SPEC_EINVAL              # unaligned rows
+    assert L.spec_w12_pack(fake + 8, 64, 64, fake, fake, fake, None) == tv.SPEC_EINVAL
     assert L.spec_w12_pack(fake, 64, 64, fake, None, fake, None) == tv.SPEC_EINVAL
     assert L.spec_w12_pack(fake, 64, 64, fake, fake, None, None) == tv.SPEC_EINVAL
     assert L.spec_w12_pack(fake, 64, 64, fake, fake + 4, fake, None) == tv.SPEC_EINVAL   # unaligned planes

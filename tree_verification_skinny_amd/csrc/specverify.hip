@@ -329,6 +329,9 @@ int spec_pack_weight(const void *w, int n, int kd, void *packed, hipStream_t str
     if (n < 1 || kd < 1) return SPEC_EINVAL;
     if (n % 16 != 0 || kd % 32 != 0) return SPEC_EUNSUPPORTED;
     if (w == packed) return SPEC_EINVAL;
+    // rows are read and written 16 bytes at a time
+    if (reinterpret_cast<uintptr_t>(w) % 16 != 0 || reinterpret_cast<uintptr_t>(packed) % 16 != 0)
+        return SPEC_EINVAL;
     SV_TRY(pack_weight(static_cast<const bf16 *>(w), n, kd, static_cast<bf16 *>(packed), stream));
     return SPEC_OK;
 }
@@ -361,6 +364,7 @@ int spec_skinny_gemm(const void *x, int m, int kd, const void *w, int n, float *
     if (rc != SPEC_OK) return rc;
     if (partial_bytes < skinny_total_bytes(g, m, n, kd)) return SPEC_EWORKSPACE;
     if (reinterpret_cast<uintptr_t>(partials) % 256 != 0) return SPEC_EINVAL;
+    if (reinterpret_cast<uintptr_t>(x) % 16 != 0) return SPEC_EINVAL;   // rows read 16 bytes at a time
     *splits = g.splits;
     bf16 *xp = reinterpret_cast<bf16 *>(reinterpret_cast<char *>(partials) +
                                         skinny_partial_bytes(g, m, n));
@@ -382,6 +386,7 @@ int spec_skinny_gemm_w12(const void *x, int m, int kd, const spec_w12_matrix *w,
     if (rc != SPEC_OK) return rc;
     if (partial_bytes < skinny_total_bytes(g, m, n, kd)) return SPEC_EWORKSPACE;
     if (reinterpret_cast<uintptr_t>(partials) % 256 != 0) return SPEC_EINVAL;
+    if (reinterpret_cast<uintptr_t>(x) % 16 != 0) return SPEC_EINVAL;   // rows read 16 bytes at a time
     *splits = g.splits;
     bf16 *xp = reinterpret_cast<bf16 *>(reinterpret_cast<char *>(partials) +
                                         skinny_partial_bytes(g, m, n));
@@ -394,17 +399,22 @@ int spec_skinny_gemm_w12(const void *x, int m, int kd, const spec_w12_matrix *w,
     return SPEC_OK;
 }
 
-static int w12_shape(const void *w, int n, int kd) {
-    if (w == nullptr) return SPEC_EINVAL;
+static int w12_dims(int n, int kd) {
     if (n < 1 || kd < 1) return SPEC_EINVAL;
     if (n % 16 != 0 || kd % 32 != 0) return SPEC_EUNSUPPORTED;
     if ((int64_t)kd * 16 > (1 << 30)) return SPEC_EUNSUPPORTED;   // positions fit an int32
     return SPEC_OK;
 }
 
+// a row-major source matrix: read 16 bytes at a time
+static int w12_shape(const void *w, int n, int kd) {
+    if (w == nullptr || reinterpret_cast<uintptr_t>(w) % 16 != 0) return SPEC_EINVAL;
+    return w12_dims(n, kd);
+}
+
 int spec_w12_plan_ints(int n, int kd, size_t *ints) {
     if (ints == nullptr) return SPEC_EINVAL;
-    int rc = w12_shape(ints, n, kd);
+    int rc = w12_dims(n, kd);
     if (rc != SPEC_OK) return rc;
     *ints = (size_t)w12_plan_ints(n);
     return SPEC_OK;
