@@ -12,7 +12,8 @@ Workloads (--config):
   batched 32 requests x block of 16, contexts uniform in [512, 8192], shuffled 16-token pages
 --weights w12 stores the projections and the output head in the lossless 12-bit layout (batch-1
 workloads only); the results are bit-identical to bf16 and the step streams a quarter fewer
-weight bytes.
+weight bytes. A bf16 run of a batch-1 workload also times the same step over that layout and
+reports it in a `w12` object (--no-w12 skips it).
 
 Prints one JSON line: verified draft tokens/s (batch * k / step time), the step's algorithmic
 HBM bytes and GB/s, the roofline of the dominant kernel (the gate/up projection GEMM with its
@@ -163,6 +164,50 @@ def pmc_traffic(config, weights="bf16"):
     return int(round((rec["fetch_kib"] * rec["fetch_scale"] + rec["write_kib"] * rec["write_scale"]) * 1024))
 
 
+def time_w12(weights, shape, kv, t_tok, t_par, t_ctx, ctx0, B, K, ctx, acc, bonus, path, ws, stream,
+             steps, warmup):
+    """Step time over W12 weights built from the same row-major tensors: graph replays timed with
+    events around the whole run, like the main line. Also checks that the first W12 pass gives
+    the bf16 pass's logits bit for bit."""
+    R = weights.rowmajor
+    w = tv.Weights(weights.cfg, weights.tensors["embed"], weights.tensors["final_norm"], R["lm_head"],
+                   R["layers"], w12=True)
+    lg16 = torch.empty((B * K, shape.vocab), dtype=torch.float32, device=t_tok.device)
+    lg12 = torch.empty_like(lg16)
+    with torch.cuda.stream(stream):
+        tv.spec_verify(weights, kv, t_tok, t_par, t_ctx, B, K, acc, bonus, path, ws, logits=lg16)
+        tv.spec_verify(w, kv, t_tok, t_par, t_ctx, B, K, acc, bonus, path, ws, logits=lg12)
+        stream.synchronize()
+        same = bool(torch.equal(lg16.view(torch.int32), lg12.view(torch.int32)))
+
+        def step():
+            tv.spec_verify(w, kv, t_tok, t_par, t_ctx, B, K, acc, bonus, path, ws)
+            tv.spec_commit_kv(w.cfg, kv, acc, path, t_ctx, B, K)
+
+        t_ctx.copy_(ctx0)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            step()
+        for _ in range(warmup):
+            graph.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            graph.replay()
+        e1.record(stream)
+        e1.synchronize()
+    t_ctx.copy_(ctx0)
+    ms = e0.elapsed_time(e1) / steps
+    nbytes = step_bytes(shape, B, K, ctx, w.w12)
+    del graph, w
+    torch.cuda.empty_cache()
+    return {"ms_per_step": round(ms, 4), "value": round(B * K / (ms / 1e3), 2),
+            "unit": "verified tokens/s", "bytes_per_step": int(nbytes),
+            "achieved_gbps": round(nbytes / (ms / 1e3) / 1e9, 1),
+            "logits_bit_identical_to_bf16": same,
+            "note": "same step over the lossless 12-bit layout of the same weights"}
+
+
 def read_probe(device, nbytes=4 << 30):
     """Streaming-read rate: the library's plain grid-stride read of a 4 GiB buffer (HIP events
     on the current stream around 5 launches)."""
@@ -254,6 +299,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
+    ap.add_argument("--no-w12", action="store_true",
+                    help="skip the extra timing of the same step over lossless 12-bit weights")
     ap.add_argument("--weights", default="bf16", choices=["bf16", "w12"],
                     help="projection weight storage: bf16, or the lossless 12-bit layout (W12)")
     args = ap.parse_args()
@@ -416,6 +463,13 @@ def main():
         log(f"gate/up projection: {ach:.0f} {result['roofline']['unit']} per launch "
             f"({s_launch * 1e6:.1f} us avg, {s_launch * L * 1e3 / ms:.1%} of the step); "
             f"copy probe {result['copy_probe_gbps']} GB/s, read probe {rp:.1f} GB/s")
+    if not w12 and not args.no_w12 and B * K <= 64 and weights.rowmajor is not None:
+        # the same step over the lossless 12-bit layout of the same weights (bit-identical
+        # results), reported beside the bf16 line; `value` stays the bf16 measurement
+        t_ctx.copy_(ctx0)
+        result["w12"] = time_w12(weights, shape, kv, t_tok, t_par, t_ctx, ctx0, B, K, ctx, acc, bonus,
+                                 path, ws, stream, args.steps, args.warmup)
+        log(f"W12: {result['w12']}")
     if not args.no_cpu_baseline:
         t_ctx.copy_(ctx0)
         result["cpu_baseline"] = cpu_baseline(weights, shape, kv, tokens, parent, ctx,
