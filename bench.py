@@ -10,6 +10,7 @@ Workloads (--config):
   block   (default) batch 1, linear block of 16 uniform-random draft tokens, context 4096
   tree    batch 1, 64-node draft tree of depth <= 10, context 8192
   batched 32 requests x block of 16, contexts uniform in [512, 8192], shuffled 16-token pages
+  prefill (a separate line, its own metric) one 4096-token prompt from an empty context
 --weights w12 stores the projections and the output head in the lossless 12-bit layout (batch-1
 workloads only); the results are bit-identical to bf16 and the step streams a quarter fewer
 weight bytes. A bf16 run of a batch-1 workload also times the same step over that layout and
@@ -47,13 +48,13 @@ METRIC = "verified tokens/sec + verify-step HBM GB/s (% peak), 27B-shape dense, 
 # figures hold for the GEMM source they were taken on; any other source reports null.
 PMC_TRAFFIC = {
     ("block", "bf16"): {"source": "tree_verification_skinny_amd/csrc/k_gemm.hip",
-                        "sha256": "3712f553d304f9815d0b8c0ebbed0fd3277c375341304fca94a0974bbb1d79fe",
-                        "fetch_kib": 174761.256, "write_kib": 544.0,
-                        "fetch_scale": 1.9999849, "write_scale": 1.0},
+                        "sha256": "f373f9dd17953c6758f365c0a86324030f6a99ed9c58cb5019dcae725401a84e",
+                        "fetch_kib": 174761.283, "write_kib": 544.0,
+                        "fetch_scale": 1.9999858, "write_scale": 1.0},
     ("block", "w12"): {"source": "tree_verification_skinny_amd/csrc/k_gemm.hip",
-                       "sha256": "3712f553d304f9815d0b8c0ebbed0fd3277c375341304fca94a0974bbb1d79fe",
-                       "fetch_kib": 131460.943, "write_kib": 544.0,
-                       "fetch_scale": 1.9999860, "write_scale": 1.0},
+                       "sha256": "f373f9dd17953c6758f365c0a86324030f6a99ed9c58cb5019dcae725401a84e",
+                       "fetch_kib": 131470.243, "write_kib": 544.0,
+                       "fetch_scale": 1.9999851, "write_scale": 1.0},
 }
 HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0     # dense bf16 matrix-core peak of MI355X
@@ -289,12 +290,75 @@ def cpu_baseline(weights, shape, kv, tokens, parent, ctx, budget_s):
                        f"({step:.1f}s per step)")}
 
 
+def prefill_bench(args, shape, device):
+    """spec_prefill of one request's prompt from an empty context (chunks of 64 positions through
+    the verify kernels), replayed from a HIP graph; prints one JSON line with prompt tokens/s.
+    Algorithmic bytes: every weight once per chunk (embedding rows only for the prompt), each
+    chunk's K/V reads of the positions before it and its own K/V writes."""
+    P = args.prompt
+    w12 = args.weights == "w12"
+    weights = build_model(shape, device, w12)
+    pages = (P + 15) // 16
+    kv = tv.PagedKV.empty(tv.ModelCfg.of(shape), pages, torch.arange(pages, dtype=torch.int32).view(1, pages),
+                          device)
+    prompt = torch.from_numpy(synth.uniform_tokens(P, shape.vocab, SEED, "prefill").astype(np.int32)).to(device)
+    prompt = prompt.view(1, P)
+    ctx = torch.zeros(1, dtype=torch.int32, device=device)
+    nt = torch.empty(1, dtype=torch.int32, device=device)
+    ws = tv.workspace(tv.spec_prefill_workspace_bytes(weights.cfg, 1, pages), device)
+    stream = torch.cuda.Stream()
+
+    def run():
+        ctx.zero_()
+        tv.spec_prefill(weights, kv, prompt, ctx, nt, ws)
+
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        run()
+        stream.synchronize()
+        assert int(ctx.item()) == P and int(nt.item()) >= 0
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            run()
+        for _ in range(max(1, args.warmup // 2)):
+            graph.replay()
+        reps = max(2, min(args.steps, 5))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            graph.replay()
+        e1.record(stream)
+        e1.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    chunks = (P + 63) // 64
+    L, H, nkv, d = shape.n_layers, shape.hidden, shape.n_kv_heads, shape.head_dim
+    per_chunk_w = step_bytes(shape, 1, 0, [0], weights.w12)                # weights, no rows
+    kv_row = L * nkv * d * 2 * 2                                           # K and V of a position
+    kv_bytes = sum(min(64, P - 64 * c) * kv_row + 64 * c * kv_row for c in range(chunks))
+    nbytes = chunks * per_chunk_w + 2 * P * H + kv_bytes
+    gbps = nbytes / (ms / 1e3) / 1e9
+    result = {
+        "metric": "prefill prompt tokens/s, 27B-shape dense, 1 GPU", "value": round(P / (ms / 1e3), 1),
+        "unit": "prompt tokens/s", "n_gpus": 1, "steps": reps, "ms_per_prefill": round(ms, 3),
+        "higher_is_better": True, "dtype": "bf16",
+        "data": "synthetic (seeded random-init weights N(0,0.02), uniform prompt tokens)",
+        "config": {"workload": f"27B-shape dense, 64 layers + lm_head, batch 1, prompt {P} from an empty "
+                               f"context, {chunks} chunks of up to 64 positions",
+                   "weights": "W12 (lossless 12-bit)" if w12 else "bf16", "hip_graph": True},
+        "hbm": {"bytes_per_prefill": int(nbytes), "achieved_gbps": round(gbps, 1),
+                "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4)},
+    }
+    log(f"prefill of {P}: {ms:.2f} ms, {P / (ms / 1e3):.0f} tokens/s, {gbps:.0f} GB/s")
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="block", choices=["block", "tree", "batched"])
+    ap.add_argument("--config", default="block", choices=["block", "tree", "batched", "prefill"])
+    ap.add_argument("--prompt", type=int, default=4096, help="prompt length of --config prefill")
     ap.add_argument("--eager", action="store_true", help="launch every step instead of a HIP graph")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -313,6 +377,9 @@ def main():
         sys.exit(2)
     device = "cuda"
     shape = synth.DENSE_27B
+    if args.config == "prefill":
+        prefill_bench(args, shape, device)
+        return
     wl = workload(args.config)
     B, K, ctx = wl["batch"], wl["k"], wl["ctx"]
     total_steps = args.steps + args.warmup + 3 + 12     # + the kernel-timing replays

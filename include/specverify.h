@@ -74,13 +74,12 @@ typedef struct {
 } spec_layer_weights;
 
 /* One projection matrix [n][kd] in W12, the lossless 12-bit layout built by spec_w12_plan and
- * spec_w12_pack (DEVICE pointers): planes (spec_w12_planes_bytes), plan (spec_w12_plan_ints
- * ints), exc (2 ints per exception); paired as given to spec_w12_pack (1 for w_gate_up). */
+ * spec_w12_pack (DEVICE pointers): planes (n*kd*3/2 bytes), plan (spec_w12_plan_ints ints),
+ * exc (2 ints per exception). */
 typedef struct {
     const void *planes;
     const int32_t *plan;
     const int32_t *exc;
-    int paired;
 } spec_w12_matrix;
 
 typedef struct {
@@ -223,16 +222,10 @@ int spec_read_probe(const void *buf, size_t bytes, uint32_t *out, hipStream_t st
  *     nibble, and exc holds (position, bf16 bits) pairs sorted by tile, then position, where
  *     position = s * 512 + l * 8 + j for value j of slot l of step s (the slots of
  *     spec_pack_weight's order);
- *   - planes (spec_w12_planes_bytes: n*kd*3/2 bytes, the tile count rounded up to a multiple
- *     of four): the 16-row tiles in groups of four, the tiles one projection workgroup streams
- *     together: four consecutive tiles, or with paired = 1 (a SwiGLU gate/up matrix, rows
- *     [0, n/2) gate and [n/2, n) up) gate tiles 2g, 2g+1 and up tiles n/32 + 2g, n/32 + 2g + 1.
- *     For group g and 32-column step s (spec_pack_weight's steps) a 3072-byte block at
- *     (g * kd/32 + s) * 3072 holds slot l of the tile at position p (0..3) as three dwords
- *     d = 3p, 3p+1, 3p+2: the low bytes of its values 0..3 (byte j = value j), of values 4..7,
- *     and the nibbles (value 2i at bits 4i..4i+3, value 2i+1 at bits 16+4i..16+4i+3); dword d
- *     of slot l sits at dword 256 (d/4) + 4 l + d%4 of the block, so that three 16-byte loads
- *     per lane read one step of all four tiles;
+ *   - planes: fragment (tile t, step s) of spec_pack_weight's order is 768 bytes at
+ *     (t * (kd/32) + s) * 768, 12 bytes per slot l at 12 l: a dword of the low bytes of values
+ *     0..3 (byte j = value j), a dword of values 4..7, a dword of nibbles (value 2i at bits
+ *     4i..4i+3, value 2i+1 at bits 16+4i..16+4i+3);
  *   - plan (int32): [0] b, [1] exception count E, [2 .. 2 + n/16] per-tile exception offsets
  *     (exclusive prefix, n/16 + 1 entries), then 256 ints of scratch.
  * The format pays where the window holds nearly every weight (about 1e-4 of N(0, 0.02) weights
@@ -241,11 +234,9 @@ int spec_read_probe(const void *buf, size_t bytes, uint32_t *out, hipStream_t st
  * planes and 8-byte aligned exc (SPEC_EINVAL). One-time, load-time transforms, enqueued on
  * `stream`. */
 int spec_w12_plan_ints(int n, int kd, size_t *ints /* HOST */);
-int spec_w12_planes_bytes(int n, int kd, size_t *bytes /* HOST */);
 int spec_w12_plan(const void *w /* bf16 [n][kd] row-major */, int n, int kd, int32_t *plan,
                   hipStream_t stream);
-int spec_w12_pack(const void *w /* bf16 [n][kd] row-major */, int n, int kd,
-                  int paired /* 0, or 1 for a gate/up matrix (n % 64 == 0) */, const int32_t *plan,
+int spec_w12_pack(const void *w /* bf16 [n][kd] row-major */, int n, int kd, const int32_t *plan,
                   void *planes, int32_t *exc, hipStream_t stream);
 
 /* spec_skinny_gemm over a W12 matrix: the same partials, bit for bit, as spec_skinny_gemm over

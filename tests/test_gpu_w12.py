@@ -43,34 +43,14 @@ def with_exceptions(w: torch.Tensor, seed, frac=0.01, big=9.5) -> torch.Tensor:
     return w
 
 
-def w12_slot(tau, T, paired):
-    """(group, position) of tile tau: the header's grouping of tiles in fours."""
-    if paired:
-        h = T // 2
-        side = 1 if tau >= h else 0
-        k = tau - side * h
-        return k // 2, (k % 2) + 2 * side
-    return tau // 4, tau % 4
-
-
 def unpack_w12(m: tv.W12Matrix) -> oracle.W12:
     """The logical planes and exception list of a W12 matrix, read back from the layout the
-    header documents (tiles in groups of four, a 3072-byte block per group and step; dword d of
-    slot l at 256 (d/4) + 4 l + d%4; the tile at position p owns d = 3p .. 3p + 2: low bytes of
-    values 0..3, of values 4..7, nibbles)."""
+    header documents (fragment order, 12 bytes per slot: two dwords of low bytes, one of
+    nibbles)."""
     n, kd = m.n, m.kd
     S, T = kd // 32, n // 16
-    G = (T + 3) // 4
     plan = m.plan.cpu().numpy()
-    assert m.planes.numel() == G * S * 3072
-    blocks = m.planes.cpu().numpy().view(np.uint32).reshape(G, S, 768)
-    lane = np.arange(64)
-    words = np.empty((T, S, 3, 64), np.uint32)       # [tile][step][component][lane]
-    for tau in range(T):
-        g, pos = w12_slot(tau, T, m.paired)
-        for c in range(3):
-            d = 3 * pos + c
-            words[tau, :, c, :] = blocks[g][:, 256 * (d // 4) + 4 * lane + d % 4]
+    words = m.planes.cpu().numpy().view(np.uint32).reshape(T, S, 64, 3).transpose(0, 1, 3, 2)
     lo = np.empty((n, kd), np.uint8)
     nib = np.empty((n, kd), np.uint8)
     lane = np.arange(64)
@@ -99,15 +79,13 @@ def unpack_w12(m: tv.W12Matrix) -> oracle.W12:
                       (exc[:, 1][order] & 0xFFFF).astype(np.uint16))
 
 
-@pytest.mark.parametrize("n,kd,frac,paired", [(64, 256, 0.0, False), (64, 256, 0.01, False),
-                                              (1408, 256, 0.002, False), (32, 17408, 0.0005, False),
-                                              (1408, 256, 0.002, True), (128, 96, 0.05, True),
-                                              (80, 64, 0.01, False)])
-def test_w12_layout_matches_oracle_definition(n, kd, frac, paired):
+@pytest.mark.parametrize("n,kd,frac", [(64, 256, 0.0), (64, 256, 0.01), (1408, 256, 0.002),
+                                       (32, 17408, 0.0005)])
+def test_w12_layout_matches_oracle_definition(n, kd, frac):
     w = synth.randn_bf16((n, kd), 0.02, DEV, "w12l", n, kd)
     if frac:
         w = with_exceptions(w, (n, kd), frac)
-    m = tv.W12Matrix(w, paired=paired)
+    m = tv.W12Matrix(w)
     torch.cuda.synchronize()
     wb = bits(w.cpu()).reshape(-1)
     ref = oracle.w12_encode(wb)
@@ -118,7 +96,7 @@ def test_w12_layout_matches_oracle_definition(n, kd, frac, paired):
     np.testing.assert_array_equal(got.lo, ref.lo)
     np.testing.assert_array_equal(got.nib, ref.nib)
     np.testing.assert_array_equal(oracle.w12_decode(got), wb)
-    assert m.planes.numel() == ((n // 16 + 3) // 4) * (kd // 32) * 3072   # 1.5 bytes per value
+    assert m.planes.numel() == n * kd * 3 // 2
 
 
 @pytest.mark.parametrize("m,n,kd,frac", [(16, 7168, 5120, 0.0), (16, 5120, 17408, 1e-4),

@@ -53,8 +53,7 @@ class LayerWeightsC(ctypes.Structure):
 
 
 class W12MatrixC(ctypes.Structure):
-    _fields_ = [("planes", ctypes.c_void_p), ("plan", ctypes.c_void_p), ("exc", ctypes.c_void_p),
-                ("paired", ctypes.c_int)]
+    _fields_ = [("planes", ctypes.c_void_p), ("plan", ctypes.c_void_p), ("exc", ctypes.c_void_p)]
 
 
 class W12LayerC(ctypes.Structure):
@@ -106,9 +105,7 @@ def lib() -> ctypes.CDLL:
         L.spec_read_probe.argtypes = [vp, sz, vp, vp]
         L.spec_w12_plan_ints.argtypes = [i32, i32, ctypes.POINTER(sz)]
         L.spec_w12_plan.argtypes = [vp, i32, i32, vp, vp]
-        L.spec_w12_pack.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp]
-        L.spec_w12_planes_bytes.argtypes = [i32, i32, ctypes.POINTER(sz)]
-        L.spec_w12_planes_bytes.restype = i32
+        L.spec_w12_pack.argtypes = [vp, i32, i32, vp, vp, vp, vp]
         L.spec_skinny_gemm_w12.argtypes = [vp, i32, i32, ctypes.POINTER(W12MatrixC), i32, vp, sz,
                                            ctypes.POINTER(i32), vp]
         L.spec_prefill_workspace_bytes.argtypes = [ctypes.POINTER(ModelCfgC), i32, i32, i32,
@@ -128,7 +125,7 @@ def lib() -> ctypes.CDLL:
 
 EXPORTED = ("spec_workspace_bytes", "spec_verify", "spec_commit_kv", "spec_accept_workspace_bytes",
             "spec_accept", "spec_pack_weight", "spec_skinny_gemm_bytes", "spec_skinny_gemm",
-            "spec_read_probe", "spec_w12_plan_ints", "spec_w12_planes_bytes", "spec_w12_plan", "spec_w12_pack",
+            "spec_read_probe", "spec_w12_plan_ints", "spec_w12_plan", "spec_w12_pack",
             "spec_skinny_gemm_w12", "spec_prefill_workspace_bytes", "spec_prefill", "spec_strerror")
 
 
@@ -195,9 +192,7 @@ class W12Matrix:
     """One projection matrix in the library's lossless 12-bit layout (spec_w12_plan, then
     spec_w12_pack): planes (uint8, n*kd*3/2), plan (int32) and exceptions (int32 pairs)."""
 
-    def __init__(self, w: torch.Tensor, paired: bool = False, stream=None):
-        """paired: w is a SwiGLU gate/up matrix (gate rows, then up rows), grouped the way the
-        projection pairs them."""
+    def __init__(self, w: torch.Tensor, stream=None):
         n, kd = w.shape
         ints = ctypes.c_size_t(0)
         _check(lib().spec_w12_plan_ints(n, kd, ctypes.byref(ints)), "spec_w12_plan_ints")
@@ -206,17 +201,14 @@ class W12Matrix:
         _check(lib().spec_w12_plan(_ptr(w), n, kd, _ptr(self.plan), _stream(stream)), "spec_w12_plan")
         self.n_exc = int(self.plan[1].item())          # waits for the plan
         self.exc = torch.empty(max(2 * self.n_exc, 2), dtype=torch.int32, device=w.device)
-        pb = ctypes.c_size_t(0)
-        _check(lib().spec_w12_planes_bytes(n, kd, ctypes.byref(pb)), "spec_w12_planes_bytes")
-        self.planes = torch.empty(pb.value, dtype=torch.uint8, device=w.device)
-        self.paired = 1 if paired else 0
-        _check(lib().spec_w12_pack(_ptr(w), n, kd, self.paired, _ptr(self.plan), _ptr(self.planes),
-                                   _ptr(self.exc), _stream(stream)), "spec_w12_pack")
-        self.c = W12MatrixC(_ptr(self.planes), _ptr(self.plan), _ptr(self.exc), self.paired)
+        self.planes = torch.empty(n * kd * 3 // 2, dtype=torch.uint8, device=w.device)
+        _check(lib().spec_w12_pack(_ptr(w), n, kd, _ptr(self.plan), _ptr(self.planes), _ptr(self.exc),
+                                   _stream(stream)), "spec_w12_pack")
+        self.c = W12MatrixC(_ptr(self.planes), _ptr(self.plan), _ptr(self.exc))
 
     def nbytes(self) -> int:
         """Bytes a pass streams: the planes, the per-tile offsets and the exceptions."""
-        return self.n * self.kd * 3 // 2 + 4 * (self.n // 16 + 1) + 8 * self.n_exc
+        return self.planes.numel() + 4 * (self.n // 16 + 1) + 8 * self.n_exc
 
 
 def spec_skinny_gemm_w12(x: torch.Tensor, w: W12Matrix, partials: torch.Tensor, stream=None) -> int:
@@ -253,8 +245,7 @@ class Weights:
             if not drop_rowmajor:
                 self.rowmajor = dict(lm_head=lm_head, layers=list(layers))
             self.w12 = dict(lm_head=W12Matrix(lm_head),
-                            layers=[{k: W12Matrix(lw[k], paired=(k == "w_gate_up")) for k in PACKED_KEYS}
-                                    for lw in layers])
+                            layers=[{k: W12Matrix(lw[k]) for k in PACKED_KEYS} for lw in layers])
             self._w12_layers = (W12LayerC * cfg.n_layers)(
                 *[W12LayerC(*[m[k].c for k in PACKED_KEYS]) for m in self.w12["layers"]])
             w12_head = self.w12["lm_head"].c

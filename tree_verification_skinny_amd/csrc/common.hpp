@@ -62,24 +62,6 @@ __device__ __forceinline__ int64_t frag_off(int64_t r, int c, int cols) {
     return (((r >> 4) * (cols >> 5) + (c >> 5)) * 64 + (r & 15) + 16 * ((c >> 3) & 3)) * 8 + (c & 7);
 }
 
-// W12 planes: tiles are stored in groups of four (a "quad"), per 32-column step, 3072 bytes a
-// group; the tile at position p of a group holds, for lane l, the dwords d = 3p .. 3p + 2 of the
-// lane's 12, dword d at dword offset 256 (d / 4) + 4 l + d % 4 of the group's step block. Groups
-// are four consecutive tiles, or, for a SwiGLU gate/up matrix (paired), two consecutive gate
-// tiles and the matching two up tiles. Returns (group, position) of tile tau of T.
-__device__ __forceinline__ int2 w12_slot(int tau, int T, int paired) {
-    if (paired) {
-        const int h = T >> 1;
-        const int side = tau >= h ? 1 : 0;
-        const int k = tau - side * h;
-        return make_int2(k >> 1, (k & 1) + 2 * side);
-    }
-    return make_int2(tau >> 2, tau & 3);
-}
-
-// Dword offset of component d (0..11) of lane l within a W12 group's step block.
-__device__ __forceinline__ int w12_dword(int d, int lane) { return 256 * (d >> 2) + 4 * lane + (d & 3); }
-
 // Four bf16 values to one 8-byte store.
 __device__ __forceinline__ void store4(bf16 *dst, float a, float b, float c, float d) {
     bf16 v[4] = {to_bf(a), to_bf(b), to_bf(c), to_bf(d)};

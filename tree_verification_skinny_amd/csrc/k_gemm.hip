@@ -170,15 +170,10 @@ struct Acc {
     floatx4 v[NT][MT];
 };
 
-// WF: 0 bf16 weights; 1 W12 weights, each tile's fragment read on its own (three dwords per
-// lane); 2 W12 weights whose four tiles form one stored group in order (three 16-byte loads per
-// lane read one step of all four).
-template <int NT, int MT, int W, int EPI, int WF>
+template <int NT, int MT, int W, int EPI, bool W12>
 __global__ __launch_bounds__(64 * W) void gemm_kernel(GemmIn in, const bf16 *__restrict__ Wp,
                                                       W12Ref w12, int N, int Kd, int n_groups,
                                                       int ksteps, GemmEpi ep) {
-    constexpr bool W12 = WF != 0;
-    static_assert(WF != 2 || NT == 4, "a stored group is four tiles");
     __shared__ floatx4 red[(W - 1) * NT * MT * 64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r16 = lane & 15, grp = lane >> 4;
@@ -191,8 +186,7 @@ __global__ __launch_bounds__(64 * W) void gemm_kernel(GemmIn in, const bf16 *__r
     const int m0 = in.m0;          // first global row of the chunk
 
     const bf16 *wp[NT];
-    const uint32_t *qp[NT];          // W12: the tile's group, step 0
-    int qd[NT];                      // W12: the tile's first dword within its group (3 x position)
+    const uint32_t *qp[NT];          // W12: lane's 12 bytes in the tile's first fragment
     W12Cursor cur[NT];
     uint32_t cb = 0;
     const int wv = __builtin_amdgcn_readfirstlane(wave);
@@ -201,9 +195,7 @@ __global__ __launch_bounds__(64 * W) void gemm_kernel(GemmIn in, const bf16 *__r
     for (int t = 0; t < NT; ++t) {
         const int tile = tile_col<NT, EPI>(ng, t, ep.F) >> 4;
         if constexpr (W12) {
-            const int2 sl = w12_slot(tile, N >> 4, w12.paired);
-            qp[t] = w12.planes + (int64_t)sl.x * S * 768;
-            qd[t] = 3 * sl.y;
+            qp[t] = w12.planes + ((int64_t)tile * S) * 192 + 3 * lane;
             cur[t].i = w12.plan[2 + tile];
             cur[t].end = w12.plan[3 + tile];
         } else {
@@ -244,51 +236,21 @@ __global__ __launch_bounds__(64 * W) void gemm_kernel(GemmIn in, const bf16 *__r
     // bytes in flight per wave
     constexpr int U16 = (NT * MT >= 8 || (W == 8 && NT * MT == 4)) ? 2 : 4;
     constexpr int U = W12 ? (NT * MT >= 8 ? 2 : (EPI == EPI_PARTIAL ? SV_W12_U : SV_W12_U_WHOLE)) : U16;
-    // lane's three dwords of tile t at step st (W12)
-    auto w12_load = [&](uint32_t (&r)[3], int t, int st) {
-        const uint32_t *blk = qp[t] + (int64_t)st * 768;
-#pragma unroll
-        for (int c = 0; c < 3; ++c) r[c] = stream_load32(blk + w12_dword(qd[t] + c, lane));
-    };
-    // lane's twelve dwords of the group at step st (WF == 2): tile t's are r[3t .. 3t + 2]
-    auto w12_load_group = [&](uint32_t (&r)[12], int st) {
-        const u32x4 *f = reinterpret_cast<const u32x4 *>(qp[0] + (int64_t)st * 768) + lane;
-#pragma unroll
-        for (int i = 0; i < 3; ++i) {
-            const u32x4 v = __builtin_nontemporal_load(f + 64 * i);
-            r[4 * i] = v.x;
-            r[4 * i + 1] = v.y;
-            r[4 * i + 2] = v.z;
-            r[4 * i + 3] = v.w;
-        }
-    };
     int s = s_begin + wv;
     for (; s + W * (U - 1) < s_end; s += W * U) {
         bf16x8 a[U][NT], b[U][MT];
         uint32_t r0[U][NT], r1[U][NT], rh[U][NT];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            if constexpr (WF == 2) {
-                uint32_t r[12];
-                w12_load_group(r, s + W * u);
 #pragma unroll
-                for (int t = 0; t < NT; ++t) {
-                    r0[u][t] = r[3 * t];
-                    r1[u][t] = r[3 * t + 1];
-                    rh[u][t] = r[3 * t + 2];
-                }
-            } else {
-#pragma unroll
-                for (int t = 0; t < NT; ++t) {
-                    if constexpr (W12) {
-                        uint32_t r[3];
-                        w12_load(r, t, s + W * u);
-                        r0[u][t] = r[0];
-                        r1[u][t] = r[1];
-                        rh[u][t] = r[2];
-                    } else {
-                        a[u][t] = stream_load((const bf16x8 *)(wp[t] + (int64_t)(s + W * u) * 512));
-                    }
+            for (int t = 0; t < NT; ++t) {
+                if constexpr (W12) {
+                    const uint32_t *f = qp[t] + (int64_t)(s + W * u) * 192;
+                    r0[u][t] = stream_load32(f);
+                    r1[u][t] = stream_load32(f + 1);
+                    rh[u][t] = stream_load32(f + 2);
+                } else {
+                    a[u][t] = stream_load((const bf16x8 *)(wp[t] + (int64_t)(s + W * u) * 512));
                 }
             }
         }
@@ -310,20 +272,11 @@ __global__ __launch_bounds__(64 * W) void gemm_kernel(GemmIn in, const bf16 *__r
     }
     for (; s < s_end; s += W) {
         bf16x8 a[NT], b[MT];
-        uint32_t rg[12];
-        if constexpr (WF == 2) w12_load_group(rg, s);
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             if constexpr (W12) {
-                uint32_t r[3];
-                if constexpr (WF == 2) {
-                    r[0] = rg[3 * t];
-                    r[1] = rg[3 * t + 1];
-                    r[2] = rg[3 * t + 2];
-                } else {
-                    w12_load(r, t, s);
-                }
-                a[t] = w12_decode(r[0], r[1], r[2], cb);
+                const uint32_t *f = qp[t] + (int64_t)s * 192;
+                a[t] = w12_decode(stream_load32(f), stream_load32(f + 1), stream_load32(f + 2), cb);
                 if (s >= cur[t].step) a[t] = w12_fixup(a[t], cur[t], w12.exc, s, lane);
             } else {
                 a[t] = stream_load((const bf16x8 *)(wp[t] + (int64_t)s * 512));
@@ -469,8 +422,7 @@ __global__ __launch_bounds__(64 * kWideWaves) void gemm_wide_kernel(GemmIn in, c
     const int nblk = (in.M_total + 15) >> 4;
 
     const bf16 *wp[TN];
-    const uint32_t *qp[TN];          // W12: the tile's group at step s_begin
-    int qd[TN];                      // W12: the tile's first dword within its group
+    const uint32_t *qp[TN];          // W12: lane's 12 bytes in the tile's fragment at s_begin
     W12Cursor cur[TN];
     uint32_t cb = 0;
     if constexpr (W12) cb = (uint32_t)(w12.plan[0] >> 1) * 0x01000100u;
@@ -478,9 +430,7 @@ __global__ __launch_bounds__(64 * kWideWaves) void gemm_wide_kernel(GemmIn in, c
     for (int t = 0; t < TN; ++t) {
         const int tile = wide_col<EPI>(ng, wave, t, ep.F) >> 4;
         if constexpr (W12) {
-            const int2 sl = w12_slot(tile, N >> 4, w12.paired);
-            qp[t] = w12.planes + ((int64_t)sl.x * S + s_begin) * 768;
-            qd[t] = 3 * sl.y;
+            qp[t] = w12.planes + ((int64_t)tile * S + s_begin) * 192 + 3 * lane;
             cur[t].i = w12.plan[2 + tile];
             cur[t].end = w12.plan[3 + tile];
         } else {
@@ -523,10 +473,8 @@ __global__ __launch_bounds__(64 * kWideWaves) void gemm_wide_kernel(GemmIn in, c
 #pragma unroll
             for (int t = 0; t < TN; ++t) {
                 if constexpr (W12) {
-                    const uint32_t *blk = qp[t] + (int64_t)s * 768;
-                    a[k][t] = s < nsteps ? W12Raw{stream_load32(blk + w12_dword(qd[t], lane)),
-                                                  stream_load32(blk + w12_dword(qd[t] + 1, lane)),
-                                                  stream_load32(blk + w12_dword(qd[t] + 2, lane))}
+                    const uint32_t *f = qp[t] + (int64_t)s * 192;
+                    a[k][t] = s < nsteps ? W12Raw{stream_load32(f), stream_load32(f + 1), stream_load32(f + 2)}
                                          : W12Raw{0u, 0u, 0u};
                 } else {
                     a[k][t] = s < nsteps ? stream_load((const bf16x8 *)(wp[t] + (int64_t)s * 512)) : bf16x8{};
@@ -671,17 +619,11 @@ static hipError_t launch(const GemmShape &g, const GemmIn &in, const bf16 *Wp, c
                          const GemmEpi &ep, hipStream_t st) {
     const int steps = g.Kd >> 5;
     const int ks = (steps + g.splits - 1) / g.splits;
-    // W12: the workgroup's four tiles are one stored group when the matrix was grouped the way
-    // this epilogue pairs its tiles (SwiGLU: gate/up pairs; otherwise consecutive tiles)
-    const bool grouped = NT == 4 && (w12.paired != 0) == (EPI == EPI_SWIGLU);
-    if (w12.planes == nullptr)
-        hipLaunchKernelGGL((gemm_kernel<NT, MT, W, EPI, 0>), dim3(gemm_groups(g) * g.splits), dim3(64 * W),
+    if (w12.planes != nullptr)
+        hipLaunchKernelGGL((gemm_kernel<NT, MT, W, EPI, true>), dim3(gemm_groups(g) * g.splits), dim3(64 * W),
                            0, st, in, Wp, w12, g.N, g.Kd, gemm_groups(g), ks, ep);
-    else if (!grouped)
-        hipLaunchKernelGGL((gemm_kernel<NT, MT, W, EPI, 1>), dim3(gemm_groups(g) * g.splits), dim3(64 * W),
-                           0, st, in, Wp, w12, g.N, g.Kd, gemm_groups(g), ks, ep);
-    else if constexpr (NT == 4)
-        hipLaunchKernelGGL((gemm_kernel<NT, MT, W, EPI, 2>), dim3(gemm_groups(g) * g.splits), dim3(64 * W),
+    else
+        hipLaunchKernelGGL((gemm_kernel<NT, MT, W, EPI, false>), dim3(gemm_groups(g) * g.splits), dim3(64 * W),
                            0, st, in, Wp, w12, g.N, g.Kd, gemm_groups(g), ks, ep);
     return hipGetLastError();
 }

@@ -13,16 +13,14 @@
 //   * a value outside the window is an exception: its planes hold the low byte and a zero
 //     nibble, and (position, 16-bit value) goes into a per-matrix list sorted by tile, then
 //     position, which the GEMM applies in registers after decoding.
-// Physical order: for every group of four tiles (w12_slot: four consecutive tiles, or for a
-// SwiGLU gate/up matrix two gate tiles and the matching two up tiles, the four tiles one
-// projection workgroup streams together) and every 32-column step s, a 3072-byte block at
-// (group * S + s) * 3072. In it, lane l (row 16t + l%16, columns 32s + 8(l/16) .. +7 of the tile
-// at position p, values v0..v7) owns dwords d = 3p + c:
-//   c = 0: low bytes of v0..v3 (byte j = v_j), c = 1: low bytes of v4..v7,
-//   c = 2: nibbles, v_{2i} at bits 4i..4i+3, v_{2i+1} at bits 16+4i..16+4i+3
-//          (one shift and mask put a pair's two nibbles under the high bytes of a bf16 pair),
-// and dword d of lane l sits at dword 256 (d/4) + 4 l + d%4: three 16-byte loads per lane (1 KB
-// per wave instruction) read one step of all four tiles.
+// Physical order follows the bf16 fragment order (16-row tiles, 32-column steps): fragment
+// (tile t, step s) is 768 bytes at (t * S + s) * 768, 12 bytes per lane, so that one 12-byte
+// load per lane reads a whole fragment. For lane l (row 16t + l%16, columns 32s + 8(l/16) .. +7,
+// values v0..v7), at dword 3l of the fragment:
+//   dword 3l     = low bytes of v0..v3 (byte j = v_j),
+//   dword 3l + 1 = low bytes of v4..v7,
+//   dword 3l + 2 = nibbles: v_{2i} at bits 4i..4i+3, v_{2i+1} at bits 16+4i..16+4i+3,
+// so that one shift and mask put a pair's two nibbles under the high bytes of a bf16 pair.
 // An exception entry is (s * 512 + l * 8 + j, bf16 bits).
 //
 // Plan (int32): [0] b, [1] total exceptions, [2 .. 2 + T] exception offsets per tile (T + 1
@@ -112,9 +110,9 @@ __global__ __launch_bounds__(256) void w12_scan_kernel(int32_t *__restrict__ pla
     }
 }
 
-// Planes and exception entries: one wave per tile, walking its steps in order; lanes take their
-// exception slots by an in-wave exclusive prefix so the list is sorted by position.
-__global__ __launch_bounds__(64) void w12_pack_kernel(const uint16_t *__restrict__ w, int kd, int paired,
+// Planes and exception entries: one wave per tile, walking its steps in order; lanes take
+// their exception slots by an in-wave exclusive prefix so the list is sorted by position.
+__global__ __launch_bounds__(64) void w12_pack_kernel(const uint16_t *__restrict__ w, int kd,
                                                       const int32_t *__restrict__ plan,
                                                       uint32_t *__restrict__ planes,
                                                       int2 *__restrict__ exc) {
@@ -122,7 +120,6 @@ __global__ __launch_bounds__(64) void w12_pack_kernel(const uint16_t *__restrict
     const int lane = threadIdx.x;
     const int b = plan[0];
     const int S = kd >> 5;
-    const int2 sl = w12_slot(tile, gridDim.x, paired);
     int32_t next = plan[2 + tile];
     const int64_t row = (int64_t)tile * 16 + (lane & 15);
     for (int s = 0; s < S; ++s) {
@@ -142,10 +139,10 @@ __global__ __launch_bounds__(64) void w12_pack_kernel(const uint16_t *__restrict
             nib |= n4 << ((j & 1) ? 16 + 4 * (j >> 1) : 4 * (j >> 1));
             if (!fits) esc_mask |= 1 << j;
         }
-        uint32_t *blk = planes + ((int64_t)sl.x * S + s) * 768;
-        blk[w12_dword(3 * sl.y, lane)] = lo0;
-        blk[w12_dword(3 * sl.y + 1, lane)] = lo1;
-        blk[w12_dword(3 * sl.y + 2, lane)] = nib;
+        uint32_t *f = planes + ((int64_t)tile * S + s) * 192 + 3 * lane;
+        f[0] = lo0;
+        f[1] = lo1;
+        f[2] = nib;
         const int cnt = __popc(esc_mask);
         // in-wave exclusive prefix of the counts
         int incl = cnt;
@@ -169,15 +166,7 @@ __global__ __launch_bounds__(64) void w12_pack_kernel(const uint16_t *__restrict
     }
 }
 
-// Zeros for the unused positions of a last, partial group of tiles.
-__global__ void w12_zero_kernel(uint32_t *__restrict__ p, int64_t n) {
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
-        p[i] = 0u;
-}
-
 int w12_plan_ints(int n) { return 2 + (n / 16 + 1) + 256; }
-
-int64_t w12_planes_bytes(int n, int kd) { return (int64_t)((n / 16 + 3) / 4) * (kd / 32) * 3072; }
 
 hipError_t w12_plan(const bf16 *w, int n, int kd, int32_t *plan, hipStream_t st) {
     const int tiles = n / 16;
@@ -195,14 +184,10 @@ hipError_t w12_plan(const bf16 *w, int n, int kd, int32_t *plan, hipStream_t st)
     return hipGetLastError();
 }
 
-hipError_t w12_pack(const bf16 *w, int n, int kd, int paired, const int32_t *plan, uint32_t *planes,
-                    int2 *exc, hipStream_t st) {
-    if ((n / 16) % 4 != 0) {
-        const int64_t words = w12_planes_bytes(n, kd) / 4;
-        hipLaunchKernelGGL(w12_zero_kernel, dim3(1024), dim3(256), 0, st, planes, words);
-    }
+hipError_t w12_pack(const bf16 *w, int n, int kd, const int32_t *plan, uint32_t *planes, int2 *exc,
+                    hipStream_t st) {
     hipLaunchKernelGGL(w12_pack_kernel, dim3(n / 16), dim3(64), 0, st,
-                       reinterpret_cast<const uint16_t *>(w), kd, paired, plan, planes, exc);
+                       reinterpret_cast<const uint16_t *>(w), kd, plan, planes, exc);
     return hipGetLastError();
 }
 

@@ -47,13 +47,11 @@ struct W12Ref {
     const uint32_t *planes;
     const int32_t *plan;
     const int2 *exc;
-    int paired;       // tiles grouped as SwiGLU gate/up pairs (see k_w12.hip)
 };
 int w12_plan_ints(int n);
-int64_t w12_planes_bytes(int n, int kd);
 hipError_t w12_plan(const bf16 *w, int n, int kd, int32_t *plan, hipStream_t st);
-hipError_t w12_pack(const bf16 *w, int n, int kd, int paired, const int32_t *plan, uint32_t *planes,
-                    int2 *exc, hipStream_t st);
+hipError_t w12_pack(const bf16 *w, int n, int kd, const int32_t *plan, uint32_t *planes, int2 *exc,
+                    hipStream_t st);
 
 int gemm_groups(const GemmShape &g);
 GemmShape plan_gemm(int M, int N, int Kd, bool allow_split, bool allow_tc = true);

@@ -127,7 +127,6 @@ W12Ref w12_ref(const spec_w12_matrix &m) {
     r.planes = static_cast<const uint32_t *>(m.planes);
     r.plan = m.plan;
     r.exc = reinterpret_cast<const int2 *>(m.exc);
-    r.paired = m.paired;
     return r;
 }
 
@@ -429,24 +428,14 @@ int spec_w12_plan(const void *w, int n, int kd, int32_t *plan, hipStream_t strea
     return SPEC_OK;
 }
 
-int spec_w12_planes_bytes(int n, int kd, size_t *bytes) {
-    if (bytes == nullptr) return SPEC_EINVAL;
-    int rc = w12_dims(n, kd);
-    if (rc != SPEC_OK) return rc;
-    *bytes = (size_t)w12_planes_bytes(n, kd);
-    return SPEC_OK;
-}
-
-int spec_w12_pack(const void *w, int n, int kd, int paired, const int32_t *plan, void *planes,
-                  int32_t *exc, hipStream_t stream) {
+int spec_w12_pack(const void *w, int n, int kd, const int32_t *plan, void *planes, int32_t *exc,
+                  hipStream_t stream) {
     int rc = w12_shape(w, n, kd);
     if (rc != SPEC_OK) return rc;
-    if (paired != 0 && paired != 1) return SPEC_EINVAL;
-    if (paired && n % 64 != 0) return SPEC_EUNSUPPORTED;   // halves of whole tile pairs
     if (plan == nullptr || planes == nullptr || exc == nullptr) return SPEC_EINVAL;
     if (reinterpret_cast<uintptr_t>(planes) % 16 != 0 || reinterpret_cast<uintptr_t>(exc) % 8 != 0)
         return SPEC_EINVAL;
-    SV_TRY(w12_pack(static_cast<const bf16 *>(w), n, kd, paired, plan, static_cast<uint32_t *>(planes),
+    SV_TRY(w12_pack(static_cast<const bf16 *>(w), n, kd, plan, static_cast<uint32_t *>(planes),
                     reinterpret_cast<int2 *>(exc), stream));
     return SPEC_OK;
 }
