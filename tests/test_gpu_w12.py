@@ -224,3 +224,26 @@ def test_w12_root_only_pass_equals_bf16():
     assert np.array_equal(outs[0].logits.view(np.int32), outs[1].logits.view(np.int32))
     assert outs[0].accepted_len[0] == outs[1].accepted_len[0] == 0
     assert outs[0].bonus[0] == outs[1].bonus[0]
+
+
+@pytest.mark.parametrize("m,n,kd", [(130, 1024, 512), (200, 384, 96)])
+def test_w12_gemm_beyond_128_rows_in_chunks(m, n, kd):
+    """From 128 rows the W12 projection runs 64-row chunks (the wide or skinny kernel per chunk)
+    where bf16 switches to its matrix-core tile kernel: checked against float64 within the fp32
+    summation bound, with exceptions planted."""
+    x = synth.randn_bf16((m, kd), 1.0, DEV, "w12xc", m, n)
+    w = with_exceptions(synth.randn_bf16((n, kd), 0.02, DEV, "w12wc", m, n), (m, n, "c"), 0.01)
+    q = tv.W12Matrix(w)
+    part = torch.full((tv.spec_skinny_gemm_bytes(m, n, kd) // 4,), float("nan"), device=DEV)
+    s = tv.spec_skinny_gemm_w12(x, q, part)
+    torch.cuda.synchronize()
+    p = part[:s * m * n].view(s, m, n).cpu().numpy()
+    y = p[0].copy()
+    for i in range(1, s):
+        y += p[i]
+    xf = x.float().cpu().numpy().astype(np.float64)
+    wf = w.float().cpu().numpy().astype(np.float64)
+    ref = xf @ wf.T
+    gamma = kd * U32 / (1 - kd * U32)
+    bound = gamma * (np.abs(xf) @ np.abs(wf).T) + s * U32 * np.abs(ref)
+    assert np.all(np.abs(y - ref) <= bound)
