@@ -13,6 +13,10 @@ steps of the definition:
   [SpecPilot digest, airadar.tv — "Risks"].
 * ar_greedy: plain one-token-at-a-time greedy decoding, the result verification must equal.
 * commit: the accepted path's K/V rows appended to the committed context.
+* rec_tree / rec_commit: a recurrent layer of a hybrid target verified over a draft tree (every
+  node continues its parent's state) and its state after acceptance; the recurrence is a
+  reading, since the pages only name tree verification for such targets [SpecPilot digest,
+  airadar.tv — "Reasons"].
 
 Arrays: bf16 tensors travel as ``numpy.uint16`` bit patterns. K/V caches are per layer,
 ``[positions][n_kv][head_dim]``.
@@ -96,6 +100,11 @@ def lib():
         L.orc_argmax.argtypes = [_f32p, ctypes.c_int, ctypes.c_int, _i32p, _f32p]
         L.orc_accept.argtypes = [_i32p, _i32p, _i32p, ctypes.c_int, _i32p, _i32p, _i32p]
         L.orc_accept.restype = ctypes.c_int
+        _f64p = ctypes.POINTER(ctypes.c_double)
+        L.orc_rec_tree.argtypes = [_f32p, _u16p, _u16p, _u16p, _f32p, _i32p, ctypes.c_int,
+                                   ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, _f64p, _i32p]
+        L.orc_rec_commit.argtypes = [_f32p, _u16p, _u16p, _f32p, _i32p, _i32p, ctypes.c_int,
+                                     ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, _f64p]
         _lib = L
     return _lib
 
@@ -444,4 +453,48 @@ def w12_decode(c: W12) -> np.ndarray:
     lib().orc_w12_decode(lo.ctypes.data_as(u8), nib.ctypes.data_as(u8), lo.size, c.base,
                          idx.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), _p(val, _u16p), idx.size,
                          _p(out, _u16p))
+    return out
+
+
+# ---------------------------------------------------------------------------------------------
+# recurrent layers of a hybrid target
+# ---------------------------------------------------------------------------------------------
+# Reading (the pages name tree verification for targets with recurrent layers [SpecPilot digest,
+# airadar.tv — "Reasons"] but give no recurrence): per head, a scalar-gated linear recurrence
+# S <- exp(g) S + k v^T, o = S^T q, the node's state continuing its parent's, the root's the
+# committed state. Computed by walking each node's root path token by token, in float64.
+
+def rec_tree(S0: np.ndarray, q: np.ndarray, k: np.ndarray, v: np.ndarray, g: np.ndarray,
+             parent: Optional[np.ndarray]):
+    """Outputs [B][K][H][dv] (float64) and status [B] (1 = malformed tree, outputs zero).
+
+    S0 fp32 [B][H][dk][dv]; q, k bf16 bits [B][K][H][dk]; v bf16 bits [B][K][H][dv];
+    g fp32 [B][K][H]; parent int32 [B][K] or None for chains."""
+    B, H, dk, dv = S0.shape
+    K = q.shape[1]
+    S0 = _c(S0, np.float32)
+    q, k, v = _c(q, np.uint16), _c(k, np.uint16), _c(v, np.uint16)
+    g = _c(g, np.float32)
+    par = None if parent is None else _c(parent, np.int32)
+    out = np.empty((B, K, H, dv), np.float64)
+    st = np.empty(B, np.int32)
+    f64 = ctypes.POINTER(ctypes.c_double)
+    lib().orc_rec_tree(_p(S0, _f32p), _p(q, _u16p), _p(k, _u16p), _p(v, _u16p), _p(g, _f32p),
+                       _p(par, _i32p), B, K, H, dk, dv, out.ctypes.data_as(f64), _p(st, _i32p))
+    return out, st
+
+
+def rec_commit(S0: np.ndarray, k: np.ndarray, v: np.ndarray, g: np.ndarray,
+               accepted_len: np.ndarray, accepted_path: np.ndarray) -> np.ndarray:
+    """State [B][H][dk][dv] (float64) after the accepted root path (S0 where accepted_len < 0)."""
+    B, H, dk, dv = S0.shape
+    K = k.shape[1]
+    S0 = _c(S0, np.float32)
+    k, v = _c(k, np.uint16), _c(v, np.uint16)
+    g = _c(g, np.float32)
+    al = _c(accepted_len, np.int32)
+    ap = _c(accepted_path, np.int32)
+    out = np.empty((B, H, dk, dv), np.float64)
+    lib().orc_rec_commit(_p(S0, _f32p), _p(k, _u16p), _p(v, _u16p), _p(g, _f32p), _p(al, _i32p),
+                         _p(ap, _i32p), B, K, H, dk, dv, out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)))
     return out

@@ -449,3 +449,109 @@ void orc_w12_decode(const uint8_t *lo, const uint8_t *nib, int64_t n, int b,
     }
     for (int64_t j = 0; j < n_esc; ++j) out[esc_idx[j]] = esc_val[j];
 }
+
+/* ------------------------------------------------------------------------------------------ */
+/* Recurrent layers of a hybrid target: tree verification by forking the state                 */
+/* ------------------------------------------------------------------------------------------ */
+/* The SpecPilot digest (airadar.tv — "Reasons") and news piece (wireai.ir — key innovations)
+ * name tree verification for targets that mix recurrent layers in, without giving the
+ * recurrence. The reading used here is a scalar-gated linear recurrence per head (the form of
+ * gated linear attention and of Mamba-2's state-space layer): with a state S of dk x dv values,
+ *     S <- a S + k v^T,   a = exp(g),   then   o = S^T q,
+ * for each token, with q, k in R^dk, v in R^dv and the log-gate g <= 0 per (token, head).
+ * In a draft tree every node continues its parent's state, and the root continues the committed
+ * state S0. The oracle runs that definition as written: for each node it walks the node's root
+ * path and applies the recurrence token by token from S0, in float64. Inputs q, k, v are bf16,
+ * S0 and g fp32. Layouts: S0 [B][H][dk][dv], q and k [B][K][H][dk], v [B][K][H][dv],
+ * g [B][K][H], out [B][K][H][dv]. */
+
+/* Root path of node i (root first) into path[]; its length, or -1 if a parent link is
+ * malformed (the root's parent must be -1, any other node's parent an earlier node). */
+static int rec_path(const int32_t *parent, int k, int i, int *path) {
+    int n = 0;
+    for (int j = i; j != -1; j = parent[j]) {
+        if (n >= k) return -1;
+        if (j == 0 ? parent[0] != -1 : (parent[j] < 0 || parent[j] >= j)) return -1;
+        path[n++] = j;
+    }
+    for (int a = 0, b = n - 1; a < b; ++a, --b) {
+        const int t = path[a];
+        path[a] = path[b];
+        path[b] = t;
+    }
+    return n;
+}
+
+/* The state after the tokens path[0..n-1] of request b, head h, from S0 (float64 [dk][dv]). */
+static void rec_run(const float *S0, const uint16_t *kk, const uint16_t *v, const float *g,
+                    int K, int H, int dk, int dv, int b, int h, const int *path, int n, double *S) {
+    const float *s0 = S0 + ((int64_t)b * H + h) * dk * dv;
+    for (int64_t e = 0; e < (int64_t)dk * dv; ++e) S[e] = s0[e];
+    for (int t = 0; t < n; ++t) {
+        const int64_t tok = (int64_t)b * K + path[t];
+        const double a = exp((double)g[tok * H + h]);
+        const uint16_t *kr = kk + (tok * H + h) * dk;
+        const uint16_t *vr = v + (tok * H + h) * dv;
+        for (int r = 0; r < dk; ++r) {
+            const double kv = bf16_to_f32(kr[r]);
+            for (int c = 0; c < dv; ++c)
+                S[(int64_t)r * dv + c] = a * S[(int64_t)r * dv + c] + kv * (double)bf16_to_f32(vr[c]);
+        }
+    }
+}
+
+/* Outputs o = S_i^T q_i of every node (float64). parent NULL = a chain. status[b] = 1 for a
+ * malformed tree (its outputs zero), else 0. */
+void orc_rec_tree(const float *S0, const uint16_t *q, const uint16_t *kk, const uint16_t *v,
+                  const float *g, const int32_t *parent, int B, int K, int H, int dk, int dv,
+                  double *out, int32_t *status) {
+    for (int b = 0; b < B; ++b) {
+        int32_t *par = malloc(sizeof(int32_t) * K);
+        int *path = malloc(sizeof(int) * K);
+        for (int i = 0; i < K; ++i) par[i] = parent ? parent[(int64_t)b * K + i] : i - 1;
+        status[b] = 0;
+        for (int i = 0; i < K; ++i)
+            if (rec_path(par, K, i, path) < 0) status[b] = 1;
+        free(path);
+#pragma omp parallel for collapse(2) schedule(dynamic)
+        for (int i = 0; i < K; ++i)
+            for (int h = 0; h < H; ++h) {
+                double *o = out + (((int64_t)b * K + i) * H + h) * dv;
+                if (status[b]) {
+                    for (int c = 0; c < dv; ++c) o[c] = 0.0;
+                    continue;
+                }
+                int *pth = malloc(sizeof(int) * K);
+                double *S = malloc(sizeof(double) * dk * dv);
+                const int n = rec_path(par, K, i, pth);
+                rec_run(S0, kk, v, g, K, H, dk, dv, b, h, pth, n, S);
+                const uint16_t *qr = q + (((int64_t)b * K + i) * H + h) * dk;
+                for (int c = 0; c < dv; ++c) {
+                    double acc = 0.0;
+                    for (int r = 0; r < dk; ++r) acc += S[(int64_t)r * dv + c] * (double)bf16_to_f32(qr[r]);
+                    o[c] = acc;
+                }
+                free(S);
+                free(pth);
+            }
+        free(par);
+    }
+}
+
+/* The committed state after acceptance: for each request whose accepted_len a >= 0, the state
+ * after the tokens path[b][0..a] (the accepted root path, the root first), from S0, into
+ * S_out (float64, same layout as S0); requests with a < 0 keep S0. */
+void orc_rec_commit(const float *S0, const uint16_t *kk, const uint16_t *v, const float *g,
+                    const int32_t *accepted_len, const int32_t *accepted_path, int B, int K, int H,
+                    int dk, int dv, double *S_out) {
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int b = 0; b < B; ++b)
+        for (int h = 0; h < H; ++h) {
+            const int a = accepted_len[b];
+            int *pth = malloc(sizeof(int) * K);
+            const int n = a < 0 ? 0 : a + 1;
+            for (int t = 0; t < n; ++t) pth[t] = accepted_path[(int64_t)b * K + t];
+            rec_run(S0, kk, v, g, K, H, dk, dv, b, h, pth, n, S_out + ((int64_t)b * H + h) * dk * dv);
+            free(pth);
+        }
+}

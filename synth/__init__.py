@@ -220,3 +220,17 @@ def page_table(n_requests: int, pages_per_request: List[int], seed, shuffle: boo
         table[b, :n] = ids[o:o + n]
         o += n
     return table, total
+
+
+def rec_inputs(B: int, K: int, H: int, dk: int, dv: int, seed, device="cpu", *parts):
+    """Seeded inputs of a recurrent layer's tree pass: state S0 fp32 [B][H][dk][dv] ~ N(0, 1/4);
+    q, k bf16 [B][K][H][dk] ~ N(0, 1/dk); v bf16 [B][K][H][dv] ~ N(0, 1); log-gates g fp32
+    [B][K][H] ~ U(log 0.6, 0), i.e. per-token decays between 0.6 and 1."""
+    gs = _gen(device, seed, "rec_state", *parts)
+    S0 = torch.randn((B, H, dk, dv), generator=gs, device=device, dtype=torch.float32).mul_(0.5)
+    q = randn_bf16((B, K, H, dk), dk ** -0.5, device, seed, "rec_q", *parts)
+    k = randn_bf16((B, K, H, dk), dk ** -0.5, device, seed, "rec_k", *parts)
+    v = randn_bf16((B, K, H, dv), 1.0, device, seed, "rec_v", *parts)
+    gg = _gen(device, seed, "rec_gate", *parts)
+    g = torch.rand((B, K, H), generator=gg, device=device, dtype=torch.float32).mul_(float(np.log(0.6)))
+    return S0, q, k, v, g
