@@ -266,6 +266,36 @@ int spec_prefill(const spec_weights *weights, const spec_kv_cache *kv, const int
                  int32_t *ctx_len, int batch, int p, int32_t *next_token, float *last_logits,
                  void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* ---- Recurrent layers of a hybrid target ------------------------------------------------------
+ * The SpecPilot digest (airadar.tv — "Reasons") names tree verification for targets that mix
+ * recurrent layers in, without giving the recurrence. This library's reading: per head, a
+ * scalar-gated linear recurrence over a state S [dk][dv] (fp32),
+ *     S <- exp(g) S + k v^T, then o = S^T q, for each token,
+ * where every node of a draft tree continues its parent's state and the root continues the
+ * committed one (the tree is conditioned on paths as for attention [JetSpec article,
+ * seventnews.com — "Technical architecture"]). dk = dv = head_dim, 64 or 128.
+ *
+ * spec_rec_tree_verify: one recurrent layer over a draft tree, reading the committed state once
+ * and writing no per-node state.
+ *   state [batch][n_heads][head_dim][head_dim] fp32 (read only); q, k, v
+ *   [batch][k][n_heads][head_dim] bf16; log_gate [batch][k][n_heads] fp32 (g, normally <= 0);
+ *   tree_parent [batch][k] int32 as for spec_verify, or NULL for chains; out
+ *   [batch][k][n_heads][head_dim] fp32; status [batch] int32 out: 0, or 1 for a malformed tree
+ *   (that request's outputs are zero).
+ * spec_rec_commit: the state of each request's accepted node, written over state in place:
+ *   the tokens accepted_path[b][0..accepted_len[b]] (node ids as spec_verify returns them)
+ *   applied to the committed state. A request with accepted_len < 0, accepted_len >= k, or a
+ *   node id outside [0, k) keeps its state. k, v, log_gate as passed to the verify call.
+ * Both: device pointers, 16-byte aligned; async on stream; k <= 64 (SPEC_EUNSUPPORTED past it
+ * or for another head_dim); SPEC_EINVAL for NULL pointers, misalignment or batch, k or n_heads
+ * below 1. Calls that overlap on one state buffer race. */
+int spec_rec_tree_verify(const float *state, const void *q, const void *k, const void *v,
+                         const float *log_gate, const int32_t *tree_parent, int batch, int k_nodes,
+                         int n_heads, int head_dim, float *out, int32_t *status, hipStream_t stream);
+int spec_rec_commit(float *state, const void *k, const void *v, const float *log_gate,
+                    const int32_t *accepted_len, const int32_t *accepted_path, int batch,
+                    int k_nodes, int n_heads, int head_dim, hipStream_t stream);
+
 /* Static text for a return code. */
 const char *spec_strerror(int code);
 

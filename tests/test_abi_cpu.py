@@ -220,3 +220,28 @@ def test_prefill_rejects_bad_arguments():
     assert L.spec_prefill(*args(b=0)) == tv.SPEC_EINVAL
     assert L.spec_prefill(*args(wsb=need - 1)) == tv.SPEC_EWORKSPACE
     assert L.spec_prefill(*args(ws=0x100010)) == tv.SPEC_EINVAL
+
+
+def test_recurrent_entries_reject_bad_arguments():
+    """Host-detectable errors of the recurrent-layer entries return before any launch."""
+    L = tv.lib()
+    f = 0x100000
+    ok = (f, f + 0x1000, f + 0x2000, f + 0x3000, f + 0x4000, None, 2, 8, 4, 128, f + 0x5000, f + 0x6000, None)
+    bad = [((None,) + ok[1:], tv.SPEC_EINVAL),
+           ((f + 8,) + ok[1:], tv.SPEC_EINVAL),                       # unaligned state
+           (ok[:4] + (None,) + ok[5:], tv.SPEC_EINVAL),               # no gates
+           (ok[:6] + (0,) + ok[7:], tv.SPEC_EINVAL),                  # batch 0
+           (ok[:7] + (65,) + ok[8:], tv.SPEC_EUNSUPPORTED),           # 65 nodes
+           (ok[:8] + (0,) + ok[9:], tv.SPEC_EINVAL),                  # no heads
+           (ok[:9] + (96,) + ok[10:], tv.SPEC_EUNSUPPORTED),          # head_dim 96
+           (ok[:10] + (None,) + ok[11:], tv.SPEC_EINVAL),             # no output
+           (ok[:10] + (f + 0x5004,) + ok[11:], tv.SPEC_EINVAL),       # unaligned output
+           (ok[:11] + (None,) + ok[12:], tv.SPEC_EINVAL)]             # no status
+    for args, code in bad:
+        assert L.spec_rec_tree_verify(*args) == code, args
+    c = (f, f + 0x1000, f + 0x2000, f + 0x3000, f + 0x4000, f + 0x5000, 2, 8, 4, 64, None)
+    assert L.spec_rec_commit(*((None,) + c[1:])) == tv.SPEC_EINVAL
+    assert L.spec_rec_commit(*(c[:4] + (None,) + c[5:])) == tv.SPEC_EINVAL
+    assert L.spec_rec_commit(*(c[:7] + (65,) + c[8:])) == tv.SPEC_EUNSUPPORTED
+    assert L.spec_rec_commit(*(c[:9] + (32,) + c[10:])) == tv.SPEC_EUNSUPPORTED
+    assert L.spec_rec_commit(*(c[:1] + (f + 2,) + c[2:])) == tv.SPEC_EINVAL

@@ -112,7 +112,10 @@ def lib() -> ctypes.CDLL:
                                                    ctypes.POINTER(sz)]
         L.spec_prefill.argtypes = [ctypes.POINTER(WeightsC), ctypes.POINTER(KVCacheC), vp, vp, i32, i32,
                                    vp, vp, vp, sz, vp]
-        for f in (L.spec_prefill_workspace_bytes, L.spec_prefill):
+        L.spec_rec_tree_verify.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp]
+        L.spec_rec_commit.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, vp]
+        for f in (L.spec_prefill_workspace_bytes, L.spec_prefill, L.spec_rec_tree_verify,
+                  L.spec_rec_commit):
             f.restype = i32
         for f in (L.spec_workspace_bytes, L.spec_verify, L.spec_commit_kv,
                   L.spec_accept_workspace_bytes, L.spec_accept, L.spec_skinny_gemm_bytes,
@@ -126,7 +129,8 @@ def lib() -> ctypes.CDLL:
 EXPORTED = ("spec_workspace_bytes", "spec_verify", "spec_commit_kv", "spec_accept_workspace_bytes",
             "spec_accept", "spec_pack_weight", "spec_skinny_gemm_bytes", "spec_skinny_gemm",
             "spec_read_probe", "spec_w12_plan_ints", "spec_w12_plan", "spec_w12_pack",
-            "spec_skinny_gemm_w12", "spec_prefill_workspace_bytes", "spec_prefill", "spec_strerror")
+            "spec_skinny_gemm_w12", "spec_prefill_workspace_bytes", "spec_prefill",
+            "spec_rec_tree_verify", "spec_rec_commit", "spec_strerror")
 
 
 def spec_strerror(code: int) -> str:
@@ -375,6 +379,42 @@ def spec_read_probe(buf: torch.Tensor, out: torch.Tensor, stream=None) -> None:
     plain stream; out: a device int32/uint32 tensor of at least one element."""
     _check(lib().spec_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(out),
                                  _stream(stream)), "spec_read_probe")
+
+
+def spec_rec_tree_verify(state: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                         log_gate: torch.Tensor, tree_parent: Optional[torch.Tensor],
+                         out: torch.Tensor, status: torch.Tensor, stream=None) -> None:
+    """One recurrent layer over draft trees. state fp32 [B][H][D][D]; q, k, v bf16 [B][K][H][D];
+    log_gate fp32 [B][K][H]; tree_parent int32 [B][K] or None (chains); out fp32 [B][K][H][D];
+    status int32 [B] (1 = malformed tree)."""
+    B, K, H, D = q.shape
+    for t in (state, q, k, v, log_gate, out, status) + ((tree_parent,) if tree_parent is not None else ()):
+        if not t.is_contiguous():
+            raise ValueError("spec_rec_tree_verify: tensors must be contiguous")
+    if (tuple(state.shape) != (B, H, D, D) or tuple(k.shape) != (B, K, H, D) or
+            tuple(v.shape) != (B, K, H, D) or tuple(log_gate.shape) != (B, K, H) or
+            tuple(out.shape) != (B, K, H, D) or status.numel() < B or
+            (tree_parent is not None and tuple(tree_parent.shape) != (B, K))):
+        raise ValueError("spec_rec_tree_verify: shapes do not match")
+    _check(lib().spec_rec_tree_verify(_ptr(state), _ptr(q), _ptr(k), _ptr(v), _ptr(log_gate),
+                                      _ptr(tree_parent), B, K, H, D, _ptr(out), _ptr(status),
+                                      _stream(stream)), "spec_rec_tree_verify")
+
+
+def spec_rec_commit(state: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_gate: torch.Tensor,
+                    accepted_len: torch.Tensor, accepted_path: torch.Tensor, stream=None) -> None:
+    """The accepted node's state written over state (fp32 [B][H][D][D]) in place; k, v, log_gate
+    as passed to spec_rec_tree_verify; accepted_len int32 [B], accepted_path int32 [B][K]."""
+    B, K, H, D = k.shape
+    for t in (state, k, v, log_gate, accepted_len, accepted_path):
+        if not t.is_contiguous():
+            raise ValueError("spec_rec_commit: tensors must be contiguous")
+    if (tuple(state.shape) != (B, H, D, D) or tuple(v.shape) != (B, K, H, D) or
+            tuple(log_gate.shape) != (B, K, H) or accepted_len.numel() < B or
+            tuple(accepted_path.shape) != (B, K)):
+        raise ValueError("spec_rec_commit: shapes do not match")
+    _check(lib().spec_rec_commit(_ptr(state), _ptr(k), _ptr(v), _ptr(log_gate), _ptr(accepted_len),
+                                 _ptr(accepted_path), B, K, H, D, _stream(stream)), "spec_rec_commit")
 
 
 def spec_skinny_gemm_bytes(m: int, n: int, kd: int) -> int:

@@ -515,6 +515,40 @@ int spec_prefill(const spec_weights *weights, const spec_kv_cache *kv, const int
     return SPEC_OK;
 }
 
+static int rec_args(const void *a, const void *b, const void *c, const void *d, int batch, int k,
+                    int n_heads, int head_dim) {
+    for (const void *p : {a, b, c, d})
+        if (p == nullptr || reinterpret_cast<uintptr_t>(p) % 16 != 0) return SPEC_EINVAL;
+    if (batch < 1 || k < 1 || n_heads < 1) return SPEC_EINVAL;
+    if (k > SPEC_MAX_K || (head_dim != 64 && head_dim != 128)) return SPEC_EUNSUPPORTED;
+    if ((int64_t)batch * n_heads > (1 << 24)) return SPEC_EUNSUPPORTED;
+    return SPEC_OK;
+}
+
+int spec_rec_tree_verify(const float *state, const void *q, const void *k, const void *v,
+                         const float *log_gate, const int32_t *tree_parent, int batch, int k_nodes,
+                         int n_heads, int head_dim, float *out, int32_t *status, hipStream_t stream) {
+    int rc = rec_args(state, q, k, v, batch, k_nodes, n_heads, head_dim);
+    if (rc != SPEC_OK) return rc;
+    if (log_gate == nullptr || out == nullptr || status == nullptr) return SPEC_EINVAL;
+    if (reinterpret_cast<uintptr_t>(out) % 16 != 0) return SPEC_EINVAL;
+    SV_TRY(rec_tree(state, static_cast<const bf16 *>(q), static_cast<const bf16 *>(k),
+                    static_cast<const bf16 *>(v), log_gate, tree_parent, batch, k_nodes, n_heads,
+                    head_dim, out, status, stream));
+    return SPEC_OK;
+}
+
+int spec_rec_commit(float *state, const void *k, const void *v, const float *log_gate,
+                    const int32_t *accepted_len, const int32_t *accepted_path, int batch,
+                    int k_nodes, int n_heads, int head_dim, hipStream_t stream) {
+    int rc = rec_args(state, k, v, state, batch, k_nodes, n_heads, head_dim);
+    if (rc != SPEC_OK) return rc;
+    if (log_gate == nullptr || accepted_len == nullptr || accepted_path == nullptr) return SPEC_EINVAL;
+    SV_TRY(rec_commit(state, static_cast<const bf16 *>(k), static_cast<const bf16 *>(v), log_gate,
+                      accepted_len, accepted_path, batch, k_nodes, n_heads, head_dim, stream));
+    return SPEC_OK;
+}
+
 int spec_read_probe(const void *buf, size_t bytes, uint32_t *out, hipStream_t stream) {
     if (buf == nullptr || out == nullptr || bytes == 0 || bytes % 16 != 0) return SPEC_EINVAL;
     if (reinterpret_cast<uintptr_t>(buf) % 16 != 0) return SPEC_EINVAL;
