@@ -11,6 +11,9 @@ Workloads (--config):
   tree    batch 1, 64-node draft tree of depth <= 10, context 8192
   batched 32 requests x block of 16, contexts uniform in [512, 8192], shuffled 16-token pages
   prefill (a separate line, its own metric) one 4096-token prompt from an empty context
+  rec     (a separate line, its own metric) the recurrent layers of a hybrid target: 32 requests
+          x 64-node trees (depth <= 10), 32 heads with 128 x 128 fp32 states, 8 layers; one step
+          is the tree pass and the state commit of every layer
 --weights w12 stores the projections and the output head in the lossless 12-bit layout (batch-1
 workloads only); the results are bit-identical to bf16 and the step streams a quarter fewer
 weight bytes. A bf16 run of a batch-1 workload also times the same step over that layout and
@@ -352,12 +355,130 @@ def prefill_bench(args, shape, device):
     print(json.dumps(result), flush=True)
 
 
+def rec_bench(args, device):
+    """Tree pass + state commit of a hybrid target's recurrent layers (spec_rec_tree_verify,
+    spec_rec_commit), 8 layers with their own states and inputs (about 1.2 GB per step, beyond
+    the memory-side cache), replayed from a HIP graph. Algorithmic bytes of a tree pass, per
+    (request, head): the state D*D*4, q, k, v K*D*2 each, gates and parents K*4 each, outputs
+    K*D*4; of a commit: the state read and written, and the path's k and v rows."""
+    B, K, H, D, L = 32, 64, 32, 128, 8
+    parents = np.stack([synth.random_tree(K, 10, SEED, "rec", b) for b in range(B)]).astype(np.int32)
+    par = torch.from_numpy(parents).to(device)
+    layers = []
+    for l in range(L):
+        S0, q, k, v, g = synth.rec_inputs(B, K, H, D, D, SEED, device, "bench", l)
+        layers.append((S0, q, k, v, g))
+    out = torch.empty((B, K, H, D), dtype=torch.float32, device=device)
+    status = torch.empty(B, dtype=torch.int32, device=device)
+    # accepted path: the root path of a seeded node of each tree (what the greedy walk returns)
+    rng = np.random.default_rng(SEED)
+    acc = np.zeros(B, np.int32)
+    path = np.zeros((B, K), np.int32)
+    for b in range(B):
+        j, p = int(rng.integers(0, K)), []
+        while j != -1:
+            p.append(j)
+            j = int(parents[b, j])
+        p = p[::-1]
+        acc[b] = len(p) - 1
+        path[b, :len(p)] = p
+    acc_t, path_t = torch.from_numpy(acc).to(device), torch.from_numpy(path).to(device)
+    stream = torch.cuda.Stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * L)]
+
+    def step(events=False):
+        for l, (S0, q, k, v, g) in enumerate(layers):
+            if events:
+                ev[2 * l].record(stream)
+            tv.spec_rec_tree_verify(S0, q, k, v, g, par, out, status)
+            if events:
+                ev[2 * l + 1].record(stream)
+            tv.spec_rec_commit(S0, k, v, g, acc_t, path_t)
+
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        step()
+        stream.synchronize()
+        assert not status.cpu().numpy().any()
+        # per-launch tree-pass time from events on this stream, eager steps
+        durs = []
+        for _ in range(3):
+            step(events=True)
+            stream.synchronize()
+            durs.extend(ev[2 * l].elapsed_time(ev[2 * l + 1]) for l in range(L))
+        t_tree = float(np.mean(durs)) / 1e3
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            step()
+        for _ in range(args.warmup):
+            graph.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            graph.replay()
+        e1.record(stream)
+        e1.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    depth_sum = 0
+    for b in range(B):
+        d = np.zeros(K, np.int64)
+        for i in range(1, K):
+            d[i] = d[parents[b, i]] + 1
+        depth_sum += int((d + 1).sum())            # path lengths, root .. node
+    tree_bytes = B * H * (D * D * 4 + 3 * K * D * 2 + 2 * K * 4 + K * D * 4)
+    commit_bytes = B * H * (2 * D * D * 4) + int((acc + 1).sum()) * H * 2 * D * 2 + B * H * K * 4
+    step_bytes_ = L * (tree_bytes + commit_bytes)
+    gbps = step_bytes_ / (ms / 1e3) / 1e9
+    ach = tree_bytes / t_tree / 1e9
+    flops = 2 * B * H * K * D * D + 4 * H * depth_sum * D      # state term + path terms
+    result = {
+        "metric": "hybrid-target recurrent layers: tree-verified node-layers/s, 1 GPU",
+        "value": round(B * K * L / (ms / 1e3), 1), "unit": "node-layers/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded states N(0,1/4), q/k N(0,1/d) and v N(0,1) bf16, decays U(0.6,1))",
+        "config": {"workload": f"recurrent layers of a hybrid target: {B} requests x {K}-node trees "
+                               f"(depth <= 10), {H} heads, {D}x{D} fp32 states, {L} layers; tree pass "
+                               f"+ state commit per layer", "hip_graph": True},
+        "hbm": {"bytes_per_step": int(step_bytes_), "achieved_gbps": round(gbps, 1),
+                "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4)},
+        "roofline": {"kernel": "rec_tree_kernel<128>", "bound": "hbm", "achieved": round(ach, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
+                     "traffic": None, "us_per_launch": round(t_tree * 1e6, 2),
+                     "bytes_per_launch": int(tree_bytes),
+                     "fp32_tflops": round(flops / t_tree / 1e12, 2)},
+    }
+    log(f"rec: {ms:.3f} ms per step ({gbps:.0f} GB/s); tree pass {t_tree * 1e6:.1f} us "
+        f"({ach:.0f} GB/s, {flops / t_tree / 1e12:.1f} TFLOP/s)")
+    if not args.no_cpu_baseline:
+        import oracle
+        S0, q, k, v, g = layers[0]
+        spent, n = 0.0, 0
+        while spent < args.cpu_seconds and n < B * H:
+            b, h = n % B, (n * 7) % H
+            sl = lambda t: t[b:b + 1, :, h:h + 1].contiguous().cpu()
+            bits = lambda t: t.view(torch.int16).numpy().view(np.uint16)
+            hs = (S0[b:b + 1, h:h + 1].contiguous().cpu().numpy(), bits(sl(q)), bits(sl(k)),
+                  bits(sl(v)), g[b:b + 1, :, h:h + 1].contiguous().cpu().numpy())
+            t0 = time.time()
+            oracle.rec_tree(*hs, parents[b:b + 1])
+            spent += time.time() - t0
+            n += 1
+        per_pair = spent / n
+        result["cpu_baseline"] = {"value": round(K / per_pair / H, 2), "unit": "node-layers/s",
+                                  "cores": oracle.threads(), "kind": "oracle",
+                                  "sample": f"{n} (request, head) tree passes of layer 0 ({spent:.1f}s), "
+                                            f"scaled to all {H} heads of a layer (commit not timed)"}
+        log(f"cpu baseline: {result['cpu_baseline']}")
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="block", choices=["block", "tree", "batched", "prefill"])
+    ap.add_argument("--config", default="block", choices=["block", "tree", "batched", "prefill", "rec"])
     ap.add_argument("--prompt", type=int, default=4096, help="prompt length of --config prefill")
     ap.add_argument("--eager", action="store_true", help="launch every step instead of a HIP graph")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -379,6 +500,9 @@ def main():
     shape = synth.DENSE_27B
     if args.config == "prefill":
         prefill_bench(args, shape, device)
+        return
+    if args.config == "rec":
+        rec_bench(args, device)
         return
     wl = workload(args.config)
     B, K, ctx = wl["batch"], wl["k"], wl["ctx"]

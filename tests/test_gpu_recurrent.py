@@ -4,11 +4,13 @@ float64 [SpecPilot digest, airadar.tv — "Reasons": tree verification for targe
 layers; the recurrence S <- exp(g) S + k v^T, o = S^T q is this library's reading].
 
 Bound. The GPU evaluates the closed form o_i = e^{c_i} q_i^T S0 + sum_j e^{c_i - c_j}
-(q_i . k_j) v_j in fp32 (path sums c in float64, rounded to fp32 before exp). With u = 2^-24,
-the dot products carry gamma_D, the sum over path nodes gamma_K, each exponential
-(|c| + 3) u, so to first order
-    |o_gpu - o_64| <= (D + K + max|c| + 16) u * (e^{c_i} |q_i|^T |S0| + sum_j e^{c_i - c_j} |q_i . k_j|_abs |v_j|),
-with |q . k|_abs = sum_r |q_r k_r|; the commit alike with n path tokens in place of D + K.
+(q_i . k_j) v_j with fp32 accumulation (path sums c in float64, rounded to fp32 before exp). The
+fp32 state and the fp32 weights enter the bf16 matrix core as three bf16 parts each (exact to
+2^-27 relative), so one output accumulates 3 D + 3 K products; with u = 2^-24 and each
+exponential good to (|c| + 3) u, to first order
+    |o_gpu - o_64| <= (3 D + 3 K + max|c| + 16) u * (e^{c_i} |q_i|^T |S0| + sum_j e^{c_i - c_j} |q_i . k_j|_abs |v_j|),
+with |q . k|_abs = sum_r |q_r k_r|. The commit runs on the vector units, n path tokens in a
+plain fp32 sum: (n + max|c| + 16) u times its own magnitude.
 """
 import numpy as np
 import pytest
@@ -67,7 +69,7 @@ def _tree_bound(S0, q, k, v, g, parents, K, D):
                 for t, j in enumerate(path):
                     mag += np.exp(ci - c[t]) * (qf[b, i, h] @ kf[b, j, h]) * vf[b, j, h]
                 cmax = np.abs(c).max()
-                bound[b, i, h] = (D + K + cmax + 16) * U32 * mag
+                bound[b, i, h] = (3 * D + 3 * K + cmax + 16) * U32 * mag
     return bound
 
 

@@ -35,155 +35,220 @@ __device__ __forceinline__ void put8(float *dst, bf16x8 v) {
 
 }  // namespace
 
-// One workgroup (256 threads) per (request, head): wg = b * H + h. Rows of q, k, v are
-// [B][K][H][D] bf16; the state [B][H][D][D] fp32; out [B][K][H][D] fp32.
+// x = hi + mid + lo with three bf16 parts, each the rounded remainder of the previous (the
+// remainders are exact in fp32): the sum carries 24 significant bits, so products with bf16
+// operands on the bf16 matrix core keep fp32 accuracy.
+__device__ __forceinline__ void split3(const float (&x)[8], bf16x8 &hi, bf16x8 &mid, bf16x8 &lo) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const bf16 a = to_bf(x[e]);
+        const float r1 = x[e] - to_f(a);
+        const bf16 m = to_bf(r1);
+        hi[e] = a;
+        mid[e] = m;
+        lo[e] = to_bf(r1 - to_f(m));
+    }
+}
+
+// One workgroup (4 waves) per (request, head): wg = b * H + h. Rows of q, k, v are
+// [B][K][H][D] bf16; the state [B][H][D][D] fp32; out [B][K][H][D] fp32. On the matrix core
+// (v_mfma_f32_16x16x32_bf16; a lane's A fragment is row l % 16, columns 8 (l / 16) .. + 7 of a
+// 16 x 32 tile, its B fragment rows 8 (l / 16) .. + 7 of column l % 16, its result rows
+// 4 (l / 16) .. + 3 of column l % 16):
+//   scores  S = Q K^T, wave w taking node tile w against the key tiles at or before it;
+//   weights W_ij = exp(c_i - c_j) S_ij on i's path, else 0, in LDS;
+//   output  O = diag(exp(c)) (Q S0) + W V, wave w taking columns 32 w .. 32 w + 31 (16 w ..
+//           at D = 64) for every node tile, with S0 and W split into three bf16 parts and V
+//           staged transposed in LDS.
 template <int D>
 __global__ __launch_bounds__(256) void rec_tree_kernel(
     const float *__restrict__ state, const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     const bf16 *__restrict__ v, const float *__restrict__ log_gate,
     const int32_t *__restrict__ tree_parent, int K, int H, float *__restrict__ out,
     int32_t *__restrict__ status) {
-    constexpr int QP = D + 4;            // padded LDS row of q and k (floats)
-    constexpr int NG = 256 / D;          // node groups in the output phase
-    constexpr int NPT = kRecMaxK / NG;   // nodes per thread there, at most
-    __shared__ __attribute__((aligned(16))) float qs[kRecMaxK * QP];
-    __shared__ __attribute__((aligned(16))) float ks[kRecMaxK * QP];
-    __shared__ __attribute__((aligned(16))) float vs[kRecMaxK * D];
-    __shared__ float w[kRecMaxK * kRecMaxK];
+    constexpr int RS = D / 32;           // 32-wide steps over the state's rows
+    constexpr int CPW = D / 64;          // 16-column tiles per wave
+    constexpr int WP = kRecMaxK + 4;     // padded LDS row of W (floats)
+    constexpr int VP = kRecMaxK + 8;     // padded LDS row of V^T (bf16)
+    __shared__ __attribute__((aligned(16))) float wl[kRecMaxK * WP];
+    __shared__ __attribute__((aligned(16))) bf16 vt[D * VP];
     __shared__ double csum[kRecMaxK];
     __shared__ uint64_t anc[kRecMaxK];
-    __shared__ float gl[kRecMaxK];
     __shared__ int bad_s;
 
     const int wg = blockIdx.x;
     const int b = wg / H, h = wg % H;
     const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int r16 = lane & 15, grp = lane >> 4;
+    const int NT = (K + 15) >> 4;        // node tiles
 
-    // ---- the tree: parent links, ancestor masks (pointer jumping), path sums of log-gates ----
+    // this wave's state fragments, in flight from the start: column 16 ct + r16, rows
+    // 32 rs + 8 grp + e
+    const float *S0 = state + ((int64_t)b * H + h) * D * D;
+    float sf[CPW][RS][8];
+#pragma unroll
+    for (int u = 0; u < CPW; ++u)
+#pragma unroll
+        for (int rs = 0; rs < RS; ++rs)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                sf[u][rs][e] = S0[(int64_t)(32 * rs + 8 * grp + e) * D + 16 * (wave * CPW + u) + r16];
+    // the query fragments of every node tile (rows past K are zero)
+    auto row_ptr = [&](const bf16 *base, int i) { return base + (((int64_t)b * K + i) * H + h) * D; };
+    bf16x8 qf[4][RS];
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const int i = 16 * it + r16;
+#pragma unroll
+        for (int rs = 0; rs < RS; ++rs)
+            qf[it][rs] = i < K ? *reinterpret_cast<const bf16x8 *>(row_ptr(q, i) + 32 * rs + 8 * grp) : bf16x8{};
+    }
+
+    // ---- the tree: parent links, ancestor masks and path sums of log-gates (pointer jumping) --
     if (t < 64) {
         int p = lane - 1;
         if (tree_parent != nullptr && lane < K) p = tree_parent[(int64_t)b * K + lane];
         const bool ok = lane >= K || (lane == 0 ? p == -1 : (p >= 0 && p < lane));
         const bool bad = __any(!ok);
-        if (lane < K) gl[lane] = log_gate[((int64_t)b * K + lane) * H + h];
         if (lane == 0) bad_s = bad ? 1 : 0;
         if (!bad) {
-            // invariant: m holds the path from lane up to (not including) ptr
+            // invariant: m holds the path from lane up to (not including) ptr, cs the sum of
+            // its log-gates (float64)
             uint64_t m = lane < K ? (1ull << lane) : 0ull;
+            double cs = lane < K ? (double)log_gate[((int64_t)b * K + lane) * H + h] : 0.0;
             int ptr = lane < K ? p : -1;
 #pragma unroll
             for (int round = 0; round < 6; ++round) {
                 const int src = ptr < 0 ? 0 : ptr;
                 const uint32_t lo = __shfl((uint32_t)m, src, 64);
                 const uint32_t hi = __shfl((uint32_t)(m >> 32), src, 64);
+                const double cp = __shfl(cs, src, 64);
                 const int pp = __shfl(ptr, src, 64);
                 if (ptr >= 0) {
                     m |= ((uint64_t)hi << 32) | lo;
+                    cs += cp;
                     ptr = pp;
                 }
             }
-            if (lane < K) anc[lane] = m;
+            if (lane < K) {
+                anc[lane] = m;
+                csum[lane] = cs;
+            }
+        }
+    }
+    // W starts at zero (pairs off the path, and key columns past the last node); V^T staged
+    for (int e = t; e < kRecMaxK * WP; e += 256) wl[e] = 0.f;
+    {
+        constexpr int TPR = D / 8;
+        constexpr int NIT = kRecMaxK * TPR / 256;
+        bf16x8 x[NIT];
+#pragma unroll
+        for (int u = 0; u < NIT; ++u) {
+            const int e = t + 256 * u, j = e / TPR, col = (e % TPR) * 8;
+            x[u] = j < K ? *reinterpret_cast<const bf16x8 *>(row_ptr(v, j) + col) : bf16x8{};
+        }
+#pragma unroll
+        for (int u = 0; u < NIT; ++u) {
+            const int e = t + 256 * u, j = e / TPR, col = (e % TPR) * 8;
+#pragma unroll
+            for (int z = 0; z < 8; ++z) vt[(col + z) * VP + j] = x[u][z];
         }
     }
     __syncthreads();
     const bool bad = bad_s != 0;
     if (h == 0 && t == 0) status[b] = bad ? 1 : 0;
     if (bad) {
-        for (int e = t; e < K * D; e += 256) {
-            const int i = e / D, c = e % D;
-            out[(((int64_t)b * K + i) * H + h) * D + c] = 0.f;
-        }
+        for (int e = t; e < K * D; e += 256)
+            out[(((int64_t)b * K + e / D) * H + h) * D + e % D] = 0.f;
         return;
     }
-    if (t < K) {
-        const uint64_t m = anc[t];
-        double s = 0.0;
-        for (int j = 0; j < K; ++j)
-            if ((m >> j) & 1ull) s += (double)gl[j];
-        csum[t] = s;
-    }
 
-    // ---- q, k, v rows into LDS as fp32 -----------------------------------------------------
-    {
-        constexpr int TPR = D / 8;       // threads per row (16 bytes each)
-        for (int e = t; e < 3 * K * TPR; e += 256) {
-            const int which = e / (K * TPR), rem = e % (K * TPR);
-            const int i = rem / TPR, col = (rem % TPR) * 8;
-            const int64_t off = (((int64_t)b * K + i) * H + h) * D + col;
-            const bf16 *src = which == 0 ? q : (which == 1 ? k : v);
-            const bf16x8 x = *reinterpret_cast<const bf16x8 *>(src + off);
-            float *dst = which == 0 ? &qs[i * QP + col] : (which == 1 ? &ks[i * QP + col] : &vs[i * D + col]);
-            put8(dst, x);
-        }
-    }
-    __syncthreads();
-
-    // ---- weights w_ij = exp(c_i - c_j) (q_i . k_j) for j on i's path, else 0 ---------------
-    {
-        const int j = lane, i0 = t >> 6;
-        float s[kRecMaxK / 4];
+    // ---- W: wave w scores node tile w against key tiles 0..w ---------------------------------
 #pragma unroll
-        for (int m = 0; m < kRecMaxK / 4; ++m) s[m] = 0.f;
-        for (int r = 0; r < D; r += 4) {
-            const float4 kv = *reinterpret_cast<const float4 *>(&ks[j * QP + r]);
+    for (int it = 0; it < 4; ++it) {
+        if (it != wave || it >= NT) continue;   // wave-uniform; keeps qf statically indexed
+        for (int jt = 0; jt <= it; ++jt) {
+            const int j = 16 * jt + r16;
+            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int m = 0; m < kRecMaxK / 4; ++m) {
-                if (i0 + 4 * m < K) {
-                    const float4 qv = *reinterpret_cast<const float4 *>(&qs[(i0 + 4 * m) * QP + r]);
-                    s[m] = __builtin_fmaf(qv.x, kv.x, s[m]);
-                    s[m] = __builtin_fmaf(qv.y, kv.y, s[m]);
-                    s[m] = __builtin_fmaf(qv.z, kv.z, s[m]);
-                    s[m] = __builtin_fmaf(qv.w, kv.w, s[m]);
-                }
+            for (int rs = 0; rs < RS; ++rs) {
+                const bf16x8 kf = j < K ? *reinterpret_cast<const bf16x8 *>(row_ptr(k, j) + 32 * rs + 8 * grp) : bf16x8{};
+                acc = mfma16x16x32(qf[it][rs], kf, acc);
             }
-        }
-        if (j < K) {
-            const double cj = csum[j];
+            if (j < K) {
+                const double cj = csum[j];
 #pragma unroll
-            for (int m = 0; m < kRecMaxK / 4; ++m) {
-                const int i = i0 + 4 * m;
-                if (i < K) {
-                    const bool on = (anc[i] >> j) & 1ull;
-                    w[i * kRecMaxK + j] = on ? expf((float)(csum[i] - cj)) * s[m] : 0.f;
+                for (int e = 0; e < 4; ++e) {
+                    const int i = 16 * it + 4 * grp + e;
+                    if (i < K && ((anc[i] >> j) & 1ull))
+                        wl[i * WP + j] = expf((float)(csum[i] - cj)) * acc[e];
                 }
             }
         }
     }
     __syncthreads();
 
-    // ---- o_i[c] = exp(c_i) (q_i^T S0)[c] + sum_j w_ij v_j[c] ---------------------------------
-    {
-        const int c = t % D, ig = t / D;   // ig uniform over a wave
-        const float *S0 = state + ((int64_t)b * H + h) * D * D;
-        float acc[NPT];
+    // ---- O = diag(exp(c)) (Q S0) + W V ------------------------------------------------------
+    floatx4 o[CPW][4];
 #pragma unroll
-        for (int m = 0; m < NPT; ++m) acc[m] = 0.f;
-        for (int r0 = 0; r0 < D; r0 += 16) {
-            float sv[16];
+    for (int u = 0; u < CPW; ++u)
 #pragma unroll
-            for (int u = 0; u < 16; ++u) sv[u] = S0[(int64_t)(r0 + u) * D + c];
+        for (int it = 0; it < 4; ++it) o[u][it] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int u4 = 0; u4 < 4; ++u4) {
+    for (int u = 0; u < CPW; ++u)
 #pragma unroll
-                for (int m = 0; m < NPT; ++m) {
-                    const int i = ig + NG * m;
-                    if (i < K) {
-                        const float4 qv = *reinterpret_cast<const float4 *>(&qs[i * QP + r0 + 4 * u4]);
-                        acc[m] = __builtin_fmaf(qv.x, sv[4 * u4 + 0], acc[m]);
-                        acc[m] = __builtin_fmaf(qv.y, sv[4 * u4 + 1], acc[m]);
-                        acc[m] = __builtin_fmaf(qv.z, sv[4 * u4 + 2], acc[m]);
-                        acc[m] = __builtin_fmaf(qv.w, sv[4 * u4 + 3], acc[m]);
-                    }
+        for (int rs = 0; rs < RS; ++rs) {
+            bf16x8 hi, mid, lo;
+            split3(sf[u][rs], hi, mid, lo);
+#pragma unroll
+            for (int it = 0; it < 4; ++it) {
+                if (it < NT) {
+                    o[u][it] = mfma16x16x32(qf[it][rs], hi, o[u][it]);
+                    o[u][it] = mfma16x16x32(qf[it][rs], mid, o[u][it]);
+                    o[u][it] = mfma16x16x32(qf[it][rs], lo, o[u][it]);
                 }
             }
         }
 #pragma unroll
-        for (int m = 0; m < NPT; ++m) {
-            const int i = ig + NG * m;
-            if (i < K) {
-                float o = expf((float)csum[i]) * acc[m];
-                for (int j = 0; j < K; ++j) o = __builtin_fmaf(w[i * kRecMaxK + j], vs[j * D + c], o);
-                out[(((int64_t)b * K + i) * H + h) * D + c] = o;
+    for (int it = 0; it < 4; ++it) {
+        if (it < NT) {
+            float ec[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 16 * it + 4 * grp + e;
+                ec[e] = i < K ? expf((float)csum[i]) : 0.f;
+            }
+#pragma unroll
+            for (int u = 0; u < CPW; ++u)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[u][it][e] *= ec[e];
+            // key steps that can hold an ancestor of the tile's nodes: j <= 16 it + 15
+            for (int js = 0; js <= (16 * it + 15) / 32 && 32 * js < K; ++js) {
+                float wv[8];
+                const float4 w0 = *reinterpret_cast<const float4 *>(&wl[(16 * it + r16) * WP + 32 * js + 8 * grp]);
+                const float4 w1 = *reinterpret_cast<const float4 *>(&wl[(16 * it + r16) * WP + 32 * js + 8 * grp + 4]);
+                wv[0] = w0.x; wv[1] = w0.y; wv[2] = w0.z; wv[3] = w0.w;
+                wv[4] = w1.x; wv[5] = w1.y; wv[6] = w1.z; wv[7] = w1.w;
+                bf16x8 hi, mid, lo;
+                split3(wv, hi, mid, lo);
+#pragma unroll
+                for (int u = 0; u < CPW; ++u) {
+                    const int cc = 16 * (wave * CPW + u) + r16;
+                    const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(&vt[cc * VP + 32 * js + 8 * grp]);
+                    o[u][it] = mfma16x16x32(hi, vf, o[u][it]);
+                    o[u][it] = mfma16x16x32(mid, vf, o[u][it]);
+                    o[u][it] = mfma16x16x32(lo, vf, o[u][it]);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < CPW; ++u) {
+                const int cc = 16 * (wave * CPW + u) + r16;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int i = 16 * it + 4 * grp + e;
+                    if (i < K) out[(((int64_t)b * K + i) * H + h) * D + cc] = o[u][it][e];
+                }
             }
         }
     }
@@ -200,6 +265,7 @@ __global__ __launch_bounds__(256) void rec_commit_kernel(
     __shared__ __attribute__((aligned(16))) float kk[kRecMaxK * D];   // e_t k_t, path order
     __shared__ __attribute__((aligned(16))) float vv[kRecMaxK * D];
     __shared__ float e_s[kRecMaxK + 1];
+    __shared__ float gp[kRecMaxK];        // log-gates of the path's nodes
     __shared__ int node[kRecMaxK];
     __shared__ int bad_s;
 
@@ -208,11 +274,21 @@ __global__ __launch_bounds__(256) void rec_commit_kernel(
     const int t = threadIdx.x;
     const int a = accepted_len[b];
     if (a < 0) return;                   // uniform: a failed request keeps its state
+    // this thread's rows rg, rg + NG, ... of column c, in flight while the path is set up
+    constexpr int RT = D / NG;
+    const int c = t % D, rg = t / D;
+    float *S = state + ((int64_t)b * H + h) * D * D;
+    float sv[RT];
+#pragma unroll
+    for (int u = 0; u < RT; ++u) sv[u] = S[(int64_t)(rg + NG * u) * D + c];
     const int n = a + 1 <= K ? a + 1 : K;
     if (t < 64) {
         const int p = t < n ? accepted_path[(int64_t)b * K + t] : 0;
         const bool bad = __any(t < n && (p < 0 || p >= K));
-        if (t < n) node[t] = p;
+        if (t < n) {
+            node[t] = p;
+            if (!bad) gp[t] = log_gate[((int64_t)b * K + p) * H + h];
+        }
         if (t == 0) bad_s = (a + 1 > K || bad) ? 1 : 0;
     }
     __syncthreads();
@@ -220,43 +296,47 @@ __global__ __launch_bounds__(256) void rec_commit_kernel(
     if (t <= n) {
         // t < n: decay from node t (exclusive) to the accepted node; t == n: from S0
         double s = 0.0;
-        for (int u = (t < n ? t + 1 : 0); u < n; ++u)
-            s += (double)log_gate[((int64_t)b * K + node[u]) * H + h];
+        for (int u = (t < n ? t + 1 : 0); u < n; ++u) s += (double)gp[u];
         e_s[t] = expf((float)s);
     }
     __syncthreads();
     {
         constexpr int TPR = D / 8;
-        for (int e = t; e < 2 * n * TPR; e += 256) {
-            const int which = e / (n * TPR), rem = e % (n * TPR);
-            const int tt = rem / TPR, col = (rem % TPR) * 8;
-            const int64_t off = (((int64_t)b * K + node[tt]) * H + h) * D + col;
-            const bf16x8 x = *reinterpret_cast<const bf16x8 *>((which == 0 ? k : v) + off);
-            if (which == 0) {
-                const float et = e_s[tt];
+        constexpr int NIT = 2 * kRecMaxK * TPR / 256;
+        bf16x8 x[NIT];
 #pragma unroll
-                for (int u = 0; u < 8; ++u) kk[tt * D + col + u] = et * to_f(x[u]);
-            } else {
-                put8(&vv[tt * D + col], x);
+        for (int u = 0; u < NIT; ++u) {
+            const int e = t + 256 * u;
+            const int which = e / (kRecMaxK * TPR), rem = e % (kRecMaxK * TPR);
+            const int tt = rem / TPR, col = (rem % TPR) * 8;
+            if (tt < n)
+                x[u] = *reinterpret_cast<const bf16x8 *>((which == 0 ? k : v) +
+                                                         (((int64_t)b * K + node[tt]) * H + h) * D + col);
+        }
+#pragma unroll
+        for (int u = 0; u < NIT; ++u) {
+            const int e = t + 256 * u;
+            const int which = e / (kRecMaxK * TPR), rem = e % (kRecMaxK * TPR);
+            const int tt = rem / TPR, col = (rem % TPR) * 8;
+            if (tt < n) {
+                if (which == 0) {
+                    const float et = e_s[tt];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) kk[tt * D + col + j] = et * to_f(x[u][j]);
+                } else {
+                    put8(&vv[tt * D + col], x[u]);
+                }
             }
         }
     }
     __syncthreads();
-    const int c = t % D, rg = t / D;
     const float e0 = e_s[n];
-    float *S = state + ((int64_t)b * H + h) * D * D;
-    constexpr int RB = 8;                // rows in flight per thread
-    for (int r0 = rg; r0 < D; r0 += NG * RB) {
-        float sv[RB];
 #pragma unroll
-        for (int u = 0; u < RB; ++u) sv[u] = S[(int64_t)(r0 + NG * u) * D + c];
-#pragma unroll
-        for (int u = 0; u < RB; ++u) {
-            const int r = r0 + NG * u;
-            float x = e0 * sv[u];
-            for (int tt = 0; tt < n; ++tt) x = __builtin_fmaf(kk[tt * D + r], vv[tt * D + c], x);
-            S[(int64_t)r * D + c] = x;
-        }
+    for (int u = 0; u < RT; ++u) {
+        const int r = rg + NG * u;
+        float x = e0 * sv[u];
+        for (int tt = 0; tt < n; ++tt) x = __builtin_fmaf(kk[tt * D + r], vv[tt * D + c], x);
+        S[(int64_t)r * D + c] = x;
     }
 }
 
