@@ -255,15 +255,19 @@ __global__ __launch_bounds__(256) void rec_tree_kernel(
 }
 
 // The accepted node's state, in place: one workgroup (256 threads) per (request, head).
-// Requests with accepted_len < 0 (failed) keep their state.
+// Requests with accepted_len < 0 (failed) keep their state. Each thread owns column c of rows
+// rg, rg + NG, ...: S[r][c] = e_0 S0[r][c] + sum_t (e_t k_t[r]) v_t[c], path order, with the
+// path's values of column c held in registers (the first 16 path tokens).
 template <int D>
 __global__ __launch_bounds__(256) void rec_commit_kernel(
     float *__restrict__ state, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     const float *__restrict__ log_gate, const int32_t *__restrict__ accepted_len,
     const int32_t *__restrict__ accepted_path, int K, int H) {
     constexpr int NG = 256 / D;
-    __shared__ __attribute__((aligned(16))) float kk[kRecMaxK * D];   // e_t k_t, path order
-    __shared__ __attribute__((aligned(16))) float vv[kRecMaxK * D];
+    constexpr int RT = D / NG;           // rows per thread
+    constexpr int VR = 16;               // path tokens whose values sit in registers
+    __shared__ __attribute__((aligned(16))) bf16 kb[kRecMaxK * D];   // k_t, path order
+    __shared__ __attribute__((aligned(16))) bf16 vb[kRecMaxK * D];   // v_t, path order
     __shared__ float e_s[kRecMaxK + 1];
     __shared__ float gp[kRecMaxK];        // log-gates of the path's nodes
     __shared__ int node[kRecMaxK];
@@ -274,8 +278,7 @@ __global__ __launch_bounds__(256) void rec_commit_kernel(
     const int t = threadIdx.x;
     const int a = accepted_len[b];
     if (a < 0) return;                   // uniform: a failed request keeps its state
-    // this thread's rows rg, rg + NG, ... of column c, in flight while the path is set up
-    constexpr int RT = D / NG;
+    // this thread's rows of column c, in flight while the path is set up
     const int c = t % D, rg = t / D;
     float *S = state + ((int64_t)b * H + h) * D * D;
     float sv[RT];
@@ -299,7 +302,6 @@ __global__ __launch_bounds__(256) void rec_commit_kernel(
         for (int u = (t < n ? t + 1 : 0); u < n; ++u) s += (double)gp[u];
         e_s[t] = expf((float)s);
     }
-    __syncthreads();
     {
         constexpr int TPR = D / 8;
         constexpr int NIT = 2 * kRecMaxK * TPR / 256;
@@ -318,24 +320,26 @@ __global__ __launch_bounds__(256) void rec_commit_kernel(
             const int e = t + 256 * u;
             const int which = e / (kRecMaxK * TPR), rem = e % (kRecMaxK * TPR);
             const int tt = rem / TPR, col = (rem % TPR) * 8;
-            if (tt < n) {
-                if (which == 0) {
-                    const float et = e_s[tt];
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) kk[tt * D + col + j] = et * to_f(x[u][j]);
-                } else {
-                    put8(&vv[tt * D + col], x[u]);
-                }
-            }
+            if (tt < n) *reinterpret_cast<bf16x8 *>(&(which == 0 ? kb : vb)[tt * D + col]) = x[u];
         }
     }
     __syncthreads();
     const float e0 = e_s[n];
+    float vr[VR], er[VR];
+#pragma unroll
+    for (int tt = 0; tt < VR; ++tt) {
+        vr[tt] = tt < n ? to_f(vb[tt * D + c]) : 0.f;
+        er[tt] = tt < n ? e_s[tt] : 0.f;
+    }
 #pragma unroll
     for (int u = 0; u < RT; ++u) {
         const int r = rg + NG * u;
         float x = e0 * sv[u];
-        for (int tt = 0; tt < n; ++tt) x = __builtin_fmaf(kk[tt * D + r], vv[tt * D + c], x);
+#pragma unroll
+        for (int tt = 0; tt < VR; ++tt)
+            if (tt < n) x = __builtin_fmaf(er[tt] * to_f(kb[tt * D + r]), vr[tt], x);
+        for (int tt = VR; tt < n; ++tt)
+            x = __builtin_fmaf(e_s[tt] * to_f(kb[tt * D + r]), to_f(vb[tt * D + c]), x);
         S[(int64_t)r * D + c] = x;
     }
 }
