@@ -360,7 +360,8 @@ def rec_bench(args, device):
     spec_rec_commit), 8 layers with their own states and inputs (about 1.2 GB per step, beyond
     the memory-side cache), replayed from a HIP graph. Algorithmic bytes of a tree pass, per
     (request, head): the state D*D*4, q, k, v K*D*2 each, gates and parents K*4 each, outputs
-    K*D*4; of a commit: the state read and written, and the path's k and v rows."""
+    K*D*4; of a commit: the state read and written, the path's k and v rows, and the K path ids
+    each (request, head) reads."""
     B, K, H, D, L = 32, 64, 32, 128, 8
     parents = np.stack([synth.random_tree(K, 10, SEED, "rec", b) for b in range(B)]).astype(np.int32)
     par = torch.from_numpy(parents).to(device)
@@ -452,23 +453,24 @@ def rec_bench(args, device):
         f"({ach:.0f} GB/s, {flops / t_tree / 1e12:.1f} TFLOP/s)")
     if not args.no_cpu_baseline:
         import oracle
-        S0, q, k, v, g = layers[0]
         spent, n = 0.0, 0
-        while spent < args.cpu_seconds and n < B * H:
-            b, h = n % B, (n * 7) % H
-            sl = lambda t: t[b:b + 1, :, h:h + 1].contiguous().cpu()
-            bits = lambda t: t.view(torch.int16).numpy().view(np.uint16)
+        bits = lambda t: t.contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+        while spent < args.cpu_seconds and n < L * B * H:
+            l, b, h = n // (B * H), n % B, (n * 7) % H
+            S0, q, k, v, g = layers[l]
+            sl = lambda t: t[b:b + 1, :, h:h + 1]
             hs = (S0[b:b + 1, h:h + 1].contiguous().cpu().numpy(), bits(sl(q)), bits(sl(k)),
-                  bits(sl(v)), g[b:b + 1, :, h:h + 1].contiguous().cpu().numpy())
+                  bits(sl(v)), sl(g).contiguous().cpu().numpy())
             t0 = time.time()
             oracle.rec_tree(*hs, parents[b:b + 1])
+            oracle.rec_commit(hs[0], hs[2], hs[3], hs[4], acc[b:b + 1], path[b:b + 1])
             spent += time.time() - t0
             n += 1
         per_pair = spent / n
         result["cpu_baseline"] = {"value": round(K / per_pair / H, 2), "unit": "node-layers/s",
                                   "cores": oracle.threads(), "kind": "oracle",
-                                  "sample": f"{n} (request, head) tree passes of layer 0 ({spent:.1f}s), "
-                                            f"scaled to all {H} heads of a layer (commit not timed)"}
+                                  "sample": f"{n} (layer, request, head) tree passes + commits "
+                                            f"({spent:.1f}s), scaled to a step's {L * B * H}"}
         log(f"cpu baseline: {result['cpu_baseline']}")
     print(json.dumps(result), flush=True)
 
