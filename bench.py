@@ -45,15 +45,20 @@ import tree_verification_skinny_amd as tv
 
 METRIC = "verified tokens/sec + verify-step HBM GB/s (% peak), 27B-shape dense, 1 GPU"
 
-# HBM traffic of one gate/up projection launch, from two rocprofv3 --pmc passes over this script
+# HBM traffic of one launch of the dominant kernel (the gate/up projection; the recurrent layers'
+# tree pass for --config rec), from two rocprofv3 --pmc passes over this script
 # (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch, averaged over the kernel's dispatches), each
 # scaled by what the same counter reads for a device-to-device copy of 4 GiB (bytes known). The
-# figures hold for the GEMM source they were taken on; any other source reports null.
+# figures hold for the kernel source they were taken on; any other source reports null.
 PMC_TRAFFIC = {
     ("block", "bf16"): {"source": "tree_verification_skinny_amd/csrc/k_gemm.hip",
                         "sha256": "f373f9dd17953c6758f365c0a86324030f6a99ed9c58cb5019dcae725401a84e",
                         "fetch_kib": 174761.283, "write_kib": 544.0,
                         "fetch_scale": 1.9999858, "write_scale": 1.0},
+    ("rec", "bf16"): {"source": "tree_verification_skinny_amd/csrc/k_recurrent.hip",
+                      "sha256": "6c7d7c1fb3d4e8bc9bc6b5e2041c3bd833034de7f5a3df5e8c39ac9b76ee7bfe",
+                      "fetch_kib": 59407.797, "write_kib": 32768.125,
+                      "fetch_scale": 1.9999851, "write_scale": 1.0},
     ("block", "w12"): {"source": "tree_verification_skinny_amd/csrc/k_gemm.hip",
                        "sha256": "f373f9dd17953c6758f365c0a86324030f6a99ed9c58cb5019dcae725401a84e",
                        "fetch_kib": 131470.243, "write_kib": 544.0,
@@ -156,8 +161,9 @@ def time_gate_up(step_with_events, events, n_layers, stream, reps):
 
 
 def pmc_traffic(config, weights="bf16"):
-    """Counter-measured HBM bytes per gate/up launch, or None when there are no counters for this
-    workload and weight layout or the GEMM source has changed since they were taken."""
+    """Counter-measured HBM bytes per launch of the workload's dominant kernel (the gate/up
+    projection; the tree pass for the recurrent layers), or None when there are no counters for
+    this workload and weight layout or the kernel's source has changed since they were taken."""
     import hashlib
     rec = PMC_TRAFFIC.get((config, weights))
     if rec is None or rec["sha256"] is None:
@@ -420,6 +426,7 @@ def rec_bench(args, device):
         e1.record(stream)
         e1.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
+    copy_gbps = copy_probe(device)     # also the calibration copy of the counter passes
     depth_sum = 0
     for b in range(B):
         d = np.zeros(K, np.int64)
@@ -442,10 +449,10 @@ def rec_bench(args, device):
                                f"(depth <= 10), {H} heads, {D}x{D} fp32 states, {L} layers; tree pass "
                                f"+ state commit per layer", "hip_graph": True},
         "hbm": {"bytes_per_step": int(step_bytes_), "achieved_gbps": round(gbps, 1),
-                "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4)},
+                "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4), "copy_probe_gbps": round(copy_gbps, 1)},
         "roofline": {"kernel": "rec_tree_kernel<128>", "bound": "hbm", "achieved": round(ach, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
-                     "traffic": None, "us_per_launch": round(t_tree * 1e6, 2),
+                     "traffic": pmc_traffic("rec"), "us_per_launch": round(t_tree * 1e6, 2),
                      "bytes_per_launch": int(tree_bytes),
                      "fp32_tflops": round(flops / t_tree / 1e12, 2)},
     }

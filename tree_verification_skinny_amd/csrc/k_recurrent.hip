@@ -241,13 +241,28 @@ __global__ __launch_bounds__(256) void rec_tree_kernel(
                     o[u][it] = mfma16x16x32(lo, vf, o[u][it]);
                 }
             }
-#pragma unroll
-            for (int u = 0; u < CPW; ++u) {
-                const int cc = 16 * (wave * CPW + u) + r16;
+            if constexpr (CPW == 2) {
+                // the wave's 32 columns of a row as one 128-byte line: lane r16 stores columns
+                // 2 r16 and 2 r16 + 1, gathered from its row group's lanes
+                const int s0 = 16 * grp + ((2 * r16) & 15), s1 = s0 + 1;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
+                    const float a0 = __shfl(o[0][it][e], s0, 64), a1 = __shfl(o[0][it][e], s1, 64);
+                    const float b0 = __shfl(o[1][it][e], s0, 64), b1 = __shfl(o[1][it][e], s1, 64);
                     const int i = 16 * it + 4 * grp + e;
-                    if (i < K) out[(((int64_t)b * K + i) * H + h) * D + cc] = o[u][it][e];
+                    if (i < K)
+                        *reinterpret_cast<float2 *>(&out[(((int64_t)b * K + i) * H + h) * D + 32 * wave + 2 * r16]) =
+                            r16 < 8 ? make_float2(a0, a1) : make_float2(b0, b1);
+                }
+            } else {
+#pragma unroll
+                for (int u = 0; u < CPW; ++u) {
+                    const int cc = 16 * (wave * CPW + u) + r16;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int i = 16 * it + 4 * grp + e;
+                        if (i < K) out[(((int64_t)b * K + i) * H + h) * D + cc] = o[u][it][e];
+                    }
                 }
             }
         }
