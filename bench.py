@@ -56,8 +56,8 @@ PMC_TRAFFIC = {
                         "fetch_kib": 174761.283, "write_kib": 544.0,
                         "fetch_scale": 1.9999858, "write_scale": 1.0},
     ("rec", "bf16"): {"source": "tree_verification_skinny_amd/csrc/k_recurrent.hip",
-                      "sha256": "6c7d7c1fb3d4e8bc9bc6b5e2041c3bd833034de7f5a3df5e8c39ac9b76ee7bfe",
-                      "fetch_kib": 59407.797, "write_kib": 32768.125,
+                      "sha256": "8372e05793d55045b458cfb26bacb76706adcb9db23234237b12dffdafc7abcb",
+                      "fetch_kib": 59449.781, "write_kib": 32768.125,
                       "fetch_scale": 1.9999851, "write_scale": 1.0},
     ("block", "w12"): {"source": "tree_verification_skinny_amd/csrc/k_gemm.hip",
                        "sha256": "f373f9dd17953c6758f365c0a86324030f6a99ed9c58cb5019dcae725401a84e",

@@ -1,5 +1,5 @@
-// k_recurrent.hip — tree verification for the recurrent layers of a hybrid target, and the
-// state commit after acceptance.
+// k_recurrent.hip — tree verification for the recurrent layers of a hybrid target (the state
+// commit after acceptance is in k_rec_commit.hip).
 //
 // The SpecPilot digest [airadar.tv — "Reasons"] and news piece [wireai.ir — key innovations]
 // name tree verification for targets that mix recurrent layers in, without the recurrence.
@@ -13,27 +13,11 @@
 // i's path (root to i, inclusive) and anc(i) that path as a 64-bit mask,
 //     o_i = exp(c_i) q_i^T S0 + sum_{j in anc(i)} exp(c_i - c_j) (q_i . k_j) v_j,
 // so the committed state is read once per (request, head) and never copied; the tree enters
-// only through the mask and the path sums, exactly as the attention layers see it. The commit
-// rebuilds the accepted node's state in place:
-//     S <- exp(c_best) S0 + sum_{t on the path} exp(c_best - c_t) k_t v_t^T.
-// Path sums are taken in float64 (at most 64 terms); everything else is fp32.
+// only through the mask and the path sums, exactly as the attention layers see it. Path sums are
+// taken in float64 (at most 64 terms); everything else accumulates in fp32.
 #include "kernels.hpp"
 
 namespace sv {
-
-namespace {
-
-constexpr int kRecMaxK = 64;
-
-// 8 bf16 -> 8 floats in LDS
-__device__ __forceinline__ void put8(float *dst, bf16x8 v) {
-    float4 a = make_float4(to_f(v[0]), to_f(v[1]), to_f(v[2]), to_f(v[3]));
-    float4 b = make_float4(to_f(v[4]), to_f(v[5]), to_f(v[6]), to_f(v[7]));
-    *reinterpret_cast<float4 *>(dst) = a;
-    *reinterpret_cast<float4 *>(dst + 4) = b;
-}
-
-}  // namespace
 
 // x = hi + mid + lo with three bf16 parts, each the rounded remainder of the previous (the
 // remainders are exact in fp32): the sum carries 24 significant bits, so products with bf16
@@ -269,96 +253,6 @@ __global__ __launch_bounds__(256) void rec_tree_kernel(
     }
 }
 
-// The accepted node's state, in place: one workgroup (256 threads) per (request, head).
-// Requests with accepted_len < 0 (failed) keep their state. Each thread owns column c of rows
-// rg, rg + NG, ...: S[r][c] = e_0 S0[r][c] + sum_t (e_t k_t[r]) v_t[c], path order, with the
-// path's values of column c held in registers (the first 16 path tokens).
-template <int D>
-__global__ __launch_bounds__(256) void rec_commit_kernel(
-    float *__restrict__ state, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
-    const float *__restrict__ log_gate, const int32_t *__restrict__ accepted_len,
-    const int32_t *__restrict__ accepted_path, int K, int H) {
-    constexpr int NG = 256 / D;
-    constexpr int RT = D / NG;           // rows per thread
-    constexpr int VR = 16;               // path tokens whose values sit in registers
-    __shared__ __attribute__((aligned(16))) bf16 kb[kRecMaxK * D];   // k_t, path order
-    __shared__ __attribute__((aligned(16))) bf16 vb[kRecMaxK * D];   // v_t, path order
-    __shared__ float e_s[kRecMaxK + 1];
-    __shared__ float gp[kRecMaxK];        // log-gates of the path's nodes
-    __shared__ int node[kRecMaxK];
-    __shared__ int bad_s;
-
-    const int wg = blockIdx.x;
-    const int b = wg / H, h = wg % H;
-    const int t = threadIdx.x;
-    const int a = accepted_len[b];
-    if (a < 0) return;                   // uniform: a failed request keeps its state
-    // this thread's rows of column c, in flight while the path is set up
-    const int c = t % D, rg = t / D;
-    float *S = state + ((int64_t)b * H + h) * D * D;
-    float sv[RT];
-#pragma unroll
-    for (int u = 0; u < RT; ++u) sv[u] = S[(int64_t)(rg + NG * u) * D + c];
-    const int n = a + 1 <= K ? a + 1 : K;
-    if (t < 64) {
-        const int p = t < n ? accepted_path[(int64_t)b * K + t] : 0;
-        const bool bad = __any(t < n && (p < 0 || p >= K));
-        if (t < n) {
-            node[t] = p;
-            if (!bad) gp[t] = log_gate[((int64_t)b * K + p) * H + h];
-        }
-        if (t == 0) bad_s = (a + 1 > K || bad) ? 1 : 0;
-    }
-    __syncthreads();
-    if (bad_s) return;                   // not a path this pass could have produced
-    if (t <= n) {
-        // t < n: decay from node t (exclusive) to the accepted node; t == n: from S0
-        double s = 0.0;
-        for (int u = (t < n ? t + 1 : 0); u < n; ++u) s += (double)gp[u];
-        e_s[t] = expf((float)s);
-    }
-    {
-        constexpr int TPR = D / 8;
-        constexpr int NIT = 2 * kRecMaxK * TPR / 256;
-        bf16x8 x[NIT];
-#pragma unroll
-        for (int u = 0; u < NIT; ++u) {
-            const int e = t + 256 * u;
-            const int which = e / (kRecMaxK * TPR), rem = e % (kRecMaxK * TPR);
-            const int tt = rem / TPR, col = (rem % TPR) * 8;
-            if (tt < n)
-                x[u] = *reinterpret_cast<const bf16x8 *>((which == 0 ? k : v) +
-                                                         (((int64_t)b * K + node[tt]) * H + h) * D + col);
-        }
-#pragma unroll
-        for (int u = 0; u < NIT; ++u) {
-            const int e = t + 256 * u;
-            const int which = e / (kRecMaxK * TPR), rem = e % (kRecMaxK * TPR);
-            const int tt = rem / TPR, col = (rem % TPR) * 8;
-            if (tt < n) *reinterpret_cast<bf16x8 *>(&(which == 0 ? kb : vb)[tt * D + col]) = x[u];
-        }
-    }
-    __syncthreads();
-    const float e0 = e_s[n];
-    float vr[VR], er[VR];
-#pragma unroll
-    for (int tt = 0; tt < VR; ++tt) {
-        vr[tt] = tt < n ? to_f(vb[tt * D + c]) : 0.f;
-        er[tt] = tt < n ? e_s[tt] : 0.f;
-    }
-#pragma unroll
-    for (int u = 0; u < RT; ++u) {
-        const int r = rg + NG * u;
-        float x = e0 * sv[u];
-#pragma unroll
-        for (int tt = 0; tt < VR; ++tt)
-            if (tt < n) x = __builtin_fmaf(er[tt] * to_f(kb[tt * D + r]), vr[tt], x);
-        for (int tt = VR; tt < n; ++tt)
-            x = __builtin_fmaf(e_s[tt] * to_f(kb[tt * D + r]), to_f(vb[tt * D + c]), x);
-        S[(int64_t)r * D + c] = x;
-    }
-}
-
 hipError_t rec_tree(const float *state, const bf16 *q, const bf16 *k, const bf16 *v,
                     const float *log_gate, const int32_t *tree_parent, int B, int K, int H, int D,
                     float *out, int32_t *status, hipStream_t st) {
@@ -369,19 +263,6 @@ hipError_t rec_tree(const float *state, const bf16 *q, const bf16 *k, const bf16
     else
         hipLaunchKernelGGL(rec_tree_kernel<64>, grid, dim3(256), 0, st, state, q, k, v, log_gate,
                            tree_parent, K, H, out, status);
-    return hipGetLastError();
-}
-
-hipError_t rec_commit(float *state, const bf16 *k, const bf16 *v, const float *log_gate,
-                      const int32_t *accepted_len, const int32_t *accepted_path, int B, int K, int H,
-                      int D, hipStream_t st) {
-    const dim3 grid((unsigned)(B * H));
-    if (D == 128)
-        hipLaunchKernelGGL(rec_commit_kernel<128>, grid, dim3(256), 0, st, state, k, v, log_gate,
-                           accepted_len, accepted_path, K, H);
-    else
-        hipLaunchKernelGGL(rec_commit_kernel<64>, grid, dim3(256), 0, st, state, k, v, log_gate,
-                           accepted_len, accepted_path, K, H);
     return hipGetLastError();
 }
 

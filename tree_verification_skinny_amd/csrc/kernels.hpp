@@ -132,8 +132,10 @@ hipError_t prefill_gather(const int32_t *prompt, int p, int c0, int n, int B, in
 hipError_t prefill_advance(const int32_t *acc, const int32_t *greedy, int n, int B, bool last,
                            int32_t *failed, int32_t *ctx_len, int32_t *next_token, hipStream_t st);
 hipError_t prefill_last_logits(const float *logits, int n, int B, int V, float *out, hipStream_t st);
-// Recurrent layers of a hybrid target (k_recurrent.hip): the tree pass over the committed state
-// and the accepted node's state written in place. D = dk = dv, 64 or 128; K <= 64.
+// Recurrent layers of a hybrid target: the tree pass over the committed state (k_recurrent.hip)
+// and the accepted node's state written in place (k_rec_commit.hip). D = dk = dv, 64 or 128;
+// K <= kRecMaxK.
+constexpr int kRecMaxK = 64;
 hipError_t rec_tree(const float *state, const bf16 *q, const bf16 *k, const bf16 *v,
                     const float *log_gate, const int32_t *tree_parent, int B, int K, int H, int D,
                     float *out, int32_t *status, hipStream_t st);
