@@ -361,6 +361,15 @@ def prefill_bench(args, shape, device):
     print(json.dumps(result), flush=True)
 
 
+def rec_bytes(B, K, H, D, accepted_len):
+    """Algorithmic bytes of one recurrent tree pass and one state commit (fp32 states, bf16 q, k,
+    v, fp32 gates and outputs, int32 parents and path ids)."""
+    tree = B * H * (D * D * 4 + 3 * K * D * 2 + 2 * K * 4 + K * D * 4)
+    commit = (B * H * (2 * D * D * 4) + int((np.asarray(accepted_len) + 1).sum()) * H * 2 * D * 2 +
+              B * H * K * 4)
+    return tree, commit
+
+
 def rec_bench(args, device):
     """Tree pass + state commit of a hybrid target's recurrent layers (spec_rec_tree_verify,
     spec_rec_commit), 8 layers with their own states and inputs (about 1.2 GB per step, beyond
@@ -433,8 +442,7 @@ def rec_bench(args, device):
         for i in range(1, K):
             d[i] = d[parents[b, i]] + 1
         depth_sum += int((d + 1).sum())            # path lengths, root .. node
-    tree_bytes = B * H * (D * D * 4 + 3 * K * D * 2 + 2 * K * 4 + K * D * 4)
-    commit_bytes = B * H * (2 * D * D * 4) + int((acc + 1).sum()) * H * 2 * D * 2 + B * H * K * 4
+    tree_bytes, commit_bytes = rec_bytes(B, K, H, D, acc)
     step_bytes_ = L * (tree_bytes + commit_bytes)
     gbps = step_bytes_ / (ms / 1e3) / 1e9
     ach = tree_bytes / t_tree / 1e9

@@ -2,6 +2,8 @@
 shapes by hand (27B-class dense: 64 layers, hidden 5120, 40 q / 8 kv heads of 128, SwiGLU 17408,
 vocab 151936): every weight read once, every context K/V row read once per layer, the draft
 rows' K/V written. No GPU needed."""
+import numpy as np
+
 import bench
 import synth
 
@@ -27,3 +29,11 @@ def test_gate_up_launch_bytes():
     # the packed [34816][5120] weight, the [16][5120] operand in, the [16][17408] SwiGLU output out
     assert bench.gate_up_bytes(shape, 16) == 2 * 34816 * 5120 + 2 * 16 * 5120 + 2 * 16 * 17408
     assert bench.gate_up_bytes(shape, 16) == 357_236_736
+
+
+def test_recurrent_bytes_from_the_shapes():
+    """Tree pass: per (request, head) the 128 x 128 fp32 state, q, k, v rows of 64 nodes, gates,
+    parents and fp32 outputs; commit: the state read and written plus the accepted rows."""
+    tree, commit = bench.rec_bytes(32, 64, 32, 128, np.full(32, 5))
+    assert tree == 1024 * (65536 + 49152 + 512 + 32768) == 151_519_232
+    assert commit == 1024 * 131072 + 32 * 6 * 32 * 512 + 1024 * 256
