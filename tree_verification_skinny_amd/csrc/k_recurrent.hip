@@ -56,6 +56,7 @@ __global__ __launch_bounds__(256) void rec_tree_kernel(
     constexpr int VP = kRecMaxK + 8;     // padded LDS row of V^T (bf16)
     __shared__ __attribute__((aligned(16))) float wl[kRecMaxK * WP];
     __shared__ __attribute__((aligned(16))) bf16 vt[D * VP];
+    __shared__ __attribute__((aligned(16))) bf16 ks[kRecMaxK * (D + 8)];   // key rows, padded
     __shared__ double csum[kRecMaxK];
     __shared__ uint64_t anc[kRecMaxK];
     __shared__ int bad_s;
@@ -66,20 +67,32 @@ __global__ __launch_bounds__(256) void rec_tree_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int r16 = lane & 15, grp = lane >> 4;
     const int NT = (K + 15) >> 4;        // node tiles
-
-    // this wave's state fragments, in flight from the start: column 16 ct + r16, rows
-    // 32 rs + 8 grp + e
-    const float *S0 = state + ((int64_t)b * H + h) * D * D;
-    float sf[CPW][RS][8];
-#pragma unroll
-    for (int u = 0; u < CPW; ++u)
-#pragma unroll
-        for (int rs = 0; rs < RS; ++rs)
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                sf[u][rs][e] = S0[(int64_t)(32 * rs + 8 * grp + e) * D + 16 * (wave * CPW + u) + r16];
-    // the query fragments of every node tile (rows past K are zero)
     auto row_ptr = [&](const bf16 *base, int i) { return base + (((int64_t)b * K + i) * H + h) * D; };
+
+    // Loads go out in the order they are needed (a wave waits for its loads in issue order):
+    // the tree's links and gates, the value and key rows (staged in LDS before the first
+    // barrier), the query fragments, the state fragments.
+    int p_in = lane - 1;
+    float g_in = 0.f;
+    if (t < 64 && lane < K) {
+        if (tree_parent != nullptr) p_in = tree_parent[(int64_t)b * K + lane];
+        g_in = log_gate[((int64_t)b * K + lane) * H + h];
+    }
+    constexpr int TPR = D / 8;
+    constexpr int NIT = kRecMaxK * TPR / 256;
+    bf16x8 vx[NIT], kx[NIT];
+#pragma unroll
+    for (int u = 0; u < NIT; ++u) {
+        const int e = t + 256 * u, j = e / TPR, col = (e % TPR) * 8;
+        vx[u] = j < K ? *reinterpret_cast<const bf16x8 *>(row_ptr(v, j) + col) : bf16x8{};
+    }
+#pragma unroll
+    for (int u = 0; u < NIT; ++u) {
+        const int e = t + 256 * u, j = e / TPR, col = (e % TPR) * 8;
+        kx[u] = j < K ? *reinterpret_cast<const bf16x8 *>(row_ptr(k, j) + col) : bf16x8{};
+    }
+
+    // the query fragments of every node tile (rows past K are zero)
     bf16x8 qf[4][RS];
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
@@ -89,10 +102,20 @@ __global__ __launch_bounds__(256) void rec_tree_kernel(
             qf[it][rs] = i < K ? *reinterpret_cast<const bf16x8 *>(row_ptr(q, i) + 32 * rs + 8 * grp) : bf16x8{};
     }
 
+    // this wave's state fragments: column 16 ct + r16, rows 32 rs + 8 grp + e
+    const float *S0 = state + ((int64_t)b * H + h) * D * D;
+    float sf[CPW][RS][8];
+#pragma unroll
+    for (int u = 0; u < CPW; ++u)
+#pragma unroll
+        for (int rs = 0; rs < RS; ++rs)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                sf[u][rs][e] = S0[(int64_t)(32 * rs + 8 * grp + e) * D + 16 * (wave * CPW + u) + r16];
+
     // ---- the tree: parent links, ancestor masks and path sums of log-gates (pointer jumping) --
     if (t < 64) {
-        int p = lane - 1;
-        if (tree_parent != nullptr && lane < K) p = tree_parent[(int64_t)b * K + lane];
+        const int p = p_in;
         const bool ok = lane >= K || (lane == 0 ? p == -1 : (p >= 0 && p < lane));
         const bool bad = __any(!ok);
         if (lane == 0) bad_s = bad ? 1 : 0;
@@ -100,7 +123,7 @@ __global__ __launch_bounds__(256) void rec_tree_kernel(
             // invariant: m holds the path from lane up to (not including) ptr, cs the sum of
             // its log-gates (float64)
             uint64_t m = lane < K ? (1ull << lane) : 0ull;
-            double cs = lane < K ? (double)log_gate[((int64_t)b * K + lane) * H + h] : 0.0;
+            double cs = lane < K ? (double)g_in : 0.0;
             int ptr = lane < K ? p : -1;
 #pragma unroll
             for (int round = 0; round < 6; ++round) {
@@ -123,21 +146,12 @@ __global__ __launch_bounds__(256) void rec_tree_kernel(
     }
     // W starts at zero (pairs off the path, and key columns past the last node); V^T staged
     for (int e = t; e < kRecMaxK * WP; e += 256) wl[e] = 0.f;
-    {
-        constexpr int TPR = D / 8;
-        constexpr int NIT = kRecMaxK * TPR / 256;
-        bf16x8 x[NIT];
 #pragma unroll
-        for (int u = 0; u < NIT; ++u) {
-            const int e = t + 256 * u, j = e / TPR, col = (e % TPR) * 8;
-            x[u] = j < K ? *reinterpret_cast<const bf16x8 *>(row_ptr(v, j) + col) : bf16x8{};
-        }
+    for (int u = 0; u < NIT; ++u) {
+        const int e = t + 256 * u, j = e / TPR, col = (e % TPR) * 8;
 #pragma unroll
-        for (int u = 0; u < NIT; ++u) {
-            const int e = t + 256 * u, j = e / TPR, col = (e % TPR) * 8;
-#pragma unroll
-            for (int z = 0; z < 8; ++z) vt[(col + z) * VP + j] = x[u][z];
-        }
+        for (int z = 0; z < 8; ++z) vt[(col + z) * VP + j] = vx[u][z];
+        *reinterpret_cast<bf16x8 *>(&ks[j * (D + 8) + col]) = kx[u];
     }
     __syncthreads();
     const bool bad = bad_s != 0;
@@ -156,10 +170,8 @@ __global__ __launch_bounds__(256) void rec_tree_kernel(
             const int j = 16 * jt + r16;
             floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int rs = 0; rs < RS; ++rs) {
-                const bf16x8 kf = j < K ? *reinterpret_cast<const bf16x8 *>(row_ptr(k, j) + 32 * rs + 8 * grp) : bf16x8{};
-                acc = mfma16x16x32(qf[it][rs], kf, acc);
-            }
+            for (int rs = 0; rs < RS; ++rs)
+                acc = mfma16x16x32(qf[it][rs], *reinterpret_cast<const bf16x8 *>(&ks[j * (D + 8) + 32 * rs + 8 * grp]), acc);
             if (j < K) {
                 const double cj = csum[j];
 #pragma unroll
