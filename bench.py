@@ -383,7 +383,7 @@ def rec_bench(args, device):
     layers = []
     for l in range(L):
         S0, q, k, v, g = synth.rec_inputs(B, K, H, D, D, SEED, device, "bench", l)
-        layers.append((S0, q, k, v, g))
+        layers.append((S0.transpose(-1, -2).contiguous(), q, k, v, g))   # the library's layout
     out = torch.empty((B, K, H, D), dtype=torch.float32, device=device)
     status = torch.empty(B, dtype=torch.int32, device=device)
     # accepted path: the root path of a seeded node of each tree (what the greedy walk returns)
@@ -474,7 +474,7 @@ def rec_bench(args, device):
             l, b, h = n // (B * H), n % B, (n * 7) % H
             S0, q, k, v, g = layers[l]
             sl = lambda t: t[b:b + 1, :, h:h + 1]
-            hs = (S0[b:b + 1, h:h + 1].contiguous().cpu().numpy(), bits(sl(q)), bits(sl(k)),
+            hs = (S0[b:b + 1, h:h + 1].transpose(-1, -2).contiguous().cpu().numpy(), bits(sl(q)), bits(sl(k)),
                   bits(sl(v)), sl(g).contiguous().cpu().numpy())
             t0 = time.time()
             oracle.rec_tree(*hs, parents[b:b + 1])

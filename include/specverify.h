@@ -277,12 +277,14 @@ int spec_prefill(const spec_weights *weights, const spec_kv_cache *kv, const int
  *
  * spec_rec_tree_verify: one recurrent layer over a draft tree, reading the committed state once
  * and writing no per-node state.
- *   state [batch][n_heads][head_dim][head_dim] fp32 (read only); q, k, v
+ *   state: S stored transposed, [batch][n_heads][dv][dk] fp32 (element [c][r] holds S[r][c],
+ *   so each value column's dk entries are contiguous; read only); q, k, v
  *   [batch][k][n_heads][head_dim] bf16; log_gate [batch][k][n_heads] fp32 (g, normally <= 0);
  *   tree_parent [batch][k] int32 as for spec_verify, or NULL for chains; out
  *   [batch][k][n_heads][head_dim] fp32; status [batch] int32 out: 0, or 1 for a malformed tree
  *   (that request's outputs are zero).
- * spec_rec_commit: the state of each request's accepted node, written over state in place:
+ * spec_rec_commit: the state of each request's accepted node, written over state in place (same
+ *   transposed layout):
  *   the tokens accepted_path[b][0..accepted_len[b]] (node ids as spec_verify returns them)
  *   applied to the committed state. A request with accepted_len < 0, accepted_len >= k, or a
  *   node id outside [0, k) keeps its state. k, v, log_gate as passed to the verify call.

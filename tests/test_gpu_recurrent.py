@@ -37,6 +37,11 @@ def _inputs(B, K, H, D, seed):
     return S0, q, k, v, g
 
 
+def _T(S):
+    """The library's state layout: S transposed, [B][H][dv][dk]."""
+    return S.transpose(-1, -2).contiguous()
+
+
 def _host(S0, q, k, v, g):
     return S0.cpu().numpy(), bits(q), bits(k), bits(v), g.cpu().numpy()
 
@@ -73,11 +78,12 @@ def _tree_bound(S0, q, k, v, g, parents, K, D):
     return bound
 
 
-def _run_tree(S0, q, k, v, g, parent):
+def _run_tree(state_t, q, k, v, g, parent):
+    """state_t: the state in the library's (transposed) layout."""
     B, K, H, D = q.shape
     out = torch.full((B, K, H, D), float("nan"), device=DEV)
     status = torch.full((B,), -7, dtype=torch.int32, device=DEV)
-    tv.spec_rec_tree_verify(S0, q, k, v, g, parent, out, status)
+    tv.spec_rec_tree_verify(state_t, q, k, v, g, parent, out, status)
     torch.cuda.synchronize()
     return out.cpu().numpy(), status.cpu().numpy()
 
@@ -93,7 +99,7 @@ def test_tree_pass_matches_oracle(B, K, H, D, tree):
     if tree:
         parents = np.stack([synth.random_tree(K, 10, K, "rec", b) for b in range(B)]).astype(np.int32)
         pt = torch.from_numpy(parents).to(DEV)
-    o, st = _run_tree(S0, q, k, v, g, pt)
+    o, st = _run_tree(_T(S0), q, k, v, g, pt)
     hs = _host(S0, q, k, v, g)
     ref, st_ref = oracle.rec_tree(*hs, parents)
     assert list(st) == list(st_ref) == [0] * B
@@ -107,7 +113,7 @@ def test_malformed_tree_flags_only_its_request():
     S0, q, k, v, g = _inputs(B, K, H, D, 99)
     parents = np.stack([synth.random_tree(K, 5, 99, b) for b in range(B)]).astype(np.int32)
     parents[1, 6] = 9          # a parent after its child
-    o, st = _run_tree(S0, q, k, v, g, torch.from_numpy(parents).to(DEV))
+    o, st = _run_tree(_T(S0), q, k, v, g, torch.from_numpy(parents).to(DEV))
     assert list(st) == [0, 1, 0]
     assert not o[1].any()
     ref, st_ref = oracle.rec_tree(*_host(S0, q, k, v, g), parents)
@@ -132,10 +138,10 @@ def test_commit_matches_oracle(B, K, H, D):
         path[b, :len(p)] = p
     acc[B - 1] = -1                          # a failed request keeps its state
     hs = _host(S0, q, k, v, g)
-    state = S0.clone()
+    state = _T(S0)
     tv.spec_rec_commit(state, k, v, g, torch.from_numpy(acc).to(DEV), torch.from_numpy(path).to(DEV))
     torch.cuda.synchronize()
-    got = state.cpu().numpy()
+    got = state.transpose(-1, -2).cpu().numpy()
     ref = oracle.rec_commit(*hs[:1], *hs[2:], acc, path)
     assert np.array_equal(got[B - 1], hs[0][B - 1])
     kf, vf = (np.abs(oracle.from_bf16(x).astype(np.float64)) for x in (hs[2], hs[3]))
@@ -157,8 +163,8 @@ def test_commit_then_pass_equals_child_in_tree():
     B, K, H, D = 1, 10, 2, 128
     S0, q, k, v, g = _inputs(B, K, H, D, 1234)
     parents = np.asarray([[-1, 0, 1, 1, 0, 3, 5, 2, 6, 6]], np.int32)
-    o, _ = _run_tree(S0, q, k, v, g, torch.from_numpy(parents).to(DEV))
-    state = S0.clone()
+    o, _ = _run_tree(_T(S0), q, k, v, g, torch.from_numpy(parents).to(DEV))
+    state = _T(S0)
     path = np.zeros((1, K), np.int32)
     path[0, :5] = [0, 1, 3, 5, 6]
     tv.spec_rec_commit(state, k, v, g, torch.tensor([4], dtype=torch.int32, device=DEV),
@@ -177,7 +183,7 @@ def test_full_size_sampled_against_oracle():
     print(f"rec full size B={B} K={K} H={H} D={D}", flush=True)
     S0, q, k, v, g = _inputs(B, K, H, D, 2026)
     parents = np.stack([synth.random_tree(K, 10, 2026, "full", b) for b in range(B)]).astype(np.int32)
-    o, st = _run_tree(S0, q, k, v, g, torch.from_numpy(parents).to(DEV))
+    o, st = _run_tree(_T(S0), q, k, v, g, torch.from_numpy(parents).to(DEV))
     assert not st.any()
     for b, h in [(0, 0), (13, 31), (31, 7)]:
         S = S0[b:b + 1, h:h + 1].contiguous()

@@ -384,7 +384,8 @@ def spec_read_probe(buf: torch.Tensor, out: torch.Tensor, stream=None) -> None:
 def spec_rec_tree_verify(state: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                          log_gate: torch.Tensor, tree_parent: Optional[torch.Tensor],
                          out: torch.Tensor, status: torch.Tensor, stream=None) -> None:
-    """One recurrent layer over draft trees. state fp32 [B][H][D][D]; q, k, v bf16 [B][K][H][D];
+    """One recurrent layer over draft trees. state fp32 [B][H][D][D], S transposed ([dv][dk]);
+    q, k, v bf16 [B][K][H][D];
     log_gate fp32 [B][K][H]; tree_parent int32 [B][K] or None (chains); out fp32 [B][K][H][D];
     status int32 [B] (1 = malformed tree)."""
     B, K, H, D = q.shape
@@ -403,7 +404,7 @@ def spec_rec_tree_verify(state: torch.Tensor, q: torch.Tensor, k: torch.Tensor, 
 
 def spec_rec_commit(state: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_gate: torch.Tensor,
                     accepted_len: torch.Tensor, accepted_path: torch.Tensor, stream=None) -> None:
-    """The accepted node's state written over state (fp32 [B][H][D][D]) in place; k, v, log_gate
+    """The accepted node's state written over state (fp32 [B][H][D][D], S transposed) in place; k, v, log_gate
     as passed to spec_rec_tree_verify; accepted_len int32 [B], accepted_path int32 [B][K]."""
     B, K, H, D = k.shape
     for t in (state, k, v, log_gate, accepted_len, accepted_path):

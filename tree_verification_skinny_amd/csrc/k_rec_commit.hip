@@ -11,18 +11,19 @@
 namespace sv {
 
 // The accepted node's state, in place: two workgroups (256 threads) per (request, head), each
-// taking half the rows, so that one round's writes overlap the next round's reads.
-// Requests with accepted_len < 0 (failed) keep their state. Each thread owns column c of rows
-// rg, rg + NG, ...: S[r][c] = e_0 S0[r][c] + sum_t (e_t k_t[r]) v_t[c], path order, with the
-// path's values of column c held in registers (the first 16 path tokens).
+// taking half the value columns, so that one round's writes overlap the next round's reads. The
+// state is stored transposed (S^T [dv][dk]); a thread owns entry r of rows c = cg, cg + NG, ...
+// of S^T: S^T[c][r] = e_0 S0^T[c][r] + sum_t (e_t k_t[r]) v_t[c], path order, with e_t k_t[r]
+// of the first 16 path tokens held in registers. Requests with accepted_len < 0 (failed) keep
+// their state.
 template <int D>
 __global__ __launch_bounds__(256) void rec_commit_kernel(
     float *__restrict__ state, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     const float *__restrict__ log_gate, const int32_t *__restrict__ accepted_len,
     const int32_t *__restrict__ accepted_path, int K, int H) {
     constexpr int NG = 256 / D;
-    constexpr int RT = D / NG / 2;       // rows per thread (each workgroup takes half the rows)
-    constexpr int VR = 16;               // path tokens whose values sit in registers
+    constexpr int RT = D / NG / 2;       // rows of S^T per thread (each workgroup takes half)
+    constexpr int VR = 16;               // path tokens whose keys sit in registers
     __shared__ __attribute__((aligned(16))) bf16 kb[kRecMaxK * D];   // k_t, path order
     __shared__ __attribute__((aligned(16))) bf16 vb[kRecMaxK * D];   // v_t, path order
     __shared__ float e_s[kRecMaxK + 1];
@@ -35,12 +36,12 @@ __global__ __launch_bounds__(256) void rec_commit_kernel(
     const int t = threadIdx.x;
     const int a = accepted_len[b];
     if (a < 0) return;                   // uniform: a failed request keeps its state
-    // this thread's rows of column c, in flight while the path is set up
-    const int c = t % D, rg = (D / 2) * half + t / D;
+    // this thread's entries of its rows, in flight while the path is set up
+    const int r = t % D, cg = (D / 2) * half + t / D;   // cg is wave-uniform
     float *S = state + ((int64_t)b * H + h) * D * D;
     float sv[RT];
 #pragma unroll
-    for (int u = 0; u < RT; ++u) sv[u] = S[(int64_t)(rg + NG * u) * D + c];
+    for (int u = 0; u < RT; ++u) sv[u] = S[(int64_t)(cg + NG * u) * D + r];
     const int n = a + 1 <= K ? a + 1 : K;
     if (t < 64) {
         const int p = t < n ? accepted_path[(int64_t)b * K + t] : 0;
@@ -82,22 +83,19 @@ __global__ __launch_bounds__(256) void rec_commit_kernel(
     }
     __syncthreads();
     const float e0 = e_s[n];
-    float vr[VR], er[VR];
+    float kr[VR];
 #pragma unroll
-    for (int tt = 0; tt < VR; ++tt) {
-        vr[tt] = tt < n ? to_f(vb[tt * D + c]) : 0.f;
-        er[tt] = tt < n ? e_s[tt] : 0.f;
-    }
+    for (int tt = 0; tt < VR; ++tt) kr[tt] = tt < n ? e_s[tt] * to_f(kb[tt * D + r]) : 0.f;
 #pragma unroll
     for (int u = 0; u < RT; ++u) {
-        const int r = rg + NG * u;
+        const int c = cg + NG * u;
         float x = e0 * sv[u];
 #pragma unroll
         for (int tt = 0; tt < VR; ++tt)
-            if (tt < n) x = __builtin_fmaf(er[tt] * to_f(kb[tt * D + r]), vr[tt], x);
+            if (tt < n) x = __builtin_fmaf(kr[tt], to_f(vb[tt * D + c]), x);
         for (int tt = VR; tt < n; ++tt)
             x = __builtin_fmaf(e_s[tt] * to_f(kb[tt * D + r]), to_f(vb[tt * D + c]), x);
-        S[(int64_t)r * D + c] = x;
+        S[(int64_t)c * D + r] = x;
     }
 }
 

@@ -35,7 +35,8 @@ __device__ __forceinline__ void split3(const float (&x)[8], bf16x8 &hi, bf16x8 &
 }
 
 // One workgroup (4 waves) per (request, head): wg = b * H + h. Rows of q, k, v are
-// [B][K][H][D] bf16; the state [B][H][D][D] fp32; out [B][K][H][D] fp32. On the matrix core
+// [B][K][H][D] bf16; the state is stored transposed, S^T [B][H][dv][dk] fp32 (element [c][r]
+// holds S[r][c]); out [B][K][H][D] fp32. On the matrix core
 // (v_mfma_f32_16x16x32_bf16; a lane's A fragment is row l % 16, columns 8 (l / 16) .. + 7 of a
 // 16 x 32 tile, its B fragment rows 8 (l / 16) .. + 7 of column l % 16, its result rows
 // 4 (l / 16) .. + 3 of column l % 16):
@@ -102,16 +103,20 @@ __global__ __launch_bounds__(256) void rec_tree_kernel(
             qf[it][rs] = i < K ? *reinterpret_cast<const bf16x8 *>(row_ptr(q, i) + 32 * rs + 8 * grp) : bf16x8{};
     }
 
-    // this wave's state fragments: column 16 ct + r16, rows 32 rs + 8 grp + e
-    const float *S0 = state + ((int64_t)b * H + h) * D * D;
+    // this wave's state fragments: column 16 ct + r16, rows 32 rs + 8 grp .. + 7, which the
+    // transposed layout keeps contiguous (two 16-byte loads per fragment)
+    const float *S0T = state + ((int64_t)b * H + h) * D * D;
     float sf[CPW][RS][8];
 #pragma unroll
     for (int u = 0; u < CPW; ++u)
 #pragma unroll
-        for (int rs = 0; rs < RS; ++rs)
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                sf[u][rs][e] = S0[(int64_t)(32 * rs + 8 * grp + e) * D + 16 * (wave * CPW + u) + r16];
+        for (int rs = 0; rs < RS; ++rs) {
+            const float *src = S0T + (int64_t)(16 * (wave * CPW + u) + r16) * D + 32 * rs + 8 * grp;
+            const float4 a = *reinterpret_cast<const float4 *>(src);
+            const float4 c4 = *reinterpret_cast<const float4 *>(src + 4);
+            sf[u][rs][0] = a.x; sf[u][rs][1] = a.y; sf[u][rs][2] = a.z; sf[u][rs][3] = a.w;
+            sf[u][rs][4] = c4.x; sf[u][rs][5] = c4.y; sf[u][rs][6] = c4.z; sf[u][rs][7] = c4.w;
+        }
 
     // ---- the tree: parent links, ancestor masks and path sums of log-gates (pointer jumping) --
     if (t < 64) {
