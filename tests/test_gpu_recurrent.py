@@ -192,3 +192,31 @@ def test_full_size_sampled_against_oracle():
         ref, _ = oracle.rec_tree(*sub, parents[b:b + 1])
         bound = _tree_bound(*sub, parents[b:b + 1], K, D)
         assert np.all(np.abs(o[b:b + 1, :, h:h + 1] - ref) <= bound), (b, h)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_commit_deep_chain_paths(D):
+    """Accepted paths longer than the 16 tokens the commit keeps in registers and LDS (41 and all
+    64 nodes of a chain): the deeper tokens come from memory and must give the same state."""
+    B, K, H = 2, 64, 2
+    print(f"rec commit deep chain D={D}", flush=True)
+    S0, q, k, v, g = _inputs(B, K, H, D, 77 + D)
+    acc = np.asarray([40, 63], np.int32)
+    path = np.tile(np.arange(K, dtype=np.int32), (B, 1))
+    hs = _host(S0, q, k, v, g)
+    state = _T(S0)
+    tv.spec_rec_commit(state, k, v, g, torch.from_numpy(acc).to(DEV), torch.from_numpy(path).to(DEV))
+    torch.cuda.synchronize()
+    got = state.transpose(-1, -2).cpu().numpy()
+    ref = oracle.rec_commit(hs[0], hs[2], hs[3], hs[4], acc, path)
+    kf, vf = (np.abs(oracle.from_bf16(x).astype(np.float64)) for x in (hs[2], hs[3]))
+    for b in range(B):
+        n = acc[b] + 1
+        for h in range(H):
+            gg = hs[4][b, :n, h].astype(np.float64)
+            suf = np.concatenate([np.cumsum(gg[::-1])[::-1][1:], [0.0]])
+            mag = np.exp(gg.sum()) * np.abs(hs[0][b, h].astype(np.float64))
+            for t in range(n):
+                mag += np.exp(suf[t]) * np.outer(kf[b, t, h], vf[b, t, h])
+            bound = (n + np.abs(np.cumsum(gg)).max() + 16) * U32 * mag
+            assert np.all(np.abs(got[b, h] - ref[b, h]) <= bound), (b, h)

@@ -14,7 +14,8 @@ namespace sv {
 // taking half the value columns, so that one round's writes overlap the next round's reads. The
 // state is stored transposed (S^T [dv][dk]); a thread owns entry r of rows c = cg, cg + NG, ...
 // of S^T: S^T[c][r] = e_0 S0^T[c][r] + sum_t (e_t k_t[r]) v_t[c], path order, with e_t k_t[r]
-// of the first 16 path tokens held in registers. Requests with accepted_len < 0 (failed) keep
+// of the first 16 path tokens held in registers and their rows staged in LDS (deeper tokens,
+// rare, are read from memory). Requests with accepted_len < 0 (failed) keep
 // their state.
 template <int D>
 __global__ __launch_bounds__(256) void rec_commit_kernel(
@@ -24,8 +25,8 @@ __global__ __launch_bounds__(256) void rec_commit_kernel(
     constexpr int NG = 256 / D;
     constexpr int RT = D / NG / 2;       // rows of S^T per thread (each workgroup takes half)
     constexpr int VR = 16;               // path tokens whose keys sit in registers
-    __shared__ __attribute__((aligned(16))) bf16 kb[kRecMaxK * D];   // k_t, path order
-    __shared__ __attribute__((aligned(16))) bf16 vb[kRecMaxK * D];   // v_t, path order
+    __shared__ __attribute__((aligned(16))) bf16 kb[VR * D];   // k_t of the first VR path tokens
+    __shared__ __attribute__((aligned(16))) bf16 vb[VR * D];   // v_t of the first VR path tokens
     __shared__ float e_s[kRecMaxK + 1];
     __shared__ float gp[kRecMaxK];        // log-gates of the path's nodes
     __shared__ int node[kRecMaxK];
@@ -62,12 +63,12 @@ __global__ __launch_bounds__(256) void rec_commit_kernel(
     }
     {
         constexpr int TPR = D / 8;
-        constexpr int NIT = 2 * kRecMaxK * TPR / 256;
+        constexpr int NIT = 2 * VR * TPR / 256;
         bf16x8 x[NIT];
 #pragma unroll
         for (int u = 0; u < NIT; ++u) {
             const int e = t + 256 * u;
-            const int which = e / (kRecMaxK * TPR), rem = e % (kRecMaxK * TPR);
+            const int which = e / (VR * TPR), rem = e % (VR * TPR);
             const int tt = rem / TPR, col = (rem % TPR) * 8;
             if (tt < n)
                 x[u] = *reinterpret_cast<const bf16x8 *>((which == 0 ? k : v) +
@@ -76,7 +77,7 @@ __global__ __launch_bounds__(256) void rec_commit_kernel(
 #pragma unroll
         for (int u = 0; u < NIT; ++u) {
             const int e = t + 256 * u;
-            const int which = e / (kRecMaxK * TPR), rem = e % (kRecMaxK * TPR);
+            const int which = e / (VR * TPR), rem = e % (VR * TPR);
             const int tt = rem / TPR, col = (rem % TPR) * 8;
             if (tt < n) *reinterpret_cast<bf16x8 *>(&(which == 0 ? kb : vb)[tt * D + col]) = x[u];
         }
@@ -93,8 +94,10 @@ __global__ __launch_bounds__(256) void rec_commit_kernel(
 #pragma unroll
         for (int tt = 0; tt < VR; ++tt)
             if (tt < n) x = __builtin_fmaf(kr[tt], to_f(vb[tt * D + c]), x);
-        for (int tt = VR; tt < n; ++tt)
-            x = __builtin_fmaf(e_s[tt] * to_f(kb[tt * D + r]), to_f(vb[tt * D + c]), x);
+        for (int tt = VR; tt < n; ++tt) {   // deeper paths (rare): rows straight from memory
+            const int64_t row = (((int64_t)b * K + node[tt]) * H + h) * D;
+            x = __builtin_fmaf(e_s[tt] * to_f(k[row + r]), to_f(v[row + c]), x);
+        }
         S[(int64_t)c * D + r] = x;
     }
 }
