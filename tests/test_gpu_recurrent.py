@@ -90,7 +90,8 @@ def _run_tree(state_t, q, k, v, g, parent):
 
 @pytest.mark.parametrize("B,K,H,D,tree", [(2, 64, 3, 128, True), (3, 16, 2, 64, False),
                                           (2, 33, 2, 128, True), (1, 1, 4, 64, False),
-                                          (2, 7, 5, 128, True), (1, 64, 2, 64, False)])
+                                          (2, 7, 5, 128, True), (1, 64, 2, 64, False),
+                                          (1, 17, 1, 128, True), (3, 48, 1, 64, True)])
 def test_tree_pass_matches_oracle(B, K, H, D, tree):
     print(f"rec tree B={B} K={K} H={H} D={D} tree={tree}", flush=True)
     S0, q, k, v, g = _inputs(B, K, H, D, K * 7 + D)
@@ -99,7 +100,10 @@ def test_tree_pass_matches_oracle(B, K, H, D, tree):
     if tree:
         parents = np.stack([synth.random_tree(K, 10, K, "rec", b) for b in range(B)]).astype(np.int32)
         pt = torch.from_numpy(parents).to(DEV)
-    o, st = _run_tree(_T(S0), q, k, v, g, pt)
+    state_t = _T(S0)
+    before = state_t.clone()
+    o, st = _run_tree(state_t, q, k, v, g, pt)
+    assert torch.equal(state_t.view(torch.int32), before.view(torch.int32))   # read only
     hs = _host(S0, q, k, v, g)
     ref, st_ref = oracle.rec_tree(*hs, parents)
     assert list(st) == list(st_ref) == [0] * B
