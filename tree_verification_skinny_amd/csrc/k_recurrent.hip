@@ -55,9 +55,13 @@ __global__ __launch_bounds__(256) void rec_tree_kernel(
     constexpr int CPW = D / 64;          // 16-column tiles per wave
     constexpr int WP = kRecMaxK + 4;     // padded LDS row of W (floats)
     constexpr int VP = kRecMaxK + 8;     // padded LDS row of V^T (bf16)
-    __shared__ __attribute__((aligned(16))) float wl[kRecMaxK * WP];
+    // key rows (bf16, padded) until the scores are done, then W (fp32, row pitch WP)
+    __shared__ __attribute__((aligned(16))) float kw[kRecMaxK * WP];
+    bf16 *ks = reinterpret_cast<bf16 *>(kw);
+    float *wl = kw;
+    static_assert(kRecMaxK * (D + 8) * 2 <= kRecMaxK * WP * 4, "key rows fit the W area");
     __shared__ __attribute__((aligned(16))) bf16 vt[D * VP];
-    __shared__ __attribute__((aligned(16))) bf16 ks[kRecMaxK * (D + 8)];   // key rows, padded
+    __shared__ __attribute__((aligned(16))) bf16 qs[kRecMaxK * (D + 8)];   // query rows, padded
     __shared__ double csum[kRecMaxK];
     __shared__ uint64_t anc[kRecMaxK];
     __shared__ int bad_s;
@@ -71,8 +75,8 @@ __global__ __launch_bounds__(256) void rec_tree_kernel(
     auto row_ptr = [&](const bf16 *base, int i) { return base + (((int64_t)b * K + i) * H + h) * D; };
 
     // Loads go out in the order they are needed (a wave waits for its loads in issue order):
-    // the tree's links and gates, the value and key rows (staged in LDS before the first
-    // barrier), the query fragments, the state fragments.
+    // the tree's links and gates, the value, key and query rows (staged in LDS before the first
+    // barrier), the state fragments.
     int p_in = lane - 1;
     float g_in = 0.f;
     if (t < 64 && lane < K) {
@@ -81,7 +85,7 @@ __global__ __launch_bounds__(256) void rec_tree_kernel(
     }
     constexpr int TPR = D / 8;
     constexpr int NIT = kRecMaxK * TPR / 256;
-    bf16x8 vx[NIT], kx[NIT];
+    bf16x8 vx[NIT], kx[NIT], qx[NIT];
 #pragma unroll
     for (int u = 0; u < NIT; ++u) {
         const int e = t + 256 * u, j = e / TPR, col = (e % TPR) * 8;
@@ -92,15 +96,10 @@ __global__ __launch_bounds__(256) void rec_tree_kernel(
         const int e = t + 256 * u, j = e / TPR, col = (e % TPR) * 8;
         kx[u] = j < K ? *reinterpret_cast<const bf16x8 *>(row_ptr(k, j) + col) : bf16x8{};
     }
-
-    // the query fragments of every node tile (rows past K are zero)
-    bf16x8 qf[4][RS];
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-        const int i = 16 * it + r16;
-#pragma unroll
-        for (int rs = 0; rs < RS; ++rs)
-            qf[it][rs] = i < K ? *reinterpret_cast<const bf16x8 *>(row_ptr(q, i) + 32 * rs + 8 * grp) : bf16x8{};
+    for (int u = 0; u < NIT; ++u) {
+        const int e = t + 256 * u, j = e / TPR, col = (e % TPR) * 8;
+        qx[u] = j < K ? *reinterpret_cast<const bf16x8 *>(row_ptr(q, j) + col) : bf16x8{};
     }
 
     // this wave's state fragments: column 16 ct + r16, rows 32 rs + 8 grp .. + 7, which the
@@ -149,14 +148,14 @@ __global__ __launch_bounds__(256) void rec_tree_kernel(
             }
         }
     }
-    // W starts at zero (pairs off the path, and key columns past the last node); V^T staged
-    for (int e = t; e < kRecMaxK * WP; e += 256) wl[e] = 0.f;
+    // V^T, key and query rows staged
 #pragma unroll
     for (int u = 0; u < NIT; ++u) {
         const int e = t + 256 * u, j = e / TPR, col = (e % TPR) * 8;
 #pragma unroll
         for (int z = 0; z < 8; ++z) vt[(col + z) * VP + j] = vx[u][z];
         *reinterpret_cast<bf16x8 *>(&ks[j * (D + 8) + col]) = kx[u];
+        *reinterpret_cast<bf16x8 *>(&qs[j * (D + 8) + col]) = qx[u];
     }
     __syncthreads();
     const bool bad = bad_s != 0;
@@ -167,24 +166,40 @@ __global__ __launch_bounds__(256) void rec_tree_kernel(
         return;
     }
 
+    // query fragment (node tile it, 32-wide step rs) from LDS; rows past K are zero
+    auto qfrag = [&](int it, int rs) __attribute__((always_inline)) {
+        return *reinterpret_cast<const bf16x8 *>(&qs[(16 * it + r16) * (D + 8) + 32 * rs + 8 * grp]);
+    };
+
     // ---- W: wave w scores node tile w against key tiles 0..w ---------------------------------
+    floatx4 sc[4];
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt) sc[jt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
-        if (it != wave || it >= NT) continue;   // wave-uniform; keeps qf statically indexed
+        if (it != wave || it >= NT) continue;   // wave-uniform: this wave's node tile only
+#pragma unroll
         for (int jt = 0; jt <= it; ++jt) {
             const int j = 16 * jt + r16;
-            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int rs = 0; rs < RS; ++rs)
-                acc = mfma16x16x32(qf[it][rs], *reinterpret_cast<const bf16x8 *>(&ks[j * (D + 8) + 32 * rs + 8 * grp]), acc);
-            if (j < K) {
-                const double cj = csum[j];
+                sc[jt] = mfma16x16x32(qfrag(it, rs), *reinterpret_cast<const bf16x8 *>(&ks[j * (D + 8) + 32 * rs + 8 * grp]), sc[jt]);
+        }
+    }
+    __syncthreads();                     // every wave is done with the key rows
+    // W rows of this wave's node tile, all 64 key columns (zero off the path and past the tile)
+    if (wave < NT) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int i = 16 * it + 4 * grp + e;
-                    if (i < K && ((anc[i] >> j) & 1ull))
-                        wl[i * WP + j] = expf((float)(csum[i] - cj)) * acc[e];
-                }
+        for (int jt = 0; jt < 4; ++jt) {
+            const int j = 16 * jt + r16;
+            const double cj = j < K ? csum[j] : 0.0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 16 * wave + 4 * grp + e;
+                float wv = 0.f;
+                if (jt <= wave && i < K && j < K && ((anc[i] >> j) & 1ull))
+                    wv = expf((float)(csum[i] - cj)) * sc[jt][e];
+                wl[i * WP + j] = wv;
             }
         }
     }
@@ -205,9 +220,10 @@ __global__ __launch_bounds__(256) void rec_tree_kernel(
 #pragma unroll
             for (int it = 0; it < 4; ++it) {
                 if (it < NT) {
-                    o[u][it] = mfma16x16x32(qf[it][rs], hi, o[u][it]);
-                    o[u][it] = mfma16x16x32(qf[it][rs], mid, o[u][it]);
-                    o[u][it] = mfma16x16x32(qf[it][rs], lo, o[u][it]);
+                    const bf16x8 qv = qfrag(it, rs);
+                    o[u][it] = mfma16x16x32(qv, hi, o[u][it]);
+                    o[u][it] = mfma16x16x32(qv, mid, o[u][it]);
+                    o[u][it] = mfma16x16x32(qv, lo, o[u][it]);
                 }
             }
         }
