@@ -56,9 +56,9 @@ PMC_TRAFFIC = {
                         "fetch_kib": 174761.283, "write_kib": 544.0,
                         "fetch_scale": 1.9999858, "write_scale": 1.0},
     ("rec", "bf16"): {"source": "tree_verification_skinny_amd/csrc/k_recurrent.hip",
-                      "sha256": "adf9f05b7c0927ca37ab5e8cdbfb40c189f2cd72fcc1dee54f4a5eb86255295d",
-                      "fetch_kib": 58650.084, "write_kib": 32768.139,
-                      "fetch_scale": 1.9999850, "write_scale": 1.0},
+                      "sha256": "77c29c1c50fbf0b85f3dc27d12e2235737ccb122353cf2ba1ac1edf1c22781a2",
+                      "fetch_kib": 58591.968, "write_kib": 32768.2,
+                      "fetch_scale": 1.9999851, "write_scale": 1.0},
     ("block", "w12"): {"source": "tree_verification_skinny_amd/csrc/k_gemm.hip",
                        "sha256": "f373f9dd17953c6758f365c0a86324030f6a99ed9c58cb5019dcae725401a84e",
                        "fetch_kib": 131470.243, "write_kib": 544.0,
