@@ -13,20 +13,21 @@ namespace sv {
 // The accepted node's state, in place: two workgroups (256 threads) per (request, head), each
 // taking half the value columns, so that one round's writes overlap the next round's reads. The
 // state is stored transposed (S^T [dv][dk]); a thread owns entry r of rows c = cg, cg + NG, ...
-// of S^T: S^T[c][r] = e_0 S0^T[c][r] + sum_t (e_t k_t[r]) v_t[c], path order, with e_t k_t[r]
-// of the first 16 path tokens held in registers and their rows staged in LDS (deeper tokens,
-// rare, are read from memory). Requests with accepted_len < 0 (failed) keep
+// of S^T: S^T[c][r] = e_0 S0^T[c][r] + sum_t (e_t k_t[r]) v_t[c], path order, with the rows of
+// the first 16 path tokens staged in LDS and e_t k_t[r] of the first 8 held in registers (deeper
+// tokens, rare, are read from memory). At most 64 registers: eight workgroups per compute unit. Requests with accepted_len < 0 (failed) keep
 // their state.
 template <int D>
-__global__ __launch_bounds__(256) void rec_commit_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void rec_commit_kernel(
     float *__restrict__ state, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     const float *__restrict__ log_gate, const int32_t *__restrict__ accepted_len,
     const int32_t *__restrict__ accepted_path, int K, int H) {
     constexpr int NG = 256 / D;
     constexpr int RT = D / NG / 2;       // rows of S^T per thread (each workgroup takes half)
-    constexpr int VR = 16;               // path tokens whose keys sit in registers
-    __shared__ __attribute__((aligned(16))) bf16 kb[VR * D];   // k_t of the first VR path tokens
-    __shared__ __attribute__((aligned(16))) bf16 vb[VR * D];   // v_t of the first VR path tokens
+    constexpr int VS = 16;               // path tokens whose rows are staged in LDS
+    constexpr int VR = 8;                // of those, tokens whose keys sit in registers
+    __shared__ __attribute__((aligned(16))) bf16 kb[VS * D];   // k_t of the first VS path tokens
+    __shared__ __attribute__((aligned(16))) bf16 vb[VS * D];   // v_t of the first VS path tokens
     __shared__ float e_s[kRecMaxK + 1];
     __shared__ float gp[kRecMaxK];        // log-gates of the path's nodes
     __shared__ int node[kRecMaxK];
@@ -63,12 +64,12 @@ __global__ __launch_bounds__(256) void rec_commit_kernel(
     }
     {
         constexpr int TPR = D / 8;
-        constexpr int NIT = 2 * VR * TPR / 256;
+        constexpr int NIT = 2 * VS * TPR / 256;
         bf16x8 x[NIT];
 #pragma unroll
         for (int u = 0; u < NIT; ++u) {
             const int e = t + 256 * u;
-            const int which = e / (VR * TPR), rem = e % (VR * TPR);
+            const int which = e / (VS * TPR), rem = e % (VS * TPR);
             const int tt = rem / TPR, col = (rem % TPR) * 8;
             if (tt < n)
                 x[u] = *reinterpret_cast<const bf16x8 *>((which == 0 ? k : v) +
@@ -77,7 +78,7 @@ __global__ __launch_bounds__(256) void rec_commit_kernel(
 #pragma unroll
         for (int u = 0; u < NIT; ++u) {
             const int e = t + 256 * u;
-            const int which = e / (VR * TPR), rem = e % (VR * TPR);
+            const int which = e / (VS * TPR), rem = e % (VS * TPR);
             const int tt = rem / TPR, col = (rem % TPR) * 8;
             if (tt < n) *reinterpret_cast<bf16x8 *>(&(which == 0 ? kb : vb)[tt * D + col]) = x[u];
         }
@@ -94,7 +95,9 @@ __global__ __launch_bounds__(256) void rec_commit_kernel(
 #pragma unroll
         for (int tt = 0; tt < VR; ++tt)
             if (tt < n) x = __builtin_fmaf(kr[tt], to_f(vb[tt * D + c]), x);
-        for (int tt = VR; tt < n; ++tt) {   // deeper paths (rare): rows straight from memory
+        for (int tt = VR; tt < n && tt < VS; ++tt)
+            x = __builtin_fmaf(e_s[tt] * to_f(kb[tt * D + r]), to_f(vb[tt * D + c]), x);
+        for (int tt = VS; tt < n; ++tt) {   // deeper paths (rare): rows straight from memory
             const int64_t row = (((int64_t)b * K + node[tt]) * H + h) * D;
             x = __builtin_fmaf(e_s[tt] * to_f(k[row + r]), to_f(v[row + c]), x);
         }
