@@ -11,12 +11,12 @@
 namespace sv {
 
 // The accepted node's state, in place: two workgroups (256 threads) per (request, head), each
-// taking half the value columns, so that one round's writes overlap the next round's reads. The
-// state is stored transposed (S^T [dv][dk]); a thread owns entry r of rows c = cg, cg + NG, ...
-// of S^T: S^T[c][r] = e_0 S0^T[c][r] + sum_t (e_t k_t[r]) v_t[c], path order, with the rows of
-// the first 16 path tokens staged in LDS and e_t k_t[r] of the first 8 held in registers (deeper
-// tokens, rare, are read from memory). At most 64 registers: eight workgroups per compute unit. Requests with accepted_len < 0 (failed) keep
-// their state.
+// taking half the value columns. The state is stored transposed (S^T [dv][dk]); a thread owns
+// entry r of rows c = cg, cg + NG, ... of S^T: S^T[c][r] = e_0 S0^T[c][r] + sum_t (e_t k_t[r])
+// v_t[c], path order, with the rows of the first 16 path tokens staged in LDS and e_t k_t[r] of
+// the first 8 held in registers (deeper tokens, rare, are read from memory). Held to 64
+// registers, eight workgroups fit a compute unit and the grid of a 32 x 32-head batch runs in
+// one round. Requests with accepted_len < 0 (failed) keep their state.
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void rec_commit_kernel(
     float *__restrict__ state, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
