@@ -400,16 +400,18 @@ def rec_bench(args, device):
         path[b, :len(p)] = p
     acc_t, path_t = torch.from_numpy(acc).to(device), torch.from_numpy(path).to(device)
     stream = torch.cuda.Stream()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * L)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 * L)]
 
     def step(events=False):
         for l, (S0, q, k, v, g) in enumerate(layers):
             if events:
-                ev[2 * l].record(stream)
+                ev[3 * l].record(stream)
             tv.spec_rec_tree_verify(S0, q, k, v, g, par, out, status)
             if events:
-                ev[2 * l + 1].record(stream)
+                ev[3 * l + 1].record(stream)
             tv.spec_rec_commit(S0, k, v, g, acc_t, path_t)
+            if events:
+                ev[3 * l + 2].record(stream)
 
     torch.cuda.synchronize()
     with torch.cuda.stream(stream):
@@ -417,12 +419,14 @@ def rec_bench(args, device):
         stream.synchronize()
         assert not status.cpu().numpy().any()
         # per-launch tree-pass time from events on this stream, eager steps
-        durs = []
+        durs, cdurs = [], []
         for _ in range(3):
             step(events=True)
             stream.synchronize()
-            durs.extend(ev[2 * l].elapsed_time(ev[2 * l + 1]) for l in range(L))
+            durs.extend(ev[3 * l].elapsed_time(ev[3 * l + 1]) for l in range(L))
+            cdurs.extend(ev[3 * l + 1].elapsed_time(ev[3 * l + 2]) for l in range(L))
         t_tree = float(np.mean(durs)) / 1e3
+        t_commit = float(np.mean(cdurs)) / 1e3
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph, stream=stream):
             step()
@@ -463,6 +467,9 @@ def rec_bench(args, device):
                      "traffic": pmc_traffic("rec"), "us_per_launch": round(t_tree * 1e6, 2),
                      "bytes_per_launch": int(tree_bytes),
                      "fp32_tflops": round(flops / t_tree / 1e12, 2)},
+        "commit_kernel": {"kernel": "rec_commit_kernel<128>", "us_per_launch": round(t_commit * 1e6, 2),
+                          "bytes_per_launch": int(commit_bytes),
+                          "achieved_gbps": round(commit_bytes / t_commit / 1e9, 1)},
     }
     log(f"rec: {ms:.3f} ms per step ({gbps:.0f} GB/s); tree pass {t_tree * 1e6:.1f} us "
         f"({ach:.0f} GB/s, {flops / t_tree / 1e12:.1f} TFLOP/s)")
