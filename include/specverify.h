@@ -155,11 +155,22 @@ int spec_verify(const spec_weights *weights, const spec_kv_cache *kv,
                 const spec_verify_extras *extras /* HOST, may be NULL */,
                 void *workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Commit the accepted path into the cache: for every layer, K and V, slot ctx_len + t receives
- * the row of slot ctx_len + accepted_path[t], t = 0..accepted_len (the moves are ordered so
- * that no source is overwritten before it is read); then ctx_len += accepted_len + 1, on the
- * device. Requests whose accepted_len is negative are left untouched. Takes the outputs of
- * spec_verify on the same stream; k and batch as given to it. */
+/* Commit the accepted path into the cache. Only the accepted root path becomes context: a draft
+ * token is kept only if it and every earlier token of its path equal the target's greedy
+ * choice [SpecPilot digest, airadar.tv — "Risks"], and a tree token's K/V row was computed for
+ * its own root path [JetSpec article, seventnews.com — "Technical architecture"]. For every
+ * layer, K and V, slot ctx_len + t receives the row of slot ctx_len + accepted_path[t],
+ * t = 0..accepted_len (every source is read before any slot is written); then
+ * ctx_len += accepted_len + 1, on the device.
+ * A request's commit is all or nothing. It applies only when 0 <= accepted_len < k,
+ * accepted_path[0] = 0 and t <= accepted_path[t] < k for t = 1..accepted_len (node ids are
+ * topological, so the node at depth t has id >= t), ctx_len >= 0, ctx_len + k fits
+ * max_pages_per_req pages, and the pages of positions ctx_len .. ctx_len + k - 1 are valid
+ * ids. Any other request (e.g. accepted_len = -1 from a failed verify) keeps its rows and its
+ * ctx_len. Device pointers: accepted_len [batch], accepted_path [batch][k], ctx_len [batch]
+ * (in/out). Takes the outputs of spec_verify on the same stream; k and batch as given to it.
+ * Host-side errors (NULL pointers, batch or k < 1, k > SPEC_MAX_K, a bad cfg) return before
+ * anything is enqueued. */
 int spec_commit_kv(const spec_model_cfg *cfg, const spec_kv_cache *kv,
                    const int32_t *accepted_len, const int32_t *accepted_path, int32_t *ctx_len,
                    int batch, int k, hipStream_t stream);

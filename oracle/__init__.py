@@ -486,7 +486,8 @@ def rec_tree(S0: np.ndarray, q: np.ndarray, k: np.ndarray, v: np.ndarray, g: np.
 
 def rec_commit(S0: np.ndarray, k: np.ndarray, v: np.ndarray, g: np.ndarray,
                accepted_len: np.ndarray, accepted_path: np.ndarray) -> np.ndarray:
-    """State [B][H][dk][dv] (float64) after the accepted root path (S0 where accepted_len < 0)."""
+    """State [B][H][dk][dv] (float64) after the accepted root path; S0 for a request with
+    accepted_len < 0 or >= K, or a path node id outside [0, K)."""
     B, H, dk, dv = S0.shape
     K = k.shape[1]
     S0 = _c(S0, np.float32)

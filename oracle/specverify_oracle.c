@@ -538,9 +538,11 @@ void orc_rec_tree(const float *S0, const uint16_t *q, const uint16_t *kk, const 
     }
 }
 
-/* The committed state after acceptance: for each request whose accepted_len a >= 0, the state
- * after the tokens path[b][0..a] (the accepted root path, the root first), from S0, into
- * S_out (float64, same layout as S0); requests with a < 0 keep S0. */
+/* The committed state after acceptance: for each request whose accepted_len a is in [0, K) and
+ * whose path entries path[b][0..a] are node ids in [0, K), the state after those tokens (the
+ * accepted root path, the root first), from S0, into S_out (float64, same layout as S0). Any
+ * other request (a < 0, a >= K, or a node id outside [0, K)) keeps S0: there is no accepted path
+ * of that request to apply. */
 void orc_rec_commit(const float *S0, const uint16_t *kk, const uint16_t *v, const float *g,
                     const int32_t *accepted_len, const int32_t *accepted_path, int B, int K, int H,
                     int dk, int dv, double *S_out) {
@@ -549,8 +551,12 @@ void orc_rec_commit(const float *S0, const uint16_t *kk, const uint16_t *v, cons
         for (int h = 0; h < H; ++h) {
             const int a = accepted_len[b];
             int *pth = malloc(sizeof(int) * K);
-            const int n = a < 0 ? 0 : a + 1;
-            for (int t = 0; t < n; ++t) pth[t] = accepted_path[(int64_t)b * K + t];
+            int n = (a < 0 || a >= K) ? 0 : a + 1;
+            for (int t = 0; t < n; ++t) {
+                const int id = accepted_path[(int64_t)b * K + t];
+                if (id < 0 || id >= K) { n = 0; break; }
+                pth[t] = id;
+            }
             rec_run(S0, kk, v, g, K, H, dk, dv, b, h, pth, n, S_out + ((int64_t)b * H + h) * dk * dv);
             free(pth);
         }

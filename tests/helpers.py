@@ -21,6 +21,11 @@ import tree_verification_skinny_amd as tv
 from tree_verification_skinny_amd import kvlayout
 
 ATOL, RTOL, NEAR_TIE = 2e-2, 1e-2, 1e-2
+# check_as_exact: how much farther from the oracle than the exact evaluation the GPU may be. A
+# correct fp32 evaluation in another summation order measures about 1.01x on a 27B-shape layer;
+# planted kernel mistakes (a dropped K step, wrong RoPE pairs or position, swapped kv heads, a 1 %
+# softmax scale error) measure 3x and more (tests/test_oracle_27b_criterion.py).
+EXACT_FACTOR = 1.25
 
 
 def bits(t: torch.Tensor) -> np.ndarray:
@@ -112,7 +117,7 @@ def check_logits(gpu: np.ndarray, orc: np.ndarray, what: str = "logits"):
     return float(err.max())
 
 
-def check_as_exact(gpu, orc, ref, what: str = "", factor: float = 2.0):
+def check_as_exact(gpu, orc, ref, what: str = "", factor: float = EXACT_FACTOR):
     """Parity where summation order alone exceeds the fixed tolerance (the 27B-class shape with
     random weights: an exact float64 evaluation of the same model and storage points already
     differs from the oracle by more than 2e-2 + 1e-2|x| in a few elements). The GPU must be as
@@ -136,7 +141,7 @@ def check_accept(r: oracle.VerifyResult, tokens, parent, gpu_greedy, gpu_a, gpu_
     """Returns True when the case was a logged near-tie (compared loosely), else False.
     `near_tie` is the top-2 margin below which a flipped greedy choice is a near-tie inversion;
     it is 1e-2 except where the exact evaluation itself moves logits by more (see
-    check_as_exact), where it is twice that movement."""
+    check_as_exact), where it is EXACT_FACTOR times that movement."""
     k = len(tokens)
     par = oracle.chain(k) if parent is None else np.asarray(parent, np.int32)
     firm = r.margin >= near_tie

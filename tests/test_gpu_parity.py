@@ -11,7 +11,7 @@ import tree_verification_skinny_amd as tv
 from tree_verification_skinny_amd import kvlayout
 
 import ref64
-from helpers import (bits, check_accept, check_as_exact, check_logits, device_weights, from_bits,
+from helpers import (EXACT_FACTOR, bits, check_accept, check_as_exact, check_logits, device_weights, from_bits,
                      make_kv, oracle_model_from, run_verify, tiny_case, upload_context)
 
 pytestmark = pytest.mark.gpu
@@ -350,7 +350,7 @@ def test_tiny_stream_attention_dominant_keys():
             ref, _ = ref64.decoder(w, synth.TINY, tokens[b], oracle.chain(k), kc, vc)
             ref = np.asarray(ref)
             print(check_as_exact(out.logits[b], r.logits, ref, f"request {b}"))
-            near_tie = max(1e-2, 2.0 * float(np.abs(ref - r.logits).max()))
+            near_tie = max(1e-2, EXACT_FACTOR * float(np.abs(ref - r.logits).max()))
             n_exact += 1
         check_accept(r, tokens[b], None, out.greedy[b], int(out.accepted_len[b]),
                      int(out.bonus[b]), out.path[b], near_tie=near_tie)
@@ -481,4 +481,4 @@ def test_27b_single_layer_parity():
     print(check_as_exact(out.logits[0], r.logits, ref_logits, "logits"))
     spread = float(np.abs(ref_logits - r.logits).max())
     check_accept(r, tokens, None, out.greedy[0], int(out.accepted_len[0]), int(out.bonus[0]),
-                 out.path[0], near_tie=max(1e-2, 2 * spread))
+                 out.path[0], near_tie=max(1e-2, EXACT_FACTOR * spread))

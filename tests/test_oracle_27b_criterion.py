@@ -1,0 +1,136 @@
+"""The 27B-shape parity criterion (check_as_exact) accepts correct fp32 arithmetic and rejects
+plausible kernel mistakes, shown on the CPU on one decoder layer at the 27B shape.
+
+At that shape the fixed tolerance (2e-2 + 1e-2|x|) is tighter than fp32 summation order alone
+allows, so the GPU is held to the distance an exact (float64) evaluation of the same storage
+points keeps from the oracle. That rule is only worth something if it still catches bugs. Here:
+  * a correct fp32 evaluation in another summation order (torch's own, through the independent
+    decoder of ref64) passes at the factor the GPU tests use;
+  * the oracle itself, run on inputs that reproduce a plausible kernel mistake exactly, fails:
+      - one 32-wide K step of the down projection dropped (a split-K remainder lost);
+      - RoPE pairs taken as interleaved (2j, 2j+1) instead of rotate-half (j, j + d/2);
+      - two kv heads exchanged (a wrong GQA head mapping for those query heads);
+      - the draft rows rotated one position too far (RoPE position off by one);
+      - attention scores scaled 1 % too high (a wrong softmax scale).
+The mistakes are planted on the CPU, in the inputs given to the oracle; the exact rotation
+identities used to build them are stated next to each.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+import ref64
+from helpers import bits, check_as_exact, oracle_cfg
+
+pytestmark = pytest.mark.slow
+
+SHAPE = synth.DENSE_27B.with_layers(1).with_vocab(1024)
+SEED, CTX, K = 31, 256, 16
+FACTOR = 1.25
+
+
+@pytest.fixture(scope="module")
+def layer_case():
+    w = synth.model_weights(SHAPE, SEED)
+    lw = {k: bits(v) for k, v in w["layers"][0].items()}
+    kx, vx = synth.kv_context(SHAPE, CTX, SEED, 0)
+    kc, vc = bits(kx), bits(vx)
+    tokens = synth.uniform_tokens(K, SHAPE.vocab, SEED, "tok")
+    x0 = bits(w["embed"][torch.from_numpy(tokens.astype(np.int64))])
+    par = oracle.chain(K)
+    cfg = oracle_cfg(SHAPE)
+    x_orc, _, _ = oracle.layer_forward(cfg, lw, kc, vc, par, x0)
+    x64, _, _ = ref64.layer(SHAPE, w["layers"][0], kc, vc, par, x0)
+    return dict(w=w, lw=lw, kc=kc, vc=vc, x0=x0, par=par, cfg=cfg,
+                orc=oracle.from_bf16(x_orc).astype(np.float64), exact=x64.numpy())
+
+
+def _oracle_out(c, lw=None, kc=None, vc=None):
+    x, _, _ = oracle.layer_forward(c["cfg"], c["lw"] if lw is None else lw,
+                                   c["kc"] if kc is None else kc, c["vc"] if vc is None else vc,
+                                   c["par"], c["x0"])
+    return oracle.from_bf16(x).astype(np.float64)
+
+
+def test_fp32_evaluation_in_another_order_passes(layer_case):
+    c = layer_case
+    x32, _, _ = ref64.layer(SHAPE, c["w"]["layers"][0], c["kc"], c["vc"], c["par"], c["x0"],
+                            dt=torch.float32)
+    print(check_as_exact(x32.double().numpy(), c["orc"], c["exact"], "fp32 torch order", FACTOR))
+
+
+def _rejects(c, got, what):
+    with pytest.raises(AssertionError) as e:
+        check_as_exact(got, c["orc"], c["exact"], what, FACTOR)
+    print(e.value)
+
+
+def test_dropped_down_k_step_is_rejected(layer_case):
+    c = layer_case
+    lw = dict(c["lw"])
+    wd = lw["w_down"].copy()
+    wd[:, 1024:1056] = 0           # the products of one 32-wide K step never added
+    lw["w_down"] = wd
+    _rejects(c, _oracle_out(c, lw=lw), "down projection without K step 32")
+
+
+def test_interleaved_rope_pairs_are_rejected(layer_case):
+    # Rotate-half on y = x[perm], perm = (0, 2, .., d-2, 1, 3, .., d-1), pairs y[j] with y[j + d/2],
+    # i.e. x[2j] with x[2j+1] at frequency j: interleaved RoPE, in permuted coordinates. With the
+    # q and k rows of w_qkv and the cached keys permuted the same way per head, every score equals
+    # the one an interleaved-RoPE kernel would compute on the original (rotate-half) cache.
+    c = layer_case
+    nq, nkv, d = SHAPE.n_q_heads, SHAPE.n_kv_heads, SHAPE.head_dim
+    perm = np.concatenate([np.arange(0, d, 2), np.arange(1, d, 2)])
+    lw = dict(c["lw"])
+    wq = lw["w_qkv"].copy()
+    for h in range(nq + nkv):                      # q heads, then k heads
+        wq[h * d:(h + 1) * d] = c["lw"]["w_qkv"][h * d + perm]
+    lw["w_qkv"] = wq
+    kc = c["kc"].reshape(CTX, nkv, d)[:, :, perm].copy()
+    _rejects(c, _oracle_out(c, lw=lw, kc=kc), "interleaved RoPE pairs")
+
+
+def test_exchanged_kv_heads_are_rejected(layer_case):
+    # kv heads 0 and 1 exchanged in the cache and in the k/v rows of w_qkv: the query heads of
+    # group 0 read head 1's keys and values and vice versa.
+    c = layer_case
+    nq, nkv, d = SHAPE.n_q_heads, SHAPE.n_kv_heads, SHAPE.head_dim
+    lw = dict(c["lw"])
+    wq = lw["w_qkv"].copy()
+    for base in (nq * d, (nq + nkv) * d):          # k rows, then v rows
+        wq[base:base + d], wq[base + d:base + 2 * d] = (c["lw"]["w_qkv"][base + d:base + 2 * d].copy(),
+                                                        c["lw"]["w_qkv"][base:base + d].copy())
+    lw["w_qkv"] = wq
+    kc = c["kc"].reshape(CTX, nkv, d)[:, [1, 0] + list(range(2, nkv))].copy()
+    vc = c["vc"].reshape(CTX, nkv, d)[:, [1, 0] + list(range(2, nkv))].copy()
+    _rejects(c, _oracle_out(c, lw=lw, kc=kc, vc=vc), "kv heads 0 and 1 exchanged")
+
+
+def test_rope_position_off_by_one_is_rejected(layer_case):
+    # Draft rows at position p + 1 instead of p: draft-draft scores keep their relative offset, and
+    # q(p + 1) . k(j) = q(p) . R(-1) k(j), so the same mistake is the oracle over cached keys
+    # rotated back by one position (rounded to bf16 again).
+    c = layer_case
+    nkv, d = SHAPE.n_kv_heads, SHAPE.head_dim
+    k = oracle.from_bf16(c["kc"]).reshape(CTX, nkv, d).astype(np.float64)
+    inv = SHAPE.rope_theta ** (-np.arange(0, d, 2, dtype=np.float64) / d)
+    cs, sn = np.cos(-inv), np.sin(-inv)
+    k1, k2 = k[..., : d // 2], k[..., d // 2:]
+    kr = np.concatenate([k1 * cs - k2 * sn, k2 * cs + k1 * sn], -1)
+    kc = oracle.to_bf16(kr.astype(np.float32))
+    _rejects(c, _oracle_out(c, kc=kc), "RoPE one position off")
+
+
+def test_softmax_scale_one_percent_high_is_rejected(layer_case):
+    # q scaled by 1.01 before RoPE (RoPE is linear): every score 1 % too large.
+    c = layer_case
+    nq, d = SHAPE.n_q_heads, SHAPE.head_dim
+    lw = dict(c["lw"])
+    wq = oracle.from_bf16(lw["w_qkv"]).copy()
+    wq[: nq * d] *= np.float32(1.01)
+    lw["w_qkv"] = oracle.to_bf16(wq)
+    _rejects(c, _oracle_out(c, lw=lw), "softmax scale x1.01")

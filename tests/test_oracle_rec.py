@@ -133,3 +133,25 @@ def test_malformed_tree_and_failed_commit():
     ref = np.exp(np.float64(g[1, 0, 0])) * S0[1, 0].astype(np.float64) + np.outer(
         oracle.from_bf16(k[1, 0, 0]).astype(np.float64), oracle.from_bf16(v[1, 0, 0]).astype(np.float64))
     np.testing.assert_allclose(S[1, 0], ref, rtol=1e-15, atol=1e-15)
+
+
+def test_commit_rejects_out_of_range_requests():
+    """A request with accepted_len >= K, or whose accepted path names a node outside [0, K),
+    has no accepted path to apply and keeps its committed state bit for bit; a valid request
+    beside them is committed as usual (the state after its path tokens, worked in float64)."""
+    B, K, H, dk, dv = 4, 5, 2, 4, 4
+    S0, q, k, v, g = _case(B, K, H, dk, dv, 21)
+    al = np.asarray([K, 2, 1, 0], np.int32)
+    ap = np.full((B, K), -1, np.int32)
+    ap[0] = [0, 1, 2, 3, 4]
+    ap[1, :3] = [0, 1, K]          # node id past the tree
+    ap[2, :2] = [0, -3]            # negative node id
+    ap[3, :1] = [0]
+    S = oracle.rec_commit(S0, k, v, g, al, ap)
+    for b in (0, 1, 2):
+        assert np.array_equal(S[b], S0[b].astype(np.float64)), b
+    for h in range(H):
+        ref = np.exp(np.float64(g[3, 0, h])) * S0[3, h].astype(np.float64) + np.outer(
+            oracle.from_bf16(k[3, 0, h]).astype(np.float64),
+            oracle.from_bf16(v[3, 0, h]).astype(np.float64))
+        np.testing.assert_allclose(S[3, h], ref, rtol=1e-15, atol=1e-15)

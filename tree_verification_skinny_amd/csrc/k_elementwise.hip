@@ -530,9 +530,36 @@ hipError_t argmax_accept(const float *amax_val, const int *amax_idx, int n_group
 }
 
 // ---- commit: slot ctx + t <- slot ctx + path[t], t = 0..a, every layer, K and V -------------
+// A request's commit is all or nothing, and both kernels below decide it by the same rule
+// (commit_part_ok, evaluated over all parts): 0 <= a < K; the path starts at the root
+// (path[0] = 0) and names a node at depth t or deeper in slot t (0 <= t <= a: t <= path[t] < K,
+// node ids being topological); ctx >= 0, ctx + K fits the request's page budget and every page
+// of positions ctx .. ctx + K - 1 is a valid page id. A request that fails keeps its rows and its
+// context.
+
+// Part i of the rule for request b: i = 0 checks a and ctx, i = 1..a+1 path entry i - 1 (i <= K),
+// i = K+1..K+5 the pages of the draft slots (K <= 64 positions span at most 5 pages).
+__device__ __forceinline__ bool commit_part_ok(int i, int a, int ctx, const int32_t *__restrict__ pr,
+                                               const int32_t *__restrict__ block_table, int max_pages,
+                                               int n_pages, int b, int K) {
+    if (a < 0 || a >= K || ctx < 0 || (int64_t)ctx + K > (int64_t)max_pages * 16) return false;
+    if (i >= 1 && i <= K) {
+        const int t = i - 1;
+        if (t > a) return true;
+        const int id = pr[t];
+        return t == 0 ? id == 0 : (id >= t && id < K);
+    }
+    if (i > K && i <= K + 5) {
+        const int p = (ctx >> 4) + (i - K - 1);
+        if (p * 16 >= ctx + K) return true;
+        const int id = page_of(block_table, max_pages, b, p * 16);
+        return id >= 0 && id < n_pages;
+    }
+    return true;
+}
+
 // One workgroup per (layer, request, kv head, K-or-V). All source rows are read into registers
-// before any is written, so overlapping moves are safe. path[t] is a node id at depth t, and
-// node ids are topological, so path[t] >= t.
+// before any is written, so overlapping moves are safe (path[t] >= t).
 __global__ __launch_bounds__(256) void commit_kv_kernel(
     const int32_t *__restrict__ accepted_len, const int32_t *__restrict__ path,
     const int32_t *__restrict__ ctx_len, const int32_t *__restrict__ block_table, int max_pages,
@@ -544,10 +571,11 @@ __global__ __launch_bounds__(256) void commit_kv_kernel(
     const int b = (id >> 1) / nkv % B;
     const int l = (id >> 1) / nkv / B;
     const int a = accepted_len[b];
-    if (a < 0 || a >= K) return;
     const int ctx = ctx_len[b];
-    if (ctx < 0 || (int64_t)ctx + K > (int64_t)max_pages * 16) return;
     const int32_t *pr = path + (int64_t)b * K;
+    const int part = threadIdx.x;     // 256 threads >= K + 6 parts
+    const bool ok = commit_part_ok(part, a, ctx, pr, block_table, max_pages, n_pages, b, K);
+    if (__syncthreads_and(ok) == 0) return;
     bf16 *pool = (kv == 0 ? k_pool : v_pool) + (int64_t)l * layer_stride;
     constexpr int kRegs = 64 * 128 / 256;
     bf16 vals[kRegs];
@@ -555,28 +583,18 @@ __global__ __launch_bounds__(256) void commit_kv_kernel(
     int r = 0;
     for (int e = threadIdx.x; e < n; e += 256, ++r) {
         const int t = e / D, d = e % D;
-        const int src = pr[t];
-        bf16 val = (bf16)0.0f;
-        if (src >= t && src < K) {
-            const int ps = ctx + src;
-            const int page = page_of(block_table, max_pages, b, ps);
-            if (page >= 0 && page < n_pages) {
-                const int64_t off = kv == 0 ? (((int64_t)page * nkv + g) * 16 + (ps & 15)) * D + d
-                                            : (((int64_t)page * nkv + g) * D + d) * 16 + (ps & 15);
-                val = pool[off];
-            }
-        }
-        vals[r] = val;
+        const int ps = ctx + pr[t];
+        const int page = page_of(block_table, max_pages, b, ps);
+        const int64_t off = kv == 0 ? (((int64_t)page * nkv + g) * 16 + (ps & 15)) * D + d
+                                    : (((int64_t)page * nkv + g) * D + d) * 16 + (ps & 15);
+        vals[r] = pool[off];
     }
     __syncthreads();
     r = 0;
     for (int e = threadIdx.x; e < n; e += 256, ++r) {
         const int t = e / D, d = e % D;
-        const int src = pr[t];
-        if (!(src >= t && src < K)) continue;
         const int pd = ctx + t;
         const int page = page_of(block_table, max_pages, b, pd);
-        if (page < 0 || page >= n_pages) continue;
         const int64_t off = kv == 0 ? (((int64_t)page * nkv + g) * 16 + (pd & 15)) * D + d
                                     : (((int64_t)page * nkv + g) * D + d) * 16 + (pd & 15);
         pool[off] = vals[r];
@@ -593,15 +611,27 @@ hipError_t commit_kv(const int32_t *accepted_len, const int32_t *path, const int
     return hipGetLastError();
 }
 
+// ctx += a + 1 for every request whose commit applies (the rule above, checked part by part by
+// one thread per request).
 __global__ void commit_ctx_kernel(const int32_t *__restrict__ accepted_len,
-                                  int32_t *__restrict__ ctx_len, int B) {
+                                  const int32_t *__restrict__ path,
+                                  const int32_t *__restrict__ block_table, int max_pages, int n_pages,
+                                  int K, int32_t *__restrict__ ctx_len, int B) {
     const int b = blockIdx.x * blockDim.x + threadIdx.x;
-    if (b < B && accepted_len[b] >= 0) ctx_len[b] += accepted_len[b] + 1;
+    if (b >= B) return;
+    const int a = accepted_len[b];
+    const int ctx = ctx_len[b];
+    const int32_t *pr = path + (int64_t)b * K;
+    bool ok = true;
+    for (int i = 0; i <= K + 5 && ok; ++i)
+        ok = commit_part_ok(i, a, ctx, pr, block_table, max_pages, n_pages, b, K);
+    if (ok) ctx_len[b] = ctx + a + 1;
 }
 
-hipError_t commit_ctx(const int32_t *accepted_len, int32_t *ctx_len, int B, hipStream_t st) {
+hipError_t commit_ctx(const int32_t *accepted_len, const int32_t *path, const int32_t *block_table,
+                      int max_pages, int n_pages, int K, int32_t *ctx_len, int B, hipStream_t st) {
     hipLaunchKernelGGL(commit_ctx_kernel, dim3((B + 255) / 256), dim3(256), 0, st, accepted_len,
-                       ctx_len, B);
+                       path, block_table, max_pages, n_pages, K, ctx_len, B);
     return hipGetLastError();
 }
 

@@ -125,7 +125,9 @@ hipError_t argmax_accept(const float *amax_val, const int *amax_idx, int n_group
 hipError_t commit_kv(const int32_t *accepted_len, const int32_t *path, const int32_t *ctx_len,
                      const int32_t *block_table, int max_pages, int n_pages, int L, int B, int K,
                      int nkv, int D, bf16 *k_pool, bf16 *v_pool, hipStream_t st);
-hipError_t commit_ctx(const int32_t *accepted_len, int32_t *ctx_len, int B, hipStream_t st);
+// ctx_len += accepted_len + 1 where commit_kv applies (the same all-or-nothing rule).
+hipError_t commit_ctx(const int32_t *accepted_len, const int32_t *path, const int32_t *block_table,
+                      int max_pages, int n_pages, int K, int32_t *ctx_len, int B, hipStream_t st);
 // Prompt prefill bookkeeping (k_prefill.hip).
 hipError_t prefill_init(int32_t *failed, int B, hipStream_t st);
 hipError_t prefill_gather(const int32_t *prompt, int p, int c0, int n, int B, int32_t *out, hipStream_t st);

@@ -313,7 +313,8 @@ int spec_commit_kv(const spec_model_cfg *cfg, const spec_kv_cache *kv, const int
     SV_TRY(commit_kv(accepted_len, accepted_path, ctx_len, kv->block_table, kv->max_pages_per_req,
                      kv->n_pages, cfg->n_layers, batch, k, cfg->n_kv_heads, cfg->head_dim,
                      static_cast<bf16 *>(kv->k_pool), static_cast<bf16 *>(kv->v_pool), stream));
-    SV_TRY(commit_ctx(accepted_len, ctx_len, batch, stream));
+    SV_TRY(commit_ctx(accepted_len, accepted_path, kv->block_table, kv->max_pages_per_req,
+                      kv->n_pages, k, ctx_len, batch, stream));
     return SPEC_OK;
 }
 
