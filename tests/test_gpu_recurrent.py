@@ -161,6 +161,30 @@ def test_commit_matches_oracle(B, K, H, D):
             assert np.all(np.abs(got[b, h] - ref[b, h]) <= bound), (b, h)
 
 
+def test_commit_rejects_invalid_paths():
+    """accepted_len >= k, or a path node id outside [0, k): no accepted path to apply, so the
+    state stays bit-identical (as the oracle says); a valid request beside them commits."""
+    B, K, H, D = 4, 16, 2, 128
+    print(f"rec commit invalid paths B={B} K={K} H={H} D={D}", flush=True)
+    S0, q, k, v, g = _inputs(B, K, H, D, 99)
+    acc = np.asarray([3, K, 2, -1], np.int32)
+    path = np.zeros((B, K), np.int32)
+    path[0, :4] = [0, 1, 2, 3]
+    path[1, :] = np.arange(K)
+    path[2, :3] = [0, 1, K + 5]
+    hs = _host(S0, q, k, v, g)
+    state = _T(S0)
+    tv.spec_rec_commit(state, k, v, g, torch.from_numpy(acc).to(DEV), torch.from_numpy(path).to(DEV))
+    torch.cuda.synchronize()
+    got = state.transpose(-1, -2).cpu().numpy()
+    ref = oracle.rec_commit(*hs[:1], *hs[2:], acc, path)
+    for b in (1, 2, 3):
+        assert np.array_equal(got[b], hs[0][b]), b
+        assert np.array_equal(ref[b], hs[0][b].astype(np.float64)), b
+    assert not np.array_equal(got[0], hs[0][0])
+    np.testing.assert_allclose(got[0], ref[0], rtol=1e-5, atol=1e-5)
+
+
 def test_commit_then_pass_equals_child_in_tree():
     """After committing root -> best, a one-token pass from the new state gives what the tree pass
     gave the same token placed under best (within both bounds)."""
