@@ -49,6 +49,7 @@ extern "C" {
 #define SPEC_EUNSUPPORTED (-2)  /* a shape this build does not implement (see spec_verify) */
 #define SPEC_EWORKSPACE (-3)    /* workspace smaller than the *_workspace_bytes answer */
 #define SPEC_EHIP (-4)          /* a HIP launch or runtime call failed */
+#define SPEC_ESCRATCH (-5)      /* larger than the fixed scratch of spec_accept_noalloc */
 
 #define SPEC_PAGE_SIZE 16       /* tokens per KV page */
 #define SPEC_MAX_K 64           /* draft nodes per request (one 64-bit ancestor mask per node) */
@@ -186,6 +187,24 @@ int spec_accept(const float *logits, const int32_t *draft_tokens, const int32_t 
                 int32_t *accepted_len, int32_t *bonus_token, int32_t *accepted_path,
                 int32_t *greedy /* [batch*k] or NULL */,
                 void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* spec_accept without a workspace argument and without any allocation, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc. Same inputs, outputs, kernels and results as spec_accept; its scratch (the
+ * per-node tree bookkeeping and the per-chunk greedy partials) is a static device array of the
+ * library, SPEC_NOALLOC_SCRATCH_BYTES per GPU, held until the process ends. Limits:
+ * batch * k <= SPEC_NOALLOC_MAX_ROWS and vocab <= SPEC_NOALLOC_MAX_VOCAB, else SPEC_ESCRATCH
+ * (returned before anything is enqueued). The current device must be the one `stream` belongs
+ * to. Every call on one GPU shares that GPU's scratch and nothing in it needs to start at zero;
+ * calls that overlap on one GPU (other streams, other threads) race and must be serialised by
+ * the caller. Other errors as for spec_accept. */
+#define SPEC_NOALLOC_MAX_ROWS 4096
+#define SPEC_NOALLOC_MAX_VOCAB 262144
+#define SPEC_NOALLOC_SCRATCH_BYTES ((size_t)4276224)
+int spec_accept_noalloc(const float *logits, const int32_t *draft_tokens,
+                        const int32_t *tree_parent, int batch, int k, int vocab,
+                        int32_t *accepted_len, int32_t *bonus_token, int32_t *accepted_path,
+                        int32_t *greedy /* [batch*k] or NULL */, hipStream_t stream);
 
 /* Convert one projection matrix from row-major w [n][kd] bf16 into the packed layout the
  * verify kernels stream (same size, n*kd*2 bytes, at `packed`, which must not overlap `w`).

@@ -245,3 +245,15 @@ def test_recurrent_entries_reject_bad_arguments():
     assert L.spec_rec_commit(*(c[:7] + (65,) + c[8:])) == tv.SPEC_EUNSUPPORTED
     assert L.spec_rec_commit(*(c[:9] + (32,) + c[10:])) == tv.SPEC_EUNSUPPORTED
     assert L.spec_rec_commit(*(c[:1] + (f + 2,) + c[2:])) == tv.SPEC_EINVAL
+
+
+def test_noalloc_accept_rejects_sizes_past_its_scratch_on_the_host():
+    """spec_accept_noalloc checks its limits before touching a device: SPEC_ESCRATCH for more
+    rows or a larger vocabulary than its static scratch holds, SPEC_EINVAL for empty shapes."""
+    L = tv.lib()
+    for batch, k, vocab, code in [(4097, 1, 1024, tv.SPEC_ESCRATCH), (65, 64, 1024, tv.SPEC_ESCRATCH),
+                                  (1, 1, tv.SPEC_NOALLOC_MAX_VOCAB + 1, tv.SPEC_ESCRATCH),
+                                  (0, 4, 1024, tv.SPEC_EINVAL), (1, 0, 1024, tv.SPEC_EINVAL)]:
+        rc = L.spec_accept_noalloc(None, None, None, batch, k, vocab, None, None, None, None, None)
+        assert rc == code, (batch, k, vocab, rc)
+    assert "scratch" in tv.spec_strerror(tv.SPEC_ESCRATCH)

@@ -31,6 +31,9 @@ SPEC_EINVAL = -1
 SPEC_EUNSUPPORTED = -2
 SPEC_EWORKSPACE = -3
 SPEC_EHIP = -4
+SPEC_ESCRATCH = -5
+SPEC_NOALLOC_MAX_ROWS = 4096
+SPEC_NOALLOC_MAX_VOCAB = 262144
 PAGE_SIZE = 16
 MAX_K = 64
 LAYER_KEYS = ("attn_norm", "w_qkv", "w_o", "mlp_norm", "w_gate_up", "w_down")
@@ -99,6 +102,7 @@ def lib() -> ctypes.CDLL:
                                      i32, i32, vp]
         L.spec_accept_workspace_bytes.argtypes = [i32, i32, i32, ctypes.POINTER(sz)]
         L.spec_accept.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
+        L.spec_accept_noalloc.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp, vp, vp, vp]
         L.spec_pack_weight.argtypes = [vp, i32, i32, vp, vp]
         L.spec_skinny_gemm_bytes.argtypes = [i32, i32, i32, ctypes.POINTER(sz)]
         L.spec_skinny_gemm.argtypes = [vp, i32, i32, vp, i32, vp, sz, ctypes.POINTER(i32), vp]
@@ -115,7 +119,7 @@ def lib() -> ctypes.CDLL:
         L.spec_rec_tree_verify.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp]
         L.spec_rec_commit.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, vp]
         for f in (L.spec_prefill_workspace_bytes, L.spec_prefill, L.spec_rec_tree_verify,
-                  L.spec_rec_commit):
+                  L.spec_rec_commit, L.spec_accept_noalloc):
             f.restype = i32
         for f in (L.spec_workspace_bytes, L.spec_verify, L.spec_commit_kv,
                   L.spec_accept_workspace_bytes, L.spec_accept, L.spec_skinny_gemm_bytes,
@@ -130,7 +134,7 @@ EXPORTED = ("spec_workspace_bytes", "spec_verify", "spec_commit_kv", "spec_accep
             "spec_accept", "spec_pack_weight", "spec_skinny_gemm_bytes", "spec_skinny_gemm",
             "spec_read_probe", "spec_w12_plan_ints", "spec_w12_plan", "spec_w12_pack",
             "spec_skinny_gemm_w12", "spec_prefill_workspace_bytes", "spec_prefill",
-            "spec_rec_tree_verify", "spec_rec_commit", "spec_strerror")
+            "spec_rec_tree_verify", "spec_rec_commit", "spec_accept_noalloc", "spec_strerror")
 
 
 def spec_strerror(code: int) -> str:
@@ -372,6 +376,18 @@ def spec_accept(logits: torch.Tensor, draft_tokens: torch.Tensor,
                            _ptr(accepted_len), _ptr(bonus_token), _ptr(accepted_path), _ptr(greedy),
                            _ptr(ws), ws.numel(), _stream(stream))
     _check(rc, "spec_accept")
+
+
+def spec_accept_noalloc(logits: torch.Tensor, draft_tokens: torch.Tensor,
+                        tree_parent: Optional[torch.Tensor], batch: int, k: int, vocab: int,
+                        accepted_len: torch.Tensor, bonus_token: torch.Tensor,
+                        accepted_path: torch.Tensor, greedy: Optional[torch.Tensor] = None,
+                        stream=None) -> None:
+    """spec_accept with the library's static per-GPU scratch instead of a workspace."""
+    rc = lib().spec_accept_noalloc(_ptr(logits), _ptr(draft_tokens), _ptr(tree_parent), batch, k,
+                                   vocab, _ptr(accepted_len), _ptr(bonus_token), _ptr(accepted_path),
+                                   _ptr(greedy), _stream(stream))
+    _check(rc, "spec_accept_noalloc")
 
 
 def spec_read_probe(buf: torch.Tensor, out: torch.Tensor, stream=None) -> None:

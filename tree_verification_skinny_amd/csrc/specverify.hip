@@ -4,6 +4,8 @@
 // the device, allocates, or keeps global state.
 #include <string.h>
 
+#include <mutex>
+
 #include "specverify.h"
 #include "kernels.hpp"
 
@@ -146,6 +148,7 @@ const char *spec_strerror(int code) {
         case SPEC_EUNSUPPORTED: return "unsupported shape";
         case SPEC_EWORKSPACE: return "workspace too small";
         case SPEC_EHIP: return "HIP runtime error";
+        case SPEC_ESCRATCH: return "larger than the fixed scratch of the no-allocation entry point";
         default: return "unknown error";
     }
 }
@@ -601,6 +604,58 @@ int spec_accept(const float *logits, const int32_t *draft_tokens, const int32_t 
     SV_TRY(argmax_accept(amv, ami, nc, draft_tokens, tree_parent, ni, batch, k, greedy, accepted_len,
                          bonus_token, accepted_path, stream));
     return SPEC_OK;
+}
+
+// ---- spec_accept without allocation: a static device scratch per GPU -----------------------------
+// Largest spec_accept workspace within the limits: depth, pos, status, anc for 4096 rows and the
+// greedy partials of 128 vocab chunks of 2048 (262144 / 2048) per row, each 256-byte aligned.
+static_assert(SPEC_NOALLOC_SCRATCH_BYTES ==
+                  4096 * 4 + 4096 * 4 + 4096 * 4 + 4096 * 8 + 128 * 4096 * 4 + 128 * 4096 * 4,
+              "scratch size = the spec_accept layout at the limits");
+
+}  // extern "C"
+
+namespace {
+// In host code this name is only a stand-in for the per-device copies; kernels get the address
+// hipGetSymbolAddress returns on each device.
+static __device__ __align__(256) unsigned char scratch[SPEC_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address, looked up once per device with that device current.
+int scratch_ptr(void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return SPEC_EHIP;
+    if (dev < 0 || dev >= kMaxDevices) return SPEC_EUNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return SPEC_EHIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return SPEC_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int spec_accept_noalloc(const float *logits, const int32_t *draft_tokens, const int32_t *tree_parent,
+                        int batch, int k, int vocab, int32_t *accepted_len, int32_t *bonus_token,
+                        int32_t *accepted_path, int32_t *greedy, hipStream_t stream) {
+    if (batch < 1 || k < 1 || vocab < 1) return SPEC_EINVAL;
+    if ((int64_t)batch * k > SPEC_NOALLOC_MAX_ROWS || vocab > SPEC_NOALLOC_MAX_VOCAB) return SPEC_ESCRATCH;
+    size_t need = 0;
+    int rc = spec_accept_workspace_bytes(batch, k, vocab, &need);
+    if (rc != SPEC_OK) return rc;
+    if (need > SPEC_NOALLOC_SCRATCH_BYTES) return SPEC_ESCRATCH;
+    void *ws = nullptr;
+    rc = scratch_ptr(&ws);
+    if (rc != SPEC_OK) return rc;
+    return spec_accept(logits, draft_tokens, tree_parent, batch, k, vocab, accepted_len, bonus_token,
+                       accepted_path, greedy, ws, SPEC_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 }  // extern "C"
