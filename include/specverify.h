@@ -126,8 +126,37 @@ typedef struct {
                                recorded on `stream` right before layer l's gate/up projection
                                kernel and events[2l+1] right after it, for per-launch timing
                                of the pass's largest kernel. Time eager calls: events captured
-                               into a HIP graph are not ordered against its kernels. */
+                               into a HIP graph are not ordered against its kernels. Used by the
+                               per-step path only. */
+    int path;               /* SPEC_PATH_AUTO (0): the library's choice (currently the per-step
+                               path); SPEC_PATH_STEPS: one kernel per step of each layer;
+                               SPEC_PATH_PERSISTENT: SPEC_EUNSUPPORTED where it does not apply. */
+    hipEvent_t *layer_events;   /* HOST array of 2 * ceil(n_layers / 16) events or NULL: recorded
+                               on `stream` right before and right after each launch of the
+                               persistent layers kernel (persistent path only; eager calls). */
+    uint64_t *phase_trace;  /* device, persistent path only, or NULL: uint64 [n_layers][G][18]
+                               with G = the device's compute units (at most 512), the
+                               s_memrealtime ticks (100 MHz) at which workgroup w reached each
+                               phase boundary of layer l: QKV wait begin, inputs ready, main loop
+                               end, done (0-3); attention items done (4); merges done (5); the same
+                               four for O (6-9), gate/up (10-13) and down (14-17). Entries of
+                               workgroups without work in a projection are left unwritten. */
 } spec_verify_extras;
+
+/* The two launch plans of spec_verify. Both compute the same pass with the same arithmetic;
+ * only the order of some fp32 sums differs.
+ *  - Per-step (SPEC_PATH_STEPS): every step of a layer (projection, split-K add with RoPE and
+ *    the K/V write, attention and its merge, residual add with RMSNorm) is its own kernel.
+ *  - Persistent (SPEC_PATH_PERSISTENT): for batch * k <= 16 rows (a block of up to 16 draft
+ *    tokens, or a few small blocks or trees), head_dim 64 or 128 and at most 8 query heads per kv
+ *    head, bf16 weights: one kernel per group of up to 16 layers, one workgroup per compute
+ *    unit, whose steps hand data to each other through memory inside the kernel. It needs the
+ *    whole GPU while it runs: if work on other streams holds compute units so that its
+ *    workgroups cannot all be resident, its bounded waits expire after about one second and
+ *    every request of the call is reported failed (accepted_len = bonus = -1). */
+#define SPEC_PATH_AUTO 0
+#define SPEC_PATH_STEPS 1
+#define SPEC_PATH_PERSISTENT 2
 
 /* Workspace bytes spec_verify needs for this shape, batch, k and cache page budget per request
  * (kv->max_pages_per_req of the calls it will serve). HOST out-pointer. */
@@ -282,7 +311,7 @@ int spec_skinny_gemm_w12(const void *x, int m, int kd, const spec_w12_matrix *w,
  * token after the last prompt token (the root of the first verify step) and sets
  * ctx_len += p on the device. A verify pass over a linear block computes exactly this for its
  * nodes (each node attends to the committed context and the nodes before it), so the prompt
- * runs through the verify kernels in chunks of up to SPEC_MAX_K positions, each chunk's K/V
+ * runs through the per-step verify kernels in chunks of up to SPEC_MAX_K positions, each chunk's K/V
  * committed before the next chunk's pass; the drafted-block view of the pages
  * [SpecPilot news piece, wireai.ir — "The main challenge"] with every block fully accepted.
  *   prompt [batch][p] int32; ctx_len [batch] in/out; next_token [batch] out (-1 for a request

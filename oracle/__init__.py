@@ -73,6 +73,7 @@ def lib():
             build(force=True)
         L = ctypes.CDLL(_LIB)
         L.orc_max_threads.restype = ctypes.c_int
+        L.orc_set_threads.argtypes = [ctypes.c_int]
         _u8p = ctypes.POINTER(ctypes.c_uint8)
         _i64p = ctypes.POINTER(ctypes.c_int64)
         L.orc_w12_base.argtypes = [_u16p, ctypes.c_int64]
@@ -123,6 +124,11 @@ def _p(a: Optional[np.ndarray], ptype):
 def threads() -> int:
     """OpenMP threads the oracle's loops use on this host."""
     return int(lib().orc_max_threads())
+
+
+def set_threads(n: int) -> None:
+    """Threads of the oracle's following parallel loops (for timing at one thread or all cores)."""
+    lib().orc_set_threads(int(n))
 
 
 # ---------------------------------------------------------------------------------------------

@@ -62,6 +62,9 @@ static uint16_t f32_to_bf16(float f) {
 /* Threads the OpenMP loops below use. */
 int orc_max_threads(void) { return omp_get_max_threads(); }
 
+/* Threads of the following parallel loops (timing at one thread and at all cores). */
+void orc_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
+
 void orc_f32_to_bf16(const float *in, uint16_t *out, int64_t n) {
     for (int64_t i = 0; i < n; ++i) out[i] = f32_to_bf16(in[i]);
 }

@@ -76,7 +76,7 @@ class VerifyOut:
 
 
 def run_verify(weights: tv.Weights, kv: tv.PagedKV, tokens: np.ndarray, parent, ctx_lens,
-               want_hidden=False, want_logits=True):
+               want_hidden=False, want_logits=True, path: str = "auto"):
     """tokens [B][K] int32; parent [B][K] or None. Returns numpy outputs."""
     dev = kv.k_pool.device
     B, K = tokens.shape
@@ -88,23 +88,23 @@ def run_verify(weights: tv.Weights, kv: tv.PagedKV, tokens: np.ndarray, parent, 
     t_ctx = torch.tensor(list(ctx_lens), dtype=torch.int32, device=dev)
     acc = torch.full((B,), -7, dtype=torch.int32, device=dev)
     bonus = torch.full((B,), -7, dtype=torch.int32, device=dev)
-    path = torch.full((B, K), -7, dtype=torch.int32, device=dev)
+    path_t = torch.full((B, K), -7, dtype=torch.int32, device=dev)
     greedy = torch.full((M,), -7, dtype=torch.int32, device=dev)
     logits = torch.full((M, cfg.vocab), float("nan"), device=dev) if want_logits else None
     hidden = (torch.empty((cfg.n_layers + 1, M, cfg.hidden), dtype=torch.bfloat16, device=dev)
               if want_hidden else None)
-    tv.spec_verify(weights, kv, t_tok, t_par, t_ctx, B, K, acc, bonus, path, ws, logits=logits,
-                   greedy=greedy, hidden=hidden)
+    tv.spec_verify(weights, kv, t_tok, t_par, t_ctx, B, K, acc, bonus, path_t, ws, logits=logits,
+                   greedy=greedy, hidden=hidden, path=path)
     torch.cuda.synchronize()
     o = VerifyOut()
     o.accepted_len = acc.cpu().numpy()
     o.bonus = bonus.cpu().numpy()
-    o.path = path.cpu().numpy()
+    o.path = path_t.cpu().numpy()
     o.greedy = greedy.cpu().numpy().reshape(B, K)
     o.logits = None if logits is None else logits.cpu().numpy().reshape(B, K, cfg.vocab)
     o.hidden = None if hidden is None else hidden
     o.ctx = t_ctx
-    o.acc_t, o.path_t = acc, path
+    o.acc_t, o.path_t = acc, path_t
     return o
 
 

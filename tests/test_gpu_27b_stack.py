@@ -37,7 +37,7 @@ def stack():
     torch.cuda.empty_cache()
 
 
-def _case(shape, w, kind):
+def _case(shape, w, kind, path="auto"):
     if kind == "block":
         k, ctx = 16, 4096
         parent = oracle.chain(k)
@@ -55,14 +55,17 @@ def _case(shape, w, kind):
     kv.v_pool.normal_(generator=g)
     ctx_rows = [kvlayout.read_rows(kv, l, 0, torch.arange(ctx)) for l in range(shape.n_layers)]
     out = run_verify(w, kv, tokens[None], None if kind == "block" else parent[None], [ctx],
-                     want_hidden=True)
+                     want_hidden=True, path=path)
     return k, ctx, parent, tokens, kv, ctx_rows, out
 
 
-@pytest.mark.parametrize("kind", ["block", "tree"])
-def test_27b_stack_teacher_forced(stack, kind):
+@pytest.mark.parametrize("kind,path", [("block", "persistent"), ("block", "steps"), ("tree", "auto")])
+def test_27b_stack_teacher_forced(stack, kind, path):
+    """The block runs both launch plans: the persistent kernel (the default at 16 rows) and one
+    kernel per step; the 64-node tree runs the per-step plan."""
     shape, w = stack
-    k, ctx, parent, tokens, kv, ctx_rows, out = _case(shape, w, kind)
+    print(f"27B stack {kind} path={path}", flush=True)
+    k, ctx, parent, tokens, kv, ctx_rows, out = _case(shape, w, kind, path)
     cfg = oracle_cfg(shape)
     for l in (0, 1, 31, 62, 63):
         lw = {nm: bits(t) for nm, t in w.rowmajor["layers"][l].items()}
@@ -143,7 +146,8 @@ def test_27b_stack_w12_bit_identical(stack):
                      w.rowmajor["layers"], w12=True)
     n_exc = sum(m.n_exc for lw in w12.w12["layers"] for m in lw.values()) + w12.w12["lm_head"].n_exc
     for kind in ("block", "tree"):
-        k, ctx, parent, tokens, kv, _, out = _case(shape, w, kind)
+        # W12 runs the per-step kernels with the bf16 plans: compare with the bf16 per-step pass
+        k, ctx, parent, tokens, kv, _, out = _case(shape, w, kind, "steps")
         k2, _, _, _, kv2, _, out2 = _case(shape, w12, kind)
         assert np.array_equal(out.logits.view(np.int32), out2.logits.view(np.int32)), kind
         assert torch.equal(out.hidden.view(torch.int16), out2.hidden.view(torch.int16)), kind

@@ -456,7 +456,9 @@ def test_repeat_runs_are_bit_identical():
 # one decoder layer at the 27B-class shape, context 4096, block of 16
 # ------------------------------------------------------------------------------------------
 
-def test_27b_single_layer_parity():
+@pytest.mark.parametrize("path", ["persistent", "steps"])
+def test_27b_single_layer_parity(path):
+    print(f"27B single layer, path {path}", flush=True)
     shape = synth.DENSE_27B.with_layers(1).with_vocab(8192)
     seed, ctx, k = 2024, 4096, 16
     w = synth.model_weights(shape, seed)
@@ -469,7 +471,7 @@ def test_27b_single_layer_parity():
     weights = device_weights(shape, w, DEV)
     kv = make_kv(shape, [ctx], k, seed, DEV)
     upload_context(kv, 0, kc, vc)
-    out = run_verify(weights, kv, tokens[None], None, [ctx], want_hidden=True)
+    out = run_verify(weights, kv, tokens[None], None, [ctx], want_hidden=True, path=path)
     # the draft rows' keys and values (QKV projection + RoPE) meet the fixed tolerance
     kg, vg = kvlayout.read_rows(kv, 0, 0, torch.arange(ctx, ctx + k))
     check_logits(kg.float().cpu().numpy(), oracle.from_bf16(r.k_new[0]), "k_new")

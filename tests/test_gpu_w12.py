@@ -3,8 +3,8 @@
 W12 is lossless, so a pass over W12 weights must give exactly what the same pass over the bf16
 weights gives: the packed layout is checked against the oracle's definition of the format, the
 projection kernel's partial sums against the bf16 kernel's bit for bit, and whole verify passes
-against both the bf16 GPU pass (bit for bit) and the CPU oracle (the usual tolerance and exact
-acceptance)."""
+against both the bf16 GPU pass with the same launch plan (one kernel per step, the plan W12 runs;
+bit for bit) and the CPU oracle (the usual tolerance and exact acceptance)."""
 import numpy as np
 import pytest
 import torch
@@ -173,7 +173,7 @@ def test_w12_tiny_block_equals_bf16_and_oracle():
         for fmt in (False, True):
             kv = make_kv(synth.TINY, [128], k, seed, DEV)
             upload_context(kv, 0, kc, vc)
-            outs.append(run_verify(tiny_weights(w, fmt), kv, tokens[None], None, [128]))
+            outs.append(run_verify(tiny_weights(w, fmt), kv, tokens[None], None, [128], path="steps"))
         b16, b12 = outs
         assert np.array_equal(b16.logits.view(np.int32), b12.logits.view(np.int32)), seed
         assert np.array_equal(b16.greedy, b12.greedy)
@@ -203,7 +203,7 @@ def test_w12_tiny_tree_equals_bf16_and_oracle(k):
         for fmt in (False, True):
             kv = make_kv(synth.TINY, [ctx], k, seed, DEV)
             upload_context(kv, 0, kc, vc)
-            outs.append(run_verify(tiny_weights(w, fmt), kv, tokens[None], parent[None], [ctx]))
+            outs.append(run_verify(tiny_weights(w, fmt), kv, tokens[None], parent[None], [ctx], path="steps"))
         b16, out = outs
         assert np.array_equal(b16.logits.view(np.int32), out.logits.view(np.int32)), seed
         assert np.array_equal(b16.path, out.path) and np.array_equal(b16.greedy, out.greedy)
@@ -220,7 +220,7 @@ def test_w12_root_only_pass_equals_bf16():
     for fmt in (False, True):
         kv = make_kv(synth.TINY, [128], 1, 5, DEV)
         upload_context(kv, 0, kc, vc)
-        outs.append(run_verify(tiny_weights(w, fmt), kv, tokens[None, :1], None, [128]))
+        outs.append(run_verify(tiny_weights(w, fmt), kv, tokens[None, :1], None, [128], path="steps"))
     assert np.array_equal(outs[0].logits.view(np.int32), outs[1].logits.view(np.int32))
     assert outs[0].accepted_len[0] == outs[1].accepted_len[0] == 0
     assert outs[0].bonus[0] == outs[1].bonus[0]

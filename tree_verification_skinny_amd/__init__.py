@@ -78,7 +78,12 @@ class KVCacheC(ctypes.Structure):
 
 class ExtrasC(ctypes.Structure):
     _fields_ = [("logits", ctypes.c_void_p), ("greedy", ctypes.c_void_p), ("hidden", ctypes.c_void_p),
-                ("gate_up_events", ctypes.c_void_p)]
+                ("gate_up_events", ctypes.c_void_p), ("path", ctypes.c_int),
+                ("layer_events", ctypes.c_void_p), ("phase_trace", ctypes.c_void_p)]
+
+
+SPEC_PATH_AUTO, SPEC_PATH_STEPS, SPEC_PATH_PERSISTENT = 0, 1, 2
+PATHS = {"auto": SPEC_PATH_AUTO, "steps": SPEC_PATH_STEPS, "persistent": SPEC_PATH_PERSISTENT}
 
 
 _lib = None
@@ -317,11 +322,16 @@ def spec_verify(weights: Weights, kv: PagedKV, draft_tokens: torch.Tensor,
                 accepted_len: torch.Tensor, bonus_token: torch.Tensor, accepted_path: torch.Tensor,
                 ws: torch.Tensor, logits: Optional[torch.Tensor] = None,
                 greedy: Optional[torch.Tensor] = None, hidden: Optional[torch.Tensor] = None,
-                gate_up_events=None, stream=None) -> None:
+                gate_up_events=None, stream=None, path: str = "auto", layer_events=None,
+                phase_trace: Optional[torch.Tensor] = None) -> None:
     """gate_up_events: optional ctypes array of 2 * n_layers hipEvent_t handles (e.g. the
-    cuda_event handles of torch timing events that have been recorded once)."""
+    cuda_event handles of torch timing events that have been recorded once), per-step path;
+    layer_events: the same, 2 * ceil(n_layers / 16) handles around the persistent launches.
+    path: "auto", "steps" or "persistent" (see SPEC_PATH_* in include/specverify.h);
+    phase_trace: int64 device tensor [n_layers][compute units][18] (persistent path)."""
     ev = None if gate_up_events is None else ctypes.cast(gate_up_events, ctypes.c_void_p)
-    extras = ExtrasC(_ptr(logits), _ptr(greedy), _ptr(hidden), ev)
+    lev = None if layer_events is None else ctypes.cast(layer_events, ctypes.c_void_p)
+    extras = ExtrasC(_ptr(logits), _ptr(greedy), _ptr(hidden), ev, PATHS[path], lev, _ptr(phase_trace))
     rc = lib().spec_verify(ctypes.byref(weights.c), ctypes.byref(kv.c), _ptr(draft_tokens),
                            _ptr(tree_parent), _ptr(ctx_len), batch, k, _ptr(accepted_len),
                            _ptr(bonus_token), _ptr(accepted_path), ctypes.byref(extras), _ptr(ws),

@@ -443,7 +443,7 @@ __global__ __launch_bounds__(1024) void argmax_accept_kernel(
     const int32_t *__restrict__ tokens, const int32_t *__restrict__ parent,
     const int32_t *__restrict__ depth, const int32_t *__restrict__ status, int M, int K,
     int32_t *__restrict__ greedy, int32_t *__restrict__ accepted_len, int32_t *__restrict__ bonus,
-    int32_t *__restrict__ path) {
+    int32_t *__restrict__ path, const uint32_t *__restrict__ err) {
     __shared__ float rv[1024];
     __shared__ int ri[1024];
     __shared__ int s_arg[64];
@@ -497,7 +497,7 @@ __global__ __launch_bounds__(1024) void argmax_accept_kernel(
     if (t != 0) return;
     int32_t *pr = path + (int64_t)b * K;
     for (int j = 0; j < K; ++j) pr[j] = -1;
-    if (status[b] != 0) {
+    if (status[b] != 0 || (err != nullptr && *err != 0u)) {
         accepted_len[b] = -1;
         bonus[b] = -1;
         return;
@@ -522,10 +522,10 @@ __global__ __launch_bounds__(1024) void argmax_accept_kernel(
 hipError_t argmax_accept(const float *amax_val, const int *amax_idx, int n_groups,
                          const int32_t *tokens, const int32_t *parent, const NodeInfo &ni, int B,
                          int K, int32_t *greedy, int32_t *accepted_len, int32_t *bonus,
-                         int32_t *path, hipStream_t st) {
+                         int32_t *path, hipStream_t st, const uint32_t *err) {
     hipLaunchKernelGGL(argmax_accept_kernel, dim3(B), dim3(1024), 0, st, amax_val, amax_idx, n_groups,
                        tokens, parent, ni.depth, ni.status, B * K, K, greedy, accepted_len, bonus,
-                       path);
+                       path, err);
     return hipGetLastError();
 }
 

@@ -118,10 +118,11 @@ hipError_t reduce_resid_norm(const float *P, int splits, int M, int H, const bf1
 hipError_t argmax_partials(const float *logits, int M, int V, float *amax_val, int *amax_idx,
                            int n_chunks, hipStream_t st);
 int argmax_chunks(int V);
+// err (device, may be NULL): when set, every request is reported failed.
 hipError_t argmax_accept(const float *amax_val, const int *amax_idx, int n_groups,
                          const int32_t *tokens, const int32_t *parent, const NodeInfo &ni, int B,
                          int K, int32_t *greedy, int32_t *accepted_len, int32_t *bonus,
-                         int32_t *path, hipStream_t st);
+                         int32_t *path, hipStream_t st, const uint32_t *err = nullptr);
 hipError_t commit_kv(const int32_t *accepted_len, const int32_t *path, const int32_t *ctx_len,
                      const int32_t *block_table, int max_pages, int n_pages, int L, int B, int K,
                      int nkv, int D, bf16 *k_pool, bf16 *v_pool, hipStream_t st);
@@ -144,6 +145,63 @@ hipError_t rec_tree(const float *state, const bf16 *q, const bf16 *k, const bf16
 hipError_t rec_commit(float *state, const bf16 *k, const bf16 *v, const float *log_gate,
                       const int32_t *accepted_len, const int32_t *accepted_path, int B, int K, int H,
                       int D, hipStream_t st);
+// ---- the persistent pass over the layers for at most 16 rows (k_fused.hip) ------------------------
+constexpr int kFusedMaxLayers = 16;    // layers per launch (their weights ride in the arguments)
+// Phase timestamps per (layer, workgroup): QKV wait begin, inputs ready, loop end, done (0-3),
+// attention items done (4), merges done (5), O (6-9), gate/up (10-13), down (14-17).
+constexpr int kFusedTraceEvents = 18;
+enum { FUSED_QKV = 0, FUSED_O = 1, FUSED_GU = 2, FUSED_DOWN = 3 };
+
+// One projection, split evenly over g_eff workgroups as ranges of (64-column group, 32-wide K
+// step) units; the same split every layer.
+struct FusedPhase {
+    int S;            // K steps
+    int groups;       // 64-column groups
+    int units;        // groups * S
+    int g_eff;        // workgroups with units: min(G, units)
+    int max_parts;    // most workgroups sharing a group
+    float *part;      // [groups][max_parts][1024] fp32 partial sums
+    uint32_t *cnt;    // [groups] arrivals (every layer adds the group's part count)
+    uint32_t *flag;   // [groups] epoch (global layer + 1) of the finished group
+};
+
+struct FusedArgs {
+    int L0, nl, Lt;                  // first layer and layer count of this launch; all layers
+    int H, nq, nkv, D, F, B, K, M;   // M = B * K <= 16
+    int G;                           // persistent workgroups (one per compute unit)
+    float eps, scale_log2;
+    const bf16 *w[kFusedMaxLayers][4];          // packed weights: qkv, o, gate/up, down
+    const bf16 *g_attn[kFusedMaxLayers], *g_mlp[kFusedMaxLayers], *g_final;
+    bf16 *k_pool, *v_pool;
+    int64_t layer_stride;
+    const int32_t *block_table;
+    int max_pages;
+    const int32_t *ctx_len, *status;
+    const uint64_t *anc;
+    const float2 *rope;
+    bf16 *x;                         // [16][H] fragment order, the residual stream
+    float *ssq_o, *ssq_d;            // [H/64][16] groups' sums of squares after O, after down
+    bf16 *q;                         // [M][nq][D]
+    bf16 *ao;                        // [16][nq*D] fragment order, the O projection's operand
+    bf16 *h;                         // [16][F] fragment order, the down projection's operand
+    bf16 *u_head;                    // [16][H] fragment order, the output head's operand
+    bf16 *trace;                     // optional [Lt + 1][M][H] residual stream
+    FusedPhase ph[4];
+    int CH, n_chunks, n_items, n_tasks;   // keys per attention item, chunks per request, items, merges
+    float *att_o;                    // [n_items][tiles][16][D]
+    uint64_t *att_ml;                // [n_items][tiles][16] (max, sum) pairs
+    uint32_t *f_att, *f_comb;        // epochs of the items and the merge tasks
+    uint32_t *err;                   // set when a wait timed out
+    uint64_t *trace_t;               // optional [Lt][G][kFusedTraceEvents] phase timestamps
+};
+// Workgroups of fused_layers that fit on one compute unit (0 when it cannot run).
+int fused_occupancy(int D);
+// Before the first launch: clears the sync words and the attention and SwiGLU operands, and
+// writes x (embedding rows, zero past M), its per-group sums of squares and the trace's first row.
+hipError_t fused_prep(const FusedArgs &a, const int32_t *tokens, const bf16 *embed, int vocab,
+                      uint32_t *sync_words, int n_sync, hipStream_t st);
+hipError_t fused_layers(const FusedArgs &a, hipStream_t st);
+
 // Reads bytes (a multiple of 16, 16-byte aligned) once as a grid-stride stream.
 hipError_t read_probe(const void *buf, int64_t bytes, uint32_t *out, hipStream_t st);
 

@@ -36,7 +36,71 @@ struct Plan {
     int attn_chunks;
     size_t o_depth, o_pos, o_status, o_anc, o_rope, o_x, o_u, o_q, o_attn, o_h, o_part, o_po,
         o_pml, o_amv, o_ami, total;
+    // the persistent path (rows <= 16): its own buffers, sized for up to kFusedSizeG workgroups
+    bool fused_shape;
+    size_t total_steps;     // the per-step plan's part of the workspace (the persistent one follows)
+    size_t f_x, f_ssq_o, f_ssq_d, f_q, f_ao, f_h, f_u, f_part[4], f_att_o, f_att_ml, f_sync;
 };
+
+// Workgroups the persistent path is sized for (one per compute unit; more units are left idle).
+constexpr int kFusedSizeG = 512;
+
+// Counts of the persistent path for G workgroups (see FusedPhase): per projection the split,
+// the largest group share and the most groups one workgroup touches; the attention items.
+struct FusedCounts {
+    int G;
+    int S[4], groups[4], units[4], g_eff[4], max_parts[4], max_seg[4];
+    int CH, n_chunks, n_items, tiles, n_tasks, n_sync;
+};
+
+int fused_wg_of(int64_t u, int g_eff, int units) { return (int)(((u + 1) * g_eff - 1) / units); }
+
+void fused_counts(const Plan &p, int G, int max_pages, FusedCounts &f) {
+    f.G = G;
+    const int N[4] = {p.nqkv, p.H, 2 * p.F, p.H};
+    const int Kd[4] = {p.H, p.qd, p.H, p.F};
+    for (int ph = 0; ph < 4; ++ph) {
+        f.S[ph] = Kd[ph] / 32;
+        f.groups[ph] = N[ph] / 64;
+        f.units[ph] = f.S[ph] * f.groups[ph];
+        f.g_eff[ph] = G < f.units[ph] ? G : f.units[ph];
+        int mp = 1, ms = 1;
+        for (int g = 0; g < f.groups[ph]; ++g) {
+            const int a = fused_wg_of((int64_t)g * f.S[ph], f.g_eff[ph], f.units[ph]);
+            const int b = fused_wg_of((int64_t)(g + 1) * f.S[ph] - 1, f.g_eff[ph], f.units[ph]);
+            if (b - a + 1 > mp) mp = b - a + 1;
+        }
+        for (int w = 0; w < f.g_eff[ph]; ++w) {
+            const int u0 = (int)((int64_t)f.units[ph] * w / f.g_eff[ph]);
+            const int u1 = (int)((int64_t)f.units[ph] * (w + 1) / f.g_eff[ph]);
+            const int seg = (u1 - 1) / f.S[ph] - u0 / f.S[ph] + 1;
+            if (seg > ms) ms = seg;
+        }
+        f.max_parts[ph] = mp;
+        f.max_seg[ph] = ms;
+    }
+    // attention: about G / (B * n_kv) chunks per (request, kv head), whole 32-key steps, at most
+    // 192 keys (the LDS of one item); more items than workgroups run in turns
+    const int64_t max_keys = (int64_t)max_pages * SPEC_PAGE_SIZE;
+    int per = G / (p.B * p.nkv);
+    if (per < 1) per = 1;
+    int64_t ch = (max_keys + 32LL * per - 1) / (32LL * per) * 32;
+    if (ch > 192) ch = 192;
+    if (ch < 32) ch = 32;
+    f.CH = (int)ch;
+    f.n_chunks = (int)((max_keys + ch - 1) / ch);
+    f.n_items = p.B * p.nkv * f.n_chunks;
+    f.tiles = (p.nq / p.nkv * p.K + 15) / 16;
+    f.n_tasks = p.B * p.nkv * f.tiles * 4;
+    int nflag = f.n_items + f.n_tasks + 1;
+    for (int ph = 0; ph < 4; ++ph) nflag += 2 * f.groups[ph];
+    f.n_sync = nflag;
+}
+
+// The persistent path takes the shape (its device check comes at the call).
+bool fused_shape_ok(const Plan &p) {
+    return p.M <= 16 && (p.D == 64 || p.D == 128) && p.nq / p.nkv <= 8;
+}
 
 int check_cfg(const spec_model_cfg *c) {
     if (c == nullptr) return SPEC_EINVAL;
@@ -113,6 +177,24 @@ int make_plan(const spec_model_cfg *c, int B, int K, int max_pages, Plan &p) {
     p.o_pml = cv.take(sizeof(float2) * (size_t)B * p.nkv * p.attn_chunks * group * K);
     p.o_amv = cv.take(sizeof(float) * (size_t)amax_groups * M);
     p.o_ami = cv.take(sizeof(int32_t) * (size_t)amax_groups * M);
+    p.fused_shape = fused_shape_ok(p);
+    p.total_steps = cv.off;
+    if (p.fused_shape) {
+        FusedCounts f;
+        fused_counts(p, kFusedSizeG, max_pages, f);
+        p.f_x = cv.take(sizeof(uint16_t) * 16 * p.H);
+        p.f_ssq_o = cv.take(sizeof(float) * (p.H / 64) * 16);
+        p.f_ssq_d = cv.take(sizeof(float) * (p.H / 64) * 16);
+        p.f_q = cv.take(sizeof(uint16_t) * M * p.qd);
+        p.f_ao = cv.take(sizeof(uint16_t) * 16 * p.qd);
+        p.f_h = cv.take(sizeof(uint16_t) * 16 * p.F);
+        p.f_u = cv.take(sizeof(uint16_t) * 16 * p.H);
+        for (int ph = 0; ph < 4; ++ph)
+            p.f_part[ph] = cv.take(sizeof(float) * 1024 * (size_t)f.groups[ph] * f.max_parts[ph]);
+        p.f_att_o = cv.take(sizeof(float) * (size_t)f.n_items * f.tiles * 16 * p.D);
+        p.f_att_ml = cv.take(sizeof(uint64_t) * (size_t)f.n_items * f.tiles * 16);
+        p.f_sync = cv.take(sizeof(uint32_t) * (size_t)f.n_sync);
+    }
     p.total = cv.off;
     return SPEC_OK;
 }
@@ -195,8 +277,28 @@ int spec_verify(const spec_weights *w, const spec_kv_cache *kv, const int32_t *d
             return SPEC_EINVAL;
         }
     }
-    if (workspace_bytes < p.total) return SPEC_EWORKSPACE;
     if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0) return SPEC_EINVAL;
+
+    const int want = extras ? extras->path : SPEC_PATH_AUTO;
+    if (want != SPEC_PATH_AUTO && want != SPEC_PATH_STEPS && want != SPEC_PATH_PERSISTENT) return SPEC_EINVAL;
+    // the persistent path: the shape, bf16 weights, and a device whose compute units each hold one
+    // of its workgroups
+    FusedCounts fc;
+    bool fused = false;
+    if (want == SPEC_PATH_PERSISTENT && p.fused_shape && !w12 && !w12_lm) {
+        int dev = 0, ncu = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+            ncu >= 1 && fused_occupancy(p.D) >= 1) {
+            fused_counts(p, ncu < kFusedSizeG ? ncu : kFusedSizeG, kv->max_pages_per_req, fc);
+            fused = fc.max_seg[FUSED_QKV] <= 2 && fc.max_seg[FUSED_O] <= 2 && fc.max_seg[FUSED_GU] <= 4 &&
+                    fc.max_seg[FUSED_DOWN] <= 2;
+        }
+    }
+    if (want == SPEC_PATH_PERSISTENT && !fused) return SPEC_EUNSUPPORTED;
+    // spec_workspace_bytes covers both plans; a caller that forces the per-step plan may pass
+    // that plan's part alone
+    if (workspace_bytes < (want == SPEC_PATH_STEPS ? p.total_steps : p.total)) return SPEC_EWORKSPACE;
 
     float *logits = extras ? extras->logits : nullptr;
     int32_t *greedy = extras ? extras->greedy : nullptr;
@@ -226,6 +328,95 @@ int spec_verify(const spec_weights *w, const spec_kv_cache *kv, const int32_t *d
     SV_TRY(tree_prep(draft_tokens, tree_parent, ctx_len, kv->block_table, kv->max_pages_per_req,
                      kv->n_pages, p.B, p.K, p.V, ni, stream));
     SV_TRY(rope_table(ni, M, p.D, w->cfg.rope_theta, stream));
+    if (fused) {
+        FusedArgs fa = {};
+        fa.Lt = p.L;
+        fa.H = p.H;
+        fa.nq = p.nq;
+        fa.nkv = p.nkv;
+        fa.D = p.D;
+        fa.F = p.F;
+        fa.B = p.B;
+        fa.K = p.K;
+        fa.M = M;
+        fa.G = fc.G;
+        fa.eps = eps;
+        fa.scale_log2 = kLog2e / sqrtf((float)p.D);
+        fa.g_final = static_cast<const bf16 *>(w->final_norm);
+        fa.k_pool = static_cast<bf16 *>(kv->k_pool);
+        fa.v_pool = static_cast<bf16 *>(kv->v_pool);
+        fa.layer_stride = layer_stride;
+        fa.block_table = kv->block_table;
+        fa.max_pages = kv->max_pages_per_req;
+        fa.ctx_len = ctx_len;
+        fa.status = ni.status;
+        fa.anc = ni.anc;
+        fa.rope = ni.rope;
+        fa.x = at<bf16>(workspace, p.f_x);
+        fa.ssq_o = at<float>(workspace, p.f_ssq_o);
+        fa.ssq_d = at<float>(workspace, p.f_ssq_d);
+        fa.q = at<bf16>(workspace, p.f_q);
+        fa.ao = at<bf16>(workspace, p.f_ao);
+        fa.h = at<bf16>(workspace, p.f_h);
+        fa.u_head = at<bf16>(workspace, p.f_u);
+        fa.trace = trace;
+        uint32_t *sync = at<uint32_t>(workspace, p.f_sync);
+        uint32_t *sw = sync;
+        for (int ph = 0; ph < 4; ++ph) {
+            FusedPhase &q = fa.ph[ph];
+            q.S = fc.S[ph];
+            q.groups = fc.groups[ph];
+            q.units = fc.units[ph];
+            q.g_eff = fc.g_eff[ph];
+            q.max_parts = fc.max_parts[ph];
+            q.part = at<float>(workspace, p.f_part[ph]);
+            q.cnt = sw;
+            sw += q.groups;
+            q.flag = sw;
+            sw += q.groups;
+        }
+        fa.CH = fc.CH;
+        fa.n_chunks = fc.n_chunks;
+        fa.n_items = fc.n_items;
+        fa.n_tasks = fc.n_tasks;
+        fa.att_o = at<float>(workspace, p.f_att_o);
+        fa.att_ml = at<uint64_t>(workspace, p.f_att_ml);
+        fa.f_att = sw;
+        sw += fc.n_items;
+        fa.f_comb = sw;
+        sw += fc.n_tasks;
+        fa.err = sw;
+        fa.trace_t = extras ? extras->phase_trace : nullptr;
+        SV_TRY(fused_prep(fa, draft_tokens, static_cast<const bf16 *>(w->embed), p.V, sync, fc.n_sync, stream));
+        hipEvent_t *lev = extras ? extras->layer_events : nullptr;
+        for (int l0 = 0, launch = 0; l0 < p.L; l0 += kFusedMaxLayers, ++launch) {
+            fa.L0 = l0;
+            fa.nl = p.L - l0 < kFusedMaxLayers ? p.L - l0 : kFusedMaxLayers;
+            for (int li = 0; li < fa.nl; ++li) {
+                const spec_layer_weights &lw = w->layers[l0 + li];
+                fa.w[li][FUSED_QKV] = static_cast<const bf16 *>(lw.w_qkv);
+                fa.w[li][FUSED_O] = static_cast<const bf16 *>(lw.w_o);
+                fa.w[li][FUSED_GU] = static_cast<const bf16 *>(lw.w_gate_up);
+                fa.w[li][FUSED_DOWN] = static_cast<const bf16 *>(lw.w_down);
+                fa.g_attn[li] = static_cast<const bf16 *>(lw.attn_norm);
+                fa.g_mlp[li] = static_cast<const bf16 *>(lw.mlp_norm);
+            }
+            if (lev) SV_TRY(hipEventRecord(lev[2 * launch], stream));
+            SV_TRY(fused_layers(fa, stream));
+            if (lev) SV_TRY(hipEventRecord(lev[2 * launch + 1], stream));
+        }
+        GemmEpi ep = {};
+        ep.logits = logits;
+        ep.amax_val = amv;
+        ep.amax_idx = ami;
+        GemmIn in = {};
+        in.Xp = fa.u_head;
+        SV_TRY(gemm(p.g_lm, EPI_ARGMAX, in, static_cast<const bf16 *>(w->lm_head), ep, stream));
+        SV_TRY(argmax_accept(amv, ami, p.lm_groups, draft_tokens, tree_parent, ni, p.B, p.K, greedy,
+                             accepted_len, bonus_token, accepted_path, stream, fa.err));
+        return SPEC_OK;
+    }
+
     SV_TRY(embed_norm(draft_tokens, static_cast<const bf16 *>(w->embed),
                       static_cast<const bf16 *>(w->layers[0].attn_norm), M, p.H, p.V, eps, x, u, trace,
                       stream));
@@ -505,6 +696,7 @@ int spec_prefill(const spec_weights *weights, const spec_kv_cache *kv, const int
         const bool last = c0 + n == p;
         SV_TRY(prefill_gather(prompt, p, c0, n, batch, tokens, stream));
         spec_verify_extras ex = {};
+        ex.path = SPEC_PATH_STEPS;      // the workspace above is sized for that plan's 64-row chunks
         ex.greedy = greedy;
         ex.logits = last ? logits : nullptr;
         rc = spec_verify(weights, kv, tokens, nullptr, ctx_len, batch, n, acc, bonus, path, &ex,
