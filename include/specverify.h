@@ -134,13 +134,16 @@ typedef struct {
     hipEvent_t *layer_events;   /* HOST array of 2 * ceil(n_layers / 16) events or NULL: recorded
                                on `stream` right before and right after each launch of the
                                persistent layers kernel (persistent path only; eager calls). */
-    uint64_t *phase_trace;  /* device, persistent path only, or NULL: uint64 [n_layers][G][18]
+    uint64_t *phase_trace;  /* device, persistent path only, or NULL: uint64 [n_layers][G][24]
                                with G = the device's compute units (at most 512), the
                                s_memrealtime ticks (100 MHz) at which workgroup w reached each
                                phase boundary of layer l: QKV wait begin, inputs ready, main loop
                                end, done (0-3); attention items done (4); merges done (5); the same
-                               four for O (6-9), gate/up (10-13) and down (14-17). Entries of
-                               workgroups without work in a projection are left unwritten. */
+                               four for O (6-9), gate/up (10-13) and down (14-17); inside the
+                               workgroup's (last) attention item: inputs ready, keys and values
+                               staged, products done (18-20); inside its (last) merge task:
+                               inputs ready, output written (21-22); 23 unused. Entries of
+                               workgroups without that work are left unwritten. */
 } spec_verify_extras;
 
 /* The two launch plans of spec_verify. Both compute the same pass with the same arithmetic;

@@ -328,7 +328,7 @@ def spec_verify(weights: Weights, kv: PagedKV, draft_tokens: torch.Tensor,
     cuda_event handles of torch timing events that have been recorded once), per-step path;
     layer_events: the same, 2 * ceil(n_layers / 16) handles around the persistent launches.
     path: "auto", "steps" or "persistent" (see SPEC_PATH_* in include/specverify.h);
-    phase_trace: int64 device tensor [n_layers][compute units][18] (persistent path)."""
+    phase_trace: int64 device tensor [n_layers][compute units][24] (persistent path)."""
     ev = None if gate_up_events is None else ctypes.cast(gate_up_events, ctypes.c_void_p)
     lev = None if layer_events is None else ctypes.cast(layer_events, ctypes.c_void_p)
     extras = ExtrasC(_ptr(logits), _ptr(greedy), _ptr(hidden), ev, PATHS[path], lev, _ptr(phase_trace))

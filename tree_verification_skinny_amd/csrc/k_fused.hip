@@ -25,9 +25,17 @@
 //     task (one wave, device-scope loads), not by a grid barrier, and every wait is bounded:
 //     past one second it sets an error word, the workgroup leaves, and the pass reports every
 //     request failed.
-// Data one workgroup hands to another is written with device-scope (write-through) stores and
-// read with device-scope loads; a writer waits for its stores to complete before it publishes
-// the epoch or the arrival. Weights and committed KV rows are read with plain non-temporal loads.
+// Data one workgroup hands to another is written with device-scope (write-through) stores, and a
+// writer waits for its stores to complete before it publishes the epoch or the arrival. Small
+// hand-offs (flags, partial sums, sums of squares, the residual read by the finisher) are read
+// with device-scope loads. The large operands (the residual stream, q, the attention output, the
+// SwiGLU output, the draft K/V rows) are read with plain, cached loads, without a cache
+// invalidation per phase (measured far too slow: every wave's acquire invalidates its L2): each
+// has one slot per layer of the launch, written once in it, and every reader waits for all
+// writers of the lines it reads, so no cache can hold a line of it from before its write in this
+// launch; across launches the kernel boundary makes the earlier writes visible. The one slot read
+// both before and after its rewrite (the launch's input, rewritten by its last layer) is read with
+// device-scope loads after the rewrite. Weights and committed KV rows use non-temporal loads.
 //
 // Arithmetic is that of the per-step kernels (bf16 storage between steps, fp32 accumulation and
 // softmax, P as a bf16 high part plus a bf16 low part); only the order of the split-K sums and
@@ -40,7 +48,7 @@ namespace {
 
 constexpr int kFW = 8;                       // waves per persistent workgroup
 constexpr int kFT = kFW * 64;
-constexpr int kCHS = 192;                    // most keys per attention item
+constexpr int kCHS = 160;                    // most keys per attention item
 constexpr int kSC1 = 16;                     // buffer-instruction cache policy: device scope
 constexpr uint64_t kWaitTicks = 100000000ull;   // one second of s_memrealtime (100 MHz)
 
@@ -98,7 +106,7 @@ __device__ __forceinline__ void stores_done() {
 template <int D>
 struct Smem {
     union {
-        floatx4 red[kFW * 4 * 64];                          // the waves' accumulators (32 KB)
+        floatx4 red[4 * kFW * 4 * 64];                      // the waves' accumulators, 4 groups (128 KB)
         struct {
             bf16 ks[kCHS * (D + 8)];                         // keys of the item, rows padded
             bf16 vt[D * (kCHS + 8)];                         // values transposed
@@ -112,12 +120,14 @@ struct Smem {
     float ss[kFT];
     float rs[16];
     int flag;
+    int last[4];
 };
 
-// Epoch wait: every word of f[0..n) reaches `epoch`. Wave 0 polls; false on a timeout or when
-// another workgroup has already timed out (the caller leaves the kernel).
+// Epoch wait: every word of the ranges f_i[0..n_i) reaches `epoch`. Wave 0 polls; false on a
+// timeout or when another workgroup has already timed out (the caller leaves the kernel).
 template <int D>
-__device__ bool wait_all(const uint32_t *f, int n, uint32_t epoch, uint32_t *err, Smem<D> &sm) {
+__device__ bool wait_ranges(const uint32_t *f0, int n0, const uint32_t *f1, int n1, const uint32_t *f2,
+                            int n2, uint32_t epoch, uint32_t *err, Smem<D> &sm) {
     if (threadIdx.x < 64) {
         int ok = 1;
         const int lane = threadIdx.x;
@@ -126,12 +136,17 @@ __device__ bool wait_all(const uint32_t *f, int n, uint32_t epoch, uint32_t *err
             if (ld_dev32(err) != 0u) { ok = 0; break; }
             // every flag load of a round is issued before any is tested
             uint32_t mn = 0xffffffffu;
-            for (int i0 = 0; i0 < n; i0 += 64 * 16) {
+            const uint32_t *fs[3] = {f0, f1, f2};
+            const int ns[3] = {n0, n1, n2};
 #pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    const int i = i0 + lane + 64 * j;
-                    const uint32_t v = i < n ? ld_dev32(f + i) : 0xffffffffu;
-                    mn = v < mn ? v : mn;
+            for (int r = 0; r < 3; ++r) {
+                for (int i0 = 0; i0 < ns[r]; i0 += 64 * 16) {
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) {
+                        const int i = i0 + lane + 64 * j;
+                        const uint32_t v = i < ns[r] ? ld_dev32(fs[r] + i) : 0xffffffffu;
+                        mn = v < mn ? v : mn;
+                    }
                 }
             }
             if (__all(mn >= epoch)) break;
@@ -149,6 +164,21 @@ __device__ bool wait_all(const uint32_t *f, int n, uint32_t epoch, uint32_t *err
     __syncthreads();
     return ok;
 }
+
+template <int D>
+__device__ __forceinline__ bool wait_all(const uint32_t *f, int n, uint32_t epoch, uint32_t *err, Smem<D> &sm) {
+    return wait_ranges<D>(f, n, nullptr, 0, nullptr, 0, epoch, err, sm);
+}
+
+// Per-layer operand slots of layer li of this launch.
+__device__ __forceinline__ bf16 *x_in(const FusedArgs &a, int li) {
+    return a.x_d + (int64_t)(li == 0 ? kFusedMaxLayers - 1 : li - 1) * 16 * a.H;
+}
+__device__ __forceinline__ bf16 *x_mid(const FusedArgs &a, int li) { return a.x_o + (int64_t)li * 16 * a.H; }
+__device__ __forceinline__ bf16 *x_out(const FusedArgs &a, int li) { return a.x_d + (int64_t)li * 16 * a.H; }
+__device__ __forceinline__ bf16 *q_of(const FusedArgs &a, int li) { return a.q + (int64_t)li * a.M * a.nq * a.D; }
+__device__ __forceinline__ bf16 *ao_of(const FusedArgs &a, int li) { return a.ao + (int64_t)li * 16 * a.nq * a.D; }
+__device__ __forceinline__ bf16 *h_of(const FusedArgs &a, int li) { return a.h + (int64_t)li * 16 * a.F; }
 
 // Phase trace (optional): s_memrealtime of event ev of workgroup blockIdx.x in layer l.
 __device__ __forceinline__ void stamp(const FusedArgs &a, int l, int ev) {
@@ -170,14 +200,14 @@ __device__ __forceinline__ int wg_of(int u, const FusedPhase &p) {
 }
 
 // 16-row weight tile of local tile t (0..3) of a 64-column group.
-template <int PH>
+template <int PH, int D>
 __device__ __forceinline__ int tile_of(int g, int t, const FusedArgs &a) {
     if constexpr (PH == FUSED_QKV) {
         // the rotation pairs (j, j + D/2) of a head in one group: its tiles 2a, 2a + 1 and the
         // two D/32 tiles further on
-        const int tph = a.D / 16, gph = a.D / 64;
+        constexpr int tph = D / 16, gph = D / 64;
         const int hd = g / gph, ha = g % gph;
-        return hd * tph + (t < 2 ? 2 * ha + t : 2 * ha + (t - 2) + a.D / 32);
+        return hd * tph + (t < 2 ? 2 * ha + t : 2 * ha + (t - 2) + D / 32);
     } else if constexpr (FUSED_GU == PH) {
         // gate columns 32g .. 32g + 31 and the matching up columns F + 32g ..
         return t < 2 ? 2 * g + t : a.F / 16 + 2 * g + (t - 2);
@@ -223,7 +253,7 @@ __device__ void epi_qkv(const FusedArgs &a, int li, int g, float y0, float y1, S
             }
             const int b = m / a.K, node = m % a.K;
             if (hd < a.nq) {
-                bf16 *qr = a.q + ((int64_t)m * a.nq + hd) * D;
+                bf16 *qr = q_of(a, li) + ((int64_t)m * a.nq + hd) * D;
                 st_dev32(qr + j, pack2bf(lo0, lo1));
                 st_dev32(qr + j + D / 2, pack2bf(hi0, hi1));
             } else if (a.status[b] == 0) {
@@ -247,9 +277,11 @@ __device__ void epi_qkv(const FusedArgs &a, int li, int g, float y0, float y1, S
     }
 }
 
-// x = bf16(x + bf16(y)) on the group's 64 columns, and the group's sum of squares per row.
+// x = bf16(x + bf16(y)) on the group's 64 columns, and the group's sum of squares per row; xo is
+// this thread's pair of x (requested by the caller ahead of the fix-up).
 template <int D>
-__device__ void epi_resid(const FusedArgs &a, int l, int g, bool down, float y0, float y1, Smem<D> &sm) {
+__device__ void epi_resid(const FusedArgs &a, int li, int l, int g, bool down, float y0, float y1, uint32_t xo,
+                          Smem<D> &sm) {
 #pragma clang fp contract(off)
     const int tau = threadIdx.x;
     const int t = tau >> 7, ln = (tau >> 1) & 63, jp = tau & 1;
@@ -257,12 +289,11 @@ __device__ void epi_resid(const FusedArgs &a, int l, int g, bool down, float y0,
     const int col = 64 * g + 16 * t + 4 * (ln >> 4) + 2 * jp;
     float x0 = 0.f, x1 = 0.f;
     if (m < a.M) {
-        bf16 *xp = a.x + frag_off(m, col, a.H);
-        const uint32_t xo = ld_dev32(xp);
+        const int64_t xo_off = frag_off(m, col, a.H);
         x0 = round_bf(bf_lo(xo) + round_bf(y0));
         x1 = round_bf(bf_hi(xo) + round_bf(y1));
         const uint32_t xn = pack2bf(x0, x1);
-        st_dev32(xp, xn);
+        st_dev32((down ? x_out(a, li) : x_mid(a, li)) + xo_off, xn);
         if (down && a.trace != nullptr)
             *reinterpret_cast<uint32_t *>(a.trace + ((int64_t)(l + 1) * a.M + m) * a.H + col) = xn;
     }
@@ -279,7 +310,7 @@ __device__ void epi_resid(const FusedArgs &a, int l, int g, bool down, float y0,
 
 // h = silu(bf16(gate)) * bf16(up) for the group's 32 columns.
 template <int D>
-__device__ void epi_swiglu(const FusedArgs &a, int g, float y0, float y1, Smem<D> &sm) {
+__device__ void epi_swiglu(const FusedArgs &a, int li, int g, float y0, float y1, Smem<D> &sm) {
 #pragma clang fp contract(off)
     const int tau = threadIdx.x;
     sm.y[2 * tau] = y0;
@@ -293,7 +324,7 @@ __device__ void epi_swiglu(const FusedArgs &a, int g, float y0, float y1, Smem<D
             const int col = 32 * g + 16 * t + 4 * (ln >> 4) + 2 * jp;
             const float g0 = round_bf(y0), g1 = round_bf(y1), u0 = round_bf(p0), u1 = round_bf(p1);
             const float h0 = (g0 / (1.0f + expf(-g0))) * u0, h1 = (g1 / (1.0f + expf(-g1))) * u1;
-            st_dev32(a.h + frag_off(m, col, a.F), pack2bf(h0, h1));
+            st_dev32(h_of(a, li) + frag_off(m, col, a.F), pack2bf(h0, h1));
         }
     }
 }
@@ -311,9 +342,66 @@ __device__ bool gemm_phase(const FusedArgs &a, int li, int l, Smem<D> &sm) {
     const int u1 = (int)((int64_t)p.units * (wg + 1) / p.g_eff);
     const int gA = u0 / S, gB = (u1 - 1) / S;
 
-    // inputs of this projection
     constexpr int ev0 = PH == FUSED_QKV ? 0 : (PH == FUSED_O ? 6 : (PH == FUSED_GU ? 10 : 14));
+    constexpr bool kNorm = PH == FUSED_QKV || PH == FUSED_GU;
     stamp(a, l, ev0);
+    floatx4 acc[MAXSEG][4];
+#pragma unroll
+    for (int s = 0; s < MAXSEG; ++s)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[s][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    // the wave's units are u0 + wave + 8 i: batches of two (units k and k + 8, k = wave + 16 j),
+    // two batches in flight while one is multiplied. Weights do not depend on the inputs: the
+    // first two batches' weights are requested before the wait for the inputs.
+    const bf16 *W = a.w[li][PH];
+    const int n = u1 - u0;
+    struct Batch {
+        bf16x8 w[2][4], x[2], g[2];
+        int slot[2], s[2];
+        bool live[2];
+    };
+    auto issue_w = [&](Batch &bt, int k, int g, int st) {
+#pragma unroll
+        for (int uu = 0; uu < 2; ++uu) {
+            bt.live[uu] = k + 8 * uu < n;
+            int gg = g, ss = st;
+            if (uu == 1) {
+                ss += 8;
+                while (ss >= S) { ss -= S; ++gg; }
+            }
+            bt.slot[uu] = gg - gA;
+            bt.s[uu] = ss;
+            if (!bt.live[uu]) continue;
+            const bf16 *wb = W + ((int64_t)ss * 64 + lane) * 8;
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                bt.w[uu][t] = stream_load((const bf16x8 *)(wb + (int64_t)tile_of<PH, D>(gg, t, a) * S * 512));
+        }
+    };
+    const bf16 *X = PH == FUSED_QKV ? x_in(a, li) : (PH == FUSED_GU ? x_mid(a, li) : (PH == FUSED_O ? ao_of(a, li) : h_of(a, li)));
+    const bf16 *gain = PH == FUSED_QKV ? a.g_attn[li] : a.g_mlp[li];
+    auto issue_x = [&](Batch &bt) {
+#pragma unroll
+        for (int uu = 0; uu < 2; ++uu) {
+            if (!bt.live[uu]) continue;
+            bt.x[uu] = *(const bf16x8 *)(X + (bt.s[uu] * 64 + lane) * 8);
+            if constexpr (kNorm) bt.g[uu] = *(const bf16x8 *)(gain + bt.s[uu] * 32 + 8 * (lane >> 4));
+        }
+    };
+    auto advance = [&](int &g, int &st) {
+        st += 16;
+        while (st >= S) { st -= S; ++g; }
+    };
+    Batch A, B;
+    int k = wave;
+    int gk = (u0 + wave) / S, sk = (u0 + wave) - gk * S;   // (group, step) of unit u0 + k
+    int gB_ = gk, sB_ = sk;
+    advance(gB_, sB_);                                    // ... of unit u0 + k + 16
+    if (k < n) issue_w(A, k, gk, sk);
+    if (k + 16 < n) issue_w(B, k + 16, gB_, sB_);
+
+    // inputs of this projection
     bool ok = true;
     if constexpr (PH == FUSED_QKV) {
         if (l > 0) ok = wait_all(a.ph[FUSED_DOWN].flag, a.ph[FUSED_DOWN].groups, (uint32_t)l, a.err, sm);
@@ -327,9 +415,6 @@ __device__ bool gemm_phase(const FusedArgs &a, int li, int l, Smem<D> &sm) {
     if (!ok) return false;
     stamp(a, l, ev0 + 1);
 
-    constexpr bool kNorm = PH == FUSED_QKV || PH == FUSED_GU;
-    const bf16 *X = PH == FUSED_QKV || PH == FUSED_GU ? a.x : (PH == FUSED_O ? a.ao : a.h);
-    const bf16 *gain = PH == FUSED_QKV ? a.g_attn[li] : a.g_mlp[li];
     float rs = 1.f;
     if constexpr (kNorm) {
         if (threadIdx.x < 16) {
@@ -341,95 +426,148 @@ __device__ bool gemm_phase(const FusedArgs &a, int li, int l, Smem<D> &sm) {
         __syncthreads();
         rs = sm.rs[lane & 15];
     }
-
-    floatx4 acc[MAXSEG][4];
-#pragma unroll
-    for (int s = 0; s < MAXSEG; ++s)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) acc[s][t] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-    const bf16 *W = a.w[li][PH];
-    const int n = u1 - u0;
-    for (int k = wave; k < n; k += 2 * kFW) {
-        bf16x8 wf[2][4], xf[2], gf[2];
-        int slot[2];
-        bool live[2];
+    auto consume = [&](const Batch &bt) {
 #pragma unroll
         for (int uu = 0; uu < 2; ++uu) {
-            const int kk = k + uu * kFW;
-            live[uu] = kk < n;
-            const int u = u0 + (live[uu] ? kk : k);
-            const int g = u / S, s = u - g * S;
-            slot[uu] = g - gA;
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-                wf[uu][t] = stream_load((const bf16x8 *)(W + (((int64_t)tile_of<PH>(g, t, a) * S + s) * 64 + lane) * 8));
-            xf[uu] = ld_dev16(X, (uint32_t)((s * 64 + lane) * 16));
-            if constexpr (kNorm) gf[uu] = *(const bf16x8 *)(gain + s * 32 + 8 * (lane >> 4));
-        }
-#pragma unroll
-        for (int uu = 0; uu < 2; ++uu) {
-            if (!live[uu]) continue;
-            bf16x8 b = xf[uu];
-            if constexpr (kNorm) b = norm_frag(b, rs, gf[uu]);
+            if (!bt.live[uu]) continue;
+            bf16x8 b = bt.x[uu];
+            if constexpr (kNorm) b = norm_frag(b, rs, bt.g[uu]);
 #pragma unroll
             for (int sl = 0; sl < MAXSEG; ++sl)
-                if (slot[uu] == sl) {
+                if (bt.slot[uu] == sl) {
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) acc[sl][t] = mfma16x16x32(wf[uu][t], b, acc[sl][t]);
+                    for (int t = 0; t < 4; ++t) acc[sl][t] = mfma16x16x32(bt.w[uu][t], b, acc[sl][t]);
                 }
         }
+    };
+    if (k < n) {
+        issue_x(A);
+        if (k + 16 < n) issue_x(B);
+        // (g3, s3): unit of the next batch to request (k + 32)
+        int g3 = gB_, s3 = sB_;
+        advance(g3, s3);
+        // A, B hold batches k, k + 16 (as far as they exist); each consumed batch's registers
+        // take the batch two ahead
+#define SV_STAGE(X_)                                      \
+        consume(X_);                                      \
+        k += 16;                                          \
+        if (k >= n) break;                                \
+        if (k + 16 < n) {                                 \
+            issue_w(X_, k + 16, g3, s3);                  \
+            issue_x(X_);                                  \
+        }                                                 \
+        advance(g3, s3);
+        while (true) {
+            SV_STAGE(A)
+            SV_STAGE(B)
+        }
+#undef SV_STAGE
     }
 
     stamp(a, l, ev0 + 2);
+    // the groups this workgroup touched: every wave's sums into LDS, one barrier, each thread
+    // adds its element over the waves in wave order
     const int nseg = gB - gA + 1;
     const int tau = threadIdx.x;
+    // the residual's old values of this thread's pairs, requested before the fix-up's round trips
+    uint32_t xo_pre[MAXSEG];
 #pragma unroll
     for (int sl = 0; sl < MAXSEG; ++sl) {
-        if (sl >= nseg) break;
-        const int g = gA + sl;
+        xo_pre[sl] = 0u;
+        if constexpr (PH == FUSED_O || PH == FUSED_DOWN) {
+            const int t = tau >> 7, ln = (tau >> 1) & 63, jp = tau & 1, m = ln & 15;
+            if (sl < nseg && m < a.M) {
+                const bf16 *xs = PH == FUSED_DOWN ? x_mid(a, li) : x_in(a, li);
+                xo_pre[sl] = ld_dev32(xs + frag_off(m, 64 * (gA + sl) + 16 * t + 4 * (ln >> 4) + 2 * jp, a.H));
+            }
+        }
+    }
 #pragma unroll
-        for (int t = 0; t < 4; ++t) sm.u.red[(wave * 4 + t) * 64 + lane] = acc[sl][t];
-        __syncthreads();
+    for (int sl = 0; sl < MAXSEG; ++sl)
+        if (sl < nseg) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) sm.u.red[((sl * kFW + wave) * 4 + t) * 64 + lane] = acc[sl][t];
+        }
+    __syncthreads();
+    float y0[MAXSEG], y1[MAXSEG];
+    {
         const int t = tau >> 7, ln = (tau >> 1) & 63, jp = tau & 1;
-        float y0 = 0.f, y1 = 0.f;
 #pragma unroll
-        for (int w = 0; w < kFW; ++w) {
-            const floatx4 v = sm.u.red[(w * 4 + t) * 64 + ln];
-            y0 += jp ? v[2] : v[0];
-            y1 += jp ? v[3] : v[1];
+        for (int sl = 0; sl < MAXSEG; ++sl) {
+            y0[sl] = 0.f;
+            y1[sl] = 0.f;
+            if (sl >= nseg) continue;
+#pragma unroll
+            for (int w = 0; w < kFW; ++w) {
+                const floatx4 v = sm.u.red[((sl * kFW + w) * 4 + t) * 64 + ln];
+                y0[sl] += jp ? v[2] : v[0];
+                y1[sl] += jp ? v[3] : v[1];
+            }
+        }
+    }
+    __syncthreads();
+    // groups shared with other workgroups: partial sums out, one completion wait, the arrivals;
+    // the last to arrive at a group finishes it
+    unsigned split = 0u, fin = 0u;
+    int np_[MAXSEG];
+#pragma unroll
+    for (int sl = 0; sl < MAXSEG; ++sl) {
+        np_[sl] = 1;
+        if (sl >= nseg) continue;
+        const int g = gA + sl;
+        if (u0 <= g * S && u1 >= (g + 1) * S) {
+            fin |= 1u << sl;
+            continue;
+        }
+        split |= 1u << sl;
+        const int wfst = wg_of(g * S, p), wlst = wg_of((g + 1) * S - 1, p);
+        np_[sl] = wlst - wfst + 1;
+        float *pp = p.part + ((int64_t)g * p.max_parts + (wg - wfst)) * 1024;
+        st_dev64(pp + 2 * tau, pack2f(y0[sl], y1[sl]));
+    }
+    if (split != 0u) {
+        stores_done();
+        __syncthreads();
+        if (tau < nseg && ((split >> tau) & 1u)) {
+            uint32_t target = 1u;
+#pragma unroll
+            for (int sl = 0; sl < MAXSEG; ++sl)
+                if (sl == tau) target = (uint32_t)np_[sl] * ep;
+            const uint32_t old = __hip_atomic_fetch_add(p.cnt + gA + tau, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            sm.last[tau] = old + 1 == target;
         }
         __syncthreads();
-        const bool whole = u0 <= g * S && u1 >= (g + 1) * S;
-        if (!whole) {
-            const int wfst = wg_of(g * S, p), wlst = wg_of((g + 1) * S - 1, p);
-            const int np = wlst - wfst + 1;
-            float *pp = p.part + ((int64_t)g * p.max_parts + (wg - wfst)) * 1024;
-            st_dev64(pp + 2 * tau, pack2f(y0, y1));
-            stores_done();
-            __syncthreads();
-            if (tau == 0) {
-                const uint32_t old = __hip_atomic_fetch_add(p.cnt + g, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                sm.flag = old + 1 == (uint32_t)np * ep;
-            }
-            __syncthreads();
-            const bool last = sm.flag != 0;
-            __syncthreads();
-            if (!last) continue;
-            y0 = 0.f;
-            y1 = 0.f;
-            const float *pb = p.part + (int64_t)g * p.max_parts * 1024 + 2 * tau;
-            for (int pi = 0; pi < np; ++pi) {
+#pragma unroll
+        for (int sl = 0; sl < MAXSEG; ++sl)
+            if (((split >> sl) & 1u) && sm.last[sl]) fin |= 1u << sl;
+        // every finishing group's parts, loads issued together, added in workgroup order
+#pragma unroll
+        for (int sl = 0; sl < MAXSEG; ++sl) {
+            if (!((split >> sl) & 1u) || !((fin >> sl) & 1u)) continue;
+            const float *pb = p.part + (int64_t)(gA + sl) * p.max_parts * 1024 + 2 * tau;
+            float a0 = 0.f, a1 = 0.f;
+            for (int pi = 0; pi < np_[sl]; ++pi) {
                 const uint64_t v = ld_dev64(pb + (int64_t)pi * 1024);
-                y0 += lo_f(v);
-                y1 += hi_f(v);
+                a0 += lo_f(v);
+                a1 += hi_f(v);
             }
+            y0[sl] = a0;
+            y1[sl] = a1;
         }
-        if constexpr (PH == FUSED_QKV) epi_qkv<D>(a, li, g, y0, y1, sm);
-        else if constexpr (PH == FUSED_GU) epi_swiglu<D>(a, g, y0, y1, sm);
-        else epi_resid<D>(a, l, g, PH == FUSED_DOWN, y0, y1, sm);
-        publish<D>(p.flag + g, ep);
+    }
+    // epilogues of the finished groups, one completion wait, their epochs
+#pragma unroll
+    for (int sl = 0; sl < MAXSEG; ++sl) {
+        if (!((fin >> sl) & 1u)) continue;
+        if constexpr (PH == FUSED_QKV) epi_qkv<D>(a, li, gA + sl, y0[sl], y1[sl], sm);
+        else if constexpr (PH == FUSED_GU) epi_swiglu<D>(a, li, gA + sl, y0[sl], y1[sl], sm);
+        else epi_resid<D>(a, li, l, gA + sl, PH == FUSED_DOWN, y0[sl], y1[sl], xo_pre[sl], sm);
         __syncthreads();
+    }
+    if (fin != 0u) {
+        stores_done();
+        __syncthreads();
+        if (tau < nseg && ((fin >> tau) & 1u)) st_dev32(p.flag + gA + tau, ep);
     }
     stamp(a, l, ev0 + 3);
     return true;
@@ -482,11 +620,40 @@ __device__ bool attn_item(const FusedArgs &a, int li, int l, int item, Smem<D> &
     // this layer's q of the group's heads and the draft K/V rows of head h
     {
         const int gph = D / 64;
-        bool ok = wait_all(a.ph[FUSED_QKV].flag + h * gq * gph, gq * gph, ep, a.err, sm);
-        ok = ok && wait_all(a.ph[FUSED_QKV].flag + (a.nq + h) * gph, gph, ep, a.err, sm);
-        ok = ok && wait_all(a.ph[FUSED_QKV].flag + (a.nq + a.nkv + h) * gph, gph, ep, a.err, sm);
-        if (!ok) return false;
+        const uint32_t *fq = a.ph[FUSED_QKV].flag;
+        if (!wait_ranges<D>(fq + h * gq * gph, gq * gph, fq + (a.nq + h) * gph, gph,
+                            fq + (a.nq + a.nkv + h) * gph, gph, ep, a.err, sm))
+            return false;
     }
+    stamp(a, li + a.L0, 18);
+    // tasks: (query tile t, key part kp), at most one per wave; tile columns rho = (q head of the
+    // group, node); a part covers whole 32-key steps of the valid ones. The task's query rows
+    // are requested first, ahead of the draft rows' keys and values.
+    const int R = gq * a.K;
+    const int T_ = (R + 15) >> 4;                 // <= 8 (at most 8 q heads per kv head)
+    const int KP = kFW / T_;
+    const int ntask = T_ * KP;
+    const int r16 = lane & 15, grp = lane >> 4;
+    const bool has = wave < ntask;
+    const int t = has ? wave % T_ : 0, kp = has ? wave / T_ : 0;
+    const int s_lo = kp * nst / KP, s_hi = (kp + 1) * nst / KP;
+    constexpr int MS = kCHS / 32;
+    const int rho = 16 * t + r16;
+    const bool col_ok = rho < R;
+    const int hh = col_ok ? rho / a.K : 0, node = col_ok ? rho % a.K : 0;
+    bf16x8 qf[D / 32];
+    uint64_t am = 0;
+    if (has) {
+        const int qrow = (b * a.K + node) * a.nq + h * gq + hh;
+#pragma unroll
+        for (int ds = 0; ds < D / 32; ++ds)
+            qf[ds] = *(const bf16x8 *)(q_of(a, li) + (int64_t)qrow * D + ds * 32 + grp * 8);
+        am = a.anc[b * a.K + node];
+    }
+    floatx4 o[D / 16];
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    float mloc = -INFINITY, psum = 0.f;
 #pragma unroll
     for (int i = 0; i < NPL; ++i) {
         const int q = tau + i * kFT;
@@ -494,7 +661,8 @@ __device__ bool attn_item(const FusedArgs &a, int li, int l, int item, Smem<D> &
         if (q < nslots && p < npages && kb + 16 * p + 16 > ctx) {
             const bool is_v = s4 >= 2 * D;
             const int page = bt[(kb >> 4) + p];
-            kv[i] = ld_dev16((is_v ? vpool : kpool) + ((int64_t)page * a.nkv + h) * 16 * D + (is_v ? s4 - 2 * D : s4) * 8, 0);
+            kv[i] = *(const bf16x8 *)((is_v ? vpool : kpool) + ((int64_t)page * a.nkv + h) * 16 * D +
+                                      (is_v ? s4 - 2 * D : s4) * 8);
         }
     }
     // into LDS: keys [key][D + 8]; values transposed [d][CHS + 8], slots past the valid keys zero
@@ -519,32 +687,9 @@ __device__ bool attn_item(const FusedArgs &a, int li, int l, int item, Smem<D> &
         }
     }
     __syncthreads();
+    stamp(a, li + a.L0, 19);
 
-    // tasks: (query tile t, key part kp), at most one per wave; tile columns rho = (q head of the
-    // group, node); a part covers whole 32-key steps of the valid ones
-    const int R = gq * a.K;
-    const int T_ = (R + 15) >> 4;                 // <= 8 (at most 8 q heads per kv head)
-    const int KP = kFW / T_;
-    const int ntask = T_ * KP;
-    const int r16 = lane & 15, grp = lane >> 4;
-    const bool has = wave < ntask;
-    const int t = has ? wave % T_ : 0, kp = has ? wave / T_ : 0;
-    const int s_lo = kp * nst / KP, s_hi = (kp + 1) * nst / KP;
-    constexpr int MS = kCHS / 32;
-    floatx4 o[D / 16];
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
-    float mloc = -INFINITY, psum = 0.f;
     if (has) {
-        const int rho = 16 * t + r16;
-        const bool col_ok = rho < R;
-        const int hh = col_ok ? rho / a.K : 0, node = col_ok ? rho % a.K : 0;
-        const int qrow = (b * a.K + node) * a.nq + h * gq + hh;
-        bf16x8 qf[D / 32];
-#pragma unroll
-        for (int ds = 0; ds < D / 32; ++ds)
-            qf[ds] = ld_dev16(a.q, (uint32_t)(((int64_t)qrow * D + ds * 32 + grp * 8) * 2));
-        const uint64_t am = a.anc[b * a.K + node];
         const int kr0 = 8 * (r16 >> 2) + (r16 & 3);
         const int nps = s_hi - s_lo;
         floatx4 s[MS][2];
@@ -613,6 +758,7 @@ __device__ bool attn_item(const FusedArgs &a, int li, int l, int item, Smem<D> &
             }
         }
     }
+    stamp(a, li + a.L0, 20);
     if (KP == 1) {
         if (has) {
             const int64_t base = ((int64_t)item * T_ + t) * 16 + r16;
@@ -661,7 +807,7 @@ __device__ bool attn_item(const FusedArgs &a, int li, int l, int item, Smem<D> &
 
 // ---- merge task: (kv head h, request b, tile t, quarter dq of the head's dims) ---------------------
 template <int D>
-__device__ bool combine_task(const FusedArgs &a, int l, int task, Smem<D> &sm) {
+__device__ bool combine_task(const FusedArgs &a, int li, int l, int task, Smem<D> &sm) {
 #pragma clang fp contract(off)
     const int dq = task & 3, rest = task >> 2;
     const int gq = a.nq / a.nkv;
@@ -670,6 +816,7 @@ __device__ bool combine_task(const FusedArgs &a, int l, int task, Smem<D> &sm) {
     const int b = hb % a.B, h = hb / a.B;
     const uint32_t ep = (uint32_t)l + 1;
     if (!wait_all(a.f_att + (int64_t)hb * a.n_chunks, a.n_chunks, ep, a.err, sm)) return false;
+    stamp(a, l, 21);
     const int tau = threadIdx.x;
     constexpr int TPC = D / 8;                  // threads per column, two dims each
     if (tau < 16 * TPC) {
@@ -683,17 +830,18 @@ __device__ bool combine_task(const FusedArgs &a, int l, int task, Smem<D> &sm) {
             if (a.status[b] == 0) {
                 const int nc = (a.ctx_len[b] + a.K + a.CH - 1) / a.CH;
                 float mx = -INFINITY;
-                for (int c0 = 0; c0 < nc; c0 += 8) {
-                    uint64_t ml[8], ov[8];
+                // chunk partials requested 16 at a time
+                for (int c0 = 0; c0 < nc; c0 += 16) {
+                    uint64_t ml[16], ov[16];
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) {
+                    for (int i = 0; i < 16; ++i) {
                         const int c = min(c0 + i, nc - 1);
                         const int64_t base = ((int64_t)(hb * a.n_chunks + c) * T_ + t) * 16 + col;
                         ml[i] = ld_dev64(a.att_ml + base);
                         ov[i] = ld_dev64(a.att_o + base * D + d);
                     }
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) {
+                    for (int i = 0; i < 16; ++i) {
                         if (c0 + i >= nc) break;
                         const float mk = lo_f(ml[i]), lk = hi_f(ml[i]);
                         if (mk == -INFINITY) continue;
@@ -708,9 +856,10 @@ __device__ bool combine_task(const FusedArgs &a, int l, int task, Smem<D> &sm) {
                 o0 = o0 / lsum;
                 o1 = o1 / lsum;
             }
-            st_dev32(a.ao + frag_off(m, head * D + d, a.nq * D), pack2bf(o0, o1));
+            st_dev32(ao_of(a, li) + frag_off(m, head * D + d, a.nq * D), pack2bf(o0, o1));
         }
     }
+    stamp(a, l, 22);
     publish<D>(a.f_comb + task, ep);
     __syncthreads();
     return true;
@@ -727,7 +876,7 @@ __global__ __launch_bounds__(kFT, 1) void fused_layers_kernel(FusedArgs a) {
             if (!attn_item<D>(a, li, l, it, sm)) return;
         stamp(a, l, 4);
         for (int tk = (int)gridDim.x - 1 - (int)blockIdx.x; tk < a.n_tasks; tk += gridDim.x)
-            if (!combine_task<D>(a, l, tk, sm)) return;
+            if (!combine_task<D>(a, li, l, tk, sm)) return;
         stamp(a, l, 5);
         if (!gemm_phase<FUSED_O, 2, D>(a, li, l, sm)) return;
         if (!gemm_phase<FUSED_GU, 4, D>(a, li, l, sm)) return;
@@ -747,7 +896,9 @@ __global__ __launch_bounds__(kFT, 1) void fused_layers_kernel(FusedArgs a) {
         const int fi = blockIdx.x * kFT + threadIdx.x;
         if (fi < nfrag) {
             const int s = fi / 64, ln = fi % 64;
-            const bf16x8 x = ld_dev16(a.x, (uint32_t)(fi * 16));
+            // device scope: this slot is also the launch's input, read (and cached) by its
+            // first layer before the last layer rewrote it
+            const bf16x8 x = ld_dev16(x_out(a, a.nl - 1), (uint32_t)(fi * 16));
             const bf16x8 g = *(const bf16x8 *)(a.g_final + s * 32 + 8 * (ln >> 4));
             *(bf16x8 *)(a.u_head + (int64_t)fi * 8) = norm_frag(x, sm.rs[ln & 15], g);
         }
@@ -765,7 +916,8 @@ __global__ __launch_bounds__(256) void fused_prep_kernel(FusedArgs a, const int3
         const int64_t stride = (int64_t)(gridDim.x - 16) * 256;
         const int64_t base = (int64_t)(blockIdx.x - 16) * 256 + tid;
         for (int64_t i = base; i < n_sync; i += stride) sync_words[i] = 0u;
-        const int64_t nao = (int64_t)16 * a.nq * a.D / 2, nh = (int64_t)16 * a.F / 2;
+        const int64_t nao = (int64_t)kFusedMaxLayers * 16 * a.nq * a.D / 2;
+        const int64_t nh = (int64_t)kFusedMaxLayers * 16 * a.F / 2;
         for (int64_t i = base; i < nao; i += stride) reinterpret_cast<uint32_t *>(a.ao)[i] = 0u;
         for (int64_t i = base; i < nh; i += stride) reinterpret_cast<uint32_t *>(a.h)[i] = 0u;
         return;
@@ -784,7 +936,7 @@ __global__ __launch_bounds__(256) void fused_prep_kernel(FusedArgs a, const int3
             const int col = 64 * g + 4 * (tid % 16);
             uint2 v = live ? *(const uint2 *)(src + col) : make_uint2(0u, 0u);
             if (m >= a.M) v = make_uint2(0u, 0u);
-            *(uint2 *)(a.x + frag_off(m, col, a.H)) = v;
+            *(uint2 *)(a.x_d + (int64_t)(kFusedMaxLayers - 1) * 16 * a.H + frag_off(m, col, a.H)) = v;
             if (a.trace != nullptr && m < a.M) *(uint2 *)(a.trace + (int64_t)m * a.H + col) = v;
             const float f0 = bf_lo(v.x), f1 = bf_hi(v.x), f2 = bf_lo(v.y), f3 = bf_hi(v.y);
             ss = ((f0 * f0 + f1 * f1) + f2 * f2) + f3 * f3;

@@ -148,8 +148,10 @@ hipError_t rec_commit(float *state, const bf16 *k, const bf16 *v, const float *l
 // ---- the persistent pass over the layers for at most 16 rows (k_fused.hip) ------------------------
 constexpr int kFusedMaxLayers = 16;    // layers per launch (their weights ride in the arguments)
 // Phase timestamps per (layer, workgroup): QKV wait begin, inputs ready, loop end, done (0-3),
-// attention items done (4), merges done (5), O (6-9), gate/up (10-13), down (14-17).
-constexpr int kFusedTraceEvents = 18;
+// attention items done (4), merges done (5), O (6-9), gate/up (10-13), down (14-17); inside the
+// (last) attention item of the workgroup: inputs ready (18), keys and values in LDS (19), products
+// done (20); inside its (last) merge task: inputs ready (21), output written (22).
+constexpr int kFusedTraceEvents = 24;
 enum { FUSED_QKV = 0, FUSED_O = 1, FUSED_GU = 2, FUSED_DOWN = 3 };
 
 // One projection, split evenly over g_eff workgroups as ranges of (64-column group, 32-wide K
@@ -179,11 +181,16 @@ struct FusedArgs {
     const int32_t *ctx_len, *status;
     const uint64_t *anc;
     const float2 *rope;
-    bf16 *x;                         // [16][H] fragment order, the residual stream
+    // Operands read with plain (cached) loads have one slot per layer of a launch, written once
+    // in it: the residual stream after O and after down ([16][H] fragment order; the input of
+    // the launch's first layer is the last down slot, which the embedding fills before layer 0),
+    // q ([M][nq][D]), the attention output ([16][nq*D] fragment order, O's operand) and the
+    // SwiGLU output ([16][F] fragment order, down's operand).
+    bf16 *x_o, *x_d;                 // [kFusedMaxLayers][16][H]
     float *ssq_o, *ssq_d;            // [H/64][16] groups' sums of squares after O, after down
-    bf16 *q;                         // [M][nq][D]
-    bf16 *ao;                        // [16][nq*D] fragment order, the O projection's operand
-    bf16 *h;                         // [16][F] fragment order, the down projection's operand
+    bf16 *q;                         // [kFusedMaxLayers][M][nq][D]
+    bf16 *ao;                        // [kFusedMaxLayers][16][nq*D]
+    bf16 *h;                         // [kFusedMaxLayers][16][F]
     bf16 *u_head;                    // [16][H] fragment order, the output head's operand
     bf16 *trace;                     // optional [Lt + 1][M][H] residual stream
     FusedPhase ph[4];

@@ -80,12 +80,12 @@ void fused_counts(const Plan &p, int G, int max_pages, FusedCounts &f) {
         f.max_seg[ph] = ms;
     }
     // attention: about G / (B * n_kv) chunks per (request, kv head), whole 32-key steps, at most
-    // 192 keys (the LDS of one item); more items than workgroups run in turns
+    // 160 keys (the registers of one item); more items than workgroups run in turns
     const int64_t max_keys = (int64_t)max_pages * SPEC_PAGE_SIZE;
     int per = G / (p.B * p.nkv);
     if (per < 1) per = 1;
     int64_t ch = (max_keys + 32LL * per - 1) / (32LL * per) * 32;
-    if (ch > 192) ch = 192;
+    if (ch > 160) ch = 160;
     if (ch < 32) ch = 32;
     f.CH = (int)ch;
     f.n_chunks = (int)((max_keys + ch - 1) / ch);
@@ -182,12 +182,13 @@ int make_plan(const spec_model_cfg *c, int B, int K, int max_pages, Plan &p) {
     if (p.fused_shape) {
         FusedCounts f;
         fused_counts(p, kFusedSizeG, max_pages, f);
-        p.f_x = cv.take(sizeof(uint16_t) * 16 * p.H);
+        const size_t nl = kFusedMaxLayers;
+        p.f_x = cv.take(sizeof(uint16_t) * 2 * nl * 16 * p.H);      // x_o slots, then x_d slots
         p.f_ssq_o = cv.take(sizeof(float) * (p.H / 64) * 16);
         p.f_ssq_d = cv.take(sizeof(float) * (p.H / 64) * 16);
-        p.f_q = cv.take(sizeof(uint16_t) * M * p.qd);
-        p.f_ao = cv.take(sizeof(uint16_t) * 16 * p.qd);
-        p.f_h = cv.take(sizeof(uint16_t) * 16 * p.F);
+        p.f_q = cv.take(sizeof(uint16_t) * nl * M * p.qd);
+        p.f_ao = cv.take(sizeof(uint16_t) * nl * 16 * p.qd);
+        p.f_h = cv.take(sizeof(uint16_t) * nl * 16 * p.F);
         p.f_u = cv.take(sizeof(uint16_t) * 16 * p.H);
         for (int ph = 0; ph < 4; ++ph)
             p.f_part[ph] = cv.take(sizeof(float) * 1024 * (size_t)f.groups[ph] * f.max_parts[ph]);
@@ -352,7 +353,8 @@ int spec_verify(const spec_weights *w, const spec_kv_cache *kv, const int32_t *d
         fa.status = ni.status;
         fa.anc = ni.anc;
         fa.rope = ni.rope;
-        fa.x = at<bf16>(workspace, p.f_x);
+        fa.x_o = at<bf16>(workspace, p.f_x);
+        fa.x_d = fa.x_o + (size_t)kFusedMaxLayers * 16 * p.H;
         fa.ssq_o = at<float>(workspace, p.f_ssq_o);
         fa.ssq_d = at<float>(workspace, p.f_ssq_d);
         fa.q = at<bf16>(workspace, p.f_q);
