@@ -21,10 +21,11 @@ import tree_verification_skinny_amd as tv
 from tree_verification_skinny_amd import kvlayout
 
 ATOL, RTOL, NEAR_TIE = 2e-2, 1e-2, 1e-2
-# check_as_exact: how much farther from the oracle than the exact evaluation the GPU may be. A
-# correct fp32 evaluation in another summation order measures about 1.01x on a 27B-shape layer;
-# planted kernel mistakes (a dropped K step, wrong RoPE pairs or position, swapped kv heads, a 1 %
-# softmax scale error) measure 3x and more (tests/test_oracle_27b_criterion.py).
+# check_as_exact: how much farther from the exact (float64) evaluation than the oracle the GPU may
+# be. The GPU's blocked sums keep it closer to the exact values than the oracle's sequential ones
+# on the 27B block (0.1x to 1.1x by layer); planted kernel mistakes (a dropped K step, wrong RoPE
+# pairs or position, swapped kv heads, a 1 % softmax scale error) measure far more
+# (tests/test_oracle_27b_criterion.py).
 EXACT_FACTOR = 1.25
 
 
@@ -117,22 +118,40 @@ def check_logits(gpu: np.ndarray, orc: np.ndarray, what: str = "logits"):
     return float(err.max())
 
 
+def bf16_ulp(v: float) -> float:
+    """Spacing of bf16 values (8 significant bits) at magnitude v."""
+    v = abs(float(v))
+    if v < 2.0 ** -126:
+        return 2.0 ** -133
+    return 2.0 ** (np.floor(np.log2(v)) - 7)
+
+
 def check_as_exact(gpu, orc, ref, what: str = "", factor: float = EXACT_FACTOR):
     """Parity where summation order alone exceeds the fixed tolerance (the 27B-class shape with
     random weights: an exact float64 evaluation of the same model and storage points already
-    differs from the oracle by more than 2e-2 + 1e-2|x| in a few elements). The GPU must be as
-    close to the oracle as that exact evaluation is: max and mean deviation, and the share of
-    elements outside the fixed tolerance, within `factor` of the exact evaluation's."""
+    differs from the oracle by more than 2e-2 + 1e-2|x| in a few elements). Both the GPU and the
+    oracle are fp32 evaluations of the same storage points, so each is measured against the exact
+    one: the GPU's max and mean deviation from it, and its share of elements outside the fixed
+    tolerance around it, must be within `factor` of the oracle's. (Measured against the oracle
+    instead, a correct GPU inherits the oracle's own rounding on top of its own, up to sqrt(2)
+    times the exact evaluation's distance, so no tight factor holds there.) The max of bf16
+    outputs moves in whole ULPs of the largest elements (one rounding flip at magnitude 64 turns
+    0.25 into 0.5), so it may exceed `factor` times the oracle's by one bf16 ULP of the worst
+    element's own magnitude; mean and out-of-tolerance share carry no such slack."""
+    ref = np.asarray(ref, np.float64)
     orc = np.asarray(orc, np.float64)
-    eg = np.abs(np.asarray(gpu, np.float64) - orc)
-    er = np.abs(np.asarray(ref, np.float64) - orc)
-    lim = ATOL + RTOL * np.abs(orc)
-    fg, fr = float(np.mean(eg > lim)), float(np.mean(er > lim))
-    msg = (f"{what}: gpu-vs-oracle max {eg.max():.3e} mean {eg.mean():.3e} out-of-tol {fg:.4f}; "
-           f"exact-vs-oracle max {er.max():.3e} mean {er.mean():.3e} out-of-tol {fr:.4f}")
-    assert eg.max() <= factor * max(er.max(), 1e-6), msg
-    assert eg.mean() <= factor * max(er.mean(), 1e-7), msg
-    assert fg <= factor * fr + 1e-3, msg
+    eg = np.abs(np.asarray(gpu, np.float64) - ref)
+    eo = np.abs(orc - ref)
+    lim = ATOL + RTOL * np.abs(ref)
+    fg, fo = float(np.mean(eg > lim)), float(np.mean(eo > lim))
+    d = np.abs(np.asarray(gpu, np.float64) - orc)
+    msg = (f"{what}: gpu-vs-exact max {eg.max():.3e} mean {eg.mean():.3e} out-of-tol {fg:.4f}; "
+           f"oracle-vs-exact max {eo.max():.3e} mean {eo.mean():.3e} out-of-tol {fo:.4f}; "
+           f"gpu-vs-oracle max {d.max():.3e} mean {d.mean():.3e}")
+    worst = float(np.abs(ref.reshape(-1)[int(np.argmax(eg))]))
+    assert eg.max() <= factor * max(eo.max(), 1e-6) + bf16_ulp(worst), msg
+    assert eg.mean() <= factor * max(eo.mean(), 1e-7), msg
+    assert fg <= factor * fo + 1e-3, msg
     return msg
 
 

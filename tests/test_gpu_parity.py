@@ -316,7 +316,7 @@ def test_tiny_stream_attention_dominant_keys():
     output; parity with the oracle. Scores 300 times larger make a few columns ill-conditioned
     (where two strong keys nearly tie, one bf16 ulp of q moves the logits by tenths, and the
     float64 evaluation itself leaves the fixed tolerance there): for such a request the GPU
-    must be as close to the oracle as that exact evaluation is."""
+    must be as close to that exact evaluation as the oracle is."""
     B, k = 24, 16
     w = synth.model_weights(synth.TINY, 555)
     m = oracle_model_from(synth.TINY, w)
@@ -477,7 +477,7 @@ def test_27b_single_layer_parity(path):
     check_logits(kg.float().cpu().numpy(), oracle.from_bf16(r.k_new[0]), "k_new")
     check_logits(vg.float().cpu().numpy(), oracle.from_bf16(r.v_new[0]), "v_new")
     assert np.mean(bits(kg) == r.k_new[0]) > 0.98
-    # layer output and logits: as close to the oracle as an exact evaluation
+    # layer output and logits: as close to an exact evaluation as the oracle is
     print(check_as_exact(out.hidden[1].float().cpu().numpy(), oracle.from_bf16(r.hidden[1]),
                          ref_hidden[1].numpy(), "layer output"))
     print(check_as_exact(out.logits[0], r.logits, ref_logits, "logits"))

@@ -2,8 +2,9 @@
 plausible kernel mistakes, shown on the CPU on one decoder layer at the 27B shape.
 
 At that shape the fixed tolerance (2e-2 + 1e-2|x|) is tighter than fp32 summation order alone
-allows, so the GPU is held to the distance an exact (float64) evaluation of the same storage
-points keeps from the oracle. That rule is only worth something if it still catches bugs. Here:
+allows, so the GPU is measured against an exact (float64) evaluation of the same storage points
+and must stay as close to it as the oracle does. That rule is only worth something if it still
+catches bugs. Here:
   * a correct fp32 evaluation in another summation order (torch's own, through the independent
     decoder of ref64) passes at the factor the GPU tests use;
   * the oracle itself, run on inputs that reproduce a plausible kernel mistake exactly, fails:
