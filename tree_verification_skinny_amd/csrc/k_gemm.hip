@@ -372,6 +372,7 @@ __global__ __launch_bounds__(64 * W) void gemm_kernel(GemmIn in, const bf16 *__r
 #ifndef SV_TC_TARGET
 #define SV_TC_TARGET 512                                // workgroups a split tile launch aims at
 #endif
+constexpr int kPlanCUs = 256;                           // compute units of the target (MI355X)
 #ifndef SV_WIDE_KS
 #define SV_WIDE_KS 4
 #endif
@@ -742,9 +743,10 @@ hipError_t gemm_w12(const GemmShape &g, int epi, const GemmIn &in_all, const W12
 // Tiles per group, waves per workgroup and K splits for a projection of N outputs over Kd at M
 // rows. Every workgroup reads the activation rows of its K range once, so a group of NT tiles
 // costs 1/NT of its weight bytes again in activation reads: groups are four tiles wide where the
-// register budget allows. Projections with few groups are split along K until about 640
-// workgroups stream (partials, added by a separate pass); projections with many groups run whole
-// and finish their epilogue in place. Eight waves when there are few groups or K splits.
+// register budget allows. Projections with few groups are split along K (partials, added by a
+// separate pass): at one block of rows into at most one workgroup per compute unit, at more rows
+// until about 640 workgroups stream. Projections with many groups run whole and finish their
+// epilogue in place. Eight waves when there are few groups or K splits.
 static GemmShape plan_skinny(int M, int N, int Kd, bool allow_split);
 
 GemmShape plan_gemm(int M, int N, int Kd, bool allow_split, bool allow_tc) {
@@ -820,9 +822,22 @@ static GemmShape plan_skinny(int M, int N, int Kd, bool allow_split) {
     const int mt = mt_for(M < 64 ? M : 64);
     g.nt = (N % 64 == 0) ? 4 : (N % 32 == 0 ? 2 : 1);
     if (mt == 4 && g.nt == 4) g.nt = 2;
+    // one block of rows, whole K, many more groups than compute units (gate/up, the output head):
+    // two-tile groups. Four times as many workgroups as units spread the stream more evenly than
+    // four-tile groups (gate/up at the 27B shape: 2.1 per unit, an eighth of the units streaming
+    // a workgroup more than the rest; 9.64 against 9.87 ms per block step)
+    if (mt == 1 && !allow_split && N % 32 == 0 && N / 64 > kPlanCUs) g.nt = 2;
     const int groups = N / (16 * g.nt);
     g.splits = 1;
-    if (allow_split && groups < 400) {
+    if (allow_split && mt == 1 && groups < kPlanCUs) {
+        // one block of rows: at most one workgroup per compute unit, as many as fit. A stream
+        // split over up to one workgroup per unit runs at the full rate; a grid that leaves some
+        // units one workgroup more than others waits for those (one 256 MB stream measured
+        // 6.7 TB/s over 256 workgroups, 5.3 over 320, 5.7 over 544)
+        g.splits = kPlanCUs / groups;
+        if (g.splits > 16) g.splits = 16;
+        while (g.splits > 1 && steps / g.splits < 16) --g.splits;
+    } else if (allow_split && groups < 400) {
         g.splits = (SV_SKINNY_TARGET + groups / 2) / groups;
         if (g.splits > 16) g.splits = 16;
         while (g.splits > 1 && steps / g.splits < 16) --g.splits;
