@@ -6,10 +6,11 @@
 // architecture"]. The path is a 64-bit ancestor mask per node (bit j set = node j is on the
 // path), so the mask test in the inner loop is one shift and one AND.
 //
-// Two work splits (split-KV), both over chunks of 128 key positions: for a small grid (one
-// request, a block of 16) one workgroup per (request, pair of kv heads, chunk), whose waves
-// stage the chunk's keys [128][D] and values [D][128] from the cache pages into LDS and take
-// 16-column query tiles each; for a large grid (a batch, a 64-node tree) one wave per (request,
+// Two work splits (split-KV): for a small grid (one request, a block of 16) one workgroup per
+// (request, kv head, chunk of 192 keys), whose waves stage the chunk's keys [192][D] and values
+// [D][192] from the cache pages into LDS and take 16-column query tiles (optionally several
+// waves per tile, one per part of the chunk, merged in LDS); for a large grid (a batch, a
+// 64-node tree), over chunks of 128 keys, one wave per (request,
 // kv head, tile group, range of chunks), which streams its keys and values through LDS 32 at a
 // time (attn_wave_kernel). The query columns are (q head of this kv group, draft node) pairs, so
 // one K/V tile in LDS serves every q head of the group. Per 32 keys and tile:
@@ -25,27 +26,37 @@
 
 namespace sv {
 
-// HPW kv heads per workgroup (NW waves each) share the chunk's page reads and halve the number
-// of workgroups, so that a typical grid is resident at once.
-template <int D, int NW, int HPW>
-__global__ __launch_bounds__(64 * NW * HPW) void attn_partial_kernel(
+// A workgroup takes one chunk of CH keys for HPW kv heads; each head's query tiles are spread
+// over NW tile slots of KS waves, the KS waves of a slot splitting the chunk's 32-key steps
+// evenly and merging their states in LDS (fixed order). More heads per workgroup share one
+// chunk's page reads; more waves per tile shorten each wave's serial chain of products and
+// softmax at the same LDS traffic.
+template <int D, int NW, int HPW, int CH, int KS>
+__global__ __launch_bounds__(64 * NW * HPW * KS) void attn_partial_kernel(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k_pool, const bf16 *__restrict__ v_pool,
     const int32_t *__restrict__ block_table, int max_pages, const int32_t *__restrict__ ctx_len,
     const uint64_t *__restrict__ anc, const int32_t *__restrict__ status, int K, int nq, int nkv,
     int n_chunks, float scale_log2, float *__restrict__ part_o, float2 *__restrict__ part_ml) {
-    constexpr int CH = kAttnChunk;
     constexpr int NS = CH / 32;  // 32-key steps per chunk
+    static_assert(CH % 32 == 0 && NS % KS == 0, "key steps split evenly over a tile's waves");
+    constexpr int MS = NS / KS;  // key steps per wave
     constexpr int KP = D + 8;    // padded LDS row of K (bf16)
     constexpr int VP = CH + 8;   // padded LDS row of V^T (bf16)
+    constexpr int WPH = NW * KS; // waves per head
     constexpr int STAGERS = 16 * D / 8;   // threads that stage one head's 16-position page
-    static_assert(STAGERS <= 64 * NW, "staging needs one thread per 16 bytes of a page");
+    static_assert(STAGERS <= 64 * WPH, "staging needs one thread per 16 bytes of a page");
+    constexpr int MSL = KS > 1 ? HPW * NW * (KS - 1) : 1;   // merge slots
     __shared__ __attribute__((aligned(16))) bf16 Ks_all[HPW * CH * KP];
     __shared__ __attribute__((aligned(16))) bf16 Vt_all[HPW * D * VP];
+    __shared__ floatx4 mg_o[MSL * (D / 16) * 64];
+    __shared__ float mg_m[MSL * 64], mg_l[MSL * 64];
 
     const int c = blockIdx.x, b = blockIdx.z;
     const int wave_all = threadIdx.x >> 6;
-    const int hl = wave_all / NW;                 // this wave's head within the workgroup
+    const int hl = wave_all / WPH;                // this wave's head within the workgroup
     const int g = blockIdx.y * HPW + hl;          // its kv head
+    const int wv = wave_all % WPH;
+    const int tw = wv / KS, kp = wv % KS;         // tile slot, key part
     const bf16 *Ks = Ks_all + hl * CH * KP;
     const bf16 *Vt = Vt_all + hl * D * VP;
     constexpr int NP = CH / 16;
@@ -68,7 +79,7 @@ __global__ __launch_bounds__(64 * NW * HPW) void attn_partial_kernel(
     const int R = group * K;
     const int QT = (R + 15) >> 4;
 
-    const int lane = threadIdx.x & 63, wave = wave_all % NW;
+    const int lane = threadIdx.x & 63;
     const int r16 = lane & 15, grp = lane >> 4;
     // the first query tile's fragments are fetched before the chunk, so the two overlap
     bf16x8 qf_next[D / 32];
@@ -80,10 +91,10 @@ __global__ __launch_bounds__(64 * NW * HPW) void attn_partial_kernel(
         return q + ((int64_t)(b * K + tok) * nq + g * group + hh) * D;
     };
     uint64_t am_next = 0;
-    if (wave < QT) {
+    if (tw < QT) {
         bool ok_;
         int tok_, hh_;
-        const bf16 *qrow = q_ptr(wave, ok_, tok_, hh_);
+        const bf16 *qrow = q_ptr(tw, ok_, tok_, hh_);
 #pragma unroll
         for (int ds = 0; ds < D / 32; ++ds) qf_next[ds] = *(const bf16x8 *)(qrow + ds * 32 + grp * 8);
         am_next = anc[b * K + tok_];
@@ -91,7 +102,7 @@ __global__ __launch_bounds__(64 * NW * HPW) void attn_partial_kernel(
 
     // ---- stage the chunk: K rows as stored, V already transposed in the page ---------------
     // Every staging thread issues all of its page loads before the first LDS store, so the
-    // chunk's 2 x 8 x 16 B per thread are in flight together.
+    // chunk's 2 x NP x 16 B per thread are in flight together.
     {
         const int hs = threadIdx.x / STAGERS;          // head this thread stages
         const int gs = blockIdx.y * HPW + hs;
@@ -128,132 +139,135 @@ __global__ __launch_bounds__(64 * NW * HPW) void attn_partial_kernel(
     __syncthreads();
 
     const int kr0 = 8 * (r16 >> 2) + (r16 & 3);   // S^T tile 0 key row of this lane (tile 1: +4)
-    // the whole chunk lies inside the committed context: no key needs the mask
-    const bool chunk_plain = nvalid == CH && kb + CH <= ctx;
+    const int s0 = kp * MS;                       // this wave's first key step
+    // the wave's keys all lie inside the committed context: no key needs the mask
+    const bool part_plain = kb + (s0 + MS) * 32 <= min(ctx, kb + nvalid);
+    const int n_iter = (QT + NW - 1) / NW;        // the same for every wave (merge barriers)
 
-    for (int t = wave; t < QT; t += NW) {
+    for (int it = 0; it < n_iter; ++it) {
+        const int t = tw + it * NW;
+        const bool has = t < QT;
         const int rho = 16 * t + r16;             // query column of this lane
-        bool col_ok;
-        int tok, hh;
-        q_ptr(t, col_ok, tok, hh);
+        bool col_ok = false;
+        int tok = 0, hh = 0;
+        if (has) q_ptr(t, col_ok, tok, hh);
         const uint64_t am = am_next;
         bf16x8 qf[D / 32];
 #pragma unroll
         for (int ds = 0; ds < D / 32; ++ds) qf[ds] = qf_next[ds];
 
-        // S^T for the whole chunk: step st, half h holds key rows st*32 + kr0 + 4h; with the row
-        // order above, this lane ends up with keys st*32 + 8*grp + e, e = 0..7. The staged chunk
-        // is zero past its valid keys, so all NS steps run (masked below). Key fragments are
-        // read from LDS one step ahead of the products that use them.
-        floatx4 s[NS][2];
-        {
-            // stage i = (step i / 2, half i % 2): D/32 key fragments, D/32 products
-            constexpr int NST = 2 * NS, FK = D / 32;
-            bf16x8 kf0[FK], kf1[FK];
-            auto kload = [&](bf16x8 (&kf)[FK], int i) {
-#pragma unroll
-                for (int ds = 0; ds < FK; ++ds)
-                    kf[ds] = *(const bf16x8 *)&Ks[((i >> 1) * 32 + kr0 + 4 * (i & 1)) * KP + grp * 8 + ds * 32];
-            };
-            kload(kf0, 0);
-#pragma unroll
-            for (int i = 0; i < NST; ++i) {
-                auto &cur = (i & 1) ? kf1 : kf0;
-                auto &nxt = (i & 1) ? kf0 : kf1;
-                if (i + 1 < NST) {
-                    kload(nxt, i + 1);
-                    __builtin_amdgcn_sched_group_barrier(0x100, FK, 0);   // LDS reads
-                }
-                floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ds = 0; ds < FK; ++ds) acc = mfma16x16x32(cur[ds], qf[ds], acc);
-                s[i >> 1][i & 1] = acc;
-                __builtin_amdgcn_sched_group_barrier(0x008, FK, 0);       // MFMAs
-            }
-        }
-        // one softmax over the chunk, in the log2 domain: m = max, p = 2^(s - m), l = sum p
-        float sv[NS][8];
-        float mloc = -INFINITY;
-        if (chunk_plain) {
-            // every key is committed context, visible to every node (columns past R are
-            // computed on a stand-in query and never stored)
-#pragma unroll
-            for (int st = 0; st < NS; ++st)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    sv[st][e] = (e < 4 ? s[st][0][e] : s[st][1][e - 4]) * scale_log2;
-                    mloc = fmaxf(mloc, sv[st][e]);
-                }
-        } else {
-#pragma unroll
-            for (int st = 0; st < NS; ++st) {
-                // visibility of this lane's 8 keys ka = k0 .. k0 + 7 as a bit mask: committed
-                // positions (< ctx) always, draft positions ctx + j when node j is an ancestor
-                const int k0 = kb + st * 32 + 8 * grp;
-                const int n_ctx = min(max(ctx - k0, 0), 8);
-                const int j0 = max(k0 + n_ctx - ctx, 0);     // first draft index among them
-                const unsigned anc8 = j0 < 64 ? (unsigned)(am >> j0) & 0xffu : 0u;
-                const int n_in = min(max(kb + nvalid - k0, 0), 8);   // keys inside the chunk
-                unsigned vis = (((1u << n_ctx) - 1u) | (anc8 << n_ctx)) & ((1u << n_in) - 1u);
-                if (!col_ok) vis = 0u;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float raw = (e < 4 ? s[st][0][e] : s[st][1][e - 4]) * scale_log2;
-                    sv[st][e] = ((vis >> e) & 1u) ? raw : -INFINITY;
-                    mloc = fmaxf(mloc, sv[st][e]);
-                }
-            }
-        }
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-        const bool none = (mloc == -INFINITY);
-        // p = p_hi + p_lo, both bf16: the two products carry ~16 bits of p, so the weighted sum
-        // of values is as precise as the fp32 probabilities it stands for.
-        bf16x8 ph[NS], pl[NS];
-        float psum = 0.f;
-#pragma unroll
-        for (int st = 0; st < NS; ++st) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float pv = none ? 0.f : __builtin_amdgcn_exp2f(sv[st][e] - mloc);
-                const bf16 hi = to_bf(pv);
-                ph[st][e] = hi;
-                pl[st][e] = to_bf(pv - to_f(hi));
-                psum += pv;
-            }
-        }
-        psum += __shfl_xor(psum, 16, 64);
-        psum += __shfl_xor(psum, 32, 64);
-
-        // O^T = V^T . P^T over the chunk, value fragments read one step ahead
         floatx4 o[D / 16];
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt) o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
-        {
-            // stage i = (step i / 2, value rows half i % 2): FV fragments, 2 FV products
-            constexpr int NST = 2 * NS, FV = D / 32;
-            bf16x8 vf0[FV], vf1[FV];
-            auto vload = [&](bf16x8 (&vf)[FV], int i) {
+        float mloc = -INFINITY, psum = 0.f;
+        if (has) {
+            // S^T over the wave's steps: stage i = (step s0 + i / 2, half i % 2) holds key rows
+            // step*32 + kr0 + 4 half; with the row order above, this lane ends up with keys
+            // step*32 + 8*grp + e, e = 0..7. The staged chunk is zero past its valid keys
+            // (masked below). Key fragments are read from LDS one stage ahead of their products.
+            floatx4 sc[MS][2];
+            {
+                constexpr int NST = 2 * MS, FK = D / 32;
+                bf16x8 kf0[FK], kf1[FK];
+                auto kload = [&](bf16x8 (&kf)[FK], int i) {
 #pragma unroll
-                for (int j = 0; j < FV; ++j)
-                    vf[j] = *(const bf16x8 *)&Vt[(r16 + ((i & 1) * FV + j) * 16) * VP + (i >> 1) * 32 + grp * 8];
-            };
-            vload(vf0, 0);
+                    for (int ds = 0; ds < FK; ++ds)
+                        kf[ds] = *(const bf16x8 *)&Ks[((s0 + (i >> 1)) * 32 + kr0 + 4 * (i & 1)) * KP + grp * 8 + ds * 32];
+                };
+                kload(kf0, 0);
 #pragma unroll
-            for (int i = 0; i < NST; ++i) {
-                auto &cur = (i & 1) ? vf1 : vf0;
-                auto &nxt = (i & 1) ? vf0 : vf1;
-                if (i + 1 < NST) {
-                    vload(nxt, i + 1);
-                    __builtin_amdgcn_sched_group_barrier(0x100, FV, 0);        // LDS reads
+                for (int i = 0; i < NST; ++i) {
+                    auto &cur = (i & 1) ? kf1 : kf0;
+                    auto &nxt = (i & 1) ? kf0 : kf1;
+                    if (i + 1 < NST) {
+                        kload(nxt, i + 1);
+                        __builtin_amdgcn_sched_group_barrier(0x100, FK, 0);   // LDS reads
+                    }
+                    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ds = 0; ds < FK; ++ds) acc = mfma16x16x32(cur[ds], qf[ds], acc);
+                    sc[i >> 1][i & 1] = acc;
+                    __builtin_amdgcn_sched_group_barrier(0x008, FK, 0);       // MFMAs
                 }
+            }
+            // one softmax over the wave's keys, in the log2 domain: m = max, p = 2^(s - m)
+            float sv[MS][8];
+            if (part_plain) {
+                // committed context only, visible to every node (columns past R are computed
+                // on a stand-in query and never stored)
 #pragma unroll
-                for (int j = 0; j < FV; ++j) {
-                    const int dt = (i & 1) * FV + j;
-                    o[dt] = mfma16x16x32(cur[j], ph[i >> 1], o[dt]);
-                    o[dt] = mfma16x16x32(cur[j], pl[i >> 1], o[dt]);
+                for (int st = 0; st < MS; ++st)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        sv[st][e] = (e < 4 ? sc[st][0][e] : sc[st][1][e - 4]) * scale_log2;
+                        mloc = fmaxf(mloc, sv[st][e]);
+                    }
+            } else {
+#pragma unroll
+                for (int st = 0; st < MS; ++st) {
+                    // visibility of this lane's 8 keys as a bit mask: committed positions
+                    // (< ctx) always, draft positions ctx + j when node j is an ancestor
+                    const int k0 = kb + (s0 + st) * 32 + 8 * grp;
+                    const int n_ctx = min(max(ctx - k0, 0), 8);
+                    const int j0 = max(k0 + n_ctx - ctx, 0);     // first draft index among them
+                    const unsigned anc8 = j0 < 64 ? (unsigned)(am >> j0) & 0xffu : 0u;
+                    const int n_in = min(max(kb + nvalid - k0, 0), 8);   // keys inside the chunk
+                    unsigned vis = (((1u << n_ctx) - 1u) | (anc8 << n_ctx)) & ((1u << n_in) - 1u);
+                    if (!col_ok) vis = 0u;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float raw = (e < 4 ? sc[st][0][e] : sc[st][1][e - 4]) * scale_log2;
+                        sv[st][e] = ((vis >> e) & 1u) ? raw : -INFINITY;
+                        mloc = fmaxf(mloc, sv[st][e]);
+                    }
                 }
-                __builtin_amdgcn_sched_group_barrier(0x008, 2 * FV, 0);    // MFMAs
+            }
+            mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
+            mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+            const bool none = (mloc == -INFINITY);
+            // p = p_hi + p_lo, both bf16: the two products carry ~16 bits of p, so the weighted
+            // sum of values is as precise as the fp32 probabilities it stands for.
+            bf16x8 ph[MS], pl[MS];
+#pragma unroll
+            for (int st = 0; st < MS; ++st) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float pv = none ? 0.f : __builtin_amdgcn_exp2f(sv[st][e] - mloc);
+                    const bf16 hi = to_bf(pv);
+                    ph[st][e] = hi;
+                    pl[st][e] = to_bf(pv - to_f(hi));
+                    psum += pv;
+                }
+            }
+            psum += __shfl_xor(psum, 16, 64);
+            psum += __shfl_xor(psum, 32, 64);
+
+            // O^T = V^T . P^T over the wave's steps, value fragments read one stage ahead
+            {
+                constexpr int NST = 2 * MS, FV = D / 32;
+                bf16x8 vf0[FV], vf1[FV];
+                auto vload = [&](bf16x8 (&vf)[FV], int i) {
+#pragma unroll
+                    for (int j = 0; j < FV; ++j)
+                        vf[j] = *(const bf16x8 *)&Vt[(r16 + ((i & 1) * FV + j) * 16) * VP + (s0 + (i >> 1)) * 32 + grp * 8];
+                };
+                vload(vf0, 0);
+#pragma unroll
+                for (int i = 0; i < NST; ++i) {
+                    auto &cur = (i & 1) ? vf1 : vf0;
+                    auto &nxt = (i & 1) ? vf0 : vf1;
+                    if (i + 1 < NST) {
+                        vload(nxt, i + 1);
+                        __builtin_amdgcn_sched_group_barrier(0x100, FV, 0);        // LDS reads
+                    }
+#pragma unroll
+                    for (int j = 0; j < FV; ++j) {
+                        const int dt = (i & 1) * FV + j;
+                        o[dt] = mfma16x16x32(cur[j], ph[i >> 1], o[dt]);
+                        o[dt] = mfma16x16x32(cur[j], pl[i >> 1], o[dt]);
+                    }
+                    __builtin_amdgcn_sched_group_barrier(0x008, 2 * FV, 0);    // MFMAs
+                }
             }
         }
         if (t + NW < QT) {   // the next tile's operands, fetched while this tile's results drain
@@ -264,7 +278,34 @@ __global__ __launch_bounds__(64 * NW * HPW) void attn_partial_kernel(
             for (int ds = 0; ds < D / 32; ++ds) qf_next[ds] = *(const bf16x8 *)(qn + ds * 32 + grp * 8);
             am_next = anc[b * K + t2];
         }
-        if (col_ok) {
+        if constexpr (KS > 1) {
+            // the tile's key parts merged into part 0, in part order
+            const int slot0 = (hl * NW + tw) * (KS - 1);
+            if (kp > 0) {
+                const int sl = slot0 + kp - 1;
+#pragma unroll
+                for (int dt = 0; dt < D / 16; ++dt) mg_o[(sl * (D / 16) + dt) * 64 + lane] = o[dt];
+                mg_m[sl * 64 + lane] = mloc;
+                mg_l[sl * 64 + lane] = psum;
+            }
+            __syncthreads();
+            if (kp == 0 && has) {
+#pragma unroll
+                for (int k2 = 0; k2 < KS - 1; ++k2) {
+                    const int sl = slot0 + k2;
+                    const float mk = mg_m[sl * 64 + lane], lk = mg_l[sl * 64 + lane];
+                    if (mk == -INFINITY) continue;
+                    const float mn = fmaxf(mloc, mk);
+                    const float a0 = exp2f(mloc - mn), a1 = exp2f(mk - mn);
+                    psum = psum * a0 + lk * a1;
+#pragma unroll
+                    for (int dt = 0; dt < D / 16; ++dt) o[dt] = o[dt] * a0 + mg_o[(sl * (D / 16) + dt) * 64 + lane] * a1;
+                    mloc = mn;
+                }
+            }
+            __syncthreads();
+        }
+        if (kp == 0 && has && col_ok) {
             const int64_t base = (((int64_t)b * nkv + g) * n_chunks + c) * R + rho;
 #pragma unroll
             for (int dt = 0; dt < D / 16; ++dt)
@@ -627,14 +668,14 @@ __global__ __launch_bounds__(256) void attn_wave_kernel(
 }
 
 // Merge the partials of one (node, q head): o = sum_c 2^(m_c - m*) O_c / sum_c 2^(m_c - m*) l_c
-// over the partials c (one per chunk, or per range of cpr chunks). 256 threads = (D/4) column
+// over the partials c (one per chunk, or per range of chunks; kpp keys each). 256 threads = (D/4) column
 // quads x CG groups; each thread merges partials c = cg, cg + CG, ... with every load issued
 // before the arithmetic, then the CG states are merged in LDS in group order.
 template <int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(
     const float *__restrict__ part_o, const float2 *__restrict__ part_ml,
     const int32_t *__restrict__ ctx_len, const int32_t *__restrict__ status, int K, int nq,
-    int nkv, int n_chunks, int cpr, bf16 *__restrict__ out) {
+    int nkv, int n_chunks, int kpp, bf16 *__restrict__ out) {
     constexpr int TQ = D / 4;            // threads per column quad set
     constexpr int CG = 256 / TQ;         // chunk groups: 8 (D=128) or 16 (D=64)
     constexpr int PER = 8;               // chunks per thread held in flight
@@ -653,7 +694,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(
     }
     const int group = nq / nkv, g = h / group, hh = h % group;
     const int R = group * K, rho = hh * K + tok;
-    const int nc = ((ctx_len[b] + K + kAttnChunk - 1) / kAttnChunk + cpr - 1) / cpr;   // partials
+    const int nc = (ctx_len[b] + K + kpp - 1) / kpp;   // partials (kpp keys each)
     const int64_t base = ((int64_t)b * nkv + g) * n_chunks * R + rho;
     float m = -INFINITY, l = 0.f;
     floatx4 o = {0.f, 0.f, 0.f, 0.f};
@@ -706,7 +747,7 @@ template <int D>
 __global__ __launch_bounds__(256) void attn_combine_few_kernel(
     const float *__restrict__ part_o, const float2 *__restrict__ part_ml,
     const int32_t *__restrict__ ctx_len, const int32_t *__restrict__ status, int K, int nq,
-    int nkv, int stride, int cpr, int64_t total, bf16 *__restrict__ out) {
+    int nkv, int stride, int kpp, int64_t total, bf16 *__restrict__ out) {
     constexpr int NQD = D / 4;
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= total) return;
@@ -721,7 +762,7 @@ __global__ __launch_bounds__(256) void attn_combine_few_kernel(
     }
     const int group = nq / nkv, g = h / group, hh = h % group;
     const int R = group * K, rho = hh * K + tok;
-    const int nc = ((ctx_len[b] + K + kAttnChunk - 1) / kAttnChunk + cpr - 1) / cpr;
+    const int nc = (ctx_len[b] + K + kpp - 1) / kpp;   // partials (kpp keys each)
     const int64_t base = ((int64_t)b * nkv + g) * stride * R + rho;
     float m = -INFINITY, l = 0.f;
     floatx4 o = {0.f, 0.f, 0.f, 0.f};
@@ -747,13 +788,17 @@ __global__ __launch_bounds__(256) void attn_combine_few_kernel(
     store4(dst, o[0] / l, o[1] / l, o[2] / l, o[3] / l);
 }
 
-// Tunables: the largest chunk-kernel grid (workgroups) before the wave kernel takes over, and
-// a fixed chunk count per wave for the wave kernel (0: chosen per launch, below).
+// Tunables: the largest chunk-kernel grid (workgroups) before the wave kernel takes over, the
+// chunk kernel's keys per workgroup and waves per query tile, and a fixed chunk count per wave
+// for the wave kernel (0: chosen per launch, below).
 #ifndef SV_ATTN_SMALL_GRID
 #define SV_ATTN_SMALL_GRID 512
 #endif
-#ifndef SV_ATTN_HPW
-#define SV_ATTN_HPW 2                                   // kv heads per chunk-kernel workgroup
+#ifndef SV_ATTN_CH
+#define SV_ATTN_CH 192                                  // keys per chunk-kernel workgroup
+#endif
+#ifndef SV_ATTN_KS
+#define SV_ATTN_KS 1                                    // waves per query tile (key parts)
 #endif
 #ifndef SV_ATTN_CPW
 #define SV_ATTN_CPW 0
@@ -761,36 +806,38 @@ __global__ __launch_bounds__(256) void attn_combine_few_kernel(
 
 hipError_t attention(const AttnArgs &a, hipStream_t st) {
     const float scale_log2 = kLog2e / sqrtf((float)a.D);
-    // waves per kv head: 5 when that takes fewer query tiles per wave than 4 (one tile each for
-    // a group of 5 q heads and a block of 16), else 4
+    // tile slots per kv head: 5 when that takes fewer query tiles per slot than 4 (one tile each
+    // for a group of 5 q heads and a block of 16), else 4
     const int R = a.nq / a.nkv * a.K;
     const int QT = (R + 15) / 16;
     const int nw = (QT + 4) / 5 < (QT + 3) / 4 ? 5 : 4;
     const int n_tg = (QT + nw - 1) / nw;
-    // A small grid (one request, a short draft) runs one chunk per workgroup, two kv heads each,
-    // so that it is resident at once. A large one (a batch, or hundreds of query rows) streams
-    // ranges of chunks through LDS, one kv head per workgroup.
-    const int64_t wgs1 = (int64_t)a.n_chunks * a.nkv * a.B * n_tg;
-    int cpr = 1, stride = a.n_chunks;
+    // A small grid (one request, a short draft) runs one chunk of SV_ATTN_CH keys and one kv
+    // head per workgroup (one per compute unit: 176 at a 4096-token context and 8 kv heads,
+    // 13.5 us on the 27B block against 14.4 for 128-key chunks over two heads, which leave half
+    // the units idle, and 16.2 for 128-key chunks over one head, eight workgroups too many for one
+    // round; two waves per tile measured 14.6). A large one (a batch, or hundreds of query rows)
+    // streams ranges of chunks through LDS, one kv head per workgroup.
+    const int64_t max_keys = (int64_t)a.max_pages * kPage;
+    const int n_small = (int)((max_keys + SV_ATTN_CH - 1) / SV_ATTN_CH);
+    const int64_t wgs1 = (int64_t)n_small * a.nkv * a.B * n_tg;
+    int kpp = SV_ATTN_CH, stride = n_small;
+    bool few = false;                      // the wave kernel's few partials per (node, q head)
     hipError_t e;
-    if (wgs1 <= SV_ATTN_SMALL_GRID) {
-        const int hpw = a.nkv % SV_ATTN_HPW == 0 ? SV_ATTN_HPW : 1;
-        const dim3 grid_h(a.n_chunks, a.nkv / hpw, a.B);
-#define SV_ATTN(DD, NWV, HP)                                                                      \
-    hipLaunchKernelGGL((attn_partial_kernel<DD, NWV, HP>), grid_h, dim3(64 * NWV * HP), 0, st,    \
-                       a.q, a.k_pool, a.v_pool, a.block_table, a.max_pages, a.ctx_len, a.anc,      \
-                       a.status, a.K, a.nq, a.nkv, a.n_chunks, scale_log2, a.part_o, a.part_ml)
-#define SV_ATTN_H(DD, NWV)          \
-    if (hpw == 2) SV_ATTN(DD, NWV, 2); \
-    else SV_ATTN(DD, NWV, 1)
+    if (wgs1 <= SV_ATTN_SMALL_GRID && n_small <= a.n_chunks) {
+        const dim3 grid_h(n_small, a.nkv, a.B);
+#define SV_ATTN(DD, NWV)                                                                          \
+    hipLaunchKernelGGL((attn_partial_kernel<DD, NWV, 1, SV_ATTN_CH, SV_ATTN_KS>), grid_h,          \
+                       dim3(64 * NWV * SV_ATTN_KS), 0, st, a.q, a.k_pool, a.v_pool, a.block_table, \
+                       a.max_pages, a.ctx_len, a.anc, a.status, a.K, a.nq, a.nkv, n_small,         \
+                       scale_log2, a.part_o, a.part_ml)
         if (a.D == 128) {
-            if (nw == 4) { SV_ATTN_H(128, 4); }
-            else { SV_ATTN_H(128, 5); }
+            if (nw == 4) { SV_ATTN(128, 4); }
+            else { SV_ATTN(128, 5); }
         } else {
-            if (nw == 4) { SV_ATTN_H(64, 4); }
-            else { SV_ATTN_H(64, 5); }
+            if (nw == 4) { SV_ATTN(64, 4); }
+            else { SV_ATTN(64, 5); }
         }
-#undef SV_ATTN_H
 #undef SV_ATTN
     } else {
         // workgroups of four waves, 4 cpw chunks per workgroup (cpw per wave), one partial per
@@ -821,7 +868,8 @@ hipError_t attention(const AttnArgs &a, hipStream_t st) {
         }
         const int n_wr = (a.n_chunks + 4 * cpw - 1) / (4 * cpw);
         stride = n_wr;
-        cpr = 4 * cpw;                     // chunks per partial, for the combine
+        kpp = 4 * cpw * kAttnChunk;        // keys per partial, for the combine
+        few = true;
         const dim3 grid_w(n_wr, a.nkv * tgs, a.B);
 #define SV_WAVE(DD, TP)                                                                           \
     hipLaunchKernelGGL((attn_wave_kernel<DD, TP>), grid_w, dim3(256), 0, st, a.q, a.k_pool,        \
@@ -838,22 +886,22 @@ hipError_t attention(const AttnArgs &a, hipStream_t st) {
     }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (cpr > 1) {
+    if (few) {
         // the wave kernel's few partials per (node, q head)
         const int64_t total = (int64_t)a.B * a.K * a.nq * (a.D / 4);
         const dim3 grid_c((unsigned)((total + 255) / 256));
         if (a.D == 128)
             hipLaunchKernelGGL(attn_combine_few_kernel<128>, grid_c, dim3(256), 0, st, a.part_o,
-                               a.part_ml, a.ctx_len, a.status, a.K, a.nq, a.nkv, stride, cpr, total, a.out);
+                               a.part_ml, a.ctx_len, a.status, a.K, a.nq, a.nkv, stride, kpp, total, a.out);
         else
             hipLaunchKernelGGL(attn_combine_few_kernel<64>, grid_c, dim3(256), 0, st, a.part_o,
-                               a.part_ml, a.ctx_len, a.status, a.K, a.nq, a.nkv, stride, cpr, total, a.out);
+                               a.part_ml, a.ctx_len, a.status, a.K, a.nq, a.nkv, stride, kpp, total, a.out);
     } else if (a.D == 128) {
         hipLaunchKernelGGL(attn_combine_kernel<128>, dim3(a.B * a.K, a.nq), dim3(256), 0, st,
-                           a.part_o, a.part_ml, a.ctx_len, a.status, a.K, a.nq, a.nkv, stride, cpr, a.out);
+                           a.part_o, a.part_ml, a.ctx_len, a.status, a.K, a.nq, a.nkv, stride, kpp, a.out);
     } else {
         hipLaunchKernelGGL(attn_combine_kernel<64>, dim3(a.B * a.K, a.nq), dim3(256), 0, st,
-                           a.part_o, a.part_ml, a.ctx_len, a.status, a.K, a.nq, a.nkv, stride, cpr, a.out);
+                           a.part_o, a.part_ml, a.ctx_len, a.status, a.K, a.nq, a.nkv, stride, kpp, a.out);
     }
     return hipGetLastError();
 }
