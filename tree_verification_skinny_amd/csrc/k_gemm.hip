@@ -373,6 +373,9 @@ __global__ __launch_bounds__(64 * W) void gemm_kernel(GemmIn in, const bf16 *__r
 #define SV_TC_TARGET 512                                // workgroups a split tile launch aims at
 #endif
 constexpr int kPlanCUs = 256;                           // compute units of the target (MI355X)
+#ifndef SV_WIDE_PER_CU
+#define SV_WIDE_PER_CU 2
+#endif
 #ifndef SV_WIDE_KS
 #define SV_WIDE_KS 4
 #endif
@@ -776,15 +779,20 @@ GemmShape plan_gemm(int M, int N, int Kd, bool allow_split, bool allow_tc) {
         return g;
     }
     if (M > 16 && N % (16 * kWideWaves * kWideTN) == 0) {
-        // wide variant: 8 tiles per workgroup; split K (multiples of the slab where possible)
-        // until at least SV_WIDE_TARGET workgroups stream (320 and 4-step slabs measured best
-        // on the 64-node tree: 15.7 ms per step against 16.6 with 256 and 8-step slabs)
+        // wide variant: 8 tiles per workgroup; split K into as many parts as keep every compute
+        // unit at SV_WIDE_PER_CU workgroups at most (64-node tree: 14.75-14.84 ms per step at two
+        // per unit, 15.54 at one, 14.93 splitting to at least SV_WIDE_TARGET = 320 workgroups in
+        // whole slabs, the rule below when SV_WIDE_PER_CU is 0)
         g.wide = true;
         g.nt = kWideWaves * kWideTN;
         g.waves = kWideWaves;
         const int groups = N / (16 * g.nt);
         g.splits = 1;
-        if (allow_split && groups < 256) {
+        if (SV_WIDE_PER_CU > 0 && allow_split && groups < kPlanCUs * SV_WIDE_PER_CU) {
+            g.splits = kPlanCUs * SV_WIDE_PER_CU / groups;
+            if (g.splits > 32) g.splits = 32;
+            while (g.splits > 1 && steps / g.splits < kWideKS) --g.splits;
+        } else if (allow_split && groups < 256) {
             int best = 0;
             for (int sp = 2; sp <= 32 && sp <= steps; ++sp) {
                 if (steps % sp != 0 || (steps / sp) % kWideKS != 0) continue;
