@@ -106,6 +106,9 @@ def lib():
                                    ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, _f64p, _i32p]
         L.orc_rec_commit.argtypes = [_f32p, _u16p, _u16p, _f32p, _i32p, _i32p, ctypes.c_int,
                                      ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, _f64p]
+        L.orc_rec_layer_forward.argtypes = [ctypes.POINTER(_Cfg), ctypes.POINTER(_LayerW), _f32p, _i32p,
+                                            ctypes.c_int, _u16p, _u16p, _u16p, _f32p]
+        L.orc_rec_layer_forward.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -175,14 +178,20 @@ class Cfg:
 LAYER_KEYS = ("attn_norm", "w_qkv", "w_o", "mlp_norm", "w_gate_up", "w_down")
 
 
+ATTENTION, RECURRENT = 0, 1
+
+
 class Model:
     """Weights as numpy uint16 (bf16 bits). ``layer_fn(l)`` returns layer l's dict, so a large
-    model can be streamed one layer at a time instead of held whole."""
+    model can be streamed one layer at a time instead of held whole. ``kinds``: per layer,
+    ATTENTION (default) or RECURRENT (a hybrid target; see rec_layer_forward)."""
 
     def __init__(self, cfg: Cfg, embed: np.ndarray, final_norm: np.ndarray, lm_head: np.ndarray,
                  layers: Optional[Sequence[dict]] = None,
-                 layer_fn: Optional[Callable[[int], dict]] = None):
+                 layer_fn: Optional[Callable[[int], dict]] = None,
+                 kinds: Optional[Sequence[int]] = None):
         self.cfg = cfg
+        self.kinds = [ATTENTION] * cfg.n_layers if kinds is None else [int(k) for k in kinds]
         self.embed = _c(embed, np.uint16)
         self.final_norm = _c(final_norm, np.uint16)
         self.lm_head = _c(lm_head, np.uint16)
@@ -298,6 +307,28 @@ def layer_forward(cfg: Cfg, lw: dict, k_ctx: np.ndarray, v_ctx: np.ndarray, pare
     return x, k_new, v_new
 
 
+def rec_layer_forward(cfg: Cfg, lw: dict, S0: np.ndarray, parent: np.ndarray, x: np.ndarray):
+    """One recurrent layer of a hybrid target over the m nodes of a draft tree (the reading is
+    written out in specverify_oracle.c): lw["w_qkv"] holds 3 nh d + nh rows (q, k, v heads, then
+    one gate row per head; nh = n_q_heads), S0 the committed state fp32 [nh][d][d]. Returns
+    (x_out, k [m][nh][d] bf16 bits, v [m][nh][d], g [m][nh] fp32 log-gates)."""
+    nh, d = cfg.n_q_heads, cfg.head_dim
+    S0 = _c(S0, np.float32).reshape(nh, d, d)
+    parent = _c(parent, np.int32)
+    x = np.array(x, dtype=np.uint16, copy=True, order="C")
+    m = x.shape[0]
+    k = np.empty((m, nh, d), np.uint16)
+    v = np.empty((m, nh, d), np.uint16)
+    g = np.empty((m, nh), np.float32)
+    c = cfg.c()
+    s = _layer_struct(lw)
+    rc = lib().orc_rec_layer_forward(ctypes.byref(c), ctypes.byref(s), _p(S0, _f32p), _p(parent, _i32p), m,
+                                     _p(x, _u16p), _p(k, _u16p), _p(v, _u16p), _p(g, _f32p))
+    if rc != 0:
+        raise ValueError("malformed draft tree")
+    return x, k, v, g
+
+
 def logits(model: Model, x: np.ndarray) -> np.ndarray:
     x = _c(x, np.uint16)
     m = x.shape[0]
@@ -344,33 +375,40 @@ class VerifyResult:
     accepted_len: int
     bonus: int
     path: np.ndarray            # int32 [k], -1 after the end
-    k_new: List[np.ndarray]     # per layer [k][nkv][d]
+    k_new: List[np.ndarray]     # per layer [k][nkv][d] (recurrent layers: [k][nh][d])
     v_new: List[np.ndarray]
     hidden: List[np.ndarray]    # residual stream entering each layer, and after the last
+    g_new: Optional[List] = None   # per layer: recurrent log-gates [k][nh] fp32, else None
 
 
 def verify(model: Model, k_ctx: Sequence[np.ndarray], v_ctx: Sequence[np.ndarray],
            tokens: np.ndarray, parent: Optional[np.ndarray] = None,
-           keep_hidden: bool = False) -> VerifyResult:
+           keep_hidden: bool = False, state: Optional[Sequence] = None) -> VerifyResult:
     """One verification pass of one request: the draft tree (node 0 = root, the last committed
     token) scored in one target pass over the committed context, then the acceptance walk.
-    ``k_ctx[l]``/``v_ctx[l]``: layer l's committed cache [ctx][nkv][d]."""
+    ``k_ctx[l]``/``v_ctx[l]``: layer l's committed cache [ctx][nkv][d]; for a recurrent layer
+    of a hybrid target ``state[l]`` is its committed state fp32 [nh][d][d] instead."""
     cfg = model.cfg
     tokens = _c(tokens, np.int32)
     parent = chain(tokens.size) if parent is None else _c(parent, np.int32)
     x = embed(model, tokens)
     hidden = [x.copy()] if keep_hidden else []
-    k_new, v_new = [], []
+    k_new, v_new, g_new = [], [], []
     for l in range(cfg.n_layers):
-        x, kn, vn = layer_forward(cfg, model.layer(l), k_ctx[l], v_ctx[l], parent, x)
+        if model.kinds[l] == RECURRENT:
+            x, kn, vn, gn = rec_layer_forward(cfg, model.layer(l), state[l], parent, x)
+        else:
+            x, kn, vn = layer_forward(cfg, model.layer(l), k_ctx[l], v_ctx[l], parent, x)
+            gn = None
         k_new.append(kn)
         v_new.append(vn)
+        g_new.append(gn)
         if keep_hidden:
             hidden.append(x.copy())
     lg = logits(model, x)
     arg, margin = argmax(lg)
     a, b, path = accept(tokens, parent, arg)
-    return VerifyResult(lg, arg, margin, a, b, path, k_new, v_new, hidden)
+    return VerifyResult(lg, arg, margin, a, b, path, k_new, v_new, hidden, g_new)
 
 
 def prefill(model: Model, prompt: np.ndarray, k_ctx=None, v_ctx=None):
@@ -388,13 +426,56 @@ def prefill(model: Model, prompt: np.ndarray, k_ctx=None, v_ctx=None):
 
 
 def commit(k_ctx, v_ctx, r: VerifyResult):
-    """Append the accepted path's K/V rows (root first) to each layer's committed cache."""
+    """Append the accepted path's K/V rows (root first) to each attention layer's committed
+    cache (a recurrent layer's cache, which holds no rows, is left as it is; see commit_rec)."""
     if r.accepted_len < 0:
         return list(k_ctx), list(v_ctx)
     sel = r.path[: r.accepted_len + 1]
-    k_out = [np.concatenate([k_ctx[l], r.k_new[l][sel]], 0) for l in range(len(k_ctx))]
-    v_out = [np.concatenate([v_ctx[l], r.v_new[l][sel]], 0) for l in range(len(v_ctx))]
+    rec = [r.g_new is not None and r.g_new[l] is not None for l in range(len(k_ctx))]
+    k_out = [k_ctx[l] if rec[l] else np.concatenate([k_ctx[l], r.k_new[l][sel]], 0) for l in range(len(k_ctx))]
+    v_out = [v_ctx[l] if rec[l] else np.concatenate([v_ctx[l], r.v_new[l][sel]], 0) for l in range(len(v_ctx))]
     return k_out, v_out
+
+
+def commit_rec(model: Model, state: Sequence, r: VerifyResult) -> list:
+    """Each recurrent layer's committed state after the accepted path (root first) of ``r``,
+    stored in fp32 as the state is kept between passes; unchanged for a failed request (None
+    for attention layers)."""
+    out = []
+    K = r.path.size
+    al = np.array([r.accepted_len], np.int32)
+    ap = np.array(r.path, np.int32).reshape(1, K)
+    for l in range(model.cfg.n_layers):
+        if model.kinds[l] != RECURRENT:
+            out.append(None)
+            continue
+        nh, d = model.cfg.n_q_heads, model.cfg.head_dim
+        S0 = _c(state[l], np.float32).reshape(1, nh, d, d)
+        S = rec_commit(S0, r.k_new[l][None], r.v_new[l][None], r.g_new[l][None], al, ap)
+        out.append(S[0].astype(np.float32))
+    return out
+
+
+def ar_greedy_hybrid(model: Model, k_ctx, v_ctx, state, first_token: int, n: int):
+    """Greedy decoding of a hybrid target one token per pass, each pass committing its token:
+    the K/V row of every attention layer, the fp32 state of every recurrent layer. Returns the n
+    greedy tokens after ``first_token``, the logits of each pass, and the caches and states."""
+    toks, lgs = [], []
+    tok = int(first_token)
+    k_ctx, v_ctx, state = list(k_ctx), list(v_ctx), list(state)
+    for _ in range(n):
+        r = verify(model, k_ctx, v_ctx, np.array([tok], np.int32), np.array([-1], np.int32), state=state)
+        st = commit_rec(model, state, r)
+        for l in range(model.cfg.n_layers):
+            if model.kinds[l] == RECURRENT:
+                state[l] = st[l]
+            else:
+                k_ctx[l] = np.concatenate([k_ctx[l], r.k_new[l]], 0)
+                v_ctx[l] = np.concatenate([v_ctx[l], r.v_new[l]], 0)
+        lgs.append(r.logits[0])
+        tok = int(r.arg[0])
+        toks.append(tok)
+    return np.array(toks, np.int32), np.stack(lgs), k_ctx, v_ctx, state
 
 
 def ar_greedy(model: Model, k_ctx, v_ctx, first_token: int, n: int):

@@ -255,6 +255,23 @@ static void residual_add(uint16_t *x, const float *y, int64_t n) {
 /* One decoder layer over the m draft nodes of one request                                    */
 /* ------------------------------------------------------------------------------------------ */
 
+/* The MLP block: x += W_down . swiglu(gate, up), [gate | up] = RMSNorm(x) * mlp_norm . W_gate_up.
+ * u [m][H], y [m][max(2F, H)], gate, up, hm [m][F]: scratch. */
+static void mlp_block(const orc_cfg *c, const orc_layer_w *w, int m, uint16_t *x, uint16_t *u,
+                      float *y, uint16_t *gate, uint16_t *up, uint16_t *hm) {
+    int H = c->hidden, F = c->ffn;
+    orc_rmsnorm(x, w->mlp_norm, m, H, c->rms_eps, u);
+    orc_linear(u, m, H, w->w_gate_up, 2 * F, y);
+    for (int i = 0; i < m; ++i)
+        for (int j = 0; j < F; ++j) {
+            gate[(int64_t)i * F + j] = f32_to_bf16(y[(int64_t)i * 2 * F + j]);
+            up[(int64_t)i * F + j] = f32_to_bf16(y[(int64_t)i * 2 * F + F + j]);
+        }
+    orc_swiglu(gate, up, (int64_t)m * F, hm);
+    orc_linear(hm, m, F, w->w_down, H, y);
+    residual_add(x, y, (int64_t)m * H);
+}
+
 /* x: [m][H] residual stream in/out. k_ctx, v_ctx: this layer's committed cache [ctx][nkv][d].
  * k_new, v_new: [m][nkv][d] out, the draft nodes' rotated keys and their values, node order.
  * Node i sits at position ctx + depth(i). Returns 0, or -1 for a malformed tree. */
@@ -300,17 +317,7 @@ int orc_layer_forward(const orc_cfg *c, const orc_layer_w *w, const uint16_t *k_
     orc_linear(o, m, nq * d, w->w_o, H, y);
     residual_add(x, y, (int64_t)m * H);
 
-    /* MLP block */
-    orc_rmsnorm(x, w->mlp_norm, m, H, c->rms_eps, u);
-    orc_linear(u, m, H, w->w_gate_up, 2 * F, y);
-    for (int i = 0; i < m; ++i)
-        for (int j = 0; j < F; ++j) {
-            gate[(int64_t)i * F + j] = f32_to_bf16(y[(int64_t)i * 2 * F + j]);
-            up[(int64_t)i * F + j] = f32_to_bf16(y[(int64_t)i * 2 * F + F + j]);
-        }
-    orc_swiglu(gate, up, (int64_t)m * F, hm);
-    orc_linear(hm, m, F, w->w_down, H, y);
-    residual_add(x, y, (int64_t)m * H);
+    mlp_block(c, w, m, x, u, y, gate, up, hm);
 
     free(depth); free(pos); free(u); free(y); free(q); free(o); free(gate); free(up); free(hm);
     return 0;
@@ -563,4 +570,71 @@ void orc_rec_commit(const float *S0, const uint16_t *kk, const uint16_t *v, cons
             rec_run(S0, kk, v, g, K, H, dk, dv, b, h, pth, n, S_out + ((int64_t)b * H + h) * dk * dv);
             free(pth);
         }
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* A recurrent layer of a hybrid target                                                       */
+/* ------------------------------------------------------------------------------------------ */
+/* The pages name targets that mix recurrent layers in (SpecPilot digest, airadar.tv —
+ * "Reasons") but give neither the recurrence nor the layer around it. The reading used here: the
+ * attention mixer of a decoder layer is replaced by the scalar-gated recurrence above, with
+ * nh = n_q_heads heads of d = head_dim:
+ *   u = RMSNorm(x) * attn_norm;
+ *   [q | k | v | a] = u . W^T, W = w_qkv with 3 nh d + nh rows (q heads, k heads, v heads, then
+ *   one gate row per head), each rounded to bf16 like every projection output;
+ *   g = -softplus(a) = -log(1 + e^a) per (node, head), in fp32 (a > 20: -a);
+ *   o = S_i^T q for each node i, S_i the state after the root path of node i applied to the
+ *   committed state S0 (see orc_rec_tree), rounded to fp32, then to bf16;
+ *   x += o . W_o^T (w_o [H][nh d]), then the MLP block.
+ * No position enters the recurrent layer (no RoPE). */
+static float neg_softplus(float a) { return a > 20.0f ? -a : -log1pf(expf(a)); }
+
+/* x [m][H] in/out; S0 [nh][d][d] fp32 (S[r][c]: key index r, value index c), read only;
+ * k_out, v_out [m][nh][d] bf16 and g_out [m][nh] fp32: the nodes' keys, values and log-gates
+ * (what a commit applies to the state). Returns 0, or -1 for a malformed tree. */
+int orc_rec_layer_forward(const orc_cfg *c, const orc_layer_w *w, const float *S0,
+                          const int32_t *parent, int m, uint16_t *x, uint16_t *k_out,
+                          uint16_t *v_out, float *g_out) {
+    int H = c->hidden, nh = c->n_q_heads, d = c->head_dim, F = c->ffn;
+    int nrow = 3 * nh * d + nh;
+    int32_t *depth = (int32_t *)malloc(sizeof(int32_t) * (size_t)m);
+    if (orc_tree_depth(parent, m, depth) != 0) {
+        free(depth);
+        return -1;
+    }
+    int ywidth = nrow;
+    if (2 * F > ywidth) ywidth = 2 * F;
+    if (H > ywidth) ywidth = H;
+    uint16_t *u = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)m * H);
+    float *y = (float *)malloc(sizeof(float) * (size_t)m * ywidth);
+    uint16_t *q = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)m * nh * d);
+    uint16_t *o = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)m * nh * d);
+    double *o64 = (double *)malloc(sizeof(double) * (size_t)m * nh * d);
+    int32_t st = 0;
+    uint16_t *gate = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)m * F);
+    uint16_t *up = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)m * F);
+    uint16_t *hm = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)m * F);
+
+    /* recurrent mixer */
+    orc_rmsnorm(x, w->attn_norm, m, H, c->rms_eps, u);
+    orc_linear(u, m, H, w->w_qkv, nrow, y);
+    for (int i = 0; i < m; ++i) {
+        const float *yi = y + (int64_t)i * nrow;
+        for (int j = 0; j < nh * d; ++j) {
+            q[(int64_t)i * nh * d + j] = f32_to_bf16(yi[j]);
+            k_out[(int64_t)i * nh * d + j] = f32_to_bf16(yi[nh * d + j]);
+            v_out[(int64_t)i * nh * d + j] = f32_to_bf16(yi[2 * nh * d + j]);
+        }
+        for (int h = 0; h < nh; ++h)
+            g_out[(int64_t)i * nh + h] = neg_softplus(bf16_to_f32(f32_to_bf16(yi[3 * nh * d + h])));
+    }
+    orc_rec_tree(S0, q, k_out, v_out, g_out, parent, 1, m, nh, d, d, o64, &st);
+    for (int64_t e = 0; e < (int64_t)m * nh * d; ++e) o[e] = f32_to_bf16((float)o64[e]);
+    orc_linear(o, m, nh * d, w->w_o, H, y);
+    residual_add(x, y, (int64_t)m * H);
+
+    mlp_block(c, w, m, x, u, y, gate, up, hm);
+
+    free(depth); free(u); free(y); free(q); free(o); free(o64); free(gate); free(up); free(hm);
+    return 0;
 }

@@ -109,6 +109,42 @@ def model_weights(shape: Shape, seed: int, device="cpu", std: float = 0.02,
     }
 
 
+# A hybrid target: the tiny shape with 4 layers, attention and recurrent layers alternating.
+HYBRID_TINY = TINY.with_layers(4)
+HYBRID_KINDS = (0, 1, 0, 1)          # 0: attention layer, 1: recurrent layer
+
+
+def rec_layer_weights(shape: Shape, seed: int, layer: int, device="cpu", std: float = 0.02,
+                      gate_std: float = 0.2, pad16: bool = False):
+    """A recurrent layer's weights: w_qkv has 3 nh d q/k/v rows (nh = n_q_heads, d = head_dim)
+    ~ N(0, std^2) and nh gate rows ~ N(0, gate_std^2) (with a unit-RMS operand the gate input then
+    spreads over about +-6, decays from ~1 to ~e^-6 per token); with pad16 zero rows follow up to
+    a multiple of 16 (the packed layout). The other matrices as an attention layer's."""
+    H, F, nh, d = shape.hidden, shape.ffn, shape.n_q_heads, shape.head_dim
+    out = {}
+    for name, shp in shape.layer_shapes().items():
+        if name.endswith("norm"):
+            out[name] = torch.ones(shp, dtype=torch.bfloat16, device=device)
+        elif name == "w_qkv":
+            qkv = randn_bf16((3 * nh * d, H), std, device, seed, "rec_layer", layer, "w_qkv")
+            gate = randn_bf16((nh, H), gate_std, device, seed, "rec_layer", layer, "w_gate")
+            rows = [qkv, gate]
+            n = 3 * nh * d + nh
+            if pad16 and n % 16:
+                rows.append(torch.zeros((16 - n % 16, H), dtype=torch.bfloat16, device=device))
+            out[name] = torch.cat(rows, 0)
+        else:
+            out[name] = randn_bf16(shp, std, device, seed, "rec_layer", layer, name)
+    return out
+
+
+def rec_state(shape: Shape, seed: int, layer: int, requests: int = 1, device="cpu"):
+    """Committed state of a recurrent layer, fp32 [requests][nh][d][d] ~ N(0, 1/4)."""
+    g = _gen(device, seed, "rec_layer_state", layer)
+    nh, d = shape.n_q_heads, shape.head_dim
+    return torch.randn((requests, nh, d, d), generator=g, device=device, dtype=torch.float32).mul_(0.5)
+
+
 def kv_context(shape: Shape, ctx: int, seed: int, layer: int, device="cpu", request: int = 0):
     """Committed K and V for one layer of one request: [ctx][n_kv][head_dim], N(0, 1) bf16."""
     s = (ctx, shape.n_kv_heads, shape.head_dim)
