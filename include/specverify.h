@@ -101,7 +101,20 @@ typedef struct {
      * otherwise). The results are bit-identical to the bf16 pass over the same weights. */
     const spec_w12_layer *w12_layers;
     spec_w12_matrix w12_lm_head;
+    /* Hybrid targets: HOST array of cfg.n_layers entries, or NULL (every layer attention).
+     * SPEC_LAYER_RECURRENT marks a layer whose attention mixer is replaced by the gated linear
+     * recurrence of spec_rec_tree_verify (the reading below, "Recurrent layers"): its w_qkv is
+     * [R][H] packed, R = 3 nq d + nq rounded up to a multiple of 16, rows = q heads, k heads,
+     * v heads (nq = n_q_heads each), one gate row per head, then zero rows; its w_o [H][nq d];
+     * the other members as an attention layer's. Per head: g = -softplus(bf16(gate input)) in
+     * fp32 (-a above a = 20), S <- e^g S + k v^T along each node's root path from the committed
+     * state, o = S^T q rounded to bf16, x += o . W_o^T. No RoPE, no cache rows. Recurrent layers
+     * need bf16 weights (no W12) and the per-step plan. */
+    const int32_t *layer_kind;
 } spec_weights;
+
+#define SPEC_LAYER_ATTENTION 0
+#define SPEC_LAYER_RECURRENT 1
 
 /* Paged KV cache, bf16. A page holds SPEC_PAGE_SIZE consecutive positions of one request.
  *   k_pool [n_layers][n_pages][n_kv_heads][16][head_dim]   (keys, one row per position)
@@ -114,6 +127,18 @@ typedef struct {
     const int32_t *block_table;
     int n_pages;
     int max_pages_per_req;
+    /* Recurrent layers of a hybrid target (all NULL for a dense one):
+     *   rec_state: HOST array of n_layers DEVICE pointers; for a recurrent layer l the committed
+     *   state fp32 [batch][nq][d][d], each head's S stored transposed as spec_rec_tree_verify
+     *   reads it; NULL for attention layers. spec_verify reads it; spec_commit_kv advances it.
+     *   rec_k, rec_v (bf16) [n_layers][batch][k][nq][d] and rec_g (fp32) [n_layers][batch][k][nq]:
+     *   written by spec_verify for each recurrent layer (that pass's keys, values and log-gates,
+     *   node order), read by spec_commit_kv with the same batch and k. The page pools keep their
+     *   n_layers layout; a recurrent layer's pages hold no rows. */
+    float *const *rec_state;
+    void *rec_k;
+    void *rec_v;
+    float *rec_g;
 } spec_kv_cache;
 
 /* Optional extra outputs of spec_verify (any member may be NULL; the struct pointer too). */
@@ -180,6 +205,10 @@ int spec_workspace_bytes(const spec_model_cfg *cfg, int batch, int k, int max_pa
  *       last node; accepted_path [batch][k]: node ids of that path from the root, then -1.
  *   Equal-depth accepted nodes (possible only with duplicate sibling tokens) resolve to the
  *   lowest node id. Arithmetic: bf16 storage between steps, fp32 accumulation and softmax.
+ * Hybrid targets (weights->layer_kind marks recurrent layers): each recurrent layer reads its
+ *   committed state from kv->rec_state and writes the pass's keys, values and log-gates to
+ *   kv->rec_k / rec_v / rec_g (no cache rows); SPEC_EINVAL when those are missing,
+ *   SPEC_EUNSUPPORTED with W12 weights or the persistent plan.
  * Shapes: 1 <= k <= SPEC_MAX_K; batch >= 1. */
 int spec_verify(const spec_weights *weights, const spec_kv_cache *kv,
                 const int32_t *draft_tokens, const int32_t *tree_parent, const int32_t *ctx_len,
@@ -202,8 +231,12 @@ int spec_verify(const spec_weights *weights, const spec_kv_cache *kv,
  * ids. Any other request (e.g. accepted_len = -1 from a failed verify) keeps its rows and its
  * ctx_len. Device pointers: accepted_len [batch], accepted_path [batch][k], ctx_len [batch]
  * (in/out). Takes the outputs of spec_verify on the same stream; k and batch as given to it.
- * Host-side errors (NULL pointers, batch or k < 1, k > SPEC_MAX_K, a bad cfg) return before
- * anything is enqueued. */
+ * Hybrid targets (kv->rec_state set): each recurrent layer's state then becomes the state after
+ * the accepted path, applied from the committed one with that pass's kv->rec_k, rec_v and rec_g
+ * (spec_rec_commit's rule: 0 <= accepted_len < k and node ids in [0, k), else the state is
+ * kept; a request that failed in spec_verify has accepted_len -1 and keeps both).
+ * Host-side errors (NULL pointers, batch or k < 1, k > SPEC_MAX_K, a bad cfg, a recurrent
+ * state without the pass's buffers) return before anything is enqueued. */
 int spec_commit_kv(const spec_model_cfg *cfg, const spec_kv_cache *kv,
                    const int32_t *accepted_len, const int32_t *accepted_path, int32_t *ctx_len,
                    int batch, int k, hipStream_t stream);

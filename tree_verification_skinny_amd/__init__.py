@@ -67,13 +67,14 @@ class WeightsC(ctypes.Structure):
     _fields_ = [("cfg", ModelCfgC), ("layers", ctypes.POINTER(LayerWeightsC)),
                 ("embed", ctypes.c_void_p), ("final_norm", ctypes.c_void_p),
                 ("lm_head", ctypes.c_void_p), ("w12_layers", ctypes.POINTER(W12LayerC)),
-                ("w12_lm_head", W12MatrixC)]
+                ("w12_lm_head", W12MatrixC), ("layer_kind", ctypes.c_void_p)]
 
 
 class KVCacheC(ctypes.Structure):
     _fields_ = [("k_pool", ctypes.c_void_p), ("v_pool", ctypes.c_void_p),
                 ("block_table", ctypes.c_void_p), ("n_pages", ctypes.c_int),
-                ("max_pages_per_req", ctypes.c_int)]
+                ("max_pages_per_req", ctypes.c_int), ("rec_state", ctypes.c_void_p),
+                ("rec_k", ctypes.c_void_p), ("rec_v", ctypes.c_void_p), ("rec_g", ctypes.c_void_p)]
 
 
 class ExtrasC(ctypes.Structure):
@@ -244,10 +245,12 @@ class Weights:
 
     def __init__(self, cfg: ModelCfg, embed: torch.Tensor, final_norm: torch.Tensor,
                  lm_head: torch.Tensor, layers: Sequence[dict], packed: bool = False,
-                 drop_rowmajor: bool = False, w12: bool = False):
+                 drop_rowmajor: bool = False, w12: bool = False, kinds: Optional[Sequence[int]] = None):
         if len(layers) != cfg.n_layers:
             raise ValueError("need one weight dict per layer")
         self.cfg = cfg
+        # hybrid targets: SPEC_LAYER_ATTENTION / SPEC_LAYER_RECURRENT per layer (host array)
+        self.kinds = None if kinds is None else (ctypes.c_int32 * cfg.n_layers)(*[int(k) for k in kinds])
         self.rowmajor = None
         self.w12 = None
         self._w12_layers = None
@@ -276,7 +279,8 @@ class Weights:
         w12p = (ctypes.cast(self._w12_layers, ctypes.POINTER(W12LayerC)) if self._w12_layers is not None
                 else None)
         self.c = WeightsC(cfg.c(), ctypes.cast(self._layers, ctypes.POINTER(LayerWeightsC)),
-                          _ptr(embed), _ptr(final_norm), _ptr(lm_head), w12p, w12_head)
+                          _ptr(embed), _ptr(final_norm), _ptr(lm_head), w12p, w12_head,
+                          None if self.kinds is None else ctypes.cast(self.kinds, ctypes.c_void_p))
 
     @staticmethod
     def from_packed(cfg: ModelCfg, embed, final_norm, lm_head_packed, layers_packed) -> "Weights":
@@ -292,7 +296,24 @@ class PagedKV:
         self.block_table = block_table.to(torch.int32).contiguous()
         self.n_pages = k_pool.shape[1]
         self.max_pages = self.block_table.shape[1]
-        self.c = KVCacheC(_ptr(k_pool), _ptr(v_pool), _ptr(self.block_table), self.n_pages, self.max_pages)
+        self.c = KVCacheC(_ptr(k_pool), _ptr(v_pool), _ptr(self.block_table), self.n_pages, self.max_pages,
+                          None, None, None, None)
+
+    def attach_rec(self, cfg: ModelCfg, states: Sequence[Optional[torch.Tensor]], batch: int, k: int):
+        """Recurrent layers of a hybrid target: ``states[l]`` layer l's committed state, fp32
+        [batch][nq][d][d] with each head's S stored transposed (None for attention layers); the
+        buffers spec_verify fills with each pass's keys, values and log-gates and spec_commit_kv
+        applies (for this batch and k)."""
+        L, nq, d = cfg.n_layers, cfg.n_q_heads, cfg.head_dim
+        dev = self.k_pool.device
+        self.rec_states = list(states)
+        self._rec_ptrs = (ctypes.c_void_p * L)(*[_ptr(t) if t is not None else None for t in states])
+        self.rec_k = torch.zeros((L, batch, k, nq, d), dtype=torch.bfloat16, device=dev)
+        self.rec_v = torch.zeros((L, batch, k, nq, d), dtype=torch.bfloat16, device=dev)
+        self.rec_g = torch.zeros((L, batch, k, nq), dtype=torch.float32, device=dev)
+        self.c.rec_state = ctypes.cast(self._rec_ptrs, ctypes.c_void_p)
+        self.c.rec_k, self.c.rec_v, self.c.rec_g = _ptr(self.rec_k), _ptr(self.rec_v), _ptr(self.rec_g)
+        return self
 
     @staticmethod
     def empty(cfg: ModelCfg, n_pages: int, block_table: torch.Tensor, device) -> "PagedKV":

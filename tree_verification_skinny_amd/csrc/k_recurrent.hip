@@ -299,4 +299,76 @@ hipError_t rec_tree(const float *state, const bf16 *q, const bf16 *k, const bf16
     return hipGetLastError();
 }
 
+// ---- a recurrent layer inside the verify pass ------------------------------------------------
+// The layer's projection leaves split-K partials P [splits][M][N] of [q | k | v | a] (N columns:
+// q, k, v heads of D, then one gate input per head, then padding). One workgroup per (row,
+// head), thread j takes dim j: the splits added in order, q, k, v rounded to bf16 ([M][H][D]),
+// and the head's log-gate g = -softplus(bf16(a)) in fp32 (-a above a = 20), [M][H].
+template <int SP>
+__global__ void reduce_rec_kernel(const float *__restrict__ P, int splits, int M, int N, int H, int D,
+                                  bf16 *__restrict__ q, bf16 *__restrict__ k, bf16 *__restrict__ v,
+                                  float *__restrict__ g) {
+    const int m = blockIdx.x, h = blockIdx.y, j = threadIdx.x;
+    const int64_t pstride = (int64_t)M * N;
+    const float *pr = P + (int64_t)m * N;
+    const int cq = h * D + j, ck = H * D + cq, cv = 2 * H * D + cq, ca = 3 * H * D + h;
+    float sq = 0.f, sk = 0.f, sv = 0.f, sa = 0.f;
+    for (int s0 = 0; s0 < splits; s0 += SP) {
+        float vq[SP], vk[SP], vv[SP], va[SP];
+#pragma unroll
+        for (int t = 0; t < SP; ++t) {
+            const int s = s0 + t < splits ? s0 + t : splits - 1;
+            vq[t] = pr[s * pstride + cq];
+            vk[t] = pr[s * pstride + ck];
+            vv[t] = pr[s * pstride + cv];
+            va[t] = j == 0 ? pr[s * pstride + ca] : 0.f;
+        }
+#pragma unroll
+        for (int t = 0; t < SP; ++t) {
+            const bool use = s0 + t < splits;
+            sq = use ? sq + vq[t] : sq;
+            sk = use ? sk + vk[t] : sk;
+            sv = use ? sv + vv[t] : sv;
+            sa = use ? sa + va[t] : sa;
+        }
+    }
+    const int64_t o = ((int64_t)m * H + h) * D + j;
+    q[o] = to_bf(sq);
+    k[o] = to_bf(sk);
+    v[o] = to_bf(sv);
+    if (j == 0) {
+        const float a = round_bf(sa);
+        g[(int64_t)m * H + h] = a > 20.0f ? -a : -log1pf(expf(a));
+    }
+}
+
+hipError_t reduce_rec(const float *P, int splits, int M, int N, int H, int D, bf16 *q, bf16 *k, bf16 *v,
+                      float *g, hipStream_t st) {
+    const dim3 grid((unsigned)M, (unsigned)H);
+#define SV_RREC(SP) hipLaunchKernelGGL(reduce_rec_kernel<SP>, grid, dim3(D), 0, st, P, splits, M, N, H, D, q, k, v, g)
+    if (splits <= 1) SV_RREC(1);
+    else if (splits <= 2) SV_RREC(2);
+    else if (splits <= 4) SV_RREC(4);
+    else SV_RREC(8);
+#undef SV_RREC
+    return hipGetLastError();
+}
+
+// The tree pass's fp32 output [M][W] (W = H D) rounded to bf16 into the O projection's operand,
+// fragment order (frag_off); one thread per 4 consecutive values.
+__global__ __launch_bounds__(256) void rec_operand_kernel(const float *__restrict__ out, int M, int W,
+                                                          bf16 *__restrict__ x) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)M * (W / 4)) return;
+    const int m = (int)(i / (W / 4)), c = (int)(i % (W / 4)) * 4;
+    const floatx4 o = *(const floatx4 *)(out + (int64_t)m * W + c);
+    store4(x + frag_off(m, c, W), o[0], o[1], o[2], o[3]);
+}
+
+hipError_t rec_operand(const float *out, int M, int W, bf16 *x, hipStream_t st) {
+    const int64_t n = (int64_t)M * (W / 4);
+    hipLaunchKernelGGL(rec_operand_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, out, M, W, x);
+    return hipGetLastError();
+}
+
 }  // namespace sv

@@ -145,6 +145,13 @@ hipError_t rec_tree(const float *state, const bf16 *q, const bf16 *k, const bf16
 hipError_t rec_commit(float *state, const bf16 *k, const bf16 *v, const float *log_gate,
                       const int32_t *accepted_len, const int32_t *accepted_path, int B, int K, int H,
                       int D, hipStream_t st);
+// A recurrent layer inside the verify pass: its projection's split-K partials [splits][M][N]
+// (N >= 3 H D + H: q, k, v heads, then the gate inputs) to q, k, v bf16 [M][H][D] and the
+// log-gates g = -softplus(bf16(a)) fp32 [M][H]; the tree pass's fp32 output [M][W] to the O
+// projection's bf16 operand in fragment order.
+hipError_t reduce_rec(const float *P, int splits, int M, int N, int H, int D, bf16 *q, bf16 *k, bf16 *v,
+                      float *g, hipStream_t st);
+hipError_t rec_operand(const float *out, int M, int W, bf16 *x, hipStream_t st);
 // ---- the persistent pass over the layers for at most 16 rows (k_fused.hip) ------------------------
 constexpr int kFusedMaxLayers = 16;    // layers per launch (their weights ride in the arguments)
 // Phase timestamps per (layer, workgroup): QKV wait begin, inputs ready, loop end, done (0-3),

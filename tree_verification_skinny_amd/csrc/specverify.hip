@@ -31,11 +31,13 @@ struct Plan {
     int L, H, nq, nkv, D, F, V;
     int qd, nqkv;
     GemmShape g_qkv, g_o, g_gu, g_down, g_lm;
+    int nrec;               // rows of a recurrent layer's projection (q, k, v, gates, padding)
+    GemmShape g_rqkv;
     GemmShape w_qkv, w_o, w_gu, w_down, w_lm;   // the same projections over W12 weights (M <= 64)
     int lm_groups, lm_groups_w12;
     int attn_chunks;
     size_t o_depth, o_pos, o_status, o_anc, o_rope, o_x, o_u, o_q, o_attn, o_h, o_part, o_po,
-        o_pml, o_amv, o_ami, total;
+        o_pml, o_amv, o_ami, o_rq, o_ro, o_rs, total;
     // the persistent path (rows <= 16): its own buffers, sized for up to kFusedSizeG workgroups
     bool fused_shape;
     size_t total_steps;     // the per-step plan's part of the workspace (the persistent one follows)
@@ -149,11 +151,13 @@ int make_plan(const spec_model_cfg *c, int B, int K, int max_pages, Plan &p) {
     p.w_down = plan_gemm_w12(M, p.H, p.F, true);
     p.w_lm = plan_gemm_w12(M, p.V, p.H, false);
     p.lm_groups_w12 = gemm_groups(p.w_lm);
+    p.nrec = (3 * p.qd + p.nq + 15) / 16 * 16;
+    p.g_rqkv = plan_gemm(M, p.nrec, p.H, true);
     const int64_t max_keys = (int64_t)max_pages * SPEC_PAGE_SIZE;
     p.attn_chunks = (int)((max_keys + kAttnChunk - 1) / kAttnChunk);
     const int group = p.nq / p.nkv;
     size_t part = 16;
-    for (const GemmShape *g : {&p.g_qkv, &p.g_o, &p.g_down, &p.w_qkv, &p.w_o, &p.w_down}) {
+    for (const GemmShape *g : {&p.g_qkv, &p.g_o, &p.g_down, &p.w_qkv, &p.w_o, &p.w_down, &p.g_rqkv}) {
         const size_t b = (size_t)g->splits * M * g->N * sizeof(float);
         if (b > part) part = b;
     }
@@ -177,6 +181,10 @@ int make_plan(const spec_model_cfg *c, int B, int K, int max_pages, Plan &p) {
     p.o_pml = cv.take(sizeof(float2) * (size_t)B * p.nkv * p.attn_chunks * group * K);
     p.o_amv = cv.take(sizeof(float) * (size_t)amax_groups * M);
     p.o_ami = cv.take(sizeof(int32_t) * (size_t)amax_groups * M);
+    // recurrent layers of a hybrid target: q, the tree pass's output, its status
+    p.o_rq = cv.take(sizeof(uint16_t) * M * p.qd);
+    p.o_ro = cv.take(sizeof(float) * M * p.qd);
+    p.o_rs = cv.take(sizeof(int32_t) * B);
     p.fused_shape = fused_shape_ok(p);
     p.total_steps = cv.off;
     if (p.fused_shape) {
@@ -279,6 +287,24 @@ int spec_verify(const spec_weights *w, const spec_kv_cache *kv, const int32_t *d
         }
     }
     if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0) return SPEC_EINVAL;
+    // recurrent layers (hybrid targets): their states and the pass's buffers, bf16 weights, the
+    // per-step plan
+    bool any_rec = false;
+    if (w->layer_kind != nullptr) {
+        for (int l = 0; l < p.L; ++l) {
+            const int kd = w->layer_kind[l];
+            if (kd != SPEC_LAYER_ATTENTION && kd != SPEC_LAYER_RECURRENT) return SPEC_EINVAL;
+            if (kd == SPEC_LAYER_RECURRENT) {
+                any_rec = true;
+                if (kv->rec_state == nullptr || kv->rec_state[l] == nullptr) return SPEC_EINVAL;
+            }
+        }
+    }
+    if (any_rec) {
+        if (kv->rec_k == nullptr || kv->rec_v == nullptr || kv->rec_g == nullptr) return SPEC_EINVAL;
+        if (w12 || w12_lm) return SPEC_EUNSUPPORTED;
+        if (p.K > kRecMaxK) return SPEC_EUNSUPPORTED;
+    }
 
     const int want = extras ? extras->path : SPEC_PATH_AUTO;
     if (want != SPEC_PATH_AUTO && want != SPEC_PATH_STEPS && want != SPEC_PATH_PERSISTENT) return SPEC_EINVAL;
@@ -286,7 +312,7 @@ int spec_verify(const spec_weights *w, const spec_kv_cache *kv, const int32_t *d
     // of its workgroups
     FusedCounts fc;
     bool fused = false;
-    if (want == SPEC_PATH_PERSISTENT && p.fused_shape && !w12 && !w12_lm) {
+    if (want == SPEC_PATH_PERSISTENT && p.fused_shape && !w12 && !w12_lm && !any_rec) {
         int dev = 0, ncu = 0;
         if (hipGetDevice(&dev) == hipSuccess &&
             hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
@@ -466,6 +492,22 @@ int spec_verify(const spec_weights *w, const spec_kv_cache *kv, const int32_t *d
         const spec_w12_layer *lq = w12 ? &w->w12_layers[l] : nullptr;
         bf16 *kl = k_pool + l * layer_stride;
         bf16 *vl = v_pool + l * layer_stride;
+        if (any_rec && w->layer_kind[l] == SPEC_LAYER_RECURRENT) {
+            // recurrent mixer: [q | k | v | a] = u . W^T; g = -softplus(a); the tree pass over the
+            // committed state; its output, rounded to bf16, is the O projection's operand. The
+            // pass's keys, values and gates stay in the cache struct's buffers for the commit.
+            const int64_t rl = (int64_t)l * M * p.qd;
+            bf16 *rk = static_cast<bf16 *>(kv->rec_k) + rl;
+            bf16 *rv = static_cast<bf16 *>(kv->rec_v) + rl;
+            float *rg = kv->rec_g + (int64_t)l * M * p.nq;
+            bf16 *rq = at<bf16>(workspace, p.o_rq);
+            float *ro = at<float>(workspace, p.o_ro);
+            SV_TRY(gemm(p.g_rqkv, EPI_PARTIAL, operand(u), static_cast<const bf16 *>(lw.w_qkv), ep, stream));
+            SV_TRY(reduce_rec(part, p.g_rqkv.splits, M, p.nrec, p.nq, p.D, rq, rk, rv, rg, stream));
+            SV_TRY(rec_tree(kv->rec_state[l], rq, rk, rv, rg, tree_parent, p.B, p.K, p.nq, p.D, ro,
+                            at<int32_t>(workspace, p.o_rs), stream));
+            SV_TRY(rec_operand(ro, M, p.qd, attn, stream));
+        } else {
         // q, k, v = u . Wqkv^T (u = RMSNorm(x) * attn_norm); RoPE; K/V into the cache
         SV_TRY(proj(p.g_qkv, p.w_qkv, EPI_PARTIAL, operand(u), lw.w_qkv, lq ? &lq->w_qkv : nullptr));
         SV_TRY(reduce_qkv(part, lq ? p.w_qkv.splits : p.g_qkv.splits, ni, ctx_len, kv->block_table, kv->max_pages_per_req,
@@ -473,6 +515,7 @@ int spec_verify(const spec_weights *w, const spec_kv_cache *kv, const int32_t *d
         aa.k_pool = kl;
         aa.v_pool = vl;
         SV_TRY(attention(aa, stream));
+        }
         // x += o . Wo^T; u = RMSNorm(x) * mlp_norm
         SV_TRY(proj(p.g_o, p.w_o, EPI_PARTIAL, operand(attn), lw.w_o, lq ? &lq->w_o : nullptr));
         SV_TRY(reduce_resid_norm(part, lq ? p.w_o.splits : p.g_o.splits, M, p.H, static_cast<const bf16 *>(lw.mlp_norm),
@@ -506,11 +549,26 @@ int spec_commit_kv(const spec_model_cfg *cfg, const spec_kv_cache *kv, const int
         return SPEC_EINVAL;
     if (batch < 1 || k < 1) return SPEC_EINVAL;
     if (k > SPEC_MAX_K) return SPEC_EUNSUPPORTED;
+    if (kv->rec_state != nullptr && (kv->rec_k == nullptr || kv->rec_v == nullptr || kv->rec_g == nullptr))
+        return SPEC_EINVAL;
     SV_TRY(commit_kv(accepted_len, accepted_path, ctx_len, kv->block_table, kv->max_pages_per_req,
                      kv->n_pages, cfg->n_layers, batch, k, cfg->n_kv_heads, cfg->head_dim,
                      static_cast<bf16 *>(kv->k_pool), static_cast<bf16 *>(kv->v_pool), stream));
     SV_TRY(commit_ctx(accepted_len, accepted_path, kv->block_table, kv->max_pages_per_req,
                       kv->n_pages, k, ctx_len, batch, stream));
+    if (kv->rec_state != nullptr) {
+        // recurrent layers of a hybrid target: each state after the accepted path, from the
+        // pass's keys, values and gates
+        const int64_t M = (int64_t)batch * k;
+        const int qd = cfg->n_q_heads * cfg->head_dim;
+        for (int l = 0; l < cfg->n_layers; ++l) {
+            if (kv->rec_state[l] == nullptr) continue;
+            SV_TRY(rec_commit(kv->rec_state[l], static_cast<const bf16 *>(kv->rec_k) + l * M * qd,
+                              static_cast<const bf16 *>(kv->rec_v) + l * M * qd,
+                              kv->rec_g + l * M * cfg->n_q_heads, accepted_len, accepted_path, batch, k,
+                              cfg->n_q_heads, cfg->head_dim, stream));
+        }
+    }
     return SPEC_OK;
 }
 
@@ -681,6 +739,9 @@ int spec_prefill(const spec_weights *weights, const spec_kv_cache *kv, const int
         return SPEC_EINVAL;
     if (batch < 1 || p < 1) return SPEC_EINVAL;
     if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0) return SPEC_EINVAL;
+    if (weights->layer_kind != nullptr)
+        for (int l = 0; l < weights->cfg.n_layers; ++l)
+            if (weights->layer_kind[l] != SPEC_LAYER_ATTENTION) return SPEC_EUNSUPPORTED;
     PrefillLayout o;
     int rc = prefill_layout(&weights->cfg, batch, kv->max_pages_per_req, last_logits != nullptr, o);
     if (rc != SPEC_OK) return rc;
