@@ -77,13 +77,16 @@ class VerifyOut:
 
 
 def run_verify(weights: tv.Weights, kv: tv.PagedKV, tokens: np.ndarray, parent, ctx_lens,
-               want_hidden=False, want_logits=True, path: str = "auto"):
-    """tokens [B][K] int32; parent [B][K] or None. Returns numpy outputs."""
+               want_hidden=False, want_logits=True, path: str = "auto", ws_fill=None):
+    """tokens [B][K] int32; parent [B][K] or None. Returns numpy outputs. ws_fill: a byte
+    value written over the whole workspace first (e.g. 0xFF: NaN floats, -1 integers)."""
     dev = kv.k_pool.device
     B, K = tokens.shape
     cfg = weights.cfg
     M = B * K
     ws = tv.workspace(tv.spec_workspace_bytes(cfg, B, K, kv.max_pages), dev)
+    if ws_fill is not None:
+        ws.fill_(ws_fill)
     t_tok = torch.from_numpy(np.ascontiguousarray(tokens, np.int32)).to(dev)
     t_par = None if parent is None else torch.from_numpy(np.ascontiguousarray(parent, np.int32)).to(dev)
     t_ctx = torch.tensor(list(ctx_lens), dtype=torch.int32, device=dev)
