@@ -304,11 +304,22 @@ def cpu_baseline(weights, shape, kv, tokens, parent, ctx, budget_s):
                        f"({step:.1f}s per step)")}
 
 
+def prefill_flops(shape, P):
+    """The method's arithmetic of a P-token prefill from an empty context (multiply-adds count 2):
+    every projection for every prompt row, causal attention (row i's scores and weighted sum over
+    i + 1 keys for every q head), the output head for the last row only."""
+    L, H, F, d = shape.n_layers, shape.hidden, shape.ffn, shape.head_dim
+    nq, nkv = shape.n_q_heads, shape.n_kv_heads
+    proj = H * (nq + 2 * nkv) * d + nq * d * H + 2 * F * H + F * H
+    attn = 4 * d * nq * P * (P + 1) // 2
+    return L * (2 * P * proj + attn) + 2 * shape.vocab * H
+
+
 def prefill_bench(args, shape, device):
-    """spec_prefill of one request's prompt from an empty context (chunks of 64 positions through
-    the verify kernels), replayed from a HIP graph; prints one JSON line with prompt tokens/s.
-    Algorithmic bytes: every weight once per chunk (embedding rows only for the prompt), each
-    chunk's K/V reads of the positions before it and its own K/V writes."""
+    """spec_prefill of one request's prompt from an empty context, replayed from a HIP graph: the
+    whole prompt (up to 4096 positions) in one pass over the tile projections, causal attention
+    over the cache, the output head for the last position. Prints one JSON line with prompt
+    tokens/s and the method's TFLOP/s against the bf16 matrix-core peak."""
     P = args.prompt
     w12 = args.weights == "w12"
     weights = build_model(shape, device, w12)
@@ -344,25 +355,23 @@ def prefill_bench(args, shape, device):
         e1.record(stream)
         e1.synchronize()
     ms = e0.elapsed_time(e1) / reps
-    chunks = (P + 63) // 64
-    L, H, nkv, d = shape.n_layers, shape.hidden, shape.n_kv_heads, shape.head_dim
-    per_chunk_w = step_bytes(shape, 1, 0, [0], weights.w12)                # weights, no rows
-    kv_row = L * nkv * d * 2 * 2                                           # K and V of a position
-    kv_bytes = sum(min(64, P - 64 * c) * kv_row + 64 * c * kv_row for c in range(chunks))
-    nbytes = chunks * per_chunk_w + 2 * P * H + kv_bytes
-    gbps = nbytes / (ms / 1e3) / 1e9
+    flops = prefill_flops(shape, P)
+    tflops = flops / (ms / 1e3) / 1e12
+    chunk = min(P, 4096)
     result = {
         "metric": "prefill prompt tokens/s, 27B-shape dense, 1 GPU", "value": round(P / (ms / 1e3), 1),
         "unit": "prompt tokens/s", "n_gpus": 1, "steps": reps, "ms_per_prefill": round(ms, 3),
         "higher_is_better": True, "dtype": "bf16",
         "data": "synthetic (seeded random-init weights N(0,0.02), uniform prompt tokens)",
         "config": {"workload": f"27B-shape dense, 64 layers + lm_head, batch 1, prompt {P} from an empty "
-                               f"context, {chunks} chunks of up to 64 positions",
+                               f"context, passes of up to {chunk} positions",
                    "weights": "W12 (lossless 12-bit)" if w12 else "bf16", "hip_graph": True},
-        "hbm": {"bytes_per_prefill": int(nbytes), "achieved_gbps": round(gbps, 1),
-                "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4)},
+        "mfma": {"flops_per_prefill": int(flops), "achieved_tflops": round(tflops, 1),
+                 "peak_tflops": MFMA_BF16_PEAK_TFLOPS, "frac_of_peak": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                 "note": "the method's arithmetic: all projections of every prompt row, causal "
+                         "attention, the output head of the last row"},
     }
-    log(f"prefill of {P}: {ms:.2f} ms, {P / (ms / 1e3):.0f} tokens/s, {gbps:.0f} GB/s")
+    log(f"prefill of {P}: {ms:.2f} ms, {P / (ms / 1e3):.0f} tokens/s, {tflops:.1f} TFLOP/s")
     print(json.dumps(result), flush=True)
 
 

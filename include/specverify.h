@@ -345,16 +345,26 @@ int spec_skinny_gemm_w12(const void *x, int m, int kd, const spec_w12_matrix *w,
  * Appends p prompt tokens per request to its committed context: writes their rotated keys and
  * values into cache slots ctx_len .. ctx_len + p - 1 of every layer, returns the target's greedy
  * token after the last prompt token (the root of the first verify step) and sets
- * ctx_len += p on the device. A verify pass over a linear block computes exactly this for its
- * nodes (each node attends to the committed context and the nodes before it), so the prompt
- * runs through the per-step verify kernels in chunks of up to SPEC_MAX_K positions, each chunk's K/V
- * committed before the next chunk's pass; the drafted-block view of the pages
- * [SpecPilot news piece, wireai.ir — "The main challenge"] with every block fully accepted.
+ * ctx_len += p on the device. Every prompt position is a node whose tokens are all given and all
+ * kept: it attends to the committed context and the positions before it, as a fully accepted
+ * linear block does in a verify pass [SpecPilot news piece, wireai.ir — "The main challenge"].
+ * The prompt runs in chunks of up to 4096 positions per pass (over all requests: 4096 / batch
+ * per request), each chunk's K/V written before its attention reads them; the projections run
+ * on the matrix cores, attention is causal over the paged cache, and the output head runs only
+ * for each request's last position.
  *   prompt [batch][p] int32; ctx_len [batch] in/out; next_token [batch] out (-1 for a request
  *   whose prompt holds a token outside the vocabulary or whose pages do not cover
  *   ctx_len + p: its ctx_len is left where its last good chunk ended and its cache rows past it
  *   are unspecified); last_logits [batch][vocab] fp32 or NULL: the last prompt position's
- *   logits. Weights as for spec_verify (bf16 or W12). Errors as for spec_verify. */
+ *   logits. Weights as for spec_verify (bf16 or W12), attention layers only (SPEC_EUNSUPPORTED
+ *   for a recurrent layer, or for more than 8 query heads per kv head).
+ * spec_prefill_workspace_bytes: the workspace for `batch` requests whose prompts may reach
+ *   max_pages_per_req * 16 positions; it does not depend on want_logits (the logits go straight
+ *   to the caller's buffer). Errors as for spec_verify: SPEC_EINVAL for NULL pointers, a
+ *   workspace that is not 256-byte aligned, batch or p below 1; SPEC_EWORKSPACE for a short
+ *   workspace. weights and kv are host structs as for spec_verify; prompt, ctx_len, next_token,
+ *   last_logits and workspace are device pointers. Async on stream; calls that overlap on one
+ *   cache race. */
 int spec_prefill_workspace_bytes(const spec_model_cfg *cfg, int batch, int max_pages_per_req,
                                  int want_logits, size_t *bytes /* HOST */);
 int spec_prefill(const spec_weights *weights, const spec_kv_cache *kv, const int32_t *prompt,

@@ -1,6 +1,13 @@
 """Prompt prefill on the GPU (spec_prefill, through the C ABI) against the CPU oracle's prefill:
 the prompt's K/V rows, the last position's logits and greedy token, the advanced context, and a
-verify step over the GPU-prefilled cache, i.e. the tiny workload end to end on the GPU."""
+verify step over the GPU-prefilled cache, i.e. the tiny workload end to end on the GPU.
+
+spec_prefill runs chunks of min(4096 / batch, page budget) positions per request, each a whole
+target pass (tile projections from 128 rows, causal attention in 32-row query blocks over 64-key
+blocks of the cache, the output head for the last position only). The cases cover one chunk and
+several, the attention's block edges (1, 31, 32, 33, 64, 65, 129 positions over empty and
+non-empty contexts), a batch with ragged contexts, bad requests failing in the first and a later
+chunk, W12 weights, and two layers of the 27B shape."""
 import numpy as np
 import pytest
 import torch
@@ -10,8 +17,9 @@ import synth
 import tree_verification_skinny_amd as tv
 from tree_verification_skinny_amd import kvlayout
 
-from helpers import (bits, check_accept, check_logits, device_weights, make_kv, oracle_model_from,
-                     run_verify, upload_context)
+import ref64
+from helpers import (EXACT_FACTOR, bits, check_accept, check_as_exact, check_logits, device_weights, make_kv,
+                     oracle_model_from, run_verify, upload_context)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -51,7 +59,7 @@ def greedy_ok(gpu_tok, last):
 @pytest.mark.parametrize("seed", [0, 1, 2])
 def test_prefill_then_verify_tiny_end_to_end(seed):
     """The tiny workload with the prompt prefilled on the GPU instead of uploaded: a 128-token
-    prompt (two chunks), then a block of 8 drafted from the oracle's greedy continuation."""
+    prompt, then a block of 8 drafted from the oracle's greedy continuation."""
     shape = synth.TINY
     w = synth.model_weights(shape, seed)
     m = oracle_model_from(shape, w)
@@ -78,8 +86,8 @@ def test_prefill_then_verify_tiny_end_to_end(seed):
 
 
 def test_prefill_batch_ragged_contexts_and_lengths():
-    """Three requests with committed contexts of 0, 37 and 150 positions and a 100-token prompt
-    (chunks of 64 and 36), shuffled pages, one request with spare pages."""
+    """Three requests with committed contexts of 0, 37 and 150 positions and a 100-token prompt,
+    shuffled pages, one request with spare pages."""
     shape = synth.TINY
     seed = 11
     w = synth.model_weights(shape, seed)
@@ -106,24 +114,28 @@ def test_prefill_batch_ragged_contexts_and_lengths():
 
 
 def test_prefill_marks_bad_requests_only():
+    """Three requests of 1400 tokens: chunks of 4096 // 3 = 1365 positions and then 35. Request
+    1's pages (3, 48 positions) do not cover the first chunk; request 2 holds a token outside
+    the vocabulary in its second chunk."""
     shape = synth.TINY
     seed = 5
     w = synth.model_weights(shape, seed)
     weights = device_weights(shape, w, DEV)
-    p = 70
-    # request 1's pages (3, 48 positions) do not cover the first chunk; request 2 holds a token
-    # outside the vocabulary in its second chunk
+    p = 1400
+    C = 4096 // 3
     table, n_pages = synth.page_table(3, [(p + 15) // 16, 3, (p + 15) // 16], seed)
     kv = tv.PagedKV.empty(tv.ModelCfg.of(shape), n_pages, torch.from_numpy(table), DEV)
     prompts = np.stack([synth.uniform_tokens(p, shape.vocab, seed, "bad", b) for b in range(3)])
-    prompts[2, 66] = shape.vocab
+    prompts[2, C + 20] = shape.vocab
     ctx, nt, _ = gpu_prefill(weights, kv, prompts, [0, 0, 0], want_logits=False)
     m = oracle_model_from(shape, w)
     kc, vc, last = oracle.prefill(m, prompts[0])
     assert ctx[0] == p and greedy_ok(nt[0], last)
     check_rows(kv, 0, kc, vc, 0, p, "good request")
     assert nt[1] == -1 and ctx[1] == 0            # fails in the first chunk
-    assert nt[2] == -1 and ctx[2] == 64           # fails in the second chunk, after the first
+    assert nt[2] == -1 and ctx[2] == C            # fails in the second chunk, after the first
+    kc2, vc2, _ = oracle.prefill(m, prompts[2][:C])
+    check_rows(kv, 2, kc2, vc2, 0, C, "first chunk of the failed request")
 
 
 def test_prefill_over_w12_weights_equals_bf16():
@@ -141,17 +153,18 @@ def test_prefill_over_w12_weights_equals_bf16():
         ctx, nt, lg = gpu_prefill(weights, kv, prompt[None], [0])
         outs.append((ctx, nt, lg, kv.k_pool.clone(), kv.v_pool.clone()))
     (c1, n1, l1, k1, v1), (c2, n2, l2, k2, v2) = outs
-    # W12 is lossless and runs the same plans as bf16 below 128 rows: bit-identical results
+    # W12 is lossless and runs the same plans as bf16 below 128 rows (a 90-row chunk): bit-identical
     assert np.array_equal(c1, c2) and c1[0] == 90 and np.array_equal(n1, n2)
     assert np.array_equal(l1.view(np.int32), l2.view(np.int32))
     assert torch.equal(k1.view(torch.int16), k2.view(torch.int16))
     assert torch.equal(v1.view(torch.int16), v2.view(torch.int16))
 
 
-@pytest.mark.parametrize("p,ctx0", [(1, 0), (1, 20), (64, 0), (65, 3), (129, 0)])
-def test_prefill_chunk_boundaries(p, ctx0):
-    """Prompt lengths at and around the 64-position chunk: a single token (also with an empty
-    context), exactly one chunk, one chunk plus one token, two chunks plus one."""
+@pytest.mark.parametrize("p,ctx0", [(1, 0), (1, 20), (31, 0), (32, 5), (33, 64), (64, 0), (65, 3), (129, 0)])
+def test_prefill_block_boundaries(p, ctx0):
+    """Prompt lengths at the attention's block edges: a single token (also with an empty
+    context), around one 32-row query block, one and two 64-key blocks, over empty and
+    non-empty contexts."""
     shape = synth.TINY
     seed = 40 + p
     w = synth.model_weights(shape, seed)
@@ -169,3 +182,69 @@ def test_prefill_chunk_boundaries(p, ctx0):
     check_logits(lg[0], last, "last logits")
     assert greedy_ok(nt[0], last)
     check_rows(kv, 0, kc, vc, 0, ctx0 + p, "rows")
+
+
+def test_prefill_two_chunks_batch():
+    """Two requests of 2100 tokens: chunks of 2048 positions and then 52, tile projections of
+    4096 rows, contexts of 0 and 75."""
+    shape = synth.TINY
+    seed = 17
+    w = synth.model_weights(shape, seed)
+    m = oracle_model_from(shape, w)
+    weights = device_weights(shape, w, DEV)
+    ctx0, p = [0, 75], 2100
+    kv = make_kv(shape, [c + p for c in ctx0], 0, seed, DEV)
+    prompts = np.stack([synth.uniform_tokens(p, shape.vocab, seed, "two", b) for b in range(2)])
+    refs = []
+    for b, c in enumerate(ctx0):
+        ctxs = [synth.kv_context(shape, c, seed, l, request=b) for l in range(shape.n_layers)]
+        kc0 = [np.ascontiguousarray(bits(x)) for x, _ in ctxs]
+        vc0 = [np.ascontiguousarray(bits(y)) for _, y in ctxs]
+        upload_context(kv, b, kc0, vc0)
+        refs.append(oracle.prefill(m, prompts[b], kc0, vc0))
+    ctx, nt, lg = gpu_prefill(weights, kv, prompts, ctx0)
+    for b, c in enumerate(ctx0):
+        kc, vc, last = refs[b]
+        assert ctx[b] == c + p
+        check_logits(lg[b], last, f"request {b} last logits")
+        assert greedy_ok(nt[b], last)
+        check_rows(kv, b, kc, vc, c, c + p, f"request {b}")
+
+
+def test_prefill_27b_shape_two_layers():
+    """Two layers of the 27B shape (vocab cut to 1024) over a 300-token prompt after a 45-token
+    context: the tile projections at full width, 40 q heads over 8 kv heads (query tiles of 5
+    heads). Layer 0's keys and values (from the embeddings) meet the fixed tolerance; layer 1's,
+    which depend on layer 0's causal attention over the whole chunk, and the last position's
+    logits are held to an exact float64 evaluation of both layers, as close to it as the oracle
+    (the 27B-shape criterion of the verify pass: there the fixed tolerance is tighter than fp32
+    summation order allows)."""
+    shape = synth.DENSE_27B.with_layers(2).with_vocab(1024)
+    seed = 27
+    w = synth.model_weights(shape, seed)
+    m = oracle_model_from(shape, w)
+    weights = device_weights(shape, w, DEV)
+    ctx0, p = 45, 300
+    kv = make_kv(shape, [ctx0 + p], 0, seed, DEV)
+    ctxs = [synth.kv_context(shape, ctx0, seed, l) for l in range(shape.n_layers)]
+    kc0 = [np.ascontiguousarray(bits(x)) for x, _ in ctxs]
+    vc0 = [np.ascontiguousarray(bits(y)) for _, y in ctxs]
+    upload_context(kv, 0, kc0, vc0)
+    prompt = synth.uniform_tokens(p, shape.vocab, seed, "27b")
+    kc, vc, last = oracle.prefill(m, prompt, kc0, vc0)
+    ctx, nt, lg = gpu_prefill(weights, kv, prompt[None], [ctx0])
+    assert ctx[0] == ctx0 + p
+    chain = oracle.chain(p)
+    x0 = bits(w["embed"][torch.from_numpy(prompt.astype(np.int64))])
+    x1, _, _ = ref64.layer(shape, w["layers"][0], kc0[0], vc0[0], chain, x0)
+    x2, k1, v1 = ref64.layer(shape, w["layers"][1], kc0[1], vc0[1], chain, x1)
+    kg0, vg0 = kvlayout.read_rows(kv, 0, 0, torch.arange(ctx0, ctx0 + p))
+    check_logits(kg0.float().cpu().numpy(), oracle.from_bf16(kc[0][ctx0:]), "27B layer 0 k")
+    check_logits(vg0.float().cpu().numpy(), oracle.from_bf16(vc[0][ctx0:]), "27B layer 0 v")
+    kg1, vg1 = kvlayout.read_rows(kv, 1, 0, torch.arange(ctx0, ctx0 + p))
+    print(check_as_exact(kg1.float().cpu().numpy(), oracle.from_bf16(kc[1][ctx0:]), k1.numpy(), "27B layer 1 k"))
+    print(check_as_exact(vg1.float().cpu().numpy(), oracle.from_bf16(vc[1][ctx0:]), v1.numpy(), "27B layer 1 v"))
+    exact = ref64.logits(shape, w["final_norm"], w["lm_head"], x2)[-1]
+    print(check_as_exact(lg[0], last, exact, "27B last logits"))
+    top = np.sort(exact)[::-1]
+    assert int(nt[0]) == int(np.argmax(exact)) or top[0] - top[1] < EXACT_FACTOR * float(np.abs(exact - last).max())

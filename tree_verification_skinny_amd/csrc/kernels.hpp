@@ -132,9 +132,21 @@ hipError_t commit_ctx(const int32_t *accepted_len, const int32_t *path, const in
 // Prompt prefill bookkeeping (k_prefill.hip).
 hipError_t prefill_init(int32_t *failed, int B, hipStream_t st);
 hipError_t prefill_gather(const int32_t *prompt, int p, int c0, int n, int B, int32_t *out, hipStream_t st);
-hipError_t prefill_advance(const int32_t *acc, const int32_t *greedy, int n, int B, bool last,
-                           int32_t *failed, int32_t *ctx_len, int32_t *next_token, hipStream_t st);
-hipError_t prefill_last_logits(const float *logits, int n, int B, int V, float *out, hipStream_t st);
+
+// Chunked prefill (k_prefill.hip): positions and per-request status of a chunk of n rows per
+// request; causal attention of the chunk over the cache into the O operand; each request's last
+// row into the output head's operand; the head's per-group maxima merged into the next tokens,
+// and the committed context advanced.
+hipError_t prefill_prep(const int32_t *tokens, int n, int B, int vocab, const int32_t *ctx_len,
+                        const int32_t *block_table, int max_pages, int n_pages, const int32_t *failed,
+                        int32_t *pos, int32_t *status, hipStream_t st);
+hipError_t prefill_attention(const bf16 *q, const bf16 *k_pool, const bf16 *v_pool, const int32_t *block_table,
+                             int max_pages, const int32_t *ctx_len, const int32_t *status, int B, int n, int nq,
+                             int nkv, int D, bf16 *out, hipStream_t st);
+hipError_t prefill_last_rows(const bf16 *u, int n, int B, int H, bf16 *out, hipStream_t st);
+hipError_t prefill_finish(const float *amv, const int *ami, int groups, int B, int n, bool last,
+                          const int32_t *status, int32_t *failed, int32_t *ctx_len, int32_t *next_token,
+                          hipStream_t st);
 // Recurrent layers of a hybrid target: the tree pass over the committed state (k_recurrent.hip)
 // and the accepted node's state written in place (k_rec_commit.hip). D = dk = dv, 64 or 128;
 // K <= kRecMaxK.

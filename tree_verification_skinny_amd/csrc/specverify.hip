@@ -695,37 +695,75 @@ int spec_w12_pack(const void *w, int n, int kd, const int32_t *plan, void *plane
     return SPEC_OK;
 }
 
-// Prefill workspace: the verify pass's workspace for chunks of SPEC_MAX_K rows, then its outputs
-// (accepted_len, bonus, path, greedy), the chunk's tokens, the failure flags and, when asked for,
-// the last chunk's fp32 logits.
+// The chunked prefill: up to kPrefillRows prompt positions per pass (over all requests), each
+// pass a full target pass over those rows: the tile projections (matrix-core bound at hundreds of
+// rows), RoPE and the cache writes, causal attention over the cache, the output head only for the
+// last position of each request.
+constexpr int kPrefillRows = 4096;
+
 struct PrefillLayout {
-    size_t verify, acc, bonus, path, greedy, tokens, failed, logits, total;
+    int C;                           // prompt positions per request per pass
+    GemmShape g_lm, w_lm;
+    size_t x, u, q, attn, h, part, pos, rope, status, failed, tokens, head_u, amv, ami, total;
 };
 
-static int prefill_layout(const spec_model_cfg *cfg, int batch, int max_pages, bool want_logits,
-                          PrefillLayout &o) {
-    size_t vb = 0;
-    const int rc = spec_workspace_bytes(cfg, batch, SPEC_MAX_K, max_pages, &vb);
+static void prefill_shapes(const spec_model_cfg *cfg, int M, GemmShape (&g)[4], GemmShape (&w)[4]) {
+    const int qd = cfg->n_q_heads * cfg->head_dim, nqkv = (cfg->n_q_heads + 2 * cfg->n_kv_heads) * cfg->head_dim;
+    const int N[4] = {nqkv, cfg->hidden, 2 * cfg->ffn, cfg->hidden};
+    const int Kd[4] = {cfg->hidden, qd, cfg->hidden, cfg->ffn};
+    for (int i = 0; i < 4; ++i) {
+        g[i] = plan_gemm(M, N[i], Kd[i], i != 2);
+        w[i] = plan_gemm_w12(M, N[i], Kd[i], i != 2);
+    }
+}
+
+// Sized for the longest prompt the page budget allows (max_pages * 16 positions per request).
+static int prefill_layout(const spec_model_cfg *cfg, int batch, int max_pages, PrefillLayout &o) {
+    int rc = check_cfg(cfg);
     if (rc != SPEC_OK) return rc;
-    const size_t rows = (size_t)batch * SPEC_MAX_K;
+    if (batch < 1 || max_pages < 1) return SPEC_EINVAL;
+    if ((int64_t)batch > kPrefillRows * 16) return SPEC_EUNSUPPORTED;
+    o.C = kPrefillRows / batch;
+    if (o.C < 1) o.C = 1;
+    if ((int64_t)o.C > (int64_t)max_pages * SPEC_PAGE_SIZE) o.C = max_pages * SPEC_PAGE_SIZE;
+    const int M = batch * o.C, Mp = (M + 15) / 16 * 16, Bp = (batch + 15) / 16 * 16;
+    const int H = cfg->hidden, qd = cfg->n_q_heads * cfg->head_dim, F = cfg->ffn, D = cfg->head_dim;
+    GemmShape g[4], w[4];
+    prefill_shapes(cfg, M, g, w);
+    size_t part = 16;
+    for (int i = 0; i < 4; ++i)
+        for (const GemmShape *s : {&g[i], &w[i]}) {
+            const size_t b = (size_t)s->splits * M * s->N * sizeof(float);
+            if (i != 2 && b > part) part = b;
+        }
+    o.g_lm = plan_gemm(batch, cfg->vocab, H, false);
+    o.w_lm = plan_gemm_w12(batch, cfg->vocab, H, false);
+    const int groups = gemm_groups(o.g_lm) > gemm_groups(o.w_lm) ? gemm_groups(o.g_lm) : gemm_groups(o.w_lm);
     Carver cv;
-    o.verify = cv.take(vb);
-    o.acc = cv.take(sizeof(int32_t) * batch);
-    o.bonus = cv.take(sizeof(int32_t) * batch);
-    o.path = cv.take(sizeof(int32_t) * rows);
-    o.greedy = cv.take(sizeof(int32_t) * rows);
-    o.tokens = cv.take(sizeof(int32_t) * rows);
+    o.x = cv.take(sizeof(uint16_t) * M * H);
+    o.u = cv.take(sizeof(uint16_t) * Mp * H);
+    o.q = cv.take(sizeof(uint16_t) * M * qd);
+    o.attn = cv.take(sizeof(uint16_t) * Mp * qd);
+    o.h = cv.take(sizeof(uint16_t) * Mp * F);
+    o.part = cv.take(part);
+    o.pos = cv.take(sizeof(int32_t) * M);
+    o.rope = cv.take(sizeof(float) * 2 * M * (D / 2));
+    o.status = cv.take(sizeof(int32_t) * batch);
     o.failed = cv.take(sizeof(int32_t) * batch);
-    o.logits = want_logits ? cv.take(sizeof(float) * rows * cfg->vocab) : 0;
+    o.tokens = cv.take(sizeof(int32_t) * M);
+    o.head_u = cv.take(sizeof(uint16_t) * Bp * H);
+    o.amv = cv.take(sizeof(float) * groups * batch);
+    o.ami = cv.take(sizeof(int32_t) * groups * batch);
     o.total = cv.off;
     return SPEC_OK;
 }
 
-int spec_prefill_workspace_bytes(const spec_model_cfg *cfg, int batch, int max_pages_per_req,
-                                 int want_logits, size_t *bytes) {
+int spec_prefill_workspace_bytes(const spec_model_cfg *cfg, int batch, int max_pages_per_req, int want_logits,
+                                 size_t *bytes) {
+    (void)want_logits;   // the last positions' logits go straight to the caller's buffer
     if (bytes == nullptr) return SPEC_EINVAL;
     PrefillLayout o;
-    const int rc = prefill_layout(cfg, batch, max_pages_per_req, want_logits != 0, o);
+    const int rc = prefill_layout(cfg, batch, max_pages_per_req, o);
     if (rc != SPEC_OK) return rc;
     *bytes = o.total;
     return SPEC_OK;
@@ -739,37 +777,113 @@ int spec_prefill(const spec_weights *weights, const spec_kv_cache *kv, const int
         return SPEC_EINVAL;
     if (batch < 1 || p < 1) return SPEC_EINVAL;
     if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0) return SPEC_EINVAL;
-    if (weights->layer_kind != nullptr)
-        for (int l = 0; l < weights->cfg.n_layers; ++l)
-            if (weights->layer_kind[l] != SPEC_LAYER_ATTENTION) return SPEC_EUNSUPPORTED;
+    if (kv->k_pool == nullptr || kv->v_pool == nullptr || kv->block_table == nullptr || kv->n_pages < 1 ||
+        kv->max_pages_per_req < 1)
+        return SPEC_EINVAL;
+    const spec_weights *w = weights;
+    if (w->layers == nullptr || w->embed == nullptr || w->final_norm == nullptr) return SPEC_EINVAL;
+    if (w->layer_kind != nullptr)
+        for (int l = 0; l < w->cfg.n_layers; ++l)
+            if (w->layer_kind[l] != SPEC_LAYER_ATTENTION) return SPEC_EUNSUPPORTED;
+    const bool w12 = w->w12_layers != nullptr;
+    const bool w12_lm = w->w12_lm_head.planes != nullptr;
+    if (!w12_lm && w->lm_head == nullptr) return SPEC_EINVAL;
+    if (w12_lm && !w12_ok(w->w12_lm_head)) return SPEC_EINVAL;
+    for (int l = 0; l < w->cfg.n_layers; ++l) {
+        const spec_layer_weights &lw = w->layers[l];
+        if (!lw.attn_norm || !lw.mlp_norm) return SPEC_EINVAL;
+        if (w12) {
+            const spec_w12_layer &q = w->w12_layers[l];
+            if (!w12_ok(q.w_qkv) || !w12_ok(q.w_o) || !w12_ok(q.w_gate_up) || !w12_ok(q.w_down)) return SPEC_EINVAL;
+        } else if (!lw.w_qkv || !lw.w_o || !lw.w_gate_up || !lw.w_down) {
+            return SPEC_EINVAL;
+        }
+    }
+    const spec_model_cfg *cfg = &w->cfg;
+    if (cfg->n_q_heads / cfg->n_kv_heads > 8) return SPEC_EUNSUPPORTED;   // query tiles per workgroup
     PrefillLayout o;
-    int rc = prefill_layout(&weights->cfg, batch, kv->max_pages_per_req, last_logits != nullptr, o);
+    int rc = prefill_layout(cfg, batch, kv->max_pages_per_req, o);
     if (rc != SPEC_OK) return rc;
     if (workspace_bytes < o.total) return SPEC_EWORKSPACE;
-    int32_t *acc = at<int32_t>(workspace, o.acc);
-    int32_t *bonus = at<int32_t>(workspace, o.bonus);
-    int32_t *path = at<int32_t>(workspace, o.path);
-    int32_t *greedy = at<int32_t>(workspace, o.greedy);
+
+    const int H = cfg->hidden, nq = cfg->n_q_heads, nkv = cfg->n_kv_heads, D = cfg->head_dim, V = cfg->vocab;
+    const float eps = cfg->rms_eps;
+    bf16 *x = at<bf16>(workspace, o.x), *u = at<bf16>(workspace, o.u), *q = at<bf16>(workspace, o.q);
+    bf16 *attn = at<bf16>(workspace, o.attn), *h = at<bf16>(workspace, o.h);
+    float *part = at<float>(workspace, o.part);
+    int32_t *status = at<int32_t>(workspace, o.status), *failed = at<int32_t>(workspace, o.failed);
     int32_t *tokens = at<int32_t>(workspace, o.tokens);
-    int32_t *failed = at<int32_t>(workspace, o.failed);
-    float *logits = last_logits ? at<float>(workspace, o.logits) : nullptr;
+    float *amv = at<float>(workspace, o.amv);
+    int *ami = at<int>(workspace, o.ami);
+    NodeInfo ni = {};
+    ni.pos = at<int32_t>(workspace, o.pos);
+    ni.status = status;
+    ni.rope = at<float2>(workspace, o.rope);
+    bf16 *k_pool = static_cast<bf16 *>(kv->k_pool), *v_pool = static_cast<bf16 *>(kv->v_pool);
+    const int64_t layer_stride = (int64_t)kv->n_pages * nkv * SPEC_PAGE_SIZE * D;
+
+    GemmEpi ep = {};
+    ep.F = cfg->ffn;
+    ep.y = part;
+    ep.h = h;
+    auto operand = [](const bf16 *Xp) {
+        GemmIn in = {};
+        in.Xp = Xp;
+        return in;
+    };
     SV_TRY(prefill_init(failed, batch, stream));
-    for (int c0 = 0; c0 < p; c0 += SPEC_MAX_K) {
-        const int n = p - c0 < SPEC_MAX_K ? p - c0 : SPEC_MAX_K;
+    for (int c0 = 0; c0 < p; c0 += o.C) {
+        const int n = p - c0 < o.C ? p - c0 : o.C;
+        const int M = batch * n;
         const bool last = c0 + n == p;
+        GemmShape g[4], gw[4];
+        prefill_shapes(cfg, M, g, gw);
+        auto proj = [&](int i, int epi, const GemmIn &in, const void *wb, const spec_w12_matrix *wq) -> hipError_t {
+            if (wq != nullptr) return gemm_w12(gw[i], epi, in, w12_ref(*wq), ep, stream);
+            return gemm(g[i], epi, in, static_cast<const bf16 *>(wb), ep, stream);
+        };
         SV_TRY(prefill_gather(prompt, p, c0, n, batch, tokens, stream));
-        spec_verify_extras ex = {};
-        ex.path = SPEC_PATH_STEPS;      // the workspace above is sized for that plan's 64-row chunks
-        ex.greedy = greedy;
-        ex.logits = last ? logits : nullptr;
-        rc = spec_verify(weights, kv, tokens, nullptr, ctx_len, batch, n, acc, bonus, path, &ex,
-                         at<void>(workspace, o.verify), o.acc - o.verify, stream);
-        if (rc != SPEC_OK) return rc;
-        SV_TRY(prefill_advance(acc, greedy, n, batch, last, failed, ctx_len, next_token, stream));
-    }
-    if (last_logits) {
-        const int n = p - (p - 1) / SPEC_MAX_K * SPEC_MAX_K;   // rows of the last chunk
-        SV_TRY(prefill_last_logits(logits, n, batch, weights->cfg.vocab, last_logits, stream));
+        SV_TRY(prefill_prep(tokens, n, batch, V, ctx_len, kv->block_table, kv->max_pages_per_req, kv->n_pages,
+                            failed, ni.pos, status, stream));
+        SV_TRY(rope_table(ni, M, D, cfg->rope_theta, stream));
+        SV_TRY(embed_norm(tokens, static_cast<const bf16 *>(w->embed),
+                          static_cast<const bf16 *>(w->layers[0].attn_norm), M, H, V, eps, x, u, nullptr, stream));
+        for (int l = 0; l < cfg->n_layers; ++l) {
+            const spec_layer_weights &lw = w->layers[l];
+            const spec_w12_layer *lq = w12 ? &w->w12_layers[l] : nullptr;
+            bf16 *kl = k_pool + l * layer_stride, *vl = v_pool + l * layer_stride;
+            SV_TRY(proj(0, EPI_PARTIAL, operand(u), lw.w_qkv, lq ? &lq->w_qkv : nullptr));
+            SV_TRY(reduce_qkv(part, (lq ? gw[0] : g[0]).splits, ni, ctx_len, kv->block_table, kv->max_pages_per_req,
+                              batch, n, nq, nkv, D, q, kl, vl, stream));
+            SV_TRY(prefill_attention(q, kl, vl, kv->block_table, kv->max_pages_per_req, ctx_len, status, batch, n, nq,
+                                     nkv, D, attn, stream));
+            SV_TRY(proj(1, EPI_PARTIAL, operand(attn), lw.w_o, lq ? &lq->w_o : nullptr));
+            SV_TRY(reduce_resid_norm(part, (lq ? gw[1] : g[1]).splits, M, H, static_cast<const bf16 *>(lw.mlp_norm),
+                                     eps, x, u, nullptr, stream));
+            SV_TRY(proj(2, EPI_SWIGLU, operand(u), lw.w_gate_up, lq ? &lq->w_gate_up : nullptr));
+            const bf16 *next_gain = l + 1 < cfg->n_layers ? static_cast<const bf16 *>(w->layers[l + 1].attn_norm)
+                                                          : static_cast<const bf16 *>(w->final_norm);
+            SV_TRY(proj(3, EPI_PARTIAL, operand(h), lw.w_down, lq ? &lq->w_down : nullptr));
+            SV_TRY(reduce_resid_norm(part, (lq ? gw[3] : g[3]).splits, M, H, next_gain, eps, x, u, nullptr, stream));
+        }
+        int groups = 0;
+        if (last) {
+            // the output head for each request's last position only
+            bf16 *hu = at<bf16>(workspace, o.head_u);
+            SV_TRY(prefill_last_rows(u, n, batch, H, hu, stream));
+            GemmEpi eh = {};
+            eh.logits = last_logits;
+            eh.amax_val = amv;
+            eh.amax_idx = ami;
+            if (w12_lm) {
+                SV_TRY(gemm_w12(o.w_lm, EPI_ARGMAX, operand(hu), w12_ref(w->w12_lm_head), eh, stream));
+                groups = gemm_groups(o.w_lm);
+            } else {
+                SV_TRY(gemm(o.g_lm, EPI_ARGMAX, operand(hu), static_cast<const bf16 *>(w->lm_head), eh, stream));
+                groups = gemm_groups(o.g_lm);
+            }
+        }
+        SV_TRY(prefill_finish(amv, ami, groups, batch, n, last, status, failed, ctx_len, next_token, stream));
     }
     return SPEC_OK;
 }
