@@ -55,17 +55,35 @@ METRIC = "verified tokens/sec + verify-step HBM GB/s (% peak), 27B-shape dense, 
 # figures hold for the kernel source they were taken on; any other source reports null.
 PMC_TRAFFIC = {
     ("block", "bf16"): {"source": "tree_verification_skinny_amd/csrc/k_gemm.hip",
-                        "sha256": "f373f9dd17953c6758f365c0a86324030f6a99ed9c58cb5019dcae725401a84e",
-                        "fetch_kib": 174761.283, "write_kib": 544.0,
-                        "fetch_scale": 1.9999858, "write_scale": 1.0},
+                        "sha256": "ddfbc8f9ca10bdbd0f872754805e7a8279958f233f49a78b1fe545ae2b832c4b",
+                        "fetch_kib": 174750.900, "write_kib": 544.0,
+                        "fetch_scale": 1.9999849, "write_scale": 1.0},
     ("rec", "bf16"): {"source": "tree_verification_skinny_amd/csrc/k_recurrent.hip",
                       "sha256": "77c29c1c50fbf0b85f3dc27d12e2235737ccb122353cf2ba1ac1edf1c22781a2",
                       "fetch_kib": 58591.968, "write_kib": 32768.2,
                       "fetch_scale": 1.9999851, "write_scale": 1.0},
     ("block", "w12"): {"source": "tree_verification_skinny_amd/csrc/k_gemm.hip",
-                       "sha256": "f373f9dd17953c6758f365c0a86324030f6a99ed9c58cb5019dcae725401a84e",
-                       "fetch_kib": 131470.243, "write_kib": 544.0,
-                       "fetch_scale": 1.9999851, "write_scale": 1.0},
+                       "sha256": "ddfbc8f9ca10bdbd0f872754805e7a8279958f233f49a78b1fe545ae2b832c4b",
+                       "fetch_kib": 131503.451, "write_kib": 544.0,
+                       "fetch_scale": 1.9999849, "write_scale": 1.0},
+}
+# Average duration of one launch of the gate/up projection kernel in a rocprofv3 kernel trace of
+# `bench.py --config C` (summaries under profiles/, each with its command). The trace times the
+# kernel alone; the bench line's own figure brackets each launch with HIP events on the stream,
+# which adds the launch's dispatch. Reported beside it while the kernel's source is unchanged.
+PROFILED = {
+    ("block", "bf16"): {"source": "tree_verification_skinny_amd/csrc/k_gemm.hip",
+                        "sha256": "ddfbc8f9ca10bdbd0f872754805e7a8279958f233f49a78b1fe545ae2b832c4b",
+                        "kernel": "gemm_kernel<2, 1, 8, 1, false>", "avg_us": 57.91,
+                        "profile": "profiles/block16_ctx4096_kernels.md"},
+    ("tree", "bf16"): {"source": "tree_verification_skinny_amd/csrc/k_gemm.hip",
+                       "sha256": "ddfbc8f9ca10bdbd0f872754805e7a8279958f233f49a78b1fe545ae2b832c4b",
+                       "kernel": "gemm_wide_kernel<4, 1, false>", "avg_us": 81.88,
+                       "profile": "profiles/tree64_ctx8192_kernels.md"},
+    ("batched", "bf16"): {"source": "tree_verification_skinny_amd/csrc/k_gemm_tc.hip",
+                          "sha256": "b4b69ebb59847102b35290782bf7e52eadcf557c320954e21a4c734a0e6afac2",
+                          "kernel": "gemm_tc_kernel<1>", "avg_us": 209.44,
+                          "profile": "profiles/batched32x16_kernels.md"},
 }
 HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0     # dense bf16 matrix-core peak of MI355X
@@ -175,6 +193,26 @@ def pmc_traffic(config, weights="bf16"):
         if hashlib.sha256(f.read()).hexdigest() != rec["sha256"]:
             return None
     return int(round((rec["fetch_kib"] * rec["fetch_scale"] + rec["write_kib"] * rec["write_scale"]) * 1024))
+
+
+def profiled(config, weights, work, bound):
+    """The kernel-trace figure of the gate/up launch for this workload (see PROFILED): its
+    duration and the roofline fraction it gives for `work` (bytes, or flops when bound is mfma),
+    or None when there is no trace for it or the kernel's source has changed since."""
+    import hashlib
+    rec = PROFILED.get((config, weights))
+    if rec is None:
+        return None
+    with open(os.path.join(ROOT, rec["source"]), "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != rec["sha256"]:
+            return None
+    s = rec["avg_us"] * 1e-6
+    if bound == "mfma":
+        ach, unit, peak = work / s / 1e12, "TFLOP/s", MFMA_BF16_PEAK_TFLOPS
+    else:
+        ach, unit, peak = work / s / 1e9, "GB/s", HBM_PEAK_GBPS
+    return {"kernel": rec["kernel"], "us_per_launch": rec["avg_us"], "achieved": round(ach, 1), "unit": unit,
+            "frac": round(ach / peak, 4), "profile": rec["profile"]}
 
 
 def time_w12(weights, shape, kv, t_tok, t_par, t_ctx, ctx0, B, K, ctx, acc, bonus, path, ws, stream,
@@ -670,7 +708,10 @@ def gate_up_roofline(step, shape, w, stream, reps, config, w12):
              "traffic": pmc_traffic(config, "w12" if w12 is not None else "bf16"),
              "bytes_per_launch": int(b_launch)}
     r.update({"us_per_launch": round(s_launch * 1e6, 2), "launches_per_step": L,
-              "ms_per_eager_step_with_events": round(ms_ev, 4)})
+              "ms_per_eager_step_with_events": round(ms_ev, 4),
+              "timing": "HIP events around each launch on the verify stream (dispatch included)",
+              "profiled": profiled(config, "w12" if w12 is not None else "bf16",
+                                   r.get("flops_per_launch", b_launch), r["bound"])})
     return r
 
 

@@ -667,6 +667,258 @@ __global__ __launch_bounds__(256) void attn_wave_kernel(
     }
 }
 
+// Many query columns per kv head (a draft tree of tens of nodes, 5 q heads per kv head: 20 query
+// tiles): one workgroup of eight waves per (request, kv head, range of rk keys), the kv head's
+// query tiles dealt to the waves in turn (wave w: tiles w, w + 8, w + 16). Each 32-key stage of
+// the range is fetched once, straight into LDS (global_load_lds, the stage's 2 D/16 blocks of
+// 1 KB spread over the waves, in the wave kernel's layout), NBUF - 1 stages ahead, and every
+// wave multiplies all of its tiles against it, so the keys and values cross HBM once whatever
+// the number of tiles. One barrier per stage: the stage has landed for every wave, and the buffer
+// refilled next was released by all of them. Online softmax per column in the log2 domain; o is
+// rescaled only when some column's maximum moved; P as a bf16 high part plus a bf16 low part as
+// in the other attention kernels; one partial per (range, column) for the combine.
+constexpr int kGroupWaves = 8;
+typedef float float2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+#ifndef SV_GROUP_NBUF
+#define SV_GROUP_NBUF 4
+#endif
+#ifndef SV_GROUP_COMBINE_FEW
+#define SV_GROUP_COMBINE_FEW 1
+#endif
+
+template <int D, int TW>
+__global__ __launch_bounds__(64 * kGroupWaves) void attn_group_kernel(
+    const bf16 *__restrict__ q, const bf16 *__restrict__ k_pool, const bf16 *__restrict__ v_pool,
+    const int32_t *__restrict__ block_table, int max_pages, const int32_t *__restrict__ ctx_len,
+    const uint64_t *__restrict__ anc, const int32_t *__restrict__ status, int K, int nq, int nkv,
+    int n_rg, int rk, float scale_log2, float *__restrict__ part_o, float2 *__restrict__ part_ml) {
+    constexpr int NW = kGroupWaves;
+    constexpr int SK = 32;                 // keys per stage
+    constexpr int CD = D / 8;              // 16-byte columns of a key row
+    constexpr int KB = D / 16;             // 1 KB blocks per stage, keys (values alike)
+    constexpr int SLOTS = 2 * KB * 64;     // 16-byte slots per stage
+    constexpr int LPW = 2 * KB / NW;       // blocks each wave loads per stage
+    static_assert(2 * KB % NW == 0 && LPW >= 1, "a stage's blocks split evenly over the waves");
+    constexpr int NBUF = SV_GROUP_NBUF;    // stage buffers (NBUF - 1 stages in flight)
+    static_assert(NBUF >= 3 && NBUF <= 6, "stage buffers");
+    constexpr int FK = D / 32, DT = D / 16;
+    __shared__ bf16x8 lds[NBUF * SLOTS];
+
+    const int r = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    if (status[b] != 0) return;            // uniform over the workgroup
+    const int ctx = ctx_len[b];
+    const int T = ctx + K;
+    const int kbeg = r * rk;
+    if (kbeg >= T) return;                 // uniform over the workgroup
+    const int n_st = (min(rk, T - kbeg) + SK - 1) / SK;
+    const int group = nq / nkv;
+    const int R = group * K;
+    const int QT = (R + 15) >> 4;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r16 = lane & 15, grp = lane >> 4;
+
+    // page ids of the range, lane i holding page i (rk <= 1024 keys: 64 pages); pages past the
+    // request's last one stand in for the range's first (in bounds; values zeroed before use)
+    const int np_req = (T + 15) >> 4;
+    int pg;
+    {
+        const int p0 = kbeg >> 4, pidx = p0 + lane;
+        pg = block_table[(int64_t)b * max_pages + (pidx < np_req ? pidx : p0)];
+    }
+    // this wave's tiles: query fragments and ancestor masks
+    bf16x8 qf[TW][FK];
+    uint64_t am[TW];
+    bool col_ok[TW];
+#pragma unroll
+    for (int j = 0; j < TW; ++j) {
+        const int rho = 16 * (wave + NW * j) + r16;
+        col_ok[j] = rho < R;
+        const int hh = col_ok[j] ? rho / K : 0, tok = col_ok[j] ? rho % K : 0;
+        const bf16 *qrow = q + ((int64_t)(b * K + tok) * nq + g * group + hh) * D;
+#pragma unroll
+        for (int ds = 0; ds < FK; ++ds) qf[j][ds] = *(const bf16x8 *)(qrow + ds * 32 + grp * 8);
+        am[j] = anc[b * K + tok];
+    }
+
+    auto issue = [&](int sl) __attribute__((always_inline)) {
+        const int64_t p0 = __builtin_amdgcn_readlane(pg, 2 * sl);
+        const int64_t p1 = __builtin_amdgcn_readlane(pg, 2 * sl + 1);
+        bf16x8 *dst = lds + (sl % NBUF) * SLOTS;
+#pragma unroll
+        for (int i = 0; i < LPW; ++i) {
+            const int j = wave + NW * i;   // keys: blocks 0 .. KB - 1; values: KB .. 2 KB - 1
+            const bf16 *src;
+            if (j < KB) {
+                const int key = j * (512 / D) + lane / CD;
+                const int64_t page = (j * (512 / D)) < 16 ? p0 : p1;
+                const int col = (lane % CD) ^ key_swz<D>(key);
+                src = k_pool + ((page * nkv + g) * 16 + (key & 15)) * D + col * 8;
+            } else {
+                const int jv = j - KB;
+                const int64_t page = jv < D / 32 ? p0 : p1;
+                const int d = (jv % (D / 32)) * 32 + (lane >> 1);
+                const int half = (lane & 1) ^ ((d >> 3) & 1);
+                src = v_pool + ((page * nkv + g) * D + d) * 16 + half * 8;
+            }
+            __builtin_amdgcn_global_load_lds((const void *)src,
+                                             (__attribute__((address_space(3))) void *)(dst + j * 64),
+                                             16, 0, 2);   // 2: non-temporal
+        }
+    };
+
+    float m_ref[TW], l_run[TW];
+    floatx4 o[TW][DT];
+#pragma unroll
+    for (int j = 0; j < TW; ++j) {
+        m_ref[j] = -INFINITY;
+        l_run[j] = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[j][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+    const int kr0 = 8 * (r16 >> 2) + (r16 & 3);   // S^T half 0 key row of this lane (half 1: +4)
+
+    // Softmax against a reference per column that moves only when a score passes it by more than
+    // 32 (log2 units): p = 2^(s - m_ref) stays below 2^32, which the fp32 sums and the bf16 high +
+    // low parts carry as well as p <= 1, and o is rescaled (with a wave-wide exchange of the
+    // column maxima) only then: at the first stage where the column sees a key, and practically
+    // never after.
+#pragma unroll
+    for (int s0 = 0; s0 < NBUF - 1; ++s0)
+        if (s0 < n_st) issue(s0);
+    for (int sl = 0; sl < n_st; ++sl) {
+        const int ahead = min(NBUF - 2, n_st - 1 - sl);   // later stages this wave has in flight
+        if (ahead >= 4) wait_vm<4 * LPW>();
+        else if (ahead == 3) wait_vm<3 * LPW>();
+        else if (ahead == 2) wait_vm<2 * LPW>();
+        else if (ahead == 1) wait_vm<LPW>();
+        else wait_vm<0>();
+        __syncthreads();                   // stage sl landed for every wave; stage sl - 1 released
+        if (sl + NBUF - 1 < n_st) issue(sl + NBUF - 1);
+        const int kb = kbeg + sl * SK;
+        const int nvalid = min(SK, T - kb);
+        bf16x8 *ks = lds + (sl % NBUF) * SLOTS;
+        const bf16x8 *vs = ks + KB * 64;
+        if (nvalid < SK) {
+            // the request's last keys: values past them (stale slots, stand-in pages) are zeroed,
+            // since a zero probability times a non-finite value is not zero
+            bf16x8 *vz = ks + KB * 64;
+            for (int idx = threadIdx.x; idx < 2 * D * 2; idx += 64 * NW) {
+                const int pi = idx / (2 * D), d = (idx >> 1) % D, h = idx & 1;
+                const int k0 = pi * 16 + h * 8;
+                if (k0 + 8 <= nvalid) continue;
+                bf16x8 *slot = vz + pi * 2 * D + d * 2 + (h ^ ((d >> 3) & 1));
+                bf16x8 v = *slot;
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (k0 + e >= nvalid) v[e] = (bf16)0.0f;
+                *slot = v;
+            }
+            __syncthreads();
+        }
+        // key fragments: half h covers key rows kr0 + 4h, so each lane ends with keys
+        // 8 grp .. 8 grp + 7 of every tile's S^T
+        bf16x8 kf[2][FK];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int key = kr0 + 4 * h;
+            const int sw = key_swz<D>(key);
+#pragma unroll
+            for (int ds = 0; ds < FK; ++ds) kf[h][ds] = ks[key * CD + ((grp + 4 * ds) ^ sw)];
+        }
+        const bool plain = nvalid == SK && kb + SK <= ctx;
+        const int k0 = kb + 8 * grp;
+        const int n_ctx = min(max(ctx - k0, 0), 8);
+        const int j0 = max(k0 + n_ctx - ctx, 0);       // first draft index among the lane's keys
+        const int n_in = min(max(kb + nvalid - k0, 0), 8);
+        bf16x8 ph[TW], pl[TW];
+        {
+#pragma unroll
+            for (int j = 0; j < TW; ++j) {
+                if (wave + NW * j >= QT) continue;      // uniform over the wave
+                floatx4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ds = 0; ds < FK; ++ds) {
+                    sa = mfma16x16x32(kf[0][ds], qf[j][ds], sa);
+                    sb = mfma16x16x32(kf[1][ds], qf[j][ds], sb);
+                }
+                float sv[8];                            // raw scores q . k
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    sv[e] = sa[e];
+                    sv[e + 4] = sb[e];
+                }
+                if (!plain) {
+                    // committed positions always, draft positions on the column's root path
+                    const unsigned anc8 = j0 < 64 ? (unsigned)(am[j] >> j0) & 0xffu : 0u;
+                    unsigned vis = (((1u << n_ctx) - 1u) | (anc8 << n_ctx)) & ((1u << n_in) - 1u);
+                    if (!col_ok[j]) vis = 0u;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) sv[e] = ((vis >> e) & 1u) ? sv[e] : -INFINITY;
+                }
+                const float mloc = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                                         fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7]))) * scale_log2;
+                if (__any(mloc > m_ref[j] + 32.f)) {
+                    float mc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
+                    mc = fmaxf(mc, __shfl_xor(mc, 32, 64));
+                    const float mn = fmaxf(m_ref[j], mc);
+                    if (mn > m_ref[j]) {
+                        // o and l are still zero where the reference was -inf
+                        const float alpha = m_ref[j] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref[j] - mn);
+                        l_run[j] *= alpha;
+#pragma unroll
+                        for (int dt = 0; dt < DT; ++dt) o[j][dt] = o[j][dt] * alpha;
+                        m_ref[j] = mn;
+                    }
+                }
+                // a column with no visible key yet has only -inf scores: any finite reference
+                // gives p = 0 there
+                const float m_use = m_ref[j] == -INFINITY ? 0.f : m_ref[j];
+#pragma unroll
+                for (int e = 0; e < 8; e += 2) {
+                    const float2v pv = {__builtin_amdgcn_exp2f(__builtin_fmaf(sv[e], scale_log2, -m_use)),
+                                        __builtin_amdgcn_exp2f(__builtin_fmaf(sv[e + 1], scale_log2, -m_use))};
+                    const bf16x2v hi = __builtin_convertvector(pv, bf16x2v);
+                    const float2v rest = {pv.x - (float)hi.x, pv.y - (float)hi.y};
+                    const bf16x2v lo = __builtin_convertvector(rest, bf16x2v);
+                    ph[j][e] = hi.x;
+                    ph[j][e + 1] = hi.y;
+                    pl[j][e] = lo.x;
+                    pl[j][e + 1] = lo.y;
+                    l_run[j] += pv.x + pv.y;
+                }
+            }
+        }
+        // O^T += V^T . P^T: one value fragment per 16 rows of d serves every tile
+        const int vp = grp >> 1, vh = grp & 1;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            const int d = r16 + 16 * dt;
+            const bf16x8 vf = vs[vp * 2 * D + d * 2 + (vh ^ ((d >> 3) & 1))];
+#pragma unroll
+            for (int j = 0; j < TW; ++j) {
+                if (wave + NW * j >= QT) continue;
+                o[j][dt] = mfma16x16x32(vf, ph[j], o[j][dt]);
+                o[j][dt] = mfma16x16x32(vf, pl[j], o[j][dt]);
+            }
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < TW; ++j) {
+        float l = l_run[j];
+        l += __shfl_xor(l, 16, 64);
+        l += __shfl_xor(l, 32, 64);
+        if (wave + NW * j >= QT || !col_ok[j]) continue;
+        const int rho = 16 * (wave + NW * j) + r16;
+        const int64_t base = (((int64_t)b * nkv + g) * n_rg + r) * R + rho;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+            *(floatx4 *)(part_o + base * D + dt * 16 + 4 * grp) = o[j][dt];
+        if (grp == 0) part_ml[base] = make_float2(m_ref[j], l);
+    }
+}
+
 // Merge the partials of one (node, q head): o = sum_c 2^(m_c - m*) O_c / sum_c 2^(m_c - m*) l_c
 // over the partials c (one per chunk, or per range of chunks; kpp keys each). 256 threads = (D/4) column
 // quads x CG groups; each thread merges partials c = cg, cg + CG, ... with every load issued
@@ -824,7 +1076,37 @@ hipError_t attention(const AttnArgs &a, hipStream_t st) {
     int kpp = SV_ATTN_CH, stride = n_small;
     bool few = false;                      // the wave kernel's few partials per (node, q head)
     hipError_t e;
-    if (wgs1 <= SV_ATTN_SMALL_GRID && n_small <= a.n_chunks) {
+    if (QT >= 8 && QT <= 3 * kGroupWaves) {
+        // many query tiles per kv head (a draft tree): the group kernel, ranges sized so that
+        // the (range, kv head, request) workgroups fill the compute units about once, each range
+        // a whole number of 32-key stages, at least one chunk and at most 64 pages
+        const int64_t max_keys = (int64_t)a.max_pages * kPage;
+        const int64_t per = (max_keys * a.nkv * a.B + 255) / 256;
+        int64_t rk64 = (per + 31) / 32 * 32;
+        if (rk64 < kAttnChunk) rk64 = kAttnChunk;
+        if (rk64 > 1024) rk64 = 1024;
+        const int rk = (int)rk64;
+        const int n_rg = (int)((max_keys + rk - 1) / rk);
+        stride = n_rg;
+        kpp = rk;
+        few = SV_GROUP_COMBINE_FEW != 0;
+        const dim3 grid_g(n_rg, a.nkv, a.B);
+        const int tw = (QT + kGroupWaves - 1) / kGroupWaves;
+#define SV_GROUP(DD, TWV)                                                                          \
+    hipLaunchKernelGGL((attn_group_kernel<DD, TWV>), grid_g, dim3(64 * kGroupWaves), 0, st, a.q,     \
+                       a.k_pool, a.v_pool, a.block_table, a.max_pages, a.ctx_len, a.anc, a.status,  \
+                       a.K, a.nq, a.nkv, n_rg, rk, scale_log2, a.part_o, a.part_ml)
+        if (a.D == 128) {
+            if (tw == 1) SV_GROUP(128, 1);
+            else if (tw == 2) SV_GROUP(128, 2);
+            else SV_GROUP(128, 3);
+        } else {
+            if (tw == 1) SV_GROUP(64, 1);
+            else if (tw == 2) SV_GROUP(64, 2);
+            else SV_GROUP(64, 3);
+        }
+#undef SV_GROUP
+    } else if (wgs1 <= SV_ATTN_SMALL_GRID && n_small <= a.n_chunks) {
         const dim3 grid_h(n_small, a.nkv, a.B);
 #define SV_ATTN(DD, NWV)                                                                          \
     hipLaunchKernelGGL((attn_partial_kernel<DD, NWV, 1, SV_ATTN_CH, SV_ATTN_KS>), grid_h,          \
