@@ -78,11 +78,11 @@ PROFILED = {
                         "profile": "profiles/block16_ctx4096_kernels.md"},
     ("tree", "bf16"): {"source": "tree_verification_skinny_amd/csrc/k_gemm.hip",
                        "sha256": "ddfbc8f9ca10bdbd0f872754805e7a8279958f233f49a78b1fe545ae2b832c4b",
-                       "kernel": "gemm_wide_kernel<4, 1, false>", "avg_us": 81.88,
+                       "kernel": "gemm_wide_kernel<4, 1, false>", "avg_us": 79.94,
                        "profile": "profiles/tree64_ctx8192_kernels.md"},
     ("batched", "bf16"): {"source": "tree_verification_skinny_amd/csrc/k_gemm_tc.hip",
                           "sha256": "b4b69ebb59847102b35290782bf7e52eadcf557c320954e21a4c734a0e6afac2",
-                          "kernel": "gemm_tc_kernel<1>", "avg_us": 209.44,
+                          "kernel": "gemm_tc_kernel<1>", "avg_us": 207.09,
                           "profile": "profiles/batched32x16_kernels.md"},
 }
 HBM_PEAK_GBPS = 8000.0
