@@ -59,9 +59,9 @@ PMC_TRAFFIC = {
                         "fetch_kib": 174750.900, "write_kib": 544.0,
                         "fetch_scale": 1.9999849, "write_scale": 1.0},
     ("rec", "bf16"): {"source": "tree_verification_skinny_amd/csrc/k_recurrent.hip",
-                      "sha256": "77c29c1c50fbf0b85f3dc27d12e2235737ccb122353cf2ba1ac1edf1c22781a2",
-                      "fetch_kib": 58591.968, "write_kib": 32768.2,
-                      "fetch_scale": 1.9999851, "write_scale": 1.0},
+                      "sha256": "e4a2e4ece68656d8812df5325d9800fc91a7a8825085a9d28257dc3739e862d6",
+                      "fetch_kib": 58592.0, "write_kib": 32768.1,
+                      "fetch_scale": 1.9999850, "write_scale": 1.0},
     ("block", "w12"): {"source": "tree_verification_skinny_amd/csrc/k_gemm.hip",
                        "sha256": "ddfbc8f9ca10bdbd0f872754805e7a8279958f233f49a78b1fe545ae2b832c4b",
                        "fetch_kib": 131503.451, "write_kib": 544.0,
