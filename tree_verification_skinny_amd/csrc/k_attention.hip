@@ -1076,10 +1076,13 @@ hipError_t attention(const AttnArgs &a, hipStream_t st) {
     int kpp = SV_ATTN_CH, stride = n_small;
     bool few = false;                      // the wave kernel's few partials per (node, q head)
     hipError_t e;
-    if (QT >= 8 && QT <= 3 * kGroupWaves) {
-        // many query tiles per kv head (a draft tree): the group kernel, ranges sized so that
-        // the (range, kv head, request) workgroups fill the compute units about once, each range
-        // a whole number of 32-key stages, at least one chunk and at most 64 pages
+    if (QT <= 3 * kGroupWaves && (QT >= 8 || wgs1 > SV_ATTN_SMALL_GRID)) {
+        // many query tiles per kv head (a draft tree), or a grid too large for one chunk per
+        // workgroup (a batch): the group kernel, ranges sized so that the (range, kv head,
+        // request) workgroups fill the compute units about once, each range a whole number of
+        // 32-key stages, at least one chunk and at most 64 pages (a batch of 32 requests x 16 at
+        // contexts up to 8192: 185 -> 134 us per layer against the wave kernel, whose waves each
+        // hold all five tiles at one wave per SIMD)
         const int64_t max_keys = (int64_t)a.max_pages * kPage;
         const int64_t per = (max_keys * a.nkv * a.B + 255) / 256;
         int64_t rk64 = (per + 31) / 32 * 32;
