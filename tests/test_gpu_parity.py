@@ -310,10 +310,10 @@ def test_tiny_batch_long_contexts_stream_attention():
 
 
 def test_tiny_stream_attention_dominant_keys():
-    """The streamed-range attention when a key far into a wave's range outscores the first keys
-    it saw by hundreds (log2 units): some context key rows are scaled by 300, so the fixed
-    per-column reference would overflow and the wave must take its second pass. No non-finite
-    output; parity with the oracle. Scores 300 times larger make a few columns ill-conditioned
+    """The streamed-range attention when a key far into a range outscores the first keys its
+    columns saw by hundreds (log2 units): some context key rows are scaled by 300, so each
+    column's softmax reference must move (and its sums be rescaled) well after its first stage.
+    No non-finite output; parity with the oracle. Scores 300 times larger make a few columns ill-conditioned
     (where two strong keys nearly tie, one bf16 ulp of q moves the logits by tenths, and the
     float64 evaluation itself leaves the fixed tolerance there): for such a request the GPU
     must be as close to that exact evaluation as the oracle is."""
@@ -393,6 +393,45 @@ def test_tiny_batched_trees_stream_attention():
         accepted += r.accepted_len
     assert near <= 2
     assert accepted > 0
+
+
+def test_gqa_group_of_8_trees_two_tile_groups():
+    """Eight q heads per kv head (16 over 2) and 64-node trees: 512 query columns, 32 tiles per kv
+    head, more than one attention workgroup holds, so the kv head's tiles split into two groups of
+    16 that stream the same keys; a batch of two over contexts of 700 and 1900 keys, unused cache
+    slots NaN. Logits at the fixed tolerance, acceptance exact up to logged near-ties."""
+    shape = synth.Shape(n_layers=2, hidden=256, n_q_heads=16, n_kv_heads=2, head_dim=64, ffn=704,
+                        vocab=1024)
+    B, k = 2, 64
+    ctxs = [700, 1900]
+    w = synth.model_weights(shape, 909)
+    m = oracle_model_from(shape, w)
+    weights = device_weights(shape, w, DEV)
+    kv = make_kv(shape, ctxs, k, 909, DEV)
+    kv.k_pool.fill_(float("nan"))
+    kv.v_pool.fill_(float("nan"))
+    toks, pars, cases = [], [], []
+    for b, ctx in enumerate(ctxs):
+        kvs = [synth.kv_context(shape, ctx, 909, l, request=b) for l in range(2)]
+        kc = [np.ascontiguousarray(bits(x)) for x, _ in kvs]
+        vc = [np.ascontiguousarray(bits(y)) for _, y in kvs]
+        upload_context(kv, b, kc, vc)
+        tokens, parent = planted_tree(m, kc, vc, k, 950 + b)
+        toks.append(tokens)
+        pars.append(parent)
+        cases.append((kc, vc))
+    tokens = np.stack(toks).astype(np.int32)
+    parents = np.stack(pars).astype(np.int32)
+    out = run_verify(weights, kv, tokens, parents, ctxs)
+    near = 0
+    for b in range(B):
+        kc, vc = cases[b]
+        r = oracle.verify(m, kc, vc, tokens[b], parents[b])
+        assert np.isfinite(out.logits[b]).all(), f"request {b}"
+        check_logits(out.logits[b], r.logits, f"request {b}")
+        near += check_accept(r, tokens[b], parents[b], out.greedy[b], int(out.accepted_len[b]),
+                             int(out.bonus[b]), out.path[b])
+    assert near <= 1
 
 
 def test_bad_requests_are_isolated():

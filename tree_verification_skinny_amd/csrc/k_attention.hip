@@ -6,22 +6,22 @@
 // architecture"]. The path is a 64-bit ancestor mask per node (bit j set = node j is on the
 // path), so the mask test in the inner loop is one shift and one AND.
 //
-// Two work splits (split-KV): for a small grid (one request, a block of 16) one workgroup per
-// (request, kv head, chunk of 192 keys), whose waves stage the chunk's keys [192][D] and values
-// [D][192] from the cache pages into LDS and take 16-column query tiles (optionally several
-// waves per tile, one per part of the chunk, merged in LDS); for a large grid (a batch, a
-// 64-node tree), over chunks of 128 keys, one wave per (request,
-// kv head, tile group, range of chunks), which streams its keys and values through LDS 32 at a
-// time (attn_wave_kernel). The query columns are (q head of this kv group, draft node) pairs, so
+// Two work splits (split-KV): for one request with few query tiles (a block of 16) one
+// workgroup per (request, kv head, chunk of 192 keys), whose waves stage the chunk's keys
+// [192][D] and values [D][192] from the cache pages into LDS and take 16-column query tiles
+// (attn_partial_kernel); for everything else (a draft tree's many tiles, a batch of requests)
+// one workgroup of eight waves per (request, kv head, group of query tiles, range of keys),
+// which streams the range through LDS 32 keys at a time for all of the group's tiles
+// (attn_group_kernel). The query columns are (q head of this kv group, draft node) pairs, so
 // one K/V tile in LDS serves every q head of the group. Per 32 keys and tile:
-//   S^T = K . Q^T   (A = keys from LDS, B = Q^T held in registers for the whole chunk)
-//   online softmax per query column, in the log2 domain
+//   S^T = K . Q^T   (A = keys from LDS, B = Q^T held in registers)
+//   softmax per query column, in the log2 domain
 //   O^T += V^T . P^T (A = transposed values from LDS, B = the probabilities this lane already
 //                     holds, as a bf16 high part plus a bf16 low part)
 // The S^T tiles take their 16 key rows in the order 8*(r/4) + 4*tile + r%4, which leaves each
 // lane holding 8 consecutive keys: exactly the P^T fragment the V^T MFMA wants, so no lane
-// exchange is needed between the two products. Chunk partials (unnormalised O, running max,
-// running sum) are merged by attn_combine.
+// exchange is needed between the two products. Chunk and range partials (unnormalised O,
+// softmax reference, running sum) are merged by attn_combine / attn_combine_few.
 #include "kernels.hpp"
 
 namespace sv {
@@ -315,16 +315,8 @@ __global__ __launch_bounds__(64 * NW * HPW * KS) void attn_partial_kernel(
     }
 }
 
-// Large grids (a batch, or a draft tree with hundreds of query rows), wave per key range: a
-// workgroup takes one (request, kv head, tile group) and 4 cpr consecutive chunks, dealt to its
-// waves in turn (wave w: chunks w, w + 4, ...). The tile group's TPW query tiles (all five of a
-// block of 16 with 5 q heads per kv head) sit in LDS once for the four waves. Each wave streams
-// its own keys and values through its own two LDS stages of 32 keys, straight from HBM
-// (global_load_lds, non-temporal, the next stage's loads out before the current one is
-// awaited), and reads only what it loaded itself, so the key loop has no workgroup barrier:
-// after s_waitcnt the stage is in LDS. Every key and value fragment read from LDS feeds TPW tiles. At the end the
-// four waves' states are merged in LDS, in wave order, into one partial per workgroup.
-// A stage is written into LDS 1 KB per wave instruction (lane l fills bytes 16 l .. 16 l + 15):
+// Staged key/value layout of the group kernel: a 32-key stage is written into LDS 1 KB per wave
+// instruction (global_load_lds, lane l fills bytes 16 l .. 16 l + 15):
 //   keys   [32][D]; 16-byte column c of key k is stored at column c ^ key_swz(k), so the 16 key
 //          rows an S^T fragment read touches fall in 16 different bank groups;
 //   values page by page as the cache holds them, [page][D][16 slots]; the two 8-slot halves of
@@ -342,334 +334,10 @@ __device__ __forceinline__ void wait_vm() {
     __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | 0x70 | 0xF00);
 }
 
-template <int D, int TPW>
-__global__ __launch_bounds__(256) void attn_wave_kernel(
-    const bf16 *__restrict__ q, const bf16 *__restrict__ k_pool, const bf16 *__restrict__ v_pool,
-    const int32_t *__restrict__ block_table, int max_pages, const int32_t *__restrict__ ctx_len,
-    const uint64_t *__restrict__ anc, const int32_t *__restrict__ status, int K, int nq, int nkv,
-    int n_wr, int cpr, int n_tg, float scale_log2, float *__restrict__ part_o,
-    float2 *__restrict__ part_ml) {
-    constexpr int SK = 32;                 // keys per stage
-    constexpr int CD = D / 8;              // 16-byte columns of a key row
-    constexpr int KB = D / 16;             // 1 KB blocks per stage, keys (values alike)
-    constexpr int SLOTS = 2 * KB * 64;     // 16-byte slots per stage
-    constexpr int FK = D / 32;
-    constexpr int DT = D / 16;
-    constexpr int PPC = kAttnChunk / 16;   // pages per chunk
-    constexpr int QOFF = 4 * 2 * SLOTS;    // query fragments after the stages
-    constexpr int MSTRIDE = TPW * DT * 64 + TPW * 16 / 2;   // merge area of one wave (slots)
-    static_assert(3 * MSTRIDE <= QOFF, "the merge reuses the stage area");
-    __shared__ bf16x8 lds[QOFF + TPW * FK * 64];
-
-    const int wr = blockIdx.x;
-    const int g = blockIdx.y / n_tg, tg = blockIdx.y % n_tg;
-    const int b = blockIdx.z;
-    if (status[b] != 0) return;            // uniform over the workgroup
-    const int ctx = ctx_len[b];
-    const int T = ctx + K;
-    const int nc = (T + kAttnChunk - 1) / kAttnChunk;
-    const int c0 = wr * 4 * cpr;
-    if (c0 >= nc) return;                  // uniform over the workgroup
-    const int group = nq / nkv;
-    const int R = group * K;
-    const int QT = (R + 15) >> 4;
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int r16 = lane & 15, grp = lane >> 4;
-
-    // the tile group's query fragments into LDS, fragment (t, ds) as 64 lanes x 16 bytes; tiles
-    // past the group reuse row 0's query and are never stored
-    for (int i = threadIdx.x; i < TPW * FK * 64; i += 256) {
-        const int t = i / (FK * 64), ds = (i / 64) % FK, l = i % 64;
-        const int tile = tg * TPW + t;
-        const int rho = 16 * tile + (l & 15);
-        const bool ok = tile < QT && rho < R;
-        const int hh = ok ? rho / K : 0, tok = ok ? rho % K : 0;
-        lds[QOFF + i] = *(const bf16x8 *)(q + ((int64_t)(b * K + tok) * nq + g * group + hh) * D +
-                                          ds * 32 + (l >> 4) * 8);
-    }
-    uint64_t am[TPW];
-    bool col_ok[TPW];
-#pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-        const int tile = tg * TPW + t;
-        const int rho = 16 * tile + r16;
-        col_ok[t] = tile < QT && rho < R;
-        am[t] = anc[b * K + (col_ok[t] ? rho % K : 0)];
-    }
-
-    // this wave's chunks c0 + wave + 4 j (j < n_ch), in stages of 32 keys: stage sl is keys
-    // 32 (sl % 4) .. of chunk j = sl / 4; only the request's last chunk is short, and it is the
-    // last chunk of the wave that holds it
-    const int c_lim = min(c0 + 4 * cpr, nc);
-    const int n_ch = c0 + wave < c_lim ? (c_lim - c0 - wave + 3) / 4 : 0;
-    const int c_last = c0 + wave + 4 * (n_ch - 1);
-    const int n_st = n_ch > 0 ? 4 * (n_ch - 1) + (min(T - c_last * kAttnChunk, kAttnChunk) + SK - 1) / SK : 0;
-    auto stage_key = [&](int sl) __attribute__((always_inline)) { return (c0 + wave + 4 * (sl >> 2)) * kAttnChunk + (sl & 3) * SK; };
-    bf16x8 *ldw = &lds[wave * 2 * SLOTS];
-    // page ids: lane 8 j + p -> page p of chunk j (cpr <= 8 chunks, so at most 64); pages past
-    // the request's last one stand in for the chunk's first (in bounds; values zeroed before use)
-    const int np_req = (T + 15) >> 4;
-    int pg = 0;
-    if ((lane >> 3) < n_ch) {
-        const int c = c0 + wave + 4 * (lane >> 3);
-        const int pidx = c * PPC + (lane & 7);
-        pg = block_table[(int64_t)b * max_pages + (pidx < np_req ? pidx : c * PPC)];
-    }
-    auto issue = [&](int sl, int buf) __attribute__((always_inline)) {
-        const int li = 8 * (sl >> 2) + 2 * (sl & 3);
-        const int64_t p0 = __builtin_amdgcn_readlane(pg, li);
-        const int64_t p1 = __builtin_amdgcn_readlane(pg, li + 1);
-        bf16x8 *dst = ldw + buf * SLOTS;
-#pragma unroll
-        for (int j = 0; j < KB; ++j) {
-            const int key = j * (512 / D) + lane / CD;     // stage key (the block's page is uniform)
-            const int64_t page = (j * (512 / D)) < 16 ? p0 : p1;
-            const int col = (lane % CD) ^ key_swz<D>(key);
-            const bf16 *src = k_pool + ((page * nkv + g) * 16 + (key & 15)) * D + col * 8;
-            __builtin_amdgcn_global_load_lds((const void *)src,
-                                             (__attribute__((address_space(3))) void *)(dst + j * 64),
-                                             16, 0, 2);   // 2: non-temporal
-        }
-#pragma unroll
-        for (int j = 0; j < KB; ++j) {
-            const int64_t page = j < D / 32 ? p0 : p1;
-            const int d = (j % (D / 32)) * 32 + (lane >> 1);
-            const int half = (lane & 1) ^ ((d >> 3) & 1);
-            const bf16 *src = v_pool + ((page * nkv + g) * D + d) * 16 + half * 8;
-            __builtin_amdgcn_global_load_lds((const void *)src,
-                                             (__attribute__((address_space(3))) void *)(dst + (KB + j) * 64),
-                                             16, 0, 2);   // 2: non-temporal
-        }
-    };
-
-    float m_run[TPW], l_run[TPW];
-    floatx4 o[TPW][DT];
-#pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-        m_run[t] = -INFINITY;
-        l_run[t] = 0.f;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) o[t][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
-    }
-    const int kr0 = 8 * (r16 >> 2) + (r16 & 3);
-    const bf16x8 *qs = lds + QOFF;
-    __syncthreads();                       // query fragments in place
-
-    // Stage sl in two halves. front: wait for the stage, start the next one's loads, S^T for
-    // every tile (masked, unscaled), and where asked each lane's maximum; back: p = 2^(s - m)
-    // against a fixed reference m per column, O^T += V^T . P^T and the column sums l += 1 . P^T
-    // on the matrix core. A column's reference is the maximum of the first stage in which it
-    // sees a key (a wave-wide exchange; o and l are still zero then): a wave's first stage, or
-    // a stage on the draft nodes. It never moves after that, so the hot loop never rescales o.
-    // o / l does not depend on the reference; p may exceed 1, and while no score passes its
-    // reference by more than 64 (log2 units) the fp32 sums and bf16 hi + lo carry it as well as
-    // p <= 1. If one does (l > 2^64 shows it), the wave finds the columns' true maxima in a
-    // max-only pass and streams its chunks again against them.
-    float s[TPW][8];
-    float mloc[TPW];
-    auto front = [&](int sl, bool want_max) __attribute__((always_inline)) {
-        const int buf = sl & 1;
-        const bf16x8 *ks = ldw + buf * SLOTS;
-        const int kb = stage_key(sl);
-        const int nvalid = min(SK, T - kb);
-        // the next stage's loads go out before this one is awaited (its buffer held stage
-        // sl - 1, consumed in the previous iteration), so two stages are in flight meanwhile
-        if (sl + 1 < n_st) {
-            issue(sl + 1, buf ^ 1);
-            wait_vm<2 * KB>();             // all but the next stage's 2 KB loads: this stage landed
-        } else {
-            wait_vm<0>();
-        }
-        if (nvalid < SK) {
-            // the request's last keys: values past them (stale slots, stand-in pages) are zeroed,
-            // since a zero probability times a non-finite value is not zero
-            bf16x8 *vz = ldw + buf * SLOTS + KB * 64;
-            for (int idx = lane; idx < 2 * D * 2; idx += 64) {
-                const int pi = idx / (2 * D), d = (idx >> 1) % D, h = idx & 1;
-                const int k0 = pi * 16 + h * 8;
-                if (k0 + 8 <= nvalid) continue;
-                bf16x8 *slot = vz + pi * 2 * D + d * 2 + (h ^ ((d >> 3) & 1));
-                bf16x8 v = *slot;
-#pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    if (k0 + j >= nvalid) v[j] = (bf16)0.0f;
-                *slot = v;
-            }
-        }
-        // key fragments of the stage: half h covers key rows kr0 + 4h, so that each lane ends
-        // with keys 8 grp .. 8 grp + 7 of every tile's S^T
-        bf16x8 kf[2][FK];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int key = kr0 + 4 * h;
-            const int sw = key_swz<D>(key);
-#pragma unroll
-            for (int ds = 0; ds < FK; ++ds) kf[h][ds] = ks[key * CD + ((grp + 4 * ds) ^ sw)];
-        }
-        const bool plain = nvalid == SK && kb + SK <= ctx;
-        const int k0 = kb + 8 * grp;
-        const int n_ctx = min(max(ctx - k0, 0), 8);
-        const int j0 = max(k0 + n_ctx - ctx, 0);
-        const int n_in = min(max(kb + nvalid - k0, 0), 8);
-#pragma unroll
-        for (int t = 0; t < TPW; ++t) {
-            floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ds = 0; ds < FK; ++ds) {
-                const bf16x8 qv = qs[(t * FK + ds) * 64 + lane];
-                s0 = mfma16x16x32(kf[0][ds], qv, s0);
-                s1 = mfma16x16x32(kf[1][ds], qv, s1);
-            }
-#pragma unroll
-            for (int e2 = 0; e2 < 4; ++e2) {
-                s[t][e2] = s0[e2];
-                s[t][e2 + 4] = s1[e2];
-            }
-            if (!plain) {
-                // committed positions always, draft positions on the column's root path
-                const unsigned anc8 = j0 < 64 ? (unsigned)(am[t] >> j0) & 0xffu : 0u;
-                unsigned vis = (((1u << n_ctx) - 1u) | (anc8 << n_ctx)) & ((1u << n_in) - 1u);
-                if (!col_ok[t]) vis = 0u;
-#pragma unroll
-                for (int e2 = 0; e2 < 8; ++e2) s[t][e2] = ((vis >> e2) & 1u) ? s[t][e2] : -INFINITY;
-            }
-            if (want_max || !plain)
-                mloc[t] = fmaxf(fmaxf(fmaxf(s[t][0], s[t][1]), fmaxf(s[t][2], s[t][3])),
-                                fmaxf(fmaxf(s[t][4], s[t][5]), fmaxf(s[t][6], s[t][7]))) * scale_log2;
-        }
-        return plain;
-    };
-    bf16x8 ones;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) ones[j] = (bf16)1.0f;
-    floatx4 lacc[TPW];
-    auto back = [&](int sl) __attribute__((always_inline)) {
-        const bf16x8 *vs = ldw + (sl & 1) * SLOTS + KB * 64;
-        bf16x8 ph[TPW], pl[TPW];
-#pragma unroll
-        for (int t = 0; t < TPW; ++t) {
-            // a column with no visible key yet has only -inf scores, so any finite reference
-            // gives p = 0 there
-            const float m_use = m_run[t] == -INFINITY ? 0.f : m_run[t];
-#pragma unroll
-            for (int e2 = 0; e2 < 8; ++e2) {
-                const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][e2], scale_log2, -m_use));
-                const bf16 hi = to_bf(pv);
-                ph[t][e2] = hi;
-                pl[t][e2] = to_bf(pv - to_f(hi));
-            }
-            lacc[t] = mfma16x16x32(ones, ph[t], lacc[t]);
-            lacc[t] = mfma16x16x32(ones, pl[t], lacc[t]);
-        }
-        // one value fragment per 16 rows of d serves every tile
-        const int vp = grp >> 1, vh = grp & 1;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-            const int d = r16 + 16 * dt;
-            const bf16x8 vf = vs[vp * 2 * D + d * 2 + (vh ^ ((d >> 3) & 1))];
-#pragma unroll
-            for (int t = 0; t < TPW; ++t) {
-                o[t][dt] = mfma16x16x32(vf, ph[t], o[t][dt]);
-                o[t][dt] = mfma16x16x32(vf, pl[t], o[t][dt]);
-            }
-        }
-    };
-    auto col_max = [&](float v) __attribute__((always_inline)) {
-        v = fmaxf(v, __shfl_xor(v, 16, 64));
-        return fmaxf(v, __shfl_xor(v, 32, 64));
-    };
-    auto pass = [&]() __attribute__((always_inline)) {
-#pragma unroll
-        for (int t = 0; t < TPW; ++t) lacc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
-        if (n_st > 0) issue(0, 0);
-        for (int sl = 0; sl < n_st; ++sl) {
-            const bool plain = front(sl, sl == 0);
-            if (sl == 0 || !plain) {
-                bool fresh = false;
-#pragma unroll
-                for (int t = 0; t < TPW; ++t) fresh |= m_run[t] == -INFINITY && mloc[t] > -INFINITY;
-                if (__any(fresh)) {
-#pragma unroll
-                    for (int t = 0; t < TPW; ++t) {
-                        const float mc = col_max(mloc[t]);
-                        if (m_run[t] == -INFINITY) m_run[t] = mc;
-                    }
-                }
-            }
-            back(sl);
-        }
-#pragma unroll
-        for (int t = 0; t < TPW; ++t) l_run[t] = lacc[t][0];
-    };
-    pass();
-    bool ovf = false;
-#pragma unroll
-    for (int t = 0; t < TPW; ++t) ovf |= !(l_run[t] <= 0x1p64f);   // NaN from an inf too
-    if (__any(ovf)) {
-        // some score passed its column's reference by more than 64: the true maxima first
-        float tmax[TPW];
-#pragma unroll
-        for (int t = 0; t < TPW; ++t) tmax[t] = -INFINITY;
-        if (n_st > 0) issue(0, 0);
-        for (int sl = 0; sl < n_st; ++sl) {
-            front(sl, true);
-#pragma unroll
-            for (int t = 0; t < TPW; ++t) tmax[t] = fmaxf(tmax[t], mloc[t]);
-        }
-#pragma unroll
-        for (int t = 0; t < TPW; ++t) {
-            m_run[t] = col_max(tmax[t]);
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) o[t][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
-        }
-        pass();
-    }
-
-    // merge the four waves' states in wave order: waves 1..3 leave theirs in the stage area
-    __syncthreads();                       // every wave is done with its stages
-    if (wave > 0) {
-        floatx4 *mo = reinterpret_cast<floatx4 *>(lds + (wave - 1) * MSTRIDE);
-        float2 *mml = reinterpret_cast<float2 *>(lds + (wave - 1) * MSTRIDE + TPW * DT * 64);
-#pragma unroll
-        for (int t = 0; t < TPW; ++t) {
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) mo[(t * DT + dt) * 64 + lane] = o[t][dt];
-            if (grp == 0) mml[t * 16 + r16] = make_float2(m_run[t], l_run[t]);
-        }
-    }
-    __syncthreads();
-    if (wave != 0) return;
-    for (int w = 1; w < 4; ++w) {
-        const floatx4 *mo = reinterpret_cast<const floatx4 *>(lds + (w - 1) * MSTRIDE);
-        const float2 *mml = reinterpret_cast<const float2 *>(lds + (w - 1) * MSTRIDE + TPW * DT * 64);
-#pragma unroll
-        for (int t = 0; t < TPW; ++t) {
-            const float2 ml = mml[t * 16 + r16];
-            if (ml.x == -INFINITY) continue;
-            const float mn = fmaxf(m_run[t], ml.x);
-            const float a = __builtin_amdgcn_exp2f(m_run[t] - mn), aw = __builtin_amdgcn_exp2f(ml.x - mn);
-            l_run[t] = l_run[t] * a + ml.y * aw;
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) o[t][dt] = o[t][dt] * a + mo[(t * DT + dt) * 64 + lane] * aw;
-            m_run[t] = mn;
-        }
-    }
-#pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-        if (!col_ok[t]) continue;
-        const int rho = 16 * (tg * TPW + t) + r16;
-        const int64_t base = (((int64_t)b * nkv + g) * n_wr + wr) * R + rho;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-            *(floatx4 *)(part_o + base * D + dt * 16 + 4 * grp) = o[t][dt];
-        if (grp == 0) part_ml[base] = make_float2(m_run[t], l_run[t]);
-    }
-}
-
 // Many query columns per kv head (a draft tree of tens of nodes, 5 q heads per kv head: 20 query
-// tiles): one workgroup of eight waves per (request, kv head, range of rk keys), the kv head's
-// query tiles dealt to the waves in turn (wave w: tiles w, w + 8, w + 16). Each 32-key stage of
+// tiles), or many requests: one workgroup of eight waves per (request, kv head, group of up to
+// 8 TW query tiles, range of rk keys), the group's query tiles dealt to the waves in turn
+// (wave w: tiles w, w + 8, w + 16 of the group). Each 32-key stage of
 // the range is fetched once, straight into LDS (global_load_lds, the stage's 2 D/16 blocks of
 // 1 KB spread over the waves, in the wave kernel's layout), NBUF - 1 stages ahead, and every
 // wave multiplies all of its tiles against it, so the keys and values cross HBM once whatever
@@ -692,7 +360,7 @@ __global__ __launch_bounds__(64 * kGroupWaves) void attn_group_kernel(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k_pool, const bf16 *__restrict__ v_pool,
     const int32_t *__restrict__ block_table, int max_pages, const int32_t *__restrict__ ctx_len,
     const uint64_t *__restrict__ anc, const int32_t *__restrict__ status, int K, int nq, int nkv,
-    int n_rg, int rk, float scale_log2, float *__restrict__ part_o, float2 *__restrict__ part_ml) {
+    int n_rg, int rk, int n_tg, float scale_log2, float *__restrict__ part_o, float2 *__restrict__ part_ml) {
     constexpr int NW = kGroupWaves;
     constexpr int SK = 32;                 // keys per stage
     constexpr int CD = D / 8;              // 16-byte columns of a key row
@@ -705,7 +373,8 @@ __global__ __launch_bounds__(64 * kGroupWaves) void attn_group_kernel(
     constexpr int FK = D / 32, DT = D / 16;
     __shared__ bf16x8 lds[NBUF * SLOTS];
 
-    const int r = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int r = blockIdx.x, g = blockIdx.y / n_tg, b = blockIdx.z;
+    const int t0 = (blockIdx.y % n_tg) * (kGroupWaves * TW);   // this workgroup's first query tile
     if (status[b] != 0) return;            // uniform over the workgroup
     const int ctx = ctx_len[b];
     const int T = ctx + K;
@@ -733,7 +402,7 @@ __global__ __launch_bounds__(64 * kGroupWaves) void attn_group_kernel(
     bool col_ok[TW];
 #pragma unroll
     for (int j = 0; j < TW; ++j) {
-        const int rho = 16 * (wave + NW * j) + r16;
+        const int rho = 16 * (t0 + wave + NW * j) + r16;
         col_ok[j] = rho < R;
         const int hh = col_ok[j] ? rho / K : 0, tok = col_ok[j] ? rho % K : 0;
         const bf16 *qrow = q + ((int64_t)(b * K + tok) * nq + g * group + hh) * D;
@@ -836,7 +505,7 @@ __global__ __launch_bounds__(64 * kGroupWaves) void attn_group_kernel(
         {
 #pragma unroll
             for (int j = 0; j < TW; ++j) {
-                if (wave + NW * j >= QT) continue;      // uniform over the wave
+                if (t0 + wave + NW * j >= QT) continue;      // uniform over the wave
                 floatx4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ds = 0; ds < FK; ++ds) {
@@ -898,7 +567,7 @@ __global__ __launch_bounds__(64 * kGroupWaves) void attn_group_kernel(
             const bf16x8 vf = vs[vp * 2 * D + d * 2 + (vh ^ ((d >> 3) & 1))];
 #pragma unroll
             for (int j = 0; j < TW; ++j) {
-                if (wave + NW * j >= QT) continue;
+                if (t0 + wave + NW * j >= QT) continue;
                 o[j][dt] = mfma16x16x32(vf, ph[j], o[j][dt]);
                 o[j][dt] = mfma16x16x32(vf, pl[j], o[j][dt]);
             }
@@ -909,8 +578,8 @@ __global__ __launch_bounds__(64 * kGroupWaves) void attn_group_kernel(
         float l = l_run[j];
         l += __shfl_xor(l, 16, 64);
         l += __shfl_xor(l, 32, 64);
-        if (wave + NW * j >= QT || !col_ok[j]) continue;
-        const int rho = 16 * (wave + NW * j) + r16;
+        if (t0 + wave + NW * j >= QT || !col_ok[j]) continue;
+        const int rho = 16 * (t0 + wave + NW * j) + r16;
         const int64_t base = (((int64_t)b * nkv + g) * n_rg + r) * R + rho;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
@@ -1040,9 +709,8 @@ __global__ __launch_bounds__(256) void attn_combine_few_kernel(
     store4(dst, o[0] / l, o[1] / l, o[2] / l, o[3] / l);
 }
 
-// Tunables: the largest chunk-kernel grid (workgroups) before the wave kernel takes over, the
-// chunk kernel's keys per workgroup and waves per query tile, and a fixed chunk count per wave
-// for the wave kernel (0: chosen per launch, below).
+// Tunables: the largest chunk-kernel grid (workgroups) before the group kernel takes over, and
+// the chunk kernel's keys per workgroup and waves per query tile.
 #ifndef SV_ATTN_SMALL_GRID
 #define SV_ATTN_SMALL_GRID 512
 #endif
@@ -1052,39 +720,39 @@ __global__ __launch_bounds__(256) void attn_combine_few_kernel(
 #ifndef SV_ATTN_KS
 #define SV_ATTN_KS 1                                    // waves per query tile (key parts)
 #endif
-#ifndef SV_ATTN_CPW
-#define SV_ATTN_CPW 0
-#endif
 
 hipError_t attention(const AttnArgs &a, hipStream_t st) {
     const float scale_log2 = kLog2e / sqrtf((float)a.D);
-    // tile slots per kv head: 5 when that takes fewer query tiles per slot than 4 (one tile each
-    // for a group of 5 q heads and a block of 16), else 4
     const int R = a.nq / a.nkv * a.K;
     const int QT = (R + 15) / 16;
-    const int nw = (QT + 4) / 5 < (QT + 3) / 4 ? 5 : 4;
-    const int n_tg = (QT + nw - 1) / nw;
-    // A small grid (one request, a short draft) runs one chunk of SV_ATTN_CH keys and one kv
-    // head per workgroup (one per compute unit: 176 at a 4096-token context and 8 kv heads,
-    // 13.5 us on the 27B block against 14.4 for 128-key chunks over two heads, which leave half
-    // the units idle, and 16.2 for 128-key chunks over one head, eight workgroups too many for one
-    // round; two waves per tile measured 14.6). A large one (a batch, or hundreds of query rows)
-    // streams ranges of chunks through LDS, one kv head per workgroup.
+    // One request and few query tiles (a block of 16 with 5 q heads per kv head: 5 tiles): one
+    // chunk of SV_ATTN_CH keys and one kv head per workgroup, a tile per wave (one workgroup per
+    // compute unit: 176 at a 4096-token context and 8 kv heads, 13.4 us on the 27B block against
+    // 14.4 for 128-key chunks over two heads, which leave half the units idle, and 16.2 for
+    // 128-key chunks over one head, eight workgroups too many for one round; two waves per tile
+    // measured 14.6). Everything else (a draft tree's many tiles, a batch of requests) runs the
+    // group kernel.
+    const int nw = (QT + 4) / 5 < (QT + 3) / 4 ? 5 : 4;   // chunk kernel: 5 tile slots or 4
     const int64_t max_keys = (int64_t)a.max_pages * kPage;
     const int n_small = (int)((max_keys + SV_ATTN_CH - 1) / SV_ATTN_CH);
-    const int64_t wgs1 = (int64_t)n_small * a.nkv * a.B * n_tg;
-    int kpp = SV_ATTN_CH, stride = n_small;
-    bool few = false;                      // the wave kernel's few partials per (node, q head)
-    hipError_t e;
-    if (QT <= 3 * kGroupWaves && (QT >= 8 || wgs1 > SV_ATTN_SMALL_GRID)) {
-        // many query tiles per kv head (a draft tree), or a grid too large for one chunk per
-        // workgroup (a batch): the group kernel, ranges sized so that the (range, kv head,
-        // request) workgroups fill the compute units about once, each range a whole number of
-        // 32-key stages, at least one chunk and at most 64 pages (a batch of 32 requests x 16 at
-        // contexts up to 8192: 185 -> 134 us per layer against the wave kernel, whose waves each
-        // hold all five tiles at one wave per SIMD)
-        const int64_t max_keys = (int64_t)a.max_pages * kPage;
-        const int64_t per = (max_keys * a.nkv * a.B + 255) / 256;
+    const int64_t wgs1 = (int64_t)n_small * a.nkv * a.B;
+    const bool small = QT < 8 && wgs1 <= SV_ATTN_SMALL_GRID && n_small <= a.n_chunks;
+    int kpp, stride;
+    bool few;
+    if (!small) {
+        // the group kernel: a kv head's query tiles in groups of up to 24 (three per wave),
+        // ranges sized so that the (range, tile group, kv head, request) workgroups fill the
+        // compute units about once, each range a whole number of 32-key stages, at least one
+        // chunk and at most 64 pages. A 64-node tree at 5 q heads per kv head is one group of 20
+        // tiles (ranges of 288 keys at an 8192-token context); a batch of 32 requests x 16 at
+        // contexts up to 8192 is one group of 5 per request (ranges of 1024 keys): 134 us per
+        // layer against 185 for a kernel whose waves each held all five tiles at one wave per
+        // SIMD, 33.6 us on the tree against 49.3 for that kernel's four tile groups, each of
+        // which streamed the same keys
+        const int n_tg = (QT + 3 * kGroupWaves - 1) / (3 * kGroupWaves);
+        const int tpg = (QT + n_tg - 1) / n_tg;                 // tiles per group
+        const int tw = (tpg + kGroupWaves - 1) / kGroupWaves;   // tiles per wave
+        const int64_t per = (max_keys * a.nkv * n_tg * a.B + 255) / 256;
         int64_t rk64 = (per + 31) / 32 * 32;
         if (rk64 < kAttnChunk) rk64 = kAttnChunk;
         if (rk64 > 1024) rk64 = 1024;
@@ -1093,12 +761,11 @@ hipError_t attention(const AttnArgs &a, hipStream_t st) {
         stride = n_rg;
         kpp = rk;
         few = SV_GROUP_COMBINE_FEW != 0;
-        const dim3 grid_g(n_rg, a.nkv, a.B);
-        const int tw = (QT + kGroupWaves - 1) / kGroupWaves;
+        const dim3 grid_g(n_rg, a.nkv * n_tg, a.B);
 #define SV_GROUP(DD, TWV)                                                                          \
     hipLaunchKernelGGL((attn_group_kernel<DD, TWV>), grid_g, dim3(64 * kGroupWaves), 0, st, a.q,     \
                        a.k_pool, a.v_pool, a.block_table, a.max_pages, a.ctx_len, a.anc, a.status,  \
-                       a.K, a.nq, a.nkv, n_rg, rk, scale_log2, a.part_o, a.part_ml)
+                       a.K, a.nq, a.nkv, n_rg, rk, n_tg, scale_log2, a.part_o, a.part_ml)
         if (a.D == 128) {
             if (tw == 1) SV_GROUP(128, 1);
             else if (tw == 2) SV_GROUP(128, 2);
@@ -1109,7 +776,10 @@ hipError_t attention(const AttnArgs &a, hipStream_t st) {
             else SV_GROUP(64, 3);
         }
 #undef SV_GROUP
-    } else if (wgs1 <= SV_ATTN_SMALL_GRID && n_small <= a.n_chunks) {
+    } else {
+        kpp = SV_ATTN_CH;
+        stride = n_small;
+        few = false;
         const dim3 grid_h(n_small, a.nkv, a.B);
 #define SV_ATTN(DD, NWV)                                                                          \
     hipLaunchKernelGGL((attn_partial_kernel<DD, NWV, 1, SV_ATTN_CH, SV_ATTN_KS>), grid_h,          \
@@ -1124,55 +794,11 @@ hipError_t attention(const AttnArgs &a, hipStream_t st) {
             else { SV_ATTN(64, 5); }
         }
 #undef SV_ATTN
-    } else {
-        // workgroups of four waves, 4 cpw chunks per workgroup (cpw per wave), one partial per
-        // workgroup; one workgroup per compute unit (two at D = 64). At least 2 and
-        // ceil(R / 128) chunks per wave (a partial, R x D fp32, then stays below about a quarter
-        // of the keys and values the workgroup covers), at most 8 (a wave's page ids fit one
-        // wave), and the count that makes the fewest rounds of workgroups (counted over the
-        // longest request) times the time of one (cpw chunks plus a fixed share)
-        const int tpw = QT <= 2 ? 2 : 5;
-        const int tgs = (QT + tpw - 1) / tpw;
-        const int per_round = a.D == 128 ? 256 : 512;
-        int cpr_min = (R + 127) / 128;
-        if (cpr_min < 2) cpr_min = 2;      // eight stages per wave at least
-        if (cpr_min > 8) cpr_min = 8;
-        int64_t best = -1;
-        int cpw = 1;
-        const int cp_lo = SV_ATTN_CPW > 0 ? SV_ATTN_CPW : cpr_min;
-        const int cp_hi = SV_ATTN_CPW > 0 ? SV_ATTN_CPW : 8;
-        for (int cp = cp_lo; cp <= cp_hi; ++cp) {
-            const int64_t wgs = (int64_t)((a.n_chunks + 4 * cp - 1) / (4 * cp)) * a.nkv * a.B * tgs;
-            // a workgroup's fixed work (query tiles, page ids, the first stage's latency, the
-            // merge, its partial and the combine's read of it) counts as about 3 chunks
-            const int64_t cost = (wgs + per_round - 1) / per_round * (cp + 3);
-            if (best < 0 || cost < best) {
-                best = cost;
-                cpw = cp;
-            }
-        }
-        const int n_wr = (a.n_chunks + 4 * cpw - 1) / (4 * cpw);
-        stride = n_wr;
-        kpp = 4 * cpw * kAttnChunk;        // keys per partial, for the combine
-        few = true;
-        const dim3 grid_w(n_wr, a.nkv * tgs, a.B);
-#define SV_WAVE(DD, TP)                                                                           \
-    hipLaunchKernelGGL((attn_wave_kernel<DD, TP>), grid_w, dim3(256), 0, st, a.q, a.k_pool,        \
-                       a.v_pool, a.block_table, a.max_pages, a.ctx_len, a.anc, a.status, a.K,     \
-                       a.nq, a.nkv, n_wr, cpw, tgs, scale_log2, a.part_o, a.part_ml)
-        if (a.D == 128) {
-            if (tpw == 2) SV_WAVE(128, 2);
-            else SV_WAVE(128, 5);
-        } else {
-            if (tpw == 2) SV_WAVE(64, 2);
-            else SV_WAVE(64, 5);
-        }
-#undef SV_WAVE
     }
-    e = hipGetLastError();
+    const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (few) {
-        // the wave kernel's few partials per (node, q head)
+        // tens of partials per (node, q head) at most: one thread per (node, q head, column quad)
         const int64_t total = (int64_t)a.B * a.K * a.nq * (a.D / 4);
         const dim3 grid_c((unsigned)((total + 255) / 256));
         if (a.D == 128)
