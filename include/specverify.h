@@ -187,7 +187,11 @@ typedef struct {
 #define SPEC_PATH_PERSISTENT 2
 
 /* Workspace bytes spec_verify needs for this shape, batch, k and cache page budget per request
- * (kv->max_pages_per_req of the calls it will serve). HOST out-pointer. */
+ * (kv->max_pages_per_req of the calls it will serve). HOST out-pointer. The library never
+ * allocates: a pass reads every weight for a handful of tokens at batch 1 and per-request
+ * overhead erodes batched gains [SpecPilot digest, airadar.tv — summary paragraph], so all
+ * scratch of a call (residual stream, split-K partials, attention partials sized by the page
+ * budget) comes from this one caller buffer. */
 int spec_workspace_bytes(const spec_model_cfg *cfg, int batch, int k, int max_pages_per_req,
                          size_t *bytes);
 
@@ -246,7 +250,10 @@ int spec_accept_workspace_bytes(int batch, int k, int vocab, size_t *bytes);
 
 /* The acceptance half of spec_verify on caller-supplied logits: per node the greedy token
  * (lowest index of the row maximum), then the accepted-path walk, with the same outputs and
- * conventions as spec_verify. logits: fp32 [batch*k][vocab]. */
+ * conventions as spec_verify. A draft token is kept only while it and every earlier token of its
+ * root path equal the target's greedy choice [SpecPilot digest, airadar.tv — "Risks"], each tree
+ * node judged on its own path [JetSpec article, seventnews.com — "Technical architecture"].
+ * logits: fp32 [batch*k][vocab]. */
 int spec_accept(const float *logits, const int32_t *draft_tokens, const int32_t *tree_parent,
                 int batch, int k, int vocab,
                 int32_t *accepted_len, int32_t *bonus_token, int32_t *accepted_path,

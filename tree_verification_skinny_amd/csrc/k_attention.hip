@@ -348,6 +348,12 @@ __device__ __forceinline__ void wait_vm() {
 constexpr int kGroupWaves = 8;
 typedef float float2v __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+#ifndef SV_GROUP_TARGET
+#define SV_GROUP_TARGET 256                             // workgroups one launch aims at
+#endif
+#ifndef SV_GROUP_RK_MAX
+#define SV_GROUP_RK_MAX 1024                            // keys per range at most (64 pages)
+#endif
 #ifndef SV_GROUP_NBUF
 #define SV_GROUP_NBUF 4
 #endif
@@ -752,10 +758,10 @@ hipError_t attention(const AttnArgs &a, hipStream_t st) {
         const int n_tg = (QT + 3 * kGroupWaves - 1) / (3 * kGroupWaves);
         const int tpg = (QT + n_tg - 1) / n_tg;                 // tiles per group
         const int tw = (tpg + kGroupWaves - 1) / kGroupWaves;   // tiles per wave
-        const int64_t per = (max_keys * a.nkv * n_tg * a.B + 255) / 256;
+        const int64_t per = (max_keys * a.nkv * n_tg * a.B + SV_GROUP_TARGET - 1) / SV_GROUP_TARGET;
         int64_t rk64 = (per + 31) / 32 * 32;
         if (rk64 < kAttnChunk) rk64 = kAttnChunk;
-        if (rk64 > 1024) rk64 = 1024;
+        if (rk64 > SV_GROUP_RK_MAX) rk64 = SV_GROUP_RK_MAX;
         const int rk = (int)rk64;
         const int n_rg = (int)((max_keys + rk - 1) / rk);
         stride = n_rg;
