@@ -77,16 +77,32 @@ hipError_t pack_weight(const bf16 *w, int n, int kd, bf16 *out, hipStream_t st) 
 }
 
 // ---- column layout of a tile group --------------------------------------------------------------
-// Contiguous for plain outputs; paired halves for SwiGLU (gate column n with up column F + n) so
+// Contiguous for plain outputs; paired halves for SwiGLU (gate column n with up column F + n) and
+// for QKV (column i of a head with column i + D/2, its rotation partner; D in the F argument) so
 // that a lane holds both operands of its outputs.
 template <int NT, int EPI>
 __device__ __forceinline__ int tile_col(int ng, int t, int F) {
     if constexpr (EPI == EPI_SWIGLU) {
         constexpr int PH = 8 * NT;   // columns in each half of a paired group
         return t < NT / 2 ? ng * PH + 16 * t : F + ng * PH + 16 * (t - NT / 2);
+    } else if constexpr (EPI == EPI_QKV) {
+        static_assert(NT == 2, "a QKV group is one 16-column tile and its rotation partner");
+        const int pph = F / 32;      // groups per head
+        return (ng / pph) * F + 16 * (ng % pph) + t * (F / 2);
     } else {
         return ng * 16 * NT + 16 * t;
     }
+}
+
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+
+// The QKV epilogue's rotation of a pair (a, c) = (x_i, x_{i + D/2}), both already rounded to bf16,
+// by the angle of (cos, sin) = cs, each output rounded to bf16 (no contraction, the arithmetic of
+// the split-K pass it replaces).
+__device__ __forceinline__ void rope_pair(float a, float c, float2 cs, bf16 &lo, bf16 &hi) {
+#pragma clang fp contract(off)
+    lo = (bf16)(a * cs.x - c * cs.y);
+    hi = (bf16)(c * cs.x + a * cs.y);
 }
 
 // ---- W12 weights (k_w12.hip) ----------------------------------------------------------------------
@@ -193,7 +209,7 @@ __global__ __launch_bounds__(64 * W) void gemm_kernel(GemmIn in, const bf16 *__r
     if constexpr (W12) cb = (uint32_t)(w12.plan[0] >> 1) * 0x01000100u;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-        const int tile = tile_col<NT, EPI>(ng, t, ep.F) >> 4;
+        const int tile = tile_col<NT, EPI>(ng, t, EPI == EPI_QKV ? ep.D : ep.F) >> 4;
         if constexpr (W12) {
             qp[t] = w12.planes + ((int64_t)tile * S) * 192 + 3 * lane;
             cur[t].i = w12.plan[2 + tile];
@@ -307,7 +323,7 @@ __global__ __launch_bounds__(64 * W) void gemm_kernel(GemmIn in, const bf16 *__r
 
     int col[NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) col[t] = tile_col<NT, EPI>(ng, t, ep.F) + 4 * grp;
+    for (int t = 0; t < NT; ++t) col[t] = tile_col<NT, EPI>(ng, t, EPI == EPI_QKV ? ep.D : ep.F) + 4 * grp;
 
     // ---- epilogues ------------------------------------------------------------------------------
 #pragma unroll
@@ -334,6 +350,46 @@ __global__ __launch_bounds__(64 * W) void gemm_kernel(GemmIn in, const bf16 *__r
                     hv[j] = (g / (1.0f + expf(-g))) * u;
                 }
                 store4(ep.h + frag_off(row, col[t], ep.F), hv[0], hv[1], hv[2], hv[3]);
+            }
+        } else if constexpr (EPI == EPI_QKV) {
+            // the sums rounded to bf16, q and k rotated, q stored, the draft K/V rows written into
+            // the request's cache slot ctx_len + node
+            if (!live) continue;
+            const int D = ep.D, half = D / 2;
+            const int hd = col[0] / D, i0 = col[0] % D;        // head; dims i0..i0+3 and + D/2
+            bf16 lo[4], hi[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float a = round_bf(acc.v[0][mt][j]), c = round_bf(acc.v[1][mt][j]);
+                if (hd < ep.nq + ep.nkv) {
+                    rope_pair(a, c, ep.rope[(int64_t)row * half + i0 + j], lo[j], hi[j]);
+                } else {
+                    lo[j] = (bf16)a;
+                    hi[j] = (bf16)c;
+                }
+            }
+            if (hd < ep.nq) {
+                bf16 *qh = ep.q + ((int64_t)row * ep.nq + hd) * D;
+                *(bf16x4 *)(qh + i0) = bf16x4{lo[0], lo[1], lo[2], lo[3]};
+                *(bf16x4 *)(qh + i0 + half) = bf16x4{hi[0], hi[1], hi[2], hi[3]};
+                continue;
+            }
+            const int b = row / ep.K, il = row % ep.K;
+            if (ep.status[b] != 0) continue;
+            const int pos = ep.ctx_len[b] + il;
+            const int64_t page = page_of(ep.block_table, ep.max_pages, b, pos);
+            const int slot = pos & 15;
+            if (hd < ep.nq + ep.nkv) {
+                bf16 *kr = ep.k_pool + ((page * ep.nkv + (hd - ep.nq)) * 16 + slot) * D;
+                *(bf16x4 *)(kr + i0) = bf16x4{lo[0], lo[1], lo[2], lo[3]};
+                *(bf16x4 *)(kr + i0 + half) = bf16x4{hi[0], hi[1], hi[2], hi[3]};
+            } else {
+                bf16 *vr = ep.v_pool + ((page * ep.nkv + (hd - ep.nq - ep.nkv)) * D) * 16 + slot;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    vr[(i0 + j) * 16] = lo[j];
+                    vr[(i0 + half + j) * 16] = hi[j];
+                }
             }
         } else if constexpr (EPI == EPI_ARGMAX) {
             float bv = -INFINITY;
@@ -650,22 +706,28 @@ template <int EPI>
 static hipError_t by_tiles(const GemmShape &g, const GemmIn &in, const bf16 *Wp, const W12Ref &w12,
                            const GemmEpi &ep, hipStream_t st) {
     const int mt = mt_for(in.M);
-    if (g.nt == 4) {
-        if (mt == 1) return by_waves<4, 1, EPI>(g, in, Wp, w12, ep, st);
-        if (mt == 2) return by_waves<4, 2, EPI>(g, in, Wp, w12, ep, st);
-        return by_waves<4, 4, EPI>(g, in, Wp, w12, ep, st);
-    }
-    if (g.nt == 2) {
-        if (mt == 1) return by_waves<2, 1, EPI>(g, in, Wp, w12, ep, st);
-        if (mt == 2) return by_waves<2, 2, EPI>(g, in, Wp, w12, ep, st);
-        return by_waves<2, 4, EPI>(g, in, Wp, w12, ep, st);
-    }
-    if constexpr (EPI == EPI_SWIGLU) {
-        return hipErrorInvalidValue;   // paired epilogue needs two tiles per group
+    if constexpr (EPI == EPI_QKV) {
+        // groups of a tile and its rotation partner, one block of rows
+        if (g.nt != 2 || mt != 1) return hipErrorInvalidValue;
+        return by_waves<2, 1, EPI>(g, in, Wp, w12, ep, st);
     } else {
-        if (mt == 1) return by_waves<1, 1, EPI>(g, in, Wp, w12, ep, st);
-        if (mt == 2) return by_waves<1, 2, EPI>(g, in, Wp, w12, ep, st);
-        return by_waves<1, 4, EPI>(g, in, Wp, w12, ep, st);
+        if (g.nt == 4) {
+            if (mt == 1) return by_waves<4, 1, EPI>(g, in, Wp, w12, ep, st);
+            if (mt == 2) return by_waves<4, 2, EPI>(g, in, Wp, w12, ep, st);
+            return by_waves<4, 4, EPI>(g, in, Wp, w12, ep, st);
+        }
+        if (g.nt == 2) {
+            if (mt == 1) return by_waves<2, 1, EPI>(g, in, Wp, w12, ep, st);
+            if (mt == 2) return by_waves<2, 2, EPI>(g, in, Wp, w12, ep, st);
+            return by_waves<2, 4, EPI>(g, in, Wp, w12, ep, st);
+        }
+        if constexpr (EPI == EPI_SWIGLU) {
+            return hipErrorInvalidValue;   // paired epilogue needs two tiles per group
+        } else {
+            if (mt == 1) return by_waves<1, 1, EPI>(g, in, Wp, w12, ep, st);
+            if (mt == 2) return by_waves<1, 2, EPI>(g, in, Wp, w12, ep, st);
+            return by_waves<1, 4, EPI>(g, in, Wp, w12, ep, st);
+        }
     }
 }
 
@@ -705,6 +767,7 @@ static hipError_t chunk(const GemmShape &g, int epi, const GemmIn &in, const bf1
         case EPI_PARTIAL: return by_tiles<EPI_PARTIAL>(g, in, Wp, w12, ep, st);
         case EPI_SWIGLU: return by_tiles<EPI_SWIGLU>(g, in, Wp, w12, ep, st);
         case EPI_ARGMAX: return by_tiles<EPI_ARGMAX>(g, in, Wp, w12, ep, st);
+        case EPI_QKV: return by_tiles<EPI_QKV>(g, in, Wp, w12, ep, st);
         default: return hipErrorInvalidValue;
     }
 }
@@ -816,6 +879,18 @@ GemmShape plan_gemm(int M, int N, int Kd, bool allow_split, bool allow_tc) {
 GemmShape plan_gemm_w12(int M, int N, int Kd, bool allow_split) {
     GemmShape g = plan_gemm(M, N, Kd, allow_split, false);
     if (!g.wide && !allow_split && g.waves == 8) g.waves = SV_W12_WHOLE_WAVES;
+    return g;
+}
+
+GemmShape plan_gemm_qkv(int M, int N, int Kd) {
+    // whole K in two-tile groups (one group per 16 columns of a head and their rotation
+    // partners): at the 27B shape 224 workgroups, like the split-K plan's, each streaming two
+    // tiles over all of K instead of four over half of it
+    GemmShape g = plan_skinny(M, N, Kd, false);
+    g.nt = 2;
+    g.splits = 1;
+    const int steps = Kd / 32;
+    g.waves = (N / 32 < 1200 && steps / 8 >= 2) ? 8 : 4;
     return g;
 }
 

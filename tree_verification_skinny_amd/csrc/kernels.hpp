@@ -21,7 +21,7 @@ struct GemmShape {
 
 // What a workgroup does with its finished tiles: partial sums of its K split, or (whole K)
 // SwiGLU or the output head's per-group greedy maximum.
-enum { EPI_PARTIAL = 0, EPI_SWIGLU = 1, EPI_ARGMAX = 2 };
+enum { EPI_PARTIAL = 0, EPI_SWIGLU = 1, EPI_ARGMAX = 2, EPI_QKV = 3 };
 
 // The B operand: activations X [M_total][Kd] in fragment order (frag_off), rows padded to a
 // multiple of 16.
@@ -39,6 +39,13 @@ struct GemmEpi {
     // ARGMAX: per tile group (max, lowest index) [n_groups][M]; optional fp32 logits [M][N]
     float *logits, *amax_val;
     int *amax_idx;
+    // QKV (whole K, groups of the two rotation halves of one head): bf16 rounding, RoPE with the
+    // (cos, sin) table [M][D/2], q [M][nq][D], and the draft K/V rows into cache slots
+    // ctx_len + node of requests whose status is 0
+    const float2 *rope;
+    const int32_t *status, *ctx_len, *block_table;
+    int max_pages, K, nq, nkv, D;
+    bf16 *q, *k_pool, *v_pool;
 };
 
 // A projection matrix in W12 form (k_w12.hip): three 4-bit planes per value in fragment order,
@@ -61,6 +68,9 @@ hipError_t gemm(const GemmShape &g, int epi, const GemmIn &in, const bf16 *Wp, c
 // plan_gemm_w12 picks, bit-identical to gemm() over the same matrix in bf16 whenever the plans
 // agree (every shape below 128 rows).
 GemmShape plan_gemm_w12(int M, int N, int Kd, bool allow_split);
+// The QKV projection with its RoPE epilogue (EPI_QKV): the skinny kernel, whole K, two-tile groups
+// (the rotation halves of one head); for passes of at most 16 rows.
+GemmShape plan_gemm_qkv(int M, int N, int Kd);
 hipError_t gemm_w12(const GemmShape &g, int epi, const GemmIn &in, const W12Ref &w, const GemmEpi &ep,
                     hipStream_t st);
 // Row-major [n][kd] -> fragment order; rows up to the next multiple of 16 are zero.

@@ -31,6 +31,8 @@ struct Plan {
     int L, H, nq, nkv, D, F, V;
     int qd, nqkv;
     GemmShape g_qkv, g_o, g_gu, g_down, g_lm;
+    bool qkv_fused;         // QKV with its RoPE epilogue (no split-K pass): passes of <= 16 rows
+    GemmShape g_qkvf;       // its plan (bf16 and W12 alike)
     int nrec;               // rows of a recurrent layer's projection (q, k, v, gates, padding)
     GemmShape g_rqkv;
     GemmShape w_qkv, w_o, w_gu, w_down, w_lm;   // the same projections over W12 weights (M <= 64)
@@ -139,6 +141,10 @@ int make_plan(const spec_model_cfg *c, int B, int K, int max_pages, Plan &p) {
     p.nqkv = (p.nq + 2 * p.nkv) * p.D;
     const int M = p.M;
     p.g_qkv = plan_gemm(M, p.nqkv, p.H, true);
+    // at most one block of 16 rows: the QKV projection runs whole-K with the RoPE and cache-write
+    // epilogue, so no split-K pass sits between it and attention
+    p.qkv_fused = M <= 16;
+    p.g_qkvf = plan_gemm_qkv(M, p.nqkv, p.H);
     p.g_o = plan_gemm(M, p.H, p.qd, true);
     p.g_gu = plan_gemm(M, 2 * p.F, p.H, false);
     p.g_down = plan_gemm(M, p.H, p.F, true);
@@ -451,6 +457,16 @@ int spec_verify(const spec_weights *w, const spec_kv_cache *kv, const int32_t *d
 
     GemmEpi ep = {};
     ep.F = p.F;
+    ep.rope = ni.rope;
+    ep.status = ni.status;
+    ep.ctx_len = ctx_len;
+    ep.block_table = kv->block_table;
+    ep.max_pages = kv->max_pages_per_req;
+    ep.K = p.K;
+    ep.nq = p.nq;
+    ep.nkv = p.nkv;
+    ep.D = p.D;
+    ep.q = q;
     ep.y = part;
     ep.h = h;
     ep.logits = logits;
@@ -509,9 +525,15 @@ int spec_verify(const spec_weights *w, const spec_kv_cache *kv, const int32_t *d
             SV_TRY(rec_operand(ro, M, p.qd, attn, stream));
         } else {
         // q, k, v = u . Wqkv^T (u = RMSNorm(x) * attn_norm); RoPE; K/V into the cache
-        SV_TRY(proj(p.g_qkv, p.w_qkv, EPI_PARTIAL, operand(u), lw.w_qkv, lq ? &lq->w_qkv : nullptr));
-        SV_TRY(reduce_qkv(part, lq ? p.w_qkv.splits : p.g_qkv.splits, ni, ctx_len, kv->block_table, kv->max_pages_per_req,
-                          p.B, p.K, p.nq, p.nkv, p.D, q, kl, vl, stream));
+        if (p.qkv_fused) {
+            ep.k_pool = kl;
+            ep.v_pool = vl;
+            SV_TRY(proj(p.g_qkvf, p.g_qkvf, EPI_QKV, operand(u), lw.w_qkv, lq ? &lq->w_qkv : nullptr));
+        } else {
+            SV_TRY(proj(p.g_qkv, p.w_qkv, EPI_PARTIAL, operand(u), lw.w_qkv, lq ? &lq->w_qkv : nullptr));
+            SV_TRY(reduce_qkv(part, lq ? p.w_qkv.splits : p.g_qkv.splits, ni, ctx_len, kv->block_table,
+                              kv->max_pages_per_req, p.B, p.K, p.nq, p.nkv, p.D, q, kl, vl, stream));
+        }
         aa.k_pool = kl;
         aa.v_pool = vl;
         SV_TRY(attention(aa, stream));
