@@ -438,6 +438,9 @@ constexpr int kPlanCUs = 256;                           // compute units of the 
 #ifndef SV_WIDE_TARGET
 #define SV_WIDE_TARGET 320
 #endif
+#ifndef SV_WIDE_BAL
+#define SV_WIDE_BAL 1
+#endif
 constexpr int kWideWaves = 4, kWideTN = 2, kWideKS = SV_WIDE_KS;
 
 // output column of tile t (0..TN-1) of wave w in group ng: SwiGLU pairs gate and up columns in the
@@ -456,7 +459,24 @@ struct W12Raw {
     uint32_t a, b, c;
 };
 
-template <int TM, int EPI, bool W12>
+// SwiGLU of four gate and up sums (each rounded to bf16 first), stored as bf16 at h + off.
+__device__ __forceinline__ void swiglu_store4(bf16 *h, int64_t off, const floatx4 &g4, const floatx4 &u4) {
+    float hv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const float g = round_bf(g4[j]);
+        const float u = round_bf(u4[j]);
+        hv[j] = (g / (1.0f + expf(-g))) * u;
+    }
+    store4(h + off, hv[0], hv[1], hv[2], hv[3]);
+}
+
+// BAL (SwiGLU over exactly one workgroup per compute unit, GemmShape::bal_q = Q): workgroup b runs
+// group b's four pairs over all of K and, first, part b % Q of the K range of leftover pair
+// 4 * n_groups + b / Q, its four waves taking every fourth step of that part. The part's sums go
+// to scratch (ep.y); the last of the pair's Q workgroups to arrive (ep.ctr) adds the parts in
+// index order, applies SwiGLU and resets the counter. Nothing waits on another workgroup.
+template <int TM, int EPI, bool W12, bool BAL>
 __global__ __launch_bounds__(64 * kWideWaves) void gemm_wide_kernel(GemmIn in, const bf16 *__restrict__ Wp,
                                                                      W12Ref w12, int N, int Kd, int n_groups,
                                                                      int ksteps, GemmEpi ep) {
@@ -465,6 +485,7 @@ __global__ __launch_bounds__(64 * kWideWaves) void gemm_wide_kernel(GemmIn in, c
     constexpr int SLOTS = KS * TM * 64;                 // 16-byte slots per slab
     constexpr int PER = SLOTS / (64 * NW);              // slots staged per thread
     static_assert(SLOTS % (64 * NW) == 0, "slab must split evenly over the threads");
+    static_assert((NW - 1) * 2 <= 2 * KS, "the leftover part's wave sums must fit the staging buffers");
     __shared__ bf16x8 xs[2][SLOTS];                     // [buffer][(step * TM + block) * 64 + lane]
     __shared__ float red_v[NW][64];
     __shared__ int red_i[NW][64];
@@ -574,7 +595,219 @@ __global__ __launch_bounds__(64 * kWideWaves) void gemm_wide_kernel(GemmIn in, c
         }
     };
 
-    if (nslabs > 0) {
+    if constexpr (BAL && EPI == EPI_SWIGLU) {
+        constexpr int XB = 5;                            // steps per load batch of the part
+        const int Q = ep.bal_q;
+        const int xp = (int)blockIdx.x / Q, qi = (int)blockIdx.x % Q;
+        const int pair = n_groups * NW + xp;
+        const int Sq = S / Q, sq0 = qi * Sq;
+        const int tl[2] = {pair, ep.F / 16 + pair};
+        floatx4 ex[2][TM];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int mt = 0; mt < TM; ++mt) ex[t][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+        const bf16 *xw[2];
+        const uint32_t *xq[2];
+        W12Cursor xc[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            if constexpr (W12) {
+                xq[t] = w12.planes + ((int64_t)tl[t] * S) * 192 + 3 * lane;
+                xc[t].i = w12.plan[2 + tl[t]];
+                xc[t].end = w12.plan[3 + tl[t]];
+            } else {
+                xw[t] = Wp + (((int64_t)tl[t] * S) * 64 + lane) * 8;
+            }
+        }
+        if constexpr (W12) {
+            int st0[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const int k = xc[t].i + lane;
+                st0[t] = k < xc[t].end ? (w12.exc[k].x >> 9) : 0x7fffffff;
+            }
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                xc[t].i = w12_first_at(w12.exc, xc[t].i, xc[t].end, sq0 + wave, lane, st0[t]);
+                xc[t].step = w12_step_of(w12.exc, xc[t].i, xc[t].end);
+            }
+        }
+        const bf16 *xa[TM];
+#pragma unroll
+        for (int mt = 0; mt < TM; ++mt) {
+            const int blk = min((m0 >> 4) + mt, nblk - 1);
+            xa[mt] = in.Xp + (((int64_t)blk * S) * 64 + lane) * 8;
+        }
+        // this wave's steps: sq0 + wave + NW i, i < nmine; loaded XB at a time
+        const int nmine = (Sq - wave + NW - 1) / NW;
+        for (int i0 = 0; i0 < nmine; i0 += XB) {
+            Frag f[XB][2];
+            bf16x8 xb[XB][TM];
+#pragma unroll
+            for (int u = 0; u < XB; ++u) {
+                const int su = sq0 + wave + NW * min(i0 + u, nmine - 1);
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    if constexpr (W12) {
+                        const uint32_t *fp = xq[t] + (int64_t)su * 192;
+                        f[u][t] = W12Raw{stream_load32(fp), stream_load32(fp + 1), stream_load32(fp + 2)};
+                    } else {
+                        f[u][t] = stream_load((const bf16x8 *)(xw[t] + (int64_t)su * 512));
+                    }
+                }
+#pragma unroll
+                for (int mt = 0; mt < TM; ++mt) xb[u][mt] = *(const bf16x8 *)(xa[mt] + (int64_t)su * 512);
+            }
+#pragma unroll
+            for (int u = 0; u < XB; ++u) {
+                if (i0 + u >= nmine) break;
+                const int su = sq0 + wave + NW * (i0 + u);
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    bf16x8 w;
+                    if constexpr (W12) {
+                        w = w12_decode(f[u][t].a, f[u][t].b, f[u][t].c, cb);
+                        if (su >= xc[t].step) w = w12_fixup(w, xc[t], w12.exc, su, lane);
+                    } else {
+                        w = f[u][t];
+                    }
+#pragma unroll
+                    for (int mt = 0; mt < TM; ++mt) ex[t][mt] = mfma16x16x32(w, xb[u][mt], ex[t][mt]);
+                }
+            }
+        }
+        // the part's sum over the waves, in wave order, into scratch slot (xp * Q + qi)
+        floatx4 *red = reinterpret_cast<floatx4 *>(&xs[0][0]);
+        if (wave > 0) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int mt = 0; mt < TM; ++mt) red[(((wave - 1) * 2 + t) * TM + mt) * 64 + lane] = ex[t][mt];
+        }
+        __syncthreads();
+        if (wave == 0) {
+            // The part's sums are written through to device scope (64-bit agent-scope stores), the
+            // wave waits for them to complete and counts itself in; the last arriver reads the
+            // parts with agent-scope loads. No fence: the L2 of this die is neither written back
+            // nor invalidated under the other workgroups' weight streams.
+            uint64_t *scr = reinterpret_cast<uint64_t *>(ep.y);
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int mt = 0; mt < TM; ++mt) {
+                    floatx4 v = ex[t][mt];
+                    for (int w = 1; w < NW; ++w) v += red[(((w - 1) * 2 + t) * TM + mt) * 64 + lane];
+                    uint64_t *d = scr + ((((int64_t)blockIdx.x * 2 + t) * TM + mt) * 64 + lane) * 2;
+                    __hip_atomic_store(d, (uint64_t)__float_as_uint(v[0]) | ((uint64_t)__float_as_uint(v[1]) << 32),
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store(d + 1, (uint64_t)__float_as_uint(v[2]) | ((uint64_t)__float_as_uint(v[3]) << 32),
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            __builtin_amdgcn_s_waitcnt(0);
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            int prev = 0;
+            if (lane == 0) prev = (int)__hip_atomic_fetch_add(ep.ctr + xp, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            prev = __shfl(prev, 0, 64);
+            if (prev == Q - 1) {
+                // every part is written: add them in index order and finish the pair
+                floatx4 sum[2][TM];
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int mt = 0; mt < TM; ++mt) {
+                        sum[t][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+                        for (int q2 = 0; q2 < Q; ++q2) {
+                            const uint64_t *sp = scr + ((((int64_t)(xp * Q + q2) * 2 + t) * TM + mt) * 64 + lane) * 2;
+                            const uint64_t a = __hip_atomic_load(const_cast<uint64_t *>(sp), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                            const uint64_t b = __hip_atomic_load(const_cast<uint64_t *>(sp + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                            const floatx4 v = {__uint_as_float((uint32_t)a), __uint_as_float((uint32_t)(a >> 32)),
+                                               __uint_as_float((uint32_t)b), __uint_as_float((uint32_t)(b >> 32))};
+                            sum[t][mt] = q2 == 0 ? v : sum[t][mt] + v;
+                        }
+                    }
+#pragma unroll
+                for (int mt = 0; mt < TM; ++mt) {
+                    const int m = 16 * mt + r16;
+                    if (m < M) swiglu_store4(ep.h, frag_off(m0 + m, pair * 16 + 4 * grp, ep.F), sum[0][mt], sum[1][mt]);
+                }
+                if (lane == 0) __hip_atomic_store(ep.ctr + xp, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+        __syncthreads();
+    }
+
+    if constexpr (BAL && !W12) {
+        // bf16: a loop body without branches, so that each wait covers only the loads it needs.
+        // Weight fragments are requested one slab ahead and activation slabs two ahead (two
+        // register sets), at the top of each half, before the multiply. Slabs run in pairs; steps
+        // past the range re-read the last step's addresses (cache hits) and their staged
+        // activations are zero, so they add nothing.
+        if (nslabs > 0) {
+            bf16x8 wa[KS][TN], wb[KS][TN];
+            bf16x8 xa[PER], xb[PER];
+            auto xload = [&](bf16x8 (&xr)[PER], int slab) {
+#pragma unroll
+                for (int r = 0; r < PER; ++r) {
+                    const int i = threadIdx.x + r * 64 * NW;
+                    const int l = i & 63, mt = (i >> 6) % TM, k = (i >> 6) / TM;
+                    const int sc = min(s_begin + slab * KS + k, s_end - 1);
+                    const int blk = min((m0 >> 4) + mt, nblk - 1);
+                    xr[r] = *(const bf16x8 *)(in.Xp + (((int64_t)blk * S + sc) * 64 + l) * 8);
+                }
+            };
+            auto xstore = [&](const bf16x8 (&xr)[PER], int buf, int slab) {
+#pragma unroll
+                for (int r = 0; r < PER; ++r) {
+                    const int i = threadIdx.x + r * 64 * NW;
+                    const int k = (i >> 6) / TM;
+                    xs[buf][i] = s_begin + slab * KS + k < s_end ? xr[r] : bf16x8{};
+                }
+            };
+            auto wload = [&](bf16x8 (&w)[KS][TN], int slab) {
+#pragma unroll
+                for (int k = 0; k < KS; ++k) {
+                    const int sr = min(slab * KS + k, nsteps - 1);
+#pragma unroll
+                    for (int t = 0; t < TN; ++t) w[k][t] = stream_load((const bf16x8 *)(wp[t] + (int64_t)sr * 512));
+                }
+            };
+            auto mul = [&](const bf16x8 (&w)[KS][TN], int buf) {
+#pragma unroll
+                for (int k = 0; k < KS; ++k) {
+                    bf16x8 bx[TM];
+#pragma unroll
+                    for (int mt = 0; mt < TM; ++mt) bx[mt] = xs[buf][(k * TM + mt) * 64 + lane];
+#pragma unroll
+                    for (int t = 0; t < TN; ++t)
+#pragma unroll
+                        for (int mt = 0; mt < TM; ++mt) acc[t][mt] = mfma16x16x32(w[k][t], bx[mt], acc[t][mt]);
+                }
+            };
+            xload(xa, 0);
+            wload(wa, 0);
+            xload(xb, 1);
+            xstore(xa, 0, 0);
+            __syncthreads();
+            const int npairs = (nslabs + 1) >> 1;
+            for (int pi = 0; pi < npairs; ++pi) {
+                const int j = 2 * pi;
+                wload(wb, j + 1);
+                xload(xa, j + 2);
+                __builtin_amdgcn_sched_barrier(0);
+                mul(wa, 0);
+                xstore(xb, 1, j + 1);
+                __syncthreads();
+                wload(wa, j + 2);
+                xload(xb, j + 3);
+                __builtin_amdgcn_sched_barrier(0);
+                mul(wb, 1);
+                xstore(xa, 0, j + 2);
+                __syncthreads();
+            }
+        }
+    } else if (nslabs > 0) {
         Frag wa[KS][TN], wb[KS][TN];
         bf16x8 xr[PER];
         stage_load(xr, 0);
@@ -615,16 +848,7 @@ __global__ __launch_bounds__(64 * kWideWaves) void gemm_wide_kernel(GemmIn in, c
                     *(floatx4 *)(ep.y + ((int64_t)split * in.M_total + row) * N + col[t]) = acc[t][mt];
             }
         } else if constexpr (EPI == EPI_SWIGLU) {
-            if (live) {
-                float hv[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float g = round_bf(acc[0][mt][j]);
-                    const float u = round_bf(acc[1][mt][j]);
-                    hv[j] = (g / (1.0f + expf(-g))) * u;
-                }
-                store4(ep.h + frag_off(row, col[0], ep.F), hv[0], hv[1], hv[2], hv[3]);
-            }
+            if (live) swiglu_store4(ep.h, frag_off(row, col[0], ep.F), acc[0][mt], acc[1][mt]);
         } else if constexpr (EPI == EPI_ARGMAX) {
             float bv = -INFINITY;
             int bi = 0x7fffffff;
@@ -672,6 +896,12 @@ __global__ __launch_bounds__(64 * kWideWaves) void gemm_wide_kernel(GemmIn in, c
 static int mt_for(int m) { return m <= 16 ? 1 : (m <= 32 ? 2 : 4); }
 
 int gemm_groups(const GemmShape &g) { return g.N / (16 * g.nt); }
+
+size_t gemm_bal_scratch_bytes(const GemmShape &g) {
+    return g.bal_q > 0 ? (size_t)kPlanCUs * 2 * 4 * 64 * sizeof(floatx4) : 0;
+}
+
+int gemm_bal_counters(const GemmShape &g) { return g.bal_q > 0 ? 4 * (gemm_groups(g) - kPlanCUs) : 0; }
 
 // The weights: bf16 fragments (Wp) or, when w12.planes is set, a W12 matrix.
 template <int NT, int MT, int W, int EPI>
@@ -731,17 +961,31 @@ static hipError_t by_tiles(const GemmShape &g, const GemmIn &in, const bf16 *Wp,
     }
 }
 
+template <int EPI, bool W12, bool BAL>
+static void launch_wide_tm(const GemmShape &g, const GemmIn &in, const bf16 *Wp, const W12Ref &w12,
+                           const GemmEpi &ep, dim3 grid, int n_groups, int ks, hipStream_t st) {
+    const dim3 block(64 * kWideWaves);
+    switch (mt_for(in.M)) {
+        case 1: hipLaunchKernelGGL((gemm_wide_kernel<1, EPI, W12, BAL>), grid, block, 0, st, in, Wp, w12, g.N, g.Kd, n_groups, ks, ep); break;
+        case 2: hipLaunchKernelGGL((gemm_wide_kernel<2, EPI, W12, BAL>), grid, block, 0, st, in, Wp, w12, g.N, g.Kd, n_groups, ks, ep); break;
+        default: hipLaunchKernelGGL((gemm_wide_kernel<4, EPI, W12, BAL>), grid, block, 0, st, in, Wp, w12, g.N, g.Kd, n_groups, ks, ep); break;
+    }
+}
+
 template <int EPI, bool W12>
 static void launch_wide_as(const GemmShape &g, const GemmIn &in, const bf16 *Wp, const W12Ref &w12,
                            const GemmEpi &ep, hipStream_t st) {
     const int steps = g.Kd >> 5;
-    const int ks = (steps + g.splits - 1) / g.splits;
-    const dim3 grid(gemm_groups(g) * g.splits), block(64 * kWideWaves);
-    switch (mt_for(in.M)) {
-        case 1: hipLaunchKernelGGL((gemm_wide_kernel<1, EPI, W12>), grid, block, 0, st, in, Wp, w12, g.N, g.Kd, gemm_groups(g), ks, ep); break;
-        case 2: hipLaunchKernelGGL((gemm_wide_kernel<2, EPI, W12>), grid, block, 0, st, in, Wp, w12, g.N, g.Kd, gemm_groups(g), ks, ep); break;
-        default: hipLaunchKernelGGL((gemm_wide_kernel<4, EPI, W12>), grid, block, 0, st, in, Wp, w12, g.N, g.Kd, gemm_groups(g), ks, ep); break;
+    if constexpr (EPI == EPI_SWIGLU) {
+        if (g.bal_q > 0 && ep.ctr != nullptr && ep.y != nullptr) {
+            GemmEpi eb = ep;
+            eb.bal_q = g.bal_q;
+            launch_wide_tm<EPI, W12, true>(g, in, Wp, w12, eb, dim3(kPlanCUs), kPlanCUs, steps, st);
+            return;
+        }
     }
+    const int ks = (steps + g.splits - 1) / g.splits;
+    launch_wide_tm<EPI, W12, false>(g, in, Wp, w12, ep, dim3(gemm_groups(g) * g.splits), gemm_groups(g), ks, st);
 }
 
 template <int EPI>
@@ -822,6 +1066,7 @@ GemmShape plan_gemm(int M, int N, int Kd, bool allow_split, bool allow_tc) {
     g.Kd = Kd;
     g.wide = false;
     g.tc = false;
+    g.bal_q = 0;
     const int steps = Kd / 32;
     if (allow_tc && M >= 128 && N % gemm_tc_columns() == 0) {
         // hundreds of rows: the matrix-core tile kernel, one launch over all 256-row tiles;
@@ -851,6 +1096,13 @@ GemmShape plan_gemm(int M, int N, int Kd, bool allow_split, bool allow_tc) {
         g.waves = kWideWaves;
         const int groups = N / (16 * g.nt);
         g.splits = 1;
+        if (SV_WIDE_BAL && !allow_split && groups > kPlanCUs && groups < 2 * kPlanCUs &&
+            kPlanCUs % (4 * (groups - kPlanCUs)) == 0 && steps % (kPlanCUs / (4 * (groups - kPlanCUs))) == 0) {
+            // whole-K projections with a few more groups than compute units (gate/up at 64 rows:
+            // 272 groups): one workgroup per unit, each with one group and a K part of a leftover
+            // pair (SwiGLU only; other epilogues ignore it)
+            g.bal_q = kPlanCUs / (4 * (groups - kPlanCUs));
+        }
         if (SV_WIDE_PER_CU > 0 && allow_split && groups < kPlanCUs * SV_WIDE_PER_CU) {
             g.splits = kPlanCUs * SV_WIDE_PER_CU / groups;
             if (g.splits > 32) g.splits = 32;

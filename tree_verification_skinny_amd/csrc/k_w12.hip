@@ -166,6 +166,12 @@ __global__ __launch_bounds__(64) void w12_pack_kernel(const uint16_t *__restrict
     }
 }
 
+hipError_t zero_ints(int *p, int n, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(zero_ints_kernel, dim3(1), dim3(256), 0, st, p, n);
+    return hipGetLastError();
+}
+
 int w12_plan_ints(int n) { return 2 + (n / 16 + 1) + 256; }
 
 hipError_t w12_plan(const bf16 *w, int n, int kd, int32_t *plan, hipStream_t st) {

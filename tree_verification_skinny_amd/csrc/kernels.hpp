@@ -17,6 +17,8 @@ struct GemmShape {
     int splits;     // K splits across workgroups (fp32 partials when > 1)
     bool wide;      // more than 16 rows: waves split the tiles, activations staged in LDS
     bool tc;        // a batch of hundreds of rows: the matrix-core-bound tile kernel
+    int bal_q = 0;  // wide SwiGLU balanced over the compute units: 0 (off), or the K parts Q of
+                    // each leftover gate/up pair (gemm_wide_kernel)
 };
 
 // What a workgroup does with its finished tiles: partial sums of its K split, or (whole K)
@@ -46,6 +48,11 @@ struct GemmEpi {
     const int32_t *status, *ctx_len, *block_table;
     int max_pages, K, nq, nkv, D;
     bf16 *q, *k_pool, *v_pool;
+    // SWIGLU balanced over the compute units (GemmShape::bal_q): the leftover pairs' K-part sums go
+    // to y (gemm_bal_scratch_bytes) and ctr holds one arrival counter per leftover pair
+    // (gemm_bal_counters ints), zero before the launch and left zero by it
+    int *ctr;
+    int bal_q;
 };
 
 // A projection matrix in W12 form (k_w12.hip): three 4-bit planes per value in fragment order,
@@ -61,6 +68,10 @@ hipError_t w12_pack(const bf16 *w, int n, int kd, const int32_t *plan, uint32_t 
                     hipStream_t st);
 
 int gemm_groups(const GemmShape &g);
+// Scratch (bytes) and counters (ints) a balanced wide SwiGLU launch needs (0 when not balanced).
+size_t gemm_bal_scratch_bytes(const GemmShape &g);
+int gemm_bal_counters(const GemmShape &g);
+hipError_t zero_ints(int *p, int n, hipStream_t st);
 GemmShape plan_gemm(int M, int N, int Kd, bool allow_split, bool allow_tc = true);
 hipError_t gemm(const GemmShape &g, int epi, const GemmIn &in, const bf16 *Wp, const GemmEpi &ep,
                 hipStream_t st);

@@ -38,8 +38,9 @@ struct Plan {
     GemmShape w_qkv, w_o, w_gu, w_down, w_lm;   // the same projections over W12 weights (M <= 64)
     int lm_groups, lm_groups_w12;
     int attn_chunks;
+    int n_ctr;              // arrival counters of a balanced gate/up launch (0: none)
     size_t o_depth, o_pos, o_status, o_anc, o_rope, o_x, o_u, o_q, o_attn, o_h, o_part, o_po,
-        o_pml, o_amv, o_ami, o_rq, o_ro, o_rs, total;
+        o_pml, o_amv, o_ami, o_rq, o_ro, o_rs, o_ctr, total;
     // the persistent path (rows <= 16): its own buffers, sized for up to kFusedSizeG workgroups
     bool fused_shape;
     size_t total_steps;     // the per-step plan's part of the workspace (the persistent one follows)
@@ -167,6 +168,12 @@ int make_plan(const spec_model_cfg *c, int B, int K, int max_pages, Plan &p) {
         const size_t b = (size_t)g->splits * M * g->N * sizeof(float);
         if (b > part) part = b;
     }
+    // a balanced gate/up launch keeps its K-part sums in the partials buffer (free between the O
+    // pass's reduction and the down projection)
+    for (const GemmShape *g : {&p.g_gu, &p.w_gu})
+        if (gemm_bal_scratch_bytes(*g) > part) part = gemm_bal_scratch_bytes(*g);
+    p.n_ctr = gemm_bal_counters(p.g_gu) > gemm_bal_counters(p.w_gu) ? gemm_bal_counters(p.g_gu)
+                                                                     : gemm_bal_counters(p.w_gu);
 
     int amax_groups = p.lm_groups > argmax_chunks(p.V) ? p.lm_groups : argmax_chunks(p.V);
     if (p.lm_groups_w12 > amax_groups) amax_groups = p.lm_groups_w12;
@@ -191,6 +198,7 @@ int make_plan(const spec_model_cfg *c, int B, int K, int max_pages, Plan &p) {
     p.o_rq = cv.take(sizeof(uint16_t) * M * p.qd);
     p.o_ro = cv.take(sizeof(float) * M * p.qd);
     p.o_rs = cv.take(sizeof(int32_t) * B);
+    p.o_ctr = cv.take(sizeof(int32_t) * (p.n_ctr > 0 ? p.n_ctr : 1));
     p.fused_shape = fused_shape_ok(p);
     p.total_steps = cv.off;
     if (p.fused_shape) {
@@ -360,6 +368,8 @@ int spec_verify(const spec_weights *w, const spec_kv_cache *kv, const int32_t *d
 
     SV_TRY(tree_prep(draft_tokens, tree_parent, ctx_len, kv->block_table, kv->max_pages_per_req,
                      kv->n_pages, p.B, p.K, p.V, ni, stream));
+    int *ctr = p.n_ctr > 0 ? at<int>(workspace, p.o_ctr) : nullptr;
+    if (ctr) SV_TRY(zero_ints(ctr, p.n_ctr, stream));
     SV_TRY(rope_table(ni, M, p.D, w->cfg.rope_theta, stream));
     if (fused) {
         FusedArgs fa = {};
@@ -468,6 +478,7 @@ int spec_verify(const spec_weights *w, const spec_kv_cache *kv, const int32_t *d
     ep.D = p.D;
     ep.q = q;
     ep.y = part;
+    ep.ctr = ctr;
     ep.h = h;
     ep.logits = logits;
     ep.amax_val = amv;
@@ -726,7 +737,8 @@ constexpr int kPrefillRows = 4096;
 struct PrefillLayout {
     int C;                           // prompt positions per request per pass
     GemmShape g_lm, w_lm;
-    size_t x, u, q, attn, h, part, pos, rope, status, failed, tokens, head_u, amv, ami, total;
+    int n_ctr;                       // arrival counters of a balanced gate/up launch (0: none)
+    size_t x, u, q, attn, h, part, pos, rope, status, failed, tokens, head_u, amv, ami, ctr, total;
 };
 
 static void prefill_shapes(const spec_model_cfg *cfg, int M, GemmShape (&g)[4], GemmShape (&w)[4]) {
@@ -758,6 +770,11 @@ static int prefill_layout(const spec_model_cfg *cfg, int batch, int max_pages, P
             const size_t b = (size_t)s->splits * M * s->N * sizeof(float);
             if (i != 2 && b > part) part = b;
         }
+    // a pass of 17..127 rows (a short last pass) runs gate/up on the wide kernel, balanced over the
+    // compute units where the shape allows: its scratch and counters
+    const GemmShape gb = plan_gemm(64, 2 * F, H, false);
+    if (gemm_bal_scratch_bytes(gb) > part) part = gemm_bal_scratch_bytes(gb);
+    o.n_ctr = gemm_bal_counters(gb);
     o.g_lm = plan_gemm(batch, cfg->vocab, H, false);
     o.w_lm = plan_gemm_w12(batch, cfg->vocab, H, false);
     const int groups = gemm_groups(o.g_lm) > gemm_groups(o.w_lm) ? gemm_groups(o.g_lm) : gemm_groups(o.w_lm);
@@ -776,6 +793,7 @@ static int prefill_layout(const spec_model_cfg *cfg, int batch, int max_pages, P
     o.head_u = cv.take(sizeof(uint16_t) * Bp * H);
     o.amv = cv.take(sizeof(float) * groups * batch);
     o.ami = cv.take(sizeof(int32_t) * groups * batch);
+    o.ctr = cv.take(sizeof(int32_t) * (o.n_ctr > 0 ? o.n_ctr : 1));
     o.total = cv.off;
     return SPEC_OK;
 }
@@ -848,12 +866,14 @@ int spec_prefill(const spec_weights *weights, const spec_kv_cache *kv, const int
     ep.F = cfg->ffn;
     ep.y = part;
     ep.h = h;
+    ep.ctr = o.n_ctr > 0 ? at<int>(workspace, o.ctr) : nullptr;
     auto operand = [](const bf16 *Xp) {
         GemmIn in = {};
         in.Xp = Xp;
         return in;
     };
     SV_TRY(prefill_init(failed, batch, stream));
+    if (ep.ctr) SV_TRY(zero_ints(ep.ctr, o.n_ctr, stream));
     for (int c0 = 0; c0 < p; c0 += o.C) {
         const int n = p - c0 < o.C ? p - c0 : o.C;
         const int M = batch * n;
