@@ -430,7 +430,7 @@ __global__ __launch_bounds__(64 * W) void gemm_kernel(GemmIn in, const bf16 *__r
 #endif
 constexpr int kPlanCUs = 256;                           // compute units of the target (MI355X)
 #ifndef SV_WIDE_PER_CU
-#define SV_WIDE_PER_CU 2
+#define SV_WIDE_PER_CU 1
 #endif
 #ifndef SV_WIDE_KS
 #define SV_WIDE_KS 4
@@ -440,6 +440,9 @@ constexpr int kPlanCUs = 256;                           // compute units of the 
 #endif
 #ifndef SV_WIDE_BAL
 #define SV_WIDE_BAL 1
+#endif
+#ifndef SV_WIDE_PIPE_PARTIAL
+#define SV_WIDE_PIPE_PARTIAL 1                          // split-K launches on the branch-free loop
 #endif
 constexpr int kWideWaves = 4, kWideTN = 2, kWideKS = SV_WIDE_KS;
 
@@ -738,14 +741,14 @@ __global__ __launch_bounds__(64 * kWideWaves) void gemm_wide_kernel(GemmIn in, c
         __syncthreads();
     }
 
-    if constexpr (BAL && !W12) {
-        // bf16: a loop body without branches, so that each wait covers only the loads it needs.
-        // Weight fragments are requested one slab ahead and activation slabs two ahead (two
-        // register sets), at the top of each half, before the multiply. Slabs run in pairs; steps
-        // past the range re-read the last step's addresses (cache hits) and their staged
-        // activations are zero, so they add nothing.
+    if constexpr (BAL || (EPI == EPI_PARTIAL && SV_WIDE_PIPE_PARTIAL)) {
+        // A loop body without branches (over W12 weights, only the rare exception patch), so that
+        // each wait covers only the loads it needs. Weight fragments are requested one slab ahead
+        // and activation slabs two ahead (two register sets), at the top of each half, before the
+        // multiply. Slabs run in pairs; steps past the range re-read the last step's addresses
+        // (cache hits) and their staged activations are zero, so they add nothing.
         if (nslabs > 0) {
-            bf16x8 wa[KS][TN], wb[KS][TN];
+            Frag wa[KS][TN], wb[KS][TN];
             bf16x8 xa[PER], xb[PER];
             auto xload = [&](bf16x8 (&xr)[PER], int slab) {
 #pragma unroll
@@ -765,24 +768,40 @@ __global__ __launch_bounds__(64 * kWideWaves) void gemm_wide_kernel(GemmIn in, c
                     xs[buf][i] = s_begin + slab * KS + k < s_end ? xr[r] : bf16x8{};
                 }
             };
-            auto wload = [&](bf16x8 (&w)[KS][TN], int slab) {
+            auto wload = [&](Frag (&w)[KS][TN], int slab) {
 #pragma unroll
                 for (int k = 0; k < KS; ++k) {
                     const int sr = min(slab * KS + k, nsteps - 1);
 #pragma unroll
-                    for (int t = 0; t < TN; ++t) w[k][t] = stream_load((const bf16x8 *)(wp[t] + (int64_t)sr * 512));
+                    for (int t = 0; t < TN; ++t) {
+                        if constexpr (W12) {
+                            const uint32_t *f = qp[t] + (int64_t)sr * 192;
+                            w[k][t] = W12Raw{stream_load32(f), stream_load32(f + 1), stream_load32(f + 2)};
+                        } else {
+                            w[k][t] = stream_load((const bf16x8 *)(wp[t] + (int64_t)sr * 512));
+                        }
+                    }
                 }
             };
-            auto mul = [&](const bf16x8 (&w)[KS][TN], int buf) {
+            auto mul = [&](const Frag (&w)[KS][TN], int buf, int slab) {
 #pragma unroll
                 for (int k = 0; k < KS; ++k) {
                     bf16x8 bx[TM];
 #pragma unroll
                     for (int mt = 0; mt < TM; ++mt) bx[mt] = xs[buf][(k * TM + mt) * 64 + lane];
 #pragma unroll
-                    for (int t = 0; t < TN; ++t)
+                    for (int t = 0; t < TN; ++t) {
+                        bf16x8 wf;
+                        if constexpr (W12) {
+                            const int su = s_begin + slab * KS + k;
+                            wf = w12_decode(w[k][t].a, w[k][t].b, w[k][t].c, cb);
+                            if (su >= cur[t].step && su < s_end) wf = w12_fixup(wf, cur[t], w12.exc, su, lane);
+                        } else {
+                            wf = w[k][t];
+                        }
 #pragma unroll
-                        for (int mt = 0; mt < TM; ++mt) acc[t][mt] = mfma16x16x32(w[k][t], bx[mt], acc[t][mt]);
+                        for (int mt = 0; mt < TM; ++mt) acc[t][mt] = mfma16x16x32(wf, bx[mt], acc[t][mt]);
+                    }
                 }
             };
             xload(xa, 0);
@@ -796,13 +815,13 @@ __global__ __launch_bounds__(64 * kWideWaves) void gemm_wide_kernel(GemmIn in, c
                 wload(wb, j + 1);
                 xload(xa, j + 2);
                 __builtin_amdgcn_sched_barrier(0);
-                mul(wa, 0);
+                mul(wa, 0, j);
                 xstore(xb, 1, j + 1);
                 __syncthreads();
                 wload(wa, j + 2);
                 xload(xb, j + 3);
                 __builtin_amdgcn_sched_barrier(0);
-                mul(wb, 1);
+                mul(wb, 1, j + 1);
                 xstore(xa, 0, j + 2);
                 __syncthreads();
             }
@@ -1088,9 +1107,10 @@ GemmShape plan_gemm(int M, int N, int Kd, bool allow_split, bool allow_tc) {
     }
     if (M > 16 && N % (16 * kWideWaves * kWideTN) == 0) {
         // wide variant: 8 tiles per workgroup; split K into as many parts as keep every compute
-        // unit at SV_WIDE_PER_CU workgroups at most (64-node tree: 14.75-14.84 ms per step at two
-        // per unit, 15.54 at one, 14.93 splitting to at least SV_WIDE_TARGET = 320 workgroups in
-        // whole slabs, the rule below when SV_WIDE_PER_CU is 0)
+        // unit at SV_WIDE_PER_CU workgroups at most. Each unit streams at a capped rate, so the
+        // launch lasts as long as its busiest unit: one workgroup per unit on the branch-free loop
+        // measured best (64-node tree: 12.89 ms per step; two per unit 13.86, one per unit on the
+        // slab loop that waits for all loads 14.26, two per unit on it 13.41)
         g.wide = true;
         g.nt = kWideWaves * kWideTN;
         g.waves = kWideWaves;
