@@ -4,7 +4,7 @@ pass with other draft tokens over the same cache, workspace and output buffers, 
 overwritten with garbage. Cases: the tiny decoder's block of 16 (the automatic and the per-step
 plans) and a batch of two 64-node trees, and a 64-row tree pass whose gate/up runs balanced over
 the compute units (its arrival counters are cleared inside the pass by a fill kernel, never by a
-memset, and left zero by the last arriver)."""
+memset, and left zero by the last arriver); and prompt prefills from an empty context."""
 import numpy as np
 import pytest
 import torch
@@ -12,6 +12,7 @@ import torch
 import oracle
 import synth
 import tree_verification_skinny_amd as tv
+from tree_verification_skinny_amd import kvlayout
 
 from helpers import bits, device_weights, make_kv, upload_context
 
@@ -89,4 +90,58 @@ def test_graph_replays_equal_eager(shape_name, B, K, tree, path):
         got = outputs()
         for name, a, b in zip(("logits", "greedy", "accepted_len", "bonus", "path"), ref, got):
             assert torch.equal(a, b), f"replay {i}: {name} differs from the eager pass"
+    del graph
+
+
+@pytest.mark.parametrize("B,p", [(2, 40), (1, 300)])
+def test_graph_prefill_replays_equal_eager(B, p):
+    """spec_prefill from an empty context replayed from a graph (as bench.py times a prefill): each
+    replay, after the contexts are reset eagerly and an eager prefill of another prompt has run,
+    gives the eager pass's next tokens, last-position logits and cache rows bit for bit."""
+    shape = synth.TINY
+    seed = 2300 + B + p
+    w = synth.model_weights(shape, seed)
+    weights = device_weights(shape, w, DEV)
+    kv = make_kv(shape, [p] * B, 1, seed, DEV)
+    rng = np.random.default_rng(synth.seed_of(seed, "graph prefill"))
+    prompts = torch.from_numpy(rng.integers(0, shape.vocab, (B, p)).astype(np.int32)).to(DEV)
+    other = torch.from_numpy(rng.integers(0, shape.vocab, (B, p)).astype(np.int32)).to(DEV)
+    ws = tv.workspace(tv.spec_prefill_workspace_bytes(weights.cfg, B, kv.max_pages, True), DEV)
+    ctx = torch.zeros(B, dtype=torch.int32, device=DEV)
+    nt = torch.empty(B, dtype=torch.int32, device=DEV)
+    lg = torch.empty((B, shape.vocab), dtype=torch.float32, device=DEV)
+
+    def run(pr):
+        tv.spec_prefill(weights, kv, pr, ctx, nt, ws, last_logits=lg)
+
+    def rows():
+        return [torch.cat([t.view(torch.int16).reshape(-1) for t in kvlayout.read_rows(kv, l, b, torch.arange(p))])
+                for l in range(shape.n_layers) for b in range(B)]
+
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        run(prompts)
+    stream.synchronize()
+    ref = [nt.clone(), lg.view(torch.int32).clone(), ctx.clone()] + rows()
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        ctx.zero_()
+    stream.synchronize()
+    with torch.cuda.graph(graph, stream=stream):
+        run(prompts)
+    torch.cuda.synchronize()
+
+    for i in range(3):
+        with torch.cuda.stream(stream):
+            ctx.zero_()
+            run(other)                          # the program's own eager prefill, another prompt
+            ctx.zero_()
+            nt.fill_(-7)
+            lg.fill_(float("nan"))
+            graph.replay()
+        stream.synchronize()
+        got = [nt.clone(), lg.view(torch.int32).clone(), ctx.clone()] + rows()
+        for j, (a, b) in enumerate(zip(ref, got)):
+            assert torch.equal(a, b), f"replay {i}: output {j} differs from the eager prefill"
     del graph
