@@ -1,7 +1,9 @@
-"""The wide gate/up projection balanced over the compute units: passes of 17..64 rows whose gate/up
-has a few more 128-column groups than there are compute units. Each workgroup takes one group over
-all of K and a K part of one leftover gate/up pair; the last of a pair's parts to arrive adds them
-in index order and applies SwiGLU. Whole verify passes at two such shapes against the CPU oracle
+"""The gate/up projection balanced over the compute units: passes of 17..64 rows whose gate/up has
+a few more 128-column groups than there are compute units (the wide kernel, one workgroup per
+unit), and passes of 1..16 rows with a few more 32-column groups than twice the units (the skinny
+kernel, two workgroups per unit). Each workgroup takes one group over all of K and a K part of one
+leftover gate/up pair; the last of a pair's parts to arrive adds them in index order and applies
+SwiGLU. Whole verify passes at two such shapes against the CPU oracle
 (logits at the fixed tolerance, acceptance exact up to logged near-ties) on a workspace poisoned
 with 0xFF bytes (the pass clears the arrival counters itself), a second pass bit for bit equal to
 the first (the counters are left zero), and the W12 pass bit for bit equal to the bf16 one (the
@@ -28,15 +30,19 @@ def setup_module(module):
     tv.lib()
 
 
-# ffn 16896: 264 groups of four pairs, the 32 leftover pairs in 8 parts of one K step each (three
-# of a workgroup's four waves have no step of its part); ffn 17408: 272 groups, 64 leftover pairs
-# in 4 parts of two steps. 64, 48 and 32 rows: four, four (the last row block partly empty) and two
-# row blocks per launch.
-@pytest.mark.parametrize("ffn,B,k,kind", [(16896, 1, 64, "tree"), (17408, 2, 24, "chain"),
-                                          (17408, 2, 16, "tree")])
-def test_balanced_gate_up_pass(ffn, B, k, kind):
-    shape = synth.Shape(n_layers=2, hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=64, ffn=ffn, vocab=1024)
-    seed = 1300 + ffn % 97 + 7 * B + k
+# Wide kernel: ffn 16896, 264 groups of four pairs, the 32 leftover pairs in 8 parts of one K step
+# each (three of a workgroup's four waves have no step of its part); ffn 17408: 272 groups, 64
+# leftover pairs in 4 parts of two steps. 64, 48 and 32 rows: four, four (the last row block partly
+# empty) and two row blocks per launch.
+# Skinny kernel (16 rows or fewer): ffn 17408 at hidden 512, 544 groups of two pairs on 512
+# workgroups, the 64 leftover pairs in 8 parts of two K steps; ffn 16896 at hidden 1024: 528
+# groups, the 32 leftover pairs in 16 parts of two steps.
+@pytest.mark.parametrize("ffn,hidden,B,k,kind", [(16896, 256, 1, 64, "tree"), (17408, 256, 2, 24, "chain"),
+                                                 (17408, 256, 2, 16, "tree"), (17408, 512, 1, 16, "tree"),
+                                                 (17408, 512, 1, 5, "chain"), (16896, 1024, 1, 16, "chain")])
+def test_balanced_gate_up_pass(ffn, hidden, B, k, kind):
+    shape = synth.Shape(n_layers=2, hidden=hidden, n_q_heads=4, n_kv_heads=2, head_dim=64, ffn=ffn, vocab=1024)
+    seed = 1300 + ffn % 97 + 7 * B + k + hidden // 256 - 1
     ctxs = [300, 900][:B]
     w = synth.model_weights(shape, seed)
     m = oracle_model_from(shape, w)

@@ -22,8 +22,8 @@
 //     and leave fp32 partials that a separate pass adds in split order (an in-kernel "last
 //     workgroup adds" fixup for every column group costs more on this chip than the extra
 //     pass); wide projections run whole and finish their epilogue in place, except that a
-//     whole-K SwiGLU launch with a few more groups than compute units splits its leftover pairs
-//     by K and lets the last of a pair's parts finish it (gemm_wide_kernel, BAL). No workgroup
+//     whole-K SwiGLU launch with a few more groups than its workgroups splits its leftover pairs
+//     by K and lets the last of a pair's parts finish it (BAL, in both kernels). No workgroup
 //     waits for another and results do not depend on timing.
 //   * Epilogues of the whole-K projections: SwiGLU (gate/up; a group holds gate tiles and the
 //     matching up tiles, so gate n and up n sit in the same lane) and the per-group greedy
@@ -183,15 +183,70 @@ __device__ __forceinline__ bf16x8 w12_fixup(bf16x8 a, W12Cursor &c, const int2 *
     return a;
 }
 
+// SwiGLU of four gate and up sums (each rounded to bf16 first), stored as bf16 at h + off.
+__device__ __forceinline__ void swiglu_store4(bf16 *h, int64_t off, const floatx4 &g4, const floatx4 &u4) {
+    float hv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const float g = round_bf(g4[j]);
+        const float u = round_bf(u4[j]);
+        hv[j] = (g / (1.0f + expf(-g))) * u;
+    }
+    store4(h + off, hv[0], hv[1], hv[2], hv[3]);
+}
+
+// The last arriver of a balanced launch: the sum of parts slot0 .. slot0 + Q - 1 (index order:
+// part 0, then + part 1, ...) of NV floatx4 values per lane, each part's values at scratch slot
+// ((slot * NV + v) * 64 + lane) as two 64-bit halves, read with agent-scope loads. QC parts'
+// loads go out together (Q a multiple of QC), so Q parts take Q / QC round trips, not Q.
+template <int NV, int QC>
+__device__ __forceinline__ void bal_add_parts(floatx4 (&sum)[NV], const uint64_t *scr, int slot0, int Q, int lane) {
+    for (int q0 = 0; q0 < Q; q0 += QC) {
+        uint64_t a[QC][NV], b[QC][NV];
+#pragma unroll
+        for (int j = 0; j < QC; ++j)
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                const uint64_t *sp = scr + (((int64_t)(slot0 + q0 + j) * NV + v) * 64 + lane) * 2;
+                a[j][v] = __hip_atomic_load(const_cast<uint64_t *>(sp), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                b[j][v] = __hip_atomic_load(const_cast<uint64_t *>(sp + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+#pragma unroll
+        for (int j = 0; j < QC; ++j)
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                const floatx4 x = {__uint_as_float((uint32_t)a[j][v]), __uint_as_float((uint32_t)(a[j][v] >> 32)),
+                                   __uint_as_float((uint32_t)b[j][v]), __uint_as_float((uint32_t)(b[j][v] >> 32))};
+                sum[v] = q0 + j == 0 ? x : sum[v] + x;
+            }
+    }
+}
+
+// Q is a power of two (a divisor of the launch's workgroup count): whole batches of up to 64
+// registers of loads.
+template <int NV>
+__device__ __forceinline__ void bal_sum(floatx4 (&sum)[NV], const uint64_t *scr, int slot0, int Q, int lane) {
+    constexpr int QC = 16 / NV > 1 ? 16 / NV : 1;
+    if (Q % QC == 0) bal_add_parts<NV, QC>(sum, scr, slot0, Q, lane);
+    else bal_add_parts<NV, 1>(sum, scr, slot0, Q, lane);
+}
+
 template <int NT, int MT>
 struct Acc {
     floatx4 v[NT][MT];
 };
 
-template <int NT, int MT, int W, int EPI, bool W12>
-__global__ __launch_bounds__(64 * W) void gemm_kernel(GemmIn in, const bf16 *__restrict__ Wp,
+// BAL (SwiGLU over one block of rows, GemmShape::bal_q = Q, bal_wg workgroups, two per compute
+// unit): workgroup b runs group b over all of K on its W waves as above and, on one more wave,
+// part b % Q of the K range of leftover gate/up pair (NT / 2) * n_groups + b / Q. The part's sums
+// go to scratch (ep.y); the last of the pair's Q workgroups to arrive (ep.ctr) adds the parts in
+// index order, applies SwiGLU and resets the counter. The part wave's loads and hand-off overlap
+// the group's stream. Nothing waits on another workgroup.
+template <int NT, int MT, int W, int EPI, bool W12, bool BAL = false>
+__global__ __launch_bounds__(64 * (W + (BAL ? 1 : 0))) void gemm_kernel(GemmIn in, const bf16 *__restrict__ Wp,
                                                       W12Ref w12, int N, int Kd, int n_groups,
                                                       int ksteps, GemmEpi ep) {
+    static_assert(!BAL || (EPI == EPI_SWIGLU && MT == 1), "balanced launch: SwiGLU over one block of rows");
     __shared__ floatx4 red[(W - 1) * NT * MT * 64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r16 = lane & 15, grp = lane >> 4;
@@ -242,6 +297,121 @@ __global__ __launch_bounds__(64 * W) void gemm_kernel(GemmIn in, const bf16 *__r
     for (int mt = 0; mt < MT; ++mt) {
         const int blk = min((m0 >> 4) + mt, nblk - 1);
         xp[mt] = in.Xp + (((int64_t)blk * S) * 64 + lane) * 8;
+    }
+
+    if constexpr (BAL) {
+        if (wv == W) {
+            // the part wave: the leftover pair's steps sq0 .. sq0 + Sq - 1 in one chain, XB at a
+            // time, then the hand-off; it meets the streaming waves at their one barrier
+            constexpr int XB = 5;
+            const int Q = ep.bal_q;
+            const int lx = (int)blockIdx.x / Q, qi = (int)blockIdx.x % Q;
+            const int pair = n_groups * (NT / 2) + lx;
+            const int Sq = S / Q, sq0 = qi * Sq;
+            const int tl[2] = {pair, ep.F / 16 + pair};
+            const bf16 *xw[2];
+            const uint32_t *xq[2];
+            W12Cursor xc[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                if constexpr (W12) {
+                    xq[t] = w12.planes + ((int64_t)tl[t] * S) * 192 + 3 * lane;
+                    xc[t].i = w12.plan[2 + tl[t]];
+                    xc[t].end = w12.plan[3 + tl[t]];
+                } else {
+                    xw[t] = Wp + (((int64_t)tl[t] * S) * 64 + lane) * 8;
+                }
+            }
+            if constexpr (W12) {
+                int st0[2];
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const int k = xc[t].i + lane;
+                    st0[t] = k < xc[t].end ? (w12.exc[k].x >> 9) : 0x7fffffff;
+                }
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    xc[t].i = w12_first_at(w12.exc, xc[t].i, xc[t].end, sq0, lane, st0[t]);
+                    xc[t].step = w12_step_of(w12.exc, xc[t].i, xc[t].end);
+                }
+            }
+            floatx4 ex[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
+            auto step = [&](const bf16x8 &xv, const bf16x8 (&f)[2], const uint32_t (&r0)[2],
+                            const uint32_t (&r1)[2], const uint32_t (&rh)[2], int su) __attribute__((always_inline)) {
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    bf16x8 w;
+                    if constexpr (W12) {
+                        w = w12_decode(r0[t], r1[t], rh[t], cb);
+                        if (su >= xc[t].step) w = w12_fixup(w, xc[t], w12.exc, su, lane);
+                    } else {
+                        w = f[t];
+                    }
+                    ex[t] = mfma16x16x32(w, xv, ex[t]);
+                }
+            };
+            auto load = [&](bf16x8 &xv, bf16x8 (&f)[2], uint32_t (&r0)[2], uint32_t (&r1)[2], uint32_t (&rh)[2],
+                            int su) __attribute__((always_inline)) {
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    if constexpr (W12) {
+                        const uint32_t *fp = xq[t] + (int64_t)su * 192;
+                        r0[t] = stream_load32(fp);
+                        r1[t] = stream_load32(fp + 1);
+                        rh[t] = stream_load32(fp + 2);
+                    } else {
+                        f[t] = stream_load((const bf16x8 *)(xw[t] + (int64_t)su * 512));
+                    }
+                }
+                xv = *(const bf16x8 *)(xp[0] + (int64_t)su * 512);
+            };
+            // whole batches of XB steps: every load is used unconditionally, so all of a batch's
+            // loads go out before its first product; then the steps left over one at a time
+            int i0 = 0;
+            for (; i0 + XB <= Sq; i0 += XB) {
+                bf16x8 f[XB][2], xb[XB];
+                uint32_t q0[XB][2], q1[XB][2], qh[XB][2];
+#pragma unroll
+                for (int u = 0; u < XB; ++u) load(xb[u], f[u], q0[u], q1[u], qh[u], sq0 + i0 + u);
+#pragma unroll
+                for (int u = 0; u < XB; ++u) step(xb[u], f[u], q0[u], q1[u], qh[u], sq0 + i0 + u);
+            }
+            for (; i0 < Sq; ++i0) {
+                bf16x8 f[2], xv;
+                uint32_t q0[2], q1[2], qh[2];
+                load(xv, f, q0, q1, qh, sq0 + i0);
+                step(xv, f, q0, q1, qh, sq0 + i0);
+            }
+            // Into scratch slot blockIdx.x, written through to device scope (64-bit agent-scope
+            // stores); the wave waits for the stores to complete, then counts itself in, and the
+            // last arriver reads the parts with agent-scope loads. No fence: this die's L2 is
+            // neither written back nor invalidated.
+            uint64_t *scr = reinterpret_cast<uint64_t *>(ep.y);
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const floatx4 v = ex[t];
+                uint64_t *d = scr + (((int64_t)blockIdx.x * 2 + t) * 64 + lane) * 2;
+                __hip_atomic_store(d, (uint64_t)__float_as_uint(v[0]) | ((uint64_t)__float_as_uint(v[1]) << 32),
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(d + 1, (uint64_t)__float_as_uint(v[2]) | ((uint64_t)__float_as_uint(v[3]) << 32),
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            __builtin_amdgcn_s_waitcnt(0);
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            int prev = 0;
+            if (lane == 0) prev = (int)__hip_atomic_fetch_add(ep.ctr + lx, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            prev = __shfl(prev, 0, 64);
+            if (prev == Q - 1) {
+                // every part is written: add them in index order and finish the pair
+                floatx4 sum[2];
+                bal_sum<2>(sum, scr, lx * Q, Q, lane);
+                if (r16 < M) swiglu_store4(ep.h, frag_off(m0 + r16, pair * 16 + 4 * grp, ep.F), sum[0], sum[1]);
+                if (lane == 0) __hip_atomic_store(ep.ctr + lx, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            __syncthreads();               // the streaming waves' one barrier (before their sums)
+            return;
+        }
     }
 
     Acc<NT, MT> acc;
@@ -445,6 +615,21 @@ constexpr int kPlanCUs = 256;                           // compute units of the 
 #ifndef SV_WIDE_BAL
 #define SV_WIDE_BAL 1
 #endif
+#ifndef SV_SKINNY_BAL
+#define SV_SKINNY_BAL 1                                 // one-block gate/up balanced (plan_gemm_swiglu)
+#endif
+#ifndef SV_SKINNY_BAL_NT
+#define SV_SKINNY_BAL_NT 4                              // tiles per group of a balanced launch
+#endif
+#ifndef SV_SKINNY_W8_MAX
+#define SV_SKINNY_W8_MAX 1200                           // eight waves below this many skinny workgroups
+#endif
+#ifndef SV_SKINNY_BAL_PAD
+#define SV_SKINNY_BAL_PAD 55                            // KB of LDS a balanced workgroup claims
+#endif
+#ifndef SV_SKINNY_BAL_PER_CU
+#define SV_SKINNY_BAL_PER_CU 2                          // its workgroups per compute unit
+#endif
 #ifndef SV_WIDE_PIPE_PARTIAL
 #define SV_WIDE_PIPE_PARTIAL 1                          // split-K launches on the branch-free loop
 #endif
@@ -465,18 +650,6 @@ __device__ __forceinline__ int wide_col(int ng, int w, int t, int F) {
 struct W12Raw {
     uint32_t a, b, c;
 };
-
-// SwiGLU of four gate and up sums (each rounded to bf16 first), stored as bf16 at h + off.
-__device__ __forceinline__ void swiglu_store4(bf16 *h, int64_t off, const floatx4 &g4, const floatx4 &u4) {
-    float hv[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const float g = round_bf(g4[j]);
-        const float u = round_bf(u4[j]);
-        hv[j] = (g / (1.0f + expf(-g))) * u;
-    }
-    store4(h + off, hv[0], hv[1], hv[2], hv[3]);
-}
 
 // BAL (SwiGLU over exactly one workgroup per compute unit, GemmShape::bal_q = Q): workgroup b runs
 // group b's four pairs over all of K and, first, part b % Q of the K range of leftover pair
@@ -719,25 +892,12 @@ __global__ __launch_bounds__(64 * kWideWaves) void gemm_wide_kernel(GemmIn in, c
             prev = __shfl(prev, 0, 64);
             if (prev == Q - 1) {
                 // every part is written: add them in index order and finish the pair
-                floatx4 sum[2][TM];
-#pragma unroll
-                for (int t = 0; t < 2; ++t)
-#pragma unroll
-                    for (int mt = 0; mt < TM; ++mt) {
-                        sum[t][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
-                        for (int q2 = 0; q2 < Q; ++q2) {
-                            const uint64_t *sp = scr + ((((int64_t)(xp * Q + q2) * 2 + t) * TM + mt) * 64 + lane) * 2;
-                            const uint64_t a = __hip_atomic_load(const_cast<uint64_t *>(sp), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                            const uint64_t b = __hip_atomic_load(const_cast<uint64_t *>(sp + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                            const floatx4 v = {__uint_as_float((uint32_t)a), __uint_as_float((uint32_t)(a >> 32)),
-                                               __uint_as_float((uint32_t)b), __uint_as_float((uint32_t)(b >> 32))};
-                            sum[t][mt] = q2 == 0 ? v : sum[t][mt] + v;
-                        }
-                    }
+                floatx4 sum[2 * TM];                      // [t * TM + mt]
+                bal_sum<2 * TM>(sum, scr, xp * Q, Q, lane);
 #pragma unroll
                 for (int mt = 0; mt < TM; ++mt) {
                     const int m = 16 * mt + r16;
-                    if (m < M) swiglu_store4(ep.h, frag_off(m0 + m, pair * 16 + 4 * grp, ep.F), sum[0][mt], sum[1][mt]);
+                    if (m < M) swiglu_store4(ep.h, frag_off(m0 + m, pair * 16 + 4 * grp, ep.F), sum[mt], sum[TM + mt]);
                 }
                 if (lane == 0) __hip_atomic_store(ep.ctr + xp, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
@@ -920,17 +1080,41 @@ static int mt_for(int m) { return m <= 16 ? 1 : (m <= 32 ? 2 : 4); }
 
 int gemm_groups(const GemmShape &g) { return g.N / (16 * g.nt); }
 
+// A balanced launch keeps one part (two tiles, every row block) per workgroup and counts arrivals
+// per leftover pair: the wide launch on kPlanCUs workgroups of four row blocks with four pairs per
+// group, the skinny one on bal_wg workgroups of one row block with NT / 2 pairs per group.
 size_t gemm_bal_scratch_bytes(const GemmShape &g) {
-    return g.bal_q > 0 ? (size_t)kPlanCUs * 2 * 4 * 64 * sizeof(floatx4) : 0;
+    if (g.bal_q <= 0) return 0;
+    return g.wide ? (size_t)kPlanCUs * 2 * 4 * 64 * sizeof(floatx4) : (size_t)g.bal_wg * 2 * 64 * sizeof(floatx4);
 }
 
-int gemm_bal_counters(const GemmShape &g) { return g.bal_q > 0 ? 4 * (gemm_groups(g) - kPlanCUs) : 0; }
+int gemm_bal_counters(const GemmShape &g) {
+    if (g.bal_q <= 0) return 0;
+    return g.wide ? 4 * (gemm_groups(g) - kPlanCUs) : (g.nt / 2) * (gemm_groups(g) - g.bal_wg);
+}
 
 // The weights: bf16 fragments (Wp) or, when w12.planes is set, a W12 matrix.
 template <int NT, int MT, int W, int EPI>
 static hipError_t launch(const GemmShape &g, const GemmIn &in, const bf16 *Wp, const W12Ref &w12,
                          const GemmEpi &ep, hipStream_t st) {
     const int steps = g.Kd >> 5;
+    if constexpr (EPI == EPI_SWIGLU && (NT == 2 || NT == 4) && MT == 1 && W == 8) {
+        if (g.bal_q > 0 && g.bal_wg > 0 && ep.ctr != nullptr && ep.y != nullptr) {
+            GemmEpi eb = ep;
+            eb.bal_q = g.bal_q;
+            // two workgroups per compute unit, never three: unused LDS up to 55 KB a workgroup
+            // keeps a third off a unit (160 KB) whatever the register count
+            constexpr size_t kRed = (size_t)(W - 1) * NT * MT * 64 * sizeof(floatx4);
+            constexpr size_t kPad = SV_SKINNY_BAL_PAD * 1024 > kRed ? SV_SKINNY_BAL_PAD * 1024 - kRed : 0;
+            if (w12.planes != nullptr)
+                hipLaunchKernelGGL((gemm_kernel<NT, MT, W, EPI, true, true>), dim3(g.bal_wg), dim3(64 * (W + 1)), kPad, st,
+                                   in, Wp, w12, g.N, g.Kd, g.bal_wg, steps, eb);
+            else
+                hipLaunchKernelGGL((gemm_kernel<NT, MT, W, EPI, false, true>), dim3(g.bal_wg), dim3(64 * (W + 1)), kPad, st,
+                                   in, Wp, w12, g.N, g.Kd, g.bal_wg, steps, eb);
+            return hipGetLastError();
+        }
+    }
     const int ks = (steps + g.splits - 1) / g.splits;
     if (w12.planes != nullptr)
         hipLaunchKernelGGL((gemm_kernel<NT, MT, W, EPI, true>), dim3(gemm_groups(g) * g.splits), dim3(64 * W),
@@ -1158,6 +1342,29 @@ GemmShape plan_gemm_w12(int M, int N, int Kd, bool allow_split) {
     return g;
 }
 
+// Gate/up (whole K, SwiGLU epilogue). At one block of rows with a few more four-tile groups than
+// two per compute unit (27B shape: 544), the skinny launch runs balanced on exactly two workgroups
+// per unit (BAL above): each unit streams the same bytes, where 1088 two-tile groups at two
+// resident per unit leave a third round of 64 on a quarter of the units. Measured at the 27B
+// shape: 57.4 us against 59.4 for the 1088 groups; two-tile groups balanced over 1024 workgroups
+// (four per unit in two rounds) took 65.7, 1088 four-wave workgroups all resident 59.7.
+GemmShape plan_gemm_swiglu(int M, int N, int Kd, bool w12) {
+    GemmShape g = w12 ? plan_gemm_w12(M, N, Kd, false) : plan_gemm(M, N, Kd, false);
+    constexpr int nt = SV_SKINNY_BAL_NT;
+    if (SV_SKINNY_BAL && !g.wide && !g.tc && M <= 16 && N % (16 * nt) == 0) {
+        const int groups = N / (16 * nt), nwg = SV_SKINNY_BAL_PER_CU * kPlanCUs, steps = Kd / 32;
+        const int lp = nt / 2 * (groups - nwg);          // leftover pairs
+        if (lp > 0 && nwg % lp == 0 && steps % (nwg / lp) == 0) {
+            g.nt = nt;
+            g.waves = 8;
+            g.splits = 1;
+            g.bal_q = nwg / lp;
+            g.bal_wg = nwg;
+        }
+    }
+    return g;
+}
+
 GemmShape plan_gemm_qkv(int M, int N, int Kd) {
     // whole K in two-tile groups (one group per 16 columns of a head and their rotation
     // partners): at the 27B shape 224 workgroups, like the split-K plan's, each streaming two
@@ -1202,7 +1409,7 @@ static GemmShape plan_skinny(int M, int N, int Kd, bool allow_split) {
         while (g.splits > 1 && steps / g.splits < 16) --g.splits;
     }
     g.waves = 4;
-    if (g.nt * mt <= 4 && (groups * g.splits < 1200) && steps / (8 * g.splits) >= 2) g.waves = 8;
+    if (g.nt * mt <= 4 && (groups * g.splits < SV_SKINNY_W8_MAX) && steps / (8 * g.splits) >= 2) g.waves = 8;
     return g;
 }
 

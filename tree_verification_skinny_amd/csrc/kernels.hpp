@@ -17,8 +17,9 @@ struct GemmShape {
     int splits;     // K splits across workgroups (fp32 partials when > 1)
     bool wide;      // more than 16 rows: waves split the tiles, activations staged in LDS
     bool tc;        // a batch of hundreds of rows: the matrix-core-bound tile kernel
-    int bal_q = 0;  // wide SwiGLU balanced over the compute units: 0 (off), or the K parts Q of
-                    // each leftover gate/up pair (gemm_wide_kernel)
+    int bal_q = 0;  // SwiGLU balanced over the compute units: 0 (off), or the K parts Q of each
+                    // leftover gate/up pair (gemm_wide_kernel; gemm_kernel at one row block)
+    int bal_wg = 0; // workgroups of a balanced skinny launch (two per compute unit)
 };
 
 // What a workgroup does with its finished tiles: partial sums of its K split, or (whole K)
@@ -73,6 +74,7 @@ size_t gemm_bal_scratch_bytes(const GemmShape &g);
 int gemm_bal_counters(const GemmShape &g);
 hipError_t zero_ints(int *p, int n, hipStream_t st);
 GemmShape plan_gemm(int M, int N, int Kd, bool allow_split, bool allow_tc = true);
+GemmShape plan_gemm_swiglu(int M, int N, int Kd, bool w12);
 hipError_t gemm(const GemmShape &g, int epi, const GemmIn &in, const bf16 *Wp, const GemmEpi &ep,
                 hipStream_t st);
 // The projection over a W12 matrix: the skinny or wide variant (never the tile kernel) as

@@ -147,14 +147,14 @@ int make_plan(const spec_model_cfg *c, int B, int K, int max_pages, Plan &p) {
     p.qkv_fused = M <= 16;
     p.g_qkvf = plan_gemm_qkv(M, p.nqkv, p.H);
     p.g_o = plan_gemm(M, p.H, p.qd, true);
-    p.g_gu = plan_gemm(M, 2 * p.F, p.H, false);
+    p.g_gu = plan_gemm_swiglu(M, 2 * p.F, p.H, false);
     p.g_down = plan_gemm(M, p.H, p.F, true);
     p.g_lm = plan_gemm(M, p.V, p.H, false);
     if (p.g_gu.nt < 2) return SPEC_EUNSUPPORTED;
     p.lm_groups = gemm_groups(p.g_lm);
     p.w_qkv = plan_gemm_w12(M, p.nqkv, p.H, true);
     p.w_o = plan_gemm_w12(M, p.H, p.qd, true);
-    p.w_gu = plan_gemm_w12(M, 2 * p.F, p.H, false);
+    p.w_gu = plan_gemm_swiglu(M, 2 * p.F, p.H, true);
     p.w_down = plan_gemm_w12(M, p.H, p.F, true);
     p.w_lm = plan_gemm_w12(M, p.V, p.H, false);
     p.lm_groups_w12 = gemm_groups(p.w_lm);
