@@ -55,21 +55,21 @@ METRIC = "verified tokens/sec + verify-step HBM GB/s (% peak), 27B-shape dense, 
 # figures hold for the kernel source they were taken on; any other source reports null.
 PMC_TRAFFIC = {
     ("block", "bf16"): {"source": "tree_verification_skinny_amd/csrc/k_gemm.hip",
-                        "sha256": "5087e0fd32f94d8434554dbdffd43fea0cdebd84127900349a33bdebae639f17",
-                        "fetch_kib": 174751.4, "write_kib": 544.0,
-                        "fetch_scale": 1.9999849, "write_scale": 1.0},
+                        "sha256": "6b99f4e24b571010585a68ea2f507bf7cca8927bc5fe7225de7c44a6c56cb96c",
+                        "fetch_kib": 175305.2, "write_kib": 2610.0,
+                        "fetch_scale": 1.9999676, "write_scale": 1.0},
     ("tree", "bf16"): {"source": "tree_verification_skinny_amd/csrc/k_gemm.hip",
-                       "sha256": "5087e0fd32f94d8434554dbdffd43fea0cdebd84127900349a33bdebae639f17",
-                       "fetch_kib": 178148.7, "write_kib": 6282.0,
-                       "fetch_scale": 1.9999850, "write_scale": 1.0},
+                       "sha256": "6b99f4e24b571010585a68ea2f507bf7cca8927bc5fe7225de7c44a6c56cb96c",
+                       "fetch_kib": 178156.6, "write_kib": 6282.0,
+                       "fetch_scale": 1.9999670, "write_scale": 1.0},
     ("rec", "bf16"): {"source": "tree_verification_skinny_amd/csrc/k_recurrent.hip",
                       "sha256": "e4a2e4ece68656d8812df5325d9800fc91a7a8825085a9d28257dc3739e862d6",
                       "fetch_kib": 58592.0, "write_kib": 32768.1,
                       "fetch_scale": 1.9999850, "write_scale": 1.0},
     ("block", "w12"): {"source": "tree_verification_skinny_amd/csrc/k_gemm.hip",
-                       "sha256": "5087e0fd32f94d8434554dbdffd43fea0cdebd84127900349a33bdebae639f17",
-                       "fetch_kib": 131498.0, "write_kib": 544.0,
-                       "fetch_scale": 1.9999849, "write_scale": 1.0},
+                       "sha256": "6b99f4e24b571010585a68ea2f507bf7cca8927bc5fe7225de7c44a6c56cb96c",
+                       "fetch_kib": 132082.5, "write_kib": 2610.0,
+                       "fetch_scale": 1.9999676, "write_scale": 1.0},
 }
 # Average duration of one launch of the gate/up projection kernel in a rocprofv3 kernel trace of
 # `bench.py --config C` (summaries under profiles/, each with its command). The trace times the
@@ -77,12 +77,12 @@ PMC_TRAFFIC = {
 # which adds the launch's dispatch. Reported beside it while the kernel's source is unchanged.
 PROFILED = {
     ("block", "bf16"): {"source": "tree_verification_skinny_amd/csrc/k_gemm.hip",
-                        "sha256": "5087e0fd32f94d8434554dbdffd43fea0cdebd84127900349a33bdebae639f17",
-                        "kernel": "gemm_kernel<2, 1, 8, 1, false>", "avg_us": 57.67,
+                        "sha256": "6b99f4e24b571010585a68ea2f507bf7cca8927bc5fe7225de7c44a6c56cb96c",
+                        "kernel": "gemm_kernel<4, 1, 8, 1, false, true>", "avg_us": 56.79,
                         "profile": "profiles/block16_ctx4096_kernels.md"},
     ("tree", "bf16"): {"source": "tree_verification_skinny_amd/csrc/k_gemm.hip",
-                       "sha256": "5087e0fd32f94d8434554dbdffd43fea0cdebd84127900349a33bdebae639f17",
-                       "kernel": "gemm_wide_kernel<4, 1, false, true>", "avg_us": 69.28,
+                       "sha256": "6b99f4e24b571010585a68ea2f507bf7cca8927bc5fe7225de7c44a6c56cb96c",
+                       "kernel": "gemm_wide_kernel<4, 1, false, true>", "avg_us": 66.10,
                        "profile": "profiles/tree64_ctx8192_kernels.md"},
     ("batched", "bf16"): {"source": "tree_verification_skinny_amd/csrc/k_gemm_tc.hip",
                           "sha256": "b4b69ebb59847102b35290782bf7e52eadcf557c320954e21a4c734a0e6afac2",
