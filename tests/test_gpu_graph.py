@@ -2,9 +2,10 @@
 pass bit for bit on every replay. Between replays the program does eager work of its own: an eager
 pass with other draft tokens over the same cache, workspace and output buffers, then the outputs
 overwritten with garbage. Cases: the tiny decoder's block of 16 (the automatic and the per-step
-plans) and a batch of two 64-node trees, and a 64-row tree pass whose gate/up runs balanced over
-the compute units (its arrival counters are cleared inside the pass by a fill kernel, never by a
-memset, and left zero by the last arriver); and prompt prefills from an empty context."""
+plans) and a batch of two 64-node trees, and a 64-row tree pass and a block of 16 whose gate/up
+runs balanced over the compute units (the wide and the skinny kernel; the arrival counters are
+cleared inside the pass by a fill kernel, never by a memset, and left zero by the last arriver);
+and prompt prefills from an empty context."""
 import numpy as np
 import pytest
 import torch
@@ -29,7 +30,8 @@ def setup_module(module):
 
 
 @pytest.mark.parametrize("shape_name,B,K,tree,path", [("tiny", 1, 16, False, "auto"), ("tiny", 1, 16, False, "steps"),
-                                                      ("tiny", 2, 64, True, "auto"), ("balanced", 1, 64, True, "auto")])
+                                                      ("tiny", 2, 64, True, "auto"), ("balanced", 1, 64, True, "auto"),
+                                                      ("balanced", 1, 16, False, "auto")])
 def test_graph_replays_equal_eager(shape_name, B, K, tree, path):
     shape = synth.TINY if shape_name == "tiny" else BALANCED
     seed = 2100 + 10 * B + K + (1 if path == "steps" else 0)
