@@ -36,10 +36,13 @@ def setup_module(module):
 # empty) and two row blocks per launch.
 # Skinny kernel (16 rows or fewer): ffn 17408 at hidden 512, 544 groups of two pairs on 512
 # workgroups, the 64 leftover pairs in 8 parts of two K steps; ffn 16896 at hidden 1024: 528
-# groups, the 32 leftover pairs in 16 parts of two steps.
+# groups, the 32 leftover pairs in 16 parts of two steps; ffn 18432 at hidden 256: 576 groups, 128
+# leftover pairs in 4 parts of two steps; ffn 24576: 768 groups, 512 leftover pairs each in one
+# part (each pair finished by the one workgroup that computes it).
 @pytest.mark.parametrize("ffn,hidden,B,k,kind", [(16896, 256, 1, 64, "tree"), (17408, 256, 2, 24, "chain"),
                                                  (17408, 256, 2, 16, "tree"), (17408, 512, 1, 16, "tree"),
-                                                 (17408, 512, 1, 5, "chain"), (16896, 1024, 1, 16, "chain")])
+                                                 (17408, 512, 1, 5, "chain"), (16896, 1024, 1, 16, "chain"),
+                                                 (18432, 256, 1, 16, "tree"), (24576, 256, 1, 7, "chain")])
 def test_balanced_gate_up_pass(ffn, hidden, B, k, kind):
     shape = synth.Shape(n_layers=2, hidden=hidden, n_q_heads=4, n_kv_heads=2, head_dim=64, ffn=ffn, vocab=1024)
     seed = 1300 + ffn % 97 + 7 * B + k + hidden // 256 - 1
