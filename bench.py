@@ -55,11 +55,11 @@ METRIC = "verified tokens/sec + verify-step HBM GB/s (% peak), 27B-shape dense, 
 # figures hold for the kernel source they were taken on; any other source reports null.
 PMC_TRAFFIC = {
     ("block", "bf16"): {"source": "tree_verification_skinny_amd/csrc/k_gemm.hip",
-                        "sha256": "6b99f4e24b571010585a68ea2f507bf7cca8927bc5fe7225de7c44a6c56cb96c",
+                        "sha256": "c2fa92e2d58b21d61d0784c079436ade6ebe53e9f7cde0eae0ab49c8f6d06c20",
                         "fetch_kib": 175305.2, "write_kib": 2610.0,
                         "fetch_scale": 1.9999676, "write_scale": 1.0},
     ("tree", "bf16"): {"source": "tree_verification_skinny_amd/csrc/k_gemm.hip",
-                       "sha256": "6b99f4e24b571010585a68ea2f507bf7cca8927bc5fe7225de7c44a6c56cb96c",
+                       "sha256": "c2fa92e2d58b21d61d0784c079436ade6ebe53e9f7cde0eae0ab49c8f6d06c20",
                        "fetch_kib": 178156.6, "write_kib": 6282.0,
                        "fetch_scale": 1.9999670, "write_scale": 1.0},
     ("rec", "bf16"): {"source": "tree_verification_skinny_amd/csrc/k_recurrent.hip",
@@ -67,9 +67,9 @@ PMC_TRAFFIC = {
                       "fetch_kib": 58592.0, "write_kib": 32768.1,
                       "fetch_scale": 1.9999850, "write_scale": 1.0},
     ("block", "w12"): {"source": "tree_verification_skinny_amd/csrc/k_gemm.hip",
-                       "sha256": "6b99f4e24b571010585a68ea2f507bf7cca8927bc5fe7225de7c44a6c56cb96c",
-                       "fetch_kib": 132082.5, "write_kib": 2610.0,
-                       "fetch_scale": 1.9999676, "write_scale": 1.0},
+                       "sha256": "c2fa92e2d58b21d61d0784c079436ade6ebe53e9f7cde0eae0ab49c8f6d06c20",
+                       "fetch_kib": 132094.1, "write_kib": 2610.0,
+                       "fetch_scale": 1.9999698, "write_scale": 1.0},
 }
 # Average duration of one launch of the gate/up projection kernel in a rocprofv3 kernel trace of
 # `bench.py --config C` (summaries under profiles/, each with its command). The trace times the
@@ -77,11 +77,11 @@ PMC_TRAFFIC = {
 # which adds the launch's dispatch. Reported beside it while the kernel's source is unchanged.
 PROFILED = {
     ("block", "bf16"): {"source": "tree_verification_skinny_amd/csrc/k_gemm.hip",
-                        "sha256": "6b99f4e24b571010585a68ea2f507bf7cca8927bc5fe7225de7c44a6c56cb96c",
+                        "sha256": "c2fa92e2d58b21d61d0784c079436ade6ebe53e9f7cde0eae0ab49c8f6d06c20",
                         "kernel": "gemm_kernel<4, 1, 8, 1, false, true>", "avg_us": 56.79,
                         "profile": "profiles/block16_ctx4096_kernels.md"},
     ("tree", "bf16"): {"source": "tree_verification_skinny_amd/csrc/k_gemm.hip",
-                       "sha256": "6b99f4e24b571010585a68ea2f507bf7cca8927bc5fe7225de7c44a6c56cb96c",
+                       "sha256": "c2fa92e2d58b21d61d0784c079436ade6ebe53e9f7cde0eae0ab49c8f6d06c20",
                        "kernel": "gemm_wide_kernel<4, 1, false, true>", "avg_us": 66.10,
                        "profile": "profiles/tree64_ctx8192_kernels.md"},
     ("batched", "bf16"): {"source": "tree_verification_skinny_amd/csrc/k_gemm_tc.hip",

@@ -145,9 +145,12 @@ __device__ __forceinline__ bf16x8 w12_patch(bf16x8 a, int lane, int pos, int val
 
 __device__ __forceinline__ uint32_t stream_load32(const uint32_t *p) { return __builtin_nontemporal_load(p); }
 
-// A wave's cursor into one tile's exception list: the next entry at or after the wave's step.
+// A wave's window on one tile's exception list: lane l holds entry i + l (a sentinel past the
+// tile's end), so the entries of a step are found with one compare and a ballot, without a load.
 struct W12Cursor {
-    int i, end, step;   // entry index, end of the tile's entries, step of entry i (INT_MAX: none)
+    int i, end, step;   // first entry of the window, end of the tile's entries, the next step
+                        // with an entry (wave-uniform; INT_MAX or beyond any step: none)
+    int x, y;           // this lane's entry: pos (step * 512 + lane * 8 + j) and bf16 bits
 };
 
 __device__ __forceinline__ int w12_step_of(const int2 *exc, int i, int end) {
@@ -167,20 +170,41 @@ __device__ __forceinline__ int w12_first_at(const int2 *exc, int i, int end, int
     }
 }
 
-// Apply the tile's exceptions that fall on step su (wave-uniform) to fragment a; entries of
-// earlier steps belong to the other waves of the workgroup and are skipped.
+// Load the window at entry c.i and the step of its first entry.
+__device__ __forceinline__ void w12_win_load(W12Cursor &c, const int2 *exc, int lane) {
+    const int k = c.i + lane;
+    const int2 e = k < c.end ? exc[k] : make_int2(0x7fffffff, 0);
+    c.x = e.x;
+    c.y = e.y;
+    c.step = __builtin_amdgcn_readfirstlane(e.x) >> 9;
+}
+
+// Apply the tile's exceptions that fall on step su (wave-uniform, never decreasing from call to
+// call; callers test su >= c.step first) to fragment a, and set c.step to the next step with an
+// entry. Entries of other steps (the other waves' or earlier ones) are passed over in registers;
+// the window moves on by 64 entries only once all of its entries lie at or before step su.
 __device__ __forceinline__ bf16x8 w12_fixup(bf16x8 a, W12Cursor &c, const int2 *exc, int su, int lane) {
-    while (c.step < su) {
-        ++c.i;
-        c.step = w12_step_of(exc, c.i, c.end);
+    while (true) {
+        unsigned long long m = __ballot((c.x >> 9) == su);
+        while (m != 0ull) {
+            const int b = __builtin_ctzll(m);
+            m &= m - 1ull;
+            a = w12_patch(a, lane, __builtin_amdgcn_readlane(c.x, b), __builtin_amdgcn_readlane(c.y, b));
+        }
+        // entries sort by step: the first lane past su holds the next step (a sentinel: none)
+        const unsigned long long after = __ballot((c.x >> 9) > su);
+        if (after != 0ull) {
+            c.step = __builtin_amdgcn_readlane(c.x, __builtin_ctzll(after)) >> 9;
+            return a;
+        }
+        if (c.i + 64 < c.end) {
+            c.i += 64;
+            w12_win_load(c, exc, lane);
+            continue;
+        }
+        c.step = 0x7fffffff;
+        return a;
     }
-    while (c.step == su) {
-        const int2 e = exc[c.i];
-        a = w12_patch(a, lane, e.x, e.y);
-        ++c.i;
-        c.step = w12_step_of(exc, c.i, c.end);
-    }
-    return a;
 }
 
 // SwiGLU of four gate and up sums (each rounded to bf16 first), stored as bf16 at h + off.
@@ -286,7 +310,7 @@ __global__ __launch_bounds__(64 * (W + (BAL ? 1 : 0))) void gemm_kernel(GemmIn i
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             cur[t].i = w12_first_at(w12.exc, cur[t].i, cur[t].end, s_begin + wv, lane, st[t]);
-            cur[t].step = w12_step_of(w12.exc, cur[t].i, cur[t].end);
+            w12_win_load(cur[t], w12.exc, lane);
         }
     }
     // activation blocks of this chunk; blocks past the last one (MT rounds the chunk up) re-read
@@ -332,7 +356,7 @@ __global__ __launch_bounds__(64 * (W + (BAL ? 1 : 0))) void gemm_kernel(GemmIn i
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
                     xc[t].i = w12_first_at(w12.exc, xc[t].i, xc[t].end, sq0, lane, st0[t]);
-                    xc[t].step = w12_step_of(w12.exc, xc[t].i, xc[t].end);
+                    w12_win_load(xc[t], w12.exc, lane);
                 }
             }
             floatx4 ex[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
@@ -708,7 +732,7 @@ __global__ __launch_bounds__(64 * kWideWaves) void gemm_wide_kernel(GemmIn in, c
 #pragma unroll
         for (int t = 0; t < TN; ++t) {
             cur[t].i = w12_first_at(w12.exc, cur[t].i, cur[t].end, s_begin, lane, st[t]);
-            cur[t].step = w12_step_of(w12.exc, cur[t].i, cur[t].end);
+            w12_win_load(cur[t], w12.exc, lane);
         }
     }
 
@@ -810,7 +834,7 @@ __global__ __launch_bounds__(64 * kWideWaves) void gemm_wide_kernel(GemmIn in, c
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 xc[t].i = w12_first_at(w12.exc, xc[t].i, xc[t].end, sq0 + wave, lane, st0[t]);
-                xc[t].step = w12_step_of(w12.exc, xc[t].i, xc[t].end);
+                w12_win_load(xc[t], w12.exc, lane);
             }
         }
         const bf16 *xa[TM];
